@@ -1,0 +1,193 @@
+"""Python binding of libhcs.so, the C-ABI library of the hybrid compressed sparse attention path.
+
+Argument marshalling only: torch tensors become device pointers and the current HIP stream;
+every step of the path runs in the library's HIP kernels. The functions mirror the C entry
+points of ``include/hcs.h`` (``hcs_compress_kv`` -> ``compress_kv`` and so on) and return
+nothing; a non-OK status raises ``HcsError`` with the library's message.
+
+There is no fallback: if ``libhcs.so`` is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhcs.so")
+
+FMT = {"bf16": 0, "fp8ds": 1, "mxfp4": 2}
+IN_DTYPE = {torch.bfloat16: 0, torch.float32: 1}
+
+
+class HcsError(RuntimeError):
+    pass
+
+
+class Paged(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
+                ("pt_stride", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("fmt", ctypes.c_int32), ("dim", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise HcsError(f"{LIB_PATH} is not built (python -m hybrid_compressed_sparse_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+        L.hcs_last_error.restype = ctypes.c_char_p
+        L.hcs_abi_version.restype = i32
+        L.hcs_compress_kv.restype = i32
+        L.hcs_compress_kv.argtypes = [vp, vp, i32, i64, vp, vp, i32, i32, i32, i32, vp, vp, Paged,
+                                      vp, i64, vp]
+        L.hcs_index_topk_workspace_size.restype = sz
+        L.hcs_index_topk_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.hcs_index_topk.restype = i32
+        L.hcs_index_topk.argtypes = [vp, vp, vp, Paged, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
+                                     vp, sz, vp]
+        L.hcs_sparse_mla_workspace_size.restype = sz
+        L.hcs_sparse_mla_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.hcs_sparse_mla_decode.restype = i32
+        L.hcs_sparse_mla_decode.argtypes = [vp, Paged, Paged, vp, i32, vp, vp, vp, i32, i32, i32, i32,
+                                            i32, i32, f32, vp, vp, vp, sz, vp]
+        L.hcs_sparse_mla_prefill_workspace_size.restype = sz
+        L.hcs_sparse_mla_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.hcs_sparse_mla_prefill_chunk.restype = i32
+        L.hcs_sparse_mla_prefill_chunk.argtypes = [vp, Paged, Paged, vp, i32, i32, i32, i32, vp, i32,
+                                                   i32, i32, i32, f32, vp, vp, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = lib().hcs_last_error().decode()
+        raise HcsError(f"{what} failed with status {status}: {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "tensor"):
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def paged(pool: torch.Tensor, page_table: torch.Tensor, fmt: str, dim: int) -> Paged:
+    """A paged cache: pool uint8 [num_pages, page_bytes], page_table int32 [num_seqs, pt_stride]."""
+    if pool.dtype != torch.uint8 or page_table.dtype != torch.int32:
+        raise TypeError("pool must be uint8 and page_table int32")
+    return Paged(_ptr(pool, name="pool"), _ptr(page_table, name="page_table"), page_table.shape[-1],
+                 pool.shape[0], FMT[fmt], dim)
+
+
+def _as_paged(c) -> Paged:
+    return c if isinstance(c, Paged) else paged(c.pool, c.page_table, c.fmt, c.dim)
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------------------ compressor
+
+def compress_kv(kv: torch.Tensor, score: torch.Tensor, cu_new: torch.Tensor, start_pos: torch.Tensor,
+                state: torch.Tensor, comp, m: int, ape: Optional[torch.Tensor] = None,
+                dbg: Optional[torch.Tensor] = None, max_new: Optional[int] = None) -> None:
+    """hcs_compress_kv. kv, score [T, d] (bf16 or f32); cu_new [B+1], start_pos [B] int32;
+    state [B, 3d] f32; comp: paged cache (bf16 or fp8ds); dbg [B, rows, d] f32 or None."""
+    if kv.dtype != score.dtype or kv.dtype not in IN_DTYPE:
+        raise TypeError("kv and score must both be bf16 or both float32")
+    B = start_pos.shape[0]
+    d = kv.shape[-1]
+    if max_new is None:
+        raise ValueError("max_new (host bound of new tokens per sequence) is required")
+    _check(lib().hcs_compress_kv(
+        _ptr(kv, name="kv"), _ptr(score, name="score"), IN_DTYPE[kv.dtype], kv.stride(0),
+        _ptr(cu_new, torch.int32, "cu_new"), _ptr(start_pos, torch.int32, "start_pos"), B, max_new, d, m,
+        _ptr(ape, torch.float32, "ape"), _ptr(state, torch.float32, "state"), _as_paged(comp),
+        _ptr(dbg, torch.float32, "dbg"), 0 if dbg is None else dbg.stride(0), _stream()), "compress_kv")
+
+
+# ------------------------------------------------------------------------------ indexer
+
+def index_topk_workspace_size(N: int, max_pos: int, m: int, topk: int) -> int:
+    return lib().hcs_index_topk_workspace_size(N, max_pos, m, topk)
+
+
+def index_topk(q, q_scale: Optional[torch.Tensor], w: torch.Tensor, keys, q_seq: torch.Tensor,
+               q_pos: torch.Tensor, m: int, topk: int, max_pos: int, out_idx: torch.Tensor,
+               out_score: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> None:
+    """hcs_index_topk. q: bf16 [N, H_I, d_I] (bf16 keys) or uint8 [N, H_I, d_I/2] with
+    q_scale uint8 [N, H_I, d_I/32] (mxfp4 keys); w f32 [N, H_I]; out_idx int32 [N, topk]."""
+    N, H_I = w.shape
+    d_I = keys.dim
+    if ws is None:
+        ws = _workspace(index_topk_workspace_size(N, max_pos, m, topk), w.device)
+    _check(lib().hcs_index_topk(
+        _ptr(q, name="q"), _ptr(q_scale, torch.uint8, "q_scale"), _ptr(w, torch.float32, "w"),
+        _as_paged(keys), _ptr(q_seq, torch.int32, "q_seq"), _ptr(q_pos, torch.int32, "q_pos"),
+        N, H_I, d_I, m, topk, max_pos, _ptr(out_idx, torch.int32, "out_idx"),
+        _ptr(out_score, torch.float32, "out_score"), _ptr(ws, name="ws"),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream()), "index_topk")
+
+
+# ------------------------------------------------------------------------------ attention
+
+def sparse_mla_workspace_size(N: int, H: int, d: int, window: int, m: int, topk: int, max_pos: int) -> int:
+    return lib().hcs_sparse_mla_workspace_size(N, H, d, window, m, topk, max_pos)
+
+
+def sparse_mla_decode(q: torch.Tensor, swa, comp, topk_idx: Optional[torch.Tensor], q_seq: torch.Tensor,
+                      q_pos: torch.Tensor, window: int, m: int, max_pos: int, scale: float,
+                      out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                      sink: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> None:
+    """hcs_sparse_mla_decode. q, out bf16 [N, H, d]; topk_idx int32 [N, k] or None (HCA)."""
+    N, H, d = q.shape
+    topk = 0 if topk_idx is None else topk_idx.shape[1]
+    if ws is None:
+        ws = _workspace(sparse_mla_workspace_size(N, H, d, window, m, topk, max_pos), q.device)
+    _check(lib().hcs_sparse_mla_decode(
+        _ptr(q, torch.bfloat16, "q"), _as_paged(swa), _as_paged(comp), _ptr(topk_idx, torch.int32, "topk_idx"),
+        topk, _ptr(q_seq, torch.int32, "q_seq"), _ptr(q_pos, torch.int32, "q_pos"),
+        _ptr(sink, torch.float32, "sink"), N, H, d, window, m, max_pos, scale,
+        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _ptr(ws, name="ws"),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream()), "sparse_mla_decode")
+
+
+def sparse_mla_prefill_workspace_size(Q: int, H: int, d: int, window: int, m: int, topk: int, P0: int) -> int:
+    return lib().hcs_sparse_mla_prefill_workspace_size(Q, H, d, window, m, topk, P0)
+
+
+def sparse_mla_prefill_chunk(q: torch.Tensor, swa, comp, topk_idx: Optional[torch.Tensor], seq: int,
+                             P0: int, window: int, m: int, scale: float, out: torch.Tensor,
+                             lse: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None,
+                             ws: Optional[torch.Tensor] = None) -> None:
+    """hcs_sparse_mla_prefill_chunk for queries P0 .. P0+Q-1 of sequence `seq`."""
+    Q, H, d = q.shape
+    topk = 0 if topk_idx is None else topk_idx.shape[1]
+    if ws is None:
+        ws = _workspace(sparse_mla_prefill_workspace_size(Q, H, d, window, m, topk, P0), q.device)
+    _check(lib().hcs_sparse_mla_prefill_chunk(
+        _ptr(q, torch.bfloat16, "q"), _as_paged(swa), _as_paged(comp), _ptr(topk_idx, torch.int32, "topk_idx"),
+        topk, seq, P0, Q, _ptr(sink, torch.float32, "sink"), H, d, window, m, scale,
+        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _ptr(ws, name="ws"),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream()), "sparse_mla_prefill_chunk")

@@ -1,0 +1,265 @@
+// C ABI entry points: host-side validation, workspace planning and kernel launches.
+// Every check runs before any HIP call, so invalid arguments never touch the device.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hcs_status fail(hcs_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+hcs_status ok() {
+  g_err[0] = 0;
+  return HCS_OK;
+}
+
+hcs_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(HCS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hcs_status check_paged(const hcs_paged& p, const char* name, int want_dim, bool allow_fp8,
+                       bool allow_mx) {
+  if (!p.base || !p.page_table) return fail(HCS_ERR_INVALID_ARG, "%s: null base or page_table", name);
+  if (p.pt_stride <= 0 || p.num_pages <= 0)
+    return fail(HCS_ERR_INVALID_ARG, "%s: pt_stride and num_pages must be positive", name);
+  if (p.fmt != HCS_FMT_BF16 && p.fmt != HCS_FMT_FP8DS && p.fmt != HCS_FMT_MXFP4)
+    return fail(HCS_ERR_INVALID_ARG, "%s: unknown format %d", name, p.fmt);
+  if (p.dim != want_dim) return fail(HCS_ERR_INVALID_ARG, "%s: dim %d, expected %d", name, p.dim, want_dim);
+  if (p.fmt == HCS_FMT_FP8DS && (!allow_fp8 || p.dim != 512))
+    return fail(HCS_ERR_UNSUPPORTED, "%s: fp8_ds rows need dim 512 and a KV cache", name);
+  if (p.fmt == HCS_FMT_MXFP4 && !allow_mx)
+    return fail(HCS_ERR_UNSUPPORTED, "%s: MXFP4 is an indexer-key format", name);
+  if (!aligned(p.base, 16)) return fail(HCS_ERR_INVALID_ARG, "%s: base must be 16-byte aligned", name);
+  return HCS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hcs_last_error(void) { return g_err; }
+int hcs_abi_version(void) { return HCS_ABI_VERSION; }
+
+// ------------------------------------------------------------------------------ compressor
+hcs_status hcs_compress_kv(const void* kv, const void* score, int in_dtype, int64_t row_stride,
+                           const int32_t* cu_new, const int32_t* start_pos, int B, int max_new,
+                           int d, int m, const float* ape, float* state, hcs_paged comp,
+                           float* dbg, int64_t dbg_seq_stride, void* stream) {
+  if (B < 0) return fail(HCS_ERR_INVALID_ARG, "B must be >= 0");
+  if (d < 1 || d > 1024 || d % 8) return fail(HCS_ERR_UNSUPPORTED, "d must be in 1..1024 and a multiple of 8");
+  if (m < 1 || m > 1024) return fail(HCS_ERR_UNSUPPORTED, "m must be in 1..1024");
+  if (in_dtype != HCS_IN_BF16 && in_dtype != HCS_IN_F32) return fail(HCS_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
+  if (B == 0) return ok();
+  if (!kv || !score || !cu_new || !start_pos || !state)
+    return fail(HCS_ERR_INVALID_ARG, "null kv, score, cu_new, start_pos or state");
+  if (row_stride < d) return fail(HCS_ERR_INVALID_ARG, "row_stride %lld < d %d", (long long)row_stride, d);
+  if (max_new < 1) return fail(HCS_ERR_INVALID_ARG, "max_new must be >= 1");
+  hcs_status s = check_paged(comp, "comp", d, true, false);
+  if (s != HCS_OK) return s;
+  if (dbg && dbg_seq_stride < 0) return fail(HCS_ERR_INVALID_ARG, "negative dbg_seq_stride");
+  hcs::CompressArgs a{};
+  a.kv = kv;
+  a.score = score;
+  a.in_bf16 = in_dtype == HCS_IN_BF16;
+  a.row_stride = row_stride;
+  a.cu_new = cu_new;
+  a.start_pos = start_pos;
+  a.B = B;
+  a.d = d;
+  a.m = m;
+  a.fmt = comp.fmt;
+  a.ape = ape;
+  a.state = state;
+  a.comp_base = static_cast<uint8_t*>(comp.base);
+  a.comp_pt = comp.page_table;
+  a.comp_pt_stride = comp.pt_stride;
+  a.comp_num_pages = comp.num_pages;
+  a.dbg = dbg;
+  a.dbg_stride = dbg_seq_stride;
+  return hip_status(hcs::launch_compress(a, max_new, static_cast<hipStream_t>(stream)), "compress_kv");
+}
+
+// ------------------------------------------------------------------------------ indexer
+size_t hcs_index_topk_workspace_size(int N, int max_pos, int m, int topk) {
+  if (N <= 0 || max_pos < 0 || m < 1 || topk < 1) return 0;
+  return hcs::topk_plan(N, max_pos, m, topk).ws_bytes;
+}
+
+hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
+                          const int32_t* q_seq, const int32_t* q_pos, int N, int H_I, int d_I,
+                          int m, int topk, int max_pos, int32_t* out_idx, float* out_score,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (N < 0) return fail(HCS_ERR_INVALID_ARG, "N must be >= 0");
+  if (H_I < 1 || H_I > 64) return fail(HCS_ERR_UNSUPPORTED, "H_I must be in 1..64");
+  if (m < 1) return fail(HCS_ERR_INVALID_ARG, "m must be >= 1");
+  if (topk < 1 || topk > 4096) return fail(HCS_ERR_UNSUPPORTED, "topk must be in 1..4096");
+  if (max_pos < 0) return fail(HCS_ERR_INVALID_ARG, "max_pos must be >= 0");
+  if (N == 0) return ok();
+  if (!q || !w || !q_seq || !q_pos || !out_idx) return fail(HCS_ERR_INVALID_ARG, "null q, w, q_seq, q_pos or out_idx");
+  hcs_status s = check_paged(keys, "keys", d_I, false, true);
+  if (s != HCS_OK) return s;
+  if (keys.fmt == HCS_FMT_BF16 && d_I != 32 && d_I != 64 && d_I != 128)
+    return fail(HCS_ERR_UNSUPPORTED, "bf16 indexer keys need d_I in {32, 64, 128}");
+  if (keys.fmt == HCS_FMT_MXFP4 && (d_I != 128 || !q_scale))
+    return fail(HCS_ERR_UNSUPPORTED, "MXFP4 indexer keys need d_I == 128 and q_scale");
+  if (!aligned(q, 16)) return fail(HCS_ERR_INVALID_ARG, "q must be 16-byte aligned");
+  if ((int64_t)keys.pt_stride * HCS_PAGE_ROWS < (int64_t)(max_pos + 1) / m)
+    return fail(HCS_ERR_INVALID_ARG, "keys: pt_stride %d does not cover %d entries", keys.pt_stride,
+                (max_pos + 1) / m);
+  const hcs::TopkPlan plan = hcs::topk_plan(N, max_pos, m, topk);
+  if (!ws || ws_bytes < plan.ws_bytes)
+    return fail(HCS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.ws_bytes, ws_bytes);
+  if (!aligned(ws, 256)) return fail(HCS_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+  hcs::IndexArgs a{};
+  a.q = static_cast<const uint8_t*>(q);
+  a.q_scale = q_scale;
+  a.w = w;
+  a.keys = hcs::to_paged(keys);
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.N = N;
+  a.H_I = H_I;
+  a.d_I = d_I;
+  a.m = m;
+  a.pos_cap = max_pos;
+  a.nv_cap = (max_pos + 1) / m;
+  a.scores = static_cast<float*>(ws);
+  a.score_stride = (int64_t)(plan.score_bytes / sizeof(float) / N);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hcs::launch_index_scores(a, keys.fmt, st);
+  if (e != hipSuccess) return hip_status(e, "index_topk scores");
+  void* cand = static_cast<uint8_t*>(ws) + (plan.score_bytes + 255) / 256 * 256;
+  return hip_status(hcs::launch_topk(a, plan, topk, out_idx, out_score, cand, st), "index_topk select");
+}
+
+// ------------------------------------------------------------------------------ attention
+static hcs_status check_attn(const void* q, const hcs_paged& swa, const hcs_paged& comp,
+                             const int32_t* topk_idx, int topk, int N, int H, int d, int window,
+                             int m, const void* out) {
+  if (N < 0) return fail(HCS_ERR_INVALID_ARG, "N must be >= 0");
+  if (d != 128 && d != 512) return fail(HCS_ERR_UNSUPPORTED, "d must be 128 or 512");
+  if (H < 1 || H > 128) return fail(HCS_ERR_UNSUPPORTED, "H must be in 1..128");
+  if (window < 0) return fail(HCS_ERR_INVALID_ARG, "window must be >= 0");
+  if (m < 1) return fail(HCS_ERR_INVALID_ARG, "m must be >= 1");
+  if (topk_idx && topk < 1) return fail(HCS_ERR_INVALID_ARG, "topk must be >= 1 with topk_idx");
+  if (N == 0) return HCS_OK;
+  if (!q || !out) return fail(HCS_ERR_INVALID_ARG, "null q or out");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(HCS_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  hcs_status s = check_paged(swa, "swa", d, true, false);
+  if (s != HCS_OK) return s;
+  s = check_paged(comp, "comp", d, true, false);
+  if (s != HCS_OK) return s;
+  if (swa.fmt != comp.fmt) return fail(HCS_ERR_UNSUPPORTED, "swa and comp must share a format");
+  return HCS_OK;
+}
+
+size_t hcs_sparse_mla_workspace_size(int N, int H, int d, int window, int m, int topk, int max_pos) {
+  if (N <= 0 || H <= 0 || m < 1 || max_pos < 0 || window < 0) return 0;
+  return hcs::attn_plan(N, H, d, window, m, topk, max_pos).ws_bytes;
+}
+
+static hcs_status run_attn(hcs::AttnArgs& a, int d, int fmt, int window, int m, int topk,
+                           int max_pos, void* ws, size_t ws_bytes, void* stream) {
+  if (window > 0 && (int64_t)a.swa.pt_stride * HCS_PAGE_ROWS <= (int64_t)max_pos)
+    return fail(HCS_ERR_INVALID_ARG, "swa: pt_stride %d does not cover position %d", a.swa.pt_stride,
+                max_pos);
+  if ((int64_t)a.comp.pt_stride * HCS_PAGE_ROWS < (int64_t)(max_pos + 1) / m)
+    return fail(HCS_ERR_INVALID_ARG, "comp: pt_stride %d does not cover %d entries", a.comp.pt_stride,
+                (max_pos + 1) / m);
+  const hcs::AttnPlan plan = hcs::attn_plan(a.N, a.H, d, window, m, topk, max_pos);
+  if (plan.ws_bytes && (!ws || ws_bytes < plan.ws_bytes))
+    return fail(HCS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.ws_bytes, ws_bytes);
+  if (plan.ws_bytes && !aligned(ws, 256)) return fail(HCS_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+  a.nsplit = plan.nsplit;
+  a.tiles_per_split = plan.tiles_per_split;
+  if (plan.nsplit > 1) {
+    a.ws_o = static_cast<float*>(ws);
+    a.ws_ml = a.ws_o + (size_t)a.N * plan.nsplit * a.H * d;
+  }
+  return hip_status(hcs::launch_sparse_mla(a, d, fmt, static_cast<hipStream_t>(stream)), "sparse_mla");
+}
+
+hcs_status hcs_sparse_mla_decode(const void* q, hcs_paged swa, hcs_paged comp,
+                                 const int32_t* topk_idx, int topk, const int32_t* q_seq,
+                                 const int32_t* q_pos, const float* sink, int N, int H, int d,
+                                 int window, int m, int max_pos, float scale, void* out,
+                                 float* lse, void* ws, size_t ws_bytes, void* stream) {
+  hcs_status s = check_attn(q, swa, comp, topk_idx, topk, N, H, d, window, m, out);
+  if (s != HCS_OK) return s;
+  if (max_pos < 0) return fail(HCS_ERR_INVALID_ARG, "max_pos must be >= 0");
+  if (N == 0) return ok();
+  if (!q_seq || !q_pos) return fail(HCS_ERR_INVALID_ARG, "null q_seq or q_pos");
+  hcs::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.swa = hcs::to_paged(swa);
+  a.comp = hcs::to_paged(comp);
+  a.topk_idx = topk_idx;
+  a.topk = topk_idx ? topk : 0;
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.sink = sink;
+  a.N = N;
+  a.H = H;
+  a.window = window;
+  a.m = m;
+  a.pos_cap = max_pos;
+  a.nv_cap = (max_pos + 1) / m;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  return run_attn(a, d, swa.fmt, window, m, a.topk, max_pos, ws, ws_bytes, stream);
+}
+
+size_t hcs_sparse_mla_prefill_workspace_size(int Q, int H, int d, int window, int m, int topk, int P0) {
+  if (Q <= 0 || P0 < 0) return 0;
+  return hcs_sparse_mla_workspace_size(Q, H, d, window, m, topk, P0 + Q - 1);
+}
+
+hcs_status hcs_sparse_mla_prefill_chunk(const void* q, hcs_paged swa, hcs_paged comp,
+                                        const int32_t* topk_idx, int topk, int seq, int P0, int Q,
+                                        const float* sink, int H, int d, int window, int m,
+                                        float scale, void* out, float* lse, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  hcs_status s = check_attn(q, swa, comp, topk_idx, topk, Q, H, d, window, m, out);
+  if (s != HCS_OK) return s;
+  if (P0 < 0 || seq < 0) return fail(HCS_ERR_INVALID_ARG, "P0 and seq must be >= 0");
+  if ((int64_t)P0 + Q > INT32_MAX) return fail(HCS_ERR_INVALID_ARG, "P0 + Q overflows int32");
+  if (Q == 0) return ok();
+  hcs::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.swa = hcs::to_paged(swa);
+  a.comp = hcs::to_paged(comp);
+  a.topk_idx = topk_idx;
+  a.topk = topk_idx ? topk : 0;
+  a.q_seq = nullptr;
+  a.q_pos = nullptr;
+  a.seq_const = seq;
+  a.p0 = P0;
+  a.sink = sink;
+  a.N = Q;
+  a.H = H;
+  a.window = window;
+  a.m = m;
+  a.pos_cap = P0 + Q - 1;
+  a.nv_cap = (P0 + Q) / m;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  return run_attn(a, d, swa.fmt, window, m, a.topk, P0 + Q - 1, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

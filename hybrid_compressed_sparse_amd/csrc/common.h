@@ -1,0 +1,76 @@
+// Shared device helpers for the gfx950 kernels of the hybrid compressed sparse attention path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hcs.h"
+
+namespace hcs {
+
+constexpr int kPageRows = HCS_PAGE_ROWS;
+constexpr int kFp8Latent = 448;      // e4m3 latent dims of an fp8_ds row
+constexpr int kFp8Rope = 64;         // bf16 rotary dims of an fp8_ds row
+constexpr int kFp8Block = 64;        // latent dims per UE8M0 scale
+constexpr int kFp8PageCodes = 0;                              // [64][448] u8
+constexpr int kFp8PageRope = kPageRows * kFp8Latent;          // [64][64] bf16 at 28672
+constexpr int kFp8PageScales = kFp8PageRope + kPageRows * kFp8Rope * 2;   // [64][8] u8 at 36864
+constexpr int kFp8PageBytes = kFp8PageScales + kPageRows * 8;             // 37376 = 64 * 584
+constexpr int kMxBlock = 32;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// A paged cache as the kernels see it.
+struct Paged {
+  const uint8_t* base;
+  const int32_t* pt;
+  int32_t pt_stride;
+  int32_t num_pages;
+};
+
+inline Paged to_paged(const hcs_paged& p) {
+  return Paged{static_cast<const uint8_t*>(p.base), p.page_table, p.pt_stride, p.num_pages};
+}
+
+// Page id of logical row `row` of sequence `seq`, or -1 if not resident.
+__device__ __forceinline__ int page_of(const Paged& c, int seq, int row) {
+  int pg = __ldg(c.pt + (int64_t)seq * c.pt_stride + (row >> 6));
+  return (pg >= 0 && pg < c.num_pages) ? pg : -1;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round-to-nearest-even float32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Order-preserving map of float32 to uint32: a < b  <=>  key(a) < key(b) (for non-NaN).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_key_f32(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+}  // namespace hcs

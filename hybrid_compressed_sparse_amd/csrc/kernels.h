@@ -1,0 +1,76 @@
+// Kernel argument blocks and host-side launchers (implemented in the *.hip files).
+#pragma once
+
+#include "common.h"
+
+namespace hcs {
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const uint16_t* q;          // [N, H, D] bf16
+  Paged swa, comp;
+  const int32_t* topk_idx;    // [N, topk] or nullptr (all visible entries)
+  int topk;
+  const int32_t* q_seq;       // [N] or nullptr: then every query is of sequence seq_const
+  const int32_t* q_pos;       // [N] or nullptr: then query t is at position p0 + t
+  int seq_const, p0;
+  const float* sink;          // [H] or nullptr
+  int N, H, window, m, nv_cap, pos_cap;
+  int nsplit, tiles_per_split;
+  float scale_log2;           // softmax scale * log2(e)
+  uint16_t* out;              // [N, H, D] bf16
+  float* lse;                 // [N, H] or nullptr
+  float* ws_o;                // [N, nsplit, H, D] partial outputs (nsplit > 1)
+  float* ws_ml;               // [N, nsplit, H, 2] partial (max, sum) in log2 units
+};
+
+struct AttnPlan {
+  int nsplit, tiles_per_split;
+  size_t ws_bytes;
+};
+AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos);
+hipError_t launch_sparse_mla(const AttnArgs& a, int d, int fmt, hipStream_t stream);
+
+// ---------------------------------------------------------------- compressor
+struct CompressArgs {
+  const void* kv;
+  const void* score;
+  int in_bf16;
+  int64_t row_stride;
+  const int32_t* cu_new;
+  const int32_t* start_pos;
+  int B, d, m, fmt;
+  const float* ape;
+  float* state;
+  uint8_t* comp_base;
+  const int32_t* comp_pt;
+  int comp_pt_stride, comp_num_pages;
+  float* dbg;
+  int64_t dbg_stride;
+};
+hipError_t launch_compress(const CompressArgs& a, int max_new, hipStream_t stream);
+
+// ---------------------------------------------------------------- indexer + top-k
+struct IndexArgs {
+  const uint8_t* q;           // bf16 [N, H_I, d_I] or packed e2m1 [N, H_I, d_I/2]
+  const uint8_t* q_scale;     // [N, H_I, d_I/32] (mxfp4)
+  const float* w;             // [N, H_I]
+  Paged keys;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  int N, H_I, d_I, m, nv_cap, pos_cap;
+  float* scores;              // [N, score_stride]
+  int64_t score_stride;
+};
+
+struct TopkPlan {
+  int two_stage;
+  int nchunks;                // stage-1 chunks per query (two-stage)
+  size_t score_bytes, cand_bytes, ws_bytes;
+};
+TopkPlan topk_plan(int N, int max_pos, int m, int topk);
+hipError_t launch_index_scores(const IndexArgs& a, int fmt, hipStream_t stream);
+hipError_t launch_topk(const IndexArgs& a, const TopkPlan& plan, int topk, int32_t* out_idx,
+                       float* out_score, void* cand, hipStream_t stream);
+
+}  // namespace hcs

@@ -1,0 +1,197 @@
+/*
+ * hcs.h -- C ABI of the hybrid compressed sparse attention hot path for MI355X (gfx950).
+ *
+ * One step of a DeepSeek-V4-style compressed attention layer, as described on the pages
+ * "DeepSeek V4 Attention: Code Reading Map" (sections "How Does Compression Actually Work?",
+ * "Phase 2" and "Phase 3: forward_mqa()") and the "DeepSeek V4.1 attention" API page:
+ *
+ *   hcs_compress_kv           the KV compressor: every block of m raw tokens becomes one
+ *                             compressed entry (per-channel softmax of the gate logits over
+ *                             the block, weighted sum of the raw KV rows), stored in the
+ *                             compressed cache in its format;
+ *   hcs_index_topk            the Lightning Indexer of CSA layers: scores of every visible
+ *                             compressed entry, I = sum_h w_h * ReLU(q_h . k), and the top-k;
+ *   hcs_sparse_mla_decode     single-KV-head attention of every query head over the query's
+ *                             sliding window plus its selected (CSA) or all visible (HCA)
+ *                             compressed entries, K = V = the shared row;
+ *   hcs_sparse_mla_prefill_chunk  the same for a chunk of consecutive queries of one sequence.
+ *
+ * Conventions shared by every call
+ *   - Pointers are device pointers unless marked "host". The caller owns every buffer; the
+ *     library allocates nothing and keeps no state between calls except the thread-local
+ *     error text.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream). Arguments are validated on the host before any launch; a non-OK
+ *     status means nothing was launched, and hcs_last_error() describes why.
+ *   - Device-side faults, if any, surface at the caller's next synchronisation.
+ *   - Positions are absolute token positions (int32). Compressed entry i of a sequence covers
+ *     positions m*i .. m*i+m-1 and is visible to a query at position p when m*i+m-1 <= p, so
+ *     n_visible(p) = (p + 1) / m. The sliding window of a query at p is positions
+ *     max(0, p-window+1) .. p (its own token included).
+ *
+ * Paged caches (hcs_paged)
+ *   A cache is a pool of pages of HCS_PAGE_ROWS = 64 rows. Logical row r of sequence s lives
+ *   in page page_table[s * pt_stride + r / 64] at slot r % 64. Logical rows are absolute
+ *   positions for the sliding-window cache and entry indices for the compressed and indexer
+ *   caches. A page id outside [0, num_pages) (e.g. -1) means "not resident": reads of such a
+ *   row are skipped (the row does not take part), writes are dropped.
+ *   Inside a page, each field of the 64 rows is stored contiguously (structure of arrays):
+ *     HCS_FMT_BF16  dim D : [64][D] bf16                                  (2*D B per row)
+ *     HCS_FMT_FP8DS dim 512: [64][448] e4m3 | [64][64] bf16 | [64][8] B    (584 B per row)
+ *                   latent dim c (< 448) = e4m3(code) * 2^(scale[c/64] - 127); bytes 0..6 of
+ *                   the 8-byte field are the UE8M0 scales, byte 7 is padding (written 0);
+ *                   dims 448..511 are the bf16 rotary dims.
+ *     HCS_FMT_MXFP4 dim D  : [64][D/2] packed e2m1 | [64][D/32] UE8M0     (68 B per row, D=128)
+ *                   element 2j is the low nibble of byte j, 2j+1 the high nibble; element c
+ *                   is scaled by 2^(scale[c/32] - 127).
+ *   e4m3 is OCP FP8 E4M3 (max 448, no infinities), e2m1 is OCP MX FP4, UE8M0 is 2^(b-127).
+ */
+#ifndef HCS_H
+#define HCS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HCS_ABI_VERSION 1
+#define HCS_PAGE_ROWS 64
+
+typedef enum {
+  HCS_OK = 0,
+  HCS_ERR_INVALID_ARG = 1,        /* a null pointer, a negative size, a bad enum value       */
+  HCS_ERR_UNSUPPORTED = 2,        /* a valid combination this library does not implement     */
+  HCS_ERR_WORKSPACE_TOO_SMALL = 3,
+  HCS_ERR_HIP = 4                 /* a HIP launch error (text in hcs_last_error())            */
+} hcs_status;
+
+typedef enum { HCS_FMT_BF16 = 0, HCS_FMT_FP8DS = 1, HCS_FMT_MXFP4 = 2 } hcs_fmt;
+typedef enum { HCS_IN_BF16 = 0, HCS_IN_F32 = 1 } hcs_in_dtype;
+
+typedef struct {
+  void* base;                 /* pool of num_pages pages in the layout of `fmt`           */
+  const int32_t* page_table;  /* [num_seqs * pt_stride] int32 page ids                    */
+  int32_t pt_stride;          /* page-table entries per sequence (> 0)                    */
+  int32_t num_pages;          /* pages in the pool                                        */
+  int32_t fmt;                /* hcs_fmt                                                  */
+  int32_t dim;                /* row dimension (512 for HCS_FMT_FP8DS)                    */
+} hcs_paged;
+
+/* Thread-local text of the last non-OK status returned on this thread ("" if none). */
+const char* hcs_last_error(void);
+/* HCS_ABI_VERSION of the loaded library. */
+int hcs_abi_version(void);
+
+/* ------------------------------------------------------------------------------------ */
+/* KV compressor.                                                                        */
+/* "Code Reading Map", "How Does Compression Actually Work?": for every completed block i */
+/* of m tokens, z[j,c] = score[m*i+j, c] + ape[j, c], alpha[., c] = softmax_j z[., c] (per */
+/* channel), entry[i, c] = sum_j alpha[j, c] * kv[m*i+j, c]. The float32 state of a      */
+/* sequence's trailing partial block carries from one call to the next, so any split of a */
+/* token stream into calls gives the same entries.                                       */
+/*                                                                                        */
+/* kv, score  [T_total, row_stride] rows of in_dtype (HCS_IN_BF16 or HCS_IN_F32); the     */
+/*            first d columns are used. Sequence b's new tokens are rows                  */
+/*            cu_new[b] .. cu_new[b+1]-1, at positions start_pos[b], start_pos[b]+1, ...  */
+/* cu_new     [B+1] int32, non-decreasing, cu_new[0] = 0.                                 */
+/* start_pos  [B] int32 >= 0.                                                             */
+/* max_new    host: an upper bound of cu_new[b+1]-cu_new[b] (sizes the launch; any value  */
+/*            >= 1 is correct, a tight one is fastest).                                   */
+/* ape        [m, d] float32 positional encoding added to the gate logits, or NULL (0).   */
+/* state      [B, 3*d] float32, in/out: per channel (running max, running sum of          */
+/*            exp(z - max), running sum of exp(z - max) * kv) of the block containing     */
+/*            position start_pos[b]-1. It is read only when start_pos[b] % m != 0 and is  */
+/*            left describing the block of the last new token (reset if that block        */
+/*            completed). Sequences with no new tokens are untouched.                     */
+/* comp       compressed cache (HCS_FMT_BF16 with dim d, or HCS_FMT_FP8DS with d = 512):  */
+/*            every entry completed by this call is written at its entry index.           */
+/*            fp8_ds: per 64-dim latent block the scale is the smallest power of two 2^e  */
+/*            with amax <= 448 * 2^e, codes are round-to-nearest-even of value / 2^e.     */
+/* dbg        optional [B, dbg_seq_stride] float32 copy of the completed entries before    */
+/*            rounding to the cache format: entry i of sequence b at                       */
+/*            dbg[b*dbg_seq_stride + (i - start_pos[b]/m) * d]. NULL to skip.             */
+/* Constraints: 1 <= d <= 1024, d % 8 == 0, 1 <= m <= 1024, B >= 0.                       */
+hcs_status hcs_compress_kv(const void* kv, const void* score, int in_dtype, int64_t row_stride,
+                           const int32_t* cu_new, const int32_t* start_pos, int B, int max_new,
+                           int d, int m, const float* ape, float* state, hcs_paged comp,
+                           float* dbg, int64_t dbg_seq_stride, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* Lightning-Indexer scores and top-k selection (CSA layers).                             */
+/* "Code Reading Map", "Aux stream 0 (CSA only)": scores between indexer queries and the  */
+/* compressed indexer keys select the top-k compressed entries. Score of entry i for      */
+/* query t: I[t,i] = sum_h w[t,h] * max(0, q[t,h,:] . k[i,:]) over i < n_visible(p_t)     */
+/* (scale factors are folded into w by the caller). The k largest are selected, ties to   */
+/* the smaller index. When n_visible(p_t) <= k every visible entry is selected ("DeepSeek */
+/* V4.1 attention" page, short-context rule) and the row is padded with -1.               */
+/*                                                                                        */
+/* q        keys.fmt == HCS_FMT_BF16 : [N, H_I, d_I] bf16, q_scale = NULL.                */
+/*          keys.fmt == HCS_FMT_MXFP4: [N, H_I, d_I/2] packed e2m1 (low nibble first) and */
+/*                                     q_scale [N, H_I, d_I/32] UE8M0 bytes.              */
+/* w        [N, H_I] float32.                                                             */
+/* keys     indexer key cache, dim d_I, by entry index.                                   */
+/* q_seq    [N] int32 sequence of each query (page-table row); q_pos [N] int32 position.  */
+/* max_pos  host: an upper bound of q_pos (positions above it are read as max_pos).       */
+/* out_idx  [N, topk] int32: the selected entry ids, in no particular order, -1 at the    */
+/*          tail when fewer than topk entries are visible.                                */
+/* out_score [N, topk] float32 scores of out_idx (unspecified where out_idx is -1), or NULL.*/
+/* ws       workspace of at least hcs_index_topk_workspace_size(N, max_pos, m, topk) bytes. */
+/* Constraints: H_I in 1..64, d_I in {32, 64, 128} (bf16) or d_I == 128 (mxfp4),           */
+/* 1 <= topk <= 4096.                                                                     */
+size_t hcs_index_topk_workspace_size(int N, int max_pos, int m, int topk);
+hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
+                          const int32_t* q_seq, const int32_t* q_pos, int N, int H_I, int d_I,
+                          int m, int topk, int max_pos, int32_t* out_idx, float* out_score,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* Sparse MLA decode (single shared KV head, MQA).                                        */
+/* "Code Reading Map", "Phase 3: forward_mqa()" and "Concrete Trace": each query head     */
+/* attends over the query's sliding-window rows plus its selected compressed entries      */
+/* (CSA: topk_idx) or all visible ones (HCA: topk_idx == NULL); both sets are attended    */
+/* together, without removing raw rows a compressed entry also covers. For head h:        */
+/*   l_r = scale * q_h . row_r,  o_h = sum_r e^{l_r} row_r / (sum_r e^{l_r} + e^{sink_h}),  */
+/*   lse_h = log(sum_r e^{l_r} + e^{sink_h}); the value of a row is the row itself.        */
+/* Selected ids outside [0, n_visible(p)) and -1 are skipped. A query with no row and no  */
+/* sink gets o = 0, lse = -inf.                                                           */
+/*                                                                                        */
+/* q        [N, H, d] bf16 (normalised and rotated upstream).                             */
+/* swa      raw KV rows by absolute position (fmt = comp.fmt, dim d).                     */
+/* comp     compressed entries by index (HCS_FMT_BF16, or HCS_FMT_FP8DS with d = 512).    */
+/* topk_idx [N, topk] int32 or NULL (HCA).                                                */
+/* q_seq, q_pos  [N] int32.     sink  [H] float32 or NULL (no sink).                      */
+/* max_pos  host: an upper bound of q_pos.     scale: softmax scale (d^-1/2 on the pages). */
+/* out      [N, H, d] bf16.     lse  [N, H] float32 (natural log) or NULL.                */
+/* ws       workspace of hcs_sparse_mla_workspace_size(N, H, d, window, m, topk, max_pos)  */
+/*          bytes (topk = 0 for HCA).                                                     */
+/* Constraints: d in {128, 512}, 1 <= H <= 128, window >= 0, m >= 1.                      */
+size_t hcs_sparse_mla_workspace_size(int N, int H, int d, int window, int m, int topk, int max_pos);
+hcs_status hcs_sparse_mla_decode(const void* q, hcs_paged swa, hcs_paged comp,
+                                 const int32_t* topk_idx, int topk, const int32_t* q_seq,
+                                 const int32_t* q_pos, const float* sink, int N, int H, int d,
+                                 int window, int m, int max_pos, float scale, void* out,
+                                 float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* Sparse MLA for a prefill chunk: hcs_sparse_mla_decode for the Q consecutive queries    */
+/* P0 .. P0+Q-1 of sequence `seq` ("DeepSeek-V4 Inference on Ascend", prefill path; the   */
+/* chunk bounds the gathered KV). Each query has its own causal n_visible(p) and window;  */
+/* the window reaches into the chunk itself, whose raw rows must already be in `swa`, and */
+/* the chunk's own completed entries must already be in `comp` (hcs_compress_kv first).   */
+/* q [Q, H, d] bf16, topk_idx [Q, topk] or NULL, out [Q, H, d] bf16, lse [Q, H] or NULL.   */
+/* ws: hcs_sparse_mla_prefill_workspace_size(...) bytes (0 is valid).                      */
+size_t hcs_sparse_mla_prefill_workspace_size(int Q, int H, int d, int window, int m, int topk,
+                                             int P0);
+hcs_status hcs_sparse_mla_prefill_chunk(const void* q, hcs_paged swa, hcs_paged comp,
+                                        const int32_t* topk_idx, int topk, int seq, int P0, int Q,
+                                        const float* sink, int H, int d, int window, int m,
+                                        float scale, void* out, float* lse, void* ws,
+                                        size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HCS_H */

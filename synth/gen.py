@@ -230,7 +230,9 @@ def build(wl: Workload, seed: int = 0, device="cpu", ctx_per_seq: Optional[list]
         ctx = [wl.P0 + wl.Q]
         q_seq = torch.zeros(wl.Q, dtype=torch.int32)
         q_pos = torch.arange(wl.P0, wl.P0 + wl.Q, dtype=torch.int32)
-        c_start, c_len = [wl.P0], [wl.Q]
+        # the stream starts at the block holding P0: tokens before P0 are the previous chunk's
+        c0 = (wl.P0 // m) * m
+        c_start, c_len = [c0], [wl.P0 + wl.Q - c0]
         n_step = wl.Q
     else:
         raise ValueError(wl.kind)

@@ -1,0 +1,90 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad arguments on the host
+(no GPU needed: every check below returns before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hybrid_compressed_sparse_amd as hcs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hcs.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(hcs.LIB_PATH), reason="libhcs.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hcs_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ["hcs_compress_kv", "hcs_index_topk", "hcs_sparse_mla_decode", "hcs_sparse_mla_prefill_chunk"]:
+        assert n in names
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(hcs.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert hcs.lib().hcs_abi_version() == 1
+
+
+def _paged(fmt=0, dim=512, base=16, pt=16, stride=4, pages=8):
+    return hcs.Paged(base, pt, stride, pages, fmt, dim)
+
+
+@needs_lib
+def test_validation_errors_before_any_launch():
+    L = hcs.lib()
+    # attention: unsupported head dim
+    st = L.hcs_sparse_mla_decode(16, _paged(), _paged(), None, 0, 16, 16, None, 4, 64, 256, 128, 4, 100,
+                                 0.1, 16, None, None, 0, None)
+    assert st == 2 and b"d must be" in L.hcs_last_error()
+    # attention: negative window
+    st = L.hcs_sparse_mla_decode(16, _paged(), _paged(), None, 0, 16, 16, None, 4, 64, 512, -1, 4, 100,
+                                 0.1, 16, None, None, 0, None)
+    assert st == 1
+    # attention: fp8_ds needs dim 512
+    st = L.hcs_sparse_mla_decode(16, _paged(1, 128), _paged(1, 128), None, 0, 16, 16, None, 4, 64, 128,
+                                 16, 4, 100, 0.1, 16, None, None, 0, None)
+    assert st == 2
+    # attention: page table too narrow for the positions
+    st = L.hcs_sparse_mla_decode(16, _paged(stride=1), _paged(), None, 0, 16, 16, None, 4, 64, 512, 128,
+                                 4, 100, 0.1, 16, None, None, 0, None)
+    assert st == 1 and b"pt_stride" in L.hcs_last_error()
+    # attention: workspace too small when the row list is split
+    need = L.hcs_sparse_mla_workspace_size(4, 64, 512, 128, 4, 0, 200)
+    assert need > 0
+    st = L.hcs_sparse_mla_decode(16, _paged(), _paged(), None, 0, 16, 16, None, 4, 64, 512, 128, 4, 200,
+                                 0.1, 16, None, 256, need - 1, None)
+    assert st == 3
+    # indexer: top-k limits and formats
+    st = L.hcs_index_topk(16, None, 16, _paged(0, 128), 16, 16, 4, 64, 128, 4, 5000, 1000, 16, None,
+                          None, 0, None)
+    assert st == 2
+    st = L.hcs_index_topk(16, None, 16, _paged(2, 128), 16, 16, 4, 64, 128, 4, 64, 1000, 16, None,
+                          None, 0, None)
+    assert st == 2 and b"q_scale" in L.hcs_last_error()
+    st = L.hcs_index_topk(16, None, 16, _paged(0, 128), 16, 16, 4, 64, 128, 4, 64, 1000, 16, None,
+                          None, 0, None)
+    assert st == 3
+    # compressor: bad dtype, coarse m, wrong cache dim
+    assert L.hcs_compress_kv(16, 16, 7, 512, 16, 16, 2, 4, 512, 4, None, 16, _paged(), None, 0, None) == 1
+    assert L.hcs_compress_kv(16, 16, 1, 512, 16, 16, 2, 4, 512, 2000, None, 16, _paged(), None, 0, None) == 2
+    assert L.hcs_compress_kv(16, 16, 1, 512, 16, 16, 2, 4, 512, 4, None, 16, _paged(0, 128), None, 0,
+                             None) == 1
+    # empty calls are fine and launch nothing
+    assert L.hcs_compress_kv(None, None, 1, 0, None, None, 0, 0, 512, 4, None, None, _paged(), None, 0,
+                             None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(hcs, "_lib", None)
+    monkeypatch.setattr(hcs, "LIB_PATH", "/nonexistent/libhcs.so")
+    with pytest.raises(hcs.HcsError):
+        hcs.lib()

@@ -1,0 +1,125 @@
+"""GPU parity of the HIP path against the oracle, through the C ABI (MI355X only)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import method as OM
+from oracle import pipeline as OP
+from synth import configs as C
+from synth import gen as G
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests import gpu_util as U
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def _check_step(sc, queries=None, sink=None, split_at=None, check_entries=True):
+    """Run the whole step on the GPU and compare every stage with the oracle."""
+    wl = sc.wl
+    U.say(f"[case] {wl.name} B={len(sc.c_cu) - 1} N={sc.N} max_pos={sc.max_pos()} seed={sc.seed}")
+    step, dbg = U.run_step(sc, sink=sink, split_at=split_at)
+    qs = list(range(sc.N)) if queries is None else queries
+    sink_np = None if sink is None else sink.double().cpu().numpy()
+    ref = OP.step(sc, queries=qs, sink=sink_np)
+    if check_entries:
+        for b in range(len(sc.c_cu) - 1):
+            U.check_entries(sc, step, dbg, ref["produced"], b)
+    worst = 0.0
+    for t in qs:
+        if wl.indexer:
+            U.check_topk(step.idx[t].cpu().numpy(), step.score[t].cpu().numpy(), ref["topk"][t],
+                         ref["scores"][t], wl.topk)
+        err, _ = U.check_attention(U.out_np(step, t), ref["o"][t], wl.kv_fmt,
+                                   step.lse[t].double().cpu().numpy(), ref["lse"][t])
+        worst = max(worst, err)
+    # attention alone on the oracle's own selection (identical row sets)
+    if wl.indexer:
+        sel = torch.full((sc.N, wl.topk), -1, dtype=torch.int32)
+        for t in qs:
+            sel[t] = torch.from_numpy(ref["topk"][t].astype(np.int32))
+        step.attend(sc.q, sc.swa, sc.comp, sc.q_seq, sc.q_pos, sink=sink, topk_idx=sel.to(sc.q.device))
+        torch.cuda.synchronize()
+        for t in qs:
+            U.check_attention(U.out_np(step, t), ref["o"][t], wl.kv_fmt)
+    U.say(f"[ok] {wl.name} worst max-abs error {worst:.3e}")
+    return step, ref
+
+
+def test_tiny_csa_full():
+    _check_step(G.build(C.TINY_CSA, seed=0, device=_dev()))
+
+
+def test_tiny_csa_sharp_logits_and_sink():
+    sc = G.build(C.TINY_CSA, seed=1, device=_dev(), q_gain=20.0, ape=True)
+    sink = torch.tensor([0.0, 2.0, -3.0, float("-inf"), 5.0, 1.0, -1.0, 0.5], device=_dev())
+    _check_step(sc, sink=sink)
+
+
+def test_tiny_csa_compressor_chunking():
+    # the stream of 1024 tokens arrives in calls of 1, 5, 250, ... tokens
+    sc = G.build(C.TINY_CSA, seed=2, device=_dev())
+    _check_step(sc, split_at=[1, 6, 7, 256, 257, 1000])
+
+
+def test_csa_decode_small_ragged():
+    wl = C.CSA_DECODE.with_(B=6, topk=100)
+    ctx = [8192, 7001, 4000, 402, 130, 64 * 7 + 3]   # n_visible from 2048 down to 32 (< k)
+    sc = G.build(wl, seed=3, device=_dev(), ctx_per_seq=ctx)
+    _check_step(sc)
+
+
+def test_csa_decode_full():
+    sc = G.build(C.CSA_DECODE, seed=0, device=_dev())
+    _check_step(sc)
+
+
+def test_hca_decode_small():
+    wl = C.HCA_DECODE.with_(B=5)
+    sc = G.build(wl, seed=4, device=_dev(), ctx_per_seq=[131072, 65536 + 77, 5000, 127, 129])
+    _check_step(sc)
+
+
+def test_hca_decode_full_sampled():
+    sc = G.build(C.HCA_DECODE, seed=0, device=_dev())
+    _check_step(sc, queries=[0, 17, 63])
+
+
+def test_hca_ratio_one_no_window_is_causal_attention():
+    """HCA with m=1, window 0 and no top-k is full causal attention (spec invariant)."""
+    wl = C.Workload(name="hca_m1", kind="tiny", B=1, ctx=300, H=64, d=512, d_rope=64, m=1, window=0,
+                    indexer=False, in_dtype="bf16", n_query=40, q_std=0.5)
+    sc = G.build(wl, seed=5, device=_dev())
+    step, ref = _check_step(sc)
+    X = OP.decode_input(sc.c_x)
+    for t in [0, 39]:
+        p = int(sc.q_pos[t])
+        q = OP.decode_rows("bf16", sc.q[t])
+        o_full, _ = OM.attention(q, X[: p + 1], 512 ** -0.5)
+        U.check_attention(U.out_np(step, t), o_full, "bf16")
+
+
+def test_fp8_decode_small():
+    wl = C.CSA_DECODE_1M_FP8.with_(B=3, topk=256)
+    sc = G.build(wl, seed=6, device=_dev(), ctx_per_seq=[65536, 20000, 900])
+    _check_step(sc)
+
+
+def test_fp8_decode_1m_sampled():
+    sc = G.build(C.CSA_DECODE_1M_FP8, seed=0, device=_dev())
+    _check_step(sc, queries=[0, 5])
+
+
+def test_prefill_small():
+    wl = C.CSA_PREFILL.with_(P0=4096 + 2, Q=300, topk=256)
+    sc = G.build(wl, seed=7, device=_dev())
+    _check_step(sc, queries=[0, 1, 2, 3, 150, 297, 298, 299])
+
+
+def test_prefill_full_sampled():
+    sc = G.build(C.CSA_PREFILL, seed=0, device=_dev())
+    _check_step(sc, queries=[0, 1, 2047, 4095])
