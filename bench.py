@@ -1,0 +1,282 @@
+#!/usr/bin/env python
+"""Benchmark of one decode step of the hybrid compressed sparse attention path on one MI355X.
+
+A step is the whole hot path over one batch: the compressor on each sequence's new token, the
+indexer scores + top-k (CSA) and the sparse MQA attention. Inputs are seeded synthetic tensors
+already resident in HBM; the step is captured in a HIP graph over several independent input sets
+(rotated, so the 256 MB Infinity Cache cannot serve the caches), replayed, and timed with HIP
+events on the capturing stream. One JSON line goes to stdout.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload csa_decode_bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode queries/sec and achieved HBM TB/s (% roofline), CSA & HCA layer, 1 GPU"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ algorithmic bytes
+
+def algo_bytes(wl, n_vis: int) -> dict:
+    """Bytes one decode step must move per op (the whole batch), by what the method reads/writes.
+
+    attention: q, the window rows, the selected (CSA) or all visible (HCA) compressed rows, the
+      top-k ids, the output, lse, and one page-table entry per distinct page touched;
+    indexer: the keys of every visible entry, q, w, the selected ids and scores, page tables;
+    compressor: read the float32 state (3d), one token's kv and score, write the state and the
+      completed entry.
+    Score scratch and split partials are not counted: they are this implementation's choice.
+    """
+    B, H, d = wl.B, wl.H, wl.d
+    row = 584 if wl.kv_fmt == "fp8ds" else 2 * d
+    rows_comp = min(wl.topk, n_vis) if wl.indexer else n_vis
+    pt_comp = math.ceil(n_vis / 64) * 4 if not wl.indexer else min(rows_comp, math.ceil(n_vis / 64)) * 4
+    attn = B * (H * d * 2                     # q
+                + wl.window * row             # sliding window rows
+                + rows_comp * row             # compressed rows
+                + (rows_comp * 4 if wl.indexer else 0)
+                + H * d * 2 + H * 4           # out, lse
+                + 3 * 4 + pt_comp)            # page-table entries
+    ix = 0
+    if wl.indexer:
+        krow = (wl.d_I // 2 + wl.d_I // 32) if wl.ix_fmt == "mxfp4" else 2 * wl.d_I
+        qb = wl.H_I * krow
+        ix = B * (n_vis * krow + qb + wl.H_I * 4 + wl.topk * 8 + math.ceil(n_vis / 64) * 4)
+    in_b = 4 if wl.in_dtype == "f32" else 2
+    comp = B * (2 * 3 * d * 4 + 2 * d * in_b + row)
+    return {"attention": attn, "index_topk": ix, "compress": comp, "step": attn + ix + comp}
+
+
+# ------------------------------------------------------------------ GPU step
+
+class Bench:
+    def __init__(self, wl, sets: int, seed: int):
+        import torch
+
+        from hybrid_compressed_sparse_amd.step import PathStep, StepShape
+        from synth import gen as G
+        import hybrid_compressed_sparse_amd as hcs
+
+        self.torch, self.hcs = torch, hcs
+        self.wl = wl
+        dev = torch.device("cuda:0")
+        self.sets = []
+        for s in range(sets):
+            sc = G.build(wl, seed=seed + s, device=dev)
+            B, d, m = wl.B, wl.d, wl.m
+            state = torch.zeros((B, 3 * d), dtype=torch.float32, device=dev)
+            # setup: the block's tokens before the step's own one
+            lens = [sc.c_cu[b + 1] - sc.c_cu[b] for b in range(B)]
+            pre = torch.cat([torch.arange(sc.c_cu[b], sc.c_cu[b + 1] - 1, device=dev) for b in range(B)])
+            last = torch.tensor([sc.c_cu[b + 1] - 1 for b in range(B)], device=dev)
+            if pre.numel():
+                cu_h = [0]
+                for n in lens:
+                    cu_h.append(cu_h[-1] + n - 1)
+                cu = torch.tensor(cu_h, dtype=torch.int32, device=dev)
+                hcs.compress_kv(sc.c_x.index_select(0, pre).contiguous(),
+                                sc.c_s.index_select(0, pre).contiguous(), cu, sc.c_start, state,
+                                sc.comp, m, max_new=max(lens))
+            step_in = dict(
+                c_kv=sc.c_x.index_select(0, last).contiguous(),
+                c_score=sc.c_s.index_select(0, last).contiguous(),
+                c_cu=torch.arange(B + 1, dtype=torch.int32, device=dev),
+                c_start=(sc.c_start + torch.tensor(lens, dtype=torch.int32, device=dev) - 1).contiguous(),
+                c_state=state, c_max_new=1)
+            if wl.indexer:
+                if isinstance(sc.ix_q, torch.Tensor):
+                    step_in.update(ix_q=sc.ix_q.contiguous(), ix_q_scale=None)
+                else:
+                    step_in.update(ix_q=sc.ix_q.codes.contiguous(), ix_q_scale=sc.ix_q.scales.contiguous())
+                step_in.update(ix_w=sc.ix_w.contiguous(), ix_keys=sc.ix)
+            step_in.update(q=sc.q, swa=sc.swa, comp=sc.comp, q_seq=sc.q_seq, q_pos=sc.q_pos)
+            self.sets.append((sc, step_in))
+            # the logical copies are only needed by the oracle
+            sc.comp.rows = sc.swa.rows = None
+            if sc.ix is not None:
+                sc.ix.rows = None
+        sc0 = self.sets[0][0]
+        self.step = PathStep(StepShape(N=sc0.N, H=wl.H, d=wl.d, m=wl.m, window=wl.window,
+                                       max_pos=sc0.max_pos(), topk=wl.topk if wl.indexer else 0),
+                             device=dev)
+        torch.cuda.synchronize()
+
+    def run_op(self, op: str, i: int):
+        sc, a = self.sets[i]
+        st = self.step
+        if op == "step":
+            st.run(**a)
+        elif op == "compress":
+            st.compress(a["c_kv"], a["c_score"], a["c_cu"], a["c_start"], a["c_state"], a["comp"],
+                        a["c_max_new"])
+        elif op == "index_topk":
+            st.select(a["ix_q"], a["ix_q_scale"], a["ix_w"], a["ix_keys"], a["q_seq"], a["q_pos"])
+        elif op == "attention":
+            st.attend(a["q"], a["swa"], a["comp"], a["q_seq"], a["q_pos"])
+
+    def graph(self, op: str):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(2):
+                for i in range(len(self.sets)):
+                    self.run_op(op, i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(len(self.sets)):
+                self.run_op(op, i)
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(self, g, reps: int, warm: int) -> float:
+        """Average ms per replay of g over `reps` replays (HIP events on the replay stream)."""
+        torch = self.torch
+        for _ in range(warm):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+
+def cpu_baseline(wl, seconds: float) -> dict:
+    from threadpoolctl import threadpool_info
+
+    from oracle import pipeline as OP
+    from synth import gen as G
+
+    sc = G.build(wl, seed=0, device="cpu")
+    OP.step(sc, queries=[0])                      # warm the caches of the decoders
+    t0 = time.perf_counter()
+    done = 0
+    # cycle over the batch's queries until the time budget is spent (at least one pass)
+    while done < sc.N or time.perf_counter() - t0 < seconds:
+        OP.step(sc, queries=[done % sc.N])
+        done += 1
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": done / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} query steps cycling over the {sc.N} queries of {wl.name} (per query: "
+                      f"compressor of the batch's streams, indexer + top-k, attention), float64 NumPy, "
+                      f"{dt:.1f} s"}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="csa_decode_bf16")
+    ap.add_argument("--sets", type=int, default=8, help="independent input sets rotated per replay")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the HCA side measurement")
+    ap.add_argument("--only", default=None, help="replay only this op's graph (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the decode path of one "
+                                   "layer needs no collectives; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    from synth import configs as C
+
+    wl = C.BY_NAME[args.workload]
+    if wl.kind != "decode":
+        sys.exit("bench workloads are the decode configurations")
+    n_vis = wl.ctx // wl.m
+    R = args.sets
+    reps = max(1, math.ceil(args.steps / R))
+    warm = max(1, math.ceil(args.warmup / R))
+    log(f"[bench] {wl.name}: building {R} input sets")
+    bench = Bench(wl, R, seed=1000)
+
+    if args.only:
+        g = bench.graph(args.only)
+        ms = bench.time_graph(g, reps, warm) / R
+        log(f"[bench] {args.only}: {ms * 1e3:.2f} us per launch")
+        print(json.dumps({"op": args.only, "us_per_launch": ms * 1e3}))
+        return
+
+    log("[bench] capturing the step graph")
+    g_step = bench.graph("step")
+    ms_step = bench.time_graph(g_step, reps, warm) / R
+    ops = ["compress", "attention"] + (["index_topk"] if wl.indexer else [])
+    op_ms = {}
+    for op in ops:
+        op_ms[op] = bench.time_graph(bench.graph(op), reps, warm) / R
+        log(f"[bench] {op}: {op_ms[op] * 1e3:.2f} us")
+    by = algo_bytes(wl, n_vis)
+    qps = wl.B / (ms_step * 1e-3)
+    step_gbs = by["step"] / (ms_step * 1e-3) / 1e9
+    dom = max(op_ms, key=op_ms.get)
+    dom_gbs = by[dom] / (op_ms[dom] * 1e-3) / 1e9
+    log(f"[bench] step {ms_step * 1e3:.2f} us, {qps:,.0f} q/s, {step_gbs:.0f} GB/s "
+        f"({100 * step_gbs / HBM_PEAK_GBS:.1f}% of HBM)")
+
+    result = {
+        "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1,
+        "steps": reps * R, "warmup": warm * R, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "context": wl.ctx, "heads": wl.H,
+                   "head_dim": wl.d, "compress_ratio": wl.m, "window": wl.window,
+                   "topk": wl.topk if wl.indexer else None,
+                   "indexer": f"{wl.H_I}x{wl.d_I} {wl.ix_fmt}" if wl.indexer else None,
+                   "kv_format": wl.kv_fmt, "input_sets_rotated": R},
+        "hbm_tb_s": step_gbs / 1e3, "hbm_frac": step_gbs / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": by["step"],
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": dom_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": by[dom], "us_per_launch": op_ms[dom] * 1e3},
+        "ops_us": {k: v * 1e3 for k, v in op_ms.items()},
+    }
+    del bench, g_step
+    torch.cuda.empty_cache()
+
+    if not args.no_extra and wl.name == "csa_decode_bf16":
+        hw = C.HCA_DECODE
+        log(f"[bench] side measurement: {hw.name}")
+        hb = Bench(hw, R, seed=2000)
+        hms = hb.time_graph(hb.graph("step"), reps, warm) / R
+        hby = algo_bytes(hw, hw.ctx // hw.m)
+        result["hca_decode_bf16"] = {"queries_per_s": hw.B / (hms * 1e-3), "ms_per_step": hms,
+                                     "hbm_frac": hby["step"] / (hms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                     "algorithmic_bytes_per_step": hby["step"]}
+        del hb
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -184,11 +184,15 @@ static hcs_status run_attn(hcs::AttnArgs& a, int d, int fmt, int window, int m, 
   if (plan.ws_bytes && (!ws || ws_bytes < plan.ws_bytes))
     return fail(HCS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.ws_bytes, ws_bytes);
   if (plan.ws_bytes && !aligned(ws, 256)) return fail(HCS_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+  a.kind = plan.kind;
   a.nsplit = plan.nsplit;
-  a.tiles_per_split = plan.tiles_per_split;
+  a.n_hg = plan.n_hg;
+  a.rows_per_split = plan.rows_per_split;
   if (plan.nsplit > 1) {
-    a.ws_o = static_cast<float*>(ws);
-    a.ws_ml = a.ws_o + (size_t)a.N * plan.nsplit * a.H * d;
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    a.ws_cnt = reinterpret_cast<int*>(w);
+    a.ws_o = reinterpret_cast<float*>(w + plan.ws_cnt_bytes);
+    a.ws_ml = reinterpret_cast<float*>(w + plan.ws_cnt_bytes + plan.ws_o_bytes);
   }
   return hip_status(hcs::launch_sparse_mla(a, d, fmt, static_cast<hipStream_t>(stream)), "sparse_mla");
 }

@@ -46,7 +46,8 @@ class PathStep:
             at_ws = sparse_mla_prefill_workspace_size(s.N, s.H, s.d, s.window, s.m, s.topk, s.P0)
         else:
             at_ws = sparse_mla_workspace_size(s.N, s.H, s.d, s.window, s.m, s.topk, s.max_pos)
-        self.at_ws = torch.empty(max(at_ws, 1), dtype=torch.uint8, device=device)
+        # zero-filled once: the split counters in it must start at zero (calls leave them zero)
+        self.at_ws = torch.zeros(max(at_ws, 1), dtype=torch.uint8, device=device)
 
     def compress(self, kv, score, cu_new, start_pos, state, comp, max_new, ape=None, dbg=None):
         compress_kv(kv, score, cu_new, start_pos, state, comp, self.shape.m, ape=ape, dbg=dbg,
