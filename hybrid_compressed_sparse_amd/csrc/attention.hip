@@ -126,11 +126,18 @@ __device__ __forceinline__ void fill_rowtab(const AttnArgs& a, int t, const Quer
 }
 
 // ---------------------------------------------------------------- row staging
-// LDS tile: 32 rows of D bf16 (no padding); 16-byte chunk c of row r sits at chunk c ^ swz(r).
-// With this swizzle both readers are free of bank conflicts: the K-operand read (8 rows, same
-// chunk) and the transposed V read (4 consecutive rows x 2 chunks per 16 lanes) touch 8 distinct
-// 16-byte bank groups.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// LDS tiles hold rows of D bf16 without padding; the 16-byte chunk c of row r sits at chunk
+// c ^ swz(r), a 4-bit XOR that depends on r mod 16. gfx950's LDS serves a 128-bit read for 16
+// lanes (256 bytes) per cycle, so a reader is free of bank conflicts when the 16-byte chunks its
+// 16 lanes touch fall on 16 distinct chunk positions mod 16 (and on 8 distinct positions mod 8
+// for a 32-bank view). Each kernel reads its tile in its own pattern, hence two swizzles:
+//   decode: K reads rows 16w + l (l = 0..15, one chunk); V^T reads rows 8g + j (+4), chunks
+//           2c, 2c+1 for two groups g at a time. swz_dec gives distinct positions in both views.
+//   prefill: K reads rows l = 0..15; V^T reads rows 4g + j (+16) for g pairs (0,1)/(2,3).
+__device__ __forceinline__ int swz_dec(int r) {
+  return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
+}
+__device__ __forceinline__ int swz_pre(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 // Each variant loads one 32-row tile's worth of 16-byte pieces per lane into registers and
 // later writes them (dequantised to bf16 for fp8_ds) into the LDS tile.
@@ -181,10 +188,9 @@ struct Stage {
   }
 
   // Write this lane's piece of row `r` (tile-local) into the LDS tile.
-  __device__ static __forceinline__ void store(uint8_t* tile, int r, int lane, const i32x4& v,
-                                               float sc) {
+  __device__ static __forceinline__ void store(uint8_t* tile, int r, int sw, int lane,
+                                               const i32x4& v, float sc) {
     const int chunk = lane_chunk(lane);
-    const int sw = swz(r);
     uint8_t* row = tile + r * RS;
     if constexpr (FMT == HCS_FMT_FP8DS) {
       if (chunk < 28) {
@@ -228,14 +234,15 @@ __device__ __forceinline__ void tile_math(const uint8_t* L, uint32_t valid, cons
   constexpr int KS = D / 32, CT = D / 16, RS = D * 2;
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
   // K operand: row mt*16 + l16, chunk (4ks + g) ^ s = 4 (ks ^ (s >> 2)) + ((g ^ s) & 3)
-  const int sk = swz(l16);
+  const int sk = swz_pre(l16);
   const int koff = l16 * RS + ((g ^ sk) & 3) * 16;
-  const int k_even = koff + ((sk >> 2) ? 64 : 0);
-  const int k_odd = koff + ((sk >> 2) ? 0 : 64);
+  int ko4[4];
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) ko4[k4] = koff + 64 * (k4 ^ (sk >> 2));
   f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const int ko = ((ks & 1) ? k_odd : k_even) + (ks >> 1) * 128;
+    const int ko = ko4[ks & 3] + (ks >> 2) * 256;
     bf16x8 qb;
     if constexpr (QLDS) qb = *(const bf16x8*)(qL + ko);
     else qb = qreg[ks];
@@ -283,14 +290,14 @@ __device__ __forceinline__ void tile_math(const uint8_t* L, uint32_t valid, cons
   // V^T: group g reads rows ra = 4g + (l16 >> 2) and ra + 16, 8 bytes at column 16 ct + 4 (l16 & 3)
   //   byte 32 ct + 8 q -> chunk (2 ct + (q >> 1)) ^ s = 2 (ct ^ (s >> 1)) + (((q >> 1) ^ s) & 1)
   const int ra = 4 * g + (l16 >> 2), q4 = l16 & 3;
-  const int sv = swz(ra);
+  const int sv = swz_pre(ra);                      // rows ra and ra + 16 share it
   const uint8_t* vb = L + ra * RS + ((((q4 >> 1) ^ sv) & 1) * 16) + (q4 & 1) * 8;
-  const uint8_t* vo[4];
+  const uint8_t* vo[8];
 #pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) vo[c4] = vb + 32 * (c4 ^ (sv >> 1));
+  for (int c8 = 0; c8 < 8; ++c8) vo[c8] = vb + 32 * (c8 ^ (sv >> 1));
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    const uint8_t* va = vo[ct & 3] + (ct >> 2) * 128;
+    const uint8_t* va = vo[ct & 7] + (ct >> 3) * 256;
     const i16x4 v0 = lds_read_tr16(va);
     const i16x4 v1 = lds_read_tr16(va + 16 * RS);
     const i16x8 v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -366,13 +373,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
   constexpr int NLD = WR / RPI;
   __shared__ __attribute__((aligned(16))) uint8_t tile0[BT * RS];
   __shared__ __attribute__((aligned(16))) uint8_t tile1[BT * RS];
-  __shared__ __attribute__((aligned(16))) uint32_t rowtab[kMaxRowsWG];
+  // ASYNC: byte address of every row (the zero row where a row does not take part);
+  // otherwise the packed (cache, page, slot) entries
+  __shared__ __attribute__((aligned(16))) uint32_t rowtab[ASYNC ? 2 * kMaxRowsWG : kMaxRowsWG];
   __shared__ __attribute__((aligned(16))) __bf16 p_lds0[16 * PR];
   __shared__ __attribute__((aligned(16))) __bf16 p_lds1[16 * PR];
   __shared__ float mx[4][16];
   __shared__ float lsum[4][16];
   __shared__ int flag0[4], flag1[4];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -388,6 +396,28 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
   const int r0 = s * a.rows_per_split;
   const int n_rows = max(0, min(q.R, r0 + a.rows_per_split) - r0);
   fill_rowtab(a, t, q, r0, n_rows, rowtab, BT);
+  if constexpr (ASYNC) {
+    // entries -> addresses, in place from the top so no entry is overwritten before it is read
+    __syncthreads();
+    const int n64 = (n_rows + BT - 1) / BT * BT;
+    uint32_t ent[kRowsPerThread];
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const int li = (int)threadIdx.x + i * kThreads;
+      ent[i] = li < n64 ? rowtab[li] : kNoRow;
+    }
+    __syncthreads();
+    uint64_t* addr = reinterpret_cast<uint64_t*>(rowtab);
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const int li = (int)threadIdx.x + i * kThreads;
+      const uint32_t e = ent[i];
+      const uint8_t* p = e != kNoRow
+                             ? ((e >> 31) ? a.comp.base : a.swa.base) + (size_t)(e & 0x7fffffffu) * RS
+                             : g_zero_row;
+      if (li < n64) addr[li] = reinterpret_cast<uint64_t>(p);
+    }
+  }
   // q of the 16 heads as the B operand (same for the 4 waves)
   bf16x8 qreg[KS];
   load_q<D>(a, t, hg * 16 + l16, qreg);
@@ -403,23 +433,37 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
   __syncthreads();
 
   // gather this wave's rows of block b into buffer tbuf
+  // per-lane source offsets of the async row loads (the swizzle is applied on the source side:
+  // LDS chunk slot `lane` of row r receives source chunk lane ^ swz(r))
+  int soff[ASYNC ? NLD : 1];
+  if constexpr (ASYNC) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int rw = i * RPI + lane / (64 / RPI);
+      soff[i] = ((lane % (64 / RPI)) ^ swz_dec(rw)) * 16;         // rows 16w + rw share swz_dec(rw)
+    }
+  }
   auto issue = [&](int b, uint8_t* tbuf) {
-    const uint32_t* rt = rowtab + b * BT + wave * WR;
     if constexpr (ASYNC) {
+      const uint64_t* at = reinterpret_cast<const uint64_t*>(rowtab) + b * BT + wave * WR;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const int rw = i * RPI + lane / (64 / RPI);           // row of this lane within the wave's rows
-        const int rl = wave * WR + rw;                          // row within the block
-        const uint32_t e = rt[rw];
-        const int chunk = (lane % (64 / RPI)) ^ swz(rl);        // source chunk landing at this lane's slot
-        const uint8_t* src = e != kNoRow
-                                 ? ((e >> 31) ? a.comp.base : a.swa.base) + (size_t)(e & 0x7fffffffu) * RS
-                                 : g_zero_row;
+        const int rw = i * RPI + lane / (64 / RPI);             // row of this lane within the wave's rows
+        uint64_t src;
+        if constexpr (RPI == 1) {
+          // both halves zero-extended (readfirstlane returns a signed int)
+          const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)at[i]);
+          const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(at[i] >> 32));
+          src = (uint64_t)lo | ((uint64_t)hi << 32);
+        } else {
+          src = at[rw];
+        }
         uint8_t* dst = tbuf + (wave * WR + i * RPI) * RS;       // 1 KiB of consecutive rows
-        __builtin_amdgcn_global_load_lds((const void*)(src + chunk * 16),
+        __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const uint8_t*>(src) + soff[i]),
                                          (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
       }
     } else {
+      const uint32_t* rt = rowtab + b * BT + wave * WR;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) S::load(a, rt[i], lane, pre[i], psc[i]);
     }
@@ -427,16 +471,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
   if (nblk > 0) issue(0, tile0);
 
   // lane-constant LDS offsets
-  const int sk = swz(l16);
-  const int koff = (wave * WR + l16) * RS + ((g ^ sk) & 3) * 16;   // K row 16 w + l16
-  const int k_even = (sk >> 2) ? 64 : 0, k_odd = (sk >> 2) ? 0 : 64;
-  const int jv = l16 >> 2, q4 = l16 & 3, h2 = q4 >> 1;
-  const int vrow = (8 * g + jv) * RS + (q4 & 1) * 8;
-  int vo0[4], vo1[4];
+  // K row 16w + l16, chunk (4ks + g) ^ s = 4 (ks ^ (s >> 2)) + ((g ^ s) & 3), s = swz_dec(l16)
+  const int sk = swz_dec(l16);
+  const int koff = (wave * WR + l16) * RS + ((g ^ sk) & 3) * 16;
+  int ko4[4];
 #pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    vo0[c4] = vrow + 32 * (c4 ^ jv) + 16 * h2;
-    vo1[c4] = vrow + 4 * RS + 32 * (c4 ^ jv) + 16 * (h2 ^ 1);
+  for (int k4 = 0; k4 < 4; ++k4) ko4[k4] = koff + 64 * (k4 ^ (sk >> 2));
+  // V^T rows 8g + jv and 8g + 4 + jv of a 32-row step: swz_dec = 2 jv + 8 (g & 1) (+1), so
+  // chunk (2 ctg + h) lands at 2 (ctg ^ (jv + 4 (g & 1))) + (h, resp. h ^ 1)
+  const int jv = l16 >> 2, q4 = l16 & 3, h2 = q4 >> 1;
+  const int vx = jv + 4 * (g & 1);
+  const int vrow = (8 * g + jv) * RS + (q4 & 1) * 8;
+  int vo0[8], vo1[8];
+#pragma unroll
+  for (int c8 = 0; c8 < 8; ++c8) {
+    vo0[c8] = vrow + 32 * (c8 ^ vx) + 16 * h2;
+    vo1[c8] = vrow + 4 * RS + 32 * (c8 ^ vx) + 16 * (h2 ^ 1);
   }
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -449,20 +499,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
   auto block = [&](int b, uint8_t* T, uint8_t* TN, __bf16* P, int* F) {
     if constexpr (!ASYNC) {
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) S::store(T, wave * WR + i, lane, pre[i], psc[i]);
+      for (int i = 0; i < NLD; ++i) S::store(T, wave * WR + i, swz_dec(i), lane, pre[i], psc[i]);
     } else {
       wait_vm_zero();                                    // this wave's rows of block b landed
     }
     lds_barrier();                                       // block b is in LDS
     if (b + 1 < nblk) issue(b + 1, TN);
-    const bool vr = rowtab[b * BT + wave * WR + (lane & 15)] != kNoRow;
+    bool vr;
+    if constexpr (ASYNC)
+      vr = reinterpret_cast<const uint64_t*>(rowtab)[b * BT + wave * WR + (lane & 15)] !=
+           reinterpret_cast<uint64_t>(g_zero_row);
+    else
+      vr = rowtab[b * BT + wave * WR + (lane & 15)] != kNoRow;
     const uint32_t valid = (uint32_t)__ballot(vr && lane < 16);
     // ---- S^T for this wave's 16 rows (two accumulators halve the dependent chain)
     f32x4 sacc2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int ko = ((ks & 1) ? k_odd : k_even) + (ks >> 1) * 128;
-      const bf16x8 av = *(const bf16x8*)(T + koff + ko);
+      const int ko = ko4[ks & 3] + (ks >> 2) * 256;
+      const bf16x8 av = *(const bf16x8*)(T + ko);
       sacc2[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[ks], sacc2[ks & 1], 0, 0, 0);
     }
     const f32x4 sacc = sacc2[0] + sacc2[1];
@@ -521,9 +576,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
 #pragma unroll
       for (int ct = 0; ct < CTW; ++ct) {
         const int ctg = wave * CTW + ct;
-        const int hi = (ctg >> 2) * 128;
-        const i16x4 v0 = lds_read_tr16(vb + vo0[ctg & 3] + hi);
-        const i16x4 v1 = lds_read_tr16(vb + vo1[ctg & 3] + hi);
+        const int hi = (ctg >> 3) * 256;
+        const i16x4 v0 = lds_read_tr16(vb + vo0[ctg & 7] + hi);
+        const i16x4 v1 = lds_read_tr16(vb + vo1[ctg & 7] + hi);
         const i16x8 v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pb, oacc[ct],
                                                            0, 0, 0);
@@ -562,51 +617,44 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
     return;
   }
 
-  // ---- split: write the partial, the last block of (query, head group) merges them
-  const int64_t pbase = ((int64_t)(t * a.n_hg + hg) * a.nsplit) * 16;   // partial rows of split 0
-  {
-    float* po = a.ws_o + (pbase + (int64_t)s * 16 + l16) * D;
+  // ---- split: write this split's partial (unnormalised O, reference max, sum); a second
+  // kernel merges the splits (a kernel boundary orders the writes before the reads on every
+  // XCD, which in-kernel device-scope fences would do at a far higher cost)
+  const int64_t prow = ((int64_t)(t * a.n_hg + hg) * a.nsplit + s) * 16 + l16;
+  float* po = a.ws_o + prow * D;
 #pragma unroll
-    for (int ct = 0; ct < CTW; ++ct) *(f32x4*)(po + 16 * (wave * CTW + ct) + 4 * g) = oacc[ct];
-    if (g == 0 && wave == 0) {
-      a.ws_ml[(pbase + (int64_t)s * 16 + l16) * 2 + 0] = M;
-      a.ws_ml[(pbase + (int64_t)s * 16 + l16) * 2 + 1] = L;
-    }
+  for (int ct = 0; ct < CTW; ++ct) *(f32x4*)(po + 16 * (wave * CTW + ct) + 4 * g) = oacc[ct];
+  if (g == 0 && wave == 0) {
+    a.ws_ml[prow * 2 + 0] = M;
+    a.ws_ml[prow * 2 + 1] = L;
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    int* cnt = a.ws_cnt + t * a.n_hg + hg;
-    const int prev = atomicAdd(cnt, 1);
-    s_last = prev == a.nsplit - 1;
-    if (s_last) *cnt = 0;               // every block of this call has arrived: reset for the next
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // thread -> head h = tid / 16, columns (tid % 16) * (D / 16) ..
+}
+
+// Merge the split partials of one (query, 16-head group): thread -> head tid / 16, D/16 columns.
+template <int D>
+__global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
   constexpr int PER = D / 16;
+  const int t = blockIdx.x, hg = blockIdx.y, tid = threadIdx.x;
   const int h = tid >> 4, c0 = (tid & 15) * PER;
   const int hq = hg * 16 + h;
+  const int64_t pbase = ((int64_t)(t * a.n_hg + hg) * a.nsplit) * 16 + h;   // row of split 0
   float Ms = kNegInf;
-  for (int ss = 0; ss < a.nsplit; ++ss)
-    Ms = fmaxf(Ms, __builtin_nontemporal_load(a.ws_ml + (pbase + (int64_t)ss * 16 + h) * 2));
+  for (int ss = 0; ss < a.nsplit; ++ss) Ms = fmaxf(Ms, a.ws_ml[(pbase + (int64_t)ss * 16) * 2]);
   float acc[PER];
 #pragma unroll
   for (int c = 0; c < PER; ++c) acc[c] = 0.f;
   float Ls = 0.f;
   if (Ms != kNegInf) {
     for (int ss = 0; ss < a.nsplit; ++ss) {
-      const int64_t pr = pbase + (int64_t)ss * 16 + h;
-      const float ms = __builtin_nontemporal_load(a.ws_ml + pr * 2);
-      const float ls = __builtin_nontemporal_load(a.ws_ml + pr * 2 + 1);
+      const int64_t pr = pbase + (int64_t)ss * 16;
+      const float ms = a.ws_ml[pr * 2], ls = a.ws_ml[pr * 2 + 1];
       if (!(ls > 0.f)) continue;
       const float f = __builtin_amdgcn_exp2f(ms - Ms);
       Ls += ls * f;
       const float* src = a.ws_o + pr * D + c0;
 #pragma unroll
       for (int c = 0; c < PER; c += 4) {
-        const f32x4 v = __builtin_nontemporal_load((const f32x4*)(src + c));
+        const f32x4 v = *(const f32x4*)(src + c);
         acc[c] += f * v[0];
         acc[c + 1] += f * v[1];
         acc[c + 2] += f * v[2];
@@ -667,7 +715,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_prefill_kernel(AttnArgs a) {
   auto store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NLDW; ++i)
-      S::store(lds_tile[buf], wave * WROWS + i * S::RPL + S::lane_row(lane), lane, pre[i], psc[i]);
+      S::store(lds_tile[buf], wave * WROWS + i * S::RPL + S::lane_row(lane),
+               swz_pre(wave * WROWS + i * S::RPL + S::lane_row(lane)), lane, pre[i], psc[i]);
   };
   if (ntiles > 0) {
     issue(0);
@@ -713,6 +762,8 @@ hipError_t launch_impl(const AttnArgs& a, hipStream_t stream) {
     const int n8 = (a.N + 7) / 8;
     dim3 grid((unsigned)(n8 * 8 * a.nsplit * a.n_hg));
     hipLaunchKernelGGL((mla_decode_kernel<D, FMT>), grid, dim3(kThreads), 0, stream, a);
+    if (a.nsplit > 1)
+      hipLaunchKernelGGL((mla_combine_kernel<D>), dim3(a.N, a.n_hg), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -750,8 +801,7 @@ AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos
     const size_t parts = (size_t)N * p.n_hg * nsplit * 16;
     p.ws_o_bytes = parts * d * sizeof(float);
     p.ws_ml_bytes = parts * 2 * sizeof(float);
-    p.ws_cnt_bytes = ((size_t)N * p.n_hg * sizeof(int) + 255) / 256 * 256;
-    p.ws_bytes = p.ws_cnt_bytes + p.ws_o_bytes + p.ws_ml_bytes;
+    p.ws_bytes = p.ws_o_bytes + p.ws_ml_bytes;
   }
   return p;
 }

@@ -21,14 +21,13 @@ struct AttnArgs {
   float scale_log2;           // softmax scale * log2(e)
   uint16_t* out;              // [N, H, D] bf16
   float* lse;                 // [N, H] or nullptr
-  int* ws_cnt;                // [N, n_hg] arrival counters (zero between calls)
   float* ws_o;                // [N, n_hg, nsplit, 16, D] partial outputs (nsplit > 1)
   float* ws_ml;               // [N, n_hg, nsplit, 16, 2] partial (max, sum), log2 units
 };
 
 struct AttnPlan {
   int kind, nsplit, n_hg, rows_per_split;
-  size_t ws_cnt_bytes, ws_o_bytes, ws_ml_bytes, ws_bytes;
+  size_t ws_o_bytes, ws_ml_bytes, ws_bytes;
 };
 AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos);
 hipError_t launch_sparse_mla(const AttnArgs& a, int d, int fmt, hipStream_t stream);

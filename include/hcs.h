@@ -165,9 +165,8 @@ hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w,
 /* max_pos  host: an upper bound of q_pos.     scale: softmax scale (d^-1/2 on the pages). */
 /* out      [N, H, d] bf16.     lse  [N, H] float32 (natural log) or NULL.                */
 /* ws       workspace of hcs_sparse_mla_workspace_size(N, H, d, window, m, topk, max_pos)  */
-/*          bytes (topk = 0 for HCA; 0 bytes means none is needed). It must be zero-filled */
-/*          before its first use: it holds arrival counters of the split row ranges, which */
-/*          every call leaves at zero again. Calls that overlap in time must not share it. */
+/*          bytes (topk = 0 for HCA; 0 bytes means none is needed): partial results of the */
+/*          split row ranges. Calls that overlap in time must not share it.               */
 /* Constraints: d in {128, 512}, 1 <= H <= 128, window >= 0, m >= 1.                      */
 size_t hcs_sparse_mla_workspace_size(int N, int H, int d, int window, int m, int topk, int max_pos);
 hcs_status hcs_sparse_mla_decode(const void* q, hcs_paged swa, hcs_paged comp,
