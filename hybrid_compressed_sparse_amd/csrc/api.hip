@@ -169,7 +169,9 @@ static hcs_status check_attn(const void* q, const hcs_paged& swa, const hcs_page
 
 size_t hcs_sparse_mla_workspace_size(int N, int H, int d, int window, int m, int topk, int max_pos) {
   if (N <= 0 || H <= 0 || m < 1 || max_pos < 0 || window < 0) return 0;
-  return hcs::attn_plan(N, H, d, window, m, topk, max_pos).ws_bytes;
+  // the plan depends on the cache format, which is not an argument here: cover both
+  return std::max(hcs::attn_plan(N, H, d, window, m, topk, max_pos, HCS_FMT_BF16).ws_bytes,
+                  hcs::attn_plan(N, H, d, window, m, topk, max_pos, HCS_FMT_FP8DS).ws_bytes);
 }
 
 static hcs_status run_attn(hcs::AttnArgs& a, int d, int fmt, int window, int m, int topk,
@@ -180,13 +182,14 @@ static hcs_status run_attn(hcs::AttnArgs& a, int d, int fmt, int window, int m, 
   if ((int64_t)a.comp.pt_stride * HCS_PAGE_ROWS < (int64_t)(max_pos + 1) / m)
     return fail(HCS_ERR_INVALID_ARG, "comp: pt_stride %d does not cover %d entries", a.comp.pt_stride,
                 (max_pos + 1) / m);
-  const hcs::AttnPlan plan = hcs::attn_plan(a.N, a.H, d, window, m, topk, max_pos);
+  const hcs::AttnPlan plan = hcs::attn_plan(a.N, a.H, d, window, m, topk, max_pos, fmt);
   if (plan.ws_bytes && (!ws || ws_bytes < plan.ws_bytes))
     return fail(HCS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.ws_bytes, ws_bytes);
   if (plan.ws_bytes && !aligned(ws, 256)) return fail(HCS_ERR_INVALID_ARG, "ws must be 256-byte aligned");
   a.kind = plan.kind;
   a.nsplit = plan.nsplit;
   a.n_hg = plan.n_hg;
+  a.n_h16 = plan.n_h16;
   a.rows_per_split = plan.rows_per_split;
   if (plan.nsplit > 1) {
     uint8_t* w = static_cast<uint8_t*>(ws);

@@ -8,26 +8,22 @@
 //   * a workgroup first resolves the physical row of every logical row it will read (window
 //     position or compressed id -> page table -> page, slot) into an LDS table, with all
 //     loads issued together and no branches, so each later row load is a single independent
-//     16-byte gather; rows that do not take part read a zero row;
-//   * the math on a 32-row tile for 16 heads, per wave: S^T = K Q^T with
-//     v_mfma_f32_16x16x32_bf16 (rows on M, heads on N, q in registers as the B operand), whose
-//     accumulator layout is already the B-operand layout of P^T, then O^T += V^T P^T with V^T
-//     read from the same LDS rows by ds_read_b64_tr_b16 (16-bit transpose across each 16-lane
-//     group); online softmax in base 2 with one head per lane (lane % 16);
-//   * fp8_ds rows are dequantised on their way into LDS (e4m3 * 2^(scale-127) is exact in bf16).
+//     gather; rows that do not take part read a zero row;
+//   * rows are walked in 64-row blocks through a double-buffered LDS ring, swizzled so that
+//     both readers below are free of bank conflicts;
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (rows on M, 16 heads on N, q in registers as
+//     the B operand), whose accumulator layout is the one P^T is written in, then
+//     O^T += V^T P^T with V^T read from the same LDS rows by ds_read_b64_tr_b16 (16-bit
+//     transpose across each 16-lane group); online softmax in base 2, one head per lane % 16;
+//   * a query's rows may be split over several workgroups; their partial (O, max, sum) are
+//     merged by a second kernel.
 //
-// Decode kernel (few queries): a workgroup is (query, split of its rows, 16 heads). Each of
-// its 4 waves walks its own 32-row sub-tiles (wave w takes sub-tiles w, w+4, ...) with a
-// private LDS buffer and a one-sub-tile register prefetch, so waves never wait for each other
-// inside the loop and a CU keeps 4 x 32 KiB of gathers in flight. The waves' softmax states
-// merge through LDS at the end. The 4 head groups of a query run on the same XCD (blocks are
-// dispatched round-robin over the 8 XCDs, and the block index is mapped so that all blocks of
-// a query share one), so a row fetched from HBM by one of them is an L2 hit for the others,
-// and split partials are merged by the last block to finish, through that XCD's L2.
-//
-// Prefill kernel (many queries): a workgroup is one query and 64 heads; wave w owns heads
-// 16w..16w+15 and all 4 waves share each 32-row tile, staged cooperatively into a
-// double-buffered LDS ring, so each gathered row is read from L2/HBM once for all heads.
+// All-heads kernel (bf16 rows): a workgroup is (query, split, 64 heads), so each gathered row is
+// read once for all heads of the query; bf16 rows go straight from the paged cache into LDS with
+// global_load_lds.
+// 16-head kernel (fp8_ds rows): a workgroup is (query, split, 16 heads); rows are dequantised
+// through registers on their way into LDS (e4m3 * 2^(scale-127) is exact in bf16). The head
+// groups of a query run on one XCD, so a row fetched by one of them is an L2 hit for the others.
 #include "kernels.h"
 
 namespace hcs {
@@ -37,7 +33,6 @@ __device__ __attribute__((aligned(64))) uint8_t g_zero_row[1024];
 
 namespace {
 
-constexpr int kTile = 32;
 constexpr int kThreads = 256;
 constexpr int kMaxRowsWG = 2304;            // rows in one workgroup's address table
 constexpr uint32_t kNoRow = 0xFFFFFFFFu;
@@ -90,7 +85,7 @@ __device__ __forceinline__ QueryRows query_rows(const AttnArgs& a, int t) {
 constexpr int kRowsPerThread = (kMaxRowsWG + kThreads - 1) / kThreads;
 
 __device__ __forceinline__ void fill_rowtab(const AttnArgs& a, int t, const QueryRows& q, int r0,
-                                            int n, uint32_t* rowtab, int pad = kTile) {
+                                            int n, uint32_t* rowtab, int pad) {
   int id[kRowsPerThread];
   const int last = max(q.R - 1, 0);
 #pragma unroll
@@ -125,6 +120,62 @@ __device__ __forceinline__ void fill_rowtab(const AttnArgs& a, int t, const Quer
   }
 }
 
+// Entries of a sequence's compressed page table that the all-heads kernel keeps in LDS.
+constexpr int kPtCache = 2048;
+
+// fill_rowtab for the all-heads kernel (NT threads), with one memory latency fewer: the page-table
+// row of the sequence's compressed cache (its first kPtCache entries) is read into LDS (ptl)
+// together with the selected ids and the window rows' page entries, so that a selected row's
+// page is then an LDS lookup. A sequence with more pages than that reads them from memory.
+// rowtab[0 .. n rounded up to `pad`) is written; ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void fill_rows(const AttnArgs& a, int t, const QueryRows& q, int r0, int n,
+                                          uint32_t* rowtab, int* ptl, int pad) {
+  constexpr int RPT = (kMaxRowsWG + NT - 1) / NT;
+  constexpr int PPT = kPtCache / NT;
+  const int tid = threadIdx.x;
+  const int npg = (q.nv + 63) >> 6;
+  const bool cached = npg <= kPtCache;
+  const int32_t* cpt = a.comp.pt + (int64_t)q.seq * a.comp.pt_stride;
+  const int32_t* spt = a.swa.pt + (int64_t)q.seq * a.swa.pt_stride;
+  int pv[PPT];
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    const int idx = tid + k * NT;
+    pv[k] = cached && idx < npg ? __ldg(cpt + idx) : 0;
+  }
+  const int last = max(q.R - 1, 0);
+  int id[RPT], spg[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int gr = min(r0 + tid + i * NT, last);
+    const int j = min(max(gr - q.n_swa, 0), max(q.n_comp - 1, 0));
+    id[i] = a.topk_idx ? __ldg(a.topk_idx + (int64_t)t * a.topk + j) : j;
+    spg[i] = gr < q.n_swa ? __ldg(spt + ((q.lo + gr) >> 6)) : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    const int idx = tid + k * NT;
+    if (idx < npg && cached) ptl[idx] = pv[k];
+  }
+  __syncthreads();
+  const int np = min((n + pad - 1) / pad * pad, kMaxRowsWG);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int li = tid + i * NT;
+    const int gr = r0 + li;
+    const bool is_swa = gr < q.n_swa;
+    const bool ok_id = is_swa || (id[i] >= 0 && id[i] < q.nv);
+    const int row = ok_id ? (is_swa ? q.lo + gr : id[i]) : 0;
+    int pg = spg[i];
+    if (!is_swa && li < np) pg = cached ? ptl[row >> 6] : __ldg(cpt + (row >> 6));
+    const int npages = is_swa ? a.swa.num_pages : a.comp.num_pages;
+    const bool ok = li < n && gr < q.R && ok_id && pg >= 0 && pg < npages;
+    if (li < np) rowtab[li] = ok ? ((is_swa ? 0u : 0x80000000u) | (uint32_t)(pg * 64 + (row & 63))) : kNoRow;
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- row staging
 // LDS tiles hold rows of D bf16 without padding; the 16-byte chunk c of row r sits at chunk
 // c ^ swz(r), a 4-bit XOR that depends on r mod 16. gfx950's LDS serves a 128-bit read for 16
@@ -137,174 +188,62 @@ __device__ __forceinline__ void fill_rowtab(const AttnArgs& a, int t, const Quer
 __device__ __forceinline__ int swz_dec(int r) {
   return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
 }
-__device__ __forceinline__ int swz_pre(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
-// Each variant loads one 32-row tile's worth of 16-byte pieces per lane into registers and
-// later writes them (dequantised to bf16 for fp8_ds) into the LDS tile.
-template <int D, int FMT>
-struct Stage {
-  static constexpr int RS = D * 2;                           // LDS row stride
-  static constexpr int PB = FMT == HCS_FMT_FP8DS ? kFp8PageBytes : kPageRows * D * 2;
-  // rows per load instruction over a wave: bf16 D=512 and fp8ds: 1; bf16 D=128: 4
-  static constexpr int RPL = (FMT == HCS_FMT_BF16 && D == 128) ? 4 : 1;
-  static constexpr int NLD_TILE = kTile / RPL;               // loads for a whole 32-row tile
+// fp8_ds rows (448 e4m3 latent + 64 bf16 rope + per-64 UE8M0 scales, D = 512): one row per
+// wave-wide register load, written dequantised to bf16 into the LDS tile.
+struct Fp8Stage {
+  static constexpr int D = 512, RS = D * 2, PB = kFp8PageBytes;
 
-  // Row within the load and 16-byte chunk index of this lane.
-  __device__ static __forceinline__ int lane_row(int lane) { return RPL == 1 ? 0 : lane >> 4; }
-  __device__ static __forceinline__ int lane_chunk(int lane) { return RPL == 1 ? lane : lane & 15; }
-
-  // Issue the load of this lane's piece of the row with table entry `e` (wave-uniform when
-  // RPL == 1, so the row address is computed once in scalar registers).
+  // Issue the load of this lane's 16-byte piece of the row with table entry `e` (wave-uniform,
+  // so the row address is computed once in scalar registers): lanes 0..27 take 16 latent
+  // codes, lanes 28..35 8 rope values, the others nothing useful.
   __device__ static __forceinline__ void load(const AttnArgs& a, uint32_t e, int lane, i32x4& v,
                                               float& sc) {
-    sc = 1.f;
-    if constexpr (FMT == HCS_FMT_FP8DS) {
-      e = (uint32_t)__builtin_amdgcn_readfirstlane((int)e);
-      const bool ok = e != kNoRow;
-      const uint32_t ridx = e & 0x7fffffffu;
-      const uint8_t* page = ok ? ((e >> 31) ? a.comp.base : a.swa.base) + (size_t)(ridx >> 6) * PB
-                               : g_zero_row;
-      const int slot = ok ? (int)(ridx & 63) : 0;
-      // lanes 0..27: 16 latent codes, lanes 28..35: 8 rope values, others: nothing useful
-      const int off = lane < 28 ? kFp8PageCodes + slot * kFp8Latent + lane * 16
-                                : (lane < 36 ? kFp8PageRope + slot * (kFp8Rope * 2) + (lane - 28) * 16
-                                             : kFp8PageCodes + slot * kFp8Latent);
-      v = ok ? *(const i32x4*)(page + off) : *(const i32x4*)(g_zero_row + (lane & 31) * 16);
-      const int se = ok ? page[kFp8PageScales + slot * 8 + (min(lane, 27) >> 2)] : 0;
-      sc = ok && lane < 28 ? __builtin_ldexpf(1.f, se - 127) : 1.f;
-    } else if constexpr (RPL == 1) {
-      e = (uint32_t)__builtin_amdgcn_readfirstlane((int)e);
-      const uint8_t* rb = e != kNoRow
-                              ? ((e >> 31) ? a.comp.base : a.swa.base) + (size_t)(e & 0x7fffffffu) * (D * 2)
-                              : g_zero_row;
-      v = *(const i32x4*)(rb + lane * 16);
-    } else {
-      const int chunk = lane_chunk(lane);
-      const bool ok = e != kNoRow;
-      const uint8_t* base = (e >> 31) ? a.comp.base : a.swa.base;
-      const uint8_t* p = ok ? base + (size_t)(e & 0x7fffffffu) * (D * 2) + chunk * 16 : g_zero_row + chunk * 16;
-      v = *(const i32x4*)p;
-    }
+    e = (uint32_t)__builtin_amdgcn_readfirstlane((int)e);
+    const bool ok = e != kNoRow;
+    const uint32_t ridx = e & 0x7fffffffu;
+    const uint8_t* page = ok ? ((e >> 31) ? a.comp.base : a.swa.base) + (size_t)(ridx >> 6) * PB
+                             : g_zero_row;
+    const int slot = ok ? (int)(ridx & 63) : 0;
+    const int off = lane < 28 ? kFp8PageCodes + slot * kFp8Latent + lane * 16
+                              : (lane < 36 ? kFp8PageRope + slot * (kFp8Rope * 2) + (lane - 28) * 16
+                                           : kFp8PageCodes + slot * kFp8Latent);
+    v = ok ? *(const i32x4*)(page + off) : *(const i32x4*)(g_zero_row + (lane & 31) * 16);
+    const int se = ok ? page[kFp8PageScales + slot * 8 + (min(lane, 27) >> 2)] : 0;
+    sc = ok && lane < 28 ? __builtin_ldexpf(1.f, se - 127) : 1.f;
   }
 
-  // Write this lane's piece of row `r` (tile-local) into the LDS tile.
+  // Write this lane's piece of row `r` (tile-local) into the LDS tile, chunks swizzled by `sw`
+  // (the bf16 row is 1 KiB: latent chunks 0..55, rope chunks 56..63).
   __device__ static __forceinline__ void store(uint8_t* tile, int r, int sw, int lane,
                                                const i32x4& v, float sc) {
-    const int chunk = lane_chunk(lane);
     uint8_t* row = tile + r * RS;
-    if constexpr (FMT == HCS_FMT_FP8DS) {
-      if (chunk < 28) {
-        i32x4 lo4, hi4;
-        lo4.x = e4m3x2_to_bf16x2<false>(v.x, sc);
-        lo4.y = e4m3x2_to_bf16x2<true>(v.x, sc);
-        lo4.z = e4m3x2_to_bf16x2<false>(v.y, sc);
-        lo4.w = e4m3x2_to_bf16x2<true>(v.y, sc);
-        hi4.x = e4m3x2_to_bf16x2<false>(v.z, sc);
-        hi4.y = e4m3x2_to_bf16x2<true>(v.z, sc);
-        hi4.z = e4m3x2_to_bf16x2<false>(v.w, sc);
-        hi4.w = e4m3x2_to_bf16x2<true>(v.w, sc);
-        *(i32x4*)(row + ((2 * chunk) ^ sw) * 16) = lo4;
-        *(i32x4*)(row + ((2 * chunk + 1) ^ sw) * 16) = hi4;
-      } else if (chunk < 36) {
-        *(i32x4*)(row + ((56 + chunk - 28) ^ sw) * 16) = v;
-      }
-    } else {
-      *(i32x4*)(row + (chunk ^ sw) * 16) = v;
+    if (lane < 28) {
+      i32x4 lo4, hi4;
+      lo4.x = e4m3x2_to_bf16x2<false>(v.x, sc);
+      lo4.y = e4m3x2_to_bf16x2<true>(v.x, sc);
+      lo4.z = e4m3x2_to_bf16x2<false>(v.y, sc);
+      lo4.w = e4m3x2_to_bf16x2<true>(v.y, sc);
+      hi4.x = e4m3x2_to_bf16x2<false>(v.z, sc);
+      hi4.y = e4m3x2_to_bf16x2<true>(v.z, sc);
+      hi4.z = e4m3x2_to_bf16x2<false>(v.w, sc);
+      hi4.w = e4m3x2_to_bf16x2<true>(v.w, sc);
+      *(i32x4*)(row + ((2 * lane) ^ sw) * 16) = lo4;
+      *(i32x4*)(row + ((2 * lane + 1) ^ sw) * 16) = hi4;
+    } else if (lane < 36) {
+      *(i32x4*)(row + ((56 + lane - 28) ^ sw) * 16) = v;
     }
   }
 };
 
-// ---------------------------------------------------------------- per-wave tile math
-// One wave, 16 heads (q in registers), one LDS tile of 32 rows; `valid` bit r = row r takes
-// part. Keeps a reference max m_ref (base 2) per head: probabilities are exp2(x - m_ref), and
-// the accumulators are rescaled only when a tile's max exceeds m_ref by more than kLazy, so
-// the rescale (a multiply of all 128 accumulators) is rare; probabilities stay below 2^kLazy.
+// ---------------------------------------------------------------- online softmax
+// Each head keeps a reference max m_ref (base 2): probabilities are exp2(x - m_ref), and the
+// accumulators are rescaled only when a block's max exceeds m_ref by more than kLazyBlock; the
+// new reference is then the block max if it is more than kLazy above the old one. Probabilities
+// stay below 2^kLazyBlock, exact enough in bf16 and far from float32 overflow, and the rescale
+// (a multiply of every accumulator) is rare.
 constexpr float kLazy = 8.f;
-// In the decode kernel the reference max may lag further behind (probabilities up to 2^32,
-// still exact enough in bf16 and far from float32 overflow), so that a new shared reference
-// is agreed on only when some wave sees scores 2^32 above it.
 constexpr float kLazyBlock = 32.f;
-
-// Q is either in registers (qreg, 4 VGPRs per k-step) or, with QLDS, in an LDS copy qL of the
-// 16 heads' rows laid out like a tile (swizzled chunks).
-template <int D, bool QLDS>
-__device__ __forceinline__ void tile_math(const uint8_t* L, uint32_t valid, const bf16x8* qreg,
-                                          const uint8_t* qL, float scale_log2, float& m_ref,
-                                          float& l_run, f32x4* oacc) {
-  constexpr int KS = D / 32, CT = D / 16, RS = D * 2;
-  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
-  // K operand: row mt*16 + l16, chunk (4ks + g) ^ s = 4 (ks ^ (s >> 2)) + ((g ^ s) & 3)
-  const int sk = swz_pre(l16);
-  const int koff = l16 * RS + ((g ^ sk) & 3) * 16;
-  int ko4[4];
-#pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4) ko4[k4] = koff + 64 * (k4 ^ (sk >> 2));
-  f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int ko = ko4[ks & 3] + (ks >> 2) * 256;
-    bf16x8 qb;
-    if constexpr (QLDS) qb = *(const bf16x8*)(qL + ko);
-    else qb = qreg[ks];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const bf16x8 av = *(const bf16x8*)(L + ko + mt * 16 * RS);
-      sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb, sacc[mt], 0, 0, 0);
-    }
-  }
-  float x[8];
-  float tmax = kNegInf;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = mt * 16 + 4 * g + i;
-      const float v = ((valid >> row) & 1u) ? sacc[mt][i] * scale_log2 : kNegInf;
-      x[mt * 4 + i] = v;
-      tmax = fmaxf(tmax, v);
-    }
-  }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-  const bool grow = tmax > m_ref + kLazy;
-  if (__any(grow)) {
-    const float mnew = grow ? tmax : m_ref;
-    const float alpha = __builtin_amdgcn_exp2f(m_ref - mnew);   // 0 when m_ref = -inf
-    l_run *= alpha;
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) oacc[ct] *= alpha;
-    m_ref = mnew;
-  }
-  const float mr = m_ref == kNegInf ? 0.f : m_ref;
-  float p[8];
-  float psum = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    p[j] = __builtin_amdgcn_exp2f(x[j] - mr);
-    psum += p[j];
-  }
-  l_run += psum;
-  bf16x8 pb;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
-  // V^T: group g reads rows ra = 4g + (l16 >> 2) and ra + 16, 8 bytes at column 16 ct + 4 (l16 & 3)
-  //   byte 32 ct + 8 q -> chunk (2 ct + (q >> 1)) ^ s = 2 (ct ^ (s >> 1)) + (((q >> 1) ^ s) & 1)
-  const int ra = 4 * g + (l16 >> 2), q4 = l16 & 3;
-  const int sv = swz_pre(ra);                      // rows ra and ra + 16 share it
-  const uint8_t* vb = L + ra * RS + ((((q4 >> 1) ^ sv) & 1) * 16) + (q4 & 1) * 8;
-  const uint8_t* vo[8];
-#pragma unroll
-  for (int c8 = 0; c8 < 8; ++c8) vo[c8] = vb + 32 * (c8 ^ (sv >> 1));
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    const uint8_t* va = vo[ct & 7] + (ct >> 3) * 256;
-    const i16x4 v0 = lds_read_tr16(va);
-    const i16x4 v1 = lds_read_tr16(va + 16 * RS);
-    const i16x8 v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-    oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pb, oacc[ct], 0,
-                                                       0, 0);
-  }
-}
 
 template <int D>
 __device__ __forceinline__ void load_q(const AttnArgs& a, int t, int head, bf16x8* qreg) {
@@ -335,15 +274,7 @@ __device__ __forceinline__ float lse_of(float m, float l) {
   return l > 0.f ? (m + __builtin_log2f(l)) * 0.6931471805599453f : kNegInf;
 }
 
-// ================================================================ decode kernel
-// A block is (query, split of its rows, 16 heads); it walks its rows in 64-row blocks held in a
-// double-buffered LDS ring. Wave w gathers rows 16w..16w+15 of the next block while the
-// current one is processed: bf16 rows go straight from the paged cache into LDS with
-// global_load_lds (no registers; the chunk swizzle is applied to the source addresses), fp8_ds
-// rows go through registers to be dequantised. Wave w computes S^T for its 16 rows, the waves
-// agree on the block's max per head through LDS, each writes its rows' probabilities (bf16) to
-// LDS, and each accumulates O^T for its own quarter of the output columns over all 64 rows:
-// 32 accumulator registers per lane, no cross-wave merge of O.
+// s_waitcnt vmcnt(0): this wave's global loads (including those into LDS) have completed.
 __device__ __forceinline__ void wait_vm_zero() {
   // s_waitcnt vmcnt(0): vmcnt 0, expcnt 7, lgkmcnt 15 (gfx9 encoding)
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -359,23 +290,26 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D, int FMT>
-__global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
-  using S = Stage<D, FMT>;
-  constexpr int RS = D * 2, KS = D / 32;
+// ================================================================ 16-head kernel (fp8_ds)
+// A block is (query, split of its rows, 16 heads); it walks its rows in 64-row blocks held in a
+// double-buffered LDS ring. Wave w loads rows 16w..16w+15 of the next block into registers
+// while the current one is processed and writes them dequantised at the start of the next.
+// Wave w computes S^T for its 16 rows, the waves agree on the block's max per head through LDS,
+// each writes its rows' probabilities (bf16) to LDS, and each accumulates O^T for its own
+// quarter of the output columns over all 64 rows: 32 accumulator registers per lane, no
+// cross-wave merge of O.
+__global__ __launch_bounds__(kThreads, 1) void mla_fp8_kernel(AttnArgs a) {
+  using S = Fp8Stage;
+  constexpr int D = S::D, RS = S::RS, KS = D / 32;
   constexpr int CTW = D / 16 / 4;                 // 16-column output tiles per wave
   constexpr int BT = 64;                          // rows per block
   constexpr int WR = BT / 4;                      // rows per wave
   constexpr int PR = BT + 8;                      // P row stride (elements), padded
-  constexpr bool ASYNC = FMT == HCS_FMT_BF16;     // rows straight to LDS
-  // bf16: rows per 1 KiB load instruction; fp8ds: one row per register load
-  constexpr int RPI = ASYNC ? 1024 / RS : 1;
-  constexpr int NLD = WR / RPI;
+  constexpr int NLD = WR;                         // one row per register load
   __shared__ __attribute__((aligned(16))) uint8_t tile0[BT * RS];
   __shared__ __attribute__((aligned(16))) uint8_t tile1[BT * RS];
-  // ASYNC: byte address of every row (the zero row where a row does not take part);
-  // otherwise the packed (cache, page, slot) entries
-  __shared__ __attribute__((aligned(16))) uint32_t rowtab[ASYNC ? 2 * kMaxRowsWG : kMaxRowsWG];
+  // packed (cache, page, slot) entries of the rows
+  __shared__ __attribute__((aligned(16))) uint32_t rowtab[kMaxRowsWG];
   __shared__ __attribute__((aligned(16))) __bf16 p_lds0[16 * PR];
   __shared__ __attribute__((aligned(16))) __bf16 p_lds1[16 * PR];
   __shared__ float mx[4][16];
@@ -396,28 +330,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
   const int r0 = s * a.rows_per_split;
   const int n_rows = max(0, min(q.R, r0 + a.rows_per_split) - r0);
   fill_rowtab(a, t, q, r0, n_rows, rowtab, BT);
-  if constexpr (ASYNC) {
-    // entries -> addresses, in place from the top so no entry is overwritten before it is read
-    __syncthreads();
-    const int n64 = (n_rows + BT - 1) / BT * BT;
-    uint32_t ent[kRowsPerThread];
-#pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-      const int li = (int)threadIdx.x + i * kThreads;
-      ent[i] = li < n64 ? rowtab[li] : kNoRow;
-    }
-    __syncthreads();
-    uint64_t* addr = reinterpret_cast<uint64_t*>(rowtab);
-#pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-      const int li = (int)threadIdx.x + i * kThreads;
-      const uint32_t e = ent[i];
-      const uint8_t* p = e != kNoRow
-                             ? ((e >> 31) ? a.comp.base : a.swa.base) + (size_t)(e & 0x7fffffffu) * RS
-                             : g_zero_row;
-      if (li < n64) addr[li] = reinterpret_cast<uint64_t>(p);
-    }
-  }
   // q of the 16 heads as the B operand (same for the 4 waves)
   bf16x8 qreg[KS];
   load_q<D>(a, t, hg * 16 + l16, qreg);
@@ -428,47 +340,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
   float m_ref = kNegInf, l_part = 0.f;
   const int nblk = (n_rows + BT - 1) / BT;
 
-  i32x4 pre[ASYNC ? 1 : NLD];
-  float psc[ASYNC ? 1 : NLD];
+  i32x4 pre[NLD];
+  float psc[NLD];
   __syncthreads();
 
-  // gather this wave's rows of block b into buffer tbuf
-  // per-lane source offsets of the async row loads (the swizzle is applied on the source side:
-  // LDS chunk slot `lane` of row r receives source chunk lane ^ swz(r))
-  int soff[ASYNC ? NLD : 1];
-  if constexpr (ASYNC) {
+  // load this wave's rows of block b into registers (written to LDS at the start of block b)
+  auto issue = [&](int b) {
+    const uint32_t* rt = rowtab + b * BT + wave * WR;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int rw = i * RPI + lane / (64 / RPI);
-      soff[i] = ((lane % (64 / RPI)) ^ swz_dec(rw)) * 16;         // rows 16w + rw share swz_dec(rw)
-    }
-  }
-  auto issue = [&](int b, uint8_t* tbuf) {
-    if constexpr (ASYNC) {
-      const uint64_t* at = reinterpret_cast<const uint64_t*>(rowtab) + b * BT + wave * WR;
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int rw = i * RPI + lane / (64 / RPI);             // row of this lane within the wave's rows
-        uint64_t src;
-        if constexpr (RPI == 1) {
-          // both halves zero-extended (readfirstlane returns a signed int)
-          const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)at[i]);
-          const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(at[i] >> 32));
-          src = (uint64_t)lo | ((uint64_t)hi << 32);
-        } else {
-          src = at[rw];
-        }
-        uint8_t* dst = tbuf + (wave * WR + i * RPI) * RS;       // 1 KiB of consecutive rows
-        __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const uint8_t*>(src) + soff[i]),
-                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-      }
-    } else {
-      const uint32_t* rt = rowtab + b * BT + wave * WR;
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) S::load(a, rt[i], lane, pre[i], psc[i]);
-    }
+    for (int i = 0; i < NLD; ++i) S::load(a, rt[i], lane, pre[i], psc[i]);
   };
-  if (nblk > 0) issue(0, tile0);
+  if (nblk > 0) issue(0);
 
   // lane-constant LDS offsets
   // K row 16w + l16, chunk (4ks + g) ^ s = 4 (ks ^ (s >> 2)) + ((g ^ s) & 3), s = swz_dec(l16)
@@ -490,27 +372,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
   }
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-  // One block; T holds it, TN receives the next one, P/F are this block's probability buffer
-  // and flags. The loop below is unrolled by two so that the two LDS buffers are distinct
-  // objects: the async loads into TN are then known not to alias reads of T (no wait).
+  // One block; T holds it, P/F are this block's probability buffer and flags (alternating, so
+  // a wave may write the next block's while another still reads this one's).
   // Shared reference max: every wave uses the same m_ref for the whole block, so each can
   // write its rows' probabilities for the column-split PV. A wave whose scores exceed
   // m_ref + kLazyBlock raises a flag; only then do the waves exchange maxima and rescale.
-  auto block = [&](int b, uint8_t* T, uint8_t* TN, __bf16* P, int* F) {
-    if constexpr (!ASYNC) {
+  auto block = [&](int b, uint8_t* T, __bf16* P, int* F) {
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) S::store(T, wave * WR + i, swz_dec(i), lane, pre[i], psc[i]);
-    } else {
-      wait_vm_zero();                                    // this wave's rows of block b landed
-    }
+    for (int i = 0; i < NLD; ++i) S::store(T, wave * WR + i, swz_dec(i), lane, pre[i], psc[i]);
     lds_barrier();                                       // block b is in LDS
-    if (b + 1 < nblk) issue(b + 1, TN);
-    bool vr;
-    if constexpr (ASYNC)
-      vr = reinterpret_cast<const uint64_t*>(rowtab)[b * BT + wave * WR + (lane & 15)] !=
-           reinterpret_cast<uint64_t>(g_zero_row);
-    else
-      vr = rowtab[b * BT + wave * WR + (lane & 15)] != kNoRow;
+    if (b + 1 < nblk) issue(b + 1);
+    const bool vr = rowtab[b * BT + wave * WR + (lane & 15)] != kNoRow;
     const uint32_t valid = (uint32_t)__ballot(vr && lane < 16);
     // ---- S^T for this wave's 16 rows (two accumulators halve the dependent chain)
     f32x4 sacc2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -586,8 +458,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
     }
   };
   for (int b = 0; b < nblk; b += 2) {
-    block(b, tile0, tile1, p_lds0, flag0);
-    if (b + 1 < nblk) block(b + 1, tile1, tile0, p_lds1, flag1);
+    block(b, tile0, p_lds0, flag0);
+    if (b + 1 < nblk) block(b + 1, tile1, p_lds1, flag1);
   }
 
   // ---- sums over the waves' rows (all waves share m_ref)
@@ -620,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
   // ---- split: write this split's partial (unnormalised O, reference max, sum); a second
   // kernel merges the splits (a kernel boundary orders the writes before the reads on every
   // XCD, which in-kernel device-scope fences would do at a far higher cost)
-  const int64_t prow = ((int64_t)(t * a.n_hg + hg) * a.nsplit + s) * 16 + l16;
+  const int64_t prow = ((int64_t)(t * a.n_h16 + hg) * a.nsplit + s) * 16 + l16;
   float* po = a.ws_o + prow * D;
 #pragma unroll
   for (int ct = 0; ct < CTW; ++ct) *(f32x4*)(po + 16 * (wave * CTW + ct) + 4 * g) = oacc[ct];
@@ -630,14 +502,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(AttnArgs a) {
   }
 }
 
-// Merge the split partials of one (query, 16-head group): thread -> head tid / 16, D/16 columns.
+// Merge the split partials of one query's heads: a block is (query, 4 heads), a wave one head,
+// each lane D/64 columns; all splits' loads of a lane are issued together.
 template <int D>
 __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
-  constexpr int PER = D / 16;
-  const int t = blockIdx.x, hg = blockIdx.y, tid = threadIdx.x;
-  const int h = tid >> 4, c0 = (tid & 15) * PER;
-  const int hq = hg * 16 + h;
-  const int64_t pbase = ((int64_t)(t * a.n_hg + hg) * a.nsplit) * 16 + h;   // row of split 0
+  constexpr int PER = D / 64;
+  const int t = blockIdx.x, h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int c0 = (threadIdx.x & 63) * PER;
+  if (h >= a.H) return;
+  const int64_t pbase = ((int64_t)(t * a.n_h16 + h / 16) * a.nsplit) * 16 + (h & 15);  // split 0
   float Ms = kNegInf;
   for (int ss = 0; ss < a.nsplit; ++ss) Ms = fmaxf(Ms, a.ws_ml[(pbase + (int64_t)ss * 16) * 2]);
   float acc[PER];
@@ -645,149 +518,369 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
   for (int c = 0; c < PER; ++c) acc[c] = 0.f;
   float Ls = 0.f;
   if (Ms != kNegInf) {
-    for (int ss = 0; ss < a.nsplit; ++ss) {
-      const int64_t pr = pbase + (int64_t)ss * 16;
-      const float ms = a.ws_ml[pr * 2], ls = a.ws_ml[pr * 2 + 1];
-      if (!(ls > 0.f)) continue;
-      const float f = __builtin_amdgcn_exp2f(ms - Ms);
-      Ls += ls * f;
-      const float* src = a.ws_o + pr * D + c0;
+    // four splits at a time, all their loads issued before any is used
+    constexpr int U = 4;
+    for (int s0 = 0; s0 < a.nsplit; s0 += U) {
+      float ms[U], ls[U];
+      float2 v[U][PER / 2];
 #pragma unroll
-      for (int c = 0; c < PER; c += 4) {
-        const f32x4 v = *(const f32x4*)(src + c);
-        acc[c] += f * v[0];
-        acc[c + 1] += f * v[1];
-        acc[c + 2] += f * v[2];
-        acc[c + 3] += f * v[3];
+      for (int u = 0; u < U; ++u) {
+        const int ss = min(s0 + u, a.nsplit - 1);
+        const int64_t pr = pbase + (int64_t)ss * 16;
+        ms[u] = a.ws_ml[pr * 2];
+        ls[u] = s0 + u < a.nsplit ? a.ws_ml[pr * 2 + 1] : 0.f;
+        const float* src = a.ws_o + pr * D + c0;
+#pragma unroll
+        for (int c = 0; c < PER / 2; ++c) v[u][c] = *(const float2*)(src + 2 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float f = ls[u] > 0.f ? __builtin_amdgcn_exp2f(ms[u] - Ms) : 0.f;
+        Ls += ls[u] * f;
+#pragma unroll
+        for (int c = 0; c < PER / 2; ++c) {
+          acc[2 * c] += f * v[u][c].x;
+          acc[2 * c + 1] += f * v[u][c].y;
+        }
       }
     }
   }
-  if (hq >= a.H) return;
-  const float f = finish_head(a, hq, Ms, Ls);
+  const float f = finish_head(a, h, Ms, Ls);
   const float inv = Ls > 0.f ? f / Ls : 0.f;
-  uint16_t* orow = a.out + ((int64_t)t * a.H + hq) * D + c0;
+  uint16_t* orow = a.out + ((int64_t)t * a.H + h) * D + c0;
 #pragma unroll
   for (int c = 0; c < PER; c += 2) *(uint32_t*)(orow + c) = pack_bf16x2(acc[c] * inv, acc[c + 1] * inv);
-  if (a.lse && (tid & 15) == 0) a.lse[(int64_t)t * a.H + hq] = lse_of(Ms, Ls);
+  if (a.lse && (threadIdx.x & 63) == 0) a.lse[(int64_t)t * a.H + h] = lse_of(Ms, Ls);
 }
 
-// ================================================================ prefill kernel
-template <int D, int FMT>
-__global__ __launch_bounds__(kThreads, 1) void mla_prefill_kernel(AttnArgs a) {
-  using S = Stage<D, FMT>;
-  constexpr int CT = D / 16, KS = D / 32;
-  // each wave stages 8 rows of every 32-row tile (RPL rows per load)
-  constexpr int NLDW = (kTile / 4) / S::RPL > 0 ? (kTile / 4) / S::RPL : 1;
-  constexpr int WROWS = NLDW * S::RPL;               // rows staged per wave per tile
-  __shared__ __attribute__((aligned(16))) uint8_t lds_tile[2][kTile * S::RS];
-  __shared__ uint32_t rowtab[kMaxRowsWG];
+// ================================================================ all-heads kernel (bf16)
+// A block is (query, split of its rows, 64 heads), so every gathered row is read once for all
+// heads of the query. Rows go from the paged cache straight into a double-buffered, swizzled
+// 64-row LDS ring with global_load_lds (no registers; the chunk swizzle is applied to the source
+// addresses), from a table of row byte addresses built once per block.
+// 8 waves, two per SIMD, so one wave's MFMAs cover another's LDS and memory waits. For S^T,
+// wave w takes heads 16 (w % 4) .. +15 (q in registers) and rows 32 (w / 4) .. +31 of a block;
+// the two waves of a head group keep the same reference max, agreed through LDS when it must
+// move. For O^T, wave w takes output columns D/8 * w .. +D/8 for all 64 heads, with P^T read
+// from LDS. A block costs two barriers (three when a reference max moves).
+constexpr int kHeadsThreads = 512;
+
+template <int D>
+__global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a) {
+  constexpr int NT = kHeadsThreads, NW = NT / 64;
+  constexpr int RS = D * 2, KS = D / 32;
+  constexpr int BT = 64;                          // rows per block
+  constexpr int WRL = BT / NW;                    // rows each wave loads per block
+  constexpr int CTW = D / 16 / NW;                // 16-column output tiles per wave
+  constexpr int PR = BT + 8;                      // P row stride (elements), padded
+  constexpr int RPI = 1024 / RS;                  // rows per 1 KiB async load
+  constexpr int LPR = 64 / RPI;                   // lanes per row in an async load
+  constexpr int NLD = WRL / RPI;                  // async loads per wave per block
+  static_assert(CTW >= 1 && NLD >= 1, "unsupported head dim");
+  __shared__ __attribute__((aligned(16))) uint8_t tile0[BT * RS];
+  __shared__ __attribute__((aligned(16))) uint8_t tile1[BT * RS];
+  __shared__ __attribute__((aligned(16))) uint32_t rowtab[kMaxRowsWG];
+  __shared__ int ptl[kPtCache];
+  __shared__ __attribute__((aligned(16))) __bf16 p_lds[64 * PR];
+  __shared__ float mx[NW][16];
+  __shared__ float alpha_lds[64];
+  __shared__ int flags[NW];
+  __shared__ float hm[64], hl[2][64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const int t = blockIdx.x;
-  const int hbase = blockIdx.y * 64 + wave * 16;
-  const int head = hbase + l16;
-  const bool wave_active = hbase < a.H;
+  const int hq = wave & 3, rh = wave >> 2;       // S^T role: head group, row half
+  const int G = a.nsplit * a.n_hg;
+  const int xcd = blockIdx.x & 7, r = blockIdx.x >> 3;
+  const int t = (r / G) * 8 + xcd;
+  if (t >= a.N) return;
+  const int j = r - (r / G) * G;
+  const int s = j / a.n_hg, hg = j - (j / a.n_hg) * a.n_hg;
+  const int hbase = hg * 64;
 
   const QueryRows q = query_rows(a, t);
-  const int n_rows = min(q.R, kMaxRowsWG);
-  fill_rowtab(a, t, q, 0, n_rows, rowtab);
+  const int r0 = s * a.rows_per_split;
+  const int n_rows = max(0, min(q.R, r0 + a.rows_per_split) - r0);
   bf16x8 qreg[KS];
-  load_q<D>(a, t, head, qreg);
-  __syncthreads();
+  load_q<D>(a, t, hbase + 16 * hq + l16, qreg);
+  fill_rows<NT>(a, t, q, r0, n_rows, rowtab, ptl, BT);
+  const int nblk = (n_rows + BT - 1) / BT;
 
-  f32x4 oacc[CT];
+  f32x4 oacc[CTW][4];
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
-  const int ntiles = (n_rows + kTile - 1) / kTile;
+  for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) oacc[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf, l_part = 0.f;            // head hbase + 16 hq + l16, rows of half rh
 
-  i32x4 pre[NLDW];
-  float psc[NLDW];
-  auto issue = [&](int tt) {
+  // async loads: wave w fills rows WRL w .. +WRL-1 of a block; lane -> (row, chunk) of a load,
+  // the swizzle applied on the source side (LDS chunk slot c of row r receives chunk c ^ swz(r))
+  // Row WRL w + i*RPI + lane/LPR has swz_dec((that row) & 15) = swz_dec(i*RPI + lane/LPR) | 8 (w & 1)
+  // (WRL = 8), so the source chunk of a lane is (lane % LPR) ^ 8 (w & 1) ^ swz_dec(...).
+  static_assert(WRL == 8, "row swizzle below assumes 8 rows per wave");
+  const int lane_x = ((lane % LPR) ^ (8 * (wave & 1))) * 16;
+  auto row_ptr = [&](uint32_t e) {
+    return e != kNoRow ? ((e >> 31) ? a.comp.base : a.swa.base) + (size_t)(e & 0x7fffffffu) * RS
+                       : g_zero_row;
+  };
+  auto issue = [&](int b, uint8_t* tbuf) {
+    const uint32_t* at = rowtab + b * BT + WRL * wave;
+    if constexpr (RPI == 1) {
+      // lane j < WRL reads the entry of row j; each load takes it from that lane
+      const uint32_t my = at[lane & (WRL - 1)];
 #pragma unroll
-    for (int i = 0; i < NLDW; ++i) {
-      const int rr = tt * kTile + wave * WROWS + i * S::RPL + S::lane_row(lane);
-      const uint32_t e = rr < n_rows ? rowtab[rr] : kNoRow;
-      S::load(a, e, lane, pre[i], psc[i]);
+      for (int i = 0; i < NLD; ++i) {
+        const uint8_t* src = row_ptr((uint32_t)__builtin_amdgcn_readlane((int)my, i));
+        __builtin_amdgcn_global_load_lds((const void*)(src + (lane_x ^ (swz_dec(i) * 16))),
+                                         (__attribute__((address_space(3))) void*)(tbuf + (WRL * wave + i) * RS),
+                                         16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const uint8_t* src = row_ptr(at[i * RPI + lane / LPR]);
+        const int sw = swz_dec(i * RPI + lane / LPR) * 16;
+        __builtin_amdgcn_global_load_lds((const void*)(src + (lane_x ^ sw)),
+                                         (__attribute__((address_space(3))) void*)(tbuf + (WRL * wave + i * RPI) * RS),
+                                         16, 0, 0);
+      }
     }
   };
-  auto store = [&](int buf) {
+  if (nblk > 0) issue(0, tile0);
+
+  // lane-constant LDS offsets
+  // K row 32 rh + 16 mt + l16, chunk (4ks + g) ^ s = 4 (ks ^ (s >> 2)) + ((g ^ s) & 3), s = swz_dec(l16)
+  const int sk = swz_dec(l16);
+  int ko4[4];
 #pragma unroll
-    for (int i = 0; i < NLDW; ++i)
-      S::store(lds_tile[buf], wave * WROWS + i * S::RPL + S::lane_row(lane),
-               swz_pre(wave * WROWS + i * S::RPL + S::lane_row(lane)), lane, pre[i], psc[i]);
+  for (int k4 = 0; k4 < 4; ++k4) ko4[k4] = (32 * rh + l16) * RS + ((g ^ sk) & 3) * 16 + 64 * (k4 ^ (sk >> 2));
+  // V^T rows 8g + jv and 8g + 4 + jv of a 32-row step: swz_dec = 2 jv + 8 (g & 1) (+1), so
+  // chunk (2 ctg + h) lands at 2 (ctg ^ (jv + 4 (g & 1))) + (h, resp. h ^ 1)
+  const int jv = l16 >> 2, q4 = l16 & 3, h2 = q4 >> 1;
+  const int vx = jv + 4 * (g & 1);
+  const int vrow = (8 * g + jv) * RS + (q4 & 1) * 8;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  __bf16* prow = p_lds + (16 * hq + l16) * PR + 32 * rh + 4 * g;
+
+  auto block = [&](int b, uint8_t* T, uint8_t* TN) {
+    wait_vm_zero();                                      // this wave's rows of block b landed
+    lds_barrier();                                       // block b is in LDS
+    if (b + 1 < nblk) issue(b + 1, TN);
+    const uint32_t valid = (uint32_t)__ballot(rowtab[b * BT + 32 * rh + (lane & 31)] != kNoRow);
+    // ---- S^T[32 rows][16 heads]
+    // one k-step of K fragments is read ahead of the MFMAs that use it; the scheduling fences
+    // keep that pipeline (and the register use) as written
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    bf16x8 kf[2][2];
+    auto kload = [&](int ks, bf16x8* f) {
+      const int ko = ko4[ks & 3] + (ks >> 2) * 256;
+      f[0] = *(const bf16x8*)(T + ko);
+      f[1] = *(const bf16x8*)(T + ko + 16 * RS);
+    };
+    kload(0, kf[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 1 < KS) kload(ks + 1, kf[(ks + 1) & 1]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks & 1][mt], qreg[ks], sacc[mt], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float x[2][4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = mt * 16 + 4 * g + i;
+        x[mt][i] = ((valid >> row) & 1u) ? sacc[mt][i] * a.scale_log2 : kNegInf;
+        tmax = fmaxf(tmax, x[mt][i]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const bool any_over = __any(tmax > m_ref + kLazyBlock);
+    if (g == 0) mx[wave][l16] = tmax;
+    if (lane == 0) flags[wave] = any_over ? 1 : 0;
+    auto probs = [&](float& psum) {
+      const float mr = m_ref == kNegInf ? 0.f : m_ref;
+      psum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        bf16x4 p4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(x[mt][i] - mr);
+          psum += pv;
+          p4[i] = (__bf16)pv;
+        }
+        *(bf16x4*)(prow + mt * 16) = p4;
+      }
+    };
+    float psum = 0.f;
+    if (!any_over) probs(psum);
+    lds_barrier();                                       // probabilities (or flags) of the block
+    int anyf = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) anyf |= flags[w];
+    if (anyf) {
+      // rare: new reference maxima, agreed by the two waves of each head group
+      const float bmax = fmaxf(mx[hq][l16], mx[hq + 4][l16]);
+      const float mnew = bmax > m_ref + kLazy ? bmax : m_ref;
+      // 0 when m_ref = -inf; 1 for a head with no row yet (-inf - -inf would be NaN)
+      const float alpha = mnew == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_ref - mnew);
+      l_part *= alpha;
+      m_ref = mnew;
+      if (rh == 0 && g == 0) alpha_lds[16 * hq + l16] = alpha;
+      probs(psum);
+      lds_barrier();
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float al = alpha_lds[16 * nt + l16];
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) oacc[ct][nt] *= al;
+      }
+    }
+    l_part += psum;
+    // ---- O^T[this wave's columns][64 heads] += V^T P^T over the block's 64 rows
+    // (V^T fragments of the next column tile are read ahead, as for S^T)
+    auto vload = [&](int kk, int ct) {
+      const int ctg = wave * CTW + ct;
+      const uint8_t* vb = T + kk * 32 * RS + vrow + 32 * ((ctg & 7) ^ vx) + (ctg >> 3) * 256;
+      const i16x4 v0 = lds_read_tr16(vb + 16 * h2);
+      const i16x4 v1 = lds_read_tr16(vb + 4 * RS + 16 * (h2 ^ 1));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+#pragma unroll
+    for (int kk = 0; kk < BT / 32; ++kk) {
+      bf16x8 pb[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) pb[nt] = *(const bf16x8*)(p_lds + (16 * nt + l16) * PR + kk * 32 + 8 * g);
+      bf16x8 vf[2];
+      vf[0] = vload(kk, 0);
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (ct + 1 < CTW) vf[(ct + 1) & 1] = vload(kk, ct + 1);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          oacc[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct & 1], pb[nt], oacc[ct][nt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  if (ntiles > 0) {
-    issue(0);
-    store(0);
+  for (int b = 0; b < nblk; b += 2) {
+    block(b, tile0, tile1);
+    if (b + 1 < nblk) block(b + 1, tile1, tile0);
   }
-  __syncthreads();
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const int buf = tt & 1;
-    const bool more = tt + 1 < ntiles;
-    if (more) issue(tt + 1);
-    const bool vr = rowtab[tt * kTile + (lane & 31)] != kNoRow;
-    const uint32_t valid = (uint32_t)__ballot(vr && lane < 32);
-    if (wave_active)
-      tile_math<D, false>(lds_tile[buf], valid, qreg, nullptr, a.scale_log2, m_run, l_run, oacc);
-    if (more) store(buf ^ 1);
-    __syncthreads();
+
+  // ---- per-head (max, sum) to every wave
+  float lt = l_part + __shfl_xor(l_part, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  if (g == 0) {
+    hl[rh][16 * hq + l16] = lt;
+    if (rh == 0) hm[16 * hq + l16] = m_ref;
   }
-  if (!wave_active) return;
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (head >= a.H) return;
-  float mfin = m_run;
-  const float f = finish_head(a, head, mfin, l_tot);
-  const float inv = l_tot > 0.f ? f / l_tot : 0.f;
-  uint16_t* orow = a.out + ((int64_t)t * a.H + head) * D;
+  __syncthreads();                                  // also: every wave is done with the tiles
+  // The result goes through LDS so that each global store writes whole rows: lane holds
+  // O^T[c = 16 (wave * CTW + ct) + 4g + i][head 16 nt + l16]; in LDS, row h holds head h with
+  // its 16-byte chunks XOR-swizzled by h mod 16 (conflict-free for both the scattered writes
+  // here and the row reads below).
+  if (a.nsplit == 1) {
+    // bf16 [64 heads][D] in tile0 (64 rows of RS bytes)
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    const f32x4 o = oacc[ct] * inv;
-    uint2 pk;
-    pk.x = pack_bf16x2(o[0], o[1]);
-    pk.y = pack_bf16x2(o[2], o[3]);
-    *(uint2*)(orow + 16 * ct + 4 * g) = pk;
+    for (int nt = 0; nt < 4; ++nt) {
+      const int hh = hbase + 16 * nt + l16;
+      float M = hm[16 * nt + l16], L = hl[0][16 * nt + l16] + hl[1][16 * nt + l16];
+      const float f = hh < a.H ? finish_head(a, hh, M, L) : 1.f;
+      const float inv = L > 0.f ? f / L : 0.f;
+      if (a.lse && g == 0 && wave == 0 && hh < a.H) a.lse[(int64_t)t * a.H + hh] = lse_of(M, L);
+      uint8_t* hrow = tile0 + (16 * nt + l16) * RS;
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        const f32x4 o = oacc[ct][nt] * inv;
+        uint2 pk;
+        pk.x = pack_bf16x2(o[0], o[1]);
+        pk.y = pack_bf16x2(o[2], o[3]);
+        const int cb = (16 * (wave * CTW + ct) + 4 * g) * 2;           // byte in the row
+        *(uint2*)(hrow + ((((cb >> 4) ^ l16) << 4) | (cb & 15))) = pk;
+      }
+    }
+    __syncthreads();
+    constexpr int LPH = RS / 16;                     // lanes per head row
+    constexpr int HPI = 64 / LPH;                    // heads per wave instruction
+#pragma unroll
+    for (int k = 0; k < 8 / HPI; ++k) {
+      const int hl_ = wave * 8 + k * HPI + lane / LPH, ch = lane % LPH;
+      const int hh = hbase + hl_;
+      const i32x4 v = *(const i32x4*)(tile0 + hl_ * RS + ((ch ^ (hl_ & 15)) << 4));
+      if (hh < a.H) *(i32x4*)(reinterpret_cast<uint8_t*>(a.out + ((int64_t)t * a.H + hh) * D) + ch * 16) = v;
+    }
+  } else {
+    // fp32 partials [64 heads][D]: heads 0..31 in tile0, 32..63 in tile1 (rows of 4D bytes)
+    constexpr int PS = D * 4;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      uint8_t* hrow = (nt < 2 ? tile0 : tile1) + (16 * (nt & 1) + l16) * PS;
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        const int ch = 4 * (wave * CTW + ct) + g;                       // 16-byte chunk in the row
+        *(f32x4*)(hrow + ((ch ^ l16) << 4)) = oacc[ct][nt];
+      }
+    }
+    if (wave == 0 && lane < 64) {
+      const int hh = hbase + lane;
+      if (hh < a.H) {
+        const int64_t prow16 = ((int64_t)(t * a.n_h16 + hh / 16) * a.nsplit + s) * 16 + (hh & 15);
+        a.ws_ml[prow16 * 2 + 0] = hm[lane];
+        a.ws_ml[prow16 * 2 + 1] = hl[0][lane] + hl[1][lane];
+      }
+    }
+    __syncthreads();
+    constexpr int LPH = PS / 16;                     // lanes per head row (128 or 32)
+    constexpr int HPW = 8;                           // heads per wave
+#pragma unroll
+    for (int k = 0; k < HPW * LPH / 64; ++k) {
+      const int fl = k * 64 + lane;                  // flat 16-byte chunk over the wave's rows
+      const int hl_ = wave * HPW + fl / LPH, ch = fl % LPH;
+      const int hh = hbase + hl_;
+      const i32x4 v = *(const i32x4*)((hl_ < 32 ? tile0 : tile1) + (hl_ & 31) * PS + ((ch ^ (hl_ & 15)) << 4));
+      if (hh < a.H) {
+        const int64_t prow16 = ((int64_t)(t * a.n_h16 + hh / 16) * a.nsplit + s) * 16 + (hh & 15);
+        *(i32x4*)(reinterpret_cast<uint8_t*>(a.ws_o + prow16 * D) + ch * 16) = v;
+      }
+    }
   }
-  if (a.lse && g == 0) a.lse[(int64_t)t * a.H + head] = lse_of(mfin, l_tot);
 }
 
 template <int D, int FMT>
 hipError_t launch_impl(const AttnArgs& a, hipStream_t stream) {
-  if (a.kind == 1) {
-    dim3 grid((unsigned)a.N, (unsigned)((a.H + 63) / 64));
-    hipLaunchKernelGGL((mla_prefill_kernel<D, FMT>), grid, dim3(kThreads), 0, stream, a);
+  const int n8 = (a.N + 7) / 8;
+  dim3 grid((unsigned)(n8 * 8 * a.nsplit * a.n_hg));
+  if constexpr (FMT == HCS_FMT_BF16) {
+    hipLaunchKernelGGL((mla_heads_kernel<D>), grid, dim3(kHeadsThreads), 0, stream, a);
   } else {
-    const int n8 = (a.N + 7) / 8;
-    dim3 grid((unsigned)(n8 * 8 * a.nsplit * a.n_hg));
-    hipLaunchKernelGGL((mla_decode_kernel<D, FMT>), grid, dim3(kThreads), 0, stream, a);
-    if (a.nsplit > 1)
-      hipLaunchKernelGGL((mla_combine_kernel<D>), dim3(a.N, a.n_hg), dim3(kThreads), 0, stream, a);
+    static_assert(D == Fp8Stage::D, "fp8_ds rows are 512 wide");
+    hipLaunchKernelGGL(mla_fp8_kernel, grid, dim3(kThreads), 0, stream, a);
   }
+  if (a.nsplit > 1)
+    hipLaunchKernelGGL((mla_combine_kernel<D>), dim3(a.N, (a.H + 3) / 4), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos) {
+AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos, int fmt) {
   AttnPlan p{};
   const int64_t nv = (int64_t)(max_pos + 1) / m;
   const int64_t rows = (int64_t)std::min(window, max_pos + 1) + (topk > 0 ? topk : nv);
-  const int64_t tiles = std::max<int64_t>(1, (rows + kTile - 1) / kTile);
-  const int64_t fits = tiles * kTile <= kMaxRowsWG;
-  // many queries and every row list fits one block: one block per query and 64 heads
-  if (fits && (int64_t)N * ((H + 63) / 64) >= 256) {
-    p.kind = 1;
-    p.nsplit = 1;
-    p.n_hg = (H + 63) / 64;
-    p.rows_per_split = (int)(tiles * kTile);
-    return p;
-  }
-  p.kind = 0;
-  p.n_hg = (H + 15) / 16;
-  constexpr int64_t kBlock = 64;                       // decode blocks walk 64 rows at a time
-  const int64_t blocks = (rows + kBlock - 1) / kBlock;
+  // bf16: 64 heads per block (all-heads kernel); fp8_ds: 16 heads per block
+  p.kind = fmt == HCS_FMT_BF16 ? 2 : 0;
+  const int hpb = p.kind == 2 ? 64 : 16;
+  p.n_hg = (H + hpb - 1) / hpb;
+  p.n_h16 = (H + 15) / 16;
+  constexpr int64_t kBlock = 64;                       // both kernels walk 64 rows at a time
+  const int64_t blocks = std::max<int64_t>(1, (rows + kBlock - 1) / kBlock);
   const int64_t max_bps = kMaxRowsWG / kBlock;
   const int64_t per_split = (int64_t)((N + 7) / 8) * 8 * p.n_hg;
   int64_t nsplit = std::max<int64_t>(1, (256 + per_split - 1) / per_split);
@@ -798,7 +891,7 @@ AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos
   p.nsplit = (int)nsplit;
   p.rows_per_split = (int)(bps * kBlock);
   if (nsplit > 1) {
-    const size_t parts = (size_t)N * p.n_hg * nsplit * 16;
+    const size_t parts = (size_t)N * p.n_h16 * nsplit * 16;
     p.ws_o_bytes = parts * d * sizeof(float);
     p.ws_ml_bytes = parts * 2 * sizeof(float);
     p.ws_bytes = p.ws_o_bytes + p.ws_ml_bytes;

@@ -16,20 +16,20 @@ struct AttnArgs {
   int seq_const, p0;
   const float* sink;          // [H] or nullptr
   int N, H, window, m, nv_cap, pos_cap;
-  int kind;                   // 0: decode kernel (16 heads per block, splits), 1: prefill kernel
-  int nsplit, n_hg, rows_per_split;
+  int kind;                   // 0: 16-head decode kernel (fp8_ds rows), 2: all-heads kernel (bf16)
+  int nsplit, n_hg, n_h16, rows_per_split;   // n_hg: head groups of a kernel block
   float scale_log2;           // softmax scale * log2(e)
   uint16_t* out;              // [N, H, D] bf16
   float* lse;                 // [N, H] or nullptr
-  float* ws_o;                // [N, n_hg, nsplit, 16, D] partial outputs (nsplit > 1)
-  float* ws_ml;               // [N, n_hg, nsplit, 16, 2] partial (max, sum), log2 units
+  float* ws_o;                // [N, n_h16, nsplit, 16, D] partial outputs (nsplit > 1)
+  float* ws_ml;               // [N, n_h16, nsplit, 16, 2] partial (max, sum), log2 units
 };
 
 struct AttnPlan {
-  int kind, nsplit, n_hg, rows_per_split;
+  int kind, nsplit, n_hg, n_h16, rows_per_split;
   size_t ws_o_bytes, ws_ml_bytes, ws_bytes;
 };
-AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos);
+AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos, int fmt);
 hipError_t launch_sparse_mla(const AttnArgs& a, int d, int fmt, hipStream_t stream);
 
 // ---------------------------------------------------------------- compressor
