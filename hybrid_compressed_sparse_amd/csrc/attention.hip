@@ -270,6 +270,16 @@ __device__ __forceinline__ float finish_head(const AttnArgs& a, int head, float&
   return f;
 }
 
+// The same with the sink logit already loaded (in log2 units; -inf when there is none).
+__device__ __forceinline__ float finish_head_s2(float s2, float& m, float& l) {
+  const float mm = fmaxf(m, s2);
+  if (mm == kNegInf || s2 == kNegInf) return 1.f;
+  const float f = __builtin_amdgcn_exp2f(m - mm);
+  l = l * f + __builtin_amdgcn_exp2f(s2 - mm);
+  m = mm;
+  return f;
+}
+
 __device__ __forceinline__ float lse_of(float m, float l) {
   return l > 0.f ? (m + __builtin_log2f(l)) * 0.6931471805599453f : kNegInf;
 }
@@ -503,45 +513,51 @@ __global__ __launch_bounds__(kThreads, 1) void mla_fp8_kernel(AttnArgs a) {
 }
 
 // Merge the split partials of one query's heads: a block is (query, 4 heads), a wave one head,
-// each lane D/64 columns; all splits' loads of a lane are issued together.
+// each lane D/64 columns. Splits are taken eight at a time with all their loads issued together,
+// merged online (running max, rescaled sum and accumulator), so a query with up to eight splits
+// costs one memory latency.
 template <int D>
 __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
   constexpr int PER = D / 64;
+  constexpr int U = 8;
   const int t = blockIdx.x, h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int c0 = (threadIdx.x & 63) * PER;
   if (h >= a.H) return;
   const int64_t pbase = ((int64_t)(t * a.n_h16 + h / 16) * a.nsplit) * 16 + (h & 15);  // split 0
-  float Ms = kNegInf;
-  for (int ss = 0; ss < a.nsplit; ++ss) Ms = fmaxf(Ms, a.ws_ml[(pbase + (int64_t)ss * 16) * 2]);
   float acc[PER];
 #pragma unroll
   for (int c = 0; c < PER; ++c) acc[c] = 0.f;
-  float Ls = 0.f;
-  if (Ms != kNegInf) {
-    // four splits at a time, all their loads issued before any is used
-    constexpr int U = 4;
-    for (int s0 = 0; s0 < a.nsplit; s0 += U) {
-      float ms[U], ls[U];
-      float2 v[U][PER / 2];
+  float Ms = kNegInf, Ls = 0.f;
+  for (int s0 = 0; s0 < a.nsplit; s0 += U) {
+    float ms[U], ls[U];
+    float2 v[U][PER / 2];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int ss = min(s0 + u, a.nsplit - 1);
-        const int64_t pr = pbase + (int64_t)ss * 16;
-        ms[u] = a.ws_ml[pr * 2];
-        ls[u] = s0 + u < a.nsplit ? a.ws_ml[pr * 2 + 1] : 0.f;
-        const float* src = a.ws_o + pr * D + c0;
+    for (int u = 0; u < U; ++u) {
+      const bool in = s0 + u < a.nsplit;
+      const int64_t pr = pbase + (int64_t)min(s0 + u, a.nsplit - 1) * 16;
+      ms[u] = in ? a.ws_ml[pr * 2] : kNegInf;
+      ls[u] = in ? a.ws_ml[pr * 2 + 1] : 0.f;
+      const float* src = a.ws_o + pr * D + c0;
 #pragma unroll
-        for (int c = 0; c < PER / 2; ++c) v[u][c] = *(const float2*)(src + 2 * c);
-      }
+      for (int c = 0; c < PER / 2; ++c) v[u][c] = in ? *(const float2*)(src + 2 * c) : float2{0.f, 0.f};
+    }
+    float mb = Ms;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float f = ls[u] > 0.f ? __builtin_amdgcn_exp2f(ms[u] - Ms) : 0.f;
-        Ls += ls[u] * f;
+    for (int u = 0; u < U; ++u) mb = ls[u] > 0.f ? fmaxf(mb, ms[u]) : mb;
+    if (mb == kNegInf) continue;                    // nothing in these splits (nor before)
+    const float r = Ms == kNegInf ? 0.f : __builtin_amdgcn_exp2f(Ms - mb);
+    Ls *= r;
 #pragma unroll
-        for (int c = 0; c < PER / 2; ++c) {
-          acc[2 * c] += f * v[u][c].x;
-          acc[2 * c + 1] += f * v[u][c].y;
-        }
+    for (int c = 0; c < PER; ++c) acc[c] *= r;
+    Ms = mb;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = ls[u] > 0.f ? __builtin_amdgcn_exp2f(ms[u] - Ms) : 0.f;
+      Ls += ls[u] * f;
+#pragma unroll
+      for (int c = 0; c < PER / 2; ++c) {
+        acc[2 * c] += f * v[u][c].x;
+        acc[2 * c + 1] += f * v[u][c].y;
       }
     }
   }
@@ -601,8 +617,25 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   const QueryRows q = query_rows(a, t);
   const int r0 = s * a.rows_per_split;
   const int n_rows = max(0, min(q.R, r0 + a.rows_per_split) - r0);
-  bf16x8 qreg[KS];
-  load_q<D>(a, t, hbase + 16 * hq + l16, qreg);
+  // q of the block's 64 heads: one contiguous row per head, copied into tile1 by async loads
+  // (wave w: heads 8w..8w+7, chunk c of head h stored at c ^ (h mod 16)); read into registers
+  // after the first rows are requested. tile1 receives rows only from the second block on, and
+  // every wave has read its q by then (the first block's barrier orders it).
+  {
+    constexpr int QLPR = RS / 16;                  // lanes per head row in one load
+    constexpr int QHPI = 64 / QLPR;                // heads per load
+#pragma unroll
+    for (int i = 0; i < 8 / QHPI; ++i) {
+      const int hl_ = 8 * wave + i * QHPI + lane / QLPR;
+      const int hh = hbase + hl_;
+      const uint8_t* src = hh < a.H ? reinterpret_cast<const uint8_t*>(a.q + ((int64_t)t * a.H + hh) * D)
+                                    : g_zero_row;
+      const int ch = (lane % QLPR) ^ (hl_ & 15);
+      __builtin_amdgcn_global_load_lds((const void*)(src + ch * 16),
+                                       (__attribute__((address_space(3))) void*)(tile1 + (8 * wave + i * QHPI) * RS),
+                                       16, 0, 0);
+    }
+  }
   fill_rows<NT>(a, t, q, r0, n_rows, rowtab, ptl, BT);
   const int nblk = (n_rows + BT - 1) / BT;
 
@@ -647,6 +680,10 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
     }
   };
   if (nblk > 0) issue(0, tile0);
+  bf16x8 qreg[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qreg[ks] = *(const bf16x8*)(tile1 + (16 * hq + l16) * RS + (((4 * ks + g) ^ l16) << 4));
 
   // lane-constant LDS offsets
   // K row 32 rh + 16 mt + l16, chunk (4ks + g) ^ s = 4 (ks ^ (s >> 2)) + ((g ^ s) & 3), s = swz_dec(l16)
@@ -775,6 +812,14 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   }
 
   // ---- per-head (max, sum) to every wave
+  // sink logits (log2 units) of the heads this lane finishes, hbase + 16 nt + l16, loaded before
+  // any store is issued (a load wait also waits for earlier stores)
+  float sink2[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int hh = hbase + 16 * nt + l16;
+    sink2[nt] = a.sink && hh < a.H && a.nsplit == 1 ? a.sink[hh] * kLog2e : kNegInf;
+  }
   float lt = l_part + __shfl_xor(l_part, 16, 64);
   lt += __shfl_xor(lt, 32, 64);
   if (g == 0) {
@@ -792,7 +837,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
     for (int nt = 0; nt < 4; ++nt) {
       const int hh = hbase + 16 * nt + l16;
       float M = hm[16 * nt + l16], L = hl[0][16 * nt + l16] + hl[1][16 * nt + l16];
-      const float f = hh < a.H ? finish_head(a, hh, M, L) : 1.f;
+      const float f = finish_head_s2(sink2[nt], M, L);
       const float inv = L > 0.f ? f / L : 0.f;
       if (a.lse && g == 0 && wave == 0 && hh < a.H) a.lse[(int64_t)t * a.H + hh] = lse_of(M, L);
       uint8_t* hrow = tile0 + (16 * nt + l16) * RS;
@@ -809,12 +854,17 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
     __syncthreads();
     constexpr int LPH = RS / 16;                     // lanes per head row
     constexpr int HPI = 64 / LPH;                    // heads per wave instruction
+    i32x4 v[8 / HPI];
+#pragma unroll
+    for (int k = 0; k < 8 / HPI; ++k) {
+      const int hl_ = wave * 8 + k * HPI + lane / LPH, ch = lane % LPH;
+      v[k] = *(const i32x4*)(tile0 + hl_ * RS + ((ch ^ (hl_ & 15)) << 4));
+    }
 #pragma unroll
     for (int k = 0; k < 8 / HPI; ++k) {
       const int hl_ = wave * 8 + k * HPI + lane / LPH, ch = lane % LPH;
       const int hh = hbase + hl_;
-      const i32x4 v = *(const i32x4*)(tile0 + hl_ * RS + ((ch ^ (hl_ & 15)) << 4));
-      if (hh < a.H) *(i32x4*)(reinterpret_cast<uint8_t*>(a.out + ((int64_t)t * a.H + hh) * D) + ch * 16) = v;
+      if (hh < a.H) *(i32x4*)(reinterpret_cast<uint8_t*>(a.out + ((int64_t)t * a.H + hh) * D) + ch * 16) = v[k];
     }
   } else {
     // fp32 partials [64 heads][D]: heads 0..31 in tile0, 32..63 in tile1 (rows of 4D bytes)
@@ -839,15 +889,22 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
     __syncthreads();
     constexpr int LPH = PS / 16;                     // lanes per head row (128 or 32)
     constexpr int HPW = 8;                           // heads per wave
+    constexpr int NK = HPW * LPH / 64;
+    i32x4 v[NK];
 #pragma unroll
-    for (int k = 0; k < HPW * LPH / 64; ++k) {
+    for (int k = 0; k < NK; ++k) {
       const int fl = k * 64 + lane;                  // flat 16-byte chunk over the wave's rows
       const int hl_ = wave * HPW + fl / LPH, ch = fl % LPH;
+      v[k] = *(const i32x4*)((hl_ < 32 ? tile0 : tile1) + (hl_ & 31) * PS + ((ch ^ (hl_ & 15)) << 4));
+    }
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int fl = k * 64 + lane;
+      const int hl_ = wave * HPW + fl / LPH, ch = fl % LPH;
       const int hh = hbase + hl_;
-      const i32x4 v = *(const i32x4*)((hl_ < 32 ? tile0 : tile1) + (hl_ & 31) * PS + ((ch ^ (hl_ & 15)) << 4));
       if (hh < a.H) {
         const int64_t prow16 = ((int64_t)(t * a.n_h16 + hh / 16) * a.nsplit + s) * 16 + (hh & 15);
-        *(i32x4*)(reinterpret_cast<uint8_t*>(a.ws_o + prow16 * D) + ch * 16) = v;
+        *(i32x4*)(reinterpret_cast<uint8_t*>(a.ws_o + prow16 * D) + ch * 16) = v[k];
       }
     }
   }

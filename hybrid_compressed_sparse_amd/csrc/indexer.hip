@@ -7,8 +7,9 @@
 // short-context rule).
 //
 // Scores: one workgroup scores 256 (bf16) or 512 (MXFP4) consecutive entries of one query.
-// The query's heads are the MFMA M dimension and stay in registers; each lane streams 16-byte
-// pieces of key rows straight from the paged cache (no LDS: every key byte is used once).
+// The query's heads are the MFMA M dimension. bf16: a wave's 64 entries are one page of the
+// cache, copied whole into LDS with async loads (as is the query), then read in MFMA operand
+// order. MXFP4: each lane streams 16-byte pieces of key rows straight from the paged cache.
 //   bf16 : v_mfma_f32_16x16x32_bf16, K = d_I in steps of 32;
 //   MXFP4: v_mfma_scale_f32_16x16x128_f8f6f4 with both operands e2m1 and the UE8M0 block
 //          scales as the instruction's scale operands; the documented cache layout (32
@@ -42,67 +43,91 @@ __device__ __forceinline__ void query_of(const IndexArgs& a, int t, int& seq, in
 }
 
 // ---------------------------------------------------------------- bf16 scores
+// A zero row for the query heads a launch pads to a multiple of 16.
+__device__ __attribute__((aligned(64))) uint8_t g_ix_zero[1024];
+
+// Block = 256 entries of one query (4 waves x one 64-entry page each). The page of a wave's
+// entries is one contiguous region of the paged cache, so it is copied into LDS with 1 KiB
+// async loads, as is the query (64 heads x d_I, shared by the waves); both are stored with the
+// 16-byte chunks of row r at chunk ^ (r mod CPR), which makes the MFMA operand reads below free
+// of bank conflicts.
 template <int DI, int MT>
 __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(IndexArgs a) {
   constexpr int KS = DI / 32;
   constexpr int NT = 4;                  // 4 x 16 entries per wave
+  constexpr int RB = DI * 2;             // bytes per key / query row
+  constexpr int CPR = RB / 16;           // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;         // rows per 1 KiB async load
+  constexpr int PAGE = kPageRows * RB;
+  __shared__ __attribute__((aligned(16))) uint8_t qs[64 * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t ks_[4][PAGE];
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  int seq, nv;
-  query_of(a, t, seq, nv);
-  const int e_base = blockIdx.y * (kScoreThreads / 64) * NT * 16 + wave * NT * 16;
-  if (e_base >= nv) return;
-
-  bf16x8 qreg[MT][KS];
+  // query rows: wave w copies heads 16w .. 16w+15 (heads >= H_I read zeros)
+  const uint8_t* q = reinterpret_cast<const uint8_t*>(a.q);
+#pragma unroll
+  for (int i = 0; i < 16 / RPI; ++i) {
+    const int h = 16 * wave + i * RPI + lane / CPR, c = lane % CPR;
+    const uint8_t* src = h < a.H_I ? q + ((int64_t)t * a.H_I + h) * RB + ((c ^ (h & (CPR - 1))) << 4)
+                                   : g_ix_zero + lane * 16;
+    __builtin_amdgcn_global_load_lds((const void*)src,
+                                     (__attribute__((address_space(3))) void*)(qs + (16 * wave + i * RPI) * RB),
+                                     16, 0, 0);
+  }
   float wreg[MT][4];
-  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int h = mt * 16 + l16;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      i32x4 v = h < a.H_I ? *(const i32x4*)(q + ((int64_t)t * a.H_I + h) * DI + 32 * ks + 8 * g)
-                          : i32x4{0, 0, 0, 0};
-      qreg[mt][ks] = __builtin_bit_cast(bf16x8, v);
-    }
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hw = mt * 16 + 4 * g + i;
       wreg[mt][i] = hw < a.H_I ? a.w[(int64_t)t * a.H_I + hw] : 0.f;
     }
-  }
-
-  bf16x8 kreg[NT][KS];
-  bool kval[NT];
+  int seq, nv;
+  query_of(a, t, seq, nv);
+  const int e_base = blockIdx.y * 256 + wave * 64;          // first entry of this wave's page
+  const bool active = e_base < nv;
+  const int pg = active ? page_of(a.keys, seq, e_base) : -1;
+  uint8_t* kl = ks_[wave];
+  if (pg >= 0) {
+    const uint8_t* page = a.keys.base + (int64_t)pg * PAGE;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int e = e_base + nt * 16 + l16;
-    const int pg = e < nv ? page_of(a.keys, seq, e) : -1;
-    kval[nt] = pg >= 0;
-    const uint8_t* row = a.keys.base + (int64_t)(pg < 0 ? 0 : pg) * (kPageRows * DI * 2) + (e & 63) * (DI * 2);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      i32x4 v = pg >= 0 ? *(const i32x4*)(row + (32 * ks + 8 * g) * 2) : i32x4{0, 0, 0, 0};
-      kreg[nt][ks] = __builtin_bit_cast(bf16x8, v);
+    for (int i = 0; i < kPageRows / RPI; ++i) {
+      const int r = i * RPI + lane / CPR, c = lane % CPR;
+      __builtin_amdgcn_global_load_lds((const void*)(page + r * RB + ((c ^ (r & (CPR - 1))) << 4)),
+                                       (__attribute__((address_space(3))) void*)(kl + i * 1024), 16, 0, 0);
     }
   }
+  __syncthreads();                                    // every wave's copies have landed
+  if (!active) return;
+  bf16x8 qreg[MT][KS];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int h = mt * 16 + l16;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      qreg[mt][kk] = *(const bf16x8*)(qs + h * RB + (((4 * kk + g) ^ (h & (CPR - 1))) << 4));
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
+    const int r = nt * 16 + l16;
+    bf16x8 kreg[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) kreg[kk] = *(const bf16x8*)(kl + r * RB + (((4 * kk + g) ^ (r & (CPR - 1))) << 4));
     float part = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qreg[mt][ks], kreg[nt][ks], acc, 0, 0, 0);
+      for (int kk = 0; kk < KS; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qreg[mt][kk], kreg[kk], acc, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) part += wreg[mt][i] * fmaxf(acc[i], 0.f);
     }
     part += __shfl_xor(part, 16, 64);
     part += __shfl_xor(part, 32, 64);
-    const int e = e_base + nt * 16 + l16;
-    if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = kval[nt] ? part : kNegInf;
+    const int e = e_base + r;
+    if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = pg >= 0 ? part : kNegInf;
   }
 }
 
@@ -179,27 +204,86 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexA
 
 // ---------------------------------------------------------------- radix select
 struct SelShared {
-  unsigned hist[256];
+  unsigned hist[2][256];                 // pass p counts into hist[p & 1]; the other is cleared
   unsigned bin, above, cnt_bin;
+  unsigned kmax, kmin, count;            // range and number of the participating keys
   unsigned out_count;
 };
 
-// Finds the k-th largest key among participating elements (k >= 1, at least k participate).
-// Returns the key; *need = how many elements equal to it belong to the top-k; *n_eq = how
-// many participate with that key.
+// Clears what radix_kth expects cleared; the caller puts a barrier between this and the call.
+__device__ __forceinline__ void sel_reset(SelShared& sh) {
+  for (int j = threadIdx.x; j < 256; j += kTopkThreads) sh.hist[0][j] = 0;
+  if (threadIdx.x == 0) {
+    sh.kmax = 0u;
+    sh.kmin = ~0u;
+    sh.count = 0u;
+  }
+}
+
+struct KthResult {
+  uint32_t prefix, mask;                 // keys with (key & mask) > prefix are above the k-th
+  unsigned need, n_eq;                   // of the n_eq keys with (key & mask) == prefix, need belong
+};
+
+// Radix select of the k-th largest key among the participating elements (1 <= k <= their
+// number). Keys first agree on a common leading part (the range min ^ max), so the digits start
+// below it: 8 bits per pass, stopping once the bin holding the k-th key holds exactly the keys
+// still needed (then every key of that bin is taken, no further digit is needed). Two barriers
+// per pass plus one for the range. Expects sel_reset() state; leaves it reset (ordered by the
+// caller's next barrier).
 template <class KeyOf>
-__device__ uint32_t radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of, unsigned* need,
-                              unsigned* n_eq) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
-  unsigned remaining = k;
-  unsigned cnt_bin = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) sh.hist[tid] = 0;
-    __syncthreads();
+__device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  // ---- range and count of the participating keys
+  uint32_t lmax = 0u, lmin = ~0u;
+  unsigned lcnt = 0;
+  for (int i = tid; i < n; i += kTopkThreads) {
+    uint32_t key;
+    if (key_of(i, key)) {
+      lmax = max(lmax, key);
+      lmin = min(lmin, key);
+      ++lcnt;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, o, 64));
+    lmin = min(lmin, (uint32_t)__shfl_xor((int)lmin, o, 64));
+    lcnt += (unsigned)__shfl_xor((int)lcnt, o, 64);
+  }
+  if (lane == 0) {
+    atomicMax(&sh.kmax, lmax);
+    atomicMin(&sh.kmin, lmin);
+    atomicAdd(&sh.count, lcnt);
+  }
+  __syncthreads();
+  const uint32_t kmax = sh.kmax, diff = kmax ^ sh.kmin;
+  const unsigned total = sh.count;
+  KthResult r;
+  if (diff == 0u) {                      // all participating keys are equal
+    __syncthreads();                     // every thread has read the range
+    if (tid == 0) {
+      sh.kmax = 0u;
+      sh.kmin = ~0u;
+      sh.count = 0u;
+    }
+    r.prefix = kmax;
+    r.mask = ~0u;
+    r.need = k;
+    r.n_eq = total;
+    return r;
+  }
+  int top = 31 - __builtin_clz(diff);    // highest bit where the keys differ
+  uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
+  uint32_t prefix = kmax & mask;
+  unsigned remaining = k, cnt_bin = total;
+  for (int pass = 0; top >= 0; ++pass) {
+    const int width = min(8, top + 1);
+    const int shift = top - width + 1;
+    unsigned* hist = sh.hist[pass & 1];
     for (int i = tid; i < n; i += kTopkThreads) {
       uint32_t key;
-      if (key_of(i, key) && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      if (key_of(i, key) && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (tid < 64) {
@@ -207,16 +291,14 @@ __device__ uint32_t radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of, un
       unsigned c[4], tot = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        c[j] = sh.hist[255 - 4 * tid - j];
+        c[j] = hist[255 - 4 * tid - j];
         tot += c[j];
       }
-      unsigned incl = tot;
+      // exclusive prefix of the lanes' totals (< 2^17) from ballots of their bits
+      const uint64_t below = (1ull << tid) - 1;
+      unsigned run = 0;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned v = __shfl_up(incl, o, 64);
-        if (tid >= o) incl += v;
-      }
-      unsigned run = incl - tot;
+      for (int b = 0; b < 17; ++b) run += (unsigned)__popcll(__ballot((tot >> b) & 1u) & below) << b;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (run < remaining && run + c[j] >= remaining) {
@@ -226,50 +308,78 @@ __device__ uint32_t radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of, un
         }
         run += c[j];
       }
+    } else {
+      for (int j = tid - 64; j < 256; j += kTopkThreads - 64) sh.hist[(pass & 1) ^ 1][j] = 0;   // next pass's
     }
     __syncthreads();
     prefix |= sh.bin << shift;
-    mask |= 255u << shift;
+    mask |= ((1u << width) - 1u) << shift;
     remaining -= sh.above;
     cnt_bin = sh.cnt_bin;
-    __syncthreads();
+    top = shift - 1;
+    // hist[pass & 1] was counted into; clear it for a later pass or call (ordered by the
+    // barriers that follow before any reuse)
+    if (tid >= 64)
+      for (int j = tid - 64; j < 256; j += kTopkThreads - 64) sh.hist[pass & 1][j] = 0;
+    if (cnt_bin == remaining) break;
   }
-  *need = remaining;
-  *n_eq = cnt_bin;
-  return prefix;
+  if (tid == 0) {                        // range state for a later call
+    sh.kmax = 0u;
+    sh.kmin = ~0u;
+    sh.count = 0u;
+  }
+  r.prefix = prefix;
+  r.mask = mask;
+  r.need = remaining;
+  r.n_eq = cnt_bin;
+  return r;
 }
 
 // Select the top-k of n elements (n > k) given key_of(i, key) and id_of(i); writes k ids (and
-// scores) in arbitrary order.
+// scores) in arbitrary order. Ties at the k-th key go to the smaller ids.
 template <class KeyOf, class IdOf, class Emit>
 __device__ void block_topk(SelShared& sh, int n, int k, KeyOf key_of, IdOf id_of, Emit emit) {
-  unsigned need, n_eq;
-  const uint32_t T = radix_kth(sh, n, (unsigned)k, key_of, &need, &n_eq);
-  uint32_t T2 = 0;          // ties: take ids whose ~id >= T2 (the `need` smallest ids)
-  const bool tie_break = n_eq > need;
+  const KthResult r = radix_kth(sh, n, (unsigned)k, key_of);
+  // ties (only possible when every bit was resolved: mask = ~0): of the keys equal to the k-th,
+  // take the r.need smallest ids, i.e. the largest ~id
+  bool tie_break = r.n_eq > r.need;
+  KthResult r2{};
   if (tie_break) {
-    unsigned need2, neq2;
-    T2 = radix_kth(
-        sh, n, need,
+    __syncthreads();
+    r2 = radix_kth(
+        sh, n, r.need,
         [&](int i, uint32_t& key) {
           uint32_t kk;
-          if (!key_of(i, kk) || kk != T) return false;
+          if (!key_of(i, kk) || (kk & r.mask) != r.prefix) return false;
           key = ~(uint32_t)id_of(i);
           return true;
-        },
-        &need2, &neq2);
+        });
   }
   if (threadIdx.x == 0) sh.out_count = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < n; i += kTopkThreads) {
-    uint32_t key;
-    if (!key_of(i, key)) continue;
-    bool take = key > T;
-    if (key == T) take = !tie_break || (~(uint32_t)id_of(i) >= T2);
+  // one counter update per wave: lanes take consecutive slots from the wave's base
+  const int lane = threadIdx.x & 63;
+  for (int i0 = threadIdx.x & ~63; i0 < n; i0 += kTopkThreads) {
+    const int i = i0 + lane;
+    uint32_t key = 0;
+    bool take = i < n && key_of(i, key);
     if (take) {
-      const unsigned slot = atomicAdd(&sh.out_count, 1u);
-      emit(slot, id_of(i), key);
+      const uint32_t km = key & r.mask;
+      take = km > r.prefix;
+      if (km == r.prefix) {
+        if (!tie_break) take = true;
+        else {
+          const uint32_t ik = ~(uint32_t)id_of(i);
+          take = (ik & r2.mask) > r2.prefix || (ik & r2.mask) == r2.prefix;   // ids are distinct
+        }
+      }
     }
+    const uint64_t tm = __ballot(take);
+    if (tm == 0) continue;
+    unsigned base = 0;
+    if (lane == __builtin_ctzll(tm)) base = atomicAdd(&sh.out_count, (unsigned)__popcll(tm));
+    base = __shfl(base, __builtin_ctzll(tm), 64);
+    if (take) emit(base + (unsigned)__popcll(tm & ((1ull << lane) - 1)), id_of(i), key);
   }
   __syncthreads();
 }
@@ -279,6 +389,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_single_kernel(IndexArgs a, 
                                                                    int32_t* out_idx,
                                                                    float* out_score) {
   __shared__ SelShared sh;
+  __shared__ uint32_t kl[kSingleMax];    // the query's order keys, read once from memory
   const int t = blockIdx.x;
   int seq, nv;
   query_of(a, t, seq, nv);
@@ -292,8 +403,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_single_kernel(IndexArgs a, 
     }
     return;
   }
+#pragma unroll 8
+  for (int i = threadIdx.x; i < nv; i += kTopkThreads) kl[i] = f32_order_key(sc[i]);
+  sel_reset(sh);
+  __syncthreads();
   block_topk(
-      sh, nv, k, [&](int i, uint32_t& key) { key = f32_order_key(sc[i]); return true; },
+      sh, nv, k, [&](int i, uint32_t& key) { key = kl[i]; return true; },
       [&](int i) { return i; },
       [&](unsigned slot, int id, uint32_t key) {
         if (slot < (unsigned)k) {
@@ -307,6 +422,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_single_kernel(IndexArgs a, 
 __global__ __launch_bounds__(kTopkThreads) void topk_stage1_kernel(IndexArgs a, int k, int nchunks,
                                                                    uint32_t* ckey, int32_t* cid) {
   __shared__ SelShared sh;
+  __shared__ uint32_t kl[kChunk];
   const int t = blockIdx.x, c = blockIdx.y;
   int seq, nv;
   query_of(a, t, seq, nv);
@@ -323,8 +439,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage1_kernel(IndexArgs a, 
     }
     return;
   }
+#pragma unroll 8
+  for (int i = threadIdx.x; i < n; i += kTopkThreads) kl[i] = f32_order_key(sc[i]);
+  sel_reset(sh);
+  __syncthreads();
   block_topk(
-      sh, n, k, [&](int i, uint32_t& key) { key = f32_order_key(sc[i]); return true; },
+      sh, n, k, [&](int i, uint32_t& key) { key = kl[i]; return true; },
       [&](int i) { return lo + i; },
       [&](unsigned slot, int id, uint32_t key) {
         if (slot < (unsigned)k) {
@@ -356,6 +476,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage2_kernel(IndexArgs a, 
   }
   const uint32_t* ck = ckey + (int64_t)t * nchunks * k;
   const int32_t* ci = cid + (int64_t)t * nchunks * k;
+  sel_reset(sh);
+  __syncthreads();
   block_topk(
       sh, nchunks * k,
       k, [&](int i, uint32_t& key) { key = ck[i]; return ci[i] >= 0; }, [&](int i) { return ci[i]; },
@@ -395,7 +517,7 @@ hipError_t launch_index_scores(const IndexArgs& a, int fmt, hipStream_t stream) 
     }
     return hipGetLastError();
   }
-  const int per_wg = (kScoreThreads / 64) * 4 * 16;
+  const int per_wg = 256;
   dim3 grid(a.N, (a.nv_cap + per_wg - 1) / per_wg);
 #define HCS_SCORE_CASE(DI_, MT_)                                                                    \
   if (a.d_I == DI_ && MT == MT_) {                                                                  \
