@@ -61,6 +61,44 @@ def algo_bytes(wl, n_vis: int) -> dict:
     return {"attention": attn, "index_topk": ix, "compress": comp, "step": attn + ix + comp}
 
 
+# ------------------------------------------------------------------ measured HBM traffic
+
+ATTN_SOURCES = ["hybrid_compressed_sparse_amd/csrc/attention.hip", "hybrid_compressed_sparse_amd/csrc/common.h",
+                "hybrid_compressed_sparse_amd/csrc/kernels.h"]
+
+
+def sources_digest(paths) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary
+    (profiles/pmc_attention_<workload>.txt: FETCH_SIZE and WRITE_SIZE per dispatch of each
+    attention kernel, scaled by the same counters' reading for a copy of known size), or None
+    when there is no summary or the attention sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_attention_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or "=" not in line:
+                continue
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("sources_digest") != sources_digest(ATTN_SOURCES):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 # ------------------------------------------------------------------ GPU step
 
 class Bench:
@@ -128,33 +166,42 @@ class Bench:
         elif op == "attention":
             st.attend(a["q"], a["swa"], a["comp"], a["q_seq"], a["q_pos"])
 
-    def graph(self, op: str):
+    def graph(self, op: str, sets=None):
+        """A HIP graph of `op` over the input sets `sets` (default: all), one launch per set."""
         torch = self.torch
+        sets = list(range(len(self.sets))) if sets is None else list(sets)
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for _ in range(2):
-                for i in range(len(self.sets)):
+                for i in sets:
                     self.run_op(op, i)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i in range(len(self.sets)):
+            for i in sets:
                 self.run_op(op, i)
         torch.cuda.synchronize()
         return g
 
     def time_graph(self, g, reps: int, warm: int) -> float:
         """Average ms per replay of g over `reps` replays (HIP events on the replay stream)."""
+        return self.time_steps([g], reps, warm)
+
+    def time_steps(self, graphs, reps: int, warm: int) -> float:
+        """ms for `reps` rounds of replaying `graphs` in order, after `warm` untimed rounds; the
+        timed region is bracketed by device synchronisation and HIP events on the replay stream."""
         torch = self.torch
         for _ in range(warm):
-            g.replay()
+            for g in graphs:
+                g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            g.replay()
+            for g in graphs:
+                g.replay()
         e1.record()
         e1.synchronize()
         return e0.elapsed_time(e1) / reps
@@ -197,6 +244,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the HCA side measurement")
     ap.add_argument("--only", default=None, help="replay only this op's graph (for profiling)")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the path: copy MIB MiB device to device --steps times (the known-size "
+                         "reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: the decode path of one "
@@ -207,42 +257,65 @@ def main():
 
     from synth import configs as C
 
+    if args.calib_copy:
+        n = args.calib_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "launches": args.steps}))
+        return
+
     wl = C.BY_NAME[args.workload]
     if wl.kind != "decode":
         sys.exit("bench workloads are the decode configurations")
     n_vis = wl.ctx // wl.m
-    R = args.sets
-    reps = max(1, math.ceil(args.steps / R))
-    warm = max(1, math.ceil(args.warmup / R))
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
+    R = max(1, min(args.sets, args.steps))
     log(f"[bench] {wl.name}: building {R} input sets")
     bench = Bench(wl, R, seed=1000)
 
+    def timed(op, steps, warmup):
+        """ms per launch of `op` over exactly `steps` launches (after `warmup` untimed ones),
+        rotating the input sets: full rounds of all sets, then the remainder."""
+        full, rem = divmod(steps, R)
+        gs = ([bench.graph(op)] * full) + ([bench.graph(op, range(rem))] if rem else [])
+        wf, wr = divmod(warmup, R)
+        for _ in range(wf):
+            gs[0].replay()
+        if wr:
+            bench.graph(op, range(wr)).replay()
+        return bench.time_steps(gs, 1, 0) / steps
+
     if args.only:
-        g = bench.graph(args.only)
-        ms = bench.time_graph(g, reps, warm) / R
+        ms = timed(args.only, args.steps, args.warmup)
         log(f"[bench] {args.only}: {ms * 1e3:.2f} us per launch")
-        print(json.dumps({"op": args.only, "us_per_launch": ms * 1e3}))
+        print(json.dumps({"op": args.only, "us_per_launch": ms * 1e3, "launches": args.steps}))
         return
 
     log("[bench] capturing the step graph")
-    g_step = bench.graph("step")
-    ms_step = bench.time_graph(g_step, reps, warm) / R
+    ms_step = timed("step", args.steps, args.warmup)
     ops = ["compress", "attention"] + (["index_topk"] if wl.indexer else [])
     op_ms = {}
     for op in ops:
-        op_ms[op] = bench.time_graph(bench.graph(op), reps, warm) / R
+        op_ms[op] = timed(op, args.steps, args.warmup)
         log(f"[bench] {op}: {op_ms[op] * 1e3:.2f} us")
     by = algo_bytes(wl, n_vis)
     qps = wl.B / (ms_step * 1e-3)
     step_gbs = by["step"] / (ms_step * 1e-3) / 1e9
-    dom = max(op_ms, key=op_ms.get)
+    # the roofline entry is the attention entry point (its main kernel plus, when a query's
+    # rows are split over blocks, the merge kernel): the largest share of the step
+    dom = "attention"
     dom_gbs = by[dom] / (op_ms[dom] * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name)
     log(f"[bench] step {ms_step * 1e3:.2f} us, {qps:,.0f} q/s, {step_gbs:.0f} GB/s "
         f"({100 * step_gbs / HBM_PEAK_GBS:.1f}% of HBM)")
 
     result = {
         "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1,
-        "steps": reps * R, "warmup": warm * R, "ms_per_step": ms_step,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "context": wl.ctx, "heads": wl.H,
@@ -252,19 +325,20 @@ def main():
                    "kv_format": wl.kv_fmt, "input_sets_rotated": R},
         "hbm_tb_s": step_gbs / 1e3, "hbm_frac": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": by["step"],
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": dom_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "bytes_per_launch": by[dom], "us_per_launch": op_ms[dom] * 1e3},
+        "roofline": {"bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "hcs_sparse_mla_decode (mla_heads_kernel<512> + mla_combine_kernel<512>)",
+                     "algorithmic_bytes_per_launch": by[dom], "us_per_launch": op_ms[dom] * 1e3},
         "ops_us": {k: v * 1e3 for k, v in op_ms.items()},
     }
-    del bench, g_step
+    del bench
     torch.cuda.empty_cache()
 
     if not args.no_extra and wl.name == "csa_decode_bf16":
         hw = C.HCA_DECODE
         log(f"[bench] side measurement: {hw.name}")
         hb = Bench(hw, R, seed=2000)
-        hms = hb.time_graph(hb.graph("step"), reps, warm) / R
+        hms = hb.time_graph(hb.graph("step"), max(1, args.steps // R), max(1, args.warmup // R)) / R
         hby = algo_bytes(hw, hw.ctx // hw.m)
         result["hca_decode_bf16"] = {"queries_per_s": hw.B / (hms * 1e-3), "ms_per_step": hms,
                                      "hbm_frac": hby["step"] / (hms * 1e-3) / 1e9 / HBM_PEAK_GBS,
