@@ -102,10 +102,10 @@ def _as_paged(c) -> Paged:
 
 
 def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
-    """A zero-filled workspace (the attention's split counters must start at zero)."""
+    """A workspace of nbytes (None when none is needed); the library needs no initial contents."""
     if nbytes == 0:
         return None
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 # ------------------------------------------------------------------------------ compressor

@@ -193,7 +193,7 @@ static hcs_status run_attn(hcs::AttnArgs& a, int d, int fmt, int window, int m, 
   a.rows_per_split = plan.rows_per_split;
   if (plan.nsplit > 1) {
     uint8_t* w = static_cast<uint8_t*>(ws);
-    a.ws_o = reinterpret_cast<float*>(w);
+    a.ws_o = reinterpret_cast<uint16_t*>(w);
     a.ws_ml = reinterpret_cast<float*>(w + plan.ws_o_bytes);
   }
   return hip_status(hcs::launch_sparse_mla(a, d, fmt, static_cast<hipStream_t>(stream)), "sparse_mla");

@@ -503,9 +503,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_fp8_kernel(AttnArgs a) {
   // kernel merges the splits (a kernel boundary orders the writes before the reads on every
   // XCD, which in-kernel device-scope fences would do at a far higher cost)
   const int64_t prow = ((int64_t)(t * a.n_h16 + hg) * a.nsplit + s) * 16 + l16;
-  float* po = a.ws_o + prow * D;
+  uint16_t* po = a.ws_o + prow * D;
+  const float pinv = L > 0.f ? 1.f / L : 0.f;         // partial rows are stored normalised, bf16
 #pragma unroll
-  for (int ct = 0; ct < CTW; ++ct) *(f32x4*)(po + 16 * (wave * CTW + ct) + 4 * g) = oacc[ct];
+  for (int ct = 0; ct < CTW; ++ct) {
+    const f32x4 o = oacc[ct] * pinv;
+    uint2 pk;
+    pk.x = pack_bf16x2(o[0], o[1]);
+    pk.y = pack_bf16x2(o[2], o[3]);
+    *(uint2*)(po + 16 * (wave * CTW + ct) + 4 * g) = pk;
+  }
   if (g == 0 && wave == 0) {
     a.ws_ml[prow * 2 + 0] = M;
     a.ws_ml[prow * 2 + 1] = L;
@@ -513,12 +520,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_fp8_kernel(AttnArgs a) {
 }
 
 // Merge the split partials of one query's heads: a block is (query, 4 heads), a wave one head,
-// each lane D/64 columns. Splits are taken eight at a time with all their loads issued together,
-// merged online (running max, rescaled sum and accumulator), so a query with up to eight splits
-// costs one memory latency.
+// each lane D/64 columns. A partial row holds that split's output normalised by its own sum
+// (bf16) and ws_ml its (max, sum) in log2 units; the merge weights split s by
+// sum_s * 2^(max_s - max). Splits are taken eight at a time with all their loads issued
+// together, merged online, so a query with up to eight splits costs one memory latency.
 template <int D>
 __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
-  constexpr int PER = D / 64;
+  constexpr int PER = D / 64;                       // 8 (one 16-byte load) or 2 (4 bytes)
   constexpr int U = 8;
   const int t = blockIdx.x, h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int c0 = (threadIdx.x & 63) * PER;
@@ -530,16 +538,20 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
   float Ms = kNegInf, Ls = 0.f;
   for (int s0 = 0; s0 < a.nsplit; s0 += U) {
     float ms[U], ls[U];
-    float2 v[U][PER / 2];
+    uint32_t v[U][PER / 2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool in = s0 + u < a.nsplit;
       const int64_t pr = pbase + (int64_t)min(s0 + u, a.nsplit - 1) * 16;
       ms[u] = in ? a.ws_ml[pr * 2] : kNegInf;
       ls[u] = in ? a.ws_ml[pr * 2 + 1] : 0.f;
-      const float* src = a.ws_o + pr * D + c0;
-#pragma unroll
-      for (int c = 0; c < PER / 2; ++c) v[u][c] = in ? *(const float2*)(src + 2 * c) : float2{0.f, 0.f};
+      const uint16_t* src = a.ws_o + pr * D + c0;
+      if constexpr (PER == 8) {
+        const i32x4 w = in ? *(const i32x4*)src : i32x4{0, 0, 0, 0};
+        v[u][0] = w.x; v[u][1] = w.y; v[u][2] = w.z; v[u][3] = w.w;
+      } else {
+        v[u][0] = in ? *(const uint32_t*)src : 0u;
+      }
     }
     float mb = Ms;
 #pragma unroll
@@ -552,12 +564,12 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
     Ms = mb;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float f = ls[u] > 0.f ? __builtin_amdgcn_exp2f(ms[u] - Ms) : 0.f;
-      Ls += ls[u] * f;
+      const float f = ls[u] > 0.f ? ls[u] * __builtin_amdgcn_exp2f(ms[u] - Ms) : 0.f;
+      Ls += f;
 #pragma unroll
       for (int c = 0; c < PER / 2; ++c) {
-        acc[2 * c] += f * v[u][c].x;
-        acc[2 * c + 1] += f * v[u][c].y;
+        acc[2 * c] += f * __uint_as_float(v[u][c] << 16);
+        acc[2 * c + 1] += f * __uint_as_float(v[u][c] & 0xffff0000u);
       }
     }
   }
@@ -831,82 +843,52 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   // O^T[c = 16 (wave * CTW + ct) + 4g + i][head 16 nt + l16]; in LDS, row h holds head h with
   // its 16-byte chunks XOR-swizzled by h mod 16 (conflict-free for both the scattered writes
   // here and the row reads below).
-  if (a.nsplit == 1) {
-    // bf16 [64 heads][D] in tile0 (64 rows of RS bytes)
+  // One path for both cases: bf16 [64 heads][D] in tile0 (64 rows of RS bytes), then whole rows
+  // to `out` (normalised, with the sink) or, when the rows are split, to this split's partial
+  // rows (normalised by this split's own sum; its (max, sum) go to ws_ml for the merge).
+  const bool split = a.nsplit > 1;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int hh = hbase + 16 * nt + l16;
-      float M = hm[16 * nt + l16], L = hl[0][16 * nt + l16] + hl[1][16 * nt + l16];
-      const float f = finish_head_s2(sink2[nt], M, L);
-      const float inv = L > 0.f ? f / L : 0.f;
-      if (a.lse && g == 0 && wave == 0 && hh < a.H) a.lse[(int64_t)t * a.H + hh] = lse_of(M, L);
-      uint8_t* hrow = tile0 + (16 * nt + l16) * RS;
-#pragma unroll
-      for (int ct = 0; ct < CTW; ++ct) {
-        const f32x4 o = oacc[ct][nt] * inv;
-        uint2 pk;
-        pk.x = pack_bf16x2(o[0], o[1]);
-        pk.y = pack_bf16x2(o[2], o[3]);
-        const int cb = (16 * (wave * CTW + ct) + 4 * g) * 2;           // byte in the row
-        *(uint2*)(hrow + ((((cb >> 4) ^ l16) << 4) | (cb & 15))) = pk;
-      }
-    }
-    __syncthreads();
-    constexpr int LPH = RS / 16;                     // lanes per head row
-    constexpr int HPI = 64 / LPH;                    // heads per wave instruction
-    i32x4 v[8 / HPI];
-#pragma unroll
-    for (int k = 0; k < 8 / HPI; ++k) {
-      const int hl_ = wave * 8 + k * HPI + lane / LPH, ch = lane % LPH;
-      v[k] = *(const i32x4*)(tile0 + hl_ * RS + ((ch ^ (hl_ & 15)) << 4));
-    }
-#pragma unroll
-    for (int k = 0; k < 8 / HPI; ++k) {
-      const int hl_ = wave * 8 + k * HPI + lane / LPH, ch = lane % LPH;
-      const int hh = hbase + hl_;
-      if (hh < a.H) *(i32x4*)(reinterpret_cast<uint8_t*>(a.out + ((int64_t)t * a.H + hh) * D) + ch * 16) = v[k];
-    }
-  } else {
-    // fp32 partials [64 heads][D]: heads 0..31 in tile0, 32..63 in tile1 (rows of 4D bytes)
-    constexpr int PS = D * 4;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      uint8_t* hrow = (nt < 2 ? tile0 : tile1) + (16 * (nt & 1) + l16) * PS;
-#pragma unroll
-      for (int ct = 0; ct < CTW; ++ct) {
-        const int ch = 4 * (wave * CTW + ct) + g;                       // 16-byte chunk in the row
-        *(f32x4*)(hrow + ((ch ^ l16) << 4)) = oacc[ct][nt];
-      }
-    }
-    if (wave == 0 && lane < 64) {
-      const int hh = hbase + lane;
-      if (hh < a.H) {
+  for (int nt = 0; nt < 4; ++nt) {
+    const int hh = hbase + 16 * nt + l16;
+    float M = hm[16 * nt + l16], L = hl[0][16 * nt + l16] + hl[1][16 * nt + l16];
+    if (split) {
+      if (g == 0 && wave == 0 && hh < a.H) {
         const int64_t prow16 = ((int64_t)(t * a.n_h16 + hh / 16) * a.nsplit + s) * 16 + (hh & 15);
-        a.ws_ml[prow16 * 2 + 0] = hm[lane];
-        a.ws_ml[prow16 * 2 + 1] = hl[0][lane] + hl[1][lane];
+        a.ws_ml[prow16 * 2 + 0] = M;
+        a.ws_ml[prow16 * 2 + 1] = L;
       }
     }
-    __syncthreads();
-    constexpr int LPH = PS / 16;                     // lanes per head row (128 or 32)
-    constexpr int HPW = 8;                           // heads per wave
-    constexpr int NK = HPW * LPH / 64;
-    i32x4 v[NK];
+    const float f = split ? 1.f : finish_head_s2(sink2[nt], M, L);
+    const float inv = L > 0.f ? f / L : 0.f;
+    if (!split && a.lse && g == 0 && wave == 0 && hh < a.H) a.lse[(int64_t)t * a.H + hh] = lse_of(M, L);
+    uint8_t* hrow = tile0 + (16 * nt + l16) * RS;
 #pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      const int fl = k * 64 + lane;                  // flat 16-byte chunk over the wave's rows
-      const int hl_ = wave * HPW + fl / LPH, ch = fl % LPH;
-      v[k] = *(const i32x4*)((hl_ < 32 ? tile0 : tile1) + (hl_ & 31) * PS + ((ch ^ (hl_ & 15)) << 4));
+    for (int ct = 0; ct < CTW; ++ct) {
+      const f32x4 o = oacc[ct][nt] * inv;
+      uint2 pk;
+      pk.x = pack_bf16x2(o[0], o[1]);
+      pk.y = pack_bf16x2(o[2], o[3]);
+      const int cb = (16 * (wave * CTW + ct) + 4 * g) * 2;           // byte in the row
+      *(uint2*)(hrow + ((((cb >> 4) ^ l16) << 4) | (cb & 15))) = pk;
     }
+  }
+  __syncthreads();
+  constexpr int LPH = RS / 16;                       // lanes per head row
+  constexpr int HPI = 64 / LPH;                      // heads per wave instruction
+  i32x4 v[8 / HPI];
 #pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      const int fl = k * 64 + lane;
-      const int hl_ = wave * HPW + fl / LPH, ch = fl % LPH;
-      const int hh = hbase + hl_;
-      if (hh < a.H) {
-        const int64_t prow16 = ((int64_t)(t * a.n_h16 + hh / 16) * a.nsplit + s) * 16 + (hh & 15);
-        *(i32x4*)(reinterpret_cast<uint8_t*>(a.ws_o + prow16 * D) + ch * 16) = v[k];
-      }
-    }
+  for (int k = 0; k < 8 / HPI; ++k) {
+    const int hl_ = wave * 8 + k * HPI + lane / LPH, ch = lane % LPH;
+    v[k] = *(const i32x4*)(tile0 + hl_ * RS + ((ch ^ (hl_ & 15)) << 4));
+  }
+#pragma unroll
+  for (int k = 0; k < 8 / HPI; ++k) {
+    const int hl_ = wave * 8 + k * HPI + lane / LPH, ch = lane % LPH;
+    const int hh = hbase + hl_;
+    if (hh >= a.H) continue;
+    uint16_t* dst = split ? a.ws_o + (((int64_t)(t * a.n_h16 + hh / 16) * a.nsplit + s) * 16 + (hh & 15)) * D
+                          : a.out + ((int64_t)t * a.H + hh) * D;
+    *(i32x4*)(reinterpret_cast<uint8_t*>(dst) + ch * 16) = v[k];
   }
 }
 
@@ -949,7 +931,7 @@ AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos
   p.rows_per_split = (int)(bps * kBlock);
   if (nsplit > 1) {
     const size_t parts = (size_t)N * p.n_h16 * nsplit * 16;
-    p.ws_o_bytes = parts * d * sizeof(float);
+    p.ws_o_bytes = parts * d * sizeof(uint16_t);
     p.ws_ml_bytes = parts * 2 * sizeof(float);
     p.ws_bytes = p.ws_o_bytes + p.ws_ml_bytes;
   }

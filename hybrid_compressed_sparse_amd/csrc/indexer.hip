@@ -51,16 +51,24 @@ __device__ __attribute__((aligned(64))) uint8_t g_ix_zero[1024];
 // async loads, as is the query (64 heads x d_I, shared by the waves); both are stored with the
 // 16-byte chunks of row r at chunk ^ (r mod CPR), which makes the MFMA operand reads below free
 // of bank conflicts.
+template <int DI>
+struct Bf16ScoreLds {
+  static constexpr int RB = DI * 2;                   // bytes per key / query row
+  static constexpr int PAGE = kPageRows * RB;
+  static constexpr int BYTES = 64 * RB + 4 * PAGE;    // q rows, then one key page per wave
+};
+
+// Scores of block (blockIdx.x = query, blockIdx.y = 256-entry chunk) into a.scores. Every
+// thread of the block must call it (it has one barrier); `smem` holds Bf16ScoreLds<DI>::BYTES.
 template <int DI, int MT>
-__global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(IndexArgs a) {
+__device__ __forceinline__ void score_block_bf16(const IndexArgs& a, uint8_t* smem) {
   constexpr int KS = DI / 32;
   constexpr int NT = 4;                  // 4 x 16 entries per wave
-  constexpr int RB = DI * 2;             // bytes per key / query row
+  constexpr int RB = Bf16ScoreLds<DI>::RB;
   constexpr int CPR = RB / 16;           // 16-byte chunks per row
   constexpr int RPI = 1024 / RB;         // rows per 1 KiB async load
-  constexpr int PAGE = kPageRows * RB;
-  __shared__ __attribute__((aligned(16))) uint8_t qs[64 * RB];
-  __shared__ __attribute__((aligned(16))) uint8_t ks_[4][PAGE];
+  constexpr int PAGE = Bf16ScoreLds<DI>::PAGE;
+  uint8_t* qs = smem;
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -88,7 +96,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(IndexAr
   const int e_base = blockIdx.y * 256 + wave * 64;          // first entry of this wave's page
   const bool active = e_base < nv;
   const int pg = active ? page_of(a.keys, seq, e_base) : -1;
-  uint8_t* kl = ks_[wave];
+  uint8_t* kl = smem + 64 * RB + wave * PAGE;
   if (pg >= 0) {
     const uint8_t* page = a.keys.base + (int64_t)pg * PAGE;
 #pragma unroll
@@ -129,6 +137,12 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(IndexAr
     const int e = e_base + r;
     if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = pg >= 0 ? part : kNegInf;
   }
+}
+
+template <int DI, int MT>
+__global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(IndexArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Bf16ScoreLds<DI>::BYTES];
+  score_block_bf16<DI, MT>(a, smem);
 }
 
 // ---------------------------------------------------------------- MXFP4 scores (d_I = 128)
@@ -211,8 +225,10 @@ struct SelShared {
 };
 
 // Clears what radix_kth expects cleared; the caller puts a barrier between this and the call.
+// NT is the block's thread count (a multiple of 64, at least 128) in all the selection helpers.
+template <int NT>
 __device__ __forceinline__ void sel_reset(SelShared& sh) {
-  for (int j = threadIdx.x; j < 256; j += kTopkThreads) sh.hist[0][j] = 0;
+  for (int j = threadIdx.x; j < 256; j += NT) sh.hist[0][j] = 0;
   if (threadIdx.x == 0) {
     sh.kmax = 0u;
     sh.kmin = ~0u;
@@ -231,13 +247,13 @@ struct KthResult {
 // still needed (then every key of that bin is taken, no further digit is needed). Two barriers
 // per pass plus one for the range. Expects sel_reset() state; leaves it reset (ordered by the
 // caller's next barrier).
-template <class KeyOf>
+template <int NT, class KeyOf>
 __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
   const int tid = threadIdx.x, lane = tid & 63;
   // ---- range and count of the participating keys
   uint32_t lmax = 0u, lmin = ~0u;
   unsigned lcnt = 0;
-  for (int i = tid; i < n; i += kTopkThreads) {
+  for (int i = tid; i < n; i += NT) {
     uint32_t key;
     if (key_of(i, key)) {
       lmax = max(lmax, key);
@@ -281,7 +297,7 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
     const int width = min(8, top + 1);
     const int shift = top - width + 1;
     unsigned* hist = sh.hist[pass & 1];
-    for (int i = tid; i < n; i += kTopkThreads) {
+    for (int i = tid; i < n; i += NT) {
       uint32_t key;
       if (key_of(i, key) && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
@@ -309,7 +325,7 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
         run += c[j];
       }
     } else {
-      for (int j = tid - 64; j < 256; j += kTopkThreads - 64) sh.hist[(pass & 1) ^ 1][j] = 0;   // next pass's
+      for (int j = tid - 64; j < 256; j += NT - 64) sh.hist[(pass & 1) ^ 1][j] = 0;   // next pass's
     }
     __syncthreads();
     prefix |= sh.bin << shift;
@@ -320,7 +336,7 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
     // hist[pass & 1] was counted into; clear it for a later pass or call (ordered by the
     // barriers that follow before any reuse)
     if (tid >= 64)
-      for (int j = tid - 64; j < 256; j += kTopkThreads - 64) sh.hist[pass & 1][j] = 0;
+      for (int j = tid - 64; j < 256; j += NT - 64) sh.hist[pass & 1][j] = 0;
     if (cnt_bin == remaining) break;
   }
   if (tid == 0) {                        // range state for a later call
@@ -337,16 +353,16 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
 
 // Select the top-k of n elements (n > k) given key_of(i, key) and id_of(i); writes k ids (and
 // scores) in arbitrary order. Ties at the k-th key go to the smaller ids.
-template <class KeyOf, class IdOf, class Emit>
+template <int NT, class KeyOf, class IdOf, class Emit>
 __device__ void block_topk(SelShared& sh, int n, int k, KeyOf key_of, IdOf id_of, Emit emit) {
-  const KthResult r = radix_kth(sh, n, (unsigned)k, key_of);
+  const KthResult r = radix_kth<NT>(sh, n, (unsigned)k, key_of);
   // ties (only possible when every bit was resolved: mask = ~0): of the keys equal to the k-th,
   // take the r.need smallest ids, i.e. the largest ~id
   bool tie_break = r.n_eq > r.need;
   KthResult r2{};
   if (tie_break) {
     __syncthreads();
-    r2 = radix_kth(
+    r2 = radix_kth<NT>(
         sh, n, r.need,
         [&](int i, uint32_t& key) {
           uint32_t kk;
@@ -359,7 +375,7 @@ __device__ void block_topk(SelShared& sh, int n, int k, KeyOf key_of, IdOf id_of
   __syncthreads();
   // one counter update per wave: lanes take consecutive slots from the wave's base
   const int lane = threadIdx.x & 63;
-  for (int i0 = threadIdx.x & ~63; i0 < n; i0 += kTopkThreads) {
+  for (int i0 = threadIdx.x & ~63; i0 < n; i0 += NT) {
     const int i = i0 + lane;
     uint32_t key = 0;
     bool take = i < n && key_of(i, key);
@@ -405,9 +421,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_single_kernel(IndexArgs a, 
   }
 #pragma unroll 8
   for (int i = threadIdx.x; i < nv; i += kTopkThreads) kl[i] = f32_order_key(sc[i]);
-  sel_reset(sh);
+  sel_reset<kTopkThreads>(sh);
   __syncthreads();
-  block_topk(
+  block_topk<kTopkThreads>(
       sh, nv, k, [&](int i, uint32_t& key) { key = kl[i]; return true; },
       [&](int i) { return i; },
       [&](unsigned slot, int id, uint32_t key) {
@@ -441,9 +457,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage1_kernel(IndexArgs a, 
   }
 #pragma unroll 8
   for (int i = threadIdx.x; i < n; i += kTopkThreads) kl[i] = f32_order_key(sc[i]);
-  sel_reset(sh);
+  sel_reset<kTopkThreads>(sh);
   __syncthreads();
-  block_topk(
+  block_topk<kTopkThreads>(
       sh, n, k, [&](int i, uint32_t& key) { key = kl[i]; return true; },
       [&](int i) { return lo + i; },
       [&](unsigned slot, int id, uint32_t key) {
@@ -476,9 +492,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage2_kernel(IndexArgs a, 
   }
   const uint32_t* ck = ckey + (int64_t)t * nchunks * k;
   const int32_t* ci = cid + (int64_t)t * nchunks * k;
-  sel_reset(sh);
+  sel_reset<kTopkThreads>(sh);
   __syncthreads();
-  block_topk(
+  block_topk<kTopkThreads>(
       sh, nchunks * k,
       k, [&](int i, uint32_t& key) { key = ck[i]; return ci[i] >= 0; }, [&](int i) { return ci[i]; },
       [&](unsigned slot, int id, uint32_t key) {

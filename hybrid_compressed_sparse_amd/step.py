@@ -46,8 +46,7 @@ class PathStep:
             at_ws = sparse_mla_prefill_workspace_size(s.N, s.H, s.d, s.window, s.m, s.topk, s.P0)
         else:
             at_ws = sparse_mla_workspace_size(s.N, s.H, s.d, s.window, s.m, s.topk, s.max_pos)
-        # zero-filled once: the split counters in it must start at zero (calls leave them zero)
-        self.at_ws = torch.zeros(max(at_ws, 1), dtype=torch.uint8, device=device)
+        self.at_ws = torch.empty(max(at_ws, 1), dtype=torch.uint8, device=device)
 
     def compress(self, kv, score, cu_new, start_pos, state, comp, max_new, ape=None, dbg=None):
         compress_kv(kv, score, cu_new, start_pos, state, comp, self.shape.m, ape=ape, dbg=dbg,
@@ -71,6 +70,9 @@ class PathStep:
     def run(self, *, q, swa, comp, q_seq, q_pos, c_kv, c_score, c_cu, c_start, c_state, c_max_new,
             ix_q=None, ix_q_scale=None, ix_w=None, ix_keys=None, ape=None, sink=None,
             dbg: Optional[torch.Tensor] = None):
+        """The step, in order on the current stream. (Running the compressor on a second stream,
+        overlapped with the indexer, measured slower inside a captured graph on MI355X: the
+        cross-stream joins cost more than the compressor.)"""
         self.compress(c_kv, c_score, c_cu, c_start, c_state, comp, c_max_new, ape=ape, dbg=dbg)
         if self.shape.topk:
             self.select(ix_q, ix_q_scale, ix_w, ix_keys, q_seq, q_pos)

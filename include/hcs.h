@@ -137,7 +137,9 @@ hcs_status hcs_compress_kv(const void* kv, const void* score, int in_dtype, int6
 /* out_idx  [N, topk] int32: the selected entry ids, in no particular order, -1 at the    */
 /*          tail when fewer than topk entries are visible.                                */
 /* out_score [N, topk] float32 scores of out_idx (unspecified where out_idx is -1), or NULL.*/
-/* ws       workspace of at least hcs_index_topk_workspace_size(N, max_pos, m, topk) bytes. */
+/* ws       workspace of at least hcs_index_topk_workspace_size(N, max_pos, m, topk) bytes, */
+/*          256-byte aligned (score scratch; no initial contents needed). Calls that overlap */
+/*          in time must not share it.                                                     */
 /* Constraints: H_I in 1..64, d_I in {32, 64, 128} (bf16) or d_I == 128 (mxfp4),           */
 /* 1 <= topk <= 4096.                                                                     */
 size_t hcs_index_topk_workspace_size(int N, int max_pos, int m, int topk);
