@@ -18,8 +18,10 @@
 // The C layout puts 4 heads x 1 entry in each lane: ReLU, the head weights and the sum over
 // heads are done in registers plus two cross-lane shuffles.
 //
-// Top-k: exact radix select on order-preserving 32-bit keys of the fp32 scores, 8 bits per
-// pass from the top, with LDS histograms in one 1024-thread workgroup per query; ties at the
+// Top-k: exact radix select on order-preserving 32-bit keys of the fp32 scores, 11 bits per
+// pass below the keys' common leading bits, with LDS histograms in one 1024-thread workgroup
+// per query (usually one pass: it stops when the k-th key's bin holds exactly the keys still
+// needed); ties at the
 // threshold are broken towards smaller entry ids by a second radix select on the ids. Queries
 // with more than 32768 visible entries go through two stages: every 16384-entry chunk keeps
 // its own exact top-k, then the chunk winners are selected again (exact: an entry of the
@@ -217,18 +219,45 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexA
 }
 
 // ---------------------------------------------------------------- radix select
+constexpr int kDigitBits = 11;                 // radix digit: 2048 bins
+constexpr int kBins = 1 << kDigitBits;
+
 struct SelShared {
-  unsigned hist[2][256];                 // pass p counts into hist[p & 1]; the other is cleared
+  unsigned hist[2][kBins];               // pass p counts into hist[p & 1]; the other is cleared
+  unsigned wsum[16];                     // per-wave bin totals of a pass
   unsigned bin, above, cnt_bin;
   unsigned kmax, kmin, count;            // range and number of the participating keys
   unsigned out_count;
 };
 
+// Wave-wide reductions through DPP row operations (no LDS round trips); every lane gets the result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return ~wave_max_u32(~v);
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Clears what radix_kth expects cleared; the caller puts a barrier between this and the call.
-// NT is the block's thread count (a multiple of 64, at least 128) in all the selection helpers.
+// NT is the block's thread count (a multiple of 64, 256..1024) in all the selection helpers.
 template <int NT>
 __device__ __forceinline__ void sel_reset(SelShared& sh) {
-  for (int j = threadIdx.x; j < 256; j += NT) sh.hist[0][j] = 0;
+  for (int j = threadIdx.x; j < kBins; j += NT) sh.hist[0][j] = 0;
   if (threadIdx.x == 0) {
     sh.kmax = 0u;
     sh.kmin = ~0u;
@@ -243,13 +272,15 @@ struct KthResult {
 
 // Radix select of the k-th largest key among the participating elements (1 <= k <= their
 // number). Keys first agree on a common leading part (the range min ^ max), so the digits start
-// below it: 8 bits per pass, stopping once the bin holding the k-th key holds exactly the keys
-// still needed (then every key of that bin is taken, no further digit is needed). Two barriers
-// per pass plus one for the range. Expects sel_reset() state; leaves it reset (ordered by the
-// caller's next barrier).
+// below it: 11 bits per pass, stopping once the bin holding the k-th key holds exactly the keys
+// still needed (then every key of that bin is taken, no further digit is needed; with 2048 bins
+// this is usually the first pass). One barrier for the range, three per pass. Expects
+// sel_reset() state; leaves it reset (ordered by the caller's next barrier).
 template <int NT, class KeyOf>
 __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
-  const int tid = threadIdx.x, lane = tid & 63;
+  static_assert(NT % 64 == 0 && NT >= 256 && NT <= 1024 && kBins % NT == 0, "block size");
+  constexpr int BPT = kBins / NT;        // bins per thread in the scan
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // ---- range and count of the participating keys
   uint32_t lmax = 0u, lmin = ~0u;
   unsigned lcnt = 0;
@@ -261,12 +292,9 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
       ++lcnt;
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, o, 64));
-    lmin = min(lmin, (uint32_t)__shfl_xor((int)lmin, o, 64));
-    lcnt += (unsigned)__shfl_xor((int)lcnt, o, 64);
-  }
+  lmax = wave_max_u32(lmax);
+  lmin = wave_min_u32(lmin);
+  lcnt = wave_sum_u32(lcnt);
   if (lane == 0) {
     atomicMax(&sh.kmax, lmax);
     atomicMin(&sh.kmin, lmin);
@@ -294,38 +322,38 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
   uint32_t prefix = kmax & mask;
   unsigned remaining = k, cnt_bin = total;
   for (int pass = 0; top >= 0; ++pass) {
-    const int width = min(8, top + 1);
+    const int width = min(kDigitBits, top + 1);
     const int shift = top - width + 1;
     unsigned* hist = sh.hist[pass & 1];
     for (int i = tid; i < n; i += NT) {
       uint32_t key;
-      if (key_of(i, key) && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      if (key_of(i, key) && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (kBins - 1)], 1u);
     }
     __syncthreads();
-    if (tid < 64) {
-      // lane l owns bins 255-4l .. 252-4l (descending)
-      unsigned c[4], tot = 0;
+    // thread i owns bins kBins-1-BPT*i .. kBins-BPT*i (descending); exclusive prefix of the
+    // threads' totals = the wave's prefix (from ballots of the totals' bits) + earlier waves'
+    unsigned c[BPT], tot = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = hist[255 - 4 * tid - j];
-        tot += c[j];
+    for (int j = 0; j < BPT; ++j) {
+      c[j] = hist[kBins - 1 - BPT * tid - j];
+      tot += c[j];
+    }
+    const uint64_t below = (1ull << lane) - 1;
+    unsigned run = 0;
+#pragma unroll
+    for (int b = 0; b < 17; ++b) run += (unsigned)__popcll(__ballot((tot >> b) & 1u) & below) << b;
+    if (lane == 63) sh.wsum[wave] = run + tot;
+    for (int j = tid; j < kBins; j += NT) sh.hist[(pass & 1) ^ 1][j] = 0;   // the next pass's
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) run += sh.wsum[w];
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      if (run < remaining && run + c[j] >= remaining) {
+        sh.bin = kBins - 1 - BPT * tid - j;
+        sh.above = run;
+        sh.cnt_bin = c[j];
       }
-      // exclusive prefix of the lanes' totals (< 2^17) from ballots of their bits
-      const uint64_t below = (1ull << tid) - 1;
-      unsigned run = 0;
-#pragma unroll
-      for (int b = 0; b < 17; ++b) run += (unsigned)__popcll(__ballot((tot >> b) & 1u) & below) << b;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (run < remaining && run + c[j] >= remaining) {
-          sh.bin = 255 - 4 * tid - j;
-          sh.above = run;
-          sh.cnt_bin = c[j];
-        }
-        run += c[j];
-      }
-    } else {
-      for (int j = tid - 64; j < 256; j += NT - 64) sh.hist[(pass & 1) ^ 1][j] = 0;   // next pass's
+      run += c[j];
     }
     __syncthreads();
     prefix |= sh.bin << shift;
@@ -335,8 +363,7 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
     top = shift - 1;
     // hist[pass & 1] was counted into; clear it for a later pass or call (ordered by the
     // barriers that follow before any reuse)
-    if (tid >= 64)
-      for (int j = tid - 64; j < 256; j += NT - 64) sh.hist[pass & 1][j] = 0;
+    for (int j = tid; j < kBins; j += NT) hist[j] = 0;
     if (cnt_bin == remaining) break;
   }
   if (tid == 0) {                        // range state for a later call
