@@ -196,28 +196,31 @@ struct Fp8Stage {
 
   // Issue the load of this lane's 16-byte piece of the row with table entry `e` (wave-uniform,
   // so the row address is computed once in scalar registers): lanes 0..27 take 16 latent
-  // codes, lanes 28..35 8 rope values, the others nothing useful.
-  __device__ static __forceinline__ void load(const AttnArgs& a, uint32_t e, int lane, i32x4& v,
-                                              float& sc) {
+  // codes, lanes 28..35 8 rope values, the others nothing useful. `se` receives the raw UE8M0
+  // byte of the lane's 64-value block. Both loads are unconditional (a row that does not take
+  // part reads the zero row), so a wave's loads of a block all stay in flight together.
+  __device__ static __forceinline__ void load(const uint8_t* swa_base, const uint8_t* comp_base,
+                                              uint32_t e, int lane, i32x4& v, int& se) {
     e = (uint32_t)__builtin_amdgcn_readfirstlane((int)e);
     const bool ok = e != kNoRow;
     const uint32_t ridx = e & 0x7fffffffu;
-    const uint8_t* page = ok ? ((e >> 31) ? a.comp.base : a.swa.base) + (size_t)(ridx >> 6) * PB
-                             : g_zero_row;
-    const int slot = ok ? (int)(ridx & 63) : 0;
+    const uint8_t* page = ((e >> 31) ? comp_base : swa_base) + (size_t)(ridx >> 6) * PB;
+    const int slot = (int)(ridx & 63);
     const int off = lane < 28 ? kFp8PageCodes + slot * kFp8Latent + lane * 16
                               : (lane < 36 ? kFp8PageRope + slot * (kFp8Rope * 2) + (lane - 28) * 16
                                            : kFp8PageCodes + slot * kFp8Latent);
-    v = ok ? *(const i32x4*)(page + off) : *(const i32x4*)(g_zero_row + (lane & 31) * 16);
-    const int se = ok ? page[kFp8PageScales + slot * 8 + (min(lane, 27) >> 2)] : 0;
-    sc = ok && lane < 28 ? __builtin_ldexpf(1.f, se - 127) : 1.f;
+    const uint8_t* src = ok ? page + off : g_zero_row + (lane & 31) * 16;
+    const uint8_t* ssrc = ok ? page + kFp8PageScales + slot * 8 + (min(lane, 27) >> 2) : g_zero_row;
+    v = *(const i32x4*)src;
+    se = *ssrc;
   }
 
   // Write this lane's piece of row `r` (tile-local) into the LDS tile, chunks swizzled by `sw`
-  // (the bf16 row is 1 KiB: latent chunks 0..55, rope chunks 56..63).
+  // (the bf16 row is 1 KiB: latent chunks 0..55, rope chunks 56..63); se is the block's UE8M0.
   __device__ static __forceinline__ void store(uint8_t* tile, int r, int sw, int lane,
-                                               const i32x4& v, float sc) {
+                                               const i32x4& v, int se) {
     uint8_t* row = tile + r * RS;
+    const float sc = __builtin_ldexpf(1.f, se - 127);
     if (lane < 28) {
       i32x4 lo4, hi4;
       lo4.x = e4m3x2_to_bf16x2<false>(v.x, sc);
@@ -351,14 +354,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_fp8_kernel(AttnArgs a) {
   const int nblk = (n_rows + BT - 1) / BT;
 
   i32x4 pre[NLD];
-  float psc[NLD];
+  int psc[NLD];
   __syncthreads();
 
   // load this wave's rows of block b into registers (written to LDS at the start of block b)
-  auto issue = [&](int b) {
+  const uint8_t* swa_base = a.swa.base;
+  const uint8_t* comp_base = a.comp.base;
+  auto issue = [&](int b) __attribute__((always_inline)) {
     const uint32_t* rt = rowtab + b * BT + wave * WR;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) S::load(a, rt[i], lane, pre[i], psc[i]);
+    for (int i = 0; i < NLD; ++i) S::load(swa_base, comp_base, rt[i], lane, pre[i], psc[i]);
   };
   if (nblk > 0) issue(0);
 
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_fp8_kernel(AttnArgs a) {
   // Shared reference max: every wave uses the same m_ref for the whole block, so each can
   // write its rows' probabilities for the column-split PV. A wave whose scores exceed
   // m_ref + kLazyBlock raises a flag; only then do the waves exchange maxima and rescale.
-  auto block = [&](int b, uint8_t* T, __bf16* P, int* F) {
+  auto block = [&](int b, uint8_t* T, __bf16* P, int* F) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) S::store(T, wave * WR + i, swz_dec(i), lane, pre[i], psc[i]);
     lds_barrier();                                       // block b is in LDS

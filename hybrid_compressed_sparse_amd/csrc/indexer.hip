@@ -9,7 +9,8 @@
 // Scores: one workgroup scores 256 (bf16) or 512 (MXFP4) consecutive entries of one query.
 // The query's heads are the MFMA M dimension. bf16: a wave's 64 entries are one page of the
 // cache, copied whole into LDS with async loads (as is the query), then read in MFMA operand
-// order. MXFP4: each lane streams 16-byte pieces of key rows straight from the paged cache.
+// order. MXFP4: the same, two pages per wave, and the cache's 32-value blocks are the MFMA
+// operands as stored.
 //   bf16 : v_mfma_f32_16x16x32_bf16, K = d_I in steps of 32;
 //   MXFP4: v_mfma_scale_f32_16x16x128_f8f6f4 with both operands e2m1 and the UE8M0 block
 //          scales as the instruction's scale operands; the documented cache layout (32
@@ -148,73 +149,102 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(IndexAr
 }
 
 // ---------------------------------------------------------------- MXFP4 scores (d_I = 128)
+// Block = 512 entries of one query: 4 waves x two 64-entry pages. A page (64 x 64 B codes, then
+// 64 x 4 UE8M0 bytes) is one contiguous region of the cache; it is copied into LDS with async
+// loads (the 16-byte code chunks of entry r stored at chunk ^ ((r >> 2) & 3), which makes the
+// operand reads conflict-free), as are the query's codes. Heads are the M dimension of
+// v_mfma_scale_f32_16x16x128_f8f6f4, entries the N dimension; a lane's operand is the 16 bytes
+// (32 e2m1 values) of one 32-value block and its scale byte.
 template <int MT>
 __global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexArgs a) {
   constexpr int DI = 128;
-  constexpr int NT = 8;                  // 8 x 16 entries per wave
-  constexpr int PAGE = kPageRows * (DI / 2 + DI / kMxBlock);     // 4352
-  constexpr int SCALES = kPageRows * (DI / 2);                   // scale region offset
+  constexpr int CB = DI / 2;                                     // code bytes per row
+  constexpr int SB = DI / kMxBlock;                              // scale bytes per row
+  constexpr int PAGE = kPageRows * (CB + SB);                    // 4352
+  constexpr int SCALES = kPageRows * CB;                         // scale region offset
+  constexpr int PPW = 2;                                         // pages per wave
+  __shared__ __attribute__((aligned(16))) uint8_t qc[64 * CB];
+  __shared__ __attribute__((aligned(16))) uint8_t kb[4][PPW][PAGE];
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  int seq, nv;
-  query_of(a, t, seq, nv);
-  const int e_base = blockIdx.y * (kScoreThreads / 64) * NT * 16 + wave * NT * 16;
-  if (e_base >= nv) return;
-
-  i32x8 qa[MT];
+  // query codes: wave w copies heads 16w .. 16w+15 (heads >= H_I read zeros)
+  {
+    const int h = 16 * wave + lane / 4, c = lane % 4;
+    const uint8_t* src = h < a.H_I ? a.q + ((int64_t)t * a.H_I + h) * CB + ((c ^ ((h >> 2) & 3)) << 4)
+                                   : g_ix_zero + lane * 16;
+    __builtin_amdgcn_global_load_lds((const void*)src,
+                                     (__attribute__((address_space(3))) void*)(qc + 16 * wave * CB), 16, 0, 0);
+  }
   int qs[MT];
   float wreg[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int h = mt * 16 + l16;
-    i32x4 v = {0, 0, 0, 0};
-    int sc = 127;
-    if (h < a.H_I) {
-      v = *(const i32x4*)(a.q + ((int64_t)t * a.H_I + h) * (DI / 2) + 16 * g);
-      sc = a.q_scale[((int64_t)t * a.H_I + h) * (DI / kMxBlock) + g];
-    }
-    qa[mt] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-    qs[mt] = sc;
+    qs[mt] = h < a.H_I ? a.q_scale[((int64_t)t * a.H_I + h) * SB + g] : 127;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hw = mt * 16 + 4 * g + i;
       wreg[mt][i] = hw < a.H_I ? a.w[(int64_t)t * a.H_I + hw] : 0.f;
     }
   }
-
-  i32x4 kc[NT];
-  int ksc[NT];
-  bool kval[NT];
+  int seq, nv;
+  query_of(a, t, seq, nv);
+  const int e_base = blockIdx.y * (4 * PPW * 64) + wave * (PPW * 64);   // first entry of the wave
+  // the wave's page ids: lane p < PPW reads page p's table entry
+  int my_pg = -1;
+  if (lane < PPW && e_base + 64 * lane < nv) {
+    const int pg = __ldg(a.keys.pt + (int64_t)seq * a.keys.pt_stride + (e_base >> 6) + lane);
+    my_pg = pg >= 0 && pg < a.keys.num_pages ? pg : -1;
+  }
+  int pgs[PPW];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int e = e_base + nt * 16 + l16;
-    const int pg = e < nv ? page_of(a.keys, seq, e) : -1;
-    kval[nt] = pg >= 0;
-    kc[nt] = i32x4{0, 0, 0, 0};
-    ksc[nt] = 127;
-    if (pg >= 0) {
-      const uint8_t* pb = a.keys.base + (int64_t)pg * PAGE;
-      kc[nt] = *(const i32x4*)(pb + (e & 63) * (DI / 2) + 16 * g);
-      ksc[nt] = pb[SCALES + (e & 63) * (DI / kMxBlock) + g];
+  for (int p = 0; p < PPW; ++p) {
+    pgs[p] = __builtin_amdgcn_readlane(my_pg, p);
+    if (pgs[p] < 0) continue;
+    const uint8_t* page = a.keys.base + (int64_t)pgs[p] * PAGE;
+    uint8_t* dst = kb[wave][p];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {                                 // codes: 16 entries per load
+      const int r = 16 * i + lane / 4, c = lane % 4;
+      __builtin_amdgcn_global_load_lds((const void*)(page + r * CB + ((c ^ ((r >> 2) & 3)) << 4)),
+                                       (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
     }
+    if (lane < 16)                                                // scales: 256 bytes
+      __builtin_amdgcn_global_load_lds((const void*)(page + SCALES + lane * 16),
+                                       (__attribute__((address_space(3))) void*)(dst + SCALES), 16, 0, 0);
+  }
+  __syncthreads();                                                // every copy has landed
+  if (e_base >= nv) return;
+  i32x8 qa[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int h = mt * 16 + l16;
+    const i32x4 v = *(const i32x4*)(qc + h * CB + ((g ^ ((h >> 2) & 3)) << 4));
+    qa[mt] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
   }
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const i32x8 kb = {kc[nt].x, kc[nt].y, kc[nt].z, kc[nt].w, 0, 0, 0, 0};
-    float part = 0.f;
+  for (int p = 0; p < PPW; ++p) {
+    const uint8_t* kp = kb[wave][p];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kb, acc, 4, 4, 0, qs[mt], 0,
-                                                              ksc[nt]);
+    for (int nt = 0; nt < 4; ++nt) {
+      const int r = nt * 16 + l16;
+      const i32x4 kc = *(const i32x4*)(kp + r * CB + ((g ^ ((r >> 2) & 3)) << 4));
+      const int ksc = kp[SCALES + r * SB + g];
+      const i32x8 kbv = {kc.x, kc.y, kc.z, kc.w, 0, 0, 0, 0};
+      float part = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part += wreg[mt][i] * fmaxf(acc[i], 0.f);
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kbv, acc, 4, 4, 0, qs[mt], 0, ksc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += wreg[mt][i] * fmaxf(acc[i], 0.f);
+      }
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      const int e = e_base + 64 * p + r;
+      if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = pgs[p] >= 0 ? part : kNegInf;
     }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
-    const int e = e_base + nt * 16 + l16;
-    if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = kval[nt] ? part : kNegInf;
   }
 }
 
@@ -504,6 +534,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage2_kernel(IndexArgs a, 
                                                                    int32_t* out_idx,
                                                                    float* out_score) {
   __shared__ SelShared sh;
+  __shared__ uint32_t kl[kSingleMax];
   const int t = blockIdx.x;
   int seq, nv;
   query_of(a, t, seq, nv);
@@ -519,17 +550,31 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage2_kernel(IndexArgs a, 
   }
   const uint32_t* ck = ckey + (int64_t)t * nchunks * k;
   const int32_t* ci = cid + (int64_t)t * nchunks * k;
+  const int n = nchunks * k;
+  auto emit = [&](unsigned slot, int id, uint32_t key) {
+    if (slot < (unsigned)k) {
+      oi[slot] = id;
+      if (os) os[slot] = order_key_f32(key);
+    }
+  };
+  if (n <= kSingleMax) {
+    // keys in LDS, read once. A padding candidate (id -1) has key 0, below every real key (the
+    // key of any score, -inf included, is larger), and at least k real candidates exist here
+    // (more than kSingleMax entries are visible), so padding is never selected.
+#pragma unroll 8
+    for (int i = threadIdx.x; i < n; i += kTopkThreads) kl[i] = ck[i];
+    sel_reset<kTopkThreads>(sh);
+    __syncthreads();
+    block_topk<kTopkThreads>(
+        sh, n, k, [&](int i, uint32_t& key) { key = kl[i]; return true; }, [&](int i) { return ci[i]; },
+        emit);
+    return;
+  }
   sel_reset<kTopkThreads>(sh);
   __syncthreads();
   block_topk<kTopkThreads>(
-      sh, nchunks * k,
-      k, [&](int i, uint32_t& key) { key = ck[i]; return ci[i] >= 0; }, [&](int i) { return ci[i]; },
-      [&](unsigned slot, int id, uint32_t key) {
-        if (slot < (unsigned)k) {
-          oi[slot] = id;
-          if (os) os[slot] = order_key_f32(key);
-        }
-      });
+      sh, n, k, [&](int i, uint32_t& key) { key = ck[i]; return ci[i] >= 0; }, [&](int i) { return ci[i]; },
+      emit);
 }
 
 }  // namespace
@@ -550,7 +595,7 @@ hipError_t launch_index_scores(const IndexArgs& a, int fmt, hipStream_t stream) 
   if (a.N == 0 || a.nv_cap == 0) return hipSuccess;
   const int MT = (a.H_I + 15) / 16;
   if (fmt == HCS_FMT_MXFP4) {
-    const int per_wg = (kScoreThreads / 64) * 8 * 16;
+    const int per_wg = 512;
     dim3 grid(a.N, (a.nv_cap + per_wg - 1) / per_wg);
     switch (MT) {
       case 1: hipLaunchKernelGGL((index_score_mxfp4_kernel<1>), grid, dim3(kScoreThreads), 0, stream, a); break;
