@@ -139,11 +139,19 @@ hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w,
   a.nv_cap = (max_pos + 1) / m;
   a.scores = static_cast<float*>(ws);
   a.score_stride = (int64_t)(plan.score_bytes / sizeof(float) / N);
+  a.topk = topk;
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  if (plan.large) {
+    a.blk_thr = reinterpret_cast<uint32_t*>(w8 + plan.thr_off);
+    a.cand_count = reinterpret_cast<unsigned*>(w8 + plan.cnt_off);
+    a.thr_stride = plan.thr_stride;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hcs::launch_index_scores(a, keys.fmt, st);
   if (e != hipSuccess) return hip_status(e, "index_topk scores");
-  void* cand = static_cast<uint8_t*>(ws) + (plan.score_bytes + 255) / 256 * 256;
-  return hip_status(hcs::launch_topk(a, plan, topk, out_idx, out_score, cand, st), "index_topk select");
+  const int blk_entries = keys.fmt == HCS_FMT_MXFP4 ? 512 : 256;   // entries per scoring block
+  return hip_status(hcs::launch_topk(a, plan, topk, out_idx, out_score, w8, blk_entries, st),
+                    "index_topk select");
 }
 
 // ------------------------------------------------------------------------------ attention

@@ -24,9 +24,11 @@
 // per query (usually one pass: it stops when the k-th key's bin holds exactly the keys still
 // needed); ties at the
 // threshold are broken towards smaller entry ids by a second radix select on the ids. Queries
-// with more than 32768 visible entries go through two stages: every 16384-entry chunk keeps
-// its own exact top-k, then the chunk winners are selected again (exact: an entry of the
-// global top-k is always in its chunk's top-k).
+// that may see more than 32768 entries are filtered first: every full scoring block also
+// records the kb-th largest of its scores (kb = ceil(k / full blocks)); the smallest of these
+// is a lower bound of the query's k-th largest score, so keeping only the scores at or above it
+// loses nothing (a filter launch appends them as candidates), and the select then runs over the
+// few candidates left.
 #include "kernels.h"
 
 namespace hcs {
@@ -35,7 +37,6 @@ namespace {
 
 constexpr int kScoreThreads = 256;
 constexpr int kTopkThreads = 1024;
-constexpr int kChunk = 16384;           // stage-1 chunk of the two-stage select
 constexpr int kSingleMax = 32768;       // largest n_visible selected in one stage
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -43,6 +44,82 @@ __device__ __forceinline__ void query_of(const IndexArgs& a, int t, int& seq, in
   seq = __ldg(a.q_seq + t);
   const int pos = min(__ldg(a.q_pos + t), a.pos_cap);
   nv = min((pos + 1) / a.m, a.nv_cap);
+}
+
+// ---------------------------------------------------------------- block thresholds
+// A lower bound of a query's k-th largest score that every scoring block can compute alone:
+// if each of the F full blocks (E entries each) contributes its kb = ceil(k / F) largest keys,
+// those F*kb >= k keys are all >= T = min over the full blocks of their kb-th largest key, so
+// the k-th largest key of the query is >= T, and selecting among the keys >= T is exact.
+constexpr int kMaxKb = 32;                      // larger kb: no bound (T = 0, every key kept)
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v);
+
+// One block's kb-th largest key (kb <= kMaxKb) over its waves' keys: lane L of wave w holds
+// keys[0..NS) (0 for none; every entry held by exactly one lane). Returns the result in every
+// thread. `wbest` is LDS of NW * kMaxKb words. Contains one barrier; call from all threads.
+template <int NS, int NW>
+__device__ __forceinline__ uint32_t block_kth_key(uint32_t (&keys)[NS], int kb, uint32_t* wbest,
+                                                  uint32_t* result) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int it = 0; it < kb; ++it) {
+    uint32_t lm = 0;
+    int li = -1;
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      if (keys[j] > lm) {
+        lm = keys[j];
+        li = j;
+      }
+    const uint32_t wm = wave_max_u32(lm);
+    const uint64_t who = __ballot(li >= 0 && lm == wm);
+    const bool mine = who != 0 && lane == (int)__builtin_ctzll(who);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) keys[j] = mine && j == li ? 0u : keys[j];
+    if (lane == 0) wbest[wave * kMaxKb + it] = wm;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    constexpr int PER = (NW * kMaxKb + 63) / 64;
+    uint32_t v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = lane + 64 * j, w = i / kMaxKb, it = i % kMaxKb;
+      v[j] = w < NW && it < kb ? wbest[i] : 0u;
+    }
+    uint32_t kth = 0;
+    for (int it = 0; it < kb; ++it) {
+      uint32_t lm = 0;
+      int li = -1;
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (v[j] > lm) {
+          lm = v[j];
+          li = j;
+        }
+      kth = wave_max_u32(lm);
+      const uint64_t who = __ballot(li >= 0 && lm == kth);
+      const bool mine = who != 0 && lane == (int)__builtin_ctzll(who);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) v[j] = mine && j == li ? 0u : v[j];
+    }
+    if (lane == 0) *result = kth;
+  }
+  __syncthreads();
+  return *result;
+}
+
+// Scoring blocks call this after writing their scores when a.blk_thr is set: E entries per
+// block, `keys` as for block_kth_key. Writes the block's threshold when the block is full.
+template <int NS, int NW, int E>
+__device__ __forceinline__ void write_block_threshold(const IndexArgs& a, int nv, uint32_t (&keys)[NS],
+                                                      uint32_t* wbest, uint32_t* result) {
+  const int full = nv / E;                             // full blocks of this query
+  if (full == 0 || (int)blockIdx.y >= full) return;    // uniform over the block
+  const int kb = (a.topk + full - 1) / full;
+  if (kb > kMaxKb) return;                             // the filter keeps every key then
+  const uint32_t kth = block_kth_key<NS, NW>(keys, kb, wbest, result);
+  if (threadIdx.x == 0) a.blk_thr[(int64_t)blockIdx.x * a.thr_stride + blockIdx.y] = kth;
 }
 
 // ---------------------------------------------------------------- bf16 scores
@@ -64,7 +141,7 @@ struct Bf16ScoreLds {
 // Scores of block (blockIdx.x = query, blockIdx.y = 256-entry chunk) into a.scores. Every
 // thread of the block must call it (it has one barrier); `smem` holds Bf16ScoreLds<DI>::BYTES.
 template <int DI, int MT>
-__device__ __forceinline__ void score_block_bf16(const IndexArgs& a, uint8_t* smem) {
+__device__ __forceinline__ void score_block_bf16(const IndexArgs& a, uint8_t* smem, uint32_t (&tkeys)[4]) {
   constexpr int KS = DI / 32;
   constexpr int NT = 4;                  // 4 x 16 entries per wave
   constexpr int RB = Bf16ScoreLds<DI>::RB;
@@ -110,6 +187,8 @@ __device__ __forceinline__ void score_block_bf16(const IndexArgs& a, uint8_t* sm
     }
   }
   __syncthreads();                                    // every wave's copies have landed
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) tkeys[nt] = 0u;
   if (!active) return;
   bf16x8 qreg[MT][KS];
 #pragma unroll
@@ -138,14 +217,24 @@ __device__ __forceinline__ void score_block_bf16(const IndexArgs& a, uint8_t* sm
     part += __shfl_xor(part, 16, 64);
     part += __shfl_xor(part, 32, 64);
     const int e = e_base + r;
-    if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = pg >= 0 ? part : kNegInf;
+    const float sv = pg >= 0 ? part : kNegInf;
+    if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = sv;
+    tkeys[nt] = g == 0 && e < nv ? f32_order_key(sv) : 0u;
   }
 }
 
 template <int DI, int MT>
 __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(IndexArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Bf16ScoreLds<DI>::BYTES];
-  score_block_bf16<DI, MT>(a, smem);
+  __shared__ uint32_t wbest[4 * kMaxKb + 1];
+  uint32_t tkeys[4];
+  if (a.cand_count && blockIdx.y == 0 && threadIdx.x == 0) a.cand_count[blockIdx.x] = 0u;
+  score_block_bf16<DI, MT>(a, smem, tkeys);
+  if (a.blk_thr) {
+    int seq, nv;
+    query_of(a, blockIdx.x, seq, nv);
+    write_block_threshold<4, 4, 256>(a, nv, tkeys, wbest, wbest + 4 * kMaxKb);
+  }
 }
 
 // ---------------------------------------------------------------- MXFP4 scores (d_I = 128)
@@ -168,6 +257,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexA
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
+  if (a.cand_count && blockIdx.y == 0 && threadIdx.x == 0) a.cand_count[t] = 0u;
   // query codes: wave w copies heads 16w .. 16w+15 (heads >= H_I read zeros)
   {
     const int h = 16 * wave + lane / 4, c = lane % 4;
@@ -215,7 +305,10 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexA
                                        (__attribute__((address_space(3))) void*)(dst + SCALES), 16, 0, 0);
   }
   __syncthreads();                                                // every copy has landed
-  if (e_base >= nv) return;
+  uint32_t tkeys[PPW * 4];
+#pragma unroll
+  for (int j = 0; j < PPW * 4; ++j) tkeys[j] = 0u;
+  if (e_base < nv) {
   i32x8 qa[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -243,8 +336,15 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexA
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);
       const int e = e_base + 64 * p + r;
-      if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = pgs[p] >= 0 ? part : kNegInf;
+      const float sv = pgs[p] >= 0 ? part : kNegInf;
+      if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = sv;
+      tkeys[p * 4 + nt] = g == 0 && e < nv ? f32_order_key(sv) : 0u;
     }
+  }
+  }
+  if (a.blk_thr) {
+    __shared__ uint32_t wbest[4 * kMaxKb + 1];
+    write_block_threshold<PPW * 4, 4, 4 * PPW * 64>(a, nv, tkeys, wbest, wbest + 4 * kMaxKb);
   }
 }
 
@@ -491,46 +591,77 @@ __global__ __launch_bounds__(kTopkThreads) void topk_single_kernel(IndexArgs a, 
       });
 }
 
-// Stage 1: the top-k of each 16384-entry chunk -> candidates (key, id); id -1 pads.
-__global__ __launch_bounds__(kTopkThreads) void topk_stage1_kernel(IndexArgs a, int k, int nchunks,
-                                                                   uint32_t* ckey, int32_t* cid) {
-  __shared__ SelShared sh;
-  __shared__ uint32_t kl[kChunk];
-  const int t = blockIdx.x, c = blockIdx.y;
+// Large selections, step 2: keep every key >= the query's threshold T (the minimum of its full
+// scoring blocks' thresholds, or 0 when there is no bound) as a candidate (key, id), appended
+// through a per-query counter that the scoring launch zeroed. Block = (query, 8192 entries).
+constexpr int kFilterChunk = 8192;
+__global__ __launch_bounds__(kScoreThreads) void topk_filter_kernel(IndexArgs a, int blk_entries,
+                                                                    uint32_t* ckey, int32_t* cid,
+                                                                    unsigned* ccount, int64_t cstride) {
+  __shared__ uint32_t wmin[kScoreThreads / 64];
+  const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int seq, nv;
   query_of(a, t, seq, nv);
-  const int lo = c * kChunk;
-  const int n = max(0, min(nv, lo + kChunk) - lo);
-  uint32_t* ok = ckey + ((int64_t)t * nchunks + c) * k;
-  int32_t* oi = cid + ((int64_t)t * nchunks + c) * k;
-  const float* sc = a.scores + (int64_t)t * a.score_stride + lo;
-  if (nv <= k) return;                   // stage 2 fills short-context queries directly
-  if (n <= k) {
-    for (int j = threadIdx.x; j < k; j += kTopkThreads) {
-      oi[j] = j < n ? lo + j : -1;
-      ok[j] = j < n ? f32_order_key(sc[j]) : 0u;
-    }
-    return;
+  const int lo = blockIdx.y * kFilterChunk;
+  if (nv <= a.topk || lo >= nv) return;              // short context: the select fills it directly
+  const int full = nv / blk_entries;
+  const int kb = full > 0 ? (a.topk + full - 1) / full : kMaxKb + 1;
+  uint32_t T = 0u;
+  if (kb <= kMaxKb) {
+    uint32_t m = ~0u;
+    for (int i = threadIdx.x; i < full; i += kScoreThreads) m = min(m, a.blk_thr[(int64_t)t * a.thr_stride + i]);
+    m = ~wave_max_u32(~m);
+    if (lane == 0) wmin[wave] = m;
+    __syncthreads();
+    T = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
   }
-#pragma unroll 8
-  for (int i = threadIdx.x; i < n; i += kTopkThreads) kl[i] = f32_order_key(sc[i]);
-  sel_reset<kTopkThreads>(sh);
+  const float* sc = a.scores + (int64_t)t * a.score_stride;
+  const int hi = min(nv, lo + kFilterChunk);
+  // keep flags of the block's entries (entry lo + 256 j + tid for j < kPer), one counter update
+  // per block: per-wave counts, block prefix in LDS, then every kept entry gets its slot
+  constexpr int kPer = kFilterChunk / kScoreThreads;
+  __shared__ unsigned wcnt[kScoreThreads / 64], wbase[kScoreThreads / 64 + 1];
+  uint32_t key[kPer];
+  uint64_t km[kPer];
+  unsigned mine = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = lo + j * kScoreThreads + threadIdx.x;
+    key[j] = i < hi ? f32_order_key(sc[i]) : 0u;
+    km[j] = __ballot(i < hi && key[j] >= T);
+    mine += (unsigned)__popcll(km[j]);
+  }
+  if (lane == 0) wcnt[wave] = mine;                  // the wave's kept entries
   __syncthreads();
-  block_topk<kTopkThreads>(
-      sh, n, k, [&](int i, uint32_t& key) { key = kl[i]; return true; },
-      [&](int i) { return lo + i; },
-      [&](unsigned slot, int id, uint32_t key) {
-        if (slot < (unsigned)k) {
-          oi[slot] = id;
-          ok[slot] = key;
-        }
-      });
+  if (threadIdx.x == 0) {
+    const unsigned tot = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    const unsigned base = tot ? atomicAdd(ccount + t, tot) : 0u;
+    unsigned run = base;
+    for (int w = 0; w < kScoreThreads / 64; ++w) {
+      wbase[w] = run;
+      run += wcnt[w];
+    }
+  }
+  __syncthreads();
+  unsigned slot = wbase[wave];
+  const uint64_t below = (1ull << lane) - 1;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if ((km[j] >> lane) & 1ull) {
+      const unsigned sl = slot + (unsigned)__popcll(km[j] & below);
+      ckey[(int64_t)t * cstride + sl] = key[j];
+      cid[(int64_t)t * cstride + sl] = lo + j * kScoreThreads + threadIdx.x;
+    }
+    slot += (unsigned)__popcll(km[j]);
+  }
 }
 
-// Stage 2: the top-k of a query's chunk winners.
-__global__ __launch_bounds__(kTopkThreads) void topk_stage2_kernel(IndexArgs a, int k, int nchunks,
+// Large selections, step 3: the top-k of a query's candidates (keys in LDS when they fit).
+__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(IndexArgs a, int k,
                                                                    const uint32_t* ckey,
                                                                    const int32_t* cid,
+                                                                   const unsigned* ccount,
+                                                                   int64_t cstride,
                                                                    int32_t* out_idx,
                                                                    float* out_score) {
   __shared__ SelShared sh;
@@ -548,9 +679,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage2_kernel(IndexArgs a, 
     }
     return;
   }
-  const uint32_t* ck = ckey + (int64_t)t * nchunks * k;
-  const int32_t* ci = cid + (int64_t)t * nchunks * k;
-  const int n = nchunks * k;
+  const uint32_t* ck = ckey + (int64_t)t * cstride;
+  const int32_t* ci = cid + (int64_t)t * cstride;
+  const int n = (int)ccount[t];                      // >= k: every key >= the k-th is a candidate
   auto emit = [&](unsigned slot, int id, uint32_t key) {
     if (slot < (unsigned)k) {
       oi[slot] = id;
@@ -558,9 +689,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage2_kernel(IndexArgs a, 
     }
   };
   if (n <= kSingleMax) {
-    // keys in LDS, read once. A padding candidate (id -1) has key 0, below every real key (the
-    // key of any score, -inf included, is larger), and at least k real candidates exist here
-    // (more than kSingleMax entries are visible), so padding is never selected.
 #pragma unroll 8
     for (int i = threadIdx.x; i < n; i += kTopkThreads) kl[i] = ck[i];
     sel_reset<kTopkThreads>(sh);
@@ -573,7 +701,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage2_kernel(IndexArgs a, 
   sel_reset<kTopkThreads>(sh);
   __syncthreads();
   block_topk<kTopkThreads>(
-      sh, n, k, [&](int i, uint32_t& key) { key = ck[i]; return ci[i] >= 0; }, [&](int i) { return ci[i]; },
+      sh, n, k, [&](int i, uint32_t& key) { key = ck[i]; return true; }, [&](int i) { return ci[i]; },
       emit);
 }
 
@@ -583,11 +711,20 @@ TopkPlan topk_plan(int N, int max_pos, int m, int topk) {
   TopkPlan p{};
   const int64_t nv = (int64_t)(max_pos + 1) / m;
   const int64_t stride = std::max<int64_t>(64, (nv + 63) / 64 * 64);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   p.score_bytes = (size_t)N * stride * sizeof(float);
-  p.two_stage = nv > kSingleMax;
-  p.nchunks = p.two_stage ? (int)((nv + kChunk - 1) / kChunk) : 0;
-  p.cand_bytes = p.two_stage ? (size_t)N * p.nchunks * topk * (sizeof(uint32_t) + sizeof(int32_t)) : 0;
-  p.ws_bytes = p.score_bytes + p.cand_bytes + 256;
+  p.large = nv > kSingleMax;
+  size_t off = up(p.score_bytes);
+  if (p.large) {
+    p.thr_stride = (int)((nv + 255) / 256);          // the smallest scoring block is 256 entries
+    p.thr_off = off;
+    off += up((size_t)N * p.thr_stride * sizeof(uint32_t));
+    p.cand_off = off;                                // keys [N, stride] then ids [N, stride]
+    off += up((size_t)N * stride * sizeof(uint32_t)) + up((size_t)N * stride * sizeof(int32_t));
+    p.cnt_off = off;
+    off += up((size_t)N * sizeof(unsigned));
+  }
+  p.ws_bytes = off;
   return p;
 }
 
@@ -620,19 +757,21 @@ hipError_t launch_index_scores(const IndexArgs& a, int fmt, hipStream_t stream) 
 }
 
 hipError_t launch_topk(const IndexArgs& a, const TopkPlan& plan, int topk, int32_t* out_idx,
-                       float* out_score, void* cand, hipStream_t stream) {
+                       float* out_score, uint8_t* ws, int blk_entries, hipStream_t stream) {
   if (a.N == 0) return hipSuccess;
-  if (!plan.two_stage) {
+  if (!plan.large) {
     hipLaunchKernelGGL(topk_single_kernel, dim3(a.N), dim3(kTopkThreads), 0, stream, a, topk,
                        out_idx, out_score);
     return hipGetLastError();
   }
-  uint32_t* ckey = static_cast<uint32_t*>(cand);
-  int32_t* cid = reinterpret_cast<int32_t*>(ckey + (size_t)a.N * plan.nchunks * topk);
-  hipLaunchKernelGGL(topk_stage1_kernel, dim3(a.N, plan.nchunks), dim3(kTopkThreads), 0, stream, a,
-                     topk, plan.nchunks, ckey, cid);
-  hipLaunchKernelGGL(topk_stage2_kernel, dim3(a.N), dim3(kTopkThreads), 0, stream, a, topk,
-                     plan.nchunks, ckey, cid, out_idx, out_score);
+  const int64_t cstride = a.score_stride;
+  uint32_t* ckey = reinterpret_cast<uint32_t*>(ws + plan.cand_off);
+  int32_t* cid = reinterpret_cast<int32_t*>(ws + plan.cand_off + ((size_t)a.N * cstride * 4 + 255) / 256 * 256);
+  unsigned* cnt = a.cand_count;
+  hipLaunchKernelGGL(topk_filter_kernel, dim3(a.N, (a.nv_cap + kFilterChunk - 1) / kFilterChunk),
+                     dim3(kScoreThreads), 0, stream, a, blk_entries, ckey, cid, cnt, cstride);
+  hipLaunchKernelGGL(topk_select_kernel, dim3(a.N), dim3(kTopkThreads), 0, stream, a, topk, ckey, cid,
+                     cnt, cstride, out_idx, out_score);
   return hipGetLastError();
 }
 

@@ -63,16 +63,21 @@ struct IndexArgs {
   int N, H_I, d_I, m, nv_cap, pos_cap;
   float* scores;              // [N, score_stride]
   int64_t score_stride;
+  // large selections: per scoring block, the kb-th largest score key of a full block
+  // (kb = ceil(topk / full blocks of the query)); nullptr when not needed
+  uint32_t* blk_thr;          // [N, thr_stride]
+  unsigned* cand_count;       // [N] candidate counters of the filter, zeroed by the scoring launch
+  int thr_stride, topk;
 };
 
 struct TopkPlan {
-  int two_stage;
-  int nchunks;                // stage-1 chunks per query (two-stage)
-  size_t score_bytes, cand_bytes, ws_bytes;
+  int large;                  // n_visible may exceed kSingleMax: threshold + filter + select
+  int thr_stride;             // block thresholds per query (scoring blocks of >= 256 entries)
+  size_t score_bytes, thr_off, cand_off, cnt_off, ws_bytes;
 };
 TopkPlan topk_plan(int N, int max_pos, int m, int topk);
 hipError_t launch_index_scores(const IndexArgs& a, int fmt, hipStream_t stream);
 hipError_t launch_topk(const IndexArgs& a, const TopkPlan& plan, int topk, int32_t* out_idx,
-                       float* out_score, void* cand, hipStream_t stream);
+                       float* out_score, uint8_t* ws, int blk_entries, hipStream_t stream);
 
 }  // namespace hcs
