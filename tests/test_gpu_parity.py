@@ -3,6 +3,8 @@ import numpy as np
 import pytest
 import torch
 
+import hybrid_compressed_sparse_amd as hcs
+from hybrid_compressed_sparse_amd.step import PathStep
 from oracle import method as OM
 from oracle import pipeline as OP
 from synth import configs as C
@@ -123,3 +125,56 @@ def test_prefill_small():
 def test_prefill_full_sampled():
     sc = G.build(C.CSA_PREFILL, seed=0, device=_dev())
     _check_step(sc, queries=[0, 1, 2047, 4095])
+
+
+def test_csa_decode_large_selection_ragged():
+    """bf16 indexer keys with more than 32768 visible entries (threshold + filter + select path)
+    in a ragged batch: a query below 32768 entries, one with fewer entries than k, one at
+    position 0 (no compressed entry, a single window row)."""
+    wl = C.CSA_DECODE.with_(B=4, topk=300)
+    ctx = [4 * 40000, 4 * 33000 + 3, 4 * 250, 1]
+    sc = G.build(wl, seed=8, device=_dev(), ctx_per_seq=ctx)
+    _check_step(sc)
+
+
+def _tie_case(nv: int, k: int, seed: int):
+    """Every indexer key equal, so every score ties: the selection must be the k smallest ids."""
+    wl = C.CSA_DECODE.with_(B=2, topk=k)
+    sc = G.build(wl, seed=seed, device=_dev(), ctx_per_seq=[4 * nv, 4 * nv + 2])
+    pool = sc.ix.pool
+    pool.copy_(pool[0:1].expand_as(pool))          # the first page everywhere ...
+    row = pool[0, : 2 * wl.d_I].clone()
+    pool.view(pool.shape[0], 64, 2 * wl.d_I).copy_(row.view(1, 1, -1).expand(pool.shape[0], 64, -1))  # ... and its first row
+    step = PathStep(U.shape_of(sc), device=_dev())
+    q, qs = U._ix_q_args(sc)
+    step.select(q, qs, sc.ix_w.contiguous(), sc.ix, sc.q_seq, sc.q_pos)
+    torch.cuda.synchronize()
+    for t in range(2):
+        got = np.sort(step.idx[t].cpu().numpy())
+        assert np.array_equal(got, np.arange(k)), (nv, k, t, got[:8], got[-8:])
+        s = step.score[t].cpu().numpy()
+        assert np.all(s == s[0])
+
+
+def test_topk_ties_go_to_smaller_ids():
+    _tie_case(nv=2048, k=512, seed=9)
+
+
+def test_topk_ties_go_to_smaller_ids_large_selection():
+    _tie_case(nv=40000, k=300, seed=10)
+
+
+def test_empty_batches_launch_nothing():
+    """N = 0 (and B = 0) calls succeed without touching any buffer."""
+    dev = _dev()
+    z32 = torch.zeros(1, dtype=torch.int32, device=dev)
+    pool = torch.zeros((1, 64 * 1024), dtype=torch.uint8, device=dev)
+    pt = torch.zeros((1, 1), dtype=torch.int32, device=dev)
+    cache = hcs.paged(pool, pt, "bf16", 512)
+    q = torch.zeros((0, 64, 512), dtype=torch.bfloat16, device=dev)
+    out = torch.zeros((0, 64, 512), dtype=torch.bfloat16, device=dev)
+    hcs.sparse_mla_decode(q, cache, cache, None, z32[:0], z32[:0], 128, 4, 100, 512 ** -0.5, out)
+    st = torch.zeros((0, 3 * 512), dtype=torch.float32, device=dev)
+    kv = torch.zeros((0, 512), dtype=torch.bfloat16, device=dev)
+    hcs.compress_kv(kv, kv, z32, z32[:0], st, cache, 4, max_new=1)
+    torch.cuda.synchronize()
