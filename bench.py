@@ -117,24 +117,30 @@ class Bench:
             sc = G.build(wl, seed=seed + s, device=dev)
             B, d, m = wl.B, wl.d, wl.m
             state = torch.zeros((B, 3 * d), dtype=torch.float32, device=dev)
-            # setup: the block's tokens before the step's own one
+            # setup: each stream's tokens before the step's own (the last n_step: one decode
+            # token, or the prefill chunk)
             lens = [sc.c_cu[b + 1] - sc.c_cu[b] for b in range(B)]
-            pre = torch.cat([torch.arange(sc.c_cu[b], sc.c_cu[b + 1] - 1, device=dev) for b in range(B)])
-            last = torch.tensor([sc.c_cu[b + 1] - 1 for b in range(B)], device=dev)
+            ns = [min(sc.n_step, n) for n in lens]
+            pre = torch.cat([torch.arange(sc.c_cu[b], sc.c_cu[b + 1] - ns[b], device=dev) for b in range(B)])
+            last = torch.cat([torch.arange(sc.c_cu[b + 1] - ns[b], sc.c_cu[b + 1], device=dev) for b in range(B)])
             if pre.numel():
                 cu_h = [0]
-                for n in lens:
-                    cu_h.append(cu_h[-1] + n - 1)
+                for n, k in zip(lens, ns):
+                    cu_h.append(cu_h[-1] + n - k)
                 cu = torch.tensor(cu_h, dtype=torch.int32, device=dev)
                 hcs.compress_kv(sc.c_x.index_select(0, pre).contiguous(),
                                 sc.c_s.index_select(0, pre).contiguous(), cu, sc.c_start, state,
                                 sc.comp, m, max_new=max(lens))
+            cu_s = [0]
+            for k in ns:
+                cu_s.append(cu_s[-1] + k)
             step_in = dict(
                 c_kv=sc.c_x.index_select(0, last).contiguous(),
                 c_score=sc.c_s.index_select(0, last).contiguous(),
-                c_cu=torch.arange(B + 1, dtype=torch.int32, device=dev),
-                c_start=(sc.c_start + torch.tensor(lens, dtype=torch.int32, device=dev) - 1).contiguous(),
-                c_state=state, c_max_new=1)
+                c_cu=torch.tensor(cu_s, dtype=torch.int32, device=dev),
+                c_start=(sc.c_start + torch.tensor([n - k for n, k in zip(lens, ns)], dtype=torch.int32,
+                                                   device=dev)).contiguous(),
+                c_state=state, c_max_new=max(ns))
             if wl.indexer:
                 if isinstance(sc.ix_q, torch.Tensor):
                     step_in.update(ix_q=sc.ix_q.contiguous(), ix_q_scale=None)
@@ -149,7 +155,8 @@ class Bench:
                 sc.ix.rows = None
         sc0 = self.sets[0][0]
         self.step = PathStep(StepShape(N=sc0.N, H=wl.H, d=wl.d, m=wl.m, window=wl.window,
-                                       max_pos=sc0.max_pos(), topk=wl.topk if wl.indexer else 0),
+                                       max_pos=sc0.max_pos(), topk=wl.topk if wl.indexer else 0,
+                                       prefill=wl.kind == "prefill", seq=0, P0=wl.P0),
                              device=dev)
         torch.cuda.synchronize()
 
@@ -231,6 +238,57 @@ def cpu_baseline(wl, seconds: float) -> dict:
                       f"{dt:.1f} s"}
 
 
+# ------------------------------------------------------------------ prefill chunk
+
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16, published
+
+
+def prefill_flops(wl) -> dict:
+    """MFMA work of one prefill chunk: the indexer's q.k over every visible entry of every query
+    (2 flops per multiply-add), attention's S = q k^T and O = P V over each query's rows."""
+    ix = at = 0
+    for j in range(wl.Q):
+        p = wl.P0 + j
+        nv = (p + 1) // wl.m
+        rows = min(wl.window, p + 1) + (min(wl.topk, nv) if wl.indexer else nv)
+        ix += 2 * nv * wl.H_I * wl.d_I if wl.indexer else 0
+        at += 2 * 2 * rows * wl.H * wl.d
+    return {"index_topk": ix, "attention": at, "step": ix + at}
+
+
+def bench_prefill(wl, args):
+    """One prefill chunk (compressor over the chunk, indexer + top-k and attention for its Q
+    queries) per step; tokens/s and the fraction of the bf16 MFMA peak."""
+    R = max(1, min(args.sets, args.steps, 2))        # q alone is 256 MB per set
+    log(f"[bench] {wl.name}: building {R} input sets")
+    bench = Bench(wl, R, seed=1000)
+    full, rem = divmod(args.steps, R)
+
+    def timed(op):
+        gs = [bench.graph(op)] * full + ([bench.graph(op, range(rem))] if rem else [])
+        for _ in range(max(1, args.warmup // R)):
+            gs[0].replay()
+        return bench.time_steps(gs, 1, 0) / args.steps
+
+    ms = {op: timed(op) for op in ["step", "compress", "index_topk", "attention"]}
+    fl = prefill_flops(wl)
+    tflops = {k: fl[k] / (ms[k] * 1e-3) / 1e12 for k in ["index_topk", "attention", "step"]}
+    for k in ms:
+        log(f"[bench] {k}: {ms[k] * 1e3:.1f} us" + (f", {tflops[k]:.0f} TFLOP/s" if k in tflops else ""))
+    print(json.dumps({
+        "metric": "prefill tokens/s and % bf16 MFMA peak, CSA chunk, 1 GPU", "value": wl.Q / (ms["step"] * 1e-3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms["step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "P0": wl.P0, "Q": wl.Q, "heads": wl.H, "head_dim": wl.d,
+                   "compress_ratio": wl.m, "window": wl.window, "topk": wl.topk, "indexer": f"{wl.H_I}x{wl.d_I} bf16"},
+        "roofline": {"bound": "mfma", "achieved": tflops["step"], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops["step"] / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "flops_per_step": fl["step"]},
+        "ops_us": {k: v * 1e3 for k, v in ms.items()},
+        "ops_tflops": tflops,
+    }))
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -268,8 +326,10 @@ def main():
         return
 
     wl = C.BY_NAME[args.workload]
+    if wl.kind == "prefill":
+        return bench_prefill(wl, args)
     if wl.kind != "decode":
-        sys.exit("bench workloads are the decode configurations")
+        sys.exit("bench workloads are the decode and prefill configurations")
     n_vis = wl.ctx // wl.m
     if args.steps < 1 or args.warmup < 0:
         sys.exit("--steps must be >= 1 and --warmup >= 0")
