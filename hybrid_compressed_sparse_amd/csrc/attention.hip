@@ -120,6 +120,12 @@ __device__ __forceinline__ void fill_rowtab(const AttnArgs& a, int t, const Quer
   }
 }
 
+// s_waitcnt vmcnt(0): this wave's global loads (including those into LDS) have completed.
+__device__ __forceinline__ void wait_vm_zero() {
+  // s_waitcnt vmcnt(0): vmcnt 0, expcnt 7, lgkmcnt 15 (gfx9 encoding)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 // Entries of a sequence's compressed page table that the all-heads kernel keeps in LDS.
 constexpr int kPtCache = 2048;
 
@@ -173,7 +179,30 @@ __device__ __forceinline__ void fill_rows(const AttnArgs& a, int t, const QueryR
     const bool ok = li < n && gr < q.R && ok_id && pg >= 0 && pg < npages;
     if (li < np) rowtab[li] = ok ? ((is_swa ? 0u : 0x80000000u) | (uint32_t)(pg * 64 + (row & 63))) : kNoRow;
   }
+  wait_vm_zero();     // LDS copies the caller started before (dma16) have landed as well
   __syncthreads();
+}
+
+// LDS byte address of a __shared__ location.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// global_load_lds_dwordx4 as inline assembly: lane i copies the 16 bytes at base + voff to LDS
+// address lds + 16 i (lds wave-uniform). The compiler does not see this LDS write, so it adds
+// no vmcnt waits of its own before later LDS reads (it cannot tell a read of the other tile of
+// a double buffer from a read of this one); the caller waits (s_waitcnt vmcnt) before the
+// destination is read. Every LDS DMA of a kernel goes through here, so no M0 value of the
+// compiler's own is live across it.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane((int)lds)) : "memory", "m0");
+}
+
+// The same with a per-lane source address.
+__device__ __forceinline__ void dma16v(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane((int)lds)) : "memory", "m0");
 }
 
 // ---------------------------------------------------------------- row staging
@@ -287,11 +316,6 @@ __device__ __forceinline__ float lse_of(float m, float l) {
   return l > 0.f ? (m + __builtin_log2f(l)) * 0.6931471805599453f : kNegInf;
 }
 
-// s_waitcnt vmcnt(0): this wave's global loads (including those into LDS) have completed.
-__device__ __forceinline__ void wait_vm_zero() {
-  // s_waitcnt vmcnt(0): vmcnt 0, expcnt 7, lgkmcnt 15 (gfx9 encoding)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-}
 
 // Workgroup barrier for LDS data written with ds_write only: waits for this wave's LDS
 // operations, not for its outstanding global loads (a __syncthreads() fence would also wait for
@@ -648,9 +672,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       const uint8_t* src = hh < a.H ? reinterpret_cast<const uint8_t*>(a.q + ((int64_t)t * a.H + hh) * D)
                                     : g_zero_row;
       const int ch = (lane % QLPR) ^ (hl_ & 15);
-      __builtin_amdgcn_global_load_lds((const void*)(src + ch * 16),
-                                       (__attribute__((address_space(3))) void*)(tile1 + (8 * wave + i * QHPI) * RS),
-                                       16, 0, 0);
+      dma16v(src + ch * 16, lds_addr(tile1) + (8 * wave + i * QHPI) * RS);
     }
   }
   fill_rows<NT>(a, t, q, r0, n_rows, rowtab, ptl, BT);
@@ -681,18 +703,14 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const uint8_t* src = row_ptr((uint32_t)__builtin_amdgcn_readlane((int)my, i));
-        __builtin_amdgcn_global_load_lds((const void*)(src + (lane_x ^ (swz_dec(i) * 16))),
-                                         (__attribute__((address_space(3))) void*)(tbuf + (WRL * wave + i) * RS),
-                                         16, 0, 0);
+        dma16(src, (uint32_t)(lane_x ^ (swz_dec(i) * 16)), lds_addr(tbuf) + (WRL * wave + i) * RS);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const uint8_t* src = row_ptr(at[i * RPI + lane / LPR]);
         const int sw = swz_dec(i * RPI + lane / LPR) * 16;
-        __builtin_amdgcn_global_load_lds((const void*)(src + (lane_x ^ sw)),
-                                         (__attribute__((address_space(3))) void*)(tbuf + (WRL * wave + i * RPI) * RS),
-                                         16, 0, 0);
+        dma16v(src + (lane_x ^ sw), lds_addr(tbuf) + (WRL * wave + i * RPI) * RS);
       }
     }
   };
