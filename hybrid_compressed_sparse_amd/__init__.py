@@ -53,6 +53,9 @@ def lib() -> ctypes.CDLL:
         L.hcs_index_topk.restype = i32
         L.hcs_index_topk.argtypes = [vp, vp, vp, Paged, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
                                      vp, sz, vp]
+        L.hcs_index_topk_chunk.restype = i32
+        L.hcs_index_topk_chunk.argtypes = [vp, vp, vp, Paged, i32, i32, i32, i32, i32, i32, i32, vp, vp,
+                                           vp, sz, vp]
         L.hcs_sparse_mla_workspace_size.restype = sz
         L.hcs_sparse_mla_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.hcs_sparse_mla_decode.restype = i32
@@ -149,6 +152,22 @@ def index_topk(q, q_scale: Optional[torch.Tensor], w: torch.Tensor, keys, q_seq:
         N, H_I, d_I, m, topk, max_pos, _ptr(out_idx, torch.int32, "out_idx"),
         _ptr(out_score, torch.float32, "out_score"), _ptr(ws, name="ws"),
         0 if ws is None else ws.numel() * ws.element_size(), _stream()), "index_topk")
+
+
+def index_topk_chunk(q, q_scale: Optional[torch.Tensor], w: torch.Tensor, keys, seq: int, P0: int,
+                     m: int, topk: int, out_idx: torch.Tensor, out_score: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None) -> None:
+    """hcs_index_topk_chunk: index_topk for the queries P0 .. P0+Q-1 of sequence `seq`
+    (Q = w.shape[0])."""
+    Q, H_I = w.shape
+    d_I = keys.dim
+    if ws is None:
+        ws = _workspace(index_topk_workspace_size(Q, P0 + Q - 1, m, topk), w.device)
+    _check(lib().hcs_index_topk_chunk(
+        _ptr(q, name="q"), _ptr(q_scale, torch.uint8, "q_scale"), _ptr(w, torch.float32, "w"),
+        _as_paged(keys), seq, P0, Q, H_I, d_I, m, topk, _ptr(out_idx, torch.int32, "out_idx"),
+        _ptr(out_score, torch.float32, "out_score"), _ptr(ws, name="ws"),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream()), "index_topk_chunk")
 
 
 # ------------------------------------------------------------------------------ attention

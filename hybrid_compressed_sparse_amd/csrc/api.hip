@@ -99,17 +99,19 @@ size_t hcs_index_topk_workspace_size(int N, int max_pos, int m, int topk) {
   return hcs::topk_plan(N, max_pos, m, topk).ws_bytes;
 }
 
-hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
-                          const int32_t* q_seq, const int32_t* q_pos, int N, int H_I, int d_I,
-                          int m, int topk, int max_pos, int32_t* out_idx, float* out_score,
-                          void* ws, size_t ws_bytes, void* stream) {
+// Checks and launches shared by both indexer entry points; q_seq == NULL means a chunk of
+// queries of sequence `seq` at positions P0 .. P0+N-1.
+static hcs_status run_index(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
+                            const int32_t* q_seq, const int32_t* q_pos, int seq, int P0, int N,
+                            int H_I, int d_I, int m, int topk, int max_pos, int32_t* out_idx,
+                            float* out_score, void* ws, size_t ws_bytes, void* stream) {
   if (N < 0) return fail(HCS_ERR_INVALID_ARG, "N must be >= 0");
   if (H_I < 1 || H_I > 64) return fail(HCS_ERR_UNSUPPORTED, "H_I must be in 1..64");
   if (m < 1) return fail(HCS_ERR_INVALID_ARG, "m must be >= 1");
   if (topk < 1 || topk > 4096) return fail(HCS_ERR_UNSUPPORTED, "topk must be in 1..4096");
   if (max_pos < 0) return fail(HCS_ERR_INVALID_ARG, "max_pos must be >= 0");
   if (N == 0) return ok();
-  if (!q || !w || !q_seq || !q_pos || !out_idx) return fail(HCS_ERR_INVALID_ARG, "null q, w, q_seq, q_pos or out_idx");
+  if (!q || !w || !out_idx) return fail(HCS_ERR_INVALID_ARG, "null q, w or out_idx");
   hcs_status s = check_paged(keys, "keys", d_I, false, true);
   if (s != HCS_OK) return s;
   if (keys.fmt == HCS_FMT_BF16 && d_I != 32 && d_I != 64 && d_I != 128)
@@ -131,6 +133,8 @@ hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w,
   a.keys = hcs::to_paged(keys);
   a.q_seq = q_seq;
   a.q_pos = q_pos;
+  a.seq_const = seq;
+  a.p0 = P0;
   a.N = N;
   a.H_I = H_I;
   a.d_I = d_I;
@@ -152,6 +156,27 @@ hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w,
   const int blk_entries = keys.fmt == HCS_FMT_MXFP4 ? 512 : 256;   // entries per scoring block
   return hip_status(hcs::launch_topk(a, plan, topk, out_idx, out_score, w8, blk_entries, st),
                     "index_topk select");
+}
+
+hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
+                          const int32_t* q_seq, const int32_t* q_pos, int N, int H_I, int d_I,
+                          int m, int topk, int max_pos, int32_t* out_idx, float* out_score,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (N > 0 && (!q_seq || !q_pos)) return fail(HCS_ERR_INVALID_ARG, "null q_seq or q_pos");
+  return run_index(q, q_scale, w, keys, q_seq, q_pos, 0, 0, N, H_I, d_I, m, topk, max_pos,
+                   out_idx, out_score, ws, ws_bytes, stream);
+}
+
+hcs_status hcs_index_topk_chunk(const void* q, const uint8_t* q_scale, const float* w,
+                                hcs_paged keys, int seq, int P0, int Q, int H_I, int d_I, int m,
+                                int topk, int32_t* out_idx, float* out_score, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (P0 < 0 || seq < 0) return fail(HCS_ERR_INVALID_ARG, "P0 and seq must be >= 0");
+  if (Q < 0) return fail(HCS_ERR_INVALID_ARG, "Q must be >= 0");
+  if ((int64_t)P0 + Q > INT32_MAX) return fail(HCS_ERR_INVALID_ARG, "P0 + Q overflows int32");
+  if (Q == 0) return ok();
+  return run_index(q, q_scale, w, keys, nullptr, nullptr, seq, P0, Q, H_I, d_I, m, topk,
+                   P0 + Q - 1, out_idx, out_score, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------------------ attention

@@ -73,4 +73,42 @@ __device__ __forceinline__ float order_key_f32(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// s_waitcnt vmcnt(0): this wave's global loads (including those into LDS) have completed.
+__device__ __forceinline__ void wait_vm_zero() {
+  // s_waitcnt vmcnt(0): vmcnt 0, expcnt 7, lgkmcnt 15 (gfx9 encoding)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// LDS byte address of a __shared__ location.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// global_load_lds_dwordx4 as inline assembly: lane i copies the 16 bytes at base + voff to LDS
+// address lds + 16 i (lds wave-uniform). The compiler does not see this LDS write, so it adds
+// no vmcnt waits of its own before later LDS reads (it cannot tell a read of the other tile of
+// a double buffer from a read of this one); the caller waits (s_waitcnt vmcnt) before the
+// destination is read. Every LDS DMA of a kernel goes through here, so no M0 value of the
+// compiler's own is live across it.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane((int)lds)) : "memory", "m0");
+}
+
+// The same with a per-lane source address.
+__device__ __forceinline__ void dma16v(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane((int)lds)) : "memory", "m0");
+}
+
+// Workgroup barrier for LDS data written with ds_write only: waits for this wave's LDS
+// operations, not for its outstanding global loads (a __syncthreads() fence would also wait for
+// the asynchronous row loads into the other buffer, which must stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0); vmcnt 63, expcnt 7 (no wait)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace hcs

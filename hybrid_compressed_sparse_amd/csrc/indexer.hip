@@ -41,8 +41,14 @@ constexpr int kSingleMax = 32768;       // largest n_visible selected in one sta
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ void query_of(const IndexArgs& a, int t, int& seq, int& nv) {
-  seq = __ldg(a.q_seq + t);
-  const int pos = min(__ldg(a.q_pos + t), a.pos_cap);
+  int pos;
+  if (a.q_seq) {
+    seq = __ldg(a.q_seq + t);
+    pos = min(__ldg(a.q_pos + t), a.pos_cap);
+  } else {
+    seq = a.seq_const;
+    pos = a.p0 + t;
+  }
   nv = min((pos + 1) / a.m, a.nv_cap);
 }
 
@@ -234,6 +240,132 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(IndexAr
     int seq, nv;
     query_of(a, blockIdx.x, seq, nv);
     write_block_threshold<4, 4, 256>(a, nv, tkeys, wbest, wbest + 4 * kMaxKb);
+  }
+}
+
+// ---------------------------------------------------------------- bf16 scores, query chunks
+// The queries of a chunk (consecutive positions of one sequence, as in prefill) score the same
+// keys, so their scores are one matrix product, [queries x heads, d_I] x [d_I, entries],
+// followed by ReLU and the weighted sum over heads. A block holds 512 consecutive entries in
+// registers (8 waves x one 64-entry page, the B operand of v_mfma_f32_16x16x32_bf16, loaded
+// once) and walks up to 64 queries: the q rows (64 x 128 bf16) and head weights of query t+1
+// are copied into the other half of a double-buffered LDS slot while query t is scored, so keys
+// are read once per 64 queries instead of once per query. Per query a wave does 64 MFMAs
+// (4 entry tiles x 4 head tiles x 4 k-steps) with q read from LDS in operand order (16-byte
+// chunk c of head h stored at c ^ (h mod 16): conflict-free). The arithmetic per score is that
+// of index_score_bf16_kernel, in the same order, so both give the same bits.
+// The scores of query t are stored one iteration later, after the wait for the copy of query
+// t+1: on gfx9 one counter covers loads and stores, and stores issued a whole query earlier
+// have completed by then, so that wait does not stall on them.
+constexpr int kChunkThreads = 512;
+constexpr int kChunkEntries = 512;               // entries per block (8 waves x 64)
+constexpr int kChunkQueries = 64;                // queries per block
+constexpr int kChunkMinQueries = 256;            // smaller chunks use the per-query kernel
+
+template <int MT>
+__global__ __launch_bounds__(kChunkThreads, 1) void index_score_chunk_kernel(IndexArgs a) {
+  constexpr int DI = 128, KS = DI / 32, RB = DI * 2, CPR = RB / 16;
+  constexpr int PAGE = kPageRows * RB;
+  __shared__ __attribute__((aligned(16))) uint8_t qbuf[2][64 * RB];
+  __shared__ __attribute__((aligned(16))) float wbuf[2][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int eb = blockIdx.x * kChunkEntries;                      // first entry of the block
+  const int e0 = eb + wave * 64;                                  // this wave's page
+  // queries t0 .. t1-1; the first that sees any entry of the block is the first with
+  // (p0 + t + 1) / m > eb, i.e. p0 + t + 1 >= (eb + 1) m
+  const int t1 = min((int)(blockIdx.y + 1) * kChunkQueries, a.N);
+  const int64_t t_vis = (int64_t)(eb + 1) * a.m - a.p0 - 1;
+  const int t0 = (int)max<int64_t>((int64_t)blockIdx.y * kChunkQueries, t_vis);
+  if (t0 >= t1 || eb >= a.nv_cap) return;                        // uniform over the block
+
+  // q rows and head weights of query t into slot `buf`: wave w copies heads 8w .. 8w+7 (rows
+  // of H_I or more read zeros); lanes 0..15 of wave 0 copy the 64 weights (H_I % 4 == 0)
+  auto copy_q = [&](int t, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int h = 8 * wave + 4 * i + lane / CPR, c = lane % CPR;
+      const uint8_t* src = h < a.H_I ? a.q + ((int64_t)t * a.H_I + h) * RB + ((c ^ (h & 15)) << 4)
+                                     : g_ix_zero + lane * 16;
+      dma16v(src, lds_addr(qbuf[buf]) + (8 * wave + 4 * i) * RB);
+    }
+    if (wave == 0 && lane < 16) {
+      const int h = 4 * lane;
+      const void* src = h < a.H_I ? (const void*)(a.w + (int64_t)t * a.H_I + h) : (const void*)g_ix_zero;
+      dma16v(src, lds_addr(wbuf[buf]));
+    }
+  };
+  copy_q(t0, 0);
+
+  // keys: kreg[nt][ks] = elements 32 ks + 8 g .. +7 of entry e0 + 16 nt + l16 (B operand)
+  bf16x8 kreg[4][KS];
+  {
+    const int pg = e0 < a.nv_cap ? page_of(a.keys, a.seq_const, e0) : -1;
+    const uint8_t* page = pg >= 0 ? a.keys.base + (int64_t)pg * PAGE : nullptr;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const i32x4 v = page ? *(const i32x4*)(page + (16 * nt + l16) * RB + 64 * ks + 16 * g)
+                             : i32x4{0, 0, 0, 0};
+        kreg[nt][ks] = __builtin_bit_cast(bf16x8, v);
+      }
+  }
+
+  float sc[4] = {0.f, 0.f, 0.f, 0.f};           // scores of the previous query, not yet stored
+  int t_prev = -1, nv_prev = 0;
+  for (int t = t0, it = 0; t < t1; ++t, ++it) {
+    const int buf = it & 1;
+    wait_vm_zero();                              // this wave's copies of query t (and keys)
+    lds_barrier();                               // every wave's copies of query t
+    // the previous query's scores (entries below its visible count)
+    if (t_prev >= 0 && g == 0) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int e = e0 + 16 * nt + l16;
+        if (e < nv_prev) a.scores[(int64_t)t_prev * a.score_stride + e] = sc[nt];
+      }
+    }
+    if (t + 1 < t1) copy_q(t + 1, buf ^ 1);
+    bf16x8 qa[MT][KS];
+    float wreg[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int h = mt * 16 + l16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qa[mt][ks] = *(const bf16x8*)(qbuf[buf] + h * RB + (((4 * ks + g) ^ (h & (CPR - 1))) << 4));
+      const f32x4 w4 = *(const f32x4*)(wbuf[buf] + mt * 16 + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wreg[mt][i] = w4[i];
+    }
+    int seq, nv;
+    query_of(a, t, seq, nv);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      float part = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kreg[nt][ks], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += wreg[mt][i] * fmaxf(acc[i], 0.f);
+      }
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      sc[nt] = part;
+    }
+    t_prev = t;
+    nv_prev = nv;
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int e = e0 + 16 * nt + l16;
+      if (e < nv_prev) a.scores[(int64_t)t_prev * a.score_stride + e] = sc[nt];
+    }
   }
 }
 
@@ -739,6 +871,16 @@ hipError_t launch_index_scores(const IndexArgs& a, int fmt, hipStream_t stream) 
       case 2: hipLaunchKernelGGL((index_score_mxfp4_kernel<2>), grid, dim3(kScoreThreads), 0, stream, a); break;
       case 3: hipLaunchKernelGGL((index_score_mxfp4_kernel<3>), grid, dim3(kScoreThreads), 0, stream, a); break;
       default: hipLaunchKernelGGL((index_score_mxfp4_kernel<4>), grid, dim3(kScoreThreads), 0, stream, a); break;
+    }
+    return hipGetLastError();
+  }
+  if (!a.q_seq && !a.blk_thr && a.d_I == 128 && a.H_I % 4 == 0 && a.N >= kChunkMinQueries) {
+    dim3 grid((a.nv_cap + kChunkEntries - 1) / kChunkEntries, (a.N + kChunkQueries - 1) / kChunkQueries);
+    switch (MT) {
+      case 1: hipLaunchKernelGGL((index_score_chunk_kernel<1>), grid, dim3(kChunkThreads), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((index_score_chunk_kernel<2>), grid, dim3(kChunkThreads), 0, stream, a); break;
+      case 3: hipLaunchKernelGGL((index_score_chunk_kernel<3>), grid, dim3(kChunkThreads), 0, stream, a); break;
+      default: hipLaunchKernelGGL((index_score_chunk_kernel<4>), grid, dim3(kChunkThreads), 0, stream, a); break;
     }
     return hipGetLastError();
   }

@@ -68,6 +68,9 @@ struct IndexArgs {
   uint32_t* blk_thr;          // [N, thr_stride]
   unsigned* cand_count;       // [N] candidate counters of the filter, zeroed by the scoring launch
   int thr_stride, topk;
+  // a chunk of consecutive queries of one sequence (q_seq == nullptr): query t is at position
+  // p0 + t of sequence seq_const
+  int seq_const, p0;
 };
 
 struct TopkPlan {

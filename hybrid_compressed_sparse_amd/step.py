@@ -13,8 +13,9 @@ from typing import Optional
 
 import torch
 
-from . import compress_kv, index_topk, index_topk_workspace_size, sparse_mla_decode, \
-    sparse_mla_prefill_chunk, sparse_mla_prefill_workspace_size, sparse_mla_workspace_size
+from . import compress_kv, index_topk, index_topk_chunk, index_topk_workspace_size, \
+    sparse_mla_decode, sparse_mla_prefill_chunk, sparse_mla_prefill_workspace_size, \
+    sparse_mla_workspace_size
 
 
 @dataclass
@@ -54,8 +55,12 @@ class PathStep:
 
     def select(self, ix_q, ix_q_scale, ix_w, ix_keys, q_seq, q_pos):
         s = self.shape
-        index_topk(ix_q, ix_q_scale, ix_w, ix_keys, q_seq, q_pos, s.m, s.topk, s.max_pos, self.idx,
-                   self.score, ws=self.ix_ws)
+        if s.prefill:
+            index_topk_chunk(ix_q, ix_q_scale, ix_w, ix_keys, s.seq, s.P0, s.m, s.topk, self.idx,
+                             self.score, ws=self.ix_ws)
+        else:
+            index_topk(ix_q, ix_q_scale, ix_w, ix_keys, q_seq, q_pos, s.m, s.topk, s.max_pos,
+                       self.idx, self.score, ws=self.ix_ws)
 
     def attend(self, q, swa, comp, q_seq=None, q_pos=None, sink=None, topk_idx=None):
         s = self.shape

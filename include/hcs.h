@@ -11,6 +11,7 @@
  *                             compressed cache in its format;
  *   hcs_index_topk            the Lightning Indexer of CSA layers: scores of every visible
  *                             compressed entry, I = sum_h w_h * ReLU(q_h . k), and the top-k;
+ *   hcs_index_topk_chunk      the same for a chunk of consecutive queries of one sequence;
  *   hcs_sparse_mla_decode     single-KV-head attention of every query head over the query's
  *                             sliding window plus its selected (CSA) or all visible (HCA)
  *                             compressed entries, K = V = the shared row;
@@ -147,6 +148,22 @@ hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w,
                           const int32_t* q_seq, const int32_t* q_pos, int N, int H_I, int d_I,
                           int m, int topk, int max_pos, int32_t* out_idx, float* out_score,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* Lightning-Indexer for a prefill chunk: hcs_index_topk for the Q consecutive queries    */
+/* P0 .. P0+Q-1 of sequence `seq` (the chunked prefill of "DeepSeek-V4 Inference on       */
+/* Ascend"; the same score and selection, each query with its own n_visible(p)). All      */
+/* queries read the same keys, so large chunks (Q >= 256, bf16 keys with d_I == 128,      */
+/* H_I % 4 == 0, and at most 32768 visible entries) are scored as one matrix product over */
+/* blocks of queries; the results are those of hcs_index_topk with q_seq[t] = seq and     */
+/* q_pos[t] = P0 + t, bit for bit.                                                        */
+/* q [Q, H_I, ...] and w [Q, H_I] as above; out_idx / out_score [Q, topk] as above.        */
+/* ws: hcs_index_topk_workspace_size(Q, P0 + Q - 1, m, topk) bytes, 256-byte aligned.      */
+/* Errors: as hcs_index_topk; P0, seq and Q must be >= 0 and P0 + Q - 1 must fit int32.   */
+hcs_status hcs_index_topk_chunk(const void* q, const uint8_t* q_scale, const float* w,
+                                hcs_paged keys, int seq, int P0, int Q, int H_I, int d_I, int m,
+                                int topk, int32_t* out_idx, float* out_score, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------ */
 /* Sparse MLA decode (single shared KV head, MQA).                                        */

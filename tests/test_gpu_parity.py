@@ -127,6 +127,27 @@ def test_prefill_full_sampled():
     _check_step(sc, queries=[0, 1, 2047, 4095])
 
 
+def test_indexer_chunk_matches_per_query_path():
+    """hcs_index_topk_chunk scores the queries of one sequence as one matrix product over
+    blocks of queries (a ragged last block of queries, a partly visible last block of entries);
+    its scores and selections are those of hcs_index_topk with explicit positions, bit for bit."""
+    wl = C.CSA_PREFILL.with_(P0=4096 + 2, Q=300, topk=256)
+    sc = G.build(wl, seed=11, device=_dev())
+    q, qs = U._ix_q_args(sc)
+    w = sc.ix_w.contiguous()
+    Q, k = w.shape[0], wl.topk
+    dev = _dev()
+    ia = torch.empty((Q, k), dtype=torch.int32, device=dev)
+    ib = torch.empty_like(ia)
+    sa = torch.empty((Q, k), dtype=torch.float32, device=dev)
+    sb = torch.empty_like(sa)
+    hcs.index_topk(q, qs, w, sc.ix, sc.q_seq, sc.q_pos, wl.m, k, wl.P0 + Q - 1, ia, sa)
+    hcs.index_topk_chunk(q, qs, w, sc.ix, int(sc.q_seq[0]), wl.P0, wl.m, k, ib, sb)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.sort(ia, dim=1).values, torch.sort(ib, dim=1).values)
+    assert torch.equal(torch.sort(sa, dim=1).values, torch.sort(sb, dim=1).values)
+
+
 def test_csa_decode_large_selection_ragged():
     """bf16 indexer keys with more than 32768 visible entries (threshold + filter + select path)
     in a ragged batch: a query below 32768 entries, one with fewer entries than k, one at
