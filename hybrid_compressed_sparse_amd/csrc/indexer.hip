@@ -40,6 +40,21 @@ constexpr int kTopkThreads = 1024;
 constexpr int kSingleMax = 32768;       // largest n_visible selected in one stage
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// max(x, 0) as one integer max on the bits (a negative float is a negative int32; -0 gives
+// +0). fmaxf costs two instructions here (it first quiets a possible NaN).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// v summed over lanes l, l ^ 16, l ^ 32, l ^ 48, in every lane, without LDS: after
+// v_permlane16_swap of v with itself its two results hold v and the value of lane l ^ 16 (in
+// one order or the other), and likewise v_permlane32_swap for lane l ^ 32. Each sum is the
+// same float as v + (value of the partner lane).
+__device__ __forceinline__ float sum_xor16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ void query_of(const IndexArgs& a, int t, int& seq, int& nv) {
   int pos;
   if (a.q_seq) {
@@ -218,10 +233,9 @@ __device__ __forceinline__ void score_block_bf16(const IndexArgs& a, uint8_t* sm
       for (int kk = 0; kk < KS; ++kk)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qreg[mt][kk], kreg[kk], acc, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part += wreg[mt][i] * fmaxf(acc[i], 0.f);
+      for (int i = 0; i < 4; ++i) part += wreg[mt][i] * relu(acc[i]);
     }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
+    part = sum_xor16_32(part);
     const int e = e_base + r;
     const float sv = pg >= 0 ? part : kNegInf;
     if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = sv;
@@ -257,21 +271,36 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(IndexAr
 // The scores of query t are stored one iteration later, after the wait for the copy of query
 // t+1: on gfx9 one counter covers loads and stores, and stores issued a whole query earlier
 // have completed by then, so that wait does not stall on them.
-constexpr int kChunkThreads = 512;
-constexpr int kChunkEntries = 512;               // entries per block (8 waves x 64)
+#ifndef HCS_CHUNK_WAVES
+#define HCS_CHUNK_WAVES 4
+#endif
+#ifndef HCS_CHUNK_TILES
+#define HCS_CHUNK_TILES 4
+#endif
+constexpr int kChunkWaves = HCS_CHUNK_WAVES;
+constexpr int kChunkThreads = 64 * kChunkWaves;
+constexpr int kChunkTiles = HCS_CHUNK_TILES;     // 16-entry tiles per wave
+constexpr int kChunkEntries = kChunkWaves * 16 * kChunkTiles;   // entries per block
 constexpr int kChunkQueries = 64;                // queries per block
 constexpr int kChunkMinQueries = 256;            // smaller chunks use the per-query kernel
+#ifndef HCS_CHUNK_PER_STEP
+#define HCS_CHUNK_PER_STEP 2
+#endif
+constexpr int kChunkPerStep = HCS_CHUNK_PER_STEP; // queries per barrier
 
 template <int MT>
-__global__ __launch_bounds__(kChunkThreads, 1) void index_score_chunk_kernel(IndexArgs a) {
+__global__ __launch_bounds__(kChunkThreads, 512 / kChunkThreads) void index_score_chunk_kernel(IndexArgs a) {
   constexpr int DI = 128, KS = DI / 32, RB = DI * 2, CPR = RB / 16;
   constexpr int PAGE = kPageRows * RB;
-  __shared__ __attribute__((aligned(16))) uint8_t qbuf[2][64 * RB];
-  __shared__ __attribute__((aligned(16))) float wbuf[2][64];
+  constexpr int QP = kChunkPerStep;               // queries per LDS slot (one barrier each)
+  __shared__ __attribute__((aligned(16))) uint8_t qbuf[2][QP][64 * RB];
+  __shared__ __attribute__((aligned(16))) float wbuf[2][QP][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int eb = blockIdx.x * kChunkEntries;                      // first entry of the block
-  const int e0 = eb + wave * 64;                                  // this wave's page
+  constexpr int NTW = kChunkTiles, HPW = 64 / kChunkWaves;        // heads each wave copies
+  static_assert(NTW == 4, "a wave's entries are one 64-entry page (score rows are whole pages)");
+  const int e0 = eb + wave * 16 * NTW;                            // this wave's entries
   // queries t0 .. t1-1; the first that sees any entry of the block is the first with
   // (p0 + t + 1) / m > eb, i.e. p0 + t + 1 >= (eb + 1) m
   const int t1 = min((int)(blockIdx.y + 1) * kChunkQueries, a.N);
@@ -279,94 +308,105 @@ __global__ __launch_bounds__(kChunkThreads, 1) void index_score_chunk_kernel(Ind
   const int t0 = (int)max<int64_t>((int64_t)blockIdx.y * kChunkQueries, t_vis);
   if (t0 >= t1 || eb >= a.nv_cap) return;                        // uniform over the block
 
-  // q rows and head weights of query t into slot `buf`: wave w copies heads 8w .. 8w+7 (rows
-  // of H_I or more read zeros); lanes 0..15 of wave 0 copy the 64 weights (H_I % 4 == 0)
+  // q rows and head weights of queries t .. t+QP-1 (those below t1) into slot `buf`: wave w
+  // copies heads HPW w .. +HPW-1, each lane at a constant offset from the query's q (a head of
+  // H_I or more reads the last real head; its weight is 0); lanes below H_I / 4 of wave 0 copy
+  // the weights (H_I % 4 == 0) into a slot whose other words stay zero
+  if (threadIdx.x < 2 * QP * 64) (&wbuf[0][0][0])[threadIdx.x] = 0.f;
+  uint32_t q_off[HPW / 4];
+#pragma unroll
+  for (int i = 0; i < HPW / 4; ++i) {
+    const int h = HPW * wave + 4 * i + lane / CPR, c = lane % CPR;
+    q_off[i] = (uint32_t)(min(h, a.H_I - 1) * RB + ((c ^ (h & 15)) << 4));
+  }
   auto copy_q = [&](int t, int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int h = 8 * wave + 4 * i + lane / CPR, c = lane % CPR;
-      const uint8_t* src = h < a.H_I ? a.q + ((int64_t)t * a.H_I + h) * RB + ((c ^ (h & 15)) << 4)
-                                     : g_ix_zero + lane * 16;
-      dma16v(src, lds_addr(qbuf[buf]) + (8 * wave + 4 * i) * RB);
-    }
-    if (wave == 0 && lane < 16) {
-      const int h = 4 * lane;
-      const void* src = h < a.H_I ? (const void*)(a.w + (int64_t)t * a.H_I + h) : (const void*)g_ix_zero;
-      dma16v(src, lds_addr(wbuf[buf]));
+    for (int u = 0; u < QP; ++u) {
+      if (t + u >= t1) break;
+      const uint8_t* qt = a.q + (int64_t)(t + u) * a.H_I * RB;
+#pragma unroll
+      for (int i = 0; i < HPW / 4; ++i) dma16(qt, q_off[i], lds_addr(qbuf[buf][u]) + (HPW * wave + 4 * i) * RB);
+      if (wave == 0 && lane < a.H_I / 4)
+        dma16(reinterpret_cast<const uint8_t*>(a.w + (int64_t)(t + u) * a.H_I), (uint32_t)lane * 16,
+              lds_addr(wbuf[buf][u]));
     }
   };
+  __syncthreads();                               // zeroed weight slots before any copy
   copy_q(t0, 0);
 
   // keys: kreg[nt][ks] = elements 32 ks + 8 g .. +7 of entry e0 + 16 nt + l16 (B operand)
-  bf16x8 kreg[4][KS];
-  {
-    const int pg = e0 < a.nv_cap ? page_of(a.keys, a.seq_const, e0) : -1;
+  bf16x8 kreg[NTW][KS];
+#pragma unroll
+  for (int p = 0; p < NTW / 4; ++p) {                             // one 64-entry page each
+    const int ep = e0 + 64 * p;
+    const int pg = ep < a.nv_cap ? page_of(a.keys, a.seq_const, ep) : -1;
     const uint8_t* page = pg >= 0 ? a.keys.base + (int64_t)pg * PAGE : nullptr;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int n4 = 0; n4 < 4; ++n4)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const i32x4 v = page ? *(const i32x4*)(page + (16 * nt + l16) * RB + 64 * ks + 16 * g)
+        const i32x4 v = page ? *(const i32x4*)(page + (16 * n4 + l16) * RB + 64 * ks + 16 * g)
                              : i32x4{0, 0, 0, 0};
-        kreg[nt][ks] = __builtin_bit_cast(bf16x8, v);
+        kreg[4 * p + n4][ks] = __builtin_bit_cast(bf16x8, v);
       }
   }
 
-  float sc[4] = {0.f, 0.f, 0.f, 0.f};           // scores of the previous query, not yet stored
-  int t_prev = -1, nv_prev = 0;
-  for (int t = t0, it = 0; t < t1; ++t, ++it) {
+  // scores of the previous step, not yet stored. A query's row is written for every entry of
+  // this wave's page, also those it does not see (the selection reads only visible ones); the
+  // row stride covers every page below nv_cap.
+  float sc[QP][NTW];
+  int t_prev = -1;
+  const bool wave_has_entries = e0 < a.nv_cap;
+  auto store_prev = [&]() {
+    if (t_prev < 0 || !wave_has_entries || g != 0) return;
+#pragma unroll
+    for (int u = 0; u < QP; ++u) {
+      const int t = t_prev + u;
+      if (t >= t1) break;
+      float* row = a.scores + (int64_t)t * a.score_stride + e0 + l16;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) row[16 * nt] = sc[u][nt];
+    }
+  };
+  for (int t = t0, it = 0; t < t1; t += QP, ++it) {
     const int buf = it & 1;
-    wait_vm_zero();                              // this wave's copies of query t (and keys)
-    lds_barrier();                               // every wave's copies of query t
-    // the previous query's scores (entries below its visible count)
-    if (t_prev >= 0 && g == 0) {
+    wait_vm_zero();                              // this wave's copies of this step (and keys)
+    lds_barrier();                               // every wave's copies of this step
+    store_prev();
+    if (t + QP < t1) copy_q(t + QP, buf ^ 1);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int e = e0 + 16 * nt + l16;
-        if (e < nv_prev) a.scores[(int64_t)t_prev * a.score_stride + e] = sc[nt];
-      }
-    }
-    if (t + 1 < t1) copy_q(t + 1, buf ^ 1);
-    bf16x8 qa[MT][KS];
-    float wreg[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int h = mt * 16 + l16;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qa[mt][ks] = *(const bf16x8*)(qbuf[buf] + h * RB + (((4 * ks + g) ^ (h & (CPR - 1))) << 4));
-      const f32x4 w4 = *(const f32x4*)(wbuf[buf] + mt * 16 + 4 * g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wreg[mt][i] = w4[i];
-    }
-    int seq, nv;
-    query_of(a, t, seq, nv);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      float part = 0.f;
+    for (int u = 0; u < QP; ++u) {
+      bf16x8 qa[MT][KS];
+      float wreg[MT][4];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int h = mt * 16 + l16;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kreg[nt][ks], acc, 0, 0, 0);
+          qa[mt][ks] = *(const bf16x8*)(qbuf[buf][u] + h * RB + (((4 * ks + g) ^ (h & (CPR - 1))) << 4));
+        const f32x4 w4 = *(const f32x4*)(wbuf[buf][u] + mt * 16 + 4 * g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part += wreg[mt][i] * fmaxf(acc[i], 0.f);
+        for (int i = 0; i < 4; ++i) wreg[mt][i] = w4[i];
       }
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
-      sc[nt] = part;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        float part = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kreg[nt][ks], acc, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part += wreg[mt][i] * relu(acc[i]);
+        }
+        part = sum_xor16_32(part);
+        sc[u][nt] = part;
+      }
     }
     t_prev = t;
-    nv_prev = nv;
   }
-  if (g == 0) {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int e = e0 + 16 * nt + l16;
-      if (e < nv_prev) a.scores[(int64_t)t_prev * a.score_stride + e] = sc[nt];
-    }
-  }
+  store_prev();
 }
 
 // ---------------------------------------------------------------- MXFP4 scores (d_I = 128)
@@ -463,10 +503,9 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexA
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kbv, acc, 4, 4, 0, qs[mt], 0, ksc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part += wreg[mt][i] * fmaxf(acc[i], 0.f);
+        for (int i = 0; i < 4; ++i) part += wreg[mt][i] * relu(acc[i]);
       }
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
+      part = sum_xor16_32(part);
       const int e = e_base + 64 * p + r;
       const float sv = pgs[p] >= 0 ? part : kNegInf;
       if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = sv;
