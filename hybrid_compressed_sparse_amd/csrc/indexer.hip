@@ -523,12 +523,17 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexA
 constexpr int kDigitBits = 11;                 // radix digit: 2048 bins
 constexpr int kBins = 1 << kDigitBits;
 
+constexpr int kCandMax = 64;            // a k-th key bin this small is resolved by ranking
+
 struct SelShared {
   unsigned hist[2][kBins];               // pass p counts into hist[p & 1]; the other is cleared
   unsigned wsum[16];                     // per-wave bin totals of a pass
   unsigned bin, above, cnt_bin;
   unsigned kmax, kmin, count;            // range and number of the participating keys
   unsigned out_count;
+  uint32_t cand_key[kCandMax];           // the keys of the k-th key's bin, and their ids
+  int cand_id[kCandMax];
+  unsigned cand_count;
 };
 
 // Wave-wide reductions through DPP row operations (no LDS round trips); every lane gets the result.
@@ -578,7 +583,7 @@ struct KthResult {
 // this is usually the first pass). One barrier for the range, three per pass. Expects
 // sel_reset() state; leaves it reset (ordered by the caller's next barrier).
 template <int NT, class KeyOf>
-__device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
+__device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of, unsigned small_bin = 0) {
   static_assert(NT % 64 == 0 && NT >= 256 && NT <= 1024 && kBins % NT == 0, "block size");
   constexpr int BPT = kBins / NT;        // bins per thread in the scan
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -646,7 +651,10 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
     if (lane == 63) sh.wsum[wave] = run + tot;
     for (int j = tid; j < kBins; j += NT) sh.hist[(pass & 1) ^ 1][j] = 0;   // the next pass's
     __syncthreads();
-    for (int w = 0; w < wave; ++w) run += sh.wsum[w];
+    {
+      const unsigned ws = lane < wave ? sh.wsum[lane] : 0u;   // lower waves' totals
+      run += wave_sum_u32(ws);
+    }
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
       if (run < remaining && run + c[j] >= remaining) {
@@ -665,7 +673,7 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
     // hist[pass & 1] was counted into; clear it for a later pass or call (ordered by the
     // barriers that follow before any reuse)
     for (int j = tid; j < kBins; j += NT) hist[j] = 0;
-    if (cnt_bin == remaining) break;
+    if (cnt_bin == remaining || cnt_bin <= small_bin) break;
   }
   if (tid == 0) {                        // range state for a later call
     sh.kmax = 0u;
@@ -681,14 +689,21 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of) {
 
 // Select the top-k of n elements (n > k) given key_of(i, key) and id_of(i); writes k ids (and
 // scores) in arbitrary order. Ties at the k-th key go to the smaller ids.
+// The radix passes stop as soon as the bin holding the k-th key has at most kCandMax keys;
+// those candidates are gathered and ranked by one wave (larger key first, then smaller id), and
+// the r.need best are taken with every key above the bin. Only a larger bin of keys that are
+// all equal to the k-th falls back to a second select on ~id.
 template <int NT, class KeyOf, class IdOf, class Emit>
 __device__ void block_topk(SelShared& sh, int n, int k, KeyOf key_of, IdOf id_of, Emit emit) {
-  const KthResult r = radix_kth<NT>(sh, n, (unsigned)k, key_of);
-  // ties (only possible when every bit was resolved: mask = ~0): of the keys equal to the k-th,
-  // take the r.need smallest ids, i.e. the largest ~id
-  bool tie_break = r.n_eq > r.need;
+  const KthResult r = radix_kth<NT>(sh, n, (unsigned)k, key_of, kCandMax);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t below = (1ull << lane) - 1;
+  const bool partial = r.n_eq > r.need;            // only part of the k-th key's bin is taken
+  const bool ranked = partial && r.n_eq <= (unsigned)kCandMax;
+  // ties of more than kCandMax equal keys (every bit resolved): the r.need smallest ids, i.e.
+  // the largest ~id
   KthResult r2{};
-  if (tie_break) {
+  if (partial && !ranked) {
     __syncthreads();
     r2 = radix_kth<NT>(
         sh, n, r.need,
@@ -699,41 +714,74 @@ __device__ void block_topk(SelShared& sh, int n, int k, KeyOf key_of, IdOf id_of
           return true;
         });
   }
-  if (threadIdx.x == 0) sh.out_count = 0;
+  if (threadIdx.x == 0) {
+    sh.out_count = 0;
+    sh.cand_count = 0;
+  }
   __syncthreads();
-  // one counter update per wave: lanes take consecutive slots from the wave's base
-  const int lane = threadIdx.x & 63;
+  // keys above the bin (and the whole bin unless only part of it is taken); the bin's keys go
+  // to the candidate slots when they are ranked. One counter update per wave.
   for (int i0 = threadIdx.x & ~63; i0 < n; i0 += NT) {
     const int i = i0 + lane;
     uint32_t key = 0;
-    bool take = i < n && key_of(i, key);
-    if (take) {
+    bool take = false, cand = false;
+    if (i < n && key_of(i, key)) {
       const uint32_t km = key & r.mask;
       take = km > r.prefix;
       if (km == r.prefix) {
-        if (!tie_break) take = true;
-        else {
-          const uint32_t ik = ~(uint32_t)id_of(i);
-          take = (ik & r2.mask) > r2.prefix || (ik & r2.mask) == r2.prefix;   // ids are distinct
-        }
+        if (!partial) take = true;
+        else if (ranked) cand = true;
+        else take = ((~(uint32_t)id_of(i)) & r2.mask) >= r2.prefix;     // ids are distinct
       }
     }
     const uint64_t tm = __ballot(take);
-    if (tm == 0) continue;
-    unsigned base = 0;
-    if (lane == __builtin_ctzll(tm)) base = atomicAdd(&sh.out_count, (unsigned)__popcll(tm));
-    base = __shfl(base, __builtin_ctzll(tm), 64);
-    if (take) emit(base + (unsigned)__popcll(tm & ((1ull << lane) - 1)), id_of(i), key);
+    if (tm != 0) {
+      unsigned base = 0;
+      if (lane == __builtin_ctzll(tm)) base = atomicAdd(&sh.out_count, (unsigned)__popcll(tm));
+      base = __shfl(base, __builtin_ctzll(tm), 64);
+      if (take) emit(base + (unsigned)__popcll(tm & below), id_of(i), key);
+    }
+    if (ranked) {
+      const uint64_t cm = __ballot(cand);
+      if (cm != 0) {
+        unsigned base = 0;
+        if (lane == __builtin_ctzll(cm)) base = atomicAdd(&sh.cand_count, (unsigned)__popcll(cm));
+        base = __shfl(base, __builtin_ctzll(cm), 64);
+        if (cand) {
+          const unsigned slot = base + (unsigned)__popcll(cm & below);
+          sh.cand_key[slot] = key;
+          sh.cand_id[slot] = id_of(i);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (ranked && wave == 0) {
+    // rank of candidate `lane` among the n_eq (all in LDS now): larger key first, then smaller id
+    const int nc = (int)r.n_eq;
+    const uint32_t mk = lane < nc ? sh.cand_key[lane] : 0u;
+    const int mi = lane < nc ? sh.cand_id[lane] : 0;
+    unsigned rank = 0;
+    for (int j = 0; j < nc; ++j) {
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, j);
+      const int ij = __builtin_amdgcn_readlane(mi, j);
+      rank += (kj > mk || (kj == mk && ij < mi)) ? 1u : 0u;
+    }
+    const bool take = lane < nc && rank < r.need;
+    const uint64_t tm = __ballot(take);
+    const unsigned base = sh.out_count;           // every other key is counted by now
+    if (take) emit(base + (unsigned)__popcll(tm & below), mi, mk);
   }
   __syncthreads();
 }
 
 // One query per workgroup: short-context fill or one-stage select over its scores.
-__global__ __launch_bounds__(kTopkThreads) void topk_single_kernel(IndexArgs a, int k,
-                                                                   int32_t* out_idx,
-                                                                   float* out_score) {
+// NT threads, at most KL visible entries.
+template <int NT, int KL>
+__global__ __launch_bounds__(NT) void topk_single_kernel(IndexArgs a, int k, int32_t* out_idx,
+                                                         float* out_score) {
   __shared__ SelShared sh;
-  __shared__ uint32_t kl[kSingleMax];    // the query's order keys, read once from memory
+  __shared__ uint32_t kl[KL];            // the query's order keys, read once from memory
   const int t = blockIdx.x;
   int seq, nv;
   query_of(a, t, seq, nv);
@@ -741,17 +789,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_single_kernel(IndexArgs a, 
   int32_t* oi = out_idx + (int64_t)t * k;
   float* os = out_score ? out_score + (int64_t)t * k : nullptr;
   if (nv <= k) {
-    for (int j = threadIdx.x; j < k; j += kTopkThreads) {
+    for (int j = threadIdx.x; j < k; j += NT) {
       oi[j] = j < nv ? j : -1;
       if (os) os[j] = j < nv ? sc[j] : 0.f;
     }
     return;
   }
 #pragma unroll 8
-  for (int i = threadIdx.x; i < nv; i += kTopkThreads) kl[i] = f32_order_key(sc[i]);
-  sel_reset<kTopkThreads>(sh);
+  for (int i = threadIdx.x; i < nv; i += NT) kl[i] = f32_order_key(sc[i]);
+  sel_reset<NT>(sh);
   __syncthreads();
-  block_topk<kTopkThreads>(
+  block_topk<NT>(
       sh, nv, k, [&](int i, uint32_t& key) { key = kl[i]; return true; },
       [&](int i) { return i; },
       [&](unsigned slot, int id, uint32_t key) {
@@ -941,8 +989,8 @@ hipError_t launch_topk(const IndexArgs& a, const TopkPlan& plan, int topk, int32
                        float* out_score, uint8_t* ws, int blk_entries, hipStream_t stream) {
   if (a.N == 0) return hipSuccess;
   if (!plan.large) {
-    hipLaunchKernelGGL(topk_single_kernel, dim3(a.N), dim3(kTopkThreads), 0, stream, a, topk,
-                       out_idx, out_score);
+    hipLaunchKernelGGL((topk_single_kernel<kTopkThreads, kSingleMax>), dim3(a.N), dim3(kTopkThreads),
+                       0, stream, a, topk, out_idx, out_score);
     return hipGetLastError();
   }
   const int64_t cstride = a.score_stride;
