@@ -122,6 +122,13 @@ def test_prefill_small():
     _check_step(sc, queries=[0, 1, 2, 3, 150, 297, 298, 299])
 
 
+def test_prefill_long_splits():
+    """A query's 1128 rows (18 blocks, the last ragged) in one split of the attention kernel."""
+    wl = C.CSA_PREFILL.with_(P0=4096 + 3, Q=256, topk=1000)
+    sc = G.build(wl, seed=12, device=_dev())
+    _check_step(sc, queries=[0, 1, 100, 254, 255])
+
+
 def test_prefill_full_sampled():
     sc = G.build(C.CSA_PREFILL, seed=0, device=_dev())
     _check_step(sc, queries=[0, 1, 2047, 4095])
