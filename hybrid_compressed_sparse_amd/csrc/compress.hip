@@ -10,9 +10,9 @@
 // partial block's KV and scores), each channel keeps the online-softmax triple
 // (running max M, running sum Z of e^(z-M), running sum A of e^(z-M) * kv) in float32: the
 // same entry A/Z, O(d) state per sequence whatever m is, and no re-gather of the block when it
-// completes. One workgroup walks one block of one sequence; each thread owns channels and
-// streams the block's tokens through the recurrence (rows are read coalesced across
-// channels). A completed entry is written straight into the paged compressed cache, either as
+// completes. One workgroup walks one block of one sequence for 256 channels; each thread owns
+// one channel and streams the block's tokens through the recurrence (rows are read coalesced
+// across channels). A completed entry is written straight into the paged compressed cache, either as
 // a bf16 row or as an fp8_ds record (per 64-dim latent block: power-of-two scale, e4m3 codes by
 // the hardware's round-to-nearest-even conversion; the 64 rotary dims as bf16). The block's
 // amax is a wave reduction, because one wave covers exactly one 64-channel block.
@@ -41,6 +41,8 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
   const int dpad = (d + 63) & ~63;
   const float kNegInf = -__builtin_huge_valf();
   float* st = a.state + (int64_t)b * 3 * d;
+  // this workgroup's channels (blockIdx.z: groups of kThreads channels, whole 64-channel waves)
+  const int c0 = blockIdx.z * kThreads, c1 = min(dpad, c0 + kThreads);
 
   // The first block (which may resume from the carried state) and the last block (which
   // leaves the state for the next call) are walked by the same workgroup, first then last, so
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
         page = a.comp_base + (int64_t)pg * pb;
       }
     }
-    for (int c = threadIdx.x; c < dpad; c += kThreads) {
+    for (int c = c0 + threadIdx.x; c < c1; c += kThreads) {
       const bool act = c < d;
       float M = kNegInf, Z = 0.f, A = 0.f;
       if (act) {
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
         const float C = act ? A / Z : 0.f;
         if (act && a.dbg) a.dbg[(int64_t)b * a.dbg_stride + (int64_t)(kb - kb_first) * d + c] = C;
         if (a.fmt == HCS_FMT_FP8DS) {
-          // one wave = one 64-channel block (dpad is a multiple of 64 and c steps by 256)
+          // one wave = one 64-channel block (dpad and c0 are multiples of 64)
           if (c < kFp8Latent) {
             const float amax = warp_max(fabsf(C));
             // smallest e with amax <= 448 * 2^e; 448 = 0.875 * 2^9
@@ -143,9 +145,12 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
 
 hipError_t launch_compress(const CompressArgs& a, int max_new, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
-  // one workgroup for the first and last block of each sequence, one per middle block
+  // one workgroup for the first and last block of each sequence, one per middle block, each
+  // split over channel groups of kThreads (one channel per thread: the state and token loads of
+  // a thread are one memory round trip)
   const int slots = std::min(65535, std::max(1, (max_new + a.m - 1) / a.m));
-  hipLaunchKernelGGL(compress_kernel, dim3(a.B, slots), dim3(kThreads), 0, stream, a);
+  const int groups = ((a.d + 63) / 64 * 64 + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(compress_kernel, dim3(a.B, slots, groups), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
