@@ -56,6 +56,10 @@ def lib() -> ctypes.CDLL:
         L.hcs_index_topk_chunk.restype = i32
         L.hcs_index_topk_chunk.argtypes = [vp, vp, vp, Paged, i32, i32, i32, i32, i32, i32, i32, vp, vp,
                                            vp, sz, vp]
+        L.hcs_index_topk_compress.restype = i32
+        L.hcs_index_topk_compress.argtypes = [vp, vp, vp, Paged, vp, vp, i32, i32, i32, i32, i32, i32,
+                                              vp, vp, vp, sz, vp, vp, i32, i64, vp, vp, i32, i32, i32,
+                                              i32, vp, vp, Paged, vp]
         L.hcs_sparse_mla_workspace_size.restype = sz
         L.hcs_sparse_mla_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.hcs_sparse_mla_decode.restype = i32
@@ -168,6 +172,34 @@ def index_topk_chunk(q, q_scale: Optional[torch.Tensor], w: torch.Tensor, keys, 
         _as_paged(keys), seq, P0, Q, H_I, d_I, m, topk, _ptr(out_idx, torch.int32, "out_idx"),
         _ptr(out_score, torch.float32, "out_score"), _ptr(ws, name="ws"),
         0 if ws is None else ws.numel() * ws.element_size(), _stream()), "index_topk_chunk")
+
+
+def index_topk_compress(q, q_scale: Optional[torch.Tensor], w: torch.Tensor, keys, q_seq: torch.Tensor,
+                        q_pos: torch.Tensor, m_ix: int, topk: int, max_pos: int, out_idx: torch.Tensor,
+                        out_score: Optional[torch.Tensor], ws: Optional[torch.Tensor],
+                        kv: torch.Tensor, score: torch.Tensor, cu_new: torch.Tensor,
+                        start_pos: torch.Tensor, state: torch.Tensor, comp, m: int,
+                        ape: Optional[torch.Tensor] = None, max_new: Optional[int] = None) -> None:
+    """hcs_index_topk_compress: index_topk(q .. ws) and compress_kv(kv .. m, ape) of one decode
+    step in one launch."""
+    N, H_I = w.shape
+    d_I = keys.dim
+    if kv.dtype != score.dtype or kv.dtype not in IN_DTYPE:
+        raise TypeError("kv and score must both be bf16 or both float32")
+    if max_new is None:
+        raise ValueError("max_new (host bound of new tokens per sequence) is required")
+    if ws is None:
+        ws = _workspace(index_topk_workspace_size(N, max_pos, m_ix, topk), w.device)
+    _check(lib().hcs_index_topk_compress(
+        _ptr(q, name="q"), _ptr(q_scale, torch.uint8, "q_scale"), _ptr(w, torch.float32, "w"),
+        _as_paged(keys), _ptr(q_seq, torch.int32, "q_seq"), _ptr(q_pos, torch.int32, "q_pos"),
+        N, H_I, d_I, m_ix, topk, max_pos, _ptr(out_idx, torch.int32, "out_idx"),
+        _ptr(out_score, torch.float32, "out_score"), _ptr(ws, name="ws"),
+        0 if ws is None else ws.numel() * ws.element_size(),
+        _ptr(kv, name="kv"), _ptr(score, name="score"), IN_DTYPE[kv.dtype], kv.stride(0),
+        _ptr(cu_new, torch.int32, "cu_new"), _ptr(start_pos, torch.int32, "start_pos"),
+        start_pos.shape[0], max_new, kv.shape[-1], m, _ptr(ape, torch.float32, "ape"),
+        _ptr(state, torch.float32, "state"), _as_paged(comp), _stream()), "index_topk_compress")
 
 
 # ------------------------------------------------------------------------------ attention

@@ -55,15 +55,17 @@ const char* hcs_last_error(void) { return g_err; }
 int hcs_abi_version(void) { return HCS_ABI_VERSION; }
 
 // ------------------------------------------------------------------------------ compressor
-hcs_status hcs_compress_kv(const void* kv, const void* score, int in_dtype, int64_t row_stride,
-                           const int32_t* cu_new, const int32_t* start_pos, int B, int max_new,
-                           int d, int m, const float* ape, float* state, hcs_paged comp,
-                           float* dbg, int64_t dbg_seq_stride, void* stream) {
+// Checks of hcs_compress_kv; fills `a` (nothing is launched). B == 0 returns HCS_OK with a.B 0.
+static hcs_status prep_compress(const void* kv, const void* score, int in_dtype, int64_t row_stride,
+                                const int32_t* cu_new, const int32_t* start_pos, int B, int max_new,
+                                int d, int m, const float* ape, float* state, hcs_paged comp,
+                                float* dbg, int64_t dbg_seq_stride, hcs::CompressArgs& a) {
+  a = hcs::CompressArgs{};
   if (B < 0) return fail(HCS_ERR_INVALID_ARG, "B must be >= 0");
   if (d < 1 || d > 1024 || d % 8) return fail(HCS_ERR_UNSUPPORTED, "d must be in 1..1024 and a multiple of 8");
   if (m < 1 || m > 1024) return fail(HCS_ERR_UNSUPPORTED, "m must be in 1..1024");
   if (in_dtype != HCS_IN_BF16 && in_dtype != HCS_IN_F32) return fail(HCS_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
-  if (B == 0) return ok();
+  if (B == 0) return HCS_OK;
   if (!kv || !score || !cu_new || !start_pos || !state)
     return fail(HCS_ERR_INVALID_ARG, "null kv, score, cu_new, start_pos or state");
   if (row_stride < d) return fail(HCS_ERR_INVALID_ARG, "row_stride %lld < d %d", (long long)row_stride, d);
@@ -71,7 +73,6 @@ hcs_status hcs_compress_kv(const void* kv, const void* score, int in_dtype, int6
   hcs_status s = check_paged(comp, "comp", d, true, false);
   if (s != HCS_OK) return s;
   if (dbg && dbg_seq_stride < 0) return fail(HCS_ERR_INVALID_ARG, "negative dbg_seq_stride");
-  hcs::CompressArgs a{};
   a.kv = kv;
   a.score = score;
   a.in_bf16 = in_dtype == HCS_IN_BF16;
@@ -90,6 +91,17 @@ hcs_status hcs_compress_kv(const void* kv, const void* score, int in_dtype, int6
   a.comp_num_pages = comp.num_pages;
   a.dbg = dbg;
   a.dbg_stride = dbg_seq_stride;
+  return HCS_OK;
+}
+
+hcs_status hcs_compress_kv(const void* kv, const void* score, int in_dtype, int64_t row_stride,
+                           const int32_t* cu_new, const int32_t* start_pos, int B, int max_new,
+                           int d, int m, const float* ape, float* state, hcs_paged comp,
+                           float* dbg, int64_t dbg_seq_stride, void* stream) {
+  hcs::CompressArgs a;
+  const hcs_status s = prep_compress(kv, score, in_dtype, row_stride, cu_new, start_pos, B, max_new, d, m,
+                                     ape, state, comp, dbg, dbg_seq_stride, a);
+  if (s != HCS_OK || B == 0) return s == HCS_OK ? ok() : s;
   return hip_status(hcs::launch_compress(a, max_new, static_cast<hipStream_t>(stream)), "compress_kv");
 }
 
@@ -99,18 +111,20 @@ size_t hcs_index_topk_workspace_size(int N, int max_pos, int m, int topk) {
   return hcs::topk_plan(N, max_pos, m, topk).ws_bytes;
 }
 
-// Checks and launches shared by both indexer entry points; q_seq == NULL means a chunk of
-// queries of sequence `seq` at positions P0 .. P0+N-1.
-static hcs_status run_index(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
-                            const int32_t* q_seq, const int32_t* q_pos, int seq, int P0, int N,
-                            int H_I, int d_I, int m, int topk, int max_pos, int32_t* out_idx,
-                            float* out_score, void* ws, size_t ws_bytes, void* stream) {
+// Checks shared by the indexer entry points; fills `a` and `plan` (nothing is launched; N == 0
+// returns HCS_OK with a.N 0). q_seq == NULL means a chunk of queries of sequence `seq` at
+// positions P0 .. P0+N-1.
+static hcs_status prep_index(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
+                             const int32_t* q_seq, const int32_t* q_pos, int seq, int P0, int N,
+                             int H_I, int d_I, int m, int topk, int max_pos, int32_t* out_idx,
+                             void* ws, size_t ws_bytes, hcs::IndexArgs& a, hcs::TopkPlan& plan) {
+  a = hcs::IndexArgs{};
   if (N < 0) return fail(HCS_ERR_INVALID_ARG, "N must be >= 0");
   if (H_I < 1 || H_I > 64) return fail(HCS_ERR_UNSUPPORTED, "H_I must be in 1..64");
   if (m < 1) return fail(HCS_ERR_INVALID_ARG, "m must be >= 1");
   if (topk < 1 || topk > 4096) return fail(HCS_ERR_UNSUPPORTED, "topk must be in 1..4096");
   if (max_pos < 0) return fail(HCS_ERR_INVALID_ARG, "max_pos must be >= 0");
-  if (N == 0) return ok();
+  if (N == 0) return HCS_OK;
   if (!q || !w || !out_idx) return fail(HCS_ERR_INVALID_ARG, "null q, w or out_idx");
   hcs_status s = check_paged(keys, "keys", d_I, false, true);
   if (s != HCS_OK) return s;
@@ -122,11 +136,10 @@ static hcs_status run_index(const void* q, const uint8_t* q_scale, const float* 
   if ((int64_t)keys.pt_stride * HCS_PAGE_ROWS < (int64_t)(max_pos + 1) / m)
     return fail(HCS_ERR_INVALID_ARG, "keys: pt_stride %d does not cover %d entries", keys.pt_stride,
                 (max_pos + 1) / m);
-  const hcs::TopkPlan plan = hcs::topk_plan(N, max_pos, m, topk);
+  plan = hcs::topk_plan(N, max_pos, m, topk);
   if (!ws || ws_bytes < plan.ws_bytes)
     return fail(HCS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.ws_bytes, ws_bytes);
   if (!aligned(ws, 256)) return fail(HCS_ERR_INVALID_ARG, "ws must be 256-byte aligned");
-  hcs::IndexArgs a{};
   a.q = static_cast<const uint8_t*>(q);
   a.q_scale = q_scale;
   a.w = w;
@@ -150,12 +163,30 @@ static hcs_status run_index(const void* q, const uint8_t* q_scale, const float* 
     a.cand_count = reinterpret_cast<unsigned*>(w8 + plan.cnt_off);
     a.thr_stride = plan.thr_stride;
   }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = hcs::launch_index_scores(a, keys.fmt, st);
-  if (e != hipSuccess) return hip_status(e, "index_topk scores");
-  const int blk_entries = keys.fmt == HCS_FMT_MXFP4 ? 512 : 256;   // entries per scoring block
-  return hip_status(hcs::launch_topk(a, plan, topk, out_idx, out_score, w8, blk_entries, st),
+  return HCS_OK;
+}
+
+// The selection launch after the scores (entries per scoring block: 512 MXFP4, 256 bf16).
+static hcs_status run_topk(const hcs::IndexArgs& a, const hcs::TopkPlan& plan, int fmt, int topk,
+                           int32_t* out_idx, float* out_score, void* ws, void* stream) {
+  const int blk_entries = fmt == HCS_FMT_MXFP4 ? 512 : 256;
+  return hip_status(hcs::launch_topk(a, plan, topk, out_idx, out_score, static_cast<uint8_t*>(ws),
+                                     blk_entries, static_cast<hipStream_t>(stream)),
                     "index_topk select");
+}
+
+static hcs_status run_index(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
+                            const int32_t* q_seq, const int32_t* q_pos, int seq, int P0, int N,
+                            int H_I, int d_I, int m, int topk, int max_pos, int32_t* out_idx,
+                            float* out_score, void* ws, size_t ws_bytes, void* stream) {
+  hcs::IndexArgs a;
+  hcs::TopkPlan plan;
+  const hcs_status s = prep_index(q, q_scale, w, keys, q_seq, q_pos, seq, P0, N, H_I, d_I, m, topk,
+                                  max_pos, out_idx, ws, ws_bytes, a, plan);
+  if (s != HCS_OK || N == 0) return s == HCS_OK ? ok() : s;
+  const hipError_t e = hcs::launch_index_scores(a, keys.fmt, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "index_topk scores");
+  return run_topk(a, plan, keys.fmt, topk, out_idx, out_score, ws, stream);
 }
 
 hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
@@ -177,6 +208,41 @@ hcs_status hcs_index_topk_chunk(const void* q, const uint8_t* q_scale, const flo
   if (Q == 0) return ok();
   return run_index(q, q_scale, w, keys, nullptr, nullptr, seq, P0, Q, H_I, d_I, m, topk,
                    P0 + Q - 1, out_idx, out_score, ws, ws_bytes, stream);
+}
+
+hcs_status hcs_index_topk_compress(const void* q, const uint8_t* q_scale, const float* w,
+                                   hcs_paged keys, const int32_t* q_seq, const int32_t* q_pos, int N,
+                                   int H_I, int d_I, int m_ix, int topk, int max_pos,
+                                   int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes,
+                                   const void* kv, const void* score, int in_dtype,
+                                   int64_t row_stride, const int32_t* cu_new,
+                                   const int32_t* start_pos, int B, int max_new, int d, int m,
+                                   const float* ape, float* state, hcs_paged comp, void* stream) {
+  if (N > 0 && (!q_seq || !q_pos)) return fail(HCS_ERR_INVALID_ARG, "null q_seq or q_pos");
+  hcs::IndexArgs a;
+  hcs::TopkPlan plan;
+  hcs_status s = prep_index(q, q_scale, w, keys, q_seq, q_pos, 0, 0, N, H_I, d_I, m_ix, topk, max_pos,
+                            out_idx, ws, ws_bytes, a, plan);
+  if (s != HCS_OK) return s;
+  hcs::CompressArgs c;
+  s = prep_compress(kv, score, in_dtype, row_stride, cu_new, start_pos, B, max_new, d, m, ape, state,
+                    comp, nullptr, 0, c);
+  if (s != HCS_OK) return s;
+  if (comp.base == keys.base) return fail(HCS_ERR_INVALID_ARG, "comp and keys must be different caches");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (N == 0) {
+    if (B == 0) return ok();
+    return hip_status(hcs::launch_compress(c, max_new, st), "compress_kv");
+  }
+  hipError_t e;
+  if (keys.fmt == HCS_FMT_BF16 && !plan.large)
+    e = hcs::launch_index_scores_compress(a, c, max_new, st);
+  else {
+    e = B > 0 ? hcs::launch_compress(c, max_new, st) : hipSuccess;
+    if (e == hipSuccess) e = hcs::launch_index_scores(a, keys.fmt, st);
+  }
+  if (e != hipSuccess) return hip_status(e, "index_topk_compress scores");
+  return run_topk(a, plan, keys.fmt, topk, out_idx, out_score, ws, stream);
 }
 
 // ------------------------------------------------------------------------------ attention

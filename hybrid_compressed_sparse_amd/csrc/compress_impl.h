@@ -1,0 +1,141 @@
+// Compressor device code, shared by its own launch (compress.hip, which says what it computes
+// and how) and the indexer launch that runs compressor blocks beside its scoring blocks.
+#pragma once
+
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace hcs {
+
+constexpr int kCompressThreads = 256;
+
+__device__ __forceinline__ float compress_load_in(const void* p, int in_bf16, int64_t idx) {
+  if (in_bf16) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[idx]);
+  return static_cast<const float*>(p)[idx];
+}
+
+// The work of compressor block (b, y, z) of a grid with ny blocks along y (see compress_grid):
+// sequence b, block slot y, channel group z. Every thread of the block calls it.
+__device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int y, int z, int ny) {
+  const int row0 = a.cu_new[b];
+  const int n = a.cu_new[b + 1] - row0;
+  if (n <= 0) return;
+  const int start = a.start_pos[b];
+  const int m = a.m, d = a.d;
+  const int kb_first = start / m;
+  const int kb_last = (start + n - 1) / m;
+  const int dpad = (d + 63) & ~63;
+  const float kNegInf = -__builtin_huge_valf();
+  float* st = a.state + (int64_t)b * 3 * d;
+  // this workgroup's channels (group z of kCompressThreads channels, whole 64-channel waves)
+  const int c0 = z * kCompressThreads, c1 = min(dpad, c0 + kCompressThreads);
+
+  // The first block (which may resume from the carried state) and the last block (which
+  // leaves the state for the next call) are walked by the same workgroup, first then last, so
+  // the state is read before it is overwritten. Middle blocks are spread over the others.
+  auto do_block = [&](int kb) {
+    const int blk_lo = kb * m;
+    const int tok_lo = max(start, blk_lo);
+    const int tok_hi = min(start + n, blk_lo + m);
+    const bool complete = blk_lo + m <= start + n;
+    const bool resume = blk_lo < start;       // the block began in an earlier call
+    // destination of a completed entry
+    const uint8_t* page = nullptr;
+    const int slot = kb & 63;
+    if (complete) {
+      const int pg = (kb >> 6) < a.comp_pt_stride
+                         ? __ldg(a.comp_pt + (int64_t)b * a.comp_pt_stride + (kb >> 6)) : -1;
+      if (pg >= 0 && pg < a.comp_num_pages) {
+        const int64_t pb = a.fmt == HCS_FMT_FP8DS ? (int64_t)kFp8PageBytes : (int64_t)kPageRows * d * 2;
+        page = a.comp_base + (int64_t)pg * pb;
+      }
+    }
+    for (int c = c0 + threadIdx.x; c < c1; c += kCompressThreads) {
+      const bool act = c < d;
+      float M = kNegInf, Z = 0.f, A = 0.f;
+      if (act) {
+        if (resume) {
+          M = st[c];
+          Z = st[d + c];
+          A = st[2 * d + c];
+        }
+        for (int tok = tok_lo; tok < tok_hi; ++tok) {
+          const int64_t r = (int64_t)(row0 + tok - start) * a.row_stride + c;
+          float z = compress_load_in(a.score, a.in_bf16, r);
+          if (a.ape) z += a.ape[(int64_t)(tok - blk_lo) * d + c];
+          const float x = compress_load_in(a.kv, a.in_bf16, r);
+          const float Mn = fmaxf(M, z);
+          const float f_old = __expf(M - Mn);      // 0 when M = -inf
+          const float f_new = __expf(z - Mn);
+          Z = Z * f_old + f_new;
+          A = A * f_old + x * f_new;
+          M = Mn;
+        }
+      }
+      if (complete) {
+        const float C = act ? A / Z : 0.f;
+        if (act && a.dbg) a.dbg[(int64_t)b * a.dbg_stride + (int64_t)(kb - kb_first) * d + c] = C;
+        if (a.fmt == HCS_FMT_FP8DS) {
+          // one wave = one 64-channel block (dpad and c0 are multiples of 64)
+          if (c < kFp8Latent) {
+            const float amax = warp_max(fabsf(C));
+            // smallest e with amax <= 448 * 2^e; 448 = 0.875 * 2^9
+            int E;
+            const float f = __builtin_frexpf(amax, &E);
+            int e = amax > 0.f ? E - 9 + (f > 0.875f ? 1 : 0) : 0;
+            e = max(-127, min(127, e));
+            const float y = __builtin_ldexpf(C, -e);
+            const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false);
+            if (page) {
+              uint8_t* pw = const_cast<uint8_t*>(page);
+              pw[kFp8PageCodes + slot * kFp8Latent + c] = (uint8_t)(packed & 0xff);
+              if ((c & 63) == 0) pw[kFp8PageScales + slot * 8 + (c >> 6)] = (uint8_t)(e + 127);
+              if (c == 0) pw[kFp8PageScales + slot * 8 + 7] = 0;
+            }
+          } else if (act && page) {
+            uint16_t* rope = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(page) + kFp8PageRope +
+                                                         slot * kFp8Rope * 2);
+            rope[c - kFp8Latent] = (uint16_t)f32_to_bf16_bits(C);
+          }
+        } else if (act && page) {
+          uint16_t* row = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(page)) + (int64_t)slot * d;
+          row[c] = (uint16_t)f32_to_bf16_bits(C);
+        }
+      }
+      if (act && kb == kb_last) {
+        if (complete) {
+          st[c] = kNegInf;
+          st[d + c] = 0.f;
+          st[2 * d + c] = 0.f;
+        } else {
+          st[c] = M;
+          st[d + c] = Z;
+          st[2 * d + c] = A;
+        }
+      }
+    }
+  };
+
+  if (y == 0) {
+    do_block(kb_first);
+    if (kb_last != kb_first) do_block(kb_last);
+  }
+  const int workers = ny > 1 ? ny - 1 : 1;
+  if (ny == 1 || y > 0) {
+    const int w0 = ny > 1 ? y - 1 : 0;
+    for (int kb = kb_first + 1 + w0; kb < kb_last; kb += workers) do_block(kb);
+  }
+}
+
+// Grid of a compressor launch: (sequences, block slots, channel groups): one workgroup for the
+// first and last block of each sequence, one per middle block, each split over channel groups
+// of kCompressThreads (one channel per thread: a thread's state and token loads are one memory
+// round trip).
+inline dim3 compress_grid(const CompressArgs& a, int max_new) {
+  const int slots = std::min(65535, std::max(1, (max_new + a.m - 1) / a.m));
+  const int groups = ((a.d + 63) / 64 * 64 + kCompressThreads - 1) / kCompressThreads;
+  return dim3(a.B, slots, groups);
+}
+
+}  // namespace hcs

@@ -29,7 +29,7 @@
 // is a lower bound of the query's k-th largest score, so keeping only the scores at or above it
 // loses nothing (a filter launch appends them as candidates), and the select then runs over the
 // few candidates left.
-#include "kernels.h"
+#include "compress_impl.h"
 
 namespace hcs {
 
@@ -159,10 +159,11 @@ struct Bf16ScoreLds {
   static constexpr int BYTES = 64 * RB + 4 * PAGE;    // q rows, then one key page per wave
 };
 
-// Scores of block (blockIdx.x = query, blockIdx.y = 256-entry chunk) into a.scores. Every
-// thread of the block must call it (it has one barrier); `smem` holds Bf16ScoreLds<DI>::BYTES.
+// Scores of query t, 256-entry chunk yb into a.scores. Every thread of the block must call it
+// (it has one barrier); `smem` holds Bf16ScoreLds<DI>::BYTES.
 template <int DI, int MT>
-__device__ __forceinline__ void score_block_bf16(const IndexArgs& a, uint8_t* smem, uint32_t (&tkeys)[4]) {
+__device__ __forceinline__ void score_block_bf16(const IndexArgs& a, uint8_t* smem, uint32_t (&tkeys)[4],
+                                                 int t, int yb) {
   constexpr int KS = DI / 32;
   constexpr int NT = 4;                  // 4 x 16 entries per wave
   constexpr int RB = Bf16ScoreLds<DI>::RB;
@@ -170,7 +171,6 @@ __device__ __forceinline__ void score_block_bf16(const IndexArgs& a, uint8_t* sm
   constexpr int RPI = 1024 / RB;         // rows per 1 KiB async load
   constexpr int PAGE = Bf16ScoreLds<DI>::PAGE;
   uint8_t* qs = smem;
-  const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   // query rows: wave w copies heads 16w .. 16w+15 (heads >= H_I read zeros)
@@ -194,7 +194,7 @@ __device__ __forceinline__ void score_block_bf16(const IndexArgs& a, uint8_t* sm
     }
   int seq, nv;
   query_of(a, t, seq, nv);
-  const int e_base = blockIdx.y * 256 + wave * 64;          // first entry of this wave's page
+  const int e_base = yb * 256 + wave * 64;                  // first entry of this wave's page
   const bool active = e_base < nv;
   const int pg = active ? page_of(a.keys, seq, e_base) : -1;
   uint8_t* kl = smem + 64 * RB + wave * PAGE;
@@ -249,12 +249,33 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(IndexAr
   __shared__ uint32_t wbest[4 * kMaxKb + 1];
   uint32_t tkeys[4];
   if (a.cand_count && blockIdx.y == 0 && threadIdx.x == 0) a.cand_count[blockIdx.x] = 0u;
-  score_block_bf16<DI, MT>(a, smem, tkeys);
+  score_block_bf16<DI, MT>(a, smem, tkeys, blockIdx.x, blockIdx.y);
   if (a.blk_thr) {
     int seq, nv;
     query_of(a, blockIdx.x, seq, nv);
     write_block_threshold<4, 4, 256>(a, nv, tkeys, wbest, wbest + 4 * kMaxKb);
   }
+}
+
+// Scoring blocks and compressor blocks in one launch (a decode step): the two touch disjoint
+// data (the indexer keys and scores; the KV compressor's state and compressed cache), so the
+// step saves one dependent launch. Blocks [0, nc) compress (they are short and start first),
+// the rest score: block nc + i is query i / chunks, chunk i % chunks.
+template <int DI, int MT>
+__global__ __launch_bounds__(kScoreThreads) void index_score_compress_kernel(IndexArgs a, CompressArgs c,
+                                                                              int chunks, int cy, int cz) {
+  static_assert(kScoreThreads == kCompressThreads, "one block size for both roles");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Bf16ScoreLds<DI>::BYTES];
+  const int nc = c.B * cy * cz;
+  const int bid = blockIdx.x;
+  if (bid < nc) {                                   // uniform over the block
+    const int z = bid % cz, y = (bid / cz) % cy, b = bid / (cz * cy);
+    compress_block(c, b, y, z, cy);
+    return;
+  }
+  const int i = bid - nc;
+  uint32_t tkeys[4];
+  score_block_bf16<DI, MT>(a, smem, tkeys, i / chunks, i % chunks);
 }
 
 // ---------------------------------------------------------------- bf16 scores, query chunks
@@ -982,6 +1003,29 @@ hipError_t launch_index_scores(const IndexArgs& a, int fmt, hipStream_t stream) 
   HCS_SCORE_CASE(64, 1) HCS_SCORE_CASE(64, 2) HCS_SCORE_CASE(64, 3) HCS_SCORE_CASE(64, 4)
   HCS_SCORE_CASE(128, 1) HCS_SCORE_CASE(128, 2) HCS_SCORE_CASE(128, 3) HCS_SCORE_CASE(128, 4)
 #undef HCS_SCORE_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_index_scores_compress(const IndexArgs& a, const CompressArgs& c, int max_new,
+                                        hipStream_t stream) {
+  const int MT = (a.H_I + 15) / 16;
+  if (a.N == 0 || a.nv_cap == 0) return launch_compress(c, max_new, stream);
+  if (c.B == 0) return launch_index_scores(a, HCS_FMT_BF16, stream);
+  const dim3 cg = compress_grid(c, max_new);
+  const int chunks = (a.nv_cap + 255) / 256;
+  const int64_t blocks = (int64_t)cg.x * cg.y * cg.z + (int64_t)a.N * chunks;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks);
+#define HCS_SC_CASE(DI_, MT_)                                                                       \
+  if (a.d_I == DI_ && MT == MT_) {                                                                  \
+    hipLaunchKernelGGL((index_score_compress_kernel<DI_, MT_>), grid, dim3(kScoreThreads), 0, stream, a, c, \
+                       chunks, (int)cg.y, (int)cg.z);                                                 \
+    return hipGetLastError();                                                                       \
+  }
+  HCS_SC_CASE(32, 1) HCS_SC_CASE(32, 2) HCS_SC_CASE(32, 3) HCS_SC_CASE(32, 4)
+  HCS_SC_CASE(64, 1) HCS_SC_CASE(64, 2) HCS_SC_CASE(64, 3) HCS_SC_CASE(64, 4)
+  HCS_SC_CASE(128, 1) HCS_SC_CASE(128, 2) HCS_SC_CASE(128, 3) HCS_SC_CASE(128, 4)
+#undef HCS_SC_CASE
   return hipErrorInvalidValue;
 }
 

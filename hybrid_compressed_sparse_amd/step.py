@@ -13,9 +13,9 @@ from typing import Optional
 
 import torch
 
-from . import compress_kv, index_topk, index_topk_chunk, index_topk_workspace_size, \
-    sparse_mla_decode, sparse_mla_prefill_chunk, sparse_mla_prefill_workspace_size, \
-    sparse_mla_workspace_size
+from . import compress_kv, index_topk, index_topk_chunk, index_topk_compress, \
+    index_topk_workspace_size, sparse_mla_decode, sparse_mla_prefill_chunk, \
+    sparse_mla_prefill_workspace_size, sparse_mla_workspace_size
 
 
 @dataclass
@@ -75,11 +75,18 @@ class PathStep:
     def run(self, *, q, swa, comp, q_seq, q_pos, c_kv, c_score, c_cu, c_start, c_state, c_max_new,
             ix_q=None, ix_q_scale=None, ix_w=None, ix_keys=None, ape=None, sink=None,
             dbg: Optional[torch.Tensor] = None):
-        """The step, in order on the current stream. (Running the compressor on a second stream,
-        overlapped with the indexer, measured slower inside a captured graph on MI355X: the
-        cross-stream joins cost more than the compressor.)"""
-        self.compress(c_kv, c_score, c_cu, c_start, c_state, comp, c_max_new, ape=ape, dbg=dbg)
-        if self.shape.topk:
-            self.select(ix_q, ix_q_scale, ix_w, ix_keys, q_seq, q_pos)
+        """The step, in order on the current stream. At decode the compressor and the indexer
+        share one launch (hcs_index_topk_compress: they touch disjoint data); running them on two
+        streams instead measured slower inside a captured graph on MI355X, where the cross-stream
+        joins cost more than the compressor."""
+        s = self.shape
+        if s.topk and not s.prefill and dbg is None:
+            index_topk_compress(ix_q, ix_q_scale, ix_w, ix_keys, q_seq, q_pos, s.m, s.topk, s.max_pos,
+                                self.idx, self.score, self.ix_ws, c_kv, c_score, c_cu, c_start, c_state,
+                                comp, s.m, ape=ape, max_new=c_max_new)
+        else:
+            self.compress(c_kv, c_score, c_cu, c_start, c_state, comp, c_max_new, ape=ape, dbg=dbg)
+            if s.topk:
+                self.select(ix_q, ix_q_scale, ix_w, ix_keys, q_seq, q_pos)
         self.attend(q, swa, comp, q_seq, q_pos, sink=sink)
         return self.out

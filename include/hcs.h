@@ -12,6 +12,8 @@
  *   hcs_index_topk            the Lightning Indexer of CSA layers: scores of every visible
  *                             compressed entry, I = sum_h w_h * ReLU(q_h . k), and the top-k;
  *   hcs_index_topk_chunk      the same for a chunk of consecutive queries of one sequence;
+ *   hcs_index_topk_compress   hcs_index_topk and hcs_compress_kv of one decode step in one
+ *                             launch (they touch disjoint data);
  *   hcs_sparse_mla_decode     single-KV-head attention of every query head over the query's
  *                             sliding window plus its selected (CSA) or all visible (HCA)
  *                             compressed entries, K = V = the shared row;
@@ -164,6 +166,26 @@ hcs_status hcs_index_topk_chunk(const void* q, const uint8_t* q_scale, const flo
                                 hcs_paged keys, int seq, int P0, int Q, int H_I, int d_I, int m,
                                 int topk, int32_t* out_idx, float* out_score, void* ws,
                                 size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* The indexer and the KV compressor of one decode step in one launch. On the pages the   */
+/* compressor and the indexer run side by side ("Code Reading Map", the multi-stream      */
+/* overlap of the compressor with the indexer's aux stream): the indexer reads the        */
+/* indexer key cache, the compressor writes the KV compressed cache and its state, and    */
+/* neither reads what the other writes. This call is hcs_index_topk(q .. out_score, ws)   */
+/* followed by hcs_compress_kv(kv .. comp) with dbg = NULL, with the same arguments,      */
+/* checks and results; bf16 keys with at most 32768 visible entries score and compress in */
+/* one grid, other cases launch the two as separate kernels. m_ix is the indexer's m      */
+/* (the keys' compression ratio), m the compressor's. `comp` must not be `keys`.          */
+/* Errors: those of either call; nothing is launched if either set of arguments fails.    */
+hcs_status hcs_index_topk_compress(const void* q, const uint8_t* q_scale, const float* w,
+                                   hcs_paged keys, const int32_t* q_seq, const int32_t* q_pos, int N,
+                                   int H_I, int d_I, int m_ix, int topk, int max_pos,
+                                   int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes,
+                                   const void* kv, const void* score, int in_dtype,
+                                   int64_t row_stride, const int32_t* cu_new,
+                                   const int32_t* start_pos, int B, int max_new, int d, int m,
+                                   const float* ape, float* state, hcs_paged comp, void* stream);
 
 /* ------------------------------------------------------------------------------------ */
 /* Sparse MLA decode (single shared KV head, MQA).                                        */

@@ -155,6 +155,48 @@ def test_indexer_chunk_matches_per_query_path():
     assert torch.equal(torch.sort(sa, dim=1).values, torch.sort(sb, dim=1).values)
 
 
+def test_index_topk_compress_matches_separate_calls():
+    """hcs_index_topk_compress (scoring and compressor blocks in one grid) leaves the same
+    scores, selections, compressor state and compressed cache as hcs_compress_kv followed by
+    hcs_index_topk, bit for bit (ragged batch; some streams end a block at the step, some not)."""
+    dev = _dev()
+    wl = C.CSA_DECODE.with_(B=5, topk=96)
+    sc = G.build(wl, seed=13, device=dev, ctx_per_seq=[1000, 2049, 4096, 3, 777])
+    B, d, m = wl.B, wl.d, wl.m
+    lens = [sc.c_cu[b + 1] - sc.c_cu[b] for b in range(B)]
+    pre = torch.cat([torch.arange(sc.c_cu[b], sc.c_cu[b + 1] - 1, device=dev) for b in range(B)])
+    last = torch.tensor([sc.c_cu[b + 1] - 1 for b in range(B)], device=dev)
+    state = torch.zeros((B, 3 * d), dtype=torch.float32, device=dev)
+    cu_pre = torch.tensor([0] + list(np.cumsum([n - 1 for n in lens])), dtype=torch.int32, device=dev)
+    hcs.compress_kv(sc.c_x.index_select(0, pre).contiguous(), sc.c_s.index_select(0, pre).contiguous(),
+                    cu_pre, sc.c_start, state, sc.comp, m, max_new=max(lens))
+    kv = sc.c_x.index_select(0, last).contiguous()
+    sco = sc.c_s.index_select(0, last).contiguous()
+    cu = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    start = (sc.c_start + torch.tensor([n - 1 for n in lens], dtype=torch.int32, device=dev)).contiguous()
+    pool0, state0 = sc.comp.pool.clone(), state.clone()
+    q, qs = U._ix_q_args(sc)
+    w = sc.ix_w.contiguous()
+    N, k, mp = sc.N, wl.topk, sc.max_pos()
+    res = []
+    for merged in (False, True):
+        sc.comp.pool.copy_(pool0)
+        st = state0.clone()
+        idx = torch.empty((N, k), dtype=torch.int32, device=dev)
+        scr = torch.empty((N, k), dtype=torch.float32, device=dev)
+        if merged:
+            hcs.index_topk_compress(q, qs, w, sc.ix, sc.q_seq, sc.q_pos, m, k, mp, idx, scr, None,
+                                    kv, sco, cu, start, st, sc.comp, m, max_new=1)
+        else:
+            hcs.compress_kv(kv, sco, cu, start, st, sc.comp, m, max_new=1)
+            hcs.index_topk(q, qs, w, sc.ix, sc.q_seq, sc.q_pos, m, k, mp, idx, scr)
+        torch.cuda.synchronize()
+        res.append((sc.comp.pool.clone(), st, torch.sort(idx, 1).values, torch.sort(scr, 1).values))
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a, b)
+    assert not torch.equal(res[0][0], pool0)          # the step did complete some entries
+
+
 def test_csa_decode_large_selection_ragged():
     """bf16 indexer keys with more than 32768 visible entries (threshold + filter + select path)
     in a ragged batch: a query below 32768 entries, one with fewer entries than k, one at
