@@ -16,6 +16,12 @@ Sources (DeepSeek-V4 pages):
     it, and is attended together with the selected compressed entries);
     softmax scale head_dim**-0.5 from the V4.1 page's attention constructor.
 
+  * full compressor -- same section, steps 1-7 and "Key design choices": for CSA
+    (coff=2) the loaded window is 2m tokens, the block's own m in the primary
+    series and the m before it in the overlapping series (the second half of the
+    kv / score columns), so boundary tokens feed two entries; then RMSNorm of the
+    entry, RoPE on its last 64 dims, and the store.
+
 Readings where the pages are open (listed in the design notes too):
   * gate granularity: the score half of kv_score has the width of the KV half,
     so the softmax over the block's m tokens runs separately for every channel;
@@ -25,7 +31,15 @@ Readings where the pages are open (listed in the design notes too):
   * V equals K: the value of a row is the whole shared d-dim row;
   * top-k ties go to the smaller entry index; selected indices outside
     [0, n_visible(p)) are ignored;
-  * a sink adds exp(sink_h) to the softmax denominator only.
+  * a sink adds exp(sink_h) to the softmax denominator only;
+  * overlap (coff=2): entry i takes a softmax over 2m logits per channel: block
+    i's tokens from the primary series (columns 0..d-1) and block i-1's tokens
+    from the overlapping series (columns d..2d-1); entry 0 has only its own m.
+    The positional encoding [m, 2d] adds its first half to the primary logits
+    and its second half to the overlapping ones, by the token's place in its block;
+  * RMSNorm: x / sqrt(mean(x^2) + eps) * weight over the d dims;
+  * RoPE: GPT-J style (interleaved pairs (2j, 2j+1)) on the last d_rope dims, at
+    the entry's position m*i, with the caller's cos/sin tables [positions, d_rope/2].
 """
 from __future__ import annotations
 
@@ -55,6 +69,76 @@ def compress(X, S, m: int, ape=None):
     alpha = e / e.sum(axis=1, keepdims=True)          # softmax over the block's m tokens, per channel
     C = (alpha * X[: nb * m].reshape(nb, m, d)).sum(axis=1)
     return C, alpha
+
+
+def compress_overlap(X, S, m: int, ape=None):
+    """Compressed entries with the overlapping window (coff = 2).
+
+    X, S: [T, 2d] raw KV rows and gate logits, primary series in columns 0..d-1 and the
+    overlapping series in columns d..2d-1. ape: [m, 2d] or None.
+    Entry i: per channel c, the softmax over the 2m logits
+      S[m*i + j, c] + ape[j, c]              (j < m, block i, primary series)
+      S[m*(i-1) + j, d + c] + ape[j, d + c]  (j < m, block i-1, overlapping series; none for i = 0)
+    weights the matching raw values X[., c] and X[., d + c].
+    Returns (C [T//m, d], alpha [T//m, 2m, d]): alpha[:, :m] weights block i's primary tokens,
+    alpha[:, m:] block i-1's overlapping tokens (all zero for entry 0).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    T, d2 = X.shape
+    d = d2 // 2
+    nb = T // m
+    z = S[: nb * m].reshape(nb, m, d2).copy()
+    if ape is not None:
+        z = z + np.asarray(ape, dtype=np.float64)[None]
+    x = X[: nb * m].reshape(nb, m, d2)
+    zl = np.full((nb, 2 * m, d), -np.inf)
+    xl = np.zeros((nb, 2 * m, d))
+    zl[:, :m] = z[:, :, :d]
+    xl[:, :m] = x[:, :, :d]
+    zl[1:, m:] = z[:-1, :, d:]                       # the previous block, overlapping series
+    xl[1:, m:] = x[:-1, :, d:]
+    zl = zl - zl.max(axis=1, keepdims=True)
+    e = np.exp(zl)
+    alpha = e / e.sum(axis=1, keepdims=True)
+    C = (alpha * xl).sum(axis=1)
+    return C, alpha
+
+
+def rms_norm(x, weight, eps: float):
+    """x / sqrt(mean(x^2) + eps) * weight over the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    r = np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    return x / r * np.asarray(weight, dtype=np.float64)
+
+
+def rope_gptj(x, cos, sin, d_rope: int):
+    """GPT-J RoPE on the last d_rope dims of each row of x: pair (2j, 2j+1) of those dims
+    becomes (a cos_j - b sin_j, a sin_j + b cos_j). cos, sin: [rows, d_rope/2]."""
+    x = np.array(x, dtype=np.float64)
+    d = x.shape[-1]
+    r = x[..., d - d_rope:]
+    a, b = r[..., 0::2].copy(), r[..., 1::2].copy()
+    cos = np.asarray(cos, dtype=np.float64)
+    sin = np.asarray(sin, dtype=np.float64)
+    r[..., 0::2] = a * cos - b * sin
+    r[..., 1::2] = a * sin + b * cos
+    return x
+
+
+def compress_full(X, S, m: int, coff: int, ape=None, norm_weight=None, eps: float = 1e-6,
+                  cos_table=None, sin_table=None, d_rope: int = 0, first_entry: int = 0):
+    """The compressor's entries after its epilogue: compress (coff 1) or compress_overlap
+    (coff 2), then RMSNorm (when norm_weight is given), then RoPE on the last d_rope dims at
+    position m * i (when the tables are given; entry i of this stream is entry first_entry + i
+    of its sequence, whose table row is m * (first_entry + i))."""
+    C, _ = compress(X, S, m, ape) if coff == 1 else compress_overlap(X, S, m, ape)
+    if norm_weight is not None:
+        C = rms_norm(C, norm_weight, eps)
+    if cos_table is not None and d_rope > 0:
+        pos = m * (first_entry + np.arange(C.shape[0]))
+        C = rope_gptj(C, np.asarray(cos_table)[pos], np.asarray(sin_table)[pos], d_rope)
+    return C
 
 
 def index_scores(q, w, K) -> np.ndarray:

@@ -73,6 +73,142 @@ def test_compressor_ape_shifts_logits_per_block_position():
     assert np.allclose(C1, X.reshape(4, 4, 6)[:, 1])
 
 
+# ------------------------------------------------------------------ full compressor (coff 2, epilogue)
+
+def test_overlap_weights_sum_to_one_and_entry0_has_no_overlap():
+    rng = np.random.default_rng(20)
+    X = rng.standard_normal((40, 12))
+    S = rng.standard_normal((40, 12)) * 4
+    C, alpha = M.compress_overlap(X, S, 4)
+    assert C.shape == (10, 6) and alpha.shape == (10, 8, 6)
+    assert np.allclose(alpha.sum(axis=1), 1.0, atol=1e-14)
+    assert np.all(alpha[0, 4:] == 0.0) and np.all(alpha[1:] > 0)
+    C1, _ = M.compress_overlap(np.full((40, 12), -0.7), S, 4)
+    assert np.allclose(C1, -0.7, atol=1e-15)
+
+
+def test_overlap_without_overlap_logits_is_the_plain_compressor():
+    # overlapping-series logits of -inf weight nothing: the primary series alone remains
+    rng = np.random.default_rng(21)
+    X = rng.standard_normal((32, 10))
+    S = rng.standard_normal((32, 10))
+    S[:, 5:] = -np.inf
+    C, _ = M.compress_overlap(X, S, 4)
+    C0, _ = M.compress(X[:, :5], S[:, :5], 4)
+    assert np.allclose(C, C0, atol=1e-15)
+    # and entry 0 never sees an overlapping token, whatever its logits
+    S2 = rng.standard_normal((32, 10))
+    Ca, _ = M.compress_overlap(X, S2, 4)
+    Cb, _ = M.compress(X[:4, :5], S2[:4, :5], 4)
+    assert np.allclose(Ca[0], Cb[0], atol=1e-15)
+
+
+def test_overlap_ratio_one_closed_form():
+    # m = 1: entry i mixes x_A[i] and x_B[i-1] with the weights of a two-way softmax
+    rng = np.random.default_rng(22)
+    X = rng.standard_normal((9, 4))
+    S = rng.standard_normal((9, 4))
+    C, _ = M.compress_overlap(X, S, 1)
+    assert np.allclose(C[0], X[0, :2])
+    for i in range(1, 9):
+        sa, sb = S[i, :2], S[i - 1, 2:]
+        wa = 1.0 / (1.0 + np.exp(sb - sa))
+        assert np.allclose(C[i], wa * X[i, :2] + (1 - wa) * X[i - 1, 2:], atol=1e-14)
+
+
+def test_overlap_equal_logits_average_the_two_windows():
+    rng = np.random.default_rng(23)
+    m, d = 4, 3
+    X = rng.standard_normal((5 * m, 2 * d))
+    S = np.full((5 * m, 2 * d), 0.25)
+    C, _ = M.compress_overlap(X, S, m)
+    for i in range(1, 5):
+        want = np.concatenate([X[m * i: m * i + m, :d], X[m * (i - 1): m * i, d:]]).mean(axis=0)
+        assert np.allclose(C[i], want, atol=1e-15)
+
+
+def test_overlap_boundary_token_feeds_both_neighbouring_entries():
+    # a token of block 2 with a dominant primary logit owns entry 2; with a dominant
+    # overlapping logit it owns entry 3
+    m, d = 4, 2
+    X = np.zeros((6 * m, 2 * d))
+    X[2 * m + 1] = [1.0, 2.0, 3.0, 4.0]
+    S = np.zeros((6 * m, 2 * d))
+    S[2 * m + 1, :d] = 80.0
+    C, _ = M.compress_overlap(X, S, m)
+    assert np.allclose(C[2], [1.0, 2.0], atol=1e-12)
+    S = np.zeros((6 * m, 2 * d))
+    S[2 * m + 1, d:] = 80.0
+    C, _ = M.compress_overlap(X, S, m)
+    assert np.allclose(C[3], [3.0, 4.0], atol=1e-12)
+    assert np.allclose(C[2], X[2 * m: 3 * m, :d].sum(axis=0) / (2 * m), atol=1e-12)
+
+
+def test_overlap_positional_encoding_halves():
+    # the encoding's first half shifts primary logits, the second half overlapping ones,
+    # by the token's place in its block: a per-place constant in the overlapping half moves
+    # the overlapping tokens' weights as a logit shift would
+    rng = np.random.default_rng(24)
+    m, d = 4, 3
+    X = rng.standard_normal((6 * m, 2 * d))
+    S = rng.standard_normal((6 * m, 2 * d))
+    ape = np.zeros((m, 2 * d))
+    ape[:, d:] = rng.standard_normal((m, d))
+    C1, _ = M.compress_overlap(X, S, m, ape=ape)
+    S2 = S.copy()
+    S2[:, d:] += np.tile(ape[:, d:], (6, 1))
+    C2, _ = M.compress_overlap(X, S2, m)
+    assert np.allclose(C1, C2, atol=1e-14)
+
+
+def test_rms_norm_invariants():
+    rng = np.random.default_rng(25)
+    x = rng.standard_normal((5, 64)) * 3
+    y = M.rms_norm(x, np.ones(64), 0.0)
+    assert np.allclose(np.sqrt((y * y).mean(axis=1)), 1.0, atol=1e-14)
+    assert np.allclose(M.rms_norm(7.5 * x, np.ones(64), 0.0), y, atol=1e-14)     # scale invariant
+    w = rng.standard_normal(64)
+    assert np.allclose(M.rms_norm(x, w, 0.0), y * w, atol=1e-14)
+    # eps: a zero row stays zero, a tiny row is damped
+    assert np.all(M.rms_norm(np.zeros((1, 8)), np.ones(8), 1e-6) == 0.0)
+
+
+def test_rope_gptj_closed_forms():
+    rng = np.random.default_rng(26)
+    x = rng.standard_normal((3, 16))
+    ones, zeros = np.ones((3, 4)), np.zeros((3, 4))
+    assert np.array_equal(M.rope_gptj(x, ones, zeros, 8), x)                 # angle 0
+    y = M.rope_gptj(x, zeros, ones, 8)                                         # quarter turn
+    assert np.array_equal(y[:, :8], x[:, :8])
+    assert np.allclose(y[:, 8::2], -x[:, 9::2]) and np.allclose(y[:, 9::2], x[:, 8::2])
+    th1, th2 = rng.uniform(-3, 3, (3, 4)), rng.uniform(-3, 3, (3, 4))
+    y1 = M.rope_gptj(M.rope_gptj(x, np.cos(th1), np.sin(th1), 8), np.cos(th2), np.sin(th2), 8)
+    y2 = M.rope_gptj(x, np.cos(th1 + th2), np.sin(th1 + th2), 8)
+    assert np.allclose(y1, y2, atol=1e-13)                                     # angles add
+    yp = y2[:, 8:].reshape(3, 4, 2)
+    xp = x[:, 8:].reshape(3, 4, 2)
+    assert np.allclose((yp ** 2).sum(-1), (xp ** 2).sum(-1), atol=1e-13)      # pair norms kept
+
+
+def test_full_compressor_norm_then_rope_at_block_positions():
+    # steps 4 and 5 of the pages in that order, RoPE at position m * i of each entry
+    rng = np.random.default_rng(27)
+    m, d, dr = 4, 16, 8
+    X = rng.standard_normal((5 * m, 2 * d))
+    S = rng.standard_normal((5 * m, 2 * d))
+    w = rng.uniform(0.5, 2.0, d)
+    ang = rng.uniform(-3, 3, (64, dr // 2))
+    C = M.compress_full(X, S, m, 2, norm_weight=w, eps=1e-6, cos_table=np.cos(ang),
+                        sin_table=np.sin(ang), d_rope=dr)
+    base, _ = M.compress_overlap(X, S, m)
+    normed = M.rms_norm(base, w, 1e-6)
+    pos = m * np.arange(5)
+    assert np.allclose(C, M.rope_gptj(normed, np.cos(ang[pos]), np.sin(ang[pos]), dr), atol=1e-14)
+    # without the epilogue it is the plain entry; coff 1 is compress()
+    assert np.allclose(M.compress_full(X, S, m, 2), base)
+    assert np.allclose(M.compress_full(X[:, :d], S[:, :d], m, 1), M.compress(X[:, :d], S[:, :d], m)[0])
+
+
 def test_compressor_partial_block_makes_no_entry():
     C, _ = M.compress(np.ones((7, 3)), np.zeros((7, 3)), 4)
     assert C.shape == (1, 3)
