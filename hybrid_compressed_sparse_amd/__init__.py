@@ -48,6 +48,9 @@ def lib() -> ctypes.CDLL:
         L.hcs_compress_kv.restype = i32
         L.hcs_compress_kv.argtypes = [vp, vp, i32, i64, vp, vp, i32, i32, i32, i32, vp, vp, Paged,
                                       vp, i64, vp]
+        L.hcs_compress_kv_full.restype = i32
+        L.hcs_compress_kv_full.argtypes = [vp, vp, i32, i64, vp, vp, i32, i32, i32, i32, i32, vp, vp,
+                                           vp, ctypes.c_float, vp, vp, i32, i32, Paged, vp, i64, vp]
         L.hcs_index_topk_workspace_size.restype = sz
         L.hcs_index_topk_workspace_size.argtypes = [i32, i32, i32, i32]
         L.hcs_index_topk.restype = i32
@@ -133,6 +136,30 @@ def compress_kv(kv: torch.Tensor, score: torch.Tensor, cu_new: torch.Tensor, sta
         _ptr(cu_new, torch.int32, "cu_new"), _ptr(start_pos, torch.int32, "start_pos"), B, max_new, d, m,
         _ptr(ape, torch.float32, "ape"), _ptr(state, torch.float32, "state"), _as_paged(comp),
         _ptr(dbg, torch.float32, "dbg"), 0 if dbg is None else dbg.stride(0), _stream()), "compress_kv")
+
+
+def compress_kv_full(kv: torch.Tensor, score: torch.Tensor, cu_new: torch.Tensor, start_pos: torch.Tensor,
+                     state: torch.Tensor, comp, m: int, coff: int, ape: Optional[torch.Tensor] = None,
+                     norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
+                     rope_cos: Optional[torch.Tensor] = None, rope_sin: Optional[torch.Tensor] = None,
+                     dbg: Optional[torch.Tensor] = None, max_new: Optional[int] = None) -> None:
+    """hcs_compress_kv_full. kv, score [T, coff*d] (bf16 or f32); state [B, 3*coff*d] f32;
+    norm_weight [d] f32; rope_cos / rope_sin [rows, d_rope/2] f32 (d_rope = 2 * columns)."""
+    if kv.dtype != score.dtype or kv.dtype not in IN_DTYPE:
+        raise TypeError("kv and score must both be bf16 or both float32")
+    if max_new is None:
+        raise ValueError("max_new (host bound of new tokens per sequence) is required")
+    B = start_pos.shape[0]
+    d = kv.shape[-1] // coff
+    d_rope = 0 if rope_cos is None else 2 * rope_cos.shape[-1]
+    rows = 0 if rope_cos is None else rope_cos.shape[0]
+    _check(lib().hcs_compress_kv_full(
+        _ptr(kv, name="kv"), _ptr(score, name="score"), IN_DTYPE[kv.dtype], kv.stride(0),
+        _ptr(cu_new, torch.int32, "cu_new"), _ptr(start_pos, torch.int32, "start_pos"), B, max_new, d, m,
+        coff, _ptr(ape, torch.float32, "ape"), _ptr(state, torch.float32, "state"),
+        _ptr(norm_weight, torch.float32, "norm_weight"), norm_eps, _ptr(rope_cos, torch.float32, "rope_cos"),
+        _ptr(rope_sin, torch.float32, "rope_sin"), d_rope, rows, _as_paged(comp),
+        _ptr(dbg, torch.float32, "dbg"), 0 if dbg is None else dbg.stride(0), _stream()), "compress_kv_full")
 
 
 # ------------------------------------------------------------------------------ indexer

@@ -105,6 +105,36 @@ hcs_status hcs_compress_kv(const void* kv, const void* score, int in_dtype, int6
   return hip_status(hcs::launch_compress(a, max_new, static_cast<hipStream_t>(stream)), "compress_kv");
 }
 
+hcs_status hcs_compress_kv_full(const void* kv, const void* score, int in_dtype, int64_t row_stride,
+                                const int32_t* cu_new, const int32_t* start_pos, int B, int max_new,
+                                int d, int m, int coff, const float* ape, float* state,
+                                const float* norm_weight, float norm_eps, const float* rope_cos,
+                                const float* rope_sin, int d_rope, int rope_rows, hcs_paged comp,
+                                float* dbg, int64_t dbg_seq_stride, void* stream) {
+  if (coff != 1 && coff != 2) return fail(HCS_ERR_UNSUPPORTED, "coff must be 1 or 2");
+  hcs::CompressArgs a;
+  hcs_status s = prep_compress(kv, score, in_dtype, row_stride, cu_new, start_pos, B, max_new, d, m,
+                               ape, state, comp, dbg, dbg_seq_stride, a);
+  if (s != HCS_OK) return s;
+  if (B > 0 && row_stride < (int64_t)coff * d)
+    return fail(HCS_ERR_INVALID_ARG, "row_stride %lld < coff * d = %d", (long long)row_stride, coff * d);
+  if (norm_weight && !(norm_eps >= 0.f)) return fail(HCS_ERR_INVALID_ARG, "norm_eps must be >= 0");
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(HCS_ERR_INVALID_ARG, "rope_cos and rope_sin are given together or not at all");
+  if (rope_cos && (d_rope < 2 || d_rope > d || d_rope % 2 || rope_rows < 1))
+    return fail(HCS_ERR_INVALID_ARG, "RoPE needs an even d_rope in 2..d and rope_rows >= 1");
+  if (B == 0) return ok();
+  a.coff = coff;
+  a.norm_w = norm_weight;
+  a.norm_eps = norm_eps;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.d_rope = rope_cos ? d_rope : 0;
+  a.rope_rows = rope_rows;
+  return hip_status(hcs::launch_compress_full(a, max_new, static_cast<hipStream_t>(stream)),
+                    "compress_kv_full");
+}
+
 // ------------------------------------------------------------------------------ indexer
 size_t hcs_index_topk_workspace_size(int N, int max_pos, int m, int topk) {
   if (N <= 0 || max_pos < 0 || m < 1 || topk < 1) return 0;

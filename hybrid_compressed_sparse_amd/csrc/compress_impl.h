@@ -15,6 +15,50 @@ __device__ __forceinline__ float compress_load_in(const void* p, int in_bf16, in
   return static_cast<const float*>(p)[idx];
 }
 
+// Stores channel c (of a completed entry kb of sequence b) of value C: the optional float32
+// copy, and the cache row (bf16, or fp8_ds: per 64-dim latent block a power-of-two scale from
+// the wave's amax, e4m3 codes by the hardware's round-to-nearest-even conversion; the 64
+// rotary dims as bf16). `page` is the entry's page (nullptr: not resident). Called by every
+// lane of a wave, a wave holding one whole 64-channel block.
+__device__ __forceinline__ void compress_store(const CompressArgs& a, int b, int kb, int kb_first,
+                                               const uint8_t* page, int c, bool act, float C) {
+  const int d = a.d, slot = kb & 63;
+  if (act && a.dbg) a.dbg[(int64_t)b * a.dbg_stride + (int64_t)(kb - kb_first) * d + c] = C;
+  if (a.fmt == HCS_FMT_FP8DS) {
+    if (c < kFp8Latent) {
+      const float amax = warp_max(fabsf(C));
+      // smallest e with amax <= 448 * 2^e; 448 = 0.875 * 2^9
+      int E;
+      const float f = __builtin_frexpf(amax, &E);
+      int e = amax > 0.f ? E - 9 + (f > 0.875f ? 1 : 0) : 0;
+      e = max(-127, min(127, e));
+      const float y = __builtin_ldexpf(C, -e);
+      const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false);
+      if (page) {
+        uint8_t* pw = const_cast<uint8_t*>(page);
+        pw[kFp8PageCodes + slot * kFp8Latent + c] = (uint8_t)(packed & 0xff);
+        if ((c & 63) == 0) pw[kFp8PageScales + slot * 8 + (c >> 6)] = (uint8_t)(e + 127);
+        if (c == 0) pw[kFp8PageScales + slot * 8 + 7] = 0;
+      }
+    } else if (act && page) {
+      uint16_t* rope = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(page) + kFp8PageRope +
+                                                   slot * kFp8Rope * 2);
+      rope[c - kFp8Latent] = (uint16_t)f32_to_bf16_bits(C);
+    }
+  } else if (act && page) {
+    uint16_t* row = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(page)) + (int64_t)slot * d;
+    row[c] = (uint16_t)f32_to_bf16_bits(C);
+  }
+}
+
+// Page of completed entry kb of sequence b in the compressed cache, or nullptr.
+__device__ __forceinline__ const uint8_t* compress_entry_page(const CompressArgs& a, int b, int kb) {
+  const int pg = (kb >> 6) < a.comp_pt_stride ? __ldg(a.comp_pt + (int64_t)b * a.comp_pt_stride + (kb >> 6)) : -1;
+  if (pg < 0 || pg >= a.comp_num_pages) return nullptr;
+  const int64_t pb = a.fmt == HCS_FMT_FP8DS ? (int64_t)kFp8PageBytes : (int64_t)kPageRows * a.d * 2;
+  return a.comp_base + (int64_t)pg * pb;
+}
+
 // The work of compressor block (b, y, z) of a grid with ny blocks along y (see compress_grid):
 // sequence b, block slot y, channel group z. Every thread of the block calls it.
 __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int y, int z, int ny) {
@@ -40,17 +84,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
     const int tok_hi = min(start + n, blk_lo + m);
     const bool complete = blk_lo + m <= start + n;
     const bool resume = blk_lo < start;       // the block began in an earlier call
-    // destination of a completed entry
-    const uint8_t* page = nullptr;
-    const int slot = kb & 63;
-    if (complete) {
-      const int pg = (kb >> 6) < a.comp_pt_stride
-                         ? __ldg(a.comp_pt + (int64_t)b * a.comp_pt_stride + (kb >> 6)) : -1;
-      if (pg >= 0 && pg < a.comp_num_pages) {
-        const int64_t pb = a.fmt == HCS_FMT_FP8DS ? (int64_t)kFp8PageBytes : (int64_t)kPageRows * d * 2;
-        page = a.comp_base + (int64_t)pg * pb;
-      }
-    }
+    const uint8_t* page = complete ? compress_entry_page(a, b, kb) : nullptr;   // its destination
     for (int c = c0 + threadIdx.x; c < c1; c += kCompressThreads) {
       const bool act = c < d;
       float M = kNegInf, Z = 0.f, A = 0.f;
@@ -73,36 +107,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
           M = Mn;
         }
       }
-      if (complete) {
-        const float C = act ? A / Z : 0.f;
-        if (act && a.dbg) a.dbg[(int64_t)b * a.dbg_stride + (int64_t)(kb - kb_first) * d + c] = C;
-        if (a.fmt == HCS_FMT_FP8DS) {
-          // one wave = one 64-channel block (dpad and c0 are multiples of 64)
-          if (c < kFp8Latent) {
-            const float amax = warp_max(fabsf(C));
-            // smallest e with amax <= 448 * 2^e; 448 = 0.875 * 2^9
-            int E;
-            const float f = __builtin_frexpf(amax, &E);
-            int e = amax > 0.f ? E - 9 + (f > 0.875f ? 1 : 0) : 0;
-            e = max(-127, min(127, e));
-            const float y = __builtin_ldexpf(C, -e);
-            const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false);
-            if (page) {
-              uint8_t* pw = const_cast<uint8_t*>(page);
-              pw[kFp8PageCodes + slot * kFp8Latent + c] = (uint8_t)(packed & 0xff);
-              if ((c & 63) == 0) pw[kFp8PageScales + slot * 8 + (c >> 6)] = (uint8_t)(e + 127);
-              if (c == 0) pw[kFp8PageScales + slot * 8 + 7] = 0;
-            }
-          } else if (act && page) {
-            uint16_t* rope = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(page) + kFp8PageRope +
-                                                         slot * kFp8Rope * 2);
-            rope[c - kFp8Latent] = (uint16_t)f32_to_bf16_bits(C);
-          }
-        } else if (act && page) {
-          uint16_t* row = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(page)) + (int64_t)slot * d;
-          row[c] = (uint16_t)f32_to_bf16_bits(C);
-        }
-      }
+      if (complete) compress_store(a, b, kb, kb_first, page, c, act, act ? A / Z : 0.f);
       if (act && kb == kb_last) {
         if (complete) {
           st[c] = kNegInf;

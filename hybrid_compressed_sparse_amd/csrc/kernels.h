@@ -49,8 +49,16 @@ struct CompressArgs {
   int comp_pt_stride, comp_num_pages;
   float* dbg;
   int64_t dbg_stride;
+  // the full compressor (launch_compress_full): overlapping window, RMSNorm, RoPE
+  int coff;                   // 1, or 2: overlapping window (kv / score rows are 2d wide)
+  const float* norm_w;        // [d] or nullptr: no RMSNorm
+  float norm_eps;
+  const float* rope_cos;      // [rope_rows, d_rope / 2] or nullptr: no RoPE
+  const float* rope_sin;
+  int d_rope, rope_rows;
 };
 hipError_t launch_compress(const CompressArgs& a, int max_new, hipStream_t stream);
+hipError_t launch_compress_full(const CompressArgs& a, int max_new, hipStream_t stream);
 
 // ---------------------------------------------------------------- indexer + top-k
 struct IndexArgs {

@@ -9,6 +9,7 @@
  *                             compressed entry (per-channel softmax of the gate logits over
  *                             the block, weighted sum of the raw KV rows), stored in the
  *                             compressed cache in its format;
+ *   hcs_compress_kv_full      the same with the CSA overlapping window, RMSNorm and RoPE;
  *   hcs_index_topk            the Lightning Indexer of CSA layers: scores of every visible
  *                             compressed entry, I = sum_h w_h * ReLU(q_h . k), and the top-k;
  *   hcs_index_topk_chunk      the same for a chunk of consecutive queries of one sequence;
@@ -120,6 +121,33 @@ hcs_status hcs_compress_kv(const void* kv, const void* score, int in_dtype, int6
                            const int32_t* cu_new, const int32_t* start_pos, int B, int max_new,
                            int d, int m, const float* ape, float* state, hcs_paged comp,
                            float* dbg, int64_t dbg_seq_stride, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* The full compressor: "Code Reading Map", "How Does Compression Actually Work?", steps  */
+/* 1-7 and "Key design choices". As hcs_compress_kv, plus:                                */
+/*   coff = 2 (CSA overlap): kv and score rows are 2d wide; entry i's softmax runs, per   */
+/*     channel c, over 2m logits: block i's tokens in columns c (primary series) and      */
+/*     block i-1's tokens in columns d + c (overlapping series; entry 0 has only its m),  */
+/*     weighting the matching kv values, so a block's tokens feed two entries. ape, when  */
+/*     given, is [m, coff * d] and adds by the token's place in its block.                */
+/*   norm_weight [d] float32 (or NULL: none): the entry becomes                          */
+/*     x / sqrt(mean(x^2) + norm_eps) * norm_weight.                                      */
+/*   rope_cos, rope_sin [rope_rows, d_rope / 2] float32 (or both NULL: none): the last    */
+/*     d_rope dims are rotated in GPT-J pairs (2j, 2j+1) at the entry's position m * i:   */
+/*     (a, b) -> (a cos - b sin, a sin + b cos) with row m * i of the tables. Every        */
+/*     emitted entry's position must be below rope_rows (a larger one reads the last row).*/
+/* Then the store in comp's format, and dbg holds the values after the epilogue.          */
+/* state    [B, 3 * coff * d] float32: zeros for a fresh sequence, else what the previous  */
+/*          call left (with coff = 2 a call starting at a block boundary reads the carried */
+/*          overlap from it).                                                             */
+/* Constraints: as hcs_compress_kv, coff in {1, 2}, row_stride >= coff * d, d <= 1024,     */
+/* d_rope even and <= d. Errors as hcs_compress_kv.                                        */
+hcs_status hcs_compress_kv_full(const void* kv, const void* score, int in_dtype, int64_t row_stride,
+                                const int32_t* cu_new, const int32_t* start_pos, int B, int max_new,
+                                int d, int m, int coff, const float* ape, float* state,
+                                const float* norm_weight, float norm_eps, const float* rope_cos,
+                                const float* rope_sin, int d_rope, int rope_rows, hcs_paged comp,
+                                float* dbg, int64_t dbg_seq_stride, void* stream);
 
 /* ------------------------------------------------------------------------------------ */
 /* Lightning-Indexer scores and top-k selection (CSA layers).                             */
