@@ -216,6 +216,60 @@ class Bench:
 
 # ------------------------------------------------------------------ CPU baseline (oracle)
 
+def bench_compress_full(wl, sets: int, reps: int) -> dict:
+    """The full compressor (overlapping window, RMSNorm, RoPE on 64 dims, bf16 store) at a decode
+    step of `wl`: one new token per sequence, each completing an entry. Inputs are seeded random
+    values of that shape; the state starts from zeros (the cost does not depend on it)."""
+    import torch
+
+    import hybrid_compressed_sparse_amd as hcs
+    from synth import gen as G
+
+    dev = torch.device("cuda:0")
+    B, d, m, coff, dr = wl.B, wl.d, wl.m, 2, 64
+    g = torch.Generator(device="cpu").manual_seed(4242)
+    ins = []
+    for s in range(sets):
+        sc = G.build(wl, seed=3000 + s, device=dev)
+        kv = (torch.randn(B, coff * d, generator=g) / d ** 0.5).to(torch.bfloat16).to(dev)
+        sco = torch.randn(B, coff * d, generator=g).to(torch.bfloat16).to(dev)
+        pos = torch.full((B,), wl.ctx - 1, dtype=torch.int32, device=dev)
+        state = torch.zeros((B, 3 * coff * d), dtype=torch.float32, device=dev)
+        ins.append((sc, kv, sco, pos, state))
+    cu = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    w = (torch.rand(d, generator=g) + 0.5).to(dev)
+    ang = torch.rand(wl.ctx, dr // 2, generator=g, dtype=torch.float64) * 6.0 - 3.0
+    cos, sin = torch.cos(ang).float().to(dev), torch.sin(ang).float().to(dev)
+
+    def run_all():
+        for sc, kv, sco, pos, state in ins:
+            hcs.compress_kv_full(kv, sco, cu, pos, state, sc.comp, m, coff, norm_weight=w,
+                                 rope_cos=cos, rope_sin=sin, max_new=1)
+
+    run_all()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        run_all()
+    for _ in range(3):
+        gr.replay()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(reps):
+        gr.replay()
+    s1.record()
+    torch.cuda.synchronize()
+    us = s0.elapsed_time(s1) * 1e3 / (reps * sets)
+    # bytes the call must move: new rows (kv and score, 2 x 2d bf16), the state read and written
+    # (2 x 6d float32), the norm weights, the RoPE rows and the stored entry
+    nbytes = B * (2 * coff * d * 2 + 2 * 3 * coff * d * 4 + d * 2 + dr * 4) + d * 4
+    del ins
+    torch.cuda.empty_cache()
+    return {"us_per_call": us, "config": f"B={B}, d={d}, m={m}, coff={coff}, RMSNorm, RoPE {dr} dims, "
+            "bf16 store, one token per sequence (each completes an entry)",
+            "algorithmic_bytes": nbytes, "gb_s": nbytes / (us * 1e-6) / 1e9}
+
+
 def cpu_baseline(wl, seconds: float) -> dict:
     from threadpoolctl import threadpool_info
 
@@ -399,6 +453,9 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extra and wl.name == "csa_decode_bf16":
+        log("[bench] side measurement: full compressor at this decode step")
+        result["compress_full"] = bench_compress_full(wl, R, max(1, args.steps // R))
+        log(f"[bench] compress_full: {result['compress_full']['us_per_call']:.2f} us")
         hw = C.HCA_DECODE
         log(f"[bench] side measurement: {hw.name}")
         hb = Bench(hw, R, seed=2000)
