@@ -36,18 +36,20 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
 // block being filled (its primary tokens plus the previous block's overlapping tokens), `nxt`
 // the overlapping tokens of that block, which start the next entry. At a block's end `cur` is
 // emitted and `nxt` becomes the next `cur`. The state [3 coff d] keeps both between calls.
-// A workgroup covers all d channels of an entry (the norm needs them all): up to four per
-// thread. Workgroup y = 0 walks the call's first block, the one after it and its last block (in
-// that order, so the carried state is read before it is overwritten); the others walk the
-// middle blocks, each re-reading the previous block's overlapping tokens.
-constexpr int kFullCPT = 4;                       // channels per thread (d <= 1024)
-
+// A workgroup covers all d channels of an entry (the norm needs them all): CPT per thread, the
+// loads of all of a thread's channels issued together (one memory round trip for the carried
+// state, the RMSNorm weights and the RoPE row, one per token). Workgroup y = 0 walks the call's
+// first block, the one after it and its last block (in that order, so the carried state is
+// read before it is overwritten); the others walk the middle blocks, each re-reading the
+// previous block's overlapping tokens.
 struct Online {
   float M, Z, A;
   __device__ __forceinline__ void empty() { M = -__builtin_huge_valf(); Z = 0.f; A = 0.f; }
+  // a triple with no weight (Z = 0: the zeros of a fresh sequence, or a reset) is empty
   __device__ __forceinline__ void add(float z, float x) {
-    const float Mn = fmaxf(M, z);
-    const float f_old = __expf(M - Mn);         // 0 when M = -inf
+    const float Mo = Z == 0.f ? -__builtin_huge_valf() : M;
+    const float Mn = fmaxf(Mo, z);
+    const float f_old = __expf(Mo - Mn);        // 0 when empty
     const float f_new = __expf(z - Mn);
     Z = Z * f_old + f_new;
     A = A * f_old + x * f_new;
@@ -55,38 +57,64 @@ struct Online {
   }
 };
 
+template <int CPT, bool BF16>
 __global__ __launch_bounds__(kCompressThreads) void compress_full_kernel(CompressArgs a) {
   const int b = blockIdx.x, y = blockIdx.y, ny = gridDim.y;
   const int row0 = a.cu_new[b];
   const int n = a.cu_new[b + 1] - row0;
-  if (n <= 0) return;
   const int start = a.start_pos[b];
+  if (n <= 0 || start < 0) return;               // (testing start too loads it beside n)
   const int m = a.m, d = a.d, coff = a.coff, w = coff * d;
   const int kb_first = start / m, kb_last = (start + n - 1) / m;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float* st = a.state + (int64_t)b * 3 * w;       // cur (M, Z, A) at 0, d, 2d; nxt at 3d, 4d, 5d
   __shared__ float red[kCompressThreads / 64];
+  // a thread's channels; loads use the clamped index so that they need no branch
+  int cc[CPT];
+  bool act[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int c = threadIdx.x + k * kCompressThreads;
+    act[k] = c < d;
+    cc[k] = min(c, d - 1);
+  }
 
-  // this call's tokens [lo, hi) of one series (col 0: primary, d: overlapping) at channel c
-  auto scan = [&](Online& o, int c, int col, int lo, int hi) __attribute__((always_inline)) {
+  // this call's tokens [lo, hi) of one series (col 0: primary, d: overlapping) into o[]
+  auto scan = [&](Online* o, int col, int lo, int hi) __attribute__((always_inline)) {
     for (int tok = lo; tok < hi; ++tok) {
-      const int64_t r = (int64_t)(row0 + tok - start) * a.row_stride + col + c;
-      float z = compress_load_in(a.score, a.in_bf16, r);
-      if (a.ape) z += a.ape[(int64_t)(tok % m) * w + col + c];
-      o.add(z, compress_load_in(a.kv, a.in_bf16, r));
+      const int64_t r = (int64_t)(row0 + tok - start) * a.row_stride + col;
+      const float* ape = a.ape ? a.ape + (int64_t)(tok % m) * w + col : nullptr;
+      float z[CPT], x[CPT], pe[CPT];
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        z[k] = compress_load_in<BF16>(a.score, r + cc[k]);
+        x[k] = compress_load_in<BF16>(a.kv, r + cc[k]);
+        pe[k] = 0.f;
+      }
+      if (ape) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) pe[k] = ape[cc[k]];
+      }
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) o[k].add(z[k] + pe[k], x[k]);
     }
   };
-  // a stored triple with no weight (Z = 0: zeros of a fresh sequence, or a reset) is empty
-  auto load_triple = [&](Online& o, int c, int off) __attribute__((always_inline)) {
-    o.M = st[off + c];
-    o.Z = st[off + d + c];
-    o.A = st[off + 2 * d + c];
-    if (o.Z == 0.f) o.empty();
+  auto load_triples = [&](Online* o, int off) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      o[k].M = st[off + cc[k]];
+      o[k].Z = st[off + d + cc[k]];
+      o[k].A = st[off + 2 * d + cc[k]];
+    }
   };
-  auto save_triple = [&](const Online& o, int c, int off) __attribute__((always_inline)) {
-    st[off + c] = o.M;
-    st[off + d + c] = o.Z;
-    st[off + 2 * d + c] = o.A;
+  auto save_triples = [&](const Online* o, int off) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      if (!act[k]) continue;
+      st[off + cc[k]] = o[k].M;
+      st[off + d + cc[k]] = o[k].Z;
+      st[off + 2 * d + cc[k]] = o[k].A;
+    }
   };
 
   auto do_block = [&](int kb) {
@@ -94,31 +122,51 @@ __global__ __launch_bounds__(kCompressThreads) void compress_full_kernel(Compres
     const int tok_lo = max(start, blk_lo), tok_hi = min(start + n, blk_lo + m);
     const bool complete = blk_lo + m <= start + n;
     const uint8_t* page = complete ? compress_entry_page(a, b, kb) : nullptr;
-    float C[kFullCPT];
-    Online cur[kFullCPT], nxt[kFullCPT];
+    Online cur[CPT], nxt[CPT];
 #pragma unroll
-    for (int k = 0; k < kFullCPT; ++k) {
-      const int c = threadIdx.x + k * kCompressThreads;
+    for (int k = 0; k < CPT; ++k) {
       cur[k].empty();
       nxt[k].empty();
-      C[k] = 0.f;
-      if (c >= d) continue;
-      if (kb == kb_first) {                      // resume from the state (empty when fresh)
-        load_triple(cur[k], c, 0);
-        if (coff == 2) load_triple(nxt[k], c, 3 * d);
-      } else if (coff == 2) {                    // the previous block's overlapping tokens
-        if (kb - 1 == kb_first) load_triple(cur[k], c, 3 * d);
-        scan(cur[k], c, d, max(start, blk_lo - m), blk_lo);
-      }
-      scan(cur[k], c, 0, tok_lo, tok_hi);
-      if (coff == 2 && kb == kb_last) scan(nxt[k], c, d, tok_lo, tok_hi);
-      if (complete) C[k] = cur[k].A / cur[k].Z;
     }
+    if (kb == kb_first) {                        // resume from the state (empty when fresh)
+      load_triples(cur, 0);
+      if (coff == 2) load_triples(nxt, 3 * d);
+    } else if (coff == 2 && kb - 1 == kb_first) {
+      load_triples(cur, 3 * d);
+    }
+    // epilogue operands (independent of the accumulation; clamped rows, used where they apply)
+    float nw[CPT], rc[CPT], rs[CPT];
+    const int r0 = d - a.d_rope, half = a.d_rope / 2;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      nw[k] = 1.f;
+      rc[k] = 1.f;
+      rs[k] = 0.f;
+    }
+    if (complete && a.norm_w) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) nw[k] = a.norm_w[cc[k]];
+    }
+    if (complete && a.rope_cos) {
+      const int64_t row = (int64_t)min(m * kb, a.rope_rows - 1) * half;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const int64_t ri = row + (max(cc[k] - r0, 0) >> 1);
+        rc[k] = a.rope_cos[ri];
+        rs[k] = a.rope_sin[ri];
+      }
+    }
+    if (kb != kb_first && coff == 2) scan(cur, d, max(start, blk_lo - m), blk_lo);   // previous block's overlap
+    scan(cur, 0, tok_lo, tok_hi);
+    if (coff == 2 && kb == kb_last) scan(nxt, d, tok_lo, tok_hi);
     if (complete) {
+      float C[CPT];
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) C[k] = act[k] ? cur[k].A / cur[k].Z : 0.f;
       if (a.norm_w) {                            // RMSNorm over the d channels
         float ss = 0.f;
 #pragma unroll
-        for (int k = 0; k < kFullCPT; ++k) ss += C[k] * C[k];
+        for (int k = 0; k < CPT; ++k) ss += C[k] * C[k];
         ss = warp_sum(ss);
         if (lane == 0) red[wave] = ss;
         __syncthreads();
@@ -128,45 +176,31 @@ __global__ __launch_bounds__(kCompressThreads) void compress_full_kernel(Compres
         __syncthreads();                         // red is reused by the next block
         const float r = 1.f / __builtin_sqrtf(tot / (float)d + a.norm_eps);
 #pragma unroll
-        for (int k = 0; k < kFullCPT; ++k) {
-          const int c = threadIdx.x + k * kCompressThreads;
-          if (c < d) C[k] = C[k] * r * a.norm_w[c];
-        }
+        for (int k = 0; k < CPT; ++k) C[k] = C[k] * r * nw[k];
       }
       if (a.rope_cos) {                          // GPT-J pairs (c, c ^ 1) of the last d_rope dims
-        const int pos = min(m * kb, a.rope_rows - 1);
-        const int half = a.d_rope / 2, r0 = d - a.d_rope;
 #pragma unroll
-        for (int k = 0; k < kFullCPT; ++k) {
-          const int c = threadIdx.x + k * kCompressThreads;
+        for (int k = 0; k < CPT; ++k) {
           const float p = __shfl_xor(C[k], 1, 64);   // the pair's other member (lane ^ 1)
-          if (c >= r0 && c < d) {
-            const int j = (c - r0) >> 1;
-            const float cs = a.rope_cos[(int64_t)pos * half + j], sn = a.rope_sin[(int64_t)pos * half + j];
-            C[k] = (c & 1) ? p * sn + C[k] * cs : C[k] * cs - p * sn;
-          }
+          if (act[k] && cc[k] >= r0) C[k] = (cc[k] & 1) ? p * rs[k] + C[k] * rc[k] : C[k] * rc[k] - p * rs[k];
         }
       }
 #pragma unroll
-      for (int k = 0; k < kFullCPT; ++k) {
+      for (int k = 0; k < CPT; ++k) {
         const int c = threadIdx.x + k * kCompressThreads;
-        if (c < ((d + 63) & ~63)) compress_store(a, b, kb, kb_first, page, c, c < d, C[k]);
+        if (c < ((d + 63) & ~63)) compress_store(a, b, kb, kb_first, page, c, act[k], C[k]);
       }
     }
     if (kb == kb_last) {
+      if (complete) {                            // the next entry starts with this block's overlap
+        Online e[CPT];
 #pragma unroll
-      for (int k = 0; k < kFullCPT; ++k) {
-        const int c = threadIdx.x + k * kCompressThreads;
-        if (c >= d) continue;
-        if (complete) {                          // the next entry starts with this block's overlap
-          Online e;
-          e.empty();
-          save_triple(coff == 2 ? nxt[k] : e, c, 0);
-          if (coff == 2) save_triple(e, c, 3 * d);
-        } else {
-          save_triple(cur[k], c, 0);
-          if (coff == 2) save_triple(nxt[k], c, 3 * d);
-        }
+        for (int k = 0; k < CPT; ++k) e[k].empty();
+        save_triples(coff == 2 ? nxt : e, 0);
+        if (coff == 2) save_triples(e, 3 * d);
+      } else {
+        save_triples(cur, 0);
+        if (coff == 2) save_triples(nxt, 3 * d);
       }
     }
   };
@@ -188,7 +222,18 @@ __global__ __launch_bounds__(kCompressThreads) void compress_full_kernel(Compres
 hipError_t launch_compress_full(const CompressArgs& a, int max_new, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
   const int slots = std::min(65535, std::max(1, (max_new + a.m - 1) / a.m));
-  hipLaunchKernelGGL(compress_full_kernel, dim3(a.B, slots), dim3(kCompressThreads), 0, stream, a);
+  const dim3 grid(a.B, slots), block(kCompressThreads);
+  const int cpt = a.d <= kCompressThreads ? 1 : a.d <= 2 * kCompressThreads ? 2 : 4;
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, a); };
+  if (a.in_bf16) {
+    if (cpt == 1) go(compress_full_kernel<1, true>);
+    else if (cpt == 2) go(compress_full_kernel<2, true>);
+    else go(compress_full_kernel<4, true>);
+  } else {
+    if (cpt == 1) go(compress_full_kernel<1, false>);
+    else if (cpt == 2) go(compress_full_kernel<2, false>);
+    else go(compress_full_kernel<4, false>);
+  }
   return hipGetLastError();
 }
 

@@ -10,9 +10,12 @@ namespace hcs {
 
 constexpr int kCompressThreads = 256;
 
-__device__ __forceinline__ float compress_load_in(const void* p, int in_bf16, int64_t idx) {
-  if (in_bf16) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[idx]);
-  return static_cast<const float*>(p)[idx];
+// element idx of a compressor input (bf16 or float32); the type is a template argument so that
+// loads of several tokens or channels are not split by a branch on it
+template <bool BF16>
+__device__ __forceinline__ float compress_load_in(const void* p, int64_t idx) {
+  if constexpr (BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[idx]);
+  else return static_cast<const float*>(p)[idx];
 }
 
 // Stores channel c (of a completed entry kb of sequence b) of value C: the optional float32
@@ -61,11 +64,12 @@ __device__ __forceinline__ const uint8_t* compress_entry_page(const CompressArgs
 
 // The work of compressor block (b, y, z) of a grid with ny blocks along y (see compress_grid):
 // sequence b, block slot y, channel group z. Every thread of the block calls it.
-__device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int y, int z, int ny) {
+template <bool BF16>
+__device__ __forceinline__ void compress_block_t(const CompressArgs& a, int b, int y, int z, int ny) {
   const int row0 = a.cu_new[b];
   const int n = a.cu_new[b + 1] - row0;
-  if (n <= 0) return;
   const int start = a.start_pos[b];
+  if (n <= 0 || start < 0) return;               // (testing start too loads it beside n)
   const int m = a.m, d = a.d;
   const int kb_first = start / m;
   const int kb_last = (start + n - 1) / m;
@@ -96,9 +100,9 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
         }
         for (int tok = tok_lo; tok < tok_hi; ++tok) {
           const int64_t r = (int64_t)(row0 + tok - start) * a.row_stride + c;
-          float z = compress_load_in(a.score, a.in_bf16, r);
+          float z = compress_load_in<BF16>(a.score, r);
           if (a.ape) z += a.ape[(int64_t)(tok - blk_lo) * d + c];
-          const float x = compress_load_in(a.kv, a.in_bf16, r);
+          const float x = compress_load_in<BF16>(a.kv, r);
           const float Mn = fmaxf(M, z);
           const float f_old = __expf(M - Mn);      // 0 when M = -inf
           const float f_new = __expf(z - Mn);
@@ -131,6 +135,11 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
     const int w0 = ny > 1 ? y - 1 : 0;
     for (int kb = kb_first + 1 + w0; kb < kb_last; kb += workers) do_block(kb);
   }
+}
+
+__device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int y, int z, int ny) {
+  if (a.in_bf16) compress_block_t<true>(a, b, y, z, ny);
+  else compress_block_t<false>(a, b, y, z, ny);
 }
 
 // Grid of a compressor launch: (sequences, block slots, channel groups): one workgroup for the
