@@ -21,6 +21,12 @@ Sources (DeepSeek-V4 pages):
     series and the m before it in the overlapping series (the second half of the
     kv / score columns), so boundary tokens feed two entries; then RMSNorm of the
     entry, RoPE on its last 64 dims, and the store.
+  * query preparation and SWA insert -- same page, "Default stream" (the fused
+    q-norm / RoPE / KV insert: per-head RMSNorm of the query heads, GPT-J RoPE on
+    the last 64 dims of every query head and of the KV row, the KV row stored in
+    the sliding-window cache), and the V4.1 page's `_fused_qnorm_rope_kv_insert`
+    (the query norm is a switch, with no weight among the op's arguments; the KV
+    row is rotated, not normalised, then stored in the cache's format).
 
 Readings where the pages are open (listed in the design notes too):
   * gate granularity: the score half of kv_score has the width of the KV half,
@@ -40,6 +46,9 @@ Readings where the pages are open (listed in the design notes too):
   * RMSNorm: x / sqrt(mean(x^2) + eps) * weight over the d dims;
   * RoPE: GPT-J style (interleaved pairs (2j, 2j+1)) on the last d_rope dims, at
     the entry's position m*i, with the caller's cos/sin tables [positions, d_rope/2].
+  * query norm: over each head's d dims, with no weight (the op takes none); a raw
+    token is rotated at its own position p, and its KV row becomes logical row p of
+    the sliding-window cache.
 """
 from __future__ import annotations
 
@@ -139,6 +148,31 @@ def compress_full(X, S, m: int, coff: int, ape=None, norm_weight=None, eps: floa
         pos = m * (first_entry + np.arange(C.shape[0]))
         C = rope_gptj(C, np.asarray(cos_table)[pos], np.asarray(sin_table)[pos], d_rope)
     return C
+
+
+def qnorm_rope(q, pos: int, cos_table, sin_table, d_rope: int, eps: float, q_norm: bool):
+    """A raw token's query heads as attention reads them: each head [H, d] normalised to unit
+    RMS over its d dims (when q_norm; no weight), then rotated (GPT-J) on its last d_rope dims
+    at the token's position pos (row pos of the tables; d_rope 0: no rotation)."""
+    q = np.asarray(q, dtype=np.float64)
+    if q_norm:
+        q = rms_norm(q, np.ones(q.shape[-1]), eps)
+    if d_rope > 0:
+        c = np.asarray(cos_table, dtype=np.float64)[pos]
+        s = np.asarray(sin_table, dtype=np.float64)[pos]
+        q = rope_gptj(q, c, s, d_rope)
+    return q
+
+
+def swa_row(kv, pos: int, cos_table, sin_table, d_rope: int):
+    """A raw token's KV row [d] as the sliding-window cache holds it (before the cache's own
+    rounding): rotated (GPT-J) on its last d_rope dims at the token's position, else as is."""
+    kv = np.asarray(kv, dtype=np.float64)
+    if d_rope == 0:
+        return kv.copy()
+    c = np.asarray(cos_table, dtype=np.float64)[pos]
+    s = np.asarray(sin_table, dtype=np.float64)[pos]
+    return rope_gptj(kv, c, s, d_rope)
 
 
 def index_scores(q, w, K) -> np.ndarray:

@@ -209,6 +209,48 @@ def test_full_compressor_norm_then_rope_at_block_positions():
     assert np.allclose(M.compress_full(X[:, :d], S[:, :d], m, 1), M.compress(X[:, :d], S[:, :d], m)[0])
 
 
+def _rope_tables(rows: int, d_rope: int, base: float = 10000.0):
+    # the standard angle table: pair j of position p turns by p * base^(-2j / d_rope)
+    theta = base ** (-2.0 * np.arange(d_rope // 2) / d_rope)
+    ang = np.arange(rows)[:, None] * theta[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def test_query_and_key_rope_depend_only_on_relative_position():
+    # rotating q at p and the KV row at p' leaves their dot product a function of p - p', and
+    # rotating both at one position keeps it: the positions index the tables consistently
+    rng = np.random.default_rng(28)
+    d, dr, H = 32, 16, 3
+    cos, sin = _rope_tables(64, dr)
+    q = rng.standard_normal((H, d))
+    k = rng.standard_normal(d)
+    def dots(p, pk):
+        return M.qnorm_rope(q, p, cos, sin, dr, 0.0, False) @ M.swa_row(k, pk, cos, sin, dr)
+    assert np.allclose(dots(9, 4), dots(30, 25), atol=1e-12)
+    assert np.allclose(dots(17, 17), q @ k, atol=1e-12)
+    assert not np.allclose(dots(9, 4), dots(9, 5), atol=1e-6)
+    # the non-rotated dims are untouched; position 0 is the identity
+    assert np.array_equal(M.swa_row(k, 11, cos, sin, dr)[: d - dr], k[: d - dr])
+    assert np.allclose(M.swa_row(k, 0, cos, sin, dr), k, atol=0)
+
+
+def test_query_norm_is_per_head_and_commutes_with_rope():
+    rng = np.random.default_rng(29)
+    H, d, dr = 4, 32, 8
+    cos, sin = _rope_tables(40, dr)
+    q = rng.standard_normal((H, d)) * rng.uniform(0.1, 10.0, (H, 1))
+    y = M.qnorm_rope(q, 21, cos, sin, dr, 0.0, True)
+    assert np.allclose(np.sqrt((y * y).mean(axis=1)), 1.0, atol=1e-14)     # unit RMS per head
+    q2 = q.copy()
+    q2[1] *= 50.0                                                            # heads independent
+    assert np.allclose(M.qnorm_rope(q2, 21, cos, sin, dr, 0.0, True), y, atol=1e-13)
+    # the rotation keeps every pair's norm, so norming after it gives the same rows
+    r = M.qnorm_rope(q, 21, cos, sin, dr, 0.0, False)
+    assert np.allclose(M.rms_norm(r, np.ones(d), 0.0), y, atol=1e-13)
+    # no norm and no rotation: the query as given
+    assert np.array_equal(M.qnorm_rope(q, 21, None, None, 0, 1e-6, False), q)
+
+
 def test_compressor_partial_block_makes_no_entry():
     C, _ = M.compress(np.ones((7, 3)), np.zeros((7, 3)), 4)
     assert C.shape == (1, 3)
