@@ -270,6 +270,66 @@ def bench_compress_full(wl, sets: int, reps: int) -> dict:
             "algorithmic_bytes": nbytes, "gb_s": nbytes / (us * 1e-6) / 1e9}
 
 
+def bench_insert(wl, n_seq: int, per_seq: int, sets: int, reps: int) -> dict:
+    """Query preparation and sliding-window insert (hcs_qnorm_rope_kv_insert: per-head RMSNorm and
+    RoPE of the query in place, RoPE of the KV row and its bf16 store) for n_seq sequences of
+    `wl`'s shape with per_seq new tokens each, at the end of their context. Inputs are seeded
+    random values of that shape, `sets` sets rotated per replay."""
+    import torch
+
+    import hybrid_compressed_sparse_amd as hcs
+    from synth import layout as SL
+
+    dev = torch.device("cuda:0")
+    H, d, dr, ctx = wl.H, wl.d, wl.d_rope, wl.ctx
+    N = n_seq * per_seq
+    g = torch.Generator(device="cpu").manual_seed(5151)
+    p0 = ctx - per_seq
+    pg0, pg1 = p0 // 64, (ctx - 1) // 64
+    n_pg = pg1 - pg0 + 1
+    pt = torch.full((n_seq, (ctx + 63) // 64), -1, dtype=torch.int32)
+    for b in range(n_seq):
+        pt[b, pg0: pg1 + 1] = torch.arange(b * n_pg, (b + 1) * n_pg, dtype=torch.int32)
+    pool = SL.new_pool(n_seq * n_pg, "bf16", d, dev)
+    swa = hcs.paged(pool, pt.to(dev), "bf16", d)
+    seq = torch.arange(n_seq, dtype=torch.int32).repeat_interleave(per_seq).to(dev)
+    pos = torch.arange(p0, ctx, dtype=torch.int32).repeat(n_seq).to(dev)
+    theta = 10000.0 ** (-2.0 * torch.arange(dr // 2, dtype=torch.float64) / dr)
+    ang = torch.arange(ctx, dtype=torch.float64)[:, None] * theta[None, :]
+    cos, sin = torch.cos(ang).float().to(dev), torch.sin(ang).float().to(dev)
+    ins = [(torch.randn(N, H, d, generator=g).to(torch.bfloat16).to(dev),
+            (torch.randn(N, d, generator=g) * 0.3).to(torch.bfloat16).to(dev)) for _ in range(sets)]
+
+    def run_all():
+        for q, kv in ins:
+            hcs.qnorm_rope_kv_insert(q, kv, seq, pos, swa, rope_cos=cos, rope_sin=sin, q_norm=True)
+
+    run_all()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        run_all()
+    for _ in range(2):
+        gr.replay()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(reps):
+        gr.replay()
+    s1.record()
+    torch.cuda.synchronize()
+    us = s0.elapsed_time(s1) * 1e3 / (reps * sets)
+    # per token: q read and written (2 x H x d bf16), the KV row read and stored (2 x d bf16),
+    # the RoPE row (cos and sin, d_rope/2 float32 each), the token's sequence and position
+    per_tok = 2 * H * d * 2 + 2 * d * 2 + dr * 4 + 8
+    nbytes = N * per_tok
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del ins, pool
+    torch.cuda.empty_cache()
+    return {"us_per_call": us, "tokens": N, "config": f"{n_seq} x {per_seq} tokens, H={H}, d={d}, "
+            f"q RMSNorm + RoPE {dr} dims, bf16 SWA rows", "algorithmic_bytes": nbytes, "gb_s": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS}
+
+
 def cpu_baseline(wl, seconds: float) -> dict:
     from threadpoolctl import threadpool_info
 
@@ -456,6 +516,13 @@ def main():
         log("[bench] side measurement: full compressor at this decode step")
         result["compress_full"] = bench_compress_full(wl, R, max(1, args.steps // R))
         log(f"[bench] compress_full: {result['compress_full']['us_per_call']:.2f} us")
+        log("[bench] side measurement: query preparation and SWA insert (decode step, prefill chunk)")
+        reps = max(1, args.steps // R)
+        result["qnorm_rope_kv_insert"] = {"decode": bench_insert(wl, wl.B, 1, R, reps),
+                                          "prefill_chunk": bench_insert(wl, 1, 4096, R, reps)}
+        for k, v in result["qnorm_rope_kv_insert"].items():
+            log(f"[bench] qnorm_rope_kv_insert {k}: {v['us_per_call']:.2f} us, {v['gb_s']:.0f} GB/s "
+                f"({100 * v['hbm_frac']:.1f}% of HBM)")
         hw = C.HCA_DECODE
         log(f"[bench] side measurement: {hw.name}")
         hb = Bench(hw, R, seed=2000)

@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.hcs_sparse_mla_prefill_chunk.restype = i32
         L.hcs_sparse_mla_prefill_chunk.argtypes = [vp, Paged, Paged, vp, i32, i32, i32, i32, vp, i32,
                                                    i32, i32, i32, f32, vp, vp, vp, sz, vp]
+        L.hcs_qnorm_rope_kv_insert.restype = i32
+        L.hcs_qnorm_rope_kv_insert.argtypes = [vp, i32, vp, i64, vp, vp, i32, i32, i32, ctypes.c_float,
+                                               vp, vp, i32, i32, Paged, vp]
         _lib = L
     return _lib
 
@@ -160,6 +163,38 @@ def compress_kv_full(kv: torch.Tensor, score: torch.Tensor, cu_new: torch.Tensor
         _ptr(norm_weight, torch.float32, "norm_weight"), norm_eps, _ptr(rope_cos, torch.float32, "rope_cos"),
         _ptr(rope_sin, torch.float32, "rope_sin"), d_rope, rows, _as_paged(comp),
         _ptr(dbg, torch.float32, "dbg"), 0 if dbg is None else dbg.stride(0), _stream()), "compress_kv_full")
+
+
+# ------------------------------------------------------------------------------ query prep + SWA insert
+
+def qnorm_rope_kv_insert(q: Optional[torch.Tensor], kv: Optional[torch.Tensor], tok_seq: Optional[torch.Tensor],
+                         tok_pos: torch.Tensor, swa=None, rope_cos: Optional[torch.Tensor] = None,
+                         rope_sin: Optional[torch.Tensor] = None, q_norm: bool = False,
+                         eps: float = 1e-6, d: Optional[int] = None) -> None:
+    """hcs_qnorm_rope_kv_insert. q [N, H, d] bf16 (in place) or None; kv [N, >= d] bf16 rows
+    (row stride kv.stride(0)) or None; tok_seq, tok_pos [N] int32; rope_cos / rope_sin
+    [rows, d_rope/2] f32 (d_rope = 2 * columns); swa: the sliding-window cache."""
+    if q is not None and q.dtype != torch.bfloat16:
+        raise TypeError("q must be bf16")
+    if kv is not None and (kv.dtype != torch.bfloat16 or kv.stride(1) != 1):
+        raise TypeError("kv must be bf16 rows with unit column stride")
+    N = tok_pos.shape[0]
+    H = 0 if q is None else q.shape[1]
+    if d is None:
+        d = q.shape[2] if q is not None else swa.dim
+    d_rope = 0 if rope_cos is None else 2 * rope_cos.shape[-1]
+    rows = 0 if rope_cos is None else rope_cos.shape[0]
+    kv_ptr = None
+    if kv is not None:
+        if not kv.is_cuda:
+            raise ValueError("kv must be on the GPU")
+        kv_ptr = kv.data_ptr()
+    sw = _as_paged(swa) if swa is not None else Paged(None, None, 0, 0, 0, d)
+    _check(lib().hcs_qnorm_rope_kv_insert(
+        _ptr(q, torch.bfloat16, "q"), H, kv_ptr, 0 if kv is None else kv.stride(0),
+        _ptr(tok_seq, torch.int32, "tok_seq"), _ptr(tok_pos, torch.int32, "tok_pos"), N, d,
+        1 if q_norm else 0, eps, _ptr(rope_cos, torch.float32, "rope_cos"),
+        _ptr(rope_sin, torch.float32, "rope_sin"), d_rope, rows, sw, _stream()), "qnorm_rope_kv_insert")
 
 
 # ------------------------------------------------------------------------------ indexer

@@ -135,6 +135,53 @@ hcs_status hcs_compress_kv_full(const void* kv, const void* score, int in_dtype,
                     "compress_kv_full");
 }
 
+// ------------------------------------------------------------------------------ query prep + SWA insert
+hcs_status hcs_qnorm_rope_kv_insert(void* q, int H, const void* kv, int64_t kv_stride,
+                                    const int32_t* tok_seq, const int32_t* tok_pos, int N, int d,
+                                    int q_norm, float eps, const float* rope_cos,
+                                    const float* rope_sin, int d_rope, int rope_rows, hcs_paged swa,
+                                    void* stream) {
+  if (N < 0) return fail(HCS_ERR_INVALID_ARG, "N must be >= 0");
+  if (H < 0 || H > 128) return fail(HCS_ERR_UNSUPPORTED, "H must be in 0..128");
+  if (d != 128 && d != 512) return fail(HCS_ERR_UNSUPPORTED, "d must be 128 or 512");
+  if (q_norm && !(eps >= 0.f)) return fail(HCS_ERR_INVALID_ARG, "eps must be >= 0");
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(HCS_ERR_INVALID_ARG, "rope_cos and rope_sin are given together or not at all");
+  if (rope_cos && (d_rope < 2 || d_rope > d || d_rope % 2 || rope_rows < 1))
+    return fail(HCS_ERR_INVALID_ARG, "RoPE needs an even d_rope in 2..d and rope_rows >= 1");
+  if (N == 0 || (H == 0 && !kv)) return ok();
+  if (!tok_pos) return fail(HCS_ERR_INVALID_ARG, "null tok_pos");
+  if (H > 0 && (!q || !aligned(q, 16))) return fail(HCS_ERR_INVALID_ARG, "q must be non-null and 16-byte aligned");
+  hcs::InsertArgs a{};
+  if (kv) {
+    if (!tok_seq) return fail(HCS_ERR_INVALID_ARG, "null tok_seq");
+    if (!aligned(kv, 16) || kv_stride < d || kv_stride % 8)
+      return fail(HCS_ERR_INVALID_ARG, "kv must be 16-byte aligned with kv_stride >= d and a multiple of 8");
+    hcs_status s = check_paged(swa, "swa", d, true, false);
+    if (s != HCS_OK) return s;
+    a.swa_base = static_cast<uint8_t*>(swa.base);
+    a.swa_pt = swa.page_table;
+    a.swa_pt_stride = swa.pt_stride;
+    a.swa_num_pages = swa.num_pages;
+    a.fmt = swa.fmt;
+  }
+  a.q = static_cast<uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(kv);
+  a.kv_stride = kv_stride;
+  a.tok_seq = tok_seq;
+  a.tok_pos = tok_pos;
+  a.N = N;
+  a.H = H;
+  a.d = d;
+  a.q_norm = q_norm ? 1 : 0;
+  a.eps = eps;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.d_rope = rope_cos ? d_rope : 0;
+  a.rope_rows = rope_rows;
+  return hip_status(hcs::launch_qrope_insert(a, static_cast<hipStream_t>(stream)), "qnorm_rope_kv_insert");
+}
+
 // ------------------------------------------------------------------------------ indexer
 size_t hcs_index_topk_workspace_size(int N, int max_pos, int m, int topk) {
   if (N <= 0 || max_pos < 0 || m < 1 || topk < 1) return 0;

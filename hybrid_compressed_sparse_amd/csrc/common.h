@@ -63,6 +63,15 @@ __device__ __forceinline__ float warp_sum(float v) {
   return v;
 }
 
+// UE8M0 exponent of an fp8_ds latent block: the smallest e with amax <= 448 * 2^e
+// (448 = 0.875 * 2^9), 0 for an all-zero block, clamped to [-127, 127].
+__device__ __forceinline__ int fp8ds_scale_exp(float amax) {
+  int E;
+  const float f = __builtin_frexpf(amax, &E);
+  const int e = amax > 0.f ? E - 9 + (f > 0.875f ? 1 : 0) : 0;
+  return max(-127, min(127, e));
+}
+
 // Order-preserving map of float32 to uint32: a < b  <=>  key(a) < key(b) (for non-NaN).
 __device__ __forceinline__ uint32_t f32_order_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -29,12 +29,7 @@ __device__ __forceinline__ void compress_store(const CompressArgs& a, int b, int
   if (act && a.dbg) a.dbg[(int64_t)b * a.dbg_stride + (int64_t)(kb - kb_first) * d + c] = C;
   if (a.fmt == HCS_FMT_FP8DS) {
     if (c < kFp8Latent) {
-      const float amax = warp_max(fabsf(C));
-      // smallest e with amax <= 448 * 2^e; 448 = 0.875 * 2^9
-      int E;
-      const float f = __builtin_frexpf(amax, &E);
-      int e = amax > 0.f ? E - 9 + (f > 0.875f ? 1 : 0) : 0;
-      e = max(-127, min(127, e));
+      const int e = fp8ds_scale_exp(warp_max(fabsf(C)));
       const float y = __builtin_ldexpf(C, -e);
       const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false);
       if (page) {

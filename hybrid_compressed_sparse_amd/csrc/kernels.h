@@ -60,6 +60,25 @@ struct CompressArgs {
 hipError_t launch_compress(const CompressArgs& a, int max_new, hipStream_t stream);
 hipError_t launch_compress_full(const CompressArgs& a, int max_new, hipStream_t stream);
 
+// ---------------------------------------------------------------- query preparation + SWA insert
+struct InsertArgs {
+  uint16_t* q;                // [N, H, d] bf16, rewritten in place (H may be 0)
+  const uint16_t* kv;         // [N, kv_stride] bf16 (first d columns), or nullptr: no insert
+  int64_t kv_stride;
+  const int32_t* tok_seq;     // [N] page-table row of each token
+  const int32_t* tok_pos;     // [N] position of each token (< 0: the token is skipped)
+  int N, H, d;
+  int q_norm;                 // unit RMS per query head before the rotation
+  float eps;
+  const float* rope_cos;      // [rope_rows, d_rope / 2] or nullptr: no rotation
+  const float* rope_sin;
+  int d_rope, rope_rows;
+  uint8_t* swa_base;
+  const int32_t* swa_pt;
+  int swa_pt_stride, swa_num_pages, fmt;
+};
+hipError_t launch_qrope_insert(const InsertArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- indexer + top-k
 struct IndexArgs {
   const uint8_t* q;           // bf16 [N, H_I, d_I] or packed e2m1 [N, H_I, d_I/2]

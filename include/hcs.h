@@ -18,7 +18,10 @@
  *   hcs_sparse_mla_decode     single-KV-head attention of every query head over the query's
  *                             sliding window plus its selected (CSA) or all visible (HCA)
  *                             compressed entries, K = V = the shared row;
- *   hcs_sparse_mla_prefill_chunk  the same for a chunk of consecutive queries of one sequence.
+ *   hcs_sparse_mla_prefill_chunk  the same for a chunk of consecutive queries of one sequence;
+ *   hcs_qnorm_rope_kv_insert  readies the new tokens' query heads (optional per-head RMSNorm,
+ *                             RoPE) and writes their rotated KV rows into the sliding-window
+ *                             cache.
  *
  * Conventions shared by every call
  *   - Pointers are device pointers unless marked "host". The caller owns every buffer; the
@@ -259,6 +262,39 @@ hcs_status hcs_sparse_mla_prefill_chunk(const void* q, hcs_paged swa, hcs_paged 
                                         const float* sink, int H, int d, int window, int m,
                                         float scale, void* out, float* lse, void* ws,
                                         size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* Query preparation and sliding-window insert of new tokens: "Code Reading Map", "Default */
+/* stream" (the fused q-norm / RoPE / KV insert) and the "DeepSeek V4.1 attention" page's  */
+/* `_fused_qnorm_rope_kv_insert`. For token t at position p = tok_pos[t]:                  */
+/*   every query head h: when q_norm, q[t,h,:] /= sqrt(mean(q[t,h,:]^2) + eps) (no weight), */
+/*     then its last d_rope dims are rotated in GPT-J pairs (2j, 2j+1) at position p:      */
+/*     (a, b) -> (a cos - b sin, a sin + b cos) with row p of the tables; written back in   */
+/*     place as bf16;                                                                     */
+/*   the KV row kv[t, 0..d-1] is rotated the same way (not normalised) and stored as       */
+/*     logical row p of sequence tok_seq[t] in `swa`, in its format (bf16, or fp8_ds with */
+/*     the compressor's scale and rounding rule; the rotary dims are the record's bf16    */
+/*     part when d_rope <= 64). kv itself is not modified.                                 */
+/* Values are computed in float32 from the bf16 inputs and rounded once.                  */
+/*                                                                                        */
+/* q        [N, H, d] bf16, in/out; may be NULL when H == 0 (insert only).                */
+/* kv       [N, kv_stride] bf16 rows (kv_stride >= d, a multiple of 8), or NULL: no        */
+/*          insert (query preparation only).                                               */
+/* tok_seq  [N] int32 page-table row of each token (needed with kv).                       */
+/* tok_pos  [N] int32 position of each token; a negative position skips the token.         */
+/* rope_cos, rope_sin [rope_rows, d_rope / 2] float32, or both NULL: no rotation. A        */
+/*          position at or past rope_rows reads the last row.                              */
+/* swa      sliding-window cache (dim d; HCS_FMT_BF16, or HCS_FMT_FP8DS with d = 512).     */
+/*          A row whose page is not resident (or past the page table) is not written.      */
+/* Tokens must have distinct (tok_seq, tok_pos) pairs: two writes of one row race.         */
+/* Constraints: d in {128, 512}, 0 <= H <= 128, eps >= 0, d_rope even in 2..d, q and kv    */
+/* 16-byte aligned. Errors: HCS_ERR_INVALID_ARG / HCS_ERR_UNSUPPORTED as stated, before any */
+/* launch.                                                                                */
+hcs_status hcs_qnorm_rope_kv_insert(void* q, int H, const void* kv, int64_t kv_stride,
+                                    const int32_t* tok_seq, const int32_t* tok_pos, int N, int d,
+                                    int q_norm, float eps, const float* rope_cos,
+                                    const float* rope_sin, int d_rope, int rope_rows, hcs_paged swa,
+                                    void* stream);
 
 #ifdef __cplusplus
 }

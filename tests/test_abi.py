@@ -83,6 +83,25 @@ def test_validation_errors_before_any_launch():
                              None) == 0
 
 
+@needs_lib
+def test_insert_validation_errors_before_any_launch():
+    L = hcs.lib()
+    f = L.hcs_qnorm_rope_kv_insert
+    # q, H, kv, kv_stride, tok_seq, tok_pos, N, d, q_norm, eps, cos, sin, d_rope, rows, swa, stream
+    assert f(16, 64, 16, 512, 16, 16, 4, 256, 0, 0.0, None, None, 0, 0, _paged(), None) == 2
+    assert f(16, 64, 16, 512, 16, 16, 4, 512, 0, 0.0, 16, None, 64, 100, _paged(), None) == 1
+    assert f(16, 64, 16, 512, 16, 16, 4, 512, 0, 0.0, 16, 16, 63, 100, _paged(), None) == 1
+    assert f(16, 64, 16, 512, 16, 16, 4, 512, 1, -1.0, None, None, 0, 0, _paged(), None) == 1
+    assert f(16, 64, 16, 500, 16, 16, 4, 512, 0, 0.0, None, None, 0, 0, _paged(), None) == 1   # stride < d
+    assert f(16, 64, 16, 512, 16, 16, 4, 512, 0, 0.0, None, None, 0, 0, _paged(0, 128), None) == 1
+    assert f(16, 64, 16, 128, 16, 16, 4, 128, 0, 0.0, None, None, 0, 0, _paged(1, 128), None) == 2  # fp8_ds at d 128
+    assert f(16, 64, 16, 512, None, 16, 4, 512, 0, 0.0, None, None, 0, 0, _paged(), None) == 1  # no tok_seq
+    assert f(18, 64, None, 0, None, 16, 4, 512, 0, 0.0, None, None, 0, 0, _paged(), None) == 1  # q misaligned
+    # nothing to do
+    assert f(None, 0, None, 0, None, None, 4, 512, 0, 0.0, None, None, 0, 0, _paged(), None) == 0
+    assert f(None, 64, None, 0, None, None, 0, 512, 0, 0.0, None, None, 0, 0, _paged(), None) == 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(hcs, "_lib", None)
     monkeypatch.setattr(hcs, "LIB_PATH", "/nonexistent/libhcs.so")
