@@ -416,6 +416,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the HCA side measurement")
     ap.add_argument("--only", default=None, help="replay only this op's graph (for profiling)")
+    ap.add_argument("--side", default=None, choices=["compress_full", "insert_decode", "insert_prefill"],
+                    help="run only this side measurement of the decode workload (for profiling)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="instead of the path: copy MIB MiB device to device --steps times (the known-size "
                          "reference for the HBM byte counters)")
@@ -440,6 +442,20 @@ def main():
         return
 
     wl = C.BY_NAME[args.workload]
+    if args.side:
+        if wl.kind != "decode":
+            sys.exit("side measurements use a decode workload's shapes")
+        R = max(1, min(args.sets, args.steps))
+        reps = max(1, args.steps // R)
+        if args.side == "compress_full":
+            res = bench_compress_full(wl, R, reps)
+        elif args.side == "insert_decode":
+            res = bench_insert(wl, wl.B, 1, R, reps)
+        else:
+            res = bench_insert(wl, 1, 4096, R, reps)
+        log(f"[bench] {args.side}: {res['us_per_call']:.2f} us")
+        print(json.dumps({"side": args.side, **res}))
+        return
     if wl.kind == "prefill":
         return bench_prefill(wl, args)
     if wl.kind != "decode":
