@@ -94,6 +94,15 @@ def decode_mxfp4(packed, scales) -> np.ndarray:
     return (v * decode_ue8m0(scales)[..., None]).reshape(*lead, 2 * half)
 
 
+FP8IX_DIM = 128
+
+
+def decode_fp8ix(codes, scale) -> np.ndarray:
+    """FP8 indexer key row (128 e4m3 codes + one float32 scale; the 132-byte row of the "DeepSeek
+    V4.1 attention" page's indexer cache, one scale per 128 dims) -> float64 [..., 128]."""
+    return decode_e4m3(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
 # ----------------------------------------------------------------- rounding (reference rules)
 
 
@@ -148,3 +157,44 @@ def quantize_fp8ds(x32):
     e = ue8m0_exponent(np.abs(lat).max(axis=-1), 448.0)
     codes = round_e4m3(lat / np.ldexp(1.0, e)[..., None]).reshape(*lead, FP8DS_LATENT)
     return codes, round_bf16(x[..., FP8DS_LATENT:]), (e + 127).astype(np.uint8)
+
+
+def round_e2m1(y) -> np.ndarray:
+    """Nearest e2m1 code (nibble, sign in bit 3) of values with |y| <= 6; a value halfway
+    between two neighbours takes the one whose code is even (mantissa bit 0), as the OCP MX
+    round-to-nearest-even conversion does."""
+    y = np.asarray(y, dtype=np.float64)
+    if np.any(np.abs(y) > 6.0):
+        raise ValueError("e2m1 rounding needs |y| <= 6 (the block scale guarantees it)")
+    a = np.abs(y)
+    mags = E2M1_TABLE[:8]                     # 0, .5, 1, 1.5, 2, 3, 4, 6 for codes 0..7
+    dist = np.abs(a[..., None] - mags)
+    best = dist.min(axis=-1, keepdims=True)
+    # among the nearest (one, or two at a tie) prefer the even code
+    cand = np.where(dist == best, np.arange(8) + 16 * (np.arange(8) & 1), 99)
+    code = (cand.min(axis=-1) % 16).astype(np.int64)
+    code = code | np.where(y < 0, 0x8, 0)     # the sign is kept, also when the value rounds to 0
+    return code.astype(np.uint8)
+
+
+def quantize_mxfp4(x32):
+    """MXFP4 row of float32 values [..., D]: per 32 values the power-of-two scale 2**e with e the
+    smallest integer such that amax <= 6 * 2**e, codes = nearest-even e2m1 of x / 2**e, element
+    2j in the low nibble of byte j. Returns (packed uint8 [..., D/2], scales uint8 [..., D/32])."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    lead, D = x.shape[:-1], x.shape[-1]
+    blk = x.reshape(*lead, D // MX_BLOCK, MX_BLOCK)
+    e = ue8m0_exponent(np.abs(blk).max(axis=-1), 6.0)
+    nib = round_e2m1(blk / np.ldexp(1.0, e)[..., None]).reshape(*lead, D)
+    packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)
+
+
+def quantize_fp8ix(x32):
+    """FP8 indexer key row of float32 values [..., 128]: one power-of-two scale 2**e for the row
+    (e the smallest integer with amax <= 448 * 2**e), codes = RNE_e4m3(x / 2**e). Returns
+    (codes uint8 [..., 128], scale float32 [...])."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    e = ue8m0_exponent(np.abs(x).max(axis=-1), 448.0)
+    codes = round_e4m3(x / np.ldexp(1.0, e)[..., None])
+    return codes, np.ldexp(1.0, e).astype(np.float32)

@@ -21,6 +21,11 @@ Sources (DeepSeek-V4 pages):
     series and the m before it in the overlapping series (the second half of the
     kv / score columns), so boundary tokens feed two entries; then RMSNorm of the
     entry, RoPE on its last 64 dims, and the store.
+  * indexer Q/K -- "DeepSeek V4.1 attention" page, `DeepseekV4Indexer` (`forward_q`: RoPE
+    and quantization of the projected query, weights times softmax_scale and
+    n_head**-0.5; `_produce_k`: k_norm (an RMSNorm) of the projected latent at
+    group-boundary tokens, RoPE at the group position, quantization into the key cache;
+    `_indexer_k_cache_head_dim`: 68-byte MXFP4 and 132-byte FP8 rows).
   * query preparation and SWA insert -- same page, "Default stream" (the fused
     q-norm / RoPE / KV insert: per-head RMSNorm of the query heads, GPT-J RoPE on
     the last 64 dims of every query head and of the KV row, the KV row stored in
@@ -46,6 +51,10 @@ Readings where the pages are open (listed in the design notes too):
   * RMSNorm: x / sqrt(mean(x^2) + eps) * weight over the d dims;
   * RoPE: GPT-J style (interleaved pairs (2j, 2j+1)) on the last d_rope dims, at
     the entry's position m*i, with the caller's cos/sin tables [positions, d_rope/2].
+  * indexer query / key production (NEXT to the scores): the query's last d_rope dims
+    are rotated at the token's position and its weights take softmax_scale * H_I^-0.5;
+    a key is RMSNorm (with weight) of the projected latent, rotated at the entry's
+    position m*i; both are then quantized to the key cache's format;
   * query norm: over each head's d dims, with no weight (the op takes none); a raw
     token is rotated at its own position p, and its KV row becomes logical row p of
     the sliding-window cache.
@@ -173,6 +182,26 @@ def swa_row(kv, pos: int, cos_table, sin_table, d_rope: int):
     c = np.asarray(cos_table, dtype=np.float64)[pos]
     s = np.asarray(sin_table, dtype=np.float64)[pos]
     return rope_gptj(kv, c, s, d_rope)
+
+
+def indexer_query(q, pos: int, cos_table, sin_table, d_rope: int, w, softmax_scale: float):
+    """Indexer query of a token: q [H_I, d_I] rotated (GPT-J) on its last d_rope dims at the
+    token's position; the head weights w [H_I] take the softmax scale and H_I^(-1/2) (both
+    positive, so they move no top-k). Returns (q [H_I, d_I], w [H_I])."""
+    q = qnorm_rope(q, pos, cos_table, sin_table, d_rope, 0.0, False)
+    w = np.asarray(w, dtype=np.float64) * softmax_scale * q.shape[0] ** -0.5
+    return q, w
+
+
+def indexer_key(k_pre, entry: int, m: int, norm_weight, eps: float, cos_table, sin_table,
+                d_rope: int):
+    """Indexer key of compressed entry `entry`: the projected latent k_pre [d_I] through RMSNorm
+    (weight norm_weight) and then GPT-J RoPE on its last d_rope dims at the entry's position
+    m * entry, the position the compressor rotates the entry at."""
+    k = rms_norm(k_pre, norm_weight, eps)
+    if d_rope > 0:
+        k = rope_gptj(k, np.asarray(cos_table)[m * entry], np.asarray(sin_table)[m * entry], d_rope)
+    return k
 
 
 def index_scores(q, w, K) -> np.ndarray:

@@ -156,3 +156,68 @@ def test_generator_mxfp4_rows_decode_to_nearest():
     assert np.allclose(np.abs(ys - xs), nearest_err)
     # element order inside a byte: element 2j in the low nibble
     assert F.decode_mxfp4(np.array([[0x21] + [0] * 15]), np.array([127]))[0, :2].tolist() == [0.5, 1.0]
+
+
+def test_e2m1_rounding_round_trips_and_ties_to_even():
+    # every magnitude code decodes and rounds back to itself, with either sign
+    for c in range(16):
+        v = F.decode_e2m1(np.array([c]))[0]
+        if c == 8:
+            continue                                     # -0 decodes to 0, which rounds to +0
+        assert F.round_e2m1(np.array([v]))[0] == c
+    # halfway points between neighbouring magnitudes go to the even code (OCP MX: RNE)
+    halfway = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}
+    for v, c in halfway.items():
+        assert F.round_e2m1(np.array([v]))[0] == c
+        assert F.round_e2m1(np.array([-v]))[0] == c | 8
+    # just off a halfway point: the nearer neighbour
+    mags = F.E2M1_TABLE[:8]
+    for k in range(7):
+        mid = (mags[k] + mags[k + 1]) / 2
+        assert F.round_e2m1(np.array([mid - 1e-9]))[0] == k
+        assert F.round_e2m1(np.array([mid + 1e-9]))[0] == k + 1
+
+
+def test_mxfp4_quantizer_scale_rule_and_error_bound():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((40, 128)) * np.exp(rng.uniform(-6, 6, (40, 1)))).astype(np.float32)
+    x[3, :32] = 0.0                                      # an all-zero block: scale byte 127
+    packed, sc = F.quantize_mxfp4(x)
+    assert packed.shape == (40, 64) and sc.shape == (40, 4)
+    assert np.all(sc[3, 0] == 127)
+    blk = np.abs(x.astype(np.float64)).reshape(40, 4, 32).max(axis=-1)
+    e = sc.astype(np.int64) - 127
+    # brute force: the smallest power of two with amax <= 6 * 2**e
+    for i in range(40):
+        for j in range(4):
+            if blk[i, j] == 0:
+                continue
+            best = min(k for k in range(-140, 140) if blk[i, j] <= 6.0 * 2.0 ** k)
+            assert e[i, j] == best
+    dec = F.decode_mxfp4(packed, sc)
+    # within half the e2m1 spacing at the value's place (spacing 0.5 below 2, 1 up to 4, 2 above)
+    y = np.abs(x.astype(np.float64)) / np.repeat(np.ldexp(1.0, e), 32, axis=1)
+    half_step = np.where(y < 2.0, 0.25, np.where(y < 4.0, 0.5, 1.0)) * np.repeat(np.ldexp(1.0, e), 32, axis=1)
+    assert np.all(np.abs(dec - x) <= half_step * (1 + 1e-12))
+    # element 2j is the low nibble of byte j
+    one = np.zeros((1, 32), dtype=np.float32)
+    one[0, 0], one[0, 1] = 6.0, 1.0
+    p1, s1 = F.quantize_mxfp4(one)
+    assert p1[0, 0] == (0x7 | (0x2 << 4)) and s1[0, 0] == 127
+
+
+def test_fp8ix_quantizer_round_trip():
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((30, 128)) * np.exp(rng.uniform(-8, 8, (30, 1)))).astype(np.float32)
+    codes, scale = F.quantize_fp8ix(x)
+    assert codes.shape == (30, 128) and scale.shape == (30,) and scale.dtype == np.float32
+    amax = np.abs(x.astype(np.float64)).max(axis=1)
+    # the scale is the smallest power of two with amax <= 448 * scale
+    assert np.all(amax <= 448.0 * scale) and np.all(amax > 224.0 * scale)
+    dec = F.decode_fp8ix(codes, scale)
+    rel = np.abs(dec - x) / np.maximum(np.abs(x), 2.0 ** -6 * scale[:, None])
+    assert rel.max() <= 2.0 ** -4 * (1 + 1e-12)          # e4m3 keeps 4 significant bits
+    # exactly representable rows come back unchanged
+    reps = F.decode_e4m3(rng.integers(0, 126, (4, 128))) * 2.0 ** 5
+    c2, s2 = F.quantize_fp8ix(reps.astype(np.float32))
+    assert np.array_equal(F.decode_fp8ix(c2, s2), reps)

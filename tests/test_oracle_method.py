@@ -251,6 +251,30 @@ def test_query_norm_is_per_head_and_commutes_with_rope():
     assert np.array_equal(M.qnorm_rope(q, 21, None, None, 0, 1e-6, False), q)
 
 
+def test_indexer_query_and_key_relative_position_and_scales():
+    rng = np.random.default_rng(30)
+    H, dI, dr, m = 4, 16, 8, 4
+    cos, sin = _rope_tables(200, dr)
+    q = rng.standard_normal((H, dI))
+    kp = rng.standard_normal(dI)
+    w = rng.uniform(0, 1, H)
+    nw = rng.uniform(0.5, 2.0, dI)
+    qr, wr = M.indexer_query(q, 37, cos, sin, dr, w, dI ** -0.5)
+    assert np.allclose(wr, w * dI ** -0.5 / 2.0, atol=0)                   # H^-1/2 = 1/2
+    # the key is the normed latent, rotated at m * entry: with a query at position p the score
+    # depends on p - m * entry only
+    def score(p, ent):
+        qq, ww = M.indexer_query(q, p, cos, sin, dr, w, 1.0)
+        return M.index_scores(qq, ww, M.indexer_key(kp, ent, m, nw, 1e-6, cos, sin, dr)[None])[0]
+    assert np.isclose(score(41, 5), score(61, 10), atol=1e-12)              # 41 - 20 = 61 - 40
+    assert not np.isclose(score(41, 5), score(41, 6), atol=1e-9)
+    k0 = M.indexer_key(kp, 0, m, nw, 1e-6, cos, sin, dr)                   # position 0: no turn
+    assert np.allclose(k0, M.rms_norm(kp, nw, 1e-6), atol=0)
+    # no rotation on the first dI - dr dims of a key at any entry
+    k7 = M.indexer_key(kp, 7, m, nw, 1e-6, cos, sin, dr)
+    assert np.array_equal(k7[: dI - dr], k0[: dI - dr])
+
+
 def test_compressor_partial_block_makes_no_entry():
     C, _ = M.compress(np.ones((7, 3)), np.zeros((7, 3)), 4)
     assert C.shape == (1, 3)
