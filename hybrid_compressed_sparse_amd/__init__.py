@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhcs.so")
 
-FMT = {"bf16": 0, "fp8ds": 1, "mxfp4": 2}
+FMT = {"bf16": 0, "fp8ds": 1, "mxfp4": 2, "fp8ix": 3}
 IN_DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 
 
@@ -76,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.hcs_qnorm_rope_kv_insert.restype = i32
         L.hcs_qnorm_rope_kv_insert.argtypes = [vp, i32, vp, i64, vp, vp, i32, i32, i32, ctypes.c_float,
                                                vp, vp, i32, i32, Paged, vp]
+        L.hcs_indexer_q_prep.restype = i32
+        L.hcs_indexer_q_prep.argtypes = [vp, vp, vp, i32, i32, i32, f32, vp, vp, i32, i32, i32, vp, vp, vp, vp]
+        L.hcs_indexer_k_store.restype = i32
+        L.hcs_indexer_k_store.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, f32, vp, vp, i32, i32, Paged, vp]
         _lib = L
     return _lib
 
@@ -197,6 +201,40 @@ def qnorm_rope_kv_insert(q: Optional[torch.Tensor], kv: Optional[torch.Tensor], 
         _ptr(rope_sin, torch.float32, "rope_sin"), d_rope, rows, sw, _stream()), "qnorm_rope_kv_insert")
 
 
+# ------------------------------------------------------------------------------ indexer Q / K production
+
+def indexer_q_prep(q: torch.Tensor, w: torch.Tensor, tok_pos: torch.Tensor, out_fmt: str, q_out: torch.Tensor,
+                   w_out: torch.Tensor, q_scale_out: Optional[torch.Tensor] = None, w_scale: float = 1.0,
+                   rope_cos: Optional[torch.Tensor] = None, rope_sin: Optional[torch.Tensor] = None) -> None:
+    """hcs_indexer_q_prep. q [N, H_I, 128] bf16, w [N, H_I] f32, tok_pos [N] int32; out_fmt
+    "bf16" (q_out bf16 [N, H_I, 128]), "mxfp4" (q_out uint8 [N, H_I, 64], q_scale_out uint8
+    [N, H_I, 4]) or "fp8ix" (q_out uint8 [N, H_I, 128], q_scale_out f32 [N, H_I])."""
+    N, H, d = q.shape
+    d_rope = 0 if rope_cos is None else 2 * rope_cos.shape[-1]
+    rows = 0 if rope_cos is None else rope_cos.shape[0]
+    _check(lib().hcs_indexer_q_prep(
+        _ptr(q, torch.bfloat16, "q"), _ptr(w, torch.float32, "w"), _ptr(tok_pos, torch.int32, "tok_pos"), N, H, d,
+        w_scale, _ptr(rope_cos, torch.float32, "rope_cos"), _ptr(rope_sin, torch.float32, "rope_sin"), d_rope, rows,
+        FMT[out_fmt], _ptr(q_out, name="q_out"), _ptr(q_scale_out, name="q_scale_out"),
+        _ptr(w_out, torch.float32, "w_out"), _stream()), "indexer_q_prep")
+
+
+def indexer_k_store(k_pre: torch.Tensor, ent_seq: torch.Tensor, ent_idx: torch.Tensor, m: int, keys,
+                    norm_weight: torch.Tensor, eps: float = 1e-6, rope_cos: Optional[torch.Tensor] = None,
+                    rope_sin: Optional[torch.Tensor] = None) -> None:
+    """hcs_indexer_k_store. k_pre [n, >= 128] bf16 rows (row stride k_pre.stride(0)); ent_seq,
+    ent_idx [n] int32; keys: the indexer key cache (bf16, mxfp4 or fp8ix, dim 128)."""
+    if k_pre.dtype != torch.bfloat16 or k_pre.stride(1) != 1 or not k_pre.is_cuda:
+        raise TypeError("k_pre must be bf16 rows on the GPU with unit column stride")
+    d_rope = 0 if rope_cos is None else 2 * rope_cos.shape[-1]
+    rows = 0 if rope_cos is None else rope_cos.shape[0]
+    _check(lib().hcs_indexer_k_store(
+        k_pre.data_ptr(), k_pre.stride(0), _ptr(ent_seq, torch.int32, "ent_seq"), _ptr(ent_idx, torch.int32, "ent_idx"),
+        ent_idx.shape[0], 128, m, _ptr(norm_weight, torch.float32, "norm_weight"), eps,
+        _ptr(rope_cos, torch.float32, "rope_cos"), _ptr(rope_sin, torch.float32, "rope_sin"), d_rope, rows,
+        _as_paged(keys), _stream()), "indexer_k_store")
+
+
 # ------------------------------------------------------------------------------ indexer
 
 def index_topk_workspace_size(N: int, max_pos: int, m: int, topk: int) -> int:
@@ -213,7 +251,7 @@ def index_topk(q, q_scale: Optional[torch.Tensor], w: torch.Tensor, keys, q_seq:
     if ws is None:
         ws = _workspace(index_topk_workspace_size(N, max_pos, m, topk), w.device)
     _check(lib().hcs_index_topk(
-        _ptr(q, name="q"), _ptr(q_scale, torch.uint8, "q_scale"), _ptr(w, torch.float32, "w"),
+        _ptr(q, name="q"), _ptr(q_scale, name="q_scale"), _ptr(w, torch.float32, "w"),
         _as_paged(keys), _ptr(q_seq, torch.int32, "q_seq"), _ptr(q_pos, torch.int32, "q_pos"),
         N, H_I, d_I, m, topk, max_pos, _ptr(out_idx, torch.int32, "out_idx"),
         _ptr(out_score, torch.float32, "out_score"), _ptr(ws, name="ws"),
@@ -230,7 +268,7 @@ def index_topk_chunk(q, q_scale: Optional[torch.Tensor], w: torch.Tensor, keys, 
     if ws is None:
         ws = _workspace(index_topk_workspace_size(Q, P0 + Q - 1, m, topk), w.device)
     _check(lib().hcs_index_topk_chunk(
-        _ptr(q, name="q"), _ptr(q_scale, torch.uint8, "q_scale"), _ptr(w, torch.float32, "w"),
+        _ptr(q, name="q"), _ptr(q_scale, name="q_scale"), _ptr(w, torch.float32, "w"),
         _as_paged(keys), seq, P0, Q, H_I, d_I, m, topk, _ptr(out_idx, torch.int32, "out_idx"),
         _ptr(out_score, torch.float32, "out_score"), _ptr(ws, name="ws"),
         0 if ws is None else ws.numel() * ws.element_size(), _stream()), "index_topk_chunk")
@@ -253,7 +291,7 @@ def index_topk_compress(q, q_scale: Optional[torch.Tensor], w: torch.Tensor, key
     if ws is None:
         ws = _workspace(index_topk_workspace_size(N, max_pos, m_ix, topk), w.device)
     _check(lib().hcs_index_topk_compress(
-        _ptr(q, name="q"), _ptr(q_scale, torch.uint8, "q_scale"), _ptr(w, torch.float32, "w"),
+        _ptr(q, name="q"), _ptr(q_scale, name="q_scale"), _ptr(w, torch.float32, "w"),
         _as_paged(keys), _ptr(q_seq, torch.int32, "q_seq"), _ptr(q_pos, torch.int32, "q_pos"),
         N, H_I, d_I, m_ix, topk, max_pos, _ptr(out_idx, torch.int32, "out_idx"),
         _ptr(out_score, torch.float32, "out_score"), _ptr(ws, name="ws"),

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhcs.so")
-SOURCES = ["api.hip", "attention.hip", "compress.hip", "indexer.hip", "insert.hip"]
+SOURCES = ["api.hip", "attention.hip", "compress.hip", "indexer.hip", "indexer_prep.hip", "insert.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -36,13 +36,15 @@ hcs_status check_paged(const hcs_paged& p, const char* name, int want_dim, bool 
   if (!p.base || !p.page_table) return fail(HCS_ERR_INVALID_ARG, "%s: null base or page_table", name);
   if (p.pt_stride <= 0 || p.num_pages <= 0)
     return fail(HCS_ERR_INVALID_ARG, "%s: pt_stride and num_pages must be positive", name);
-  if (p.fmt != HCS_FMT_BF16 && p.fmt != HCS_FMT_FP8DS && p.fmt != HCS_FMT_MXFP4)
+  if (p.fmt != HCS_FMT_BF16 && p.fmt != HCS_FMT_FP8DS && p.fmt != HCS_FMT_MXFP4 && p.fmt != HCS_FMT_FP8IX)
     return fail(HCS_ERR_INVALID_ARG, "%s: unknown format %d", name, p.fmt);
   if (p.dim != want_dim) return fail(HCS_ERR_INVALID_ARG, "%s: dim %d, expected %d", name, p.dim, want_dim);
   if (p.fmt == HCS_FMT_FP8DS && (!allow_fp8 || p.dim != 512))
     return fail(HCS_ERR_UNSUPPORTED, "%s: fp8_ds rows need dim 512 and a KV cache", name);
-  if (p.fmt == HCS_FMT_MXFP4 && !allow_mx)
-    return fail(HCS_ERR_UNSUPPORTED, "%s: MXFP4 is an indexer-key format", name);
+  if ((p.fmt == HCS_FMT_MXFP4 || p.fmt == HCS_FMT_FP8IX) && !allow_mx)
+    return fail(HCS_ERR_UNSUPPORTED, "%s: MXFP4 and FP8IX are indexer-key formats", name);
+  if (p.fmt == HCS_FMT_FP8IX && p.dim != 128)
+    return fail(HCS_ERR_UNSUPPORTED, "%s: FP8IX rows have 128 dims", name);
   if (!aligned(p.base, 16)) return fail(HCS_ERR_INVALID_ARG, "%s: base must be 16-byte aligned", name);
   return HCS_OK;
 }
@@ -182,6 +184,88 @@ hcs_status hcs_qnorm_rope_kv_insert(void* q, int H, const void* kv, int64_t kv_s
   return hip_status(hcs::launch_qrope_insert(a, static_cast<hipStream_t>(stream)), "qnorm_rope_kv_insert");
 }
 
+// ------------------------------------------------------------------------------ indexer Q / K production
+static hcs_status check_rope(const float* rope_cos, const float* rope_sin, int d_rope, int rope_rows, int d) {
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(HCS_ERR_INVALID_ARG, "rope_cos and rope_sin are given together or not at all");
+  if (rope_cos && (d_rope < 2 || d_rope > d || d_rope % 2 || rope_rows < 1))
+    return fail(HCS_ERR_INVALID_ARG, "RoPE needs an even d_rope in 2..d and rope_rows >= 1");
+  return HCS_OK;
+}
+
+hcs_status hcs_indexer_q_prep(const void* q, const float* w, const int32_t* tok_pos, int N, int H_I,
+                              int d_I, float w_scale, const float* rope_cos, const float* rope_sin,
+                              int d_rope, int rope_rows, int out_fmt, void* q_out,
+                              void* q_scale_out, float* w_out, void* stream) {
+  if (N < 0) return fail(HCS_ERR_INVALID_ARG, "N must be >= 0");
+  if (H_I < 1 || H_I > 64) return fail(HCS_ERR_UNSUPPORTED, "H_I must be in 1..64");
+  if (d_I != 128) return fail(HCS_ERR_UNSUPPORTED, "d_I must be 128");
+  if (out_fmt != HCS_FMT_BF16 && out_fmt != HCS_FMT_MXFP4 && out_fmt != HCS_FMT_FP8IX)
+    return fail(HCS_ERR_INVALID_ARG, "out_fmt must be HCS_FMT_BF16, HCS_FMT_MXFP4 or HCS_FMT_FP8IX");
+  hcs_status s = check_rope(rope_cos, rope_sin, d_rope, rope_rows, d_I);
+  if (s != HCS_OK) return s;
+  if (N == 0) return ok();
+  if (!q || !w || !tok_pos || !q_out || !w_out) return fail(HCS_ERR_INVALID_ARG, "null q, w, tok_pos, q_out or w_out");
+  if (out_fmt != HCS_FMT_BF16 && !q_scale_out) return fail(HCS_ERR_INVALID_ARG, "null q_scale_out");
+  if (!aligned(q, 16) || !aligned(q_out, 16)) return fail(HCS_ERR_INVALID_ARG, "q and q_out must be 16-byte aligned");
+  if (out_fmt == HCS_FMT_FP8IX && !aligned(q_scale_out, 4))
+    return fail(HCS_ERR_INVALID_ARG, "q_scale_out must be 4-byte aligned");
+  hcs::IxQArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.w = w;
+  a.tok_pos = tok_pos;
+  a.N = N;
+  a.H = H_I;
+  a.fmt = out_fmt;
+  a.w_scale = w_scale;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.d_rope = rope_cos ? d_rope : 0;
+  a.rope_rows = rope_rows;
+  a.q_out16 = static_cast<uint16_t*>(q_out);
+  a.q_out8 = static_cast<uint8_t*>(q_out);
+  a.q_scale8 = static_cast<uint8_t*>(q_scale_out);
+  a.q_scalef = static_cast<float*>(q_scale_out);
+  a.w_out = w_out;
+  return hip_status(hcs::launch_indexer_q(a, static_cast<hipStream_t>(stream)), "indexer_q_prep");
+}
+
+hcs_status hcs_indexer_k_store(const void* k_pre, int64_t k_stride, const int32_t* ent_seq,
+                               const int32_t* ent_idx, int n, int d_I, int m,
+                               const float* norm_weight, float eps, const float* rope_cos,
+                               const float* rope_sin, int d_rope, int rope_rows, hcs_paged keys,
+                               void* stream) {
+  if (n < 0) return fail(HCS_ERR_INVALID_ARG, "n must be >= 0");
+  if (d_I != 128) return fail(HCS_ERR_UNSUPPORTED, "d_I must be 128");
+  if (m < 1) return fail(HCS_ERR_INVALID_ARG, "m must be >= 1");
+  if (!(eps >= 0.f)) return fail(HCS_ERR_INVALID_ARG, "eps must be >= 0");
+  hcs_status s = check_rope(rope_cos, rope_sin, d_rope, rope_rows, d_I);
+  if (s != HCS_OK) return s;
+  if (n == 0) return ok();
+  if (!k_pre || !ent_seq || !ent_idx || !norm_weight)
+    return fail(HCS_ERR_INVALID_ARG, "null k_pre, ent_seq, ent_idx or norm_weight");
+  if (!aligned(k_pre, 16) || k_stride < d_I || k_stride % 8)
+    return fail(HCS_ERR_INVALID_ARG, "k_pre must be 16-byte aligned with k_stride >= d_I and a multiple of 8");
+  s = check_paged(keys, "keys", d_I, false, true);
+  if (s != HCS_OK) return s;
+  hcs::IxKArgs a{};
+  a.k = static_cast<const uint16_t*>(k_pre);
+  a.k_stride = k_stride;
+  a.ent_seq = ent_seq;
+  a.ent_idx = ent_idx;
+  a.n = n;
+  a.m = m;
+  a.fmt = keys.fmt;
+  a.norm_w = norm_weight;
+  a.eps = eps;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.d_rope = rope_cos ? d_rope : 0;
+  a.rope_rows = rope_rows;
+  a.keys = hcs::to_paged(keys);
+  return hip_status(hcs::launch_indexer_k(a, static_cast<hipStream_t>(stream)), "indexer_k_store");
+}
+
 // ------------------------------------------------------------------------------ indexer
 size_t hcs_index_topk_workspace_size(int N, int max_pos, int m, int topk) {
   if (N <= 0 || max_pos < 0 || m < 1 || topk < 1) return 0;
@@ -207,6 +291,8 @@ static hcs_status prep_index(const void* q, const uint8_t* q_scale, const float*
   if (s != HCS_OK) return s;
   if (keys.fmt == HCS_FMT_BF16 && d_I != 32 && d_I != 64 && d_I != 128)
     return fail(HCS_ERR_UNSUPPORTED, "bf16 indexer keys need d_I in {32, 64, 128}");
+  if (keys.fmt == HCS_FMT_FP8IX && (d_I != 128 || !q_scale || !aligned(q_scale, 4)))
+    return fail(HCS_ERR_UNSUPPORTED, "FP8IX indexer keys need d_I == 128 and a 4-byte aligned float32 q_scale");
   if (keys.fmt == HCS_FMT_MXFP4 && (d_I != 128 || !q_scale))
     return fail(HCS_ERR_UNSUPPORTED, "MXFP4 indexer keys need d_I == 128 and q_scale");
   if (!aligned(q, 16)) return fail(HCS_ERR_INVALID_ARG, "q must be 16-byte aligned");
@@ -246,7 +332,7 @@ static hcs_status prep_index(const void* q, const uint8_t* q_scale, const float*
 // The selection launch after the scores (entries per scoring block: 512 MXFP4, 256 bf16).
 static hcs_status run_topk(const hcs::IndexArgs& a, const hcs::TopkPlan& plan, int fmt, int topk,
                            int32_t* out_idx, float* out_score, void* ws, void* stream) {
-  const int blk_entries = fmt == HCS_FMT_MXFP4 ? 512 : 256;
+  const int blk_entries = fmt == HCS_FMT_MXFP4 || fmt == HCS_FMT_FP8IX ? 512 : 256;
   return hip_status(hcs::launch_topk(a, plan, topk, out_idx, out_score, static_cast<uint8_t*>(ws),
                                      blk_entries, static_cast<hipStream_t>(stream)),
                     "index_topk select");

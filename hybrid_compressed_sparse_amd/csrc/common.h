@@ -63,13 +63,27 @@ __device__ __forceinline__ float warp_sum(float v) {
   return v;
 }
 
-// UE8M0 exponent of an fp8_ds latent block: the smallest e with amax <= 448 * 2^e
-// (448 = 0.875 * 2^9), 0 for an all-zero block, clamped to [-127, 127].
-__device__ __forceinline__ int fp8ds_scale_exp(float amax) {
+// UE8M0 exponent of a block scaled into a format whose largest value is qf * 2^qe (qf in
+// [0.5, 1)): the smallest e with amax <= qf * 2^(qe + e), 0 for an all-zero block, clamped to
+// [-127, 127].
+__device__ __forceinline__ int ue8m0_scale_exp(float amax, float qf, int qe) {
   int E;
   const float f = __builtin_frexpf(amax, &E);
-  const int e = amax > 0.f ? E - 9 + (f > 0.875f ? 1 : 0) : 0;
+  const int e = amax > 0.f ? E - qe + (f > qf ? 1 : 0) : 0;
   return max(-127, min(127, e));
+}
+// e4m3: 448 = 0.875 * 2^9 (the fp8_ds latent blocks and the FP8 indexer rows)
+__device__ __forceinline__ int fp8ds_scale_exp(float amax) { return ue8m0_scale_exp(amax, 0.875f, 9); }
+// e2m1: 6 = 0.75 * 2^3 (MXFP4 blocks)
+__device__ __forceinline__ int mxfp4_scale_exp(float amax) { return ue8m0_scale_exp(amax, 0.75f, 3); }
+
+// Nearest e2m1 code of y (|y| <= 6), ties to the even code: the magnitude code counts the
+// thresholds |y| passes (halfway points; those that round up to an even code are inclusive).
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float a = fabsf(y);
+  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                     (a >= 3.5f) + (a > 5.f);
+  return c | (y < 0.f ? 8u : 0u);
 }
 
 // Order-preserving map of float32 to uint32: a < b  <=>  key(a) < key(b) (for non-NaN).

@@ -6,7 +6,7 @@
 // more entries than k, all of them are selected ("DeepSeek V4.1 attention" API page,
 // short-context rule).
 //
-// Scores: one workgroup scores 256 (bf16) or 512 (MXFP4) consecutive entries of one query.
+// Scores: one workgroup scores 256 (bf16) or 512 (MXFP4, FP8) consecutive entries of one query.
 // The query's heads are the MFMA M dimension. bf16: a wave's 64 entries are one page of the
 // cache, copied whole into LDS with async loads (as is the query), then read in MFMA operand
 // order. MXFP4: the same, two pages per wave, and the cache's 32-value blocks are the MFMA
@@ -540,6 +540,115 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexA
   }
 }
 
+// ---------------------------------------------------------------- FP8 scores (d_I = 128)
+// The MXFP4 kernel's structure for the 132-byte FP8 rows (128 e4m3 codes, one float32 scale):
+// 512 entries of one query per block, 4 waves x two pages. A page is [64 x 128 B codes][64 x
+// float32 scales]; a row's 16-byte chunk c is stored in LDS at c ^ ((r >> 1) & 7), so the 16
+// rows of an operand read fall on distinct banks. The codes go to
+// v_mfma_scale_f32_16x16x128_f8f6f4 as e4m3 with unit block scales (a lane's operand is 32
+// consecutive codes of one row); the float scales are applied after the product: the query's
+// per head with its weight (ReLU commutes with a positive factor), the key's per entry after the
+// sum over heads.
+template <int MT>
+__global__ __launch_bounds__(kScoreThreads) void index_score_fp8_kernel(IndexArgs a) {
+  constexpr int DI = 128;
+  constexpr int PAGE = kPageRows * (DI + 4);                     // 8448
+  constexpr int SCALES = kPageRows * DI;                         // scale region offset
+  constexpr int PPW = 2;                                         // pages per wave
+  __shared__ __attribute__((aligned(16))) uint8_t qc[64 * DI];
+  __shared__ __attribute__((aligned(16))) uint8_t kb[4][PPW][PAGE];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  if (a.cand_count && blockIdx.y == 0 && threadIdx.x == 0) a.cand_count[t] = 0u;
+  // query codes: wave w copies heads 16w .. 16w+15, 2 loads of 8 heads (heads >= H_I read zeros)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int h = 16 * wave + 8 * i + lane / 8, c = lane % 8;
+    const uint8_t* src = h < a.H_I ? a.q + ((int64_t)t * a.H_I + h) * DI + ((c ^ ((h >> 1) & 7)) << 4)
+                                   : g_ix_zero + lane * 16;
+    __builtin_amdgcn_global_load_lds((const void*)src,
+                                     (__attribute__((address_space(3))) void*)(qc + (16 * wave + 8 * i) * DI), 16, 0, 0);
+  }
+  const float* q_scalef = reinterpret_cast<const float*>(a.q_scale);
+  float wq[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hw = mt * 16 + 4 * g + i;
+      wq[mt][i] = hw < a.H_I ? a.w[(int64_t)t * a.H_I + hw] * q_scalef[(int64_t)t * a.H_I + hw] : 0.f;
+    }
+  }
+  int seq, nv;
+  query_of(a, t, seq, nv);
+  const int e_base = blockIdx.y * (4 * PPW * 64) + wave * (PPW * 64);
+  int my_pg = -1;
+  if (lane < PPW && e_base + 64 * lane < nv) {
+    const int pg = __ldg(a.keys.pt + (int64_t)seq * a.keys.pt_stride + (e_base >> 6) + lane);
+    my_pg = pg >= 0 && pg < a.keys.num_pages ? pg : -1;
+  }
+  int pgs[PPW];
+#pragma unroll
+  for (int p = 0; p < PPW; ++p) {
+    pgs[p] = __builtin_amdgcn_readlane(my_pg, p);
+    if (pgs[p] < 0) continue;
+    const uint8_t* page = a.keys.base + (int64_t)pgs[p] * PAGE;
+    uint8_t* dst = kb[wave][p];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {                                 // codes: 8 entries per load
+      const int r = 8 * i + lane / 8, c = lane % 8;
+      __builtin_amdgcn_global_load_lds((const void*)(page + r * DI + ((c ^ ((r >> 1) & 7)) << 4)),
+                                       (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+    }
+    if (lane < 16)                                                // scales: 256 bytes
+      __builtin_amdgcn_global_load_lds((const void*)(page + SCALES + lane * 16),
+                                       (__attribute__((address_space(3))) void*)(dst + SCALES), 16, 0, 0);
+  }
+  __syncthreads();                                                // every copy has landed
+  uint32_t tkeys[PPW * 4];
+#pragma unroll
+  for (int j = 0; j < PPW * 4; ++j) tkeys[j] = 0u;
+  if (e_base < nv) {
+    // a lane's operand: codes 32g .. 32g+31 of its row = chunks 2g and 2g+1
+    auto operand = [&](const uint8_t* base, int r) __attribute__((always_inline)) {
+      const int f = (r >> 1) & 7;
+      const i32x4 lo = *(const i32x4*)(base + r * DI + (((2 * g) ^ f) << 4));
+      const i32x4 hi = *(const i32x4*)(base + r * DI + (((2 * g + 1) ^ f) << 4));
+      return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    };
+    i32x8 qa[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) qa[mt] = operand(qc, mt * 16 + l16);
+#pragma unroll
+    for (int p = 0; p < PPW; ++p) {
+      const uint8_t* kp = kb[wave][p];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int r = nt * 16 + l16;
+        const i32x8 kbv = operand(kp, r);
+        float part = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kbv, acc, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part += wq[mt][i] * relu(acc[i]);
+        }
+        part = sum_xor16_32(part) * reinterpret_cast<const float*>(kp + SCALES)[r];
+        const int e = e_base + 64 * p + r;
+        const float sv = pgs[p] >= 0 ? part : kNegInf;
+        if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = sv;
+        tkeys[p * 4 + nt] = g == 0 && e < nv ? f32_order_key(sv) : 0u;
+      }
+    }
+  }
+  if (a.blk_thr) {
+    __shared__ uint32_t wbest[4 * kMaxKb + 1];
+    write_block_threshold<PPW * 4, 4, 4 * PPW * 64>(a, nv, tkeys, wbest, wbest + 4 * kMaxKb);
+  }
+}
+
 // ---------------------------------------------------------------- radix select
 constexpr int kDigitBits = 11;                 // radix digit: 2048 bins
 constexpr int kBins = 1 << kDigitBits;
@@ -971,6 +1080,16 @@ TopkPlan topk_plan(int N, int max_pos, int m, int topk) {
 hipError_t launch_index_scores(const IndexArgs& a, int fmt, hipStream_t stream) {
   if (a.N == 0 || a.nv_cap == 0) return hipSuccess;
   const int MT = (a.H_I + 15) / 16;
+  if (fmt == HCS_FMT_FP8IX) {
+    dim3 grid(a.N, (a.nv_cap + 511) / 512);
+    switch (MT) {
+      case 1: hipLaunchKernelGGL((index_score_fp8_kernel<1>), grid, dim3(kScoreThreads), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((index_score_fp8_kernel<2>), grid, dim3(kScoreThreads), 0, stream, a); break;
+      case 3: hipLaunchKernelGGL((index_score_fp8_kernel<3>), grid, dim3(kScoreThreads), 0, stream, a); break;
+      default: hipLaunchKernelGGL((index_score_fp8_kernel<4>), grid, dim3(kScoreThreads), 0, stream, a); break;
+    }
+    return hipGetLastError();
+  }
   if (fmt == HCS_FMT_MXFP4) {
     const int per_wg = 512;
     dim3 grid(a.N, (a.nv_cap + per_wg - 1) / per_wg);

@@ -79,6 +79,39 @@ struct InsertArgs {
 };
 hipError_t launch_qrope_insert(const InsertArgs& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- indexer query / key production
+struct IxQArgs {
+  const uint16_t* q;          // [N, H, 128] bf16
+  const float* w;             // [N, H]
+  const int32_t* tok_pos;     // [N]
+  int N, H, fmt;              // fmt: output format (HCS_FMT_BF16 / MXFP4 / FP8IX)
+  float w_scale;
+  const float* rope_cos;      // [rope_rows, d_rope / 2] or nullptr
+  const float* rope_sin;
+  int d_rope, rope_rows;
+  uint16_t* q_out16;          // bf16 output
+  uint8_t* q_out8;            // MXFP4 / FP8 codes
+  uint8_t* q_scale8;          // MXFP4 scale bytes [N, H, 4]
+  float* q_scalef;            // FP8 row scales [N, H]
+  float* w_out;               // [N, H]
+};
+hipError_t launch_indexer_q(const IxQArgs& a, hipStream_t stream);
+
+struct IxKArgs {
+  const uint16_t* k;          // [n, k_stride] bf16
+  int64_t k_stride;
+  const int32_t* ent_seq;
+  const int32_t* ent_idx;
+  int n, m, fmt;
+  const float* norm_w;        // [128]
+  float eps;
+  const float* rope_cos;
+  const float* rope_sin;
+  int d_rope, rope_rows;
+  Paged keys;
+};
+hipError_t launch_indexer_k(const IxKArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- indexer + top-k
 struct IndexArgs {
   const uint8_t* q;           // bf16 [N, H_I, d_I] or packed e2m1 [N, H_I, d_I/2]

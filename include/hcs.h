@@ -21,7 +21,11 @@
  *   hcs_sparse_mla_prefill_chunk  the same for a chunk of consecutive queries of one sequence;
  *   hcs_qnorm_rope_kv_insert  readies the new tokens' query heads (optional per-head RMSNorm,
  *                             RoPE) and writes their rotated KV rows into the sliding-window
- *                             cache.
+ *                             cache;
+ *   hcs_indexer_q_prep        the indexer queries of new tokens (RoPE, quantization to the key
+ *                             cache's format) and their head weights;
+ *   hcs_indexer_k_store       the indexer keys of new compressed entries (RMSNorm, RoPE,
+ *                             quantization), stored in the indexer key cache.
  *
  * Conventions shared by every call
  *   - Pointers are device pointers unless marked "host". The caller owns every buffer; the
@@ -51,6 +55,8 @@
  *     HCS_FMT_MXFP4 dim D  : [64][D/2] packed e2m1 | [64][D/32] UE8M0     (68 B per row, D=128)
  *                   element 2j is the low nibble of byte j, 2j+1 the high nibble; element c
  *                   is scaled by 2^(scale[c/32] - 127).
+ *     HCS_FMT_FP8IX dim 128: [64][128] e4m3 | [64] float32 scale          (132 B per row)
+ *                   element c = e4m3(code c) * scale (an indexer key format).
  *   e4m3 is OCP FP8 E4M3 (max 448, no infinities), e2m1 is OCP MX FP4, UE8M0 is 2^(b-127).
  */
 #ifndef HCS_H
@@ -74,7 +80,7 @@ typedef enum {
   HCS_ERR_HIP = 4                 /* a HIP launch error (text in hcs_last_error())            */
 } hcs_status;
 
-typedef enum { HCS_FMT_BF16 = 0, HCS_FMT_FP8DS = 1, HCS_FMT_MXFP4 = 2 } hcs_fmt;
+typedef enum { HCS_FMT_BF16 = 0, HCS_FMT_FP8DS = 1, HCS_FMT_MXFP4 = 2, HCS_FMT_FP8IX = 3 } hcs_fmt;
 typedef enum { HCS_IN_BF16 = 0, HCS_IN_F32 = 1 } hcs_in_dtype;
 
 typedef struct {
@@ -164,6 +170,8 @@ hcs_status hcs_compress_kv_full(const void* kv, const void* score, int in_dtype,
 /* q        keys.fmt == HCS_FMT_BF16 : [N, H_I, d_I] bf16, q_scale = NULL.                */
 /*          keys.fmt == HCS_FMT_MXFP4: [N, H_I, d_I/2] packed e2m1 (low nibble first) and */
 /*                                     q_scale [N, H_I, d_I/32] UE8M0 bytes.              */
+/*          keys.fmt == HCS_FMT_FP8IX: [N, H_I, 128] e4m3 codes and q_scale [N, H_I]      */
+/*                                     float32 (passed through the uint8_t pointer).       */
 /* w        [N, H_I] float32.                                                             */
 /* keys     indexer key cache, dim d_I, by entry index.                                   */
 /* q_seq    [N] int32 sequence of each query (page-table row); q_pos [N] int32 position.  */
@@ -174,7 +182,7 @@ hcs_status hcs_compress_kv_full(const void* kv, const void* score, int in_dtype,
 /* ws       workspace of at least hcs_index_topk_workspace_size(N, max_pos, m, topk) bytes, */
 /*          256-byte aligned (score scratch; no initial contents needed). Calls that overlap */
 /*          in time must not share it.                                                     */
-/* Constraints: H_I in 1..64, d_I in {32, 64, 128} (bf16) or d_I == 128 (mxfp4),           */
+/* Constraints: H_I in 1..64, d_I in {32, 64, 128} (bf16) or d_I == 128 (mxfp4, fp8ix),   */
 /* 1 <= topk <= 4096.                                                                     */
 size_t hcs_index_topk_workspace_size(int N, int max_pos, int m, int topk);
 hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
@@ -295,6 +303,47 @@ hcs_status hcs_qnorm_rope_kv_insert(void* q, int H, const void* kv, int64_t kv_s
                                     int q_norm, float eps, const float* rope_cos,
                                     const float* rope_sin, int d_rope, int rope_rows, hcs_paged swa,
                                     void* stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* Indexer queries of new tokens: "DeepSeek V4.1 attention", `DeepseekV4Indexer.forward_q` */
+/* (after the wq_b projection: RoPE and quantization of the query, and the head weights    */
+/* times softmax_scale * n_head^-1/2). For token t at position p = tok_pos[t] and head h:   */
+/*   the last d_rope dims of q[t,h,:] are rotated in GPT-J pairs at position p, as in       */
+/*   hcs_qnorm_rope_kv_insert (no norm), then written in out_fmt:                           */
+/*     HCS_FMT_BF16 : q_out [N, H_I, d_I] bf16 (q_out == q rewrites in place), q_scale_out  */
+/*                    NULL;                                                                 */
+/*     HCS_FMT_MXFP4: q_out [N, H_I, d_I/2] packed e2m1 (element 2j in the low nibble),     */
+/*                    q_scale_out [N, H_I, d_I/32] UE8M0 bytes: per 32 values the smallest  */
+/*                    2^e with amax <= 6 * 2^e, codes round-to-nearest-even of value / 2^e; */
+/*     HCS_FMT_FP8IX: q_out [N, H_I, d_I] e4m3 codes, q_scale_out [N, H_I] float32: per row */
+/*                    the smallest power of two s with amax <= 448 * s, codes RNE(value/s); */
+/*   w_out[t,h] = w[t,h] * w_scale (w_scale = softmax_scale * H_I^-1/2 on the pages).        */
+/* Values are computed in float32 from the bf16 input and rounded once.                   */
+/* q [N, H_I, d_I] bf16, w [N, H_I] float32, tok_pos [N] int32 (a negative position skips   */
+/* the token: nothing of it is written). rope_cos / rope_sin as hcs_qnorm_rope_kv_insert.   */
+/* Constraints: d_I == 128, 1 <= H_I <= 64, q and q_out 16-byte aligned.                   */
+hcs_status hcs_indexer_q_prep(const void* q, const float* w, const int32_t* tok_pos, int N, int H_I,
+                              int d_I, float w_scale, const float* rope_cos, const float* rope_sin,
+                              int d_rope, int rope_rows, int out_fmt, void* q_out,
+                              void* q_scale_out, float* w_out, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* Indexer keys of new compressed entries: "DeepSeek V4.1 attention",                    */
+/* `DeepseekV4Indexer._produce_k` (after the wk projection of the compressor's latent: the  */
+/* k_norm RMSNorm, RoPE at the group position, quantization into the paged key cache). For  */
+/* row r (entry i = ent_idx[r] of sequence ent_seq[r]):                                    */
+/*   k = k_pre[r,:] / sqrt(mean(k_pre[r,:]^2) + eps) * norm_weight, then its last d_rope    */
+/*   dims rotated in GPT-J pairs at position m * i, then stored as logical row i of        */
+/*   `keys` in its format (bf16; MXFP4 and FP8IX with hcs_indexer_q_prep's rules). A row   */
+/*   whose page is not resident (or past the page table), or with i < 0, is not written.    */
+/* k_pre [n, k_stride] bf16 (first d_I columns; k_stride >= d_I, a multiple of 8),          */
+/* ent_seq, ent_idx [n] int32, norm_weight [d_I] float32.                                   */
+/* Constraints: d_I == 128, m >= 1, eps >= 0; rows must name distinct entries.             */
+hcs_status hcs_indexer_k_store(const void* k_pre, int64_t k_stride, const int32_t* ent_seq,
+                               const int32_t* ent_idx, int n, int d_I, int m,
+                               const float* norm_weight, float eps, const float* rope_cos,
+                               const float* rope_sin, int d_rope, int rope_rows, hcs_paged keys,
+                               void* stream);
 
 #ifdef __cplusplus
 }

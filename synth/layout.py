@@ -14,6 +14,7 @@ on an aligned boundary:
                         = 37376 B per page = 584 B per row
   mxfp4  (dim D)      : [64 x D/2 packed e2m1, element 2j in the low nibble][64 x D/32 UE8M0]
                         = 68 B per row for D = 128
+  fp8ix  (dim 128)    : [64 x 128 e4m3 codes][64 x float32 scale] = 132 B per row
 
 The record widths follow the DeepSeek-V4 pages: 584 B per fp8_ds_mla token
 (448 fp8 latent dims + 64 bf16 rotary dims + block scales; "DeepSeek V4.1
@@ -35,6 +36,7 @@ PAGE_ROWS = 64
 FMT_BF16 = "bf16"
 FMT_FP8DS = "fp8ds"
 FMT_MXFP4 = "mxfp4"
+FMT_FP8IX = "fp8ix"
 
 FP8DS_DIM = 512
 FP8DS_LATENT = 448
@@ -43,6 +45,7 @@ FP8DS_BLOCK = 64
 FP8DS_NSCALE = FP8DS_LATENT // FP8DS_BLOCK  # 7
 FP8DS_SCALE_BYTES = 8                       # 7 scales + 1 pad byte
 MX_BLOCK = 32
+FP8IX_DIM = 128
 
 
 @dataclass
@@ -72,6 +75,19 @@ class Mxfp4Rows:
         return Mxfp4Rows(self.codes.to(device), self.scales.to(device))
 
 
+@dataclass
+class Fp8ixRows:
+    """Logical FP8 indexer key rows: 128 e4m3 codes and one float32 scale."""
+    codes: torch.Tensor   # uint8 [..., 128]
+    scale: torch.Tensor   # float32 [...]
+
+    def index(self, idx):
+        return Fp8ixRows(self.codes[idx], self.scale[idx])
+
+    def to(self, device):
+        return Fp8ixRows(self.codes.to(device), self.scale.to(device))
+
+
 def _regions(fmt: str, dim: int):
     """(name, bytes per row) for each region of a page, in page order."""
     if fmt == FMT_BF16:
@@ -84,6 +100,10 @@ def _regions(fmt: str, dim: int):
         if dim % MX_BLOCK:
             raise ValueError("mxfp4 rows need dim % 32 == 0")
         return [("codes", dim // 2), ("scales", dim // MX_BLOCK)]
+    if fmt == FMT_FP8IX:
+        if dim != FP8IX_DIM:
+            raise ValueError("fp8ix rows have 128 dims")
+        return [("codes", FP8IX_DIM), ("scale", 4)]
     raise ValueError(f"unknown format {fmt}")
 
 
@@ -108,6 +128,9 @@ def _row_fields(fmt: str, rows):
                 torch.cat([rows.scales, pad], dim=1)]
     if fmt == FMT_MXFP4:
         return [rows.codes.contiguous(), rows.scales.contiguous()]
+    if fmt == FMT_FP8IX:
+        n = rows.codes.shape[0]
+        return [rows.codes.contiguous(), rows.scale.contiguous().view(torch.uint8).reshape(n, 4)]
     raise ValueError(fmt)
 
 
@@ -149,4 +172,6 @@ def gather_rows(buf: torch.Tensor, fmt: str, dim: int, page_table_row: torch.Ten
     if fmt == FMT_FP8DS:
         return Fp8dsRows(fields[0].contiguous(), fields[1].contiguous().view(torch.bfloat16).reshape(n, FP8DS_ROPE),
                          fields[2][:, :FP8DS_NSCALE].contiguous())
+    if fmt == FMT_FP8IX:
+        return Fp8ixRows(fields[0].contiguous(), fields[1].contiguous().view(torch.float32).reshape(n))
     return Mxfp4Rows(fields[0].contiguous(), fields[1].contiguous())

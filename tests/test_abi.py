@@ -102,6 +102,27 @@ def test_insert_validation_errors_before_any_launch():
     assert f(None, 64, None, 0, None, None, 0, 512, 0, 0.0, None, None, 0, 0, _paged(), None) == 0
 
 
+@needs_lib
+def test_indexer_prep_validation_errors_before_any_launch():
+    L = hcs.lib()
+    q = L.hcs_indexer_q_prep
+    # q, w, tok_pos, N, H_I, d_I, w_scale, cos, sin, d_rope, rows, out_fmt, q_out, q_scale_out, w_out, stream
+    assert q(16, 16, 16, 4, 64, 64, 1.0, None, None, 0, 0, 0, 16, None, 16, None) == 2          # d_I
+    assert q(16, 16, 16, 4, 65, 128, 1.0, None, None, 0, 0, 0, 16, None, 16, None) == 2         # H_I
+    assert q(16, 16, 16, 4, 64, 128, 1.0, None, None, 0, 0, 1, 16, 16, 16, None) == 1           # fp8_ds out
+    assert q(16, 16, 16, 4, 64, 128, 1.0, None, None, 0, 0, 2, 16, None, 16, None) == 1         # no scales
+    assert q(16, 16, 16, 4, 64, 128, 1.0, 16, 16, 63, 10, 0, 16, None, 16, None) == 1           # odd d_rope
+    assert q(16, 16, 16, 0, 64, 128, 1.0, None, None, 0, 0, 0, None, None, None, None) == 0     # empty
+    k = L.hcs_indexer_k_store
+    # k, k_stride, ent_seq, ent_idx, n, d_I, m, norm_w, eps, cos, sin, d_rope, rows, keys, stream
+    assert k(16, 128, 16, 16, 4, 128, 0, 16, 1e-6, None, None, 0, 0, _paged(2, 128), None) == 1   # m
+    assert k(16, 120, 16, 16, 4, 128, 4, 16, 1e-6, None, None, 0, 0, _paged(2, 128), None) == 1   # stride
+    assert k(16, 128, 16, 16, 4, 128, 4, None, 1e-6, None, None, 0, 0, _paged(2, 128), None) == 1  # weight
+    assert k(16, 128, 16, 16, 4, 128, 4, 16, 1e-6, None, None, 0, 0, _paged(1, 512), None) == 1   # dim
+    assert k(16, 128, 16, 16, 4, 128, 4, 16, 1e-6, None, None, 0, 0, _paged(3, 64), None) == 1    # fp8ix dim
+    assert k(16, 128, 16, 16, 0, 128, 4, 16, 1e-6, None, None, 0, 0, _paged(3, 128), None) == 0   # empty
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(hcs, "_lib", None)
     monkeypatch.setattr(hcs, "LIB_PATH", "/nonexistent/libhcs.so")
