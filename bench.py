@@ -330,6 +330,103 @@ def bench_insert(wl, n_seq: int, per_seq: int, sets: int, reps: int) -> dict:
             "hbm_frac": gbs / HBM_PEAK_GBS}
 
 
+def bench_indexer_formats(wl, sets: int, reps: int) -> dict:
+    """The indexer (scores + top-k, hcs_index_topk) at `wl`'s shape with keys and queries made by
+    hcs_indexer_k_store / hcs_indexer_q_prep from the same seeded values in three formats: bf16,
+    MXFP4 (68-byte rows) and FP8 (132-byte rows). Reports each format's time per call (over
+    `sets` disjoint groups of sequences, so the keys stream from HBM) and the share of the bf16
+    selection that the quantized formats also select. The values are synthetic (normal latents
+    through RMSNorm and RoPE), not a trained model's keys."""
+    import torch
+
+    import hybrid_compressed_sparse_amd as hcs
+    from synth import layout as SL
+
+    dev = torch.device("cuda:0")
+    B, H, DI, m, k = wl.B, wl.H_I, wl.d_I, wl.m, wl.topk
+    n_vis = wl.ctx // m
+    S = sets
+    n_seq = B * S
+    dr = 64
+    g = torch.Generator(device=dev).manual_seed(777)
+    theta = 10000.0 ** (-2.0 * torch.arange(dr // 2, dtype=torch.float64) / dr)
+    ang = torch.arange(wl.ctx, dtype=torch.float64)[:, None] * theta[None, :]
+    cos, sin = torch.cos(ang).float().to(dev), torch.sin(ang).float().to(dev)
+    pt = torch.arange(n_seq * ((n_vis + 63) // 64), dtype=torch.int32, device=dev).view(n_seq, -1)
+    nw = torch.ones(DI, device=dev)
+    caches = {f: SL.new_pool(pt.numel(), f, DI, dev) for f in ("bf16", "mxfp4", "fp8ix")}
+    # keys: every entry of every sequence, written in slices of 64 sequences
+    for s0 in range(0, n_seq, 64):
+        ns = min(64, n_seq - s0)
+        k_pre = torch.randn(ns * n_vis, DI, generator=g, device=dev).to(torch.bfloat16)
+        ent_seq = torch.arange(s0, s0 + ns, dtype=torch.int32, device=dev).repeat_interleave(n_vis)
+        ent_idx = torch.arange(n_vis, dtype=torch.int32, device=dev).repeat(ns)
+        for f, pool in caches.items():
+            hcs.indexer_k_store(k_pre, ent_seq, ent_idx, m, hcs.paged(pool, pt, f, DI), nw, 1e-6, cos, sin)
+        del k_pre, ent_seq, ent_idx
+    q = torch.randn(S, B, H, DI, generator=g, device=dev).to(torch.bfloat16)
+    w = torch.rand(S, B, H, generator=g, device=dev)
+    q_pos = torch.full((B,), wl.ctx - 1, dtype=torch.int32, device=dev)
+    q_seq = [torch.arange(i * B, (i + 1) * B, dtype=torch.int32, device=dev) for i in range(S)]
+    w_scale = DI ** -0.5 * H ** -0.5
+    res = {}
+    sel = {}
+    for f, pool in caches.items():
+        qs, qsc, ws = [], [], []
+        for i in range(S):
+            if f == "bf16":
+                qo, sc = torch.empty(B, H, DI, dtype=torch.bfloat16, device=dev), None
+            elif f == "mxfp4":
+                qo = torch.empty(B, H, DI // 2, dtype=torch.uint8, device=dev)
+                sc = torch.empty(B, H, DI // 32, dtype=torch.uint8, device=dev)
+            else:
+                qo = torch.empty(B, H, DI, dtype=torch.uint8, device=dev)
+                sc = torch.empty(B, H, dtype=torch.float32, device=dev)
+            wo = torch.empty(B, H, device=dev)
+            hcs.indexer_q_prep(q[i], w[i], q_pos, f, qo, wo, sc, w_scale, cos, sin)
+            qs.append(qo)
+            qsc.append(sc)
+            ws.append(wo)
+        paged = hcs.paged(pool, pt, f, DI)
+        out = [torch.empty(B, k, dtype=torch.int32, device=dev) for _ in range(S)]
+        wsp = torch.empty(hcs.index_topk_workspace_size(B, wl.ctx - 1, m, k), dtype=torch.uint8, device=dev)
+
+        def run_all():
+            for i in range(S):
+                hcs.index_topk(qs[i], qsc[i], ws[i], paged, q_seq[i], q_pos, m, k, wl.ctx - 1, out[i], ws=wsp)
+
+        run_all()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            run_all()
+        gr.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f] = {"us_per_call": e0.elapsed_time(e1) * 1e3 / (reps * S),
+                  "key_bytes_per_row": SL.row_bytes(f, DI)}
+        sel[f] = torch.stack(out).cpu().numpy()
+        del gr, qs, qsc, ws, out, wsp
+    ref = sel["bf16"]
+    for f in ("mxfp4", "fp8ix"):
+        hit = []
+        for i in range(S):
+            for b in range(B):
+                hit.append(len(set(ref[i, b].tolist()) & set(sel[f][i, b].tolist())) / k)
+        res[f]["recall_vs_bf16"] = float(sum(hit) / len(hit))
+        res[f]["missed_vs_bf16"] = 1.0 - res[f]["recall_vs_bf16"]
+        res[f]["speedup_vs_bf16"] = res["bf16"]["us_per_call"] / res[f]["us_per_call"]
+    del caches
+    torch.cuda.empty_cache()
+    res["config"] = (f"{wl.name}: {B} queries per call, {n_vis} visible entries each, top-{k}, "
+                     f"H_I={H}, d_I={DI}, {S} disjoint sets of sequences; synthetic values")
+    return res
+
+
 def cpu_baseline(wl, seconds: float) -> dict:
     from threadpoolctl import threadpool_info
 
@@ -416,7 +513,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the HCA side measurement")
     ap.add_argument("--only", default=None, help="replay only this op's graph (for profiling)")
-    ap.add_argument("--side", default=None, choices=["compress_full", "insert_decode", "insert_prefill"],
+    ap.add_argument("--side", default=None, choices=["compress_full", "insert_decode", "insert_prefill",
+                                                     "indexer_formats"],
                     help="run only this side measurement of the decode workload (for profiling)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="instead of the path: copy MIB MiB device to device --steps times (the known-size "
@@ -449,6 +547,9 @@ def main():
         reps = max(1, args.steps // R)
         if args.side == "compress_full":
             res = bench_compress_full(wl, R, reps)
+        elif args.side == "indexer_formats":
+            res = bench_indexer_formats(wl, 16 if wl.ctx <= 65536 else 1, reps)
+            res["us_per_call"] = res["mxfp4"]["us_per_call"]
         elif args.side == "insert_decode":
             res = bench_insert(wl, wl.B, 1, R, reps)
         else:
@@ -539,6 +640,13 @@ def main():
         for k, v in result["qnorm_rope_kv_insert"].items():
             log(f"[bench] qnorm_rope_kv_insert {k}: {v['us_per_call']:.2f} us, {v['gb_s']:.0f} GB/s "
                 f"({100 * v['hbm_frac']:.1f}% of HBM)")
+        log("[bench] side measurement: indexer key formats (bf16 / MXFP4 / FP8), time and recall")
+        result["indexer_formats"] = {wl.name: bench_indexer_formats(wl, 16, max(1, reps // 2)),
+                                     C.CSA_DECODE_1M_FP8.name: bench_indexer_formats(C.CSA_DECODE_1M_FP8, 1, reps)}
+        for name, v in result["indexer_formats"].items():
+            log(f"[bench] indexer {name}: " + ", ".join(
+                f"{f} {v[f]['us_per_call']:.1f} us" + (f" (recall {100 * v[f]['recall_vs_bf16']:.2f}%)" if f != "bf16" else "")
+                for f in ("bf16", "mxfp4", "fp8ix")))
         hw = C.HCA_DECODE
         log(f"[bench] side measurement: {hw.name}")
         hb = Bench(hw, R, seed=2000)
