@@ -291,7 +291,8 @@ def bench_insert(wl, n_seq: int, per_seq: int, sets: int, reps: int) -> dict:
     for b in range(n_seq):
         pt[b, pg0: pg1 + 1] = torch.arange(b * n_pg, (b + 1) * n_pg, dtype=torch.int32)
     pool = SL.new_pool(n_seq * n_pg, "bf16", d, dev)
-    swa = hcs.paged(pool, pt.to(dev), "bf16", d)
+    ptd = pt.to(dev)
+    swa = hcs.paged(pool, ptd, "bf16", d)
     seq = torch.arange(n_seq, dtype=torch.int32).repeat_interleave(per_seq).to(dev)
     pos = torch.arange(p0, ctx, dtype=torch.int32).repeat(n_seq).to(dev)
     theta = 10000.0 ** (-2.0 * torch.arange(dr // 2, dtype=torch.float64) / dr)

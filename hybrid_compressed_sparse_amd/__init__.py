@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhcs.so")
 
-FMT = {"bf16": 0, "fp8ds": 1, "mxfp4": 2, "fp8ix": 3}
+FMT = {"bf16": 0, "fp8ds": 1, "mxfp4": 2, "fp8ix": 3, "mxfp8": 4, "nvfp4": 5}
 IN_DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 
 
@@ -107,11 +107,15 @@ def _stream() -> int:
 
 
 def paged(pool: torch.Tensor, page_table: torch.Tensor, fmt: str, dim: int) -> Paged:
-    """A paged cache: pool uint8 [num_pages, page_bytes], page_table int32 [num_seqs, pt_stride]."""
+    """A paged cache: pool uint8 [num_pages, page_bytes], page_table int32 [num_seqs, pt_stride].
+    The descriptor holds references to both tensors, so their memory stays allocated for as long
+    as the descriptor lives (it carries only their addresses to the library)."""
     if pool.dtype != torch.uint8 or page_table.dtype != torch.int32:
         raise TypeError("pool must be uint8 and page_table int32")
-    return Paged(_ptr(pool, name="pool"), _ptr(page_table, name="page_table"), page_table.shape[-1],
-                 pool.shape[0], FMT[fmt], dim)
+    p = Paged(_ptr(pool, name="pool"), _ptr(page_table, name="page_table"), page_table.shape[-1],
+              pool.shape[0], FMT[fmt], dim)
+    p._tensors = (pool, page_table)
+    return p
 
 
 def _as_paged(c) -> Paged:

@@ -36,11 +36,11 @@ hcs_status check_paged(const hcs_paged& p, const char* name, int want_dim, bool 
   if (!p.base || !p.page_table) return fail(HCS_ERR_INVALID_ARG, "%s: null base or page_table", name);
   if (p.pt_stride <= 0 || p.num_pages <= 0)
     return fail(HCS_ERR_INVALID_ARG, "%s: pt_stride and num_pages must be positive", name);
-  if (p.fmt != HCS_FMT_BF16 && p.fmt != HCS_FMT_FP8DS && p.fmt != HCS_FMT_MXFP4 && p.fmt != HCS_FMT_FP8IX)
+  if (p.fmt < HCS_FMT_BF16 || p.fmt > HCS_FMT_NVFP4)
     return fail(HCS_ERR_INVALID_ARG, "%s: unknown format %d", name, p.fmt);
   if (p.dim != want_dim) return fail(HCS_ERR_INVALID_ARG, "%s: dim %d, expected %d", name, p.dim, want_dim);
-  if (p.fmt == HCS_FMT_FP8DS && (!allow_fp8 || p.dim != 512))
-    return fail(HCS_ERR_UNSUPPORTED, "%s: fp8_ds rows need dim 512 and a KV cache", name);
+  if ((p.fmt == HCS_FMT_FP8DS || p.fmt == HCS_FMT_MXFP8 || p.fmt == HCS_FMT_NVFP4) && (!allow_fp8 || p.dim != 512))
+    return fail(HCS_ERR_UNSUPPORTED, "%s: fp8_ds / MXFP8 / NVFP4 rows need dim 512 and a KV cache", name);
   if ((p.fmt == HCS_FMT_MXFP4 || p.fmt == HCS_FMT_FP8IX) && !allow_mx)
     return fail(HCS_ERR_UNSUPPORTED, "%s: MXFP4 and FP8IX are indexer-key formats", name);
   if (p.fmt == HCS_FMT_FP8IX && p.dim != 128)
@@ -161,6 +161,8 @@ hcs_status hcs_qnorm_rope_kv_insert(void* q, int H, const void* kv, int64_t kv_s
       return fail(HCS_ERR_INVALID_ARG, "kv must be 16-byte aligned with kv_stride >= d and a multiple of 8");
     hcs_status s = check_paged(swa, "swa", d, true, false);
     if (s != HCS_OK) return s;
+    if (swa.fmt == HCS_FMT_NVFP4)
+      return fail(HCS_ERR_UNSUPPORTED, "swa: window rows are stored as bf16, fp8_ds or MXFP8");
     a.swa_base = static_cast<uint8_t*>(swa.base);
     a.swa_pt = swa.page_table;
     a.swa_pt_stride = swa.pt_stride;
@@ -425,7 +427,9 @@ static hcs_status check_attn(const void* q, const hcs_paged& swa, const hcs_page
   if (s != HCS_OK) return s;
   s = check_paged(comp, "comp", d, true, false);
   if (s != HCS_OK) return s;
-  if (swa.fmt != comp.fmt) return fail(HCS_ERR_UNSUPPORTED, "swa and comp must share a format");
+  if (!hcs::attn_formats_supported(d, swa.fmt, comp.fmt))
+    return fail(HCS_ERR_UNSUPPORTED, "swa / comp formats %d / %d: supported are bf16 / bf16, fp8_ds / fp8_ds, "
+                "MXFP8 / MXFP8 and MXFP8 / NVFP4", swa.fmt, comp.fmt);
   return HCS_OK;
 }
 
@@ -436,7 +440,7 @@ size_t hcs_sparse_mla_workspace_size(int N, int H, int d, int window, int m, int
                   hcs::attn_plan(N, H, d, window, m, topk, max_pos, HCS_FMT_FP8DS).ws_bytes);
 }
 
-static hcs_status run_attn(hcs::AttnArgs& a, int d, int fmt, int window, int m, int topk,
+static hcs_status run_attn(hcs::AttnArgs& a, int d, int fmt, int comp_fmt, int window, int m, int topk,
                            int max_pos, void* ws, size_t ws_bytes, void* stream) {
   if (window > 0 && (int64_t)a.swa.pt_stride * HCS_PAGE_ROWS <= (int64_t)max_pos)
     return fail(HCS_ERR_INVALID_ARG, "swa: pt_stride %d does not cover position %d", a.swa.pt_stride,
@@ -458,7 +462,7 @@ static hcs_status run_attn(hcs::AttnArgs& a, int d, int fmt, int window, int m, 
     a.ws_o = reinterpret_cast<uint16_t*>(w);
     a.ws_ml = reinterpret_cast<float*>(w + plan.ws_o_bytes);
   }
-  return hip_status(hcs::launch_sparse_mla(a, d, fmt, static_cast<hipStream_t>(stream)), "sparse_mla");
+  return hip_status(hcs::launch_sparse_mla(a, d, fmt, comp_fmt, static_cast<hipStream_t>(stream)), "sparse_mla");
 }
 
 hcs_status hcs_sparse_mla_decode(const void* q, hcs_paged swa, hcs_paged comp,
@@ -489,7 +493,7 @@ hcs_status hcs_sparse_mla_decode(const void* q, hcs_paged swa, hcs_paged comp,
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  return run_attn(a, d, swa.fmt, window, m, a.topk, max_pos, ws, ws_bytes, stream);
+  return run_attn(a, d, swa.fmt, comp.fmt, window, m, a.topk, max_pos, ws, ws_bytes, stream);
 }
 
 size_t hcs_sparse_mla_prefill_workspace_size(int Q, int H, int d, int window, int m, int topk, int P0) {
@@ -527,7 +531,7 @@ hcs_status hcs_sparse_mla_prefill_chunk(const void* q, hcs_paged swa, hcs_paged 
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  return run_attn(a, d, swa.fmt, window, m, a.topk, P0 + Q - 1, ws, ws_bytes, stream);
+  return run_attn(a, d, swa.fmt, comp.fmt, window, m, a.topk, P0 + Q - 1, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -21,8 +21,9 @@
 // All-heads kernel (bf16 rows): a workgroup is (query, split, 64 heads), so each gathered row is
 // read once for all heads of the query; bf16 rows go straight from the paged cache into LDS with
 // global_load_lds.
-// 16-head kernel (fp8_ds rows): a workgroup is (query, split, 16 heads); rows are dequantised
-// through registers on their way into LDS (e4m3 * 2^(scale-127) is exact in bf16). The head
+// 16-head kernel (quantized rows: fp8_ds, MXFP8, NVFP4): a workgroup is (query, split, 16
+// heads); rows are dequantised through registers on their way into LDS (every format's values
+// are exact in bf16). The head
 // groups of a query run on one XCD, so a row fetched by one of them is an L2 hit for the others.
 #include "kernels.h"
 
@@ -190,37 +191,30 @@ __device__ __forceinline__ int swz_dec(int r) {
   return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
 }
 
-// fp8_ds rows (448 e4m3 latent + 64 bf16 rope + per-64 UE8M0 scales, D = 512): one row per
-// wave-wide register load, written dequantised to bf16 into the LDS tile.
-struct Fp8Stage {
-  static constexpr int D = 512, RS = D * 2, PB = kFp8PageBytes;
+// Quantized 512-dim rows, one row per wave-wide register load, written dequantised to bf16 into
+// the LDS tile (every format's value is exact in bf16). For each format: `load` takes this
+// lane's 16-byte piece of row `slot` of `page` (nullptr: the row does not take part; it then
+// reads the zero row, so a wave's loads never branch and all stay in flight together) and the
+// scale bits the piece needs; `store` writes the piece's bf16 values into the tile row, its
+// 16-byte chunks swizzled by `sw` (the bf16 row is 1 KiB = 64 chunks).
+template <int FMT>
+struct RowFmt;
 
-  // Issue the load of this lane's 16-byte piece of the row with table entry `e` (wave-uniform,
-  // so the row address is computed once in scalar registers): lanes 0..27 take 16 latent
-  // codes, lanes 28..35 8 rope values, the others nothing useful. `se` receives the raw UE8M0
-  // byte of the lane's 64-value block. Both loads are unconditional (a row that does not take
-  // part reads the zero row), so a wave's loads of a block all stay in flight together.
-  __device__ static __forceinline__ void load(const uint8_t* swa_base, const uint8_t* comp_base,
-                                              uint32_t e, int lane, i32x4& v, int& se) {
-    e = (uint32_t)__builtin_amdgcn_readfirstlane((int)e);
-    const bool ok = e != kNoRow;
-    const uint32_t ridx = e & 0x7fffffffu;
-    const uint8_t* page = ((e >> 31) ? comp_base : swa_base) + (size_t)(ridx >> 6) * PB;
-    const int slot = (int)(ridx & 63);
+// fp8_ds: 448 e4m3 latent + 64 bf16 rope + a UE8M0 scale per 64 latent dims. Lanes 0..27 take
+// 16 latent codes, lanes 28..35 8 rope values, the others nothing.
+template <>
+struct RowFmt<HCS_FMT_FP8DS> {
+  static constexpr int PB = kFp8PageBytes;
+  __device__ static __forceinline__ void load(const uint8_t* page, int slot, int lane, i32x4& v, int& se) {
     const int off = lane < 28 ? kFp8PageCodes + slot * kFp8Latent + lane * 16
                               : (lane < 36 ? kFp8PageRope + slot * (kFp8Rope * 2) + (lane - 28) * 16
                                            : kFp8PageCodes + slot * kFp8Latent);
-    const uint8_t* src = ok ? page + off : g_zero_row + (lane & 31) * 16;
-    const uint8_t* ssrc = ok ? page + kFp8PageScales + slot * 8 + (min(lane, 27) >> 2) : g_zero_row;
+    const uint8_t* src = page ? page + off : g_zero_row + (lane & 31) * 16;
+    const uint8_t* ssrc = page ? page + kFp8PageScales + slot * 8 + (min(lane, 27) >> 2) : g_zero_row;
     v = *(const i32x4*)src;
     se = *ssrc;
   }
-
-  // Write this lane's piece of row `r` (tile-local) into the LDS tile, chunks swizzled by `sw`
-  // (the bf16 row is 1 KiB: latent chunks 0..55, rope chunks 56..63); se is the block's UE8M0.
-  __device__ static __forceinline__ void store(uint8_t* tile, int r, int sw, int lane,
-                                               const i32x4& v, int se) {
-    uint8_t* row = tile + r * RS;
+  __device__ static __forceinline__ void store(uint8_t* row, int sw, int lane, const i32x4& v, int se) {
     const float sc = __builtin_ldexpf(1.f, se - 127);
     if (lane < 28) {
       i32x4 lo4, hi4;
@@ -237,6 +231,95 @@ struct Fp8Stage {
     } else if (lane < 36) {
       *(i32x4*)(row + ((56 + lane - 28) ^ sw) * 16) = v;
     }
+  }
+};
+
+// MXFP8: 512 e4m3 + a UE8M0 scale per 32 dims. Lanes 0..31 take 16 codes (half a scale block).
+template <>
+struct RowFmt<HCS_FMT_MXFP8> {
+  static constexpr int PB = kMx8PageBytes;
+  __device__ static __forceinline__ void load(const uint8_t* page, int slot, int lane, i32x4& v, int& se) {
+    const uint8_t* src = page ? page + slot * 512 + (lane & 31) * 16 : g_zero_row + (lane & 31) * 16;
+    const uint8_t* ssrc = page ? page + kMx8Scales + slot * 16 + ((lane & 31) >> 1) : g_zero_row;
+    v = *(const i32x4*)src;
+    se = *ssrc;
+  }
+  __device__ static __forceinline__ void store(uint8_t* row, int sw, int lane, const i32x4& v, int se) {
+    if (lane >= 32) return;
+    const float sc = __builtin_ldexpf(1.f, se - 127);
+    i32x4 lo4, hi4;
+    lo4.x = e4m3x2_to_bf16x2<false>(v.x, sc);
+    lo4.y = e4m3x2_to_bf16x2<true>(v.x, sc);
+    lo4.z = e4m3x2_to_bf16x2<false>(v.y, sc);
+    lo4.w = e4m3x2_to_bf16x2<true>(v.y, sc);
+    hi4.x = e4m3x2_to_bf16x2<false>(v.z, sc);
+    hi4.y = e4m3x2_to_bf16x2<true>(v.z, sc);
+    hi4.z = e4m3x2_to_bf16x2<false>(v.w, sc);
+    hi4.w = e4m3x2_to_bf16x2<true>(v.w, sc);
+    *(i32x4*)(row + ((2 * lane) ^ sw) * 16) = lo4;
+    *(i32x4*)(row + ((2 * lane + 1) ^ sw) * 16) = hi4;
+  }
+};
+
+// NVFP4: 512 e2m1 (two per byte, element 2j low) + an e4m3 scale per 16 dims. Lanes 0..15 take
+// 32 values and their two scale bytes.
+template <>
+struct RowFmt<HCS_FMT_NVFP4> {
+  static constexpr int PB = kNv4PageBytes;
+  __device__ static __forceinline__ void load(const uint8_t* page, int slot, int lane, i32x4& v, int& se) {
+    const uint8_t* src = page ? page + slot * 256 + (lane & 15) * 16 : g_zero_row + (lane & 15) * 16;
+    const uint8_t* ssrc = page ? page + kNv4Scales + slot * 32 + 2 * (lane & 15) : g_zero_row;
+    v = *(const i32x4*)src;
+    se = *(const uint16_t*)ssrc;
+  }
+  __device__ static __forceinline__ void store(uint8_t* row, int sw, int lane, const i32x4& v, int se) {
+    if (lane >= 16) return;
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8(se, false);   // the two block scales
+    const uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {                  // chunk c: 8 values of word c
+      const float s = c < 2 ? sc.x : sc.y;
+      i32x4 o;
+      uint32_t ov[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t b = (w[c] >> (8 * k)) & 0xffu;
+        ov[k] = pack_bf16x2(e2m1_value(b & 0xfu) * s, e2m1_value(b >> 4) * s);
+      }
+      o.x = (int)ov[0];
+      o.y = (int)ov[1];
+      o.z = (int)ov[2];
+      o.w = (int)ov[3];
+      *(i32x4*)(row + ((4 * lane + c) ^ sw) * 16) = o;
+    }
+  }
+};
+
+// The rows of one attention call: window rows in format SF, compressed rows in format CF. The
+// row table entry's top bit says which cache a row comes from (wave-uniform); the source rides
+// along in bit 16 of the scale bits until the store.
+template <int SF, int CF>
+struct QuantStage {
+  static constexpr int D = 512, RS = D * 2;
+  __device__ static __forceinline__ void load(const uint8_t* swa_base, const uint8_t* comp_base,
+                                              uint32_t e, int lane, i32x4& v, int& se) {
+    e = (uint32_t)__builtin_amdgcn_readfirstlane((int)e);
+    const bool ok = e != kNoRow;
+    const bool comp = (e >> 31) != 0;
+    const uint32_t ridx = e & 0x7fffffffu;
+    const int slot = (int)(ridx & 63);
+    if (comp) {
+      RowFmt<CF>::load(ok ? comp_base + (size_t)(ridx >> 6) * RowFmt<CF>::PB : nullptr, slot, lane, v, se);
+      se |= 1 << 16;
+    } else {
+      RowFmt<SF>::load(ok ? swa_base + (size_t)(ridx >> 6) * RowFmt<SF>::PB : nullptr, slot, lane, v, se);
+    }
+  }
+  __device__ static __forceinline__ void store(uint8_t* tile, int r, int sw, int lane, const i32x4& v, int se) {
+    uint8_t* row = tile + r * RS;
+    if (se >> 16) RowFmt<CF>::store(row, sw, lane, v, se & 0xffff);
+    else RowFmt<SF>::store(row, sw, lane, v, se);
   }
 };
 
@@ -298,8 +381,8 @@ __device__ __forceinline__ float lse_of(float m, float l) {
 // each writes its rows' probabilities (bf16) to LDS, and each accumulates O^T for its own
 // quarter of the output columns over all 64 rows: 32 accumulator registers per lane, no
 // cross-wave merge of O.
+template <class S>
 __global__ __launch_bounds__(kThreads, 1) void mla_fp8_kernel(AttnArgs a) {
-  using S = Fp8Stage;
   constexpr int D = S::D, RS = S::RS, KS = D / 32;
   constexpr int CTW = D / 16 / 4;                 // 16-column output tiles per wave
   constexpr int BT = 64;                          // rows per block
@@ -878,15 +961,15 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   }
 }
 
-template <int D, int FMT>
+template <int D, int SF, int CF>
 hipError_t launch_impl(const AttnArgs& a, hipStream_t stream) {
   const int n8 = (a.N + 7) / 8;
   dim3 grid((unsigned)(n8 * 8 * a.nsplit * a.n_hg));
-  if constexpr (FMT == HCS_FMT_BF16) {
+  if constexpr (SF == HCS_FMT_BF16) {
     hipLaunchKernelGGL((mla_heads_kernel<D>), grid, dim3(kHeadsThreads), 0, stream, a);
   } else {
-    static_assert(D == Fp8Stage::D, "fp8_ds rows are 512 wide");
-    hipLaunchKernelGGL(mla_fp8_kernel, grid, dim3(kThreads), 0, stream, a);
+    static_assert(D == QuantStage<SF, CF>::D, "quantized rows are 512 wide");
+    hipLaunchKernelGGL((mla_fp8_kernel<QuantStage<SF, CF>>), grid, dim3(kThreads), 0, stream, a);
   }
   if (a.nsplit > 1)
     hipLaunchKernelGGL((mla_combine_kernel<D>), dim3(a.N, (a.H + 3) / 4), dim3(kThreads), 0, stream, a);
@@ -924,11 +1007,23 @@ AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos
   return p;
 }
 
-hipError_t launch_sparse_mla(const AttnArgs& a, int d, int fmt, hipStream_t stream) {
+bool attn_formats_supported(int d, int swa_fmt, int comp_fmt) {
+  if (swa_fmt == HCS_FMT_BF16) return comp_fmt == HCS_FMT_BF16 && (d == 512 || d == 128);
+  if (d != 512) return false;
+  return (swa_fmt == HCS_FMT_FP8DS && comp_fmt == HCS_FMT_FP8DS) ||
+         (swa_fmt == HCS_FMT_MXFP8 && (comp_fmt == HCS_FMT_MXFP8 || comp_fmt == HCS_FMT_NVFP4));
+}
+
+hipError_t launch_sparse_mla(const AttnArgs& a, int d, int swa_fmt, int comp_fmt, hipStream_t stream) {
   if (a.N == 0) return hipSuccess;
-  if (d == 512 && fmt == HCS_FMT_BF16) return launch_impl<512, HCS_FMT_BF16>(a, stream);
-  if (d == 512 && fmt == HCS_FMT_FP8DS) return launch_impl<512, HCS_FMT_FP8DS>(a, stream);
-  if (d == 128 && fmt == HCS_FMT_BF16) return launch_impl<128, HCS_FMT_BF16>(a, stream);
+  if (d == 512 && swa_fmt == HCS_FMT_BF16) return launch_impl<512, HCS_FMT_BF16, HCS_FMT_BF16>(a, stream);
+  if (d == 128 && swa_fmt == HCS_FMT_BF16) return launch_impl<128, HCS_FMT_BF16, HCS_FMT_BF16>(a, stream);
+  if (d == 512 && swa_fmt == HCS_FMT_FP8DS && comp_fmt == HCS_FMT_FP8DS)
+    return launch_impl<512, HCS_FMT_FP8DS, HCS_FMT_FP8DS>(a, stream);
+  if (d == 512 && swa_fmt == HCS_FMT_MXFP8 && comp_fmt == HCS_FMT_MXFP8)
+    return launch_impl<512, HCS_FMT_MXFP8, HCS_FMT_MXFP8>(a, stream);
+  if (d == 512 && swa_fmt == HCS_FMT_MXFP8 && comp_fmt == HCS_FMT_NVFP4)
+    return launch_impl<512, HCS_FMT_MXFP8, HCS_FMT_NVFP4>(a, stream);
   return hipErrorInvalidValue;
 }
 

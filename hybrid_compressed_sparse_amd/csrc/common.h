@@ -17,6 +17,12 @@ constexpr int kFp8PageRope = kPageRows * kFp8Latent;          // [64][64] bf16 a
 constexpr int kFp8PageScales = kFp8PageRope + kPageRows * kFp8Rope * 2;   // [64][8] u8 at 36864
 constexpr int kFp8PageBytes = kFp8PageScales + kPageRows * 8;             // 37376 = 64 * 584
 constexpr int kMxBlock = 32;
+// MXFP8 rows (512 e4m3 + one UE8M0 per 32): [64][512] codes | [64][16] scales
+constexpr int kMx8Scales = kPageRows * 512;                   // 32768
+constexpr int kMx8PageBytes = kMx8Scales + kPageRows * 16;     // 33792 = 64 * 528
+// NVFP4 rows (512 e2m1 + one e4m3 per 16): [64][256] packed codes | [64][32] scales
+constexpr int kNv4Scales = kPageRows * 256;                   // 16384
+constexpr int kNv4PageBytes = kNv4Scales + kPageRows * 32;     // 18432 = 64 * 288
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -76,6 +82,22 @@ __device__ __forceinline__ int ue8m0_scale_exp(float amax, float qf, int qe) {
 __device__ __forceinline__ int fp8ds_scale_exp(float amax) { return ue8m0_scale_exp(amax, 0.875f, 9); }
 // e2m1: 6 = 0.75 * 2^3 (MXFP4 blocks)
 __device__ __forceinline__ int mxfp4_scale_exp(float amax) { return ue8m0_scale_exp(amax, 0.75f, 3); }
+
+// Bytes of a 64-row page of a 512-dim KV cache in `fmt` (bf16 pages are 64 x 1 KiB).
+__host__ __device__ inline int64_t kv_page_bytes(int fmt) {
+  return fmt == HCS_FMT_FP8DS ? kFp8PageBytes
+         : fmt == HCS_FMT_MXFP8 ? kMx8PageBytes
+         : fmt == HCS_FMT_NVFP4 ? kNv4PageBytes
+                                : (int64_t)kPageRows * 512 * 2;
+}
+
+// e2m1 nibble (sign in bit 3) -> float
+__device__ __forceinline__ float e2m1_value(uint32_t n) {
+  const uint32_t mag = n & 7u;
+  const float f = mag < 2u ? 0.5f * (float)mag
+                           : __uint_as_float(((126u + (mag >> 1)) << 23) | ((mag & 1u) << 22));
+  return (n & 8u) ? -f : f;
+}
 
 // Nearest e2m1 code of y (|y| <= 6), ties to the even code: the magnitude code counts the
 // thresholds |y| passes (halfway points; those that round up to an even code are inclusive).

@@ -19,10 +19,11 @@ __device__ __forceinline__ float compress_load_in(const void* p, int64_t idx) {
 }
 
 // Stores channel c (of a completed entry kb of sequence b) of value C: the optional float32
-// copy, and the cache row (bf16, or fp8_ds: per 64-dim latent block a power-of-two scale from
+// copy, and the cache row: bf16; fp8_ds (per 64-dim latent block a power-of-two scale from
 // the wave's amax, e4m3 codes by the hardware's round-to-nearest-even conversion; the 64
-// rotary dims as bf16). `page` is the entry's page (nullptr: not resident). Called by every
-// lane of a wave, a wave holding one whole 64-channel block.
+// rotary dims as bf16); MXFP8 (the same per 32 dims, all 512 in e4m3); NVFP4 (per 16 dims an
+// e4m3 scale nearest amax / 6, e2m1 codes). `page` is the entry's page (nullptr: not resident).
+// Called by every lane of a wave, a wave holding 64 consecutive channels.
 __device__ __forceinline__ void compress_store(const CompressArgs& a, int b, int kb, int kb_first,
                                                const uint8_t* page, int c, bool act, float C) {
   const int d = a.d, slot = kb & 63;
@@ -43,6 +44,35 @@ __device__ __forceinline__ void compress_store(const CompressArgs& a, int b, int
                                                    slot * kFp8Rope * 2);
       rope[c - kFp8Latent] = (uint16_t)f32_to_bf16_bits(C);
     }
+  } else if (a.fmt == HCS_FMT_MXFP8) {            // 512 e4m3, one power-of-two scale per 32
+    float amax = fabsf(C);
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const int e = fp8ds_scale_exp(amax);
+    const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(C, -e), 0.f, 0, false);
+    if (page) {
+      uint8_t* pw = const_cast<uint8_t*>(page);
+      pw[slot * 512 + c] = (uint8_t)(packed & 0xff);
+      if ((c & 31) == 0) pw[kMx8Scales + slot * 16 + (c >> 5)] = (uint8_t)(e + 127);
+    }
+  } else if (a.fmt == HCS_FMT_NVFP4) {            // 512 e2m1, one e4m3 scale per 16
+    float amax = fabsf(C);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    // scale: e4m3 nearest amax / 6 (the quotient in float32); codes: nearest-even e2m1 of
+    // C / scale, saturated to 6; a zero scale stores zero codes
+    const int sc = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(amax / 6.f, 448.f), 0.f, 0, false) & 0xff;
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 sv2 = __builtin_amdgcn_cvt_pk_f32_fp8(sc, false);
+    const float sv = sv2.x;
+    const float y = sv > 0.f ? fminf(fmaxf(C / sv, -6.f), 6.f) : 0.f;
+    const uint32_t code = e2m1_code(y);
+    const uint32_t pair = code | (__shfl_xor(code, 1, 64) << 4);   // element 2j low, 2j+1 high
+    if (page) {
+      uint8_t* pw = const_cast<uint8_t*>(page);
+      if ((c & 1) == 0) pw[slot * 256 + (c >> 1)] = (uint8_t)pair;
+      if ((c & 15) == 0) pw[kNv4Scales + slot * 32 + (c >> 4)] = (uint8_t)sc;
+    }
   } else if (act && page) {
     uint16_t* row = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(page)) + (int64_t)slot * d;
     row[c] = (uint16_t)f32_to_bf16_bits(C);
@@ -53,7 +83,7 @@ __device__ __forceinline__ void compress_store(const CompressArgs& a, int b, int
 __device__ __forceinline__ const uint8_t* compress_entry_page(const CompressArgs& a, int b, int kb) {
   const int pg = (kb >> 6) < a.comp_pt_stride ? __ldg(a.comp_pt + (int64_t)b * a.comp_pt_stride + (kb >> 6)) : -1;
   if (pg < 0 || pg >= a.comp_num_pages) return nullptr;
-  const int64_t pb = a.fmt == HCS_FMT_FP8DS ? (int64_t)kFp8PageBytes : (int64_t)kPageRows * a.d * 2;
+  const int64_t pb = a.fmt == HCS_FMT_BF16 ? (int64_t)kPageRows * a.d * 2 : kv_page_bytes(a.fmt);
   return a.comp_base + (int64_t)pg * pb;
 }
 

@@ -5,8 +5,8 @@
 // `_fused_qnorm_rope_kv_insert`: for every new token, each query head is optionally brought to
 // unit RMS over its d dims (no weight) and its last d_rope dims are rotated in GPT-J pairs at
 // the token's position; the token's KV row is rotated the same way and written to the
-// sliding-window cache at logical row = the token's position, as a bf16 row or an fp8_ds
-// record. The query is rewritten in place; the KV input is not modified.
+// sliding-window cache at logical row = the token's position, as a bf16 row, an fp8_ds record or
+// an MXFP8 record. The query is rewritten in place; the KV input is not modified.
 //
 // Design: one wave per (token, group of G query heads) and one per (token, KV row), four waves
 // to a workgroup. A lane holds E = d / 64 consecutive dims of a row (16 B at d = 512), so a row
@@ -143,7 +143,27 @@ __device__ __forceinline__ void insert_kv_row(const InsertArgs& a, int t, int se
     store_bf16_row<E>(page + (int64_t)slot * d + lane * E, x);
     return;
   }
-  if constexpr (E == 8) {                        // fp8_ds record (d = 512)
+  if constexpr (E == 8) {
+    if (a.fmt == HCS_FMT_MXFP8) {                // MXFP8 record: 4 lanes = one 32-value block
+      uint8_t* page = a.swa_base + (int64_t)pg * kMx8PageBytes;
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(x[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      const int e = fp8ds_scale_exp(amax);
+      float y[E];
+#pragma unroll
+      for (int i = 0; i < E; ++i) y[i] = __builtin_ldexpf(x[i], -e);
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+      *reinterpret_cast<uint2*>(page + slot * 512 + lane * E) = make_uint2((uint32_t)lo, (uint32_t)hi);
+      if ((lane & 3) == 0) page[kMx8Scales + slot * 16 + (lane >> 2)] = (uint8_t)(e + 127);
+      return;
+    }
+    // fp8_ds record (d = 512)
     uint8_t* page = a.swa_base + (int64_t)pg * kFp8PageBytes;
     float amax = 0.f;
 #pragma unroll

@@ -57,6 +57,11 @@
  *                   is scaled by 2^(scale[c/32] - 127).
  *     HCS_FMT_FP8IX dim 128: [64][128] e4m3 | [64] float32 scale          (132 B per row)
  *                   element c = e4m3(code c) * scale (an indexer key format).
+ *     HCS_FMT_MXFP8 dim 512: [64][512] e4m3 | [64][16] UE8M0                (528 B per row)
+ *                   element c = e4m3(code c) * 2^(scale[c/32] - 127) (the V4.1 KV record).
+ *     HCS_FMT_NVFP4 dim 512: [64][256] packed e2m1 | [64][32] e4m3 scales   (288 B per row)
+ *                   element 2j in the low nibble of byte j; element c = e2m1(c) *
+ *                   e4m3(scale[c/16]) (the V4.1 compressed record).
  *   e4m3 is OCP FP8 E4M3 (max 448, no infinities), e2m1 is OCP MX FP4, UE8M0 is 2^(b-127).
  */
 #ifndef HCS_H
@@ -80,7 +85,14 @@ typedef enum {
   HCS_ERR_HIP = 4                 /* a HIP launch error (text in hcs_last_error())            */
 } hcs_status;
 
-typedef enum { HCS_FMT_BF16 = 0, HCS_FMT_FP8DS = 1, HCS_FMT_MXFP4 = 2, HCS_FMT_FP8IX = 3 } hcs_fmt;
+typedef enum {
+  HCS_FMT_BF16 = 0,
+  HCS_FMT_FP8DS = 1,
+  HCS_FMT_MXFP4 = 2,
+  HCS_FMT_FP8IX = 3,
+  HCS_FMT_MXFP8 = 4,
+  HCS_FMT_NVFP4 = 5
+} hcs_fmt;
 typedef enum { HCS_IN_BF16 = 0, HCS_IN_F32 = 1 } hcs_in_dtype;
 
 typedef struct {
@@ -118,10 +130,14 @@ int hcs_abi_version(void);
 /*            position start_pos[b]-1. It is read only when start_pos[b] % m != 0 and is  */
 /*            left describing the block of the last new token (reset if that block        */
 /*            completed). Sequences with no new tokens are untouched.                     */
-/* comp       compressed cache (HCS_FMT_BF16 with dim d, or HCS_FMT_FP8DS with d = 512):  */
-/*            every entry completed by this call is written at its entry index.           */
+/* comp       compressed cache (HCS_FMT_BF16 with dim d, or HCS_FMT_FP8DS, HCS_FMT_MXFP8  */
+/*            or HCS_FMT_NVFP4 with d = 512): every entry completed by this call is        */
+/*            written at its entry index.                                                  */
 /*            fp8_ds: per 64-dim latent block the scale is the smallest power of two 2^e  */
 /*            with amax <= 448 * 2^e, codes are round-to-nearest-even of value / 2^e.     */
+/*            MXFP8: the same rule per 32 dims over all 512. NVFP4: per 16 dims the scale */
+/*            is the e4m3 value nearest amax / 6 (the quotient in float32), codes the      */
+/*            nearest-even e2m1 of value / scale saturated to +-6 (0 if the scale is 0).   */
 /* dbg        optional [B, dbg_seq_stride] float32 copy of the completed entries before    */
 /*            rounding to the cache format: entry i of sequence b at                       */
 /*            dbg[b*dbg_seq_stride + (i - start_pos[b]/m) * d]. NULL to skip.             */
@@ -238,8 +254,9 @@ hcs_status hcs_index_topk_compress(const void* q, const uint8_t* q_scale, const 
 /* sink gets o = 0, lse = -inf.                                                           */
 /*                                                                                        */
 /* q        [N, H, d] bf16 (normalised and rotated upstream).                             */
-/* swa      raw KV rows by absolute position (fmt = comp.fmt, dim d).                     */
-/* comp     compressed entries by index (HCS_FMT_BF16, or HCS_FMT_FP8DS with d = 512).    */
+/* swa      raw KV rows by absolute position (dim d).                                      */
+/* comp     compressed entries by index. Format pairs (swa / comp): bf16 / bf16; with      */
+/*          d = 512 also fp8_ds / fp8_ds, MXFP8 / MXFP8 and MXFP8 / NVFP4 (the V4.1 records). */
 /* topk_idx [N, topk] int32 or NULL (HCA).                                                */
 /* q_seq, q_pos  [N] int32.     sink  [H] float32 or NULL (no sink).                      */
 /* max_pos  host: an upper bound of q_pos.     scale: softmax scale (d^-1/2 on the pages). */
@@ -280,9 +297,9 @@ hcs_status hcs_sparse_mla_prefill_chunk(const void* q, hcs_paged swa, hcs_paged 
 /*     (a, b) -> (a cos - b sin, a sin + b cos) with row p of the tables; written back in   */
 /*     place as bf16;                                                                     */
 /*   the KV row kv[t, 0..d-1] is rotated the same way (not normalised) and stored as       */
-/*     logical row p of sequence tok_seq[t] in `swa`, in its format (bf16, or fp8_ds with */
-/*     the compressor's scale and rounding rule; the rotary dims are the record's bf16    */
-/*     part when d_rope <= 64). kv itself is not modified.                                 */
+/*     logical row p of sequence tok_seq[t] in `swa`, in its format (bf16; fp8_ds or     */
+/*     MXFP8 with the compressor's scale and rounding rules; in fp8_ds the rotary dims are */
+/*     the record's bf16 part when d_rope <= 64). kv itself is not modified.               */
 /* Values are computed in float32 from the bf16 inputs and rounded once.                  */
 /*                                                                                        */
 /* q        [N, H, d] bf16, in/out; may be NULL when H == 0 (insert only).                */
@@ -292,7 +309,8 @@ hcs_status hcs_sparse_mla_prefill_chunk(const void* q, hcs_paged swa, hcs_paged 
 /* tok_pos  [N] int32 position of each token; a negative position skips the token.         */
 /* rope_cos, rope_sin [rope_rows, d_rope / 2] float32, or both NULL: no rotation. A        */
 /*          position at or past rope_rows reads the last row.                              */
-/* swa      sliding-window cache (dim d; HCS_FMT_BF16, or HCS_FMT_FP8DS with d = 512).     */
+/* swa      sliding-window cache (dim d; HCS_FMT_BF16, or HCS_FMT_FP8DS / HCS_FMT_MXFP8    */
+/*          with d = 512).                                                                 */
 /*          A row whose page is not resident (or past the page table) is not written.      */
 /* Tokens must have distinct (tok_seq, tok_pos) pairs: two writes of one row race.         */
 /* Constraints: d in {128, 512}, 0 <= H <= 128, eps >= 0, d_rope even in 2..d, q and kv    */

@@ -103,6 +103,32 @@ def decode_fp8ix(codes, scale) -> np.ndarray:
     return decode_e4m3(codes) * np.asarray(scale, dtype=np.float64)[..., None]
 
 
+MXFP8_DIM, MXFP8_BLOCK = 512, 32
+NVFP4_DIM, NVFP4_BLOCK = 512, 16
+
+
+def decode_mxfp8(codes, scales) -> np.ndarray:
+    """MXFP8 row (the "DeepSeek V4.1 attention" page's 528-byte KV record: 512 e4m3 codes and one
+    UE8M0 scale per 32 values) -> float64 [..., 512]: value c = e4m3(code c) * 2**(scale[c // 32] - 127)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    lead = codes.shape[:-1]
+    v = decode_e4m3(codes).reshape(*lead, MXFP8_DIM // MXFP8_BLOCK, MXFP8_BLOCK)
+    return (v * decode_ue8m0(scales)[..., None]).reshape(*lead, MXFP8_DIM)
+
+
+def decode_nvfp4(packed, scales) -> np.ndarray:
+    """NVFP4 row (the same page's 288-byte compressed record: 256 bytes of e2m1 pairs, element 2j
+    in the low nibble of byte j, and one e4m3 scale per 16 values) -> float64 [..., 512]:
+    value c = e2m1(code c) * e4m3(scale[c // 16])."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    lead = packed.shape[:-1]
+    nib = np.empty(lead + (2 * packed.shape[-1],), dtype=np.uint8)
+    nib[..., 0::2] = packed & 0xF
+    nib[..., 1::2] = packed >> 4
+    v = decode_e2m1(nib).reshape(*lead, NVFP4_DIM // NVFP4_BLOCK, NVFP4_BLOCK)
+    return (v * decode_e4m3(scales)[..., None]).reshape(*lead, NVFP4_DIM)
+
+
 # ----------------------------------------------------------------- rounding (reference rules)
 
 
@@ -198,3 +224,35 @@ def quantize_fp8ix(x32):
     e = ue8m0_exponent(np.abs(x).max(axis=-1), 448.0)
     codes = round_e4m3(x / np.ldexp(1.0, e)[..., None])
     return codes, np.ldexp(1.0, e).astype(np.float32)
+
+
+def quantize_mxfp8(x32):
+    """MXFP8 row of float32 values [..., 512]: per 32 values the power-of-two scale 2**e with e the
+    smallest integer such that amax <= 448 * 2**e, codes = RNE_e4m3(x / 2**e).
+    Returns (codes uint8 [..., 512], scales uint8 [..., 16])."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    lead = x.shape[:-1]
+    blk = x.reshape(*lead, MXFP8_DIM // MXFP8_BLOCK, MXFP8_BLOCK)
+    e = ue8m0_exponent(np.abs(blk).max(axis=-1), 448.0)
+    codes = round_e4m3(blk / np.ldexp(1.0, e)[..., None]).reshape(*lead, MXFP8_DIM)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def quantize_nvfp4(x32):
+    """NVFP4 row of float32 values [..., 512]: per 16 values the scale s = RNE_e4m3(amax / 6)
+    (the quotient taken in float32), codes = nearest-even e2m1 of x / s in float32, saturated to
+    +-6 (a scale rounded down can leave amax / s slightly above 6); a block whose scale rounds to
+    0 stores zero codes. Returns (packed uint8 [..., 256], scales uint8 [..., 32])."""
+    x = np.asarray(x32, dtype=np.float32)
+    lead = x.shape[:-1]
+    blk = x.reshape(*lead, NVFP4_DIM // NVFP4_BLOCK, NVFP4_BLOCK)
+    amax = np.abs(blk).max(axis=-1)
+    sq = (amax / np.float32(6.0)).astype(np.float32)
+    sc = round_e4m3(np.minimum(sq.astype(np.float64), 448.0))
+    sv = decode_e4m3(sc).astype(np.float32)
+    safe = np.where(sv > 0, sv, np.float32(1.0)).astype(np.float32)
+    y = (blk / safe[..., None]).astype(np.float32).astype(np.float64)
+    y = np.where(sv[..., None] > 0, np.clip(y, -6.0, 6.0), 0.0)
+    nib = round_e2m1(y).reshape(*lead, NVFP4_DIM)
+    packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    return packed, sc

@@ -32,6 +32,10 @@ def decode_rows(fmt: str, rows) -> np.ndarray:
                               _np(rows.scales))
     if fmt == "mxfp4":
         return F.decode_mxfp4(_np(rows.codes), _np(rows.scales))
+    if fmt == "mxfp8":
+        return F.decode_mxfp8(_np(rows.codes), _np(rows.scales))
+    if fmt == "nvfp4":
+        return F.decode_nvfp4(_np(rows.codes), _np(rows.scales))
     raise ValueError(fmt)
 
 
@@ -50,6 +54,12 @@ def store_entry(C: np.ndarray, fmt: str):
     if fmt == "fp8ds":
         rec = F.quantize_fp8ds(C.astype(np.float32))
         return F.decode_fp8ds(*rec), rec
+    if fmt == "mxfp8":
+        rec = F.quantize_mxfp8(C.astype(np.float32))
+        return F.decode_mxfp8(*rec), rec
+    if fmt == "nvfp4":
+        rec = F.quantize_nvfp4(C.astype(np.float32))
+        return F.decode_nvfp4(*rec), rec
     raise ValueError(fmt)
 
 
@@ -66,7 +76,7 @@ def compress_step(sc):
         X = decode_input(sc.c_x[lo:hi])
         S = decode_input(sc.c_s[lo:hi])
         C, _ = M.compress(X, S, m, ape)
-        stored, _ = store_entry(C, sc.wl.kv_fmt) if C.shape[0] else (C, None)
+        stored, _ = store_entry(C, sc.wl.cfmt) if C.shape[0] else (C, None)
         out.append((starts[b] // m, C, stored))
     return out
 
@@ -76,7 +86,7 @@ def comp_values(sc, b: int, ids: np.ndarray, produced) -> np.ndarray:
     ids = np.asarray(ids, dtype=np.int64)
     if ids.size == 0:
         return np.zeros((0, sc.wl.d))
-    vals = decode_rows(sc.wl.kv_fmt, sc.comp.logical(b, torch.from_numpy(ids)))
+    vals = decode_rows(sc.wl.cfmt, sc.comp.logical(b, torch.from_numpy(ids)))
     first, _, stored = produced[b]
     hit = (ids >= first) & (ids < first + stored.shape[0])
     if hit.any():

@@ -24,13 +24,19 @@ class Workload:
     H_I: int = 0         # indexer heads
     d_I: int = 0         # indexer dim
     topk: int = 0
-    kv_fmt: str = "bf16"     # "bf16" or "fp8ds" (block-scaled e4m3, 584 B per row)
+    kv_fmt: str = "bf16"     # window rows (and compressed rows unless comp_fmt is set): "bf16",
+                             # "fp8ds" (584 B per row) or "mxfp8" (528 B per row)
+    comp_fmt: str = ""       # compressed rows when they differ: "nvfp4" (288 B per row)
     ix_fmt: str = "bf16"     # "bf16" or "mxfp4" (e2m1 + UE8M0 per 32)
     in_dtype: str = "f32"    # compressor input dtype ("bf16" or "f32")
     P0: int = 0              # prefill: absolute position of the first new token
     Q: int = 0               # prefill: new tokens (= queries) in the chunk
     n_query: int = 0         # tiny: decode queries at the end of the one sequence
     q_std: float = 0.0       # std of q (and indexer q); 0 -> 1/sqrt(dim)
+
+    @property
+    def cfmt(self) -> str:
+        return self.comp_fmt or self.kv_fmt
 
     @property
     def n_queries(self) -> int:

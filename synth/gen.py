@@ -79,6 +79,32 @@ def make_mxfp4(x: torch.Tensor) -> L.Mxfp4Rows:
     return L.Mxfp4Rows(codes=packed.contiguous(), scales=(e + 127).to(torch.uint8))
 
 
+def make_mxfp8(x: torch.Tensor) -> L.Mxfp4Rows:
+    """MXFP8 rows (512 e4m3 + one power-of-two scale per 32) from float values [..., 512]."""
+    lead = x.shape[:-1]
+    blk = x.float().reshape(*lead, L.V41_DIM // L.MXFP8_BLOCK, L.MXFP8_BLOCK)
+    e = _pow2_exponent_for(blk.abs().amax(-1), 448.0)
+    y = blk * torch.pow(2.0, -e.float())[..., None]
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(*lead, L.V41_DIM)
+    return L.Mxfp4Rows(codes=codes, scales=(e + 127).to(torch.uint8))
+
+
+def make_nvfp4(x: torch.Tensor) -> L.Mxfp4Rows:
+    """NVFP4 rows (512 e2m1, element 2j in the low nibble, + one e4m3 scale per 16) from float
+    values [..., 512]: the scale is torch's e4m3 cast of amax / 6, the codes the nearest e2m1
+    magnitude of x / scale (clamped to 6)."""
+    lead = x.shape[:-1]
+    blk = x.float().reshape(*lead, L.V41_DIM // L.NVFP4_BLOCK, L.NVFP4_BLOCK)
+    s8 = (blk.abs().amax(-1) / 6.0).clamp(max=448.0).to(torch.float8_e4m3fn)
+    sv = s8.float()
+    y = torch.where(sv[..., None] > 0, blk / sv.clamp(min=1e-30)[..., None], torch.zeros_like(blk)).clamp(-6, 6)
+    mags = _E2M1_MAG.to(x.device)
+    code = (y.abs()[..., None] - mags).abs().argmin(-1).to(torch.uint8)
+    code = (code | ((y < 0).to(torch.uint8) << 3)).reshape(*lead, L.V41_DIM)
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return L.Mxfp4Rows(codes=packed.contiguous(), scales=s8.view(torch.uint8))
+
+
 def encode_rows(x: torch.Tensor, fmt: str):
     if fmt == L.FMT_BF16:
         return x.to(torch.bfloat16)
@@ -86,6 +112,10 @@ def encode_rows(x: torch.Tensor, fmt: str):
         return make_fp8ds(x)
     if fmt == L.FMT_MXFP4:
         return make_mxfp4(x)
+    if fmt == L.FMT_MXFP8:
+        return make_mxfp8(x)
+    if fmt == L.FMT_NVFP4:
+        return make_nvfp4(x)
     raise ValueError(fmt)
 
 
@@ -276,7 +306,7 @@ def build(wl: Workload, seed: int = 0, device="cpu", ctx_per_seq: Optional[list]
     # compressed entries 0 .. n_vis(max pos)-1 (entries the stream completes are rewritten by it)
     n_ent = [(c // m) for c in ctx]
     cpt_w = (max(n_ent) + L.PAGE_ROWS - 1) // L.PAGE_ROWS if max(n_ent) else 1
-    comp = build_paged(seed, "comp", wl.kv_fmt, d, [(0, n) for n in n_ent], cpt_w, device, kv_std)
+    comp = build_paged(seed, "comp", wl.cfmt, d, [(0, n) for n in n_ent], cpt_w, device, kv_std)
 
     ix_q = ix_w = ix = None
     if wl.indexer:

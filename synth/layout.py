@@ -15,6 +15,8 @@ on an aligned boundary:
   mxfp4  (dim D)      : [64 x D/2 packed e2m1, element 2j in the low nibble][64 x D/32 UE8M0]
                         = 68 B per row for D = 128
   fp8ix  (dim 128)    : [64 x 128 e4m3 codes][64 x float32 scale] = 132 B per row
+  mxfp8  (dim 512)    : [64 x 512 e4m3 codes][64 x 16 UE8M0] = 528 B per row
+  nvfp4  (dim 512)    : [64 x 256 packed e2m1][64 x 32 e4m3 scales] = 288 B per row
 
 The record widths follow the DeepSeek-V4 pages: 584 B per fp8_ds_mla token
 (448 fp8 latent dims + 64 bf16 rotary dims + block scales; "DeepSeek V4.1
@@ -37,6 +39,8 @@ FMT_BF16 = "bf16"
 FMT_FP8DS = "fp8ds"
 FMT_MXFP4 = "mxfp4"
 FMT_FP8IX = "fp8ix"
+FMT_MXFP8 = "mxfp8"
+FMT_NVFP4 = "nvfp4"
 
 FP8DS_DIM = 512
 FP8DS_LATENT = 448
@@ -46,6 +50,9 @@ FP8DS_NSCALE = FP8DS_LATENT // FP8DS_BLOCK  # 7
 FP8DS_SCALE_BYTES = 8                       # 7 scales + 1 pad byte
 MX_BLOCK = 32
 FP8IX_DIM = 128
+V41_DIM = 512            # MXFP8 and NVFP4 records hold 512 dims
+MXFP8_BLOCK = 32
+NVFP4_BLOCK = 16
 
 
 @dataclass
@@ -104,6 +111,12 @@ def _regions(fmt: str, dim: int):
         if dim != FP8IX_DIM:
             raise ValueError("fp8ix rows have 128 dims")
         return [("codes", FP8IX_DIM), ("scale", 4)]
+    if fmt in (FMT_MXFP8, FMT_NVFP4):
+        if dim != V41_DIM:
+            raise ValueError(f"{fmt} rows have 512 dims")
+        if fmt == FMT_MXFP8:
+            return [("codes", V41_DIM), ("scales", V41_DIM // MXFP8_BLOCK)]
+        return [("codes", V41_DIM // 2), ("scales", V41_DIM // NVFP4_BLOCK)]
     raise ValueError(f"unknown format {fmt}")
 
 
@@ -126,7 +139,7 @@ def _row_fields(fmt: str, rows):
         return [rows.codes.contiguous(),
                 rows.rope.contiguous().view(torch.uint8).reshape(n, -1),
                 torch.cat([rows.scales, pad], dim=1)]
-    if fmt == FMT_MXFP4:
+    if fmt in (FMT_MXFP4, FMT_MXFP8, FMT_NVFP4):
         return [rows.codes.contiguous(), rows.scales.contiguous()]
     if fmt == FMT_FP8IX:
         n = rows.codes.shape[0]

@@ -24,7 +24,7 @@ from hybrid_compressed_sparse_amd.step import PathStep, StepShape
 from oracle import formats as OF
 from oracle import pipeline as OP
 
-ATTN_TOL = {"bf16": 2e-2, "fp8ds": 6e-2}
+ATTN_TOL = {"bf16": 2e-2, "fp8ds": 6e-2, "mxfp8": 6e-2}
 REL_FRO = 1e-2
 
 
@@ -124,8 +124,12 @@ def check_entries(sc, step, dbg, produced, b: int):
     # stored rows in the cache
     from synth import layout as L
     ids = torch.arange(first, first + n, device=sc.comp.pool.device)
-    stored = L.gather_rows(sc.comp.pool, sc.wl.kv_fmt, sc.wl.d, sc.comp.page_table[b], ids)
-    if sc.wl.kv_fmt == "bf16":
+    fmt = sc.wl.cfmt
+    stored = L.gather_rows(sc.comp.pool, fmt, sc.wl.d, sc.comp.page_table[b], ids)
+    if fmt in ("mxfp8", "nvfp4"):
+        check_v41_rows(fmt, stored, C)
+        return
+    if fmt == "bf16":
         # the stored value is the GPU's float32 entry rounded to nearest bf16: within half a bf16
         # ulp of it, and the float32 entry is within 1e-4 of the row's scale of the exact one
         gv = OF.decode_bf16(stored.view(torch.int16).cpu().numpy().view(np.uint16))
@@ -143,6 +147,38 @@ def check_entries(sc, step, dbg, produced, b: int):
         step_ = np.repeat(OF.decode_ue8m0(rec[2]), 64, axis=-1) * 32.0
         assert np.all(np.abs(gv[:, :448] - rv[:, :448]) <= step_)
         assert np.all(np.abs(gv[:, 448:] - rv[:, 448:]) <= np.abs(rv[:, 448:]) * 2.0 ** -7 + 1e-30)
+
+
+def _nibbles(packed: np.ndarray) -> np.ndarray:
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = packed & 0xF
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def check_v41_rows(fmt: str, stored, C: np.ndarray, min_same: float = 0.999):
+    """Stored MXFP8 / NVFP4 rows against the oracle's encoding of the float64 rows C: codes and
+    scales agree at least min_same (both sides decide them on float32 values computed in
+    different orders), and every decoded value is within one step of the oracle's."""
+    codes = stored.codes.cpu().numpy()
+    scales = stored.scales.cpu().numpy()
+    gv = OP.decode_rows(fmt, stored)
+    if fmt == "mxfp8":
+        rc, rs = OF.quantize_mxfp8(C.astype(np.float32))
+        rv = OF.decode_mxfp8(rc, rs)
+        assert (codes == rc).mean() >= min_same, f"only {(codes == rc).mean():.4f} of e4m3 codes agree"
+        assert (scales == rs).mean() >= min_same
+        step_ = np.repeat(OF.decode_ue8m0(rs), 32, axis=-1) * 32.0
+        assert np.all(np.abs(gv - rv) <= step_)
+    else:
+        rc, rs = OF.quantize_nvfp4(C.astype(np.float32))
+        rv = OF.decode_nvfp4(rc, rs)
+        same = (_nibbles(codes) == _nibbles(rc)).mean()
+        assert same >= min_same, f"only {same:.4f} of e2m1 codes agree"
+        assert (scales == rs).mean() >= min_same
+        # one e2m1 step (at most 2) of the larger of the two scales
+        sv = np.maximum(OF.decode_e4m3(rs), OF.decode_e4m3(scales))
+        assert np.all(np.abs(gv - rv) <= np.repeat(sv, 16, axis=-1) * 2.0 + 1e-30)
 
 
 def check_topk(gpu_idx: np.ndarray, gpu_score: np.ndarray, ref_idx: np.ndarray, ref_scores: np.ndarray,

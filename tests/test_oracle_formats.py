@@ -221,3 +221,51 @@ def test_fp8ix_quantizer_round_trip():
     reps = F.decode_e4m3(rng.integers(0, 126, (4, 128))) * 2.0 ** 5
     c2, s2 = F.quantize_fp8ix(reps.astype(np.float32))
     assert np.array_equal(F.decode_fp8ix(c2, s2), reps)
+
+
+def test_mxfp8_record_round_trip_and_scale_rule():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((20, 512)) * np.exp(rng.uniform(-5, 5, (20, 16))).repeat(32, axis=1)).astype(np.float32)
+    codes, sc = F.quantize_mxfp8(x)
+    assert codes.shape == (20, 512) and sc.shape == (20, 16)
+    blk = np.abs(x.astype(np.float64)).reshape(20, 16, 32).max(axis=-1)
+    s = np.ldexp(1.0, sc.astype(np.int64) - 127)
+    assert np.all(blk <= 448.0 * s) and np.all(blk > 224.0 * s)      # smallest power of two
+    dec = F.decode_mxfp8(codes, sc)
+    tiny = np.repeat(s, 32, axis=1) * 2.0 ** -9                      # e4m3 subnormal step
+    assert np.all(np.abs(dec - x) <= np.abs(x) * 2.0 ** -4 + tiny / 2)
+    # a row of representable values comes back exactly; the block of dim c is c // 32
+    reps = F.decode_e4m3(rng.integers(1, 126, (2, 512))) * 2.0 ** -3
+    c2, s2 = F.quantize_mxfp8(reps.astype(np.float32))
+    assert np.array_equal(F.decode_mxfp8(c2, s2), reps)
+    one = np.zeros((1, 512), dtype=np.float32)
+    one[0, 40] = 448.0 * 4                                           # block 1 only
+    c3, s3 = F.quantize_mxfp8(one)
+    assert s3[0, 1] == 129 and s3[0, 0] == 127 and c3[0, 40] == 0x7E
+
+
+def test_nvfp4_record_scale_and_codes():
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((30, 512)) * np.exp(rng.uniform(-4, 4, (30, 32))).repeat(16, axis=1)).astype(np.float32)
+    packed, sc = F.quantize_nvfp4(x)
+    assert packed.shape == (30, 256) and sc.shape == (30, 32)
+    amax = np.abs(x.astype(np.float64)).reshape(30, 32, 16).max(axis=-1)
+    sv = F.decode_e4m3(sc)
+    # the scale is the e4m3 value nearest amax / 6 (brute force over the positive codes)
+    pos = F.decode_e4m3(np.arange(0, 127))
+    for i in range(30):
+        for j in range(32):
+            d = np.abs(pos - amax[i, j] / 6.0)
+            assert abs(sv[i, j] - amax[i, j] / 6.0) <= d.min() * (1 + 1e-6) + 1e-30
+    dec = F.decode_nvfp4(packed, sc)
+    # each value within half an e2m1 step of x / s (in units of s), or saturated at 6 s
+    y = x.astype(np.float64) / np.repeat(sv, 16, axis=1)
+    half = np.where(np.abs(y) < 2, 0.25, np.where(np.abs(y) < 4, 0.5, 1.0)) * np.repeat(sv, 16, axis=1)
+    sat = np.abs(y) > 6
+    assert np.all((np.abs(dec - x) <= half * (1 + 1e-6)) | sat)
+    assert np.all(np.abs(dec[sat]) == 6 * np.repeat(sv, 16, axis=1)[sat])
+    # low nibble first, scale per 16 values
+    one = np.zeros((1, 512), dtype=np.float32)
+    one[0, 16], one[0, 17] = 6.0, 3.0                                # block 1: amax 6 -> scale 1
+    p1, s1 = F.quantize_nvfp4(one)
+    assert s1[0, 1] == 0x38 and p1[0, 8] == (0x7 | (0x5 << 4)) and s1[0, 0] == 0
