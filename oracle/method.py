@@ -26,6 +26,11 @@ Sources (DeepSeek-V4 pages):
     n_head**-0.5; `_produce_k`: k_norm (an RMSNorm) of the projected latent at
     group-boundary tokens, RoPE at the group position, quantization into the key cache;
     `_indexer_k_cache_head_dim`: 68-byte MXFP4 and 132-byte FP8 rows).
+  * candidate filtering -- same page, `DeepseekV4Indexer` docstring: the indexer of the
+    candidate source layer also publishes its top blocks of consecutive compressed
+    positions, and later indexers mask their scores to those blocks before their own
+    top-k (readings: a block's score is the max of its entries; entries outside the
+    blocks do not take part, and fewer than k taking part are all selected, -1 padded).
   * query preparation and SWA insert -- same page, "Default stream" (the fused
     q-norm / RoPE / KV insert: per-head RMSNorm of the query heads, GPT-J RoPE on
     the last 64 dims of every query head and of the KV row, the KV row stored in
@@ -220,6 +225,33 @@ def topk(scores, k: int) -> np.ndarray:
     out = np.full(k, -1, dtype=np.int64)
     take = min(k, n)
     out[:take] = order[:take]
+    return out
+
+
+def candidate_blocks(scores, block: int, n_cand: int) -> np.ndarray:
+    """Two-level candidate filtering, source side: the n_cand blocks of `block` consecutive
+    entries with the largest block score (the max of the block's entries), ordered by
+    (-score, block id); -1 pads when there are fewer blocks."""
+    scores = np.asarray(scores, dtype=np.float64)
+    nb = -(-scores.shape[0] // block)
+    bmax = np.array([scores[b * block:(b + 1) * block].max() for b in range(nb)])
+    return topk(bmax, n_cand)
+
+
+def topk_in_blocks(scores, blocks, block: int, k: int) -> np.ndarray:
+    """Two-level candidate filtering, consumer side: the top-k (ties to the smaller id) among
+    only the entries of the listed blocks (ids >= 0, each block once); every listed entry is
+    selected when there are no more than k of them, and -1 pads."""
+    scores = np.asarray(scores, dtype=np.float64)
+    n = scores.shape[0]
+    ids = np.array(sorted(e for b in blocks if b >= 0 for e in range(b * block, min(n, (b + 1) * block))),
+                   dtype=np.int64)
+    out = np.full(k, -1, dtype=np.int64)
+    if ids.size == 0:
+        return out
+    order = np.lexsort((ids, -scores[ids]))
+    sel = ids[order[:k]]
+    out[: sel.size] = sel
     return out
 
 

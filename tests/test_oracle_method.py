@@ -275,6 +275,42 @@ def test_indexer_query_and_key_relative_position_and_scales():
     assert np.array_equal(k7[: dI - dr], k0[: dI - dr])
 
 
+def test_candidate_blocks_reduce_to_topk_and_block_max():
+    rng = np.random.default_rng(40)
+    sc = rng.standard_normal(103)
+    # blocks of one entry: the candidate blocks are the plain top-k
+    assert np.array_equal(M.candidate_blocks(sc, 1, 17), M.topk(sc, 17))
+    # brute force over blocks of 8 (the last one ragged): sort by (-max, id)
+    bm = [(-sc[b * 8:(b + 1) * 8].max(), b) for b in range(13)]
+    want = [b for _, b in sorted(bm)][:5]
+    assert list(M.candidate_blocks(sc, 8, 5)) == want
+    # fewer blocks than asked: all of them, -1 padded
+    got = M.candidate_blocks(sc, 64, 4)
+    assert sorted(got[:2].tolist()) == [0, 1] and list(got[2:]) == [-1, -1]
+    # equal block maxima: the smaller block id first
+    eq = np.zeros(32)
+    assert list(M.candidate_blocks(eq, 8, 2)) == [0, 1]
+
+
+def test_topk_in_blocks_restricts_the_selection():
+    rng = np.random.default_rng(41)
+    sc = rng.standard_normal(300)
+    # every block listed: the plain top-k
+    assert np.array_equal(M.topk_in_blocks(sc, list(range(10)), 32, 40), M.topk(sc, 40))
+    blocks = [7, 2, -1, 9]
+    got = M.topk_in_blocks(sc, blocks, 32, 20)
+    inside = np.array([e for b in (2, 7, 9) for e in range(32 * b, min(300, 32 * b + 32))])
+    assert set(got.tolist()) <= set(inside.tolist())
+    assert sc[inside].max() == sc[got].max()
+    assert np.all(sc[np.setdiff1d(inside, got)] <= sc[got].min())
+    # fewer entries than k (block 9 holds 12 visible entries): all selected, -1 padded
+    got = M.topk_in_blocks(sc, [9], 32, 20)
+    assert sorted(got[:12].tolist()) == list(range(288, 300)) and np.all(got[12:] == -1)
+    # the two levels together with blocks of one entry: the consumer's top-k is the source's
+    src = M.candidate_blocks(sc, 1, 40)
+    assert set(M.topk_in_blocks(sc, src, 1, 40).tolist()) == set(M.topk(sc, 40).tolist())
+
+
 def test_compressor_partial_block_makes_no_entry():
     C, _ = M.compress(np.ones((7, 3)), np.zeros((7, 3)), 4)
     assert C.shape == (1, 3)
