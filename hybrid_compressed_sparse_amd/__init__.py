@@ -80,6 +80,11 @@ def lib() -> ctypes.CDLL:
         L.hcs_indexer_q_prep.argtypes = [vp, vp, vp, i32, i32, i32, f32, vp, vp, i32, i32, i32, vp, vp, vp, vp]
         L.hcs_indexer_k_store.restype = i32
         L.hcs_indexer_k_store.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, f32, vp, vp, i32, i32, Paged, vp]
+        L.hcs_index_topk_cand_workspace_size.restype = sz
+        L.hcs_index_topk_cand_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.hcs_index_topk_cand.restype = i32
+        L.hcs_index_topk_cand.argtypes = [vp, vp, vp, Paged, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                          vp, vp, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -260,6 +265,26 @@ def index_topk(q, q_scale: Optional[torch.Tensor], w: torch.Tensor, keys, q_seq:
         N, H_I, d_I, m, topk, max_pos, _ptr(out_idx, torch.int32, "out_idx"),
         _ptr(out_score, torch.float32, "out_score"), _ptr(ws, name="ws"),
         0 if ws is None else ws.numel() * ws.element_size(), _stream()), "index_topk")
+
+
+def index_topk_cand(q, q_scale: Optional[torch.Tensor], w: torch.Tensor, keys, q_seq: torch.Tensor,
+                    q_pos: torch.Tensor, m: int, topk: int, max_pos: int, cand_block: int, n_cand: int,
+                    out_idx: torch.Tensor, cand_in: Optional[torch.Tensor] = None,
+                    cand_out: Optional[torch.Tensor] = None, out_score: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None) -> None:
+    """hcs_index_topk_cand: index_topk plus two-level candidate filtering; give cand_out
+    (int32 [N, n_cand], source) or cand_in (int32 [N, n_cand], consumer)."""
+    N, H_I = w.shape
+    d_I = keys.dim
+    if ws is None:
+        n = lib().hcs_index_topk_cand_workspace_size(N, max_pos, m, topk, cand_block, n_cand)
+        ws = _workspace(n, w.device)
+    _check(lib().hcs_index_topk_cand(
+        _ptr(q, name="q"), _ptr(q_scale, name="q_scale"), _ptr(w, torch.float32, "w"), _as_paged(keys),
+        _ptr(q_seq, torch.int32, "q_seq"), _ptr(q_pos, torch.int32, "q_pos"), N, H_I, d_I, m, topk, max_pos,
+        cand_block, n_cand, _ptr(cand_in, torch.int32, "cand_in"), _ptr(cand_out, torch.int32, "cand_out"),
+        _ptr(out_idx, torch.int32, "out_idx"), _ptr(out_score, torch.float32, "out_score"), _ptr(ws, name="ws"),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream()), "index_topk_cand")
 
 
 def index_topk_chunk(q, q_scale: Optional[torch.Tensor], w: torch.Tensor, keys, seq: int, P0: int,

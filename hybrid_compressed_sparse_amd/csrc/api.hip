@@ -363,6 +363,51 @@ hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w,
                    out_idx, out_score, ws, ws_bytes, stream);
 }
 
+size_t hcs_index_topk_cand_workspace_size(int N, int max_pos, int m, int topk, int cand_block, int n_cand) {
+  if (N <= 0 || max_pos < 0 || m < 1 || topk < 1 || cand_block < 1 || n_cand < 1) return 0;
+  const hcs::TopkPlan plan = hcs::topk_plan(N, max_pos, m, topk);
+  return hcs::cand_plan(plan, N, (max_pos + 1) / m, cand_block, n_cand).ws_bytes;
+}
+
+hcs_status hcs_index_topk_cand(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
+                               const int32_t* q_seq, const int32_t* q_pos, int N, int H_I, int d_I, int m,
+                               int topk, int max_pos, int cand_block, int n_cand, const int32_t* cand_in,
+                               int32_t* cand_out, int32_t* out_idx, float* out_score, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if ((cand_in == nullptr) == (cand_out == nullptr))
+    return fail(HCS_ERR_INVALID_ARG, "exactly one of cand_in (consumer) and cand_out (source) is given");
+  if (cand_block < 1) return fail(HCS_ERR_INVALID_ARG, "cand_block must be >= 1");
+  if (n_cand < 1 || n_cand > 4096) return fail(HCS_ERR_UNSUPPORTED, "n_cand must be in 1..4096");
+  if (m >= 1 && max_pos >= 0 && cand_out && ((int64_t)(max_pos + 1) / m + cand_block - 1) / cand_block > 32768)
+    return fail(HCS_ERR_UNSUPPORTED, "a query may see more than 32768 blocks of cand_block entries");
+  if ((int64_t)n_cand * cand_block > INT32_MAX) return fail(HCS_ERR_INVALID_ARG, "n_cand * cand_block overflows");
+  if (N > 0 && (!q_seq || !q_pos)) return fail(HCS_ERR_INVALID_ARG, "null q_seq or q_pos");
+  hcs::IndexArgs a;
+  hcs::TopkPlan plan;
+  hcs_status s = prep_index(q, q_scale, w, keys, q_seq, q_pos, 0, 0, N, H_I, d_I, m, topk, max_pos, out_idx,
+                            ws, ws_bytes, a, plan);
+  if (s != HCS_OK || N == 0) return s == HCS_OK ? ok() : s;
+  const hcs::CandPlan cp = hcs::cand_plan(plan, N, a.nv_cap, cand_block, n_cand);
+  if (ws_bytes < cp.ws_bytes)
+    return fail(HCS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", cp.ws_bytes, ws_bytes);
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cand_in) {                                     // consumer: no block thresholds, own counters
+    a.blk_thr = nullptr;
+    a.cand_count = reinterpret_cast<unsigned*>(w8 + cp.cnt_off);
+    hipError_t e = hcs::launch_index_scores(a, keys.fmt, st);
+    if (e == hipSuccess)
+      e = hcs::launch_topk_in_blocks(a, cp, w8, cand_in, n_cand, cand_block, topk, out_idx, out_score, st);
+    return hip_status(e, "index_topk_cand (consumer)");
+  }
+  hipError_t e = hcs::launch_index_scores(a, keys.fmt, st);
+  if (e != hipSuccess) return hip_status(e, "index_topk_cand scores");
+  s = run_topk(a, plan, keys.fmt, topk, out_idx, out_score, ws, stream);
+  if (s != HCS_OK) return s;
+  return hip_status(hcs::launch_candidate_blocks(a, cp, w8, cand_block, n_cand, cand_out, st),
+                    "index_topk_cand (source)");
+}
+
 hcs_status hcs_index_topk_chunk(const void* q, const uint8_t* q_scale, const float* w,
                                 hcs_paged keys, int seq, int P0, int Q, int H_I, int d_I, int m,
                                 int topk, int32_t* out_idx, float* out_score, void* ws,

@@ -65,6 +65,7 @@ __device__ __forceinline__ void query_of(const IndexArgs& a, int t, int& seq, in
     pos = a.p0 + t;
   }
   nv = min((pos + 1) / a.m, a.nv_cap);
+  if (a.nv_div > 0) nv = (nv + a.nv_div - 1) / a.nv_div;
 }
 
 // ---------------------------------------------------------------- block thresholds
@@ -1012,7 +1013,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(IndexArgs a, 
                                                                    const unsigned* ccount,
                                                                    int64_t cstride,
                                                                    int32_t* out_idx,
-                                                                   float* out_score) {
+                                                                   float* out_score,
+                                                                   int cand_mode) {
   __shared__ SelShared sh;
   __shared__ uint32_t kl[kSingleMax];
   const int t = blockIdx.x;
@@ -1020,7 +1022,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(IndexArgs a, 
   query_of(a, t, seq, nv);
   int32_t* oi = out_idx + (int64_t)t * k;
   float* os = out_score ? out_score + (int64_t)t * k : nullptr;
-  if (nv <= k) {
+  if (cand_mode) {                                   // the listed blocks' entries are the candidates
+    const int n = (int)ccount[t];
+    if (n <= k) {
+      const uint32_t* ck = ckey + (int64_t)t * cstride;
+      const int32_t* ci = cid + (int64_t)t * cstride;
+      for (int j = threadIdx.x; j < k; j += kTopkThreads) {
+        oi[j] = j < n ? ci[j] : -1;
+        if (os) os[j] = j < n ? order_key_f32(ck[j]) : 0.f;
+      }
+      return;
+    }
+  } else if (nv <= k) {
     const float* sc = a.scores + (int64_t)t * a.score_stride;
     for (int j = threadIdx.x; j < k; j += kTopkThreads) {
       oi[j] = j < nv ? j : -1;
@@ -1030,7 +1043,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(IndexArgs a, 
   }
   const uint32_t* ck = ckey + (int64_t)t * cstride;
   const int32_t* ci = cid + (int64_t)t * cstride;
-  const int n = (int)ccount[t];                      // >= k: every key >= the k-th is a candidate
+  const int n = (int)ccount[t];                      // > k: every key >= the k-th is a candidate
   auto emit = [&](unsigned slot, int id, uint32_t key) {
     if (slot < (unsigned)k) {
       oi[slot] = id;
@@ -1052,6 +1065,60 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(IndexArgs a, 
   block_topk<kTopkThreads>(
       sh, n, k, [&](int i, uint32_t& key) { key = ck[i]; return true; }, [&](int i) { return ci[i]; },
       emit);
+}
+
+// ---------------------------------------------------------------- two-level candidate filtering
+// Consumer: the entries of a query's listed blocks (block j = entries j*cb .. j*cb+cb-1, the
+// visible ones) become its selection candidates (key, id), appended through the per-query
+// counter that the scoring launch zeroed. Block = (query, listed block).
+__global__ __launch_bounds__(kScoreThreads) void cand_gather_kernel(IndexArgs a, const int32_t* cand, int n_cand,
+                                                                    int cb, uint32_t* ckey, int32_t* cid,
+                                                                    unsigned* ccount, int64_t cstride) {
+  __shared__ unsigned wcnt[kScoreThreads / 64], wbase[kScoreThreads / 64];
+  const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int seq, nv;
+  query_of(a, t, seq, nv);
+  const int blk = cand[(int64_t)t * n_cand + blockIdx.y];
+  if (blk < 0 || (int64_t)blk * cb >= nv) return;
+  const int lo = blk * cb, hi = (int)min((int64_t)nv, (int64_t)lo + cb);
+  const float* sc = a.scores + (int64_t)t * a.score_stride;
+  for (int c0 = lo; c0 < hi; c0 += kScoreThreads) {
+    const int i = c0 + threadIdx.x;
+    const bool in = i < hi;
+    const uint64_t bm = __ballot(in);
+    if (lane == 0) wcnt[wave] = (unsigned)__popcll(bm);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const unsigned tot = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+      unsigned run = atomicAdd(ccount + t, tot);
+      for (int w = 0; w < kScoreThreads / 64; ++w) {
+        wbase[w] = run;
+        run += wcnt[w];
+      }
+    }
+    __syncthreads();
+    if (in) {
+      const unsigned sl = wbase[wave] + (unsigned)__popcll(bm & ((1ull << lane) - 1));
+      ckey[(int64_t)t * cstride + sl] = f32_order_key(sc[i]);
+      cid[(int64_t)t * cstride + sl] = i;
+    }
+    __syncthreads();                                 // wcnt / wbase are reused
+  }
+}
+
+// Source: block b's score is the max of its visible entries' scores. Thread = (query, block).
+__global__ __launch_bounds__(kScoreThreads) void block_max_kernel(IndexArgs a, int cb, float* bmax,
+                                                                  int64_t bstride) {
+  const int t = blockIdx.x;
+  int seq, nv;
+  query_of(a, t, seq, nv);
+  const int b = blockIdx.y * kScoreThreads + threadIdx.x;
+  if ((int64_t)b * cb >= nv) return;
+  const float* sc = a.scores + (int64_t)t * a.score_stride + (int64_t)b * cb;
+  const int n = (int)min((int64_t)cb, (int64_t)nv - (int64_t)b * cb);
+  float m = kNegInf;
+  for (int i = 0; i < n; ++i) m = fmaxf(m, sc[i]);
+  bmax[(int64_t)t * bstride + b] = m;
 }
 
 }  // namespace
@@ -1163,7 +1230,57 @@ hipError_t launch_topk(const IndexArgs& a, const TopkPlan& plan, int topk, int32
   hipLaunchKernelGGL(topk_filter_kernel, dim3(a.N, (a.nv_cap + kFilterChunk - 1) / kFilterChunk),
                      dim3(kScoreThreads), 0, stream, a, blk_entries, ckey, cid, cnt, cstride);
   hipLaunchKernelGGL(topk_select_kernel, dim3(a.N), dim3(kTopkThreads), 0, stream, a, topk, ckey, cid,
-                     cnt, cstride, out_idx, out_score);
+                     cnt, cstride, out_idx, out_score, 0);
+  return hipGetLastError();
+}
+
+CandPlan cand_plan(const TopkPlan& base, int N, int nv_cap, int cand_block, int n_cand) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  CandPlan c{};
+  c.cstride = ((int64_t)n_cand * cand_block + 63) / 64 * 64;
+  c.bstride = std::max<int64_t>(64, ((int64_t)nv_cap / cand_block + 1 + 63) / 64 * 64);
+  size_t off = base.ws_bytes;
+  c.ckey_off = off;
+  off += up((size_t)N * c.cstride * sizeof(uint32_t));
+  c.cid_off = off;
+  off += up((size_t)N * c.cstride * sizeof(int32_t));
+  c.cnt_off = off;
+  off += up((size_t)N * sizeof(unsigned));
+  c.bmax_off = off;
+  off += up((size_t)N * c.bstride * sizeof(float));
+  c.ws_bytes = off;
+  return c;
+}
+
+hipError_t launch_topk_in_blocks(const IndexArgs& a, const CandPlan& cp, uint8_t* ws, const int32_t* cand_in,
+                                 int n_cand, int cand_block, int topk, int32_t* out_idx, float* out_score,
+                                 hipStream_t stream) {
+  if (a.N == 0) return hipSuccess;
+  uint32_t* ckey = reinterpret_cast<uint32_t*>(ws + cp.ckey_off);
+  int32_t* cid = reinterpret_cast<int32_t*>(ws + cp.cid_off);
+  unsigned* cnt = reinterpret_cast<unsigned*>(ws + cp.cnt_off);
+  hipLaunchKernelGGL(cand_gather_kernel, dim3(a.N, n_cand), dim3(kScoreThreads), 0, stream, a, cand_in, n_cand,
+                     cand_block, ckey, cid, cnt, cp.cstride);
+  hipLaunchKernelGGL(topk_select_kernel, dim3(a.N), dim3(kTopkThreads), 0, stream, a, topk, ckey, cid, cnt,
+                     cp.cstride, out_idx, out_score, 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_candidate_blocks(const IndexArgs& a, const CandPlan& cp, uint8_t* ws, int cand_block,
+                                   int n_cand, int32_t* cand_out, hipStream_t stream) {
+  if (a.N == 0) return hipSuccess;
+  float* bmax = reinterpret_cast<float*>(ws + cp.bmax_off);
+  const int nb_cap = (a.nv_cap + cand_block - 1) / cand_block;
+  hipLaunchKernelGGL(block_max_kernel, dim3(a.N, (nb_cap + kScoreThreads - 1) / kScoreThreads), dim3(kScoreThreads),
+                     0, stream, a, cand_block, bmax, cp.bstride);
+  IndexArgs b = a;                                   // the selection over block scores
+  b.scores = bmax;
+  b.score_stride = cp.bstride;
+  b.nv_div = cand_block;
+  b.blk_thr = nullptr;
+  b.cand_count = nullptr;
+  hipLaunchKernelGGL((topk_single_kernel<kTopkThreads, kSingleMax>), dim3(a.N), dim3(kTopkThreads), 0, stream, b,
+                     n_cand, cand_out, static_cast<float*>(nullptr));
   return hipGetLastError();
 }
 

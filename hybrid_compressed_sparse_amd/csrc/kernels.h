@@ -132,6 +132,8 @@ struct IndexArgs {
   // a chunk of consecutive queries of one sequence (q_seq == nullptr): query t is at position
   // p0 + t of sequence seq_const
   int seq_const, p0;
+  // > 0: a query's count is of blocks of nv_div entries (ceil), for selections over block scores
+  int nv_div;
 };
 
 struct TopkPlan {
@@ -147,5 +149,21 @@ hipError_t launch_index_scores_compress(const IndexArgs& a, const CompressArgs& 
                                         hipStream_t stream);
 hipError_t launch_topk(const IndexArgs& a, const TopkPlan& plan, int topk, int32_t* out_idx,
                        float* out_score, uint8_t* ws, int blk_entries, hipStream_t stream);
+
+// Two-level candidate filtering. Workspace past the plain plan's: candidate keys and ids
+// [N, cstride] and counters [N] (consumer), or block scores [N, bstride] (source).
+struct CandPlan {
+  int64_t cstride, bstride;
+  size_t ckey_off, cid_off, cnt_off, bmax_off, ws_bytes;
+};
+CandPlan cand_plan(const TopkPlan& base, int N, int nv_cap, int cand_block, int n_cand);
+// consumer: after the scores (launched with a.cand_count = the plan's counters, a.blk_thr null),
+// gather the entries of the listed blocks and select the top-k among them
+hipError_t launch_topk_in_blocks(const IndexArgs& a, const CandPlan& cp, uint8_t* ws, const int32_t* cand_in,
+                                 int n_cand, int cand_block, int topk, int32_t* out_idx, float* out_score,
+                                 hipStream_t stream);
+// source: after its own top-k, the n_cand blocks with the largest block max
+hipError_t launch_candidate_blocks(const IndexArgs& a, const CandPlan& cp, uint8_t* ws, int cand_block,
+                                   int n_cand, int32_t* cand_out, hipStream_t stream);
 
 }  // namespace hcs

@@ -13,6 +13,8 @@
  *   hcs_index_topk            the Lightning Indexer of CSA layers: scores of every visible
  *                             compressed entry, I = sum_h w_h * ReLU(q_h . k), and the top-k;
  *   hcs_index_topk_chunk      the same for a chunk of consecutive queries of one sequence;
+ *   hcs_index_topk_cand       the same with two-level candidate filtering (publish or follow
+ *                             the top blocks of compressed positions);
  *   hcs_index_topk_compress   hcs_index_topk and hcs_compress_kv of one decode step in one
  *                             launch (they touch disjoint data);
  *   hcs_sparse_mla_decode     single-KV-head attention of every query head over the query's
@@ -205,6 +207,30 @@ hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w,
                           const int32_t* q_seq, const int32_t* q_pos, int N, int H_I, int d_I,
                           int m, int topk, int max_pos, int32_t* out_idx, float* out_score,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* Two-level candidate filtering ("DeepSeek V4.1 attention", `DeepseekV4Indexer`: the      */
+/* indexer of the candidate source layer also publishes its top blocks of consecutive      */
+/* compressed positions; later indexers mask their scores to those blocks before their own  */
+/* top-k). Arguments and scores as hcs_index_topk, plus cand_block (entries per block:      */
+/* block j = entries j*cand_block .. j*cand_block+cand_block-1) and n_cand. Exactly one of:  */
+/*   cand_out [N, n_cand] int32 (source): after the top-k, the n_cand blocks with the       */
+/*            largest block score (the max of the block's visible entries' scores), ties to */
+/*            the smaller block id, in no particular order, -1 at the tail when the query   */
+/*            sees fewer blocks. At most 32768 blocks may be visible to a query.             */
+/*   cand_in  [N, n_cand] int32 (consumer): only the visible entries of the listed blocks   */
+/*            take part in the top-k (ties to the smaller id); when no more than topk of     */
+/*            them exist, all are selected and out_idx is padded with -1. Ids < 0 are        */
+/*            skipped; a block must not be listed twice for one query.                       */
+/* ws       hcs_index_topk_cand_workspace_size(N, max_pos, m, topk, cand_block, n_cand)     */
+/*          bytes, 256-byte aligned.                                                        */
+/* Constraints: as hcs_index_topk, cand_block >= 1, 1 <= n_cand <= 4096.                    */
+size_t hcs_index_topk_cand_workspace_size(int N, int max_pos, int m, int topk, int cand_block, int n_cand);
+hcs_status hcs_index_topk_cand(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
+                               const int32_t* q_seq, const int32_t* q_pos, int N, int H_I, int d_I, int m,
+                               int topk, int max_pos, int cand_block, int n_cand, const int32_t* cand_in,
+                               int32_t* cand_out, int32_t* out_idx, float* out_score, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------ */
 /* Lightning-Indexer for a prefill chunk: hcs_index_topk for the Q consecutive queries    */

@@ -123,6 +123,24 @@ def test_indexer_prep_validation_errors_before_any_launch():
     assert k(16, 128, 16, 16, 0, 128, 4, 16, 1e-6, None, None, 0, 0, _paged(3, 128), None) == 0   # empty
 
 
+@needs_lib
+def test_candidate_filtering_validation_errors_before_any_launch():
+    L = hcs.lib()
+    f = L.hcs_index_topk_cand
+    # q, q_scale, w, keys, q_seq, q_pos, N, H_I, d_I, m, topk, max_pos, cb, n_cand, cand_in, cand_out,
+    # out_idx, out_score, ws, ws_bytes, stream
+    k0 = _paged(0, 128)
+    assert f(16, None, 16, k0, 16, 16, 4, 64, 128, 4, 64, 1000, 64, 8, None, None, 16, None, 16, 1 << 20, None) == 1
+    assert f(16, None, 16, k0, 16, 16, 4, 64, 128, 4, 64, 1000, 64, 8, 16, 16, 16, None, 16, 1 << 20, None) == 1
+    assert f(16, None, 16, k0, 16, 16, 4, 64, 128, 4, 64, 1000, 0, 8, 16, None, 16, None, 16, 1 << 20, None) == 1
+    assert f(16, None, 16, k0, 16, 16, 4, 64, 128, 4, 64, 1000, 64, 5000, 16, None, 16, None, 16, 1 << 20, None) == 2
+    # a source whose queries may see more than 32768 blocks
+    assert f(16, None, 16, k0, 16, 16, 4, 64, 128, 1, 64, 40000, 1, 8, None, 16, 16, None, 16, 1 << 30, None) == 2
+    need = L.hcs_index_topk_cand_workspace_size(4, 1000, 4, 64, 64, 8)
+    assert need > L.hcs_index_topk_workspace_size(4, 1000, 4, 64)
+    assert f(16, None, 16, k0, 16, 16, 4, 64, 128, 4, 64, 1000, 64, 8, 16, None, 16, None, 256, need - 1, None) == 3
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(hcs, "_lib", None)
     monkeypatch.setattr(hcs, "LIB_PATH", "/nonexistent/libhcs.so")
