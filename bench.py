@@ -42,12 +42,14 @@ def algo_bytes(wl, n_vis: int) -> dict:
     Score scratch and split partials are not counted: they are this implementation's choice.
     """
     B, H, d = wl.B, wl.H, wl.d
-    row = 584 if wl.kv_fmt == "fp8ds" else 2 * d
+    row_of = {"fp8ds": 584, "mxfp8": 528, "nvfp4": 288}
+    row = row_of.get(wl.kv_fmt, 2 * d)                  # window rows
+    crow = row_of.get(wl.cfmt, 2 * d)                   # compressed rows
     rows_comp = min(wl.topk, n_vis) if wl.indexer else n_vis
     pt_comp = math.ceil(n_vis / 64) * 4 if not wl.indexer else min(rows_comp, math.ceil(n_vis / 64)) * 4
     attn = B * (H * d * 2                     # q
                 + wl.window * row             # sliding window rows
-                + rows_comp * row             # compressed rows
+                + rows_comp * crow            # compressed rows
                 + (rows_comp * 4 if wl.indexer else 0)
                 + H * d * 2 + H * 4           # out, lse
                 + 3 * 4 + pt_comp)            # page-table entries
@@ -57,7 +59,7 @@ def algo_bytes(wl, n_vis: int) -> dict:
         qb = wl.H_I * krow
         ix = B * (n_vis * krow + qb + wl.H_I * 4 + wl.topk * 8 + math.ceil(n_vis / 64) * 4)
     in_b = 4 if wl.in_dtype == "f32" else 2
-    comp = B * (2 * 3 * d * 4 + 2 * d * in_b + row)
+    comp = B * (2 * 3 * d * 4 + 2 * d * in_b + crow)
     return {"attention": attn, "index_topk": ix, "compress": comp, "step": attn + ix + comp}
 
 

@@ -261,38 +261,35 @@ struct RowFmt<HCS_FMT_MXFP8> {
   }
 };
 
-// NVFP4: 512 e2m1 (two per byte, element 2j low) + an e4m3 scale per 16 dims. Lanes 0..15 take
-// 32 values and their two scale bytes.
+// NVFP4: 512 e2m1 (two per byte, element 2j low) + an e4m3 scale per 16 dims. Every lane takes
+// 8 values (4 code bytes, one 16-byte bf16 chunk) and the scale byte of its half block.
 template <>
 struct RowFmt<HCS_FMT_NVFP4> {
   static constexpr int PB = kNv4PageBytes;
   __device__ static __forceinline__ void load(const uint8_t* page, int slot, int lane, i32x4& v, int& se) {
-    const uint8_t* src = page ? page + slot * 256 + (lane & 15) * 16 : g_zero_row + (lane & 15) * 16;
-    const uint8_t* ssrc = page ? page + kNv4Scales + slot * 32 + 2 * (lane & 15) : g_zero_row;
-    v = *(const i32x4*)src;
-    se = *(const uint16_t*)ssrc;
+    const uint8_t* src = page ? page + slot * 256 + lane * 4 : g_zero_row + lane * 4;
+    const uint8_t* ssrc = page ? page + kNv4Scales + slot * 32 + (lane >> 1) : g_zero_row;
+    v.x = *(const int*)src;
+    se = *ssrc;
+  }
+  // byte k of the codes -> its two values (low nibble first) as bf16 by the hardware conversion
+  // (unit scale), then times the e4m3 block scale; the product has at most 6 significant bits,
+  // so it is exact in bf16 and the float32 result's upper half is the bf16
+  template <int K>
+  __device__ static __forceinline__ uint32_t pair(uint32_t w, float s) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, K);
+    uint32_t u;
+    __builtin_memcpy(&u, &r, 4);
+    const float lo = __uint_as_float(u << 16) * s, hi = __uint_as_float(u & 0xffff0000u) * s;
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
   }
   __device__ static __forceinline__ void store(uint8_t* row, int sw, int lane, const i32x4& v, int se) {
-    if (lane >= 16) return;
     typedef float f32x2 __attribute__((ext_vector_type(2)));
-    const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8(se, false);   // the two block scales
-    const uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {                  // chunk c: 8 values of word c
-      const float s = c < 2 ? sc.x : sc.y;
-      i32x4 o;
-      uint32_t ov[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t b = (w[c] >> (8 * k)) & 0xffu;
-        ov[k] = pack_bf16x2(e2m1_value(b & 0xfu) * s, e2m1_value(b >> 4) * s);
-      }
-      o.x = (int)ov[0];
-      o.y = (int)ov[1];
-      o.z = (int)ov[2];
-      o.w = (int)ov[3];
-      *(i32x4*)(row + ((4 * lane + c) ^ sw) * 16) = o;
-    }
+    const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8(se, false);
+    const uint32_t w = (uint32_t)v.x;
+    *(i32x4*)(row + (lane ^ sw) * 16) = i32x4{(int)pair<0>(w, sc.x), (int)pair<1>(w, sc.x),
+                                              (int)pair<2>(w, sc.x), (int)pair<3>(w, sc.x)};
   }
 };
 
@@ -309,7 +306,10 @@ struct QuantStage {
     const bool comp = (e >> 31) != 0;
     const uint32_t ridx = e & 0x7fffffffu;
     const int slot = (int)(ridx & 63);
-    if (comp) {
+    if constexpr (SF == CF) {
+      RowFmt<SF>::load(ok ? (comp ? comp_base : swa_base) + (size_t)(ridx >> 6) * RowFmt<SF>::PB : nullptr,
+                       slot, lane, v, se);
+    } else if (comp) {
       RowFmt<CF>::load(ok ? comp_base + (size_t)(ridx >> 6) * RowFmt<CF>::PB : nullptr, slot, lane, v, se);
       se |= 1 << 16;
     } else {
@@ -318,8 +318,13 @@ struct QuantStage {
   }
   __device__ static __forceinline__ void store(uint8_t* tile, int r, int sw, int lane, const i32x4& v, int se) {
     uint8_t* row = tile + r * RS;
-    if (se >> 16) RowFmt<CF>::store(row, sw, lane, v, se & 0xffff);
-    else RowFmt<SF>::store(row, sw, lane, v, se);
+    if constexpr (SF == CF) {
+      RowFmt<SF>::store(row, sw, lane, v, se);
+    } else {
+      // every lane holds the same row, so its source is wave-uniform: branch on a scalar
+      if (__builtin_amdgcn_readfirstlane(se >> 16)) RowFmt<CF>::store(row, sw, lane, v, se & 0xffff);
+      else RowFmt<SF>::store(row, sw, lane, v, se);
+    }
   }
 };
 

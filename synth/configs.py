@@ -76,5 +76,8 @@ CSA_DECODE_1M_FP8 = Workload(
     name="csa_decode_1m_fp8", kind="decode", B=8, ctx=1048576, H=64, d=512, d_rope=64, m=4,
     window=128, indexer=True, H_I=64, d_I=128, topk=2048, kv_fmt="fp8ds", ix_fmt="mxfp4")
 
-ALL = [TINY_CSA, CSA_DECODE, HCA_DECODE, CSA_PREFILL, CSA_DECODE_1M_FP8]
+# The same with the V4.1 records: MXFP8 window rows (528 B), NVFP4 compressed rows (288 B).
+CSA_DECODE_1M_V41 = CSA_DECODE_1M_FP8.with_(name="csa_decode_1m_v41", kv_fmt="mxfp8", comp_fmt="nvfp4")
+
+ALL = [TINY_CSA, CSA_DECODE, HCA_DECODE, CSA_PREFILL, CSA_DECODE_1M_FP8, CSA_DECODE_1M_V41]
 BY_NAME = {w.name: w for w in ALL}
