@@ -9,7 +9,8 @@
 //     position or compressed id -> page table -> page, slot) into an LDS table, with all
 //     loads issued together and no branches, so each later row load is a single independent
 //     gather; rows that do not take part read a zero row;
-//   * rows are walked in 64-row blocks through a double-buffered LDS ring, swizzled so that
+//   * rows are walked in blocks through an LDS ring (64-row blocks, double-buffered, in the
+//     16-head kernel; 32-row blocks in a ring of four in the all-heads kernel), swizzled so that
 //     both readers below are free of bank conflicts;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (rows on M, 16 heads on N, q in registers as
 //     the B operand), whose accumulator layout is the one P^T is written in, then
@@ -663,41 +664,49 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
 
 // ================================================================ all-heads kernel (bf16)
 // A block is (query, split of its rows, 64 heads), so every gathered row is read once for all
-// heads of the query. Rows go from the paged cache straight into a double-buffered, swizzled
-// 64-row LDS ring with global_load_lds (no registers; the chunk swizzle is applied to the source
+// heads of the query. Rows go from the paged cache straight into a ring of four 32-row LDS
+// tiles with global_load_lds (no registers; the chunk swizzle is applied to the source
 // addresses), from a table of row byte addresses built once per block.
-// 8 waves, two per SIMD, so one wave's MFMAs cover another's LDS and memory waits. For S^T,
-// wave w takes heads 16 (w % 4) .. +15 (q in registers) and rows 32 (w / 4) .. +31 of a block;
-// the two waves of a head group keep the same reference max, agreed through LDS when it must
-// move. For O^T, wave w takes output columns D/8 * w .. +D/8 for all 64 heads, with P^T read
-// from LDS. A block costs two barriers (three when a reference max moves).
+// The eight waves have two roles, one of each per SIMD, and work on consecutive row blocks at
+// the same time, so that one role's MFMAs cover the other's LDS waits:
+//   S waves (0..3): wave w holds q of heads 16w .. 16w+15 in registers and computes S^T for all
+//     32 rows of block i, its online softmax (each wave owns whole heads, so no cross-wave
+//     max), and writes P^T (bf16) and any rescale factors to LDS;
+//   O waves (4..7): wave 4+c accumulates O^T for output columns D/4 * c .. +D/4 of all 64
+//     heads over block i-1, from that block's tile and P^T.
+// While block i is scored and block i-1 accumulated, the rows of blocks i+1 and i+2 are in
+// flight into the other two tiles. Each role runs its own loop (so q and the O accumulators are
+// never live in the same wave) and both pass one barrier per block.
 constexpr int kHeadsThreads = 512;
+
+// s_waitcnt vmcnt(n) (gfx9 encoding, n < 16): expcnt and lgkmcnt not waited for
+#define HCS_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
 template <int D>
 __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a) {
-  constexpr int NT = kHeadsThreads, NW = NT / 64;
   constexpr int RS = D * 2, KS = D / 32;
-  constexpr int BT = 64;                          // rows per block
-  constexpr int WRL = BT / NW;                    // rows each wave loads per block
-  constexpr int CTW = D / 16 / NW;                // 16-column output tiles per wave
+  constexpr int BT = 32;                          // rows per block
+  constexpr int TB = BT * RS;                     // bytes per tile
+  constexpr int CTO = D / 16 / 4;                 // 16-column output tiles per O wave
   constexpr int PR = BT + 8;                      // P row stride (elements), padded
   constexpr int RPI = 1024 / RS;                  // rows per 1 KiB async load
   constexpr int LPR = 64 / RPI;                   // lanes per row in an async load
+  constexpr int WRL = BT / 8;                     // rows each wave loads per block
   constexpr int NLD = WRL / RPI;                  // async loads per wave per block
-  static_assert(CTW >= 1 && NLD >= 1, "unsupported head dim");
-  __shared__ __attribute__((aligned(16))) uint8_t tile0[BT * RS];
-  __shared__ __attribute__((aligned(16))) uint8_t tile1[BT * RS];
+  constexpr int PD = 4;                           // K-fragment steps read ahead in S^T
+  static_assert(CTO >= 1 && NLD >= 1 && NLD < 16 && KS % PD == 0, "unsupported head dim");
+  // tiles 2 and 3 first hold q of the 64 heads (64 rows of RS bytes)
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[4 * TB];
   __shared__ __attribute__((aligned(16))) uint32_t rowtab[kMaxRowsWG];
   __shared__ int ptl[kPtCache];
-  __shared__ __attribute__((aligned(16))) __bf16 p_lds[64 * PR];
-  __shared__ float mx[NW][16];
-  __shared__ float alpha_lds[64];
-  __shared__ int flags[NW];
-  __shared__ float hm[64], hl[2][64];
+  __shared__ __attribute__((aligned(16))) __bf16 p_lds[2][64 * PR];
+  __shared__ float alpha_lds[2][64];
+  __shared__ int flags[2][4];
+  __shared__ float hm[64], hl[64];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  const int hq = wave & 3, rh = wave >> 2;       // S^T role: head group, row half
   const int G = a.nsplit * a.n_hg;
   const int xcd = blockIdx.x & 7, r = blockIdx.x >> 3;
   const int t = (r / G) * 8 + xcd;
@@ -709,10 +718,11 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   const QueryRows q = query_rows(a, t);
   const int r0 = s * a.rows_per_split;
   const int n_rows = max(0, min(q.R, r0 + a.rows_per_split) - r0);
-  // q of the block's 64 heads: one contiguous row per head, copied into tile1 by async loads
-  // (wave w: heads 8w..8w+7, chunk c of head h stored at c ^ (h mod 16)); read into registers
-  // after the first rows are requested. tile1 receives rows only from the second block on, and
-  // every wave has read its q by then (the first block's barrier orders it).
+  uint8_t* const qstage = tiles + 2 * TB;
+  // q of the block's 64 heads: one contiguous row per head, copied into tiles 2-3 by async
+  // loads (wave w: heads 8w..8w+7, chunk c of head h stored at c ^ (h mod 16)); the S waves read
+  // it into registers before the first barrier of the block loop, and tile 2 receives rows only
+  // after that barrier.
   {
     constexpr int QLPR = RS / 16;                  // lanes per head row in one load
     constexpr int QHPI = 64 / QLPR;                // heads per load
@@ -723,30 +733,20 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       const uint8_t* src = hh < a.H ? reinterpret_cast<const uint8_t*>(a.q + ((int64_t)t * a.H + hh) * D)
                                     : g_zero_row;
       const int ch = (lane % QLPR) ^ (hl_ & 15);
-      dma16v(src + ch * 16, lds_addr(tile1) + (8 * wave + i * QHPI) * RS);
+      dma16v(src + ch * 16, lds_addr(qstage) + (8 * wave + i * QHPI) * RS);
     }
   }
-  fill_rows<NT>(a, t, q, r0, n_rows, rowtab, ptl, BT);
+  fill_rows<kHeadsThreads>(a, t, q, r0, n_rows, rowtab, ptl, BT);
   const int nblk = (n_rows + BT - 1) / BT;
 
-  f32x4 oacc[CTW][4];
-#pragma unroll
-  for (int ct = 0; ct < CTW; ++ct)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) oacc[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegInf, l_part = 0.f;            // head hbase + 16 hq + l16, rows of half rh
-
-  // async loads: wave w fills rows WRL w .. +WRL-1 of a block; lane -> (row, chunk) of a load,
-  // the swizzle applied on the source side (LDS chunk slot c of row r receives chunk c ^ swz(r))
-  // Row WRL w + i*RPI + lane/LPR has swz_dec((that row) & 15) = swz_dec(i*RPI + lane/LPR) | 8 (w & 1)
-  // (WRL = 8), so the source chunk of a lane is (lane % LPR) ^ 8 (w & 1) ^ swz_dec(...).
-  static_assert(WRL == 8, "row swizzle below assumes 8 rows per wave");
-  const int lane_x = ((lane % LPR) ^ (8 * (wave & 1))) * 16;
+  // async loads: wave w fills rows WRL w .. +WRL-1 of a block; LDS chunk slot c of row r
+  // receives source chunk c ^ swz_dec(r mod 16)
   auto row_ptr = [&](uint32_t e) {
     return e != kNoRow ? ((e >> 31) ? a.comp.base : a.swa.base) + (size_t)(e & 0x7fffffffu) * RS
                        : g_zero_row;
   };
-  auto issue = [&](int b, uint8_t* tbuf) {
+  auto issue = [&](int b) {
+    uint8_t* tb = tiles + (b & 3) * TB;
     const uint32_t* at = rowtab + b * BT + WRL * wave;
     if constexpr (RPI == 1) {
       // lane j < WRL reads the entry of row j; each load takes it from that lane
@@ -754,206 +754,216 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const uint8_t* src = row_ptr((uint32_t)__builtin_amdgcn_readlane((int)my, i));
-        dma16(src, (uint32_t)(lane_x ^ (swz_dec(i) * 16)), lds_addr(tbuf) + (WRL * wave + i) * RS);
+        const int sw = swz_dec((WRL * wave + i) & 15);
+        dma16(src, (uint32_t)((lane ^ sw) * 16), lds_addr(tb) + (WRL * wave + i) * RS);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const uint8_t* src = row_ptr(at[i * RPI + lane / LPR]);
-        const int sw = swz_dec(i * RPI + lane / LPR) * 16;
-        dma16v(src + (lane_x ^ sw), lds_addr(tbuf) + (WRL * wave + i * RPI) * RS);
+        const int rl = i * RPI + lane / LPR;
+        const uint8_t* src = row_ptr(at[rl]);
+        const int sw = swz_dec((WRL * wave + rl) & 15);
+        dma16v(src + (((lane % LPR) ^ sw) * 16), lds_addr(tb) + (WRL * wave + i * RPI) * RS);
       }
     }
   };
-  if (nblk > 0) issue(0, tile0);
-  bf16x8 qreg[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qreg[ks] = *(const bf16x8*)(tile1 + (16 * hq + l16) * RS + (((4 * ks + g) ^ l16) << 4));
+  if (nblk > 0) issue(0);
+  if (nblk > 1) issue(1);
+  // top of block step i: this wave's copies of block i have landed (those of block i+1 may
+  // still be in flight), then the barrier makes every wave's copies and the previous step's
+  // LDS writes visible
+  auto step_sync = [&](int i) {
+    if (i + 1 < nblk) HCS_WAIT_VMCNT(NLD);
+    else wait_vm_zero();
+    lds_barrier();
+    if (i + 2 < nblk) issue(i + 2);
+  };
 
-  // lane-constant LDS offsets
-  // K row 32 rh + 16 mt + l16, chunk (4ks + g) ^ s = 4 (ks ^ (s >> 2)) + ((g ^ s) & 3), s = swz_dec(l16)
-  const int sk = swz_dec(l16);
-  int ko4[4];
-#pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4) ko4[k4] = (32 * rh + l16) * RS + ((g ^ sk) & 3) * 16 + 64 * (k4 ^ (sk >> 2));
-  // V^T rows 8g + jv and 8g + 4 + jv of a 32-row step: swz_dec = 2 jv + 8 (g & 1) (+1), so
-  // chunk (2 ctg + h) lands at 2 (ctg ^ (jv + 4 (g & 1))) + (h, resp. h ^ 1)
-  const int jv = l16 >> 2, q4 = l16 & 3, h2 = q4 >> 1;
-  const int vx = jv + 4 * (g & 1);
-  const int vrow = (8 * g + jv) * RS + (q4 & 1) * 8;
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  __bf16* prow = p_lds + (16 * hq + l16) * PR + 32 * rh + 4 * g;
-
-  auto block = [&](int b, uint8_t* T, uint8_t* TN) {
-    wait_vm_zero();                                      // this wave's rows of block b landed
-    lds_barrier();                                       // block b is in LDS
-    if (b + 1 < nblk) issue(b + 1, TN);
-    const uint32_t valid = (uint32_t)__ballot(rowtab[b * BT + 32 * rh + (lane & 31)] != kNoRow);
-    // ---- S^T[32 rows][16 heads]
-    // one k-step of K fragments is read ahead of the MFMAs that use it; the scheduling fences
-    // keep that pipeline (and the register use) as written
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    bf16x8 kf[2][2];
-    auto kload = [&](int ks, bf16x8* f) {
-      const int ko = ko4[ks & 3] + (ks >> 2) * 256;
-      f[0] = *(const bf16x8*)(T + ko);
-      f[1] = *(const bf16x8*)(T + ko + 16 * RS);
-    };
-    kload(0, kf[0]);
+  const bool split = a.nsplit > 1;
+  if (wave < 4) {
+    // ================= S waves: heads hbase + 16 wave + l16
+    bf16x8 qreg[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks)
+      qreg[ks] = *(const bf16x8*)(qstage + (16 * wave + l16) * RS + (((4 * ks + g) ^ l16) << 4));
+    // K row 16 mt + l16, chunk (4ks + g) ^ s = 4 (ks ^ (s >> 2)) + ((g ^ s) & 3), s = swz_dec(l16)
+    const int sk = swz_dec(l16);
+    int ko4[4];
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) ko4[k4] = l16 * RS + ((g ^ sk) & 3) * 16 + 64 * (k4 ^ (sk >> 2));
+    float m_ref = kNegInf, l_part = 0.f;
+    for (int i = 0; i <= nblk; ++i) {
+      step_sync(i);
+      if (i == nblk) break;
+      const uint8_t* T = tiles + (i & 3) * TB;
+      const int pb = i & 1;
+      const uint32_t valid = (uint32_t)__ballot(rowtab[i * BT + (lane & 31)] != kNoRow);
+      // ---- S^T[32 rows][16 heads], K fragments read PD k-steps ahead of their MFMAs
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      bf16x8 kf[PD][2];
+      auto kload = [&](int ks, bf16x8* f) {
+        const int ko = ko4[ks & 3] + (ks >> 2) * 256;
+        f[0] = *(const bf16x8*)(T + ko);
+        f[1] = *(const bf16x8*)(T + ko + 16 * RS);
+      };
+#pragma unroll
+      for (int ks = 0; ks < PD; ++ks) kload(ks, kf[ks]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % PD][mt], qreg[ks], sacc[mt], 0, 0, 0);
+        if (ks + PD < KS) kload(ks + PD, kf[ks % PD]);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      if (ks + 1 < KS) kload(ks + 1, kf[(ks + 1) & 1]);
+      // ---- online softmax over the block's rows (this wave owns its heads' rows)
+      float x[2][4];
+      float tmax = kNegInf;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks & 1][mt], qreg[ks], sacc[mt], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    float x[2][4];
-    float tmax = kNegInf;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = mt * 16 + 4 * g + i;
-        x[mt][i] = ((valid >> row) & 1u) ? sacc[mt][i] * a.scale_log2 : kNegInf;
-        tmax = fmaxf(tmax, x[mt][i]);
+        for (int e = 0; e < 4; ++e) {
+          const int row = mt * 16 + 4 * g + e;
+          x[mt][e] = ((valid >> row) & 1u) ? sacc[mt][e] * a.scale_log2 : kNegInf;
+          tmax = fmaxf(tmax, x[mt][e]);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const bool any_over = __any(tmax > m_ref + kLazyBlock);
+      if (any_over) {
+        // rare: new reference maxima for this wave's heads
+        const float mnew = tmax > m_ref + kLazy ? tmax : m_ref;
+        // 0 when m_ref = -inf; 1 for a head with no row yet (-inf - -inf would be NaN)
+        const float alpha = mnew == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_ref - mnew);
+        l_part *= alpha;
+        m_ref = mnew;
+        if (g == 0) alpha_lds[pb][16 * wave + l16] = alpha;
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const bool any_over = __any(tmax > m_ref + kLazyBlock);
-    if (g == 0) mx[wave][l16] = tmax;
-    if (lane == 0) flags[wave] = any_over ? 1 : 0;
-    auto probs = [&](float& psum) {
+      if (lane == 0) flags[pb][wave] = any_over ? 1 : 0;
       const float mr = m_ref == kNegInf ? 0.f : m_ref;
-      psum = 0.f;
+      __bf16* prow = p_lds[pb] + (16 * wave + l16) * PR + 4 * g;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         bf16x4 p4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(x[mt][i] - mr);
-          psum += pv;
-          p4[i] = (__bf16)pv;
+        for (int e = 0; e < 4; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(x[mt][e] - mr);
+          l_part += pv;
+          p4[e] = (__bf16)pv;
         }
         *(bf16x4*)(prow + mt * 16) = p4;
       }
-    };
-    float psum = 0.f;
-    if (!any_over) probs(psum);
-    lds_barrier();                                       // probabilities (or flags) of the block
-    int anyf = 0;
+    }
+    float lt = l_part + __shfl_xor(l_part, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (g == 0) {
+      hl[16 * wave + l16] = lt;
+      hm[16 * wave + l16] = m_ref;
+    }
+    __syncthreads();                                // (E1) per-head (max, sum) published
+    __syncthreads();                                // (E2) O waves have staged the output
+  } else {
+    // ================= O waves: output columns D/4 * ow .. +D/4 of all 64 heads
+    const int ow = wave - 4;
+    f32x4 oacc[CTO][4];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) anyf |= flags[w];
-    if (anyf) {
-      // rare: new reference maxima, agreed by the two waves of each head group
-      const float bmax = fmaxf(mx[hq][l16], mx[hq + 4][l16]);
-      const float mnew = bmax > m_ref + kLazy ? bmax : m_ref;
-      // 0 when m_ref = -inf; 1 for a head with no row yet (-inf - -inf would be NaN)
-      const float alpha = mnew == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_ref - mnew);
-      l_part *= alpha;
-      m_ref = mnew;
-      if (rh == 0 && g == 0) alpha_lds[16 * hq + l16] = alpha;
-      probs(psum);
-      lds_barrier();
+    for (int ct = 0; ct < CTO; ++ct)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) oacc[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // V^T rows 8g + jv and 8g + 4 + jv: swz_dec = 2 jv + 8 (g & 1) (+1), so chunk (2 ctg + h)
+    // lands at 2 (ctg ^ (jv + 4 (g & 1))) + (h, resp. h ^ 1)
+    const int jv = l16 >> 2, q4 = l16 & 3, h2 = q4 >> 1;
+    const int vx = jv + 4 * (g & 1);
+    const int vrow = (8 * g + jv) * RS + (q4 & 1) * 8;
+    for (int i = 0; i <= nblk; ++i) {
+      step_sync(i);
+      if (i == 0) continue;
+      const int b = i - 1;
+      const uint8_t* T = tiles + (b & 3) * TB;
+      const int pb = b & 1;
+      // rescale the heads whose reference max moved in block b
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const float al = alpha_lds[16 * nt + l16];
+        if (flags[pb][nt]) {
+          const float al = alpha_lds[pb][16 * nt + l16];
 #pragma unroll
-        for (int ct = 0; ct < CTW; ++ct) oacc[ct][nt] *= al;
+          for (int ct = 0; ct < CTO; ++ct) oacc[ct][nt] *= al;
+        }
       }
-    }
-    l_part += psum;
-    // ---- O^T[this wave's columns][64 heads] += V^T P^T over the block's 64 rows
-    // (V^T fragments of the next column tile are read ahead, as for S^T)
-    auto vload = [&](int kk, int ct) {
-      const int ctg = wave * CTW + ct;
-      const uint8_t* vb = T + kk * 32 * RS + vrow + 32 * ((ctg & 7) ^ vx) + (ctg >> 3) * 256;
-      const i16x4 v0 = lds_read_tr16(vb + 16 * h2);
-      const i16x4 v1 = lds_read_tr16(vb + 4 * RS + 16 * (h2 ^ 1));
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
+      auto vload = [&](int ct) {
+        const int ctg = ow * CTO + ct;
+        const uint8_t* vb = T + vrow + 32 * ((ctg & 7) ^ vx) + (ctg >> 3) * 256;
+        const i16x4 v0 = lds_read_tr16(vb + 16 * h2);
+        const i16x4 v1 = lds_read_tr16(vb + 4 * RS + 16 * (h2 ^ 1));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 pbf[4];
 #pragma unroll
-    for (int kk = 0; kk < BT / 32; ++kk) {
-      bf16x8 pb[4];
+      for (int nt = 0; nt < 4; ++nt) pbf[nt] = *(const bf16x8*)(p_lds[pb] + (16 * nt + l16) * PR + 8 * g);
+      constexpr int VD = CTO < 2 ? CTO : 2;         // V^T fragments read ahead
+      bf16x8 vf[VD];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) pb[nt] = *(const bf16x8*)(p_lds + (16 * nt + l16) * PR + kk * 32 + 8 * g);
-      bf16x8 vf[2];
-      vf[0] = vload(kk, 0);
+      for (int ct = 0; ct < VD; ++ct) vf[ct] = vload(ct);
 #pragma unroll
-      for (int ct = 0; ct < CTW; ++ct) {
+      for (int ct = 0; ct < CTO; ++ct) {
         __builtin_amdgcn_sched_barrier(0);
-        if (ct + 1 < CTW) vf[(ct + 1) & 1] = vload(kk, ct + 1);
+        const bf16x8 v = vf[ct % VD];
+        if (ct + VD < CTO) vf[ct % VD] = vload(ct + VD);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
-          oacc[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct & 1], pb[nt], oacc[ct][nt], 0, 0, 0);
+          oacc[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pbf[nt], oacc[ct][nt], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  for (int b = 0; b < nblk; b += 2) {
-    block(b, tile0, tile1);
-    if (b + 1 < nblk) block(b + 1, tile1, tile0);
-  }
-
-  // ---- per-head (max, sum) to every wave
-  // sink logits (log2 units) of the heads this lane finishes, hbase + 16 nt + l16, loaded before
-  // any store is issued (a load wait also waits for earlier stores)
-  float sink2[4];
+    // sink logits (log2 units) of the heads this lane finishes, hbase + 16 nt + l16, loaded before
+    // any store is issued (a load wait also waits for earlier stores)
+    float sink2[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int hh = hbase + 16 * nt + l16;
-    sink2[nt] = a.sink && hh < a.H && a.nsplit == 1 ? a.sink[hh] * kLog2e : kNegInf;
-  }
-  float lt = l_part + __shfl_xor(l_part, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
-  if (g == 0) {
-    hl[rh][16 * hq + l16] = lt;
-    if (rh == 0) hm[16 * hq + l16] = m_ref;
-  }
-  __syncthreads();                                  // also: every wave is done with the tiles
-  // The result goes through LDS so that each global store writes whole rows: lane holds
-  // O^T[c = 16 (wave * CTW + ct) + 4g + i][head 16 nt + l16]; in LDS, row h holds head h with
-  // its 16-byte chunks XOR-swizzled by h mod 16 (conflict-free for both the scattered writes
-  // here and the row reads below).
-  // One path for both cases: bf16 [64 heads][D] in tile0 (64 rows of RS bytes), then whole rows
-  // to `out` (normalised, with the sink) or, when the rows are split, to this split's partial
-  // rows (normalised by this split's own sum; its (max, sum) go to ws_ml for the merge).
-  const bool split = a.nsplit > 1;
+    for (int nt = 0; nt < 4; ++nt) {
+      const int hh = hbase + 16 * nt + l16;
+      sink2[nt] = a.sink && hh < a.H && !split ? a.sink[hh] * kLog2e : kNegInf;
+    }
+    __syncthreads();                                // (E1)
+    // The result goes through LDS so that each global store writes whole rows: lane holds
+    // O^T[c = 16 (ow * CTO + ct) + 4g + e][head 16 nt + l16]; in LDS (tiles 0-1, free now), row h
+    // holds head h with its 16-byte chunks XOR-swizzled by h mod 16 (conflict-free for both the
+    // scattered writes here and the row reads below). Whole rows then go to `out` (normalised,
+    // with the sink) or, when the rows are split, to this split's partial rows (normalised by
+    // this split's own sum; its (max, sum) go to ws_ml for the merge).
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int hh = hbase + 16 * nt + l16;
-    float M = hm[16 * nt + l16], L = hl[0][16 * nt + l16] + hl[1][16 * nt + l16];
-    if (split) {
-      if (g == 0 && wave == 0 && hh < a.H) {
+    for (int nt = 0; nt < 4; ++nt) {
+      const int hh = hbase + 16 * nt + l16;
+      float M = hm[16 * nt + l16], L = hl[16 * nt + l16];
+      if (split && g == 0 && ow == 0 && hh < a.H) {
         const int64_t prow16 = ((int64_t)(t * a.n_h16 + hh / 16) * a.nsplit + s) * 16 + (hh & 15);
         a.ws_ml[prow16 * 2 + 0] = M;
         a.ws_ml[prow16 * 2 + 1] = L;
       }
-    }
-    const float f = split ? 1.f : finish_head_s2(sink2[nt], M, L);
-    const float inv = L > 0.f ? f / L : 0.f;
-    if (!split && a.lse && g == 0 && wave == 0 && hh < a.H) a.lse[(int64_t)t * a.H + hh] = lse_of(M, L);
-    uint8_t* hrow = tile0 + (16 * nt + l16) * RS;
+      const float f = split ? 1.f : finish_head_s2(sink2[nt], M, L);
+      const float inv = L > 0.f ? f / L : 0.f;
+      if (!split && a.lse && g == 0 && ow == 0 && hh < a.H) a.lse[(int64_t)t * a.H + hh] = lse_of(M, L);
+      uint8_t* hrow = tiles + (16 * nt + l16) * RS;
 #pragma unroll
-    for (int ct = 0; ct < CTW; ++ct) {
-      const f32x4 o = oacc[ct][nt] * inv;
-      uint2 pk;
-      pk.x = pack_bf16x2(o[0], o[1]);
-      pk.y = pack_bf16x2(o[2], o[3]);
-      const int cb = (16 * (wave * CTW + ct) + 4 * g) * 2;           // byte in the row
-      *(uint2*)(hrow + ((((cb >> 4) ^ l16) << 4) | (cb & 15))) = pk;
+      for (int ct = 0; ct < CTO; ++ct) {
+        const f32x4 o = oacc[ct][nt] * inv;
+        uint2 pk;
+        pk.x = pack_bf16x2(o[0], o[1]);
+        pk.y = pack_bf16x2(o[2], o[3]);
+        const int cb = (16 * (ow * CTO + ct) + 4 * g) * 2;           // byte in the row
+        *(uint2*)(hrow + ((((cb >> 4) ^ l16) << 4) | (cb & 15))) = pk;
+      }
     }
+    __syncthreads();                                // (E2)
   }
-  __syncthreads();
   constexpr int LPH = RS / 16;                       // lanes per head row
   constexpr int HPI = 64 / LPH;                      // heads per wave instruction
   i32x4 v[8 / HPI];
 #pragma unroll
   for (int k = 0; k < 8 / HPI; ++k) {
     const int hl_ = wave * 8 + k * HPI + lane / LPH, ch = lane % LPH;
-    v[k] = *(const i32x4*)(tile0 + hl_ * RS + ((ch ^ (hl_ & 15)) << 4));
+    v[k] = *(const i32x4*)(tiles + hl_ * RS + ((ch ^ (hl_ & 15)) << 4));
   }
 #pragma unroll
   for (int k = 0; k < 8 / HPI; ++k) {
