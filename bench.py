@@ -66,6 +66,7 @@ def algo_bytes(wl, n_vis: int) -> dict:
 # ------------------------------------------------------------------ measured HBM traffic
 
 ATTN_SOURCES = ["hybrid_compressed_sparse_amd/csrc/attention.hip", "hybrid_compressed_sparse_amd/csrc/common.h",
+                "hybrid_compressed_sparse_amd/csrc/select.h",
                 "hybrid_compressed_sparse_amd/csrc/kernels.h"]
 
 
@@ -103,8 +104,15 @@ def measured_traffic(workload: str):
 
 # ------------------------------------------------------------------ GPU step
 
+def select_in_attention_ok(wl) -> bool:
+    """The CSA decode shapes whose top-k can be taken inside the attention launch."""
+    from hybrid_compressed_sparse_amd.step import SELECT_MAX_VISIBLE
+    return (wl.kind == "decode" and wl.indexer and wl.d == 512 and wl.kv_fmt == "bf16"
+            and wl.cfmt == "bf16" and wl.ctx // wl.m <= SELECT_MAX_VISIBLE)
+
+
 class Bench:
-    def __init__(self, wl, sets: int, seed: int):
+    def __init__(self, wl, sets: int, seed: int, select_in_attention: bool = False):
         import torch
 
         from hybrid_compressed_sparse_amd.step import PathStep, StepShape
@@ -159,7 +167,7 @@ class Bench:
         self.step = PathStep(StepShape(N=sc0.N, H=wl.H, d=wl.d, m=wl.m, window=wl.window,
                                        max_pos=sc0.max_pos(), topk=wl.topk if wl.indexer else 0,
                                        prefill=wl.kind == "prefill", seq=0, P0=wl.P0),
-                             device=dev)
+                             device=dev, select_in_attention=select_in_attention)
         torch.cuda.synchronize()
 
     def run_op(self, op: str, i: int):
@@ -475,7 +483,8 @@ def bench_prefill(wl, args):
     queries) per step; tokens/s and the fraction of the bf16 MFMA peak."""
     R = max(1, min(args.sets, args.steps, 2))        # q alone is 256 MB per set
     log(f"[bench] {wl.name}: building {R} input sets")
-    bench = Bench(wl, R, seed=1000)
+    fused = select_in_attention_ok(wl) and not args.two_call
+    bench = Bench(wl, R, seed=1000, select_in_attention=fused)
     full, rem = divmod(args.steps, R)
 
     def timed(op):
@@ -515,6 +524,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the HCA side measurement")
+    ap.add_argument("--two-call", action="store_true",
+                    help="CSA decode: top-k in the indexer launch (hcs_index_topk_compress + "
+                         "hcs_sparse_mla_decode) instead of inside the attention")
     ap.add_argument("--only", default=None, help="replay only this op's graph (for profiling)")
     ap.add_argument("--side", default=None, choices=["compress_full", "insert_decode", "insert_prefill",
                                                      "indexer_formats"],
@@ -569,7 +581,8 @@ def main():
         sys.exit("--steps must be >= 1 and --warmup >= 0")
     R = max(1, min(args.sets, args.steps))
     log(f"[bench] {wl.name}: building {R} input sets")
-    bench = Bench(wl, R, seed=1000)
+    fused = select_in_attention_ok(wl) and not args.two_call
+    bench = Bench(wl, R, seed=1000, select_in_attention=fused)
 
     def timed(op, steps, warmup):
         """ms per launch of `op` over exactly `steps` launches (after `warmup` untimed ones),
@@ -596,17 +609,23 @@ def main():
     log("[bench] capturing the step graph")
     ms_step = timed("step", args.steps, args.warmup)
     ops = ["compress", "attention"] + (["index_topk"] if wl.indexer else [])
+    # with the selection inside the attention, the indexer op produces the scores only
+    label = {"index_topk": "index_scores", "attention": "attention_select"} if fused else {}
     op_ms = {}
     for op in ops:
         op_ms[op] = timed(op, args.steps, args.warmup)
-        log(f"[bench] {op}: {op_ms[op] * 1e3:.2f} us")
+        log(f"[bench] {label.get(op, op)}: {op_ms[op] * 1e3:.2f} us")
     by = algo_bytes(wl, n_vis)
     qps = wl.B / (ms_step * 1e-3)
     step_gbs = by["step"] / (ms_step * 1e-3) / 1e9
     # the roofline entry is the attention entry point (its main kernel plus, when a query's
     # rows are split over blocks, the merge kernel): the largest share of the step
     dom = "attention"
-    dom_gbs = by[dom] / (op_ms[dom] * 1e-3) / 1e9
+    dom_bytes = by[dom]
+    if fused:
+        # the attention launch reads every visible entry's score instead of the selected ids
+        dom_bytes += wl.B * (n_vis * 4 - min(wl.topk, n_vis) * 4)
+    dom_gbs = dom_bytes / (op_ms[dom] * 1e-3) / 1e9
     traffic = measured_traffic(wl.name)
     log(f"[bench] step {ms_step * 1e3:.2f} us, {qps:,.0f} q/s, {step_gbs:.0f} GB/s "
         f"({100 * step_gbs / HBM_PEAK_GBS:.1f}% of HBM)")
@@ -625,9 +644,12 @@ def main():
         "algorithmic_bytes_per_step": by["step"],
         "roofline": {"bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "hcs_sparse_mla_decode (mla_heads_kernel<512> + mla_combine_kernel<512>)",
-                     "algorithmic_bytes_per_launch": by[dom], "us_per_launch": op_ms[dom] * 1e3},
-        "ops_us": {k: v * 1e3 for k, v in op_ms.items()},
+                     "kernel": ("hcs_sparse_mla_decode_select (mla_heads_kernel<512, select> + "
+                                "mla_combine_kernel<512>)") if fused else
+                               "hcs_sparse_mla_decode (mla_heads_kernel<512> + mla_combine_kernel<512>)",
+                     "algorithmic_bytes_per_launch": dom_bytes, "us_per_launch": op_ms[dom] * 1e3},
+        "ops_us": {label.get(k, k): v * 1e3 for k, v in op_ms.items()},
+        "select_in_attention": fused,
     }
     del bench
     torch.cuda.empty_cache()

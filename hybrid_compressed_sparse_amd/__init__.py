@@ -63,6 +63,13 @@ def lib() -> ctypes.CDLL:
         L.hcs_index_topk_compress.argtypes = [vp, vp, vp, Paged, vp, vp, i32, i32, i32, i32, i32, i32,
                                               vp, vp, vp, sz, vp, vp, i32, i64, vp, vp, i32, i32, i32,
                                               i32, vp, vp, Paged, vp]
+        L.hcs_index_scores_compress.restype = i32
+        L.hcs_index_scores_compress.argtypes = [vp, vp, vp, Paged, vp, vp, i32, i32, i32, i32, i32, vp, i64,
+                                                vp, vp, i32, i64, vp, vp, i32, i32, i32, i32, vp, vp, Paged,
+                                                vp]
+        L.hcs_sparse_mla_decode_select.restype = i32
+        L.hcs_sparse_mla_decode_select.argtypes = [vp, Paged, Paged, vp, i64, i32, vp, vp, vp, i32, i32,
+                                                   i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
         L.hcs_sparse_mla_workspace_size.restype = sz
         L.hcs_sparse_mla_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.hcs_sparse_mla_decode.restype = i32
@@ -331,6 +338,36 @@ def index_topk_compress(q, q_scale: Optional[torch.Tensor], w: torch.Tensor, key
         _ptr(state, torch.float32, "state"), _as_paged(comp), _stream()), "index_topk_compress")
 
 
+def index_scores_compress(q, q_scale: Optional[torch.Tensor], w: torch.Tensor, keys, q_seq: torch.Tensor,
+                          q_pos: torch.Tensor, m_ix: int, max_pos: int, scores: torch.Tensor,
+                          kv: Optional[torch.Tensor] = None, score: Optional[torch.Tensor] = None,
+                          cu_new: Optional[torch.Tensor] = None, start_pos: Optional[torch.Tensor] = None,
+                          state: Optional[torch.Tensor] = None, comp=None, m: int = 1,
+                          ape: Optional[torch.Tensor] = None, max_new: Optional[int] = None) -> None:
+    """hcs_index_scores_compress: the indexer scores float32 [N, >= n_visible] (no top-k) and,
+    when kv is given, compress_kv(kv .. m, ape) of the same decode step in the same launch."""
+    N, H_I = w.shape
+    d_I = keys.dim
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
+        raise TypeError("scores must be float32 [N, stride] with unit column stride")
+    B = 0
+    in_dtype, row_stride, d = 0, 0, 0
+    if kv is not None:
+        if kv.dtype != score.dtype or kv.dtype not in IN_DTYPE:
+            raise TypeError("kv and score must both be bf16 or both float32")
+        if max_new is None:
+            raise ValueError("max_new (host bound of new tokens per sequence) is required")
+        B, in_dtype, row_stride, d = start_pos.shape[0], IN_DTYPE[kv.dtype], kv.stride(0), kv.shape[-1]
+    _check(lib().hcs_index_scores_compress(
+        _ptr(q, name="q"), _ptr(q_scale, name="q_scale"), _ptr(w, torch.float32, "w"),
+        _as_paged(keys), _ptr(q_seq, torch.int32, "q_seq"), _ptr(q_pos, torch.int32, "q_pos"),
+        N, H_I, d_I, m_ix, max_pos, scores.data_ptr(), scores.stride(0),
+        _ptr(kv, name="kv"), _ptr(score, name="score"), in_dtype, row_stride,
+        _ptr(cu_new, torch.int32, "cu_new"), _ptr(start_pos, torch.int32, "start_pos"),
+        B, max_new or 0, d, m, _ptr(ape, torch.float32, "ape"), _ptr(state, torch.float32, "state"),
+        _as_paged(comp) if comp is not None else Paged(), _stream()), "index_scores_compress")
+
+
 # ------------------------------------------------------------------------------ attention
 
 def sparse_mla_workspace_size(N: int, H: int, d: int, window: int, m: int, topk: int, max_pos: int) -> int:
@@ -352,6 +389,28 @@ def sparse_mla_decode(q: torch.Tensor, swa, comp, topk_idx: Optional[torch.Tenso
         _ptr(sink, torch.float32, "sink"), N, H, d, window, m, max_pos, scale,
         _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _ptr(ws, name="ws"),
         0 if ws is None else ws.numel() * ws.element_size(), _stream()), "sparse_mla_decode")
+
+
+def sparse_mla_decode_select(q: torch.Tensor, swa, comp, scores: torch.Tensor, topk: int,
+                             q_seq: torch.Tensor, q_pos: torch.Tensor, window: int, m: int, max_pos: int,
+                             scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                             sel_idx: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None,
+                             ws: Optional[torch.Tensor] = None) -> None:
+    """hcs_sparse_mla_decode_select: CSA decode attention that takes each query's top-k of the
+    indexer scores (float32 [N, >= n_visible]) itself; sel_idx int32 [N, topk] receives the
+    selected ids in ascending order (-1 padded) when given."""
+    N, H, d = q.shape
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
+        raise TypeError("scores must be float32 [N, stride] with unit column stride")
+    if ws is None:
+        ws = _workspace(sparse_mla_workspace_size(N, H, d, window, m, topk, max_pos), q.device)
+    _check(lib().hcs_sparse_mla_decode_select(
+        _ptr(q, torch.bfloat16, "q"), _as_paged(swa), _as_paged(comp), scores.data_ptr(), scores.stride(0),
+        topk, _ptr(q_seq, torch.int32, "q_seq"), _ptr(q_pos, torch.int32, "q_pos"),
+        _ptr(sink, torch.float32, "sink"), N, H, d, window, m, max_pos, scale,
+        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"),
+        _ptr(sel_idx, torch.int32, "sel_idx"), _ptr(ws, name="ws"),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream()), "sparse_mla_decode_select")
 
 
 def sparse_mla_prefill_workspace_size(Q: int, H: int, d: int, window: int, m: int, topk: int, P0: int) -> int:

@@ -274,21 +274,19 @@ size_t hcs_index_topk_workspace_size(int N, int max_pos, int m, int topk) {
   return hcs::topk_plan(N, max_pos, m, topk).ws_bytes;
 }
 
-// Checks shared by the indexer entry points; fills `a` and `plan` (nothing is launched; N == 0
-// returns HCS_OK with a.N 0). q_seq == NULL means a chunk of queries of sequence `seq` at
-// positions P0 .. P0+N-1.
-static hcs_status prep_index(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
-                             const int32_t* q_seq, const int32_t* q_pos, int seq, int P0, int N,
-                             int H_I, int d_I, int m, int topk, int max_pos, int32_t* out_idx,
-                             void* ws, size_t ws_bytes, hcs::IndexArgs& a, hcs::TopkPlan& plan) {
+// Checks shared by the indexer entry points that do not depend on the selection; fills `a`
+// except its scores and selection fields. q_seq == NULL means a chunk of queries of sequence
+// `seq` at positions P0 .. P0+N-1.
+static hcs_status prep_index_args(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
+                                  const int32_t* q_seq, const int32_t* q_pos, int seq, int P0, int N,
+                                  int H_I, int d_I, int m, int max_pos, hcs::IndexArgs& a) {
   a = hcs::IndexArgs{};
   if (N < 0) return fail(HCS_ERR_INVALID_ARG, "N must be >= 0");
   if (H_I < 1 || H_I > 64) return fail(HCS_ERR_UNSUPPORTED, "H_I must be in 1..64");
   if (m < 1) return fail(HCS_ERR_INVALID_ARG, "m must be >= 1");
-  if (topk < 1 || topk > 4096) return fail(HCS_ERR_UNSUPPORTED, "topk must be in 1..4096");
   if (max_pos < 0) return fail(HCS_ERR_INVALID_ARG, "max_pos must be >= 0");
   if (N == 0) return HCS_OK;
-  if (!q || !w || !out_idx) return fail(HCS_ERR_INVALID_ARG, "null q, w or out_idx");
+  if (!q || !w) return fail(HCS_ERR_INVALID_ARG, "null q or w");
   hcs_status s = check_paged(keys, "keys", d_I, false, true);
   if (s != HCS_OK) return s;
   if (keys.fmt == HCS_FMT_BF16 && d_I != 32 && d_I != 64 && d_I != 128)
@@ -301,10 +299,6 @@ static hcs_status prep_index(const void* q, const uint8_t* q_scale, const float*
   if ((int64_t)keys.pt_stride * HCS_PAGE_ROWS < (int64_t)(max_pos + 1) / m)
     return fail(HCS_ERR_INVALID_ARG, "keys: pt_stride %d does not cover %d entries", keys.pt_stride,
                 (max_pos + 1) / m);
-  plan = hcs::topk_plan(N, max_pos, m, topk);
-  if (!ws || ws_bytes < plan.ws_bytes)
-    return fail(HCS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.ws_bytes, ws_bytes);
-  if (!aligned(ws, 256)) return fail(HCS_ERR_INVALID_ARG, "ws must be 256-byte aligned");
   a.q = static_cast<const uint8_t*>(q);
   a.q_scale = q_scale;
   a.w = w;
@@ -319,6 +313,23 @@ static hcs_status prep_index(const void* q, const uint8_t* q_scale, const float*
   a.m = m;
   a.pos_cap = max_pos;
   a.nv_cap = (max_pos + 1) / m;
+  return HCS_OK;
+}
+
+// Checks shared by the indexer entry points with a selection; fills `a` and `plan` (nothing is
+// launched; N == 0 returns HCS_OK with a.N 0).
+static hcs_status prep_index(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
+                             const int32_t* q_seq, const int32_t* q_pos, int seq, int P0, int N,
+                             int H_I, int d_I, int m, int topk, int max_pos, int32_t* out_idx,
+                             void* ws, size_t ws_bytes, hcs::IndexArgs& a, hcs::TopkPlan& plan) {
+  if (topk < 1 || topk > 4096) return fail(HCS_ERR_UNSUPPORTED, "topk must be in 1..4096");
+  hcs_status s = prep_index_args(q, q_scale, w, keys, q_seq, q_pos, seq, P0, N, H_I, d_I, m, max_pos, a);
+  if (s != HCS_OK || N == 0) return s;
+  if (!out_idx) return fail(HCS_ERR_INVALID_ARG, "null out_idx");
+  plan = hcs::topk_plan(N, max_pos, m, topk);
+  if (!ws || ws_bytes < plan.ws_bytes)
+    return fail(HCS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.ws_bytes, ws_bytes);
+  if (!aligned(ws, 256)) return fail(HCS_ERR_INVALID_ARG, "ws must be 256-byte aligned");
   a.scores = static_cast<float*>(ws);
   a.score_stride = (int64_t)(plan.score_bytes / sizeof(float) / N);
   a.topk = topk;
@@ -455,6 +466,45 @@ hcs_status hcs_index_topk_compress(const void* q, const uint8_t* q_scale, const 
   return run_topk(a, plan, keys.fmt, topk, out_idx, out_score, ws, stream);
 }
 
+hcs_status hcs_index_scores_compress(const void* q, const uint8_t* q_scale, const float* w,
+                                     hcs_paged keys, const int32_t* q_seq, const int32_t* q_pos, int N,
+                                     int H_I, int d_I, int m_ix, int max_pos, float* scores,
+                                     int64_t score_stride, const void* kv, const void* score,
+                                     int in_dtype, int64_t row_stride, const int32_t* cu_new,
+                                     const int32_t* start_pos, int B, int max_new, int d, int m,
+                                     const float* ape, float* state, hcs_paged comp, void* stream) {
+  if (N > 0 && (!q_seq || !q_pos)) return fail(HCS_ERR_INVALID_ARG, "null q_seq or q_pos");
+  hcs::IndexArgs a;
+  hcs_status s = prep_index_args(q, q_scale, w, keys, q_seq, q_pos, 0, 0, N, H_I, d_I, m_ix, max_pos, a);
+  if (s != HCS_OK) return s;
+  if (N > 0) {
+    if (!scores || !aligned(scores, 4)) return fail(HCS_ERR_INVALID_ARG, "scores must be a non-null float32 buffer");
+    if (score_stride < a.nv_cap)
+      return fail(HCS_ERR_INVALID_ARG, "score_stride %lld < %d visible entries", (long long)score_stride, a.nv_cap);
+    a.scores = scores;
+    a.score_stride = score_stride;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hcs::CompressArgs c;
+  if (B > 0) {
+    s = prep_compress(kv, score, in_dtype, row_stride, cu_new, start_pos, B, max_new, d, m, ape, state,
+                      comp, nullptr, 0, c);
+    if (s != HCS_OK) return s;
+    if (N > 0 && comp.base == keys.base) return fail(HCS_ERR_INVALID_ARG, "comp and keys must be different caches");
+  } else if (B < 0) {
+    return fail(HCS_ERR_INVALID_ARG, "B must be >= 0");
+  }
+  if (N == 0) return B > 0 ? hip_status(hcs::launch_compress(c, max_new, st), "compress_kv") : ok();
+  hipError_t e;
+  if (B > 0 && keys.fmt == HCS_FMT_BF16 && a.nv_cap <= 32768)
+    e = hcs::launch_index_scores_compress(a, c, max_new, st);
+  else {
+    e = B > 0 ? hcs::launch_compress(c, max_new, st) : hipSuccess;
+    if (e == hipSuccess) e = hcs::launch_index_scores(a, keys.fmt, st);
+  }
+  return hip_status(e, "index_scores_compress");
+}
+
 // ------------------------------------------------------------------------------ attention
 static hcs_status check_attn(const void* q, const hcs_paged& swa, const hcs_paged& comp,
                              const int32_t* topk_idx, int topk, int N, int H, int d, int window,
@@ -539,6 +589,51 @@ hcs_status hcs_sparse_mla_decode(const void* q, hcs_paged swa, hcs_paged comp,
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   return run_attn(a, d, swa.fmt, comp.fmt, window, m, a.topk, max_pos, ws, ws_bytes, stream);
+}
+
+hcs_status hcs_sparse_mla_decode_select(const void* q, hcs_paged swa, hcs_paged comp,
+                                        const float* scores, int64_t score_stride, int topk,
+                                        const int32_t* q_seq, const int32_t* q_pos, const float* sink,
+                                        int N, int H, int d, int window, int m, int max_pos,
+                                        float scale, void* out, float* lse, int32_t* sel_idx,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  if (topk < 1 || topk > 4096) return fail(HCS_ERR_UNSUPPORTED, "topk must be in 1..4096");
+  hcs_status s = check_attn(q, swa, comp, nullptr, topk, N, H, d, window, m, out);
+  if (s != HCS_OK) return s;
+  if (max_pos < 0) return fail(HCS_ERR_INVALID_ARG, "max_pos must be >= 0");
+  if (N == 0) return ok();
+  if (d != 512 || swa.fmt != HCS_FMT_BF16 || comp.fmt != HCS_FMT_BF16)
+    return fail(HCS_ERR_UNSUPPORTED, "selection inside the attention needs d = 512 and bf16 caches");
+  const int nv_cap = (max_pos + 1) / m;
+  if (nv_cap > hcs::kSelMax)
+    return fail(HCS_ERR_UNSUPPORTED, "selection inside the attention takes at most %d visible entries, got %d",
+                hcs::kSelMax, nv_cap);
+  if (!q_seq || !q_pos) return fail(HCS_ERR_INVALID_ARG, "null q_seq or q_pos");
+  if (!scores || !aligned(scores, 4)) return fail(HCS_ERR_INVALID_ARG, "scores must be a non-null float32 buffer");
+  if (score_stride < nv_cap)
+    return fail(HCS_ERR_INVALID_ARG, "score_stride %lld < %d visible entries", (long long)score_stride, nv_cap);
+  hcs::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.swa = hcs::to_paged(swa);
+  a.comp = hcs::to_paged(comp);
+  a.topk_idx = nullptr;
+  a.topk = topk;
+  a.scores = scores;
+  a.score_stride = score_stride;
+  a.sel_out = sel_idx;
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.sink = sink;
+  a.N = N;
+  a.H = H;
+  a.window = window;
+  a.m = m;
+  a.pos_cap = max_pos;
+  a.nv_cap = nv_cap;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  return run_attn(a, d, swa.fmt, comp.fmt, window, m, topk, max_pos, ws, ws_bytes, stream);
 }
 
 size_t hcs_sparse_mla_prefill_workspace_size(int Q, int H, int d, int window, int m, int topk, int P0) {

@@ -27,6 +27,7 @@
 // are exact in bf16). The head
 // groups of a query run on one XCD, so a row fetched by one of them is an L2 hit for the others.
 #include "kernels.h"
+#include "select.h"
 
 namespace hcs {
 
@@ -75,7 +76,7 @@ __device__ __forceinline__ QueryRows query_rows(const AttnArgs& a, int t) {
   q.lo = max(0, q.pos - a.window + 1);
   q.n_swa = a.window > 0 ? q.pos - q.lo + 1 : 0;
   q.nv = min((q.pos + 1) / a.m, a.nv_cap);
-  q.n_comp = a.topk_idx ? a.topk : q.nv;
+  q.n_comp = a.topk_idx || a.scores ? a.topk : q.nv;
   q.R = q.n_swa + q.n_comp;
   return q;
 }
@@ -174,6 +175,138 @@ __device__ __forceinline__ void fill_rows(const AttnArgs& a, int t, const QueryR
     const int npages = is_swa ? a.swa.num_pages : a.comp.num_pages;
     const bool ok = li < n && gr < q.R && ok_id && pg >= 0 && pg < npages;
     if (li < np) rowtab[li] = ok ? ((is_swa ? 0u : 0x80000000u) | (uint32_t)(pg * 64 + (row & 63))) : kNoRow;
+  }
+  wait_vm_zero();     // LDS copies the caller started before (dma16) have landed as well
+  __syncthreads();
+}
+
+// fill_rows for a block that selects its query's compressed rows itself from the indexer scores
+// (a.scores): the top-k of the visible entries' scores, by the same exact radix select as the
+// indexer's selection kernels (ties at the k-th score go to the smaller ids), or every visible
+// entry when there are at most k. The selected ids are ordered by id, so that every split of the
+// query computes the same row order and takes its own range of it. `scratch` is LDS of
+// kSelScratch bytes that nothing else uses until the caller's next barrier; rowtab[0 .. n
+// rounded up to `pad`) is written; ends with a barrier. Split 0 writes the ids to a.sel_out.
+constexpr int kSelScratch = 4 * kSelMax + 17 * 1024 + kSelMax;   // keys, SelShared, id flags
+static_assert(sizeof(SelShared) <= 17 * 1024, "selection scratch layout");
+
+template <int NT>
+__device__ __forceinline__ void fill_rows_sel(const AttnArgs& a, int t, int s, const QueryRows& q, int r0,
+                                              int n, uint32_t* rowtab, int* ptl, int pad, uint8_t* scratch) {
+  constexpr int RPT = (kMaxRowsWG + NT - 1) / NT;
+  constexpr int PPT = kPtCache / NT;
+  constexpr int IPT = kSelMax / NT;              // scores per thread in the loads
+  uint32_t* kl = reinterpret_cast<uint32_t*>(scratch);
+  SelShared& sh = *reinterpret_cast<SelShared*>(scratch + 4 * kSelMax);
+  uint8_t* flag = scratch + 4 * kSelMax + 17 * 1024;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nv = q.nv, k = a.topk;
+  const int npg = (nv + 63) >> 6;
+  const bool cached = npg <= kPtCache;
+  const int32_t* cpt = a.comp.pt + (int64_t)q.seq * a.comp.pt_stride;
+  const int32_t* spt = a.swa.pt + (int64_t)q.seq * a.swa.pt_stride;
+  const float* sc = a.scores + (int64_t)t * a.score_stride;
+  // ---- every load at once: compressed page table, window rows' pages, the scores
+  int pv[PPT];
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int idx = tid + j * NT;
+    pv[j] = cached && idx < npg ? __ldg(cpt + idx) : 0;
+  }
+  int spg[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int gr = r0 + tid + i * NT;
+    spg[i] = gr < q.n_swa ? __ldg(spt + ((q.lo + gr) >> 6)) : 0;
+  }
+  float sv[IPT];
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const int i = tid + j * NT;
+    sv[j] = i < nv ? __ldg(sc + i) : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int idx = tid + j * NT;
+    if (idx < npg && cached) ptl[idx] = pv[j];
+  }
+  const bool all = nv <= k;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const int i = tid + j * NT;
+    kl[i] = f32_order_key(sv[j]);
+    flag[i] = all && i < nv ? 1 : 0;
+  }
+  const int np = min((n + pad - 1) / pad * pad, kMaxRowsWG);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int li = tid + i * NT;
+    if (li < np) rowtab[li] = kNoRow;
+  }
+  sel_reset<NT>(sh);
+  __syncthreads();
+  if (!all)
+    block_topk<NT>(
+        sh, nv, k, [&](int i, uint32_t& key) { key = kl[i]; return true; }, [&](int i) { return i; },
+        [&](unsigned, int id, uint32_t) { flag[id] = 1; });      // ends with a barrier
+  // ---- position of each selected id in id order: exclusive prefix of the flag counts
+  constexpr int FPT = kSelMax / NT;              // ids per thread in the scan
+  static_assert(FPT % 4 == 0, "the scan reads 4 id flags per word");
+  const int i0 = tid * FPT;
+  uint32_t fw[FPT / 4];
+  unsigned cnt = 0;
+#pragma unroll
+  for (int j = 0; j < FPT / 4; ++j) {
+    fw[j] = *reinterpret_cast<const uint32_t*>(flag + i0 + 4 * j);
+    cnt += (unsigned)__popc(fw[j]);                 // flags are 0 / 1 bytes
+  }
+  const uint64_t below = (1ull << lane) - 1;
+  unsigned run = 0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) run += (unsigned)__popcll(__ballot((cnt >> b) & 1u) & below) << b;
+  if (lane == 63) sh.wsum[wave] = run + cnt;
+  __syncthreads();
+  unsigned total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const unsigned ws = sh.wsum[w];
+    run += w < wave ? ws : 0u;
+    total += ws;
+  }
+  int32_t* out = a.sel_out && s == 0 ? a.sel_out + (int64_t)t * k : nullptr;
+#pragma unroll
+  for (int j = 0; j < FPT; ++j) {
+    if ((fw[j >> 2] >> (8 * (j & 3))) & 1u) {
+      const int li = q.n_swa + (int)run - r0;
+      if (li >= 0 && li < n) rowtab[li] = (uint32_t)(i0 + j);
+      if (out) out[run] = i0 + j;
+      ++run;
+    }
+  }
+  if (out)
+    for (int j = (int)total + tid; j < k; j += NT) out[j] = -1;
+  __syncthreads();
+  // ---- ids -> row entries (each thread converts the entries it owns)
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int li = tid + i * NT;
+    if (li >= np) continue;
+    const int gr = r0 + li;
+    uint32_t e = kNoRow;
+    if (li < n && gr < q.R) {
+      if (gr < q.n_swa) {
+        const int pg = spg[i];
+        const int row = q.lo + gr;
+        if (pg >= 0 && pg < a.swa.num_pages) e = (uint32_t)(pg * 64 + (row & 63));
+      } else {
+        const uint32_t id = rowtab[li];
+        if (id != kNoRow) {
+          const int pg = cached ? ptl[id >> 6] : __ldg(cpt + (id >> 6));
+          if (pg >= 0 && pg < a.comp.num_pages) e = 0x80000000u | (uint32_t)(pg * 64 + (id & 63));
+        }
+      }
+    }
+    rowtab[li] = e;
   }
   wait_vm_zero();     // LDS copies the caller started before (dma16) have landed as well
   __syncthreads();
@@ -682,7 +815,7 @@ constexpr int kHeadsThreads = 512;
 // s_waitcnt vmcnt(n) (gfx9 encoding, n < 16): expcnt and lgkmcnt not waited for
 #define HCS_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
-template <int D>
+template <int D, bool SEL>
 __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a) {
   constexpr int RS = D * 2, KS = D / 32;
   constexpr int BT = 32;                          // rows per block
@@ -695,6 +828,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   constexpr int NLD = WRL / RPI;                  // async loads per wave per block
   constexpr int PD = 4;                           // K-fragment steps read ahead in S^T
   static_assert(CTO >= 1 && NLD >= 1 && NLD < 16 && KS % PD == 0, "unsupported head dim");
+  static_assert(!SEL || 2 * TB >= kSelScratch, "the row selection's scratch lives in tiles 0-1");
   // tiles 2 and 3 first hold q of the 64 heads (64 rows of RS bytes)
   __shared__ __attribute__((aligned(16))) uint8_t tiles[4 * TB];
   __shared__ __attribute__((aligned(16))) uint32_t rowtab[kMaxRowsWG];
@@ -736,7 +870,8 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       dma16v(src + ch * 16, lds_addr(qstage) + (8 * wave + i * QHPI) * RS);
     }
   }
-  fill_rows<kHeadsThreads>(a, t, q, r0, n_rows, rowtab, ptl, BT);
+  if constexpr (SEL) fill_rows_sel<kHeadsThreads>(a, t, s, q, r0, n_rows, rowtab, ptl, BT, tiles);
+  else fill_rows<kHeadsThreads>(a, t, q, r0, n_rows, rowtab, ptl, BT);
   const int nblk = (n_rows + BT - 1) / BT;
 
   // async loads: wave w fills rows WRL w .. +WRL-1 of a block; LDS chunk slot c of row r
@@ -981,7 +1116,13 @@ hipError_t launch_impl(const AttnArgs& a, hipStream_t stream) {
   const int n8 = (a.N + 7) / 8;
   dim3 grid((unsigned)(n8 * 8 * a.nsplit * a.n_hg));
   if constexpr (SF == HCS_FMT_BF16) {
-    hipLaunchKernelGGL((mla_heads_kernel<D>), grid, dim3(kHeadsThreads), 0, stream, a);
+    if (!a.scores) {
+      hipLaunchKernelGGL((mla_heads_kernel<D, false>), grid, dim3(kHeadsThreads), 0, stream, a);
+    } else if constexpr (D == 512) {
+      hipLaunchKernelGGL((mla_heads_kernel<D, true>), grid, dim3(kHeadsThreads), 0, stream, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else {
     static_assert(D == QuantStage<SF, CF>::D, "quantized rows are 512 wide");
     hipLaunchKernelGGL((mla_fp8_kernel<QuantStage<SF, CF>>), grid, dim3(kThreads), 0, stream, a);
@@ -1002,12 +1143,16 @@ AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos
   const int hpb = p.kind == 2 ? 64 : 16;
   p.n_hg = (H + hpb - 1) / hpb;
   p.n_h16 = (H + 15) / 16;
-  constexpr int64_t kBlock = 64;                       // both kernels walk 64 rows at a time
+  // rows per block: 64 in the 16-head kernel, 32 in the all-heads kernel; splits are whole blocks
+  const int64_t kBlock = p.kind == 2 ? 32 : 64;
   const int64_t blocks = std::max<int64_t>(1, (rows + kBlock - 1) / kBlock);
   const int64_t max_bps = kMaxRowsWG / kBlock;
   const int64_t per_split = (int64_t)((N + 7) / 8) * 8 * p.n_hg;
+  // enough splits to give every CU a block, but (all-heads kernel) at least four blocks each:
+  // a split adds 64 KiB of partial stores and merge reads per query
+  const int64_t min_bps = p.kind == 2 ? 4 : 1;
   int64_t nsplit = std::max<int64_t>(1, (256 + per_split - 1) / per_split);
-  nsplit = std::min(nsplit, blocks);
+  nsplit = std::min(nsplit, std::max<int64_t>(1, blocks / min_bps));
   nsplit = std::max<int64_t>(nsplit, (blocks + max_bps - 1) / max_bps);
   const int64_t bps = (blocks + nsplit - 1) / nsplit;
   nsplit = (blocks + bps - 1) / bps;

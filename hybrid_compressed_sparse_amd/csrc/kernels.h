@@ -24,7 +24,16 @@ struct AttnArgs {
   uint16_t* ws_o;             // [N, n_h16, nsplit, 16, D] bf16 partial outputs, each
                               // normalised by its split's sum (nsplit > 1)
   float* ws_ml;               // [N, n_h16, nsplit, 16, 2] partial (max, sum), log2 units
+  // rows selected by the kernel itself (topk_idx == nullptr): the top-k of each query's indexer
+  // scores [N, score_stride] over its visible entries; the selected ids in ascending order go
+  // to sel_out [N, topk] (-1 padded) when it is set
+  const float* scores;
+  int64_t score_stride;
+  int32_t* sel_out;
 };
+
+// Most visible entries a query may have when the attention kernel selects its own rows.
+constexpr int kSelMax = 8192;
 
 struct AttnPlan {
   int kind, nsplit, n_hg, n_h16, rows_per_split;

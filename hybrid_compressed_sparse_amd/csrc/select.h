@@ -1,0 +1,268 @@
+// Exact top-k selection helpers shared by the indexer's selection kernels and the attention
+// kernel that selects its own rows from indexer scores: radix select of the k-th largest
+// order key with LDS histograms, and the emission of the selected ids (ties at the k-th key go
+// to the smaller ids). Included by one translation unit each (internal linkage).
+#pragma once
+
+#include "common.h"
+
+namespace hcs {
+namespace {
+// ---------------------------------------------------------------- radix select
+constexpr int kDigitBits = 11;                 // radix digit: 2048 bins
+constexpr int kBins = 1 << kDigitBits;
+
+constexpr int kCandMax = 64;            // a k-th key bin this small is resolved by ranking
+
+struct SelShared {
+  unsigned hist[2][kBins];               // pass p counts into hist[p & 1]; the other is cleared
+  unsigned wsum[16];                     // per-wave bin totals of a pass
+  unsigned bin, above, cnt_bin;
+  unsigned kmax, kmin, count;            // range and number of the participating keys
+  unsigned out_count;
+  uint32_t cand_key[kCandMax];           // the keys of the k-th key's bin, and their ids
+  int cand_id[kCandMax];
+  unsigned cand_count;
+};
+
+// Wave-wide reductions through DPP row operations (no LDS round trips); every lane gets the result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return ~wave_max_u32(~v);
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Clears what radix_kth expects cleared; the caller puts a barrier between this and the call.
+// NT is the block's thread count (a multiple of 64, 256..1024) in all the selection helpers.
+template <int NT>
+__device__ __forceinline__ void sel_reset(SelShared& sh) {
+  for (int j = threadIdx.x; j < kBins; j += NT) sh.hist[0][j] = 0;
+  if (threadIdx.x == 0) {
+    sh.kmax = 0u;
+    sh.kmin = ~0u;
+    sh.count = 0u;
+  }
+}
+
+struct KthResult {
+  uint32_t prefix, mask;                 // keys with (key & mask) > prefix are above the k-th
+  unsigned need, n_eq;                   // of the n_eq keys with (key & mask) == prefix, need belong
+};
+
+// Radix select of the k-th largest key among the participating elements (1 <= k <= their
+// number). Keys first agree on a common leading part (the range min ^ max), so the digits start
+// below it: 11 bits per pass, stopping once the bin holding the k-th key holds exactly the keys
+// still needed (then every key of that bin is taken, no further digit is needed; with 2048 bins
+// this is usually the first pass). One barrier for the range, three per pass. Expects
+// sel_reset() state; leaves it reset (ordered by the caller's next barrier).
+template <int NT, class KeyOf>
+__device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of, unsigned small_bin = 0) {
+  static_assert(NT % 64 == 0 && NT >= 256 && NT <= 1024 && kBins % NT == 0, "block size");
+  constexpr int BPT = kBins / NT;        // bins per thread in the scan
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // ---- range and count of the participating keys
+  uint32_t lmax = 0u, lmin = ~0u;
+  unsigned lcnt = 0;
+  for (int i = tid; i < n; i += NT) {
+    uint32_t key;
+    if (key_of(i, key)) {
+      lmax = max(lmax, key);
+      lmin = min(lmin, key);
+      ++lcnt;
+    }
+  }
+  lmax = wave_max_u32(lmax);
+  lmin = wave_min_u32(lmin);
+  lcnt = wave_sum_u32(lcnt);
+  if (lane == 0) {
+    atomicMax(&sh.kmax, lmax);
+    atomicMin(&sh.kmin, lmin);
+    atomicAdd(&sh.count, lcnt);
+  }
+  __syncthreads();
+  const uint32_t kmax = sh.kmax, diff = kmax ^ sh.kmin;
+  const unsigned total = sh.count;
+  KthResult r;
+  if (diff == 0u) {                      // all participating keys are equal
+    __syncthreads();                     // every thread has read the range
+    if (tid == 0) {
+      sh.kmax = 0u;
+      sh.kmin = ~0u;
+      sh.count = 0u;
+    }
+    r.prefix = kmax;
+    r.mask = ~0u;
+    r.need = k;
+    r.n_eq = total;
+    return r;
+  }
+  int top = 31 - __builtin_clz(diff);    // highest bit where the keys differ
+  uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
+  uint32_t prefix = kmax & mask;
+  unsigned remaining = k, cnt_bin = total;
+  for (int pass = 0; top >= 0; ++pass) {
+    const int width = min(kDigitBits, top + 1);
+    const int shift = top - width + 1;
+    unsigned* hist = sh.hist[pass & 1];
+    for (int i = tid; i < n; i += NT) {
+      uint32_t key;
+      if (key_of(i, key) && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (kBins - 1)], 1u);
+    }
+    __syncthreads();
+    // thread i owns bins kBins-1-BPT*i .. kBins-BPT*i (descending); exclusive prefix of the
+    // threads' totals = the wave's prefix (from ballots of the totals' bits) + earlier waves'
+    unsigned c[BPT], tot = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      c[j] = hist[kBins - 1 - BPT * tid - j];
+      tot += c[j];
+    }
+    const uint64_t below = (1ull << lane) - 1;
+    unsigned run = 0;
+#pragma unroll
+    for (int b = 0; b < 17; ++b) run += (unsigned)__popcll(__ballot((tot >> b) & 1u) & below) << b;
+    if (lane == 63) sh.wsum[wave] = run + tot;
+    for (int j = tid; j < kBins; j += NT) sh.hist[(pass & 1) ^ 1][j] = 0;   // the next pass's
+    __syncthreads();
+    {
+      const unsigned ws = lane < wave ? sh.wsum[lane] : 0u;   // lower waves' totals
+      run += wave_sum_u32(ws);
+    }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      if (run < remaining && run + c[j] >= remaining) {
+        sh.bin = kBins - 1 - BPT * tid - j;
+        sh.above = run;
+        sh.cnt_bin = c[j];
+      }
+      run += c[j];
+    }
+    __syncthreads();
+    prefix |= sh.bin << shift;
+    mask |= ((1u << width) - 1u) << shift;
+    remaining -= sh.above;
+    cnt_bin = sh.cnt_bin;
+    top = shift - 1;
+    // hist[pass & 1] was counted into; clear it for a later pass or call (ordered by the
+    // barriers that follow before any reuse)
+    for (int j = tid; j < kBins; j += NT) hist[j] = 0;
+    if (cnt_bin == remaining || cnt_bin <= small_bin) break;
+  }
+  if (tid == 0) {                        // range state for a later call
+    sh.kmax = 0u;
+    sh.kmin = ~0u;
+    sh.count = 0u;
+  }
+  r.prefix = prefix;
+  r.mask = mask;
+  r.need = remaining;
+  r.n_eq = cnt_bin;
+  return r;
+}
+
+// Select the top-k of n elements (n > k) given key_of(i, key) and id_of(i); writes k ids (and
+// scores) in arbitrary order. Ties at the k-th key go to the smaller ids.
+// The radix passes stop as soon as the bin holding the k-th key has at most kCandMax keys;
+// those candidates are gathered and ranked by one wave (larger key first, then smaller id), and
+// the r.need best are taken with every key above the bin. Only a larger bin of keys that are
+// all equal to the k-th falls back to a second select on ~id.
+template <int NT, class KeyOf, class IdOf, class Emit>
+__device__ void block_topk(SelShared& sh, int n, int k, KeyOf key_of, IdOf id_of, Emit emit) {
+  const KthResult r = radix_kth<NT>(sh, n, (unsigned)k, key_of, kCandMax);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t below = (1ull << lane) - 1;
+  const bool partial = r.n_eq > r.need;            // only part of the k-th key's bin is taken
+  const bool ranked = partial && r.n_eq <= (unsigned)kCandMax;
+  // ties of more than kCandMax equal keys (every bit resolved): the r.need smallest ids, i.e.
+  // the largest ~id
+  KthResult r2{};
+  if (partial && !ranked) {
+    __syncthreads();
+    r2 = radix_kth<NT>(
+        sh, n, r.need,
+        [&](int i, uint32_t& key) {
+          uint32_t kk;
+          if (!key_of(i, kk) || (kk & r.mask) != r.prefix) return false;
+          key = ~(uint32_t)id_of(i);
+          return true;
+        });
+  }
+  if (threadIdx.x == 0) {
+    sh.out_count = 0;
+    sh.cand_count = 0;
+  }
+  __syncthreads();
+  // keys above the bin (and the whole bin unless only part of it is taken); the bin's keys go
+  // to the candidate slots when they are ranked. One counter update per wave.
+  for (int i0 = threadIdx.x & ~63; i0 < n; i0 += NT) {
+    const int i = i0 + lane;
+    uint32_t key = 0;
+    bool take = false, cand = false;
+    if (i < n && key_of(i, key)) {
+      const uint32_t km = key & r.mask;
+      take = km > r.prefix;
+      if (km == r.prefix) {
+        if (!partial) take = true;
+        else if (ranked) cand = true;
+        else take = ((~(uint32_t)id_of(i)) & r2.mask) >= r2.prefix;     // ids are distinct
+      }
+    }
+    const uint64_t tm = __ballot(take);
+    if (tm != 0) {
+      unsigned base = 0;
+      if (lane == __builtin_ctzll(tm)) base = atomicAdd(&sh.out_count, (unsigned)__popcll(tm));
+      base = __shfl(base, __builtin_ctzll(tm), 64);
+      if (take) emit(base + (unsigned)__popcll(tm & below), id_of(i), key);
+    }
+    if (ranked) {
+      const uint64_t cm = __ballot(cand);
+      if (cm != 0) {
+        unsigned base = 0;
+        if (lane == __builtin_ctzll(cm)) base = atomicAdd(&sh.cand_count, (unsigned)__popcll(cm));
+        base = __shfl(base, __builtin_ctzll(cm), 64);
+        if (cand) {
+          const unsigned slot = base + (unsigned)__popcll(cm & below);
+          sh.cand_key[slot] = key;
+          sh.cand_id[slot] = id_of(i);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (ranked && wave == 0) {
+    // rank of candidate `lane` among the n_eq (all in LDS now): larger key first, then smaller id
+    const int nc = (int)r.n_eq;
+    const uint32_t mk = lane < nc ? sh.cand_key[lane] : 0u;
+    const int mi = lane < nc ? sh.cand_id[lane] : 0;
+    unsigned rank = 0;
+    for (int j = 0; j < nc; ++j) {
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, j);
+      const int ij = __builtin_amdgcn_readlane(mi, j);
+      rank += (kj > mk || (kj == mk && ij < mi)) ? 1u : 0u;
+    }
+    const bool take = lane < nc && rank < r.need;
+    const uint64_t tm = __ballot(take);
+    const unsigned base = sh.out_count;           // every other key is counted by now
+    if (take) emit(base + (unsigned)__popcll(tm & below), mi, mk);
+  }
+  __syncthreads();
+}
+
+}  // namespace
+}  // namespace hcs

@@ -3,8 +3,10 @@
 This is the order of a compressed attention layer's step on the DeepSeek-V4 pages ("Code
 Reading Map", Phase 2 then Phase 3): the compressor stores the step's completed entries, the
 indexer selects compressed entries for each query, and the attention reads both caches. The
-class only owns the output and workspace buffers and calls the three C entry points in order
-on the current stream; no arithmetic happens here.
+class only owns the output and workspace buffers and calls the C entry points in order on the
+current stream; no arithmetic happens here. At CSA decode the top-k may instead be taken inside
+the attention launch from the indexer's scores (hcs_index_scores_compress, then
+hcs_sparse_mla_decode_select): the same selection, one launch fewer.
 """
 from __future__ import annotations
 
@@ -13,9 +15,12 @@ from typing import Optional
 
 import torch
 
-from . import compress_kv, index_topk, index_topk_chunk, index_topk_compress, \
-    index_topk_workspace_size, sparse_mla_decode, sparse_mla_prefill_chunk, \
+from . import compress_kv, index_scores_compress, index_topk, index_topk_chunk, index_topk_compress, \
+    index_topk_workspace_size, sparse_mla_decode, sparse_mla_decode_select, sparse_mla_prefill_chunk, \
     sparse_mla_prefill_workspace_size, sparse_mla_workspace_size
+
+# most visible entries per query that hcs_sparse_mla_decode_select selects among
+SELECT_MAX_VISIBLE = 8192
 
 
 @dataclass
@@ -33,10 +38,19 @@ class StepShape:
 
 
 class PathStep:
-    """Buffers for one step of a given shape, reused across calls."""
+    """Buffers for one step of a given shape, reused across calls. select_in_attention: at CSA
+    decode with d = 512 and bf16 caches, take the top-k inside the attention launch (raises if the
+    shape does not allow it)."""
 
-    def __init__(self, shape: StepShape, device="cuda"):
+    def __init__(self, shape: StepShape, device="cuda", select_in_attention: bool = False):
         s = self.shape = shape
+        self.fused = select_in_attention
+        if self.fused and not (s.topk and not s.prefill and s.d == 512
+                               and (s.max_pos + 1) // s.m <= SELECT_MAX_VISIBLE):
+            raise ValueError("selection inside the attention needs CSA decode, d = 512 and at most "
+                             f"{SELECT_MAX_VISIBLE} visible entries")
+        self.scores = torch.empty((s.N, (s.max_pos + 1) // s.m), dtype=torch.float32,
+                                  device=device) if self.fused else None
         self.out = torch.empty((s.N, s.H, s.d), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((s.N, s.H), dtype=torch.float32, device=device)
         self.idx = torch.empty((s.N, max(s.topk, 1)), dtype=torch.int32, device=device) if s.topk else None
@@ -54,8 +68,11 @@ class PathStep:
                     max_new=max_new)
 
     def select(self, ix_q, ix_q_scale, ix_w, ix_keys, q_seq, q_pos):
+        """The indexer: top-k ids into self.idx, or (select_in_attention) the scores only."""
         s = self.shape
-        if s.prefill:
+        if self.fused:
+            index_scores_compress(ix_q, ix_q_scale, ix_w, ix_keys, q_seq, q_pos, s.m, s.max_pos, self.scores)
+        elif s.prefill:
             index_topk_chunk(ix_q, ix_q_scale, ix_w, ix_keys, s.seq, s.P0, s.m, s.topk, self.idx,
                              self.score, ws=self.ix_ws)
         else:
@@ -65,7 +82,11 @@ class PathStep:
     def attend(self, q, swa, comp, q_seq=None, q_pos=None, sink=None, topk_idx=None):
         s = self.shape
         idx = topk_idx if topk_idx is not None else self.idx
-        if s.prefill:
+        if self.fused and topk_idx is None:
+            sparse_mla_decode_select(q, swa, comp, self.scores, s.topk, q_seq, q_pos, s.window, s.m,
+                                     s.max_pos, s.d ** -0.5, self.out, self.lse, sel_idx=self.idx,
+                                     sink=sink, ws=self.at_ws)
+        elif s.prefill:
             sparse_mla_prefill_chunk(q, swa, comp, idx, s.seq, s.P0, s.window, s.m, s.d ** -0.5,
                                      self.out, self.lse, sink=sink, ws=self.at_ws)
         else:
@@ -80,7 +101,11 @@ class PathStep:
         streams instead measured slower inside a captured graph on MI355X, where the cross-stream
         joins cost more than the compressor."""
         s = self.shape
-        if s.topk and not s.prefill and dbg is None:
+        if self.fused and dbg is None:
+            index_scores_compress(ix_q, ix_q_scale, ix_w, ix_keys, q_seq, q_pos, s.m, s.max_pos, self.scores,
+                                  c_kv, c_score, c_cu, c_start, c_state, comp, s.m, ape=ape,
+                                  max_new=c_max_new)
+        elif s.topk and not s.prefill and dbg is None:
             index_topk_compress(ix_q, ix_q_scale, ix_w, ix_keys, q_seq, q_pos, s.m, s.topk, s.max_pos,
                                 self.idx, self.score, self.ix_ws, c_kv, c_score, c_cu, c_start, c_state,
                                 comp, s.m, ape=ape, max_new=c_max_new)

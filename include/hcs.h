@@ -17,9 +17,12 @@
  *                             the top blocks of compressed positions);
  *   hcs_index_topk_compress   hcs_index_topk and hcs_compress_kv of one decode step in one
  *                             launch (they touch disjoint data);
+ *   hcs_index_scores_compress the indexer's scores without the top-k (and the compressor);
  *   hcs_sparse_mla_decode     single-KV-head attention of every query head over the query's
  *                             sliding window plus its selected (CSA) or all visible (HCA)
  *                             compressed entries, K = V = the shared row;
+ *   hcs_sparse_mla_decode_select  the same for CSA with the top-k of the indexer scores taken
+ *                             inside the attention launch;
  *   hcs_sparse_mla_prefill_chunk  the same for a chunk of consecutive queries of one sequence;
  *   hcs_qnorm_rope_kv_insert  readies the new tokens' query heads (optional per-head RMSNorm,
  *                             RoPE) and writes their rotated KV rows into the sliding-window
@@ -269,6 +272,25 @@ hcs_status hcs_index_topk_compress(const void* q, const uint8_t* q_scale, const 
                                    const float* ape, float* state, hcs_paged comp, void* stream);
 
 /* ------------------------------------------------------------------------------------ */
+/* The indexer's scores without the selection ("Code Reading Map", "Aux stream 0 (CSA     */
+/* only)": the per-entry scores the top-k is taken over), optionally with the KV          */
+/* compressor of the same decode step in the same launch, as in hcs_index_topk_compress.  */
+/* For query t: scores[t, i] = sum_h w[t,h] * ReLU(q[t,h] . k_i) for i < n_visible(q_pos[t])*/
+/* with the arithmetic of hcs_index_topk (entries from n_visible on are not written).     */
+/* With B > 0 it is also hcs_compress_kv(kv .. comp) with dbg = NULL; B = 0 only scores,  */
+/* N = 0 only compresses. hcs_sparse_mla_decode_select consumes the scores.               */
+/* scores   [N, score_stride] float32, score_stride >= (max_pos + 1) / m_ix.              */
+/* Errors: those of hcs_index_topk (without topk, out_idx and ws) and of hcs_compress_kv; */
+/* nothing is launched if either set of arguments fails.                                  */
+hcs_status hcs_index_scores_compress(const void* q, const uint8_t* q_scale, const float* w,
+                                     hcs_paged keys, const int32_t* q_seq, const int32_t* q_pos, int N,
+                                     int H_I, int d_I, int m_ix, int max_pos, float* scores,
+                                     int64_t score_stride, const void* kv, const void* score,
+                                     int in_dtype, int64_t row_stride, const int32_t* cu_new,
+                                     const int32_t* start_pos, int B, int max_new, int d, int m,
+                                     const float* ape, float* state, hcs_paged comp, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
 /* Sparse MLA decode (single shared KV head, MQA).                                        */
 /* "Code Reading Map", "Phase 3: forward_mqa()" and "Concrete Trace": each query head     */
 /* attends over the query's sliding-window rows plus its selected compressed entries      */
@@ -297,6 +319,29 @@ hcs_status hcs_sparse_mla_decode(const void* q, hcs_paged swa, hcs_paged comp,
                                  const int32_t* q_pos, const float* sink, int N, int H, int d,
                                  int window, int m, int max_pos, float scale, void* out,
                                  float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
+/* hcs_sparse_mla_decode for CSA with the selection inside the attention launch: query    */
+/* t's compressed rows are the top-k of its indexer scores scores[t, i], i < n_visible,   */
+/* chosen exactly as hcs_index_topk chooses them ("Code Reading Map", "Aux stream 0": the */
+/* top-k of the per-entry scores; ties at the k-th score to the smaller ids, every       */
+/* visible entry when there are at most topk), so the attended set is that of            */
+/* hcs_index_topk followed by hcs_sparse_mla_decode. Each workgroup of a query selects     */
+/* the same set and attends its share of it in id order; the result equals the two-call  */
+/* path up to the order of the floating-point sums.                                       */
+/* scores   [N, score_stride] float32 (hcs_index_scores_compress), score_stride >=        */
+/*          n_visible(max_pos).                                                           */
+/* sel_idx  [N, topk] int32 or NULL: the selected ids in ascending order, -1 padded.      */
+/* Other arguments as for hcs_sparse_mla_decode; ws: hcs_sparse_mla_workspace_size(N, H,  */
+/* d, window, m, topk, max_pos) bytes.                                                    */
+/* Constraints: d = 512, bf16 swa and comp, 1 <= topk <= 4096 and n_visible(max_pos) <=   */
+/* 8192, else HCS_ERR_UNSUPPORTED (use hcs_index_topk and hcs_sparse_mla_decode).         */
+hcs_status hcs_sparse_mla_decode_select(const void* q, hcs_paged swa, hcs_paged comp,
+                                        const float* scores, int64_t score_stride, int topk,
+                                        const int32_t* q_seq, const int32_t* q_pos, const float* sink,
+                                        int N, int H, int d, int window, int m, int max_pos,
+                                        float scale, void* out, float* lse, int32_t* sel_idx,
+                                        void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------ */
 /* Sparse MLA for a prefill chunk: hcs_sparse_mla_decode for the Q consecutive queries    */

@@ -58,9 +58,10 @@ def test_validation_errors_before_any_launch():
                                  4, 100, 0.1, 16, None, None, 0, None)
     assert st == 1 and b"pt_stride" in L.hcs_last_error()
     # attention: workspace too small when the row list is split
-    need = L.hcs_sparse_mla_workspace_size(4, 64, 512, 128, 4, 0, 200)
+    need = L.hcs_sparse_mla_workspace_size(4, 64, 512, 128, 4, 0, 2000)
     assert need > 0
-    st = L.hcs_sparse_mla_decode(16, _paged(), _paged(), None, 0, 16, 16, None, 4, 64, 512, 128, 4, 200,
+    st = L.hcs_sparse_mla_decode(16, _paged(stride=32), _paged(stride=32), None, 0, 16, 16, None, 4, 64, 512,
+                                 128, 4, 2000,
                                  0.1, 16, None, 256, need - 1, None)
     assert st == 3
     # indexer: top-k limits and formats
