@@ -48,6 +48,23 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 __attribute__((address_space(3)))*)(p));
 }
 
+// max of v over lanes l, l ^ 16, l ^ 32, l ^ 48, in every lane, with two VALU lane swaps
+// (v_permlane16_swap / v_permlane32_swap of v with itself give v and the partner lane's value).
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// the same for a sum: (v_l + v_{l^16}) + (v_{l^32} + v_{l^48})
+__device__ __forceinline__ float sum_xor16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
@@ -835,7 +852,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   __shared__ int ptl[kPtCache];
   __shared__ __attribute__((aligned(16))) __bf16 p_lds[2][64 * PR];
   __shared__ float alpha_lds[2][64];
-  __shared__ int flags[2][4];
+  __shared__ __attribute__((aligned(16))) int flags[2][4];
   __shared__ float hm[64], hl[64];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -880,38 +897,53 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
     return e != kNoRow ? ((e >> 31) ? a.comp.base : a.swa.base) + (size_t)(e & 0x7fffffffu) * RS
                        : g_zero_row;
   };
-  auto issue = [&](int b) {
-    uint8_t* tb = tiles + (b & 3) * TB;
+  // A block's copies in two halves: the source addresses come from the row table (fixed after
+  // the prologue), so they are read before a step's waits; the copies themselves are issued
+  // after its barrier, once their tile is free. RPI == 1: one row per copy, the address
+  // wave-uniform; otherwise each lane has its own row's address.
+  struct RowSrc { const uint8_t* p[NLD]; };
+  auto prep = [&](int b) {
+    RowSrc r;
     const uint32_t* at = rowtab + b * BT + WRL * wave;
     if constexpr (RPI == 1) {
-      // lane j < WRL reads the entry of row j; each load takes it from that lane
+      // lane j < WRL reads the entry of row j; each copy takes it from that lane
       const uint32_t my = at[lane & (WRL - 1)];
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const uint8_t* src = row_ptr((uint32_t)__builtin_amdgcn_readlane((int)my, i));
-        const int sw = swz_dec((WRL * wave + i) & 15);
-        dma16(src, (uint32_t)((lane ^ sw) * 16), lds_addr(tb) + (WRL * wave + i) * RS);
-      }
+      for (int i = 0; i < NLD; ++i) r.p[i] = row_ptr((uint32_t)__builtin_amdgcn_readlane((int)my, i));
     } else {
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const int rl = i * RPI + lane / LPR;
-        const uint8_t* src = row_ptr(at[rl]);
         const int sw = swz_dec((WRL * wave + rl) & 15);
-        dma16v(src + (((lane % LPR) ^ sw) * 16), lds_addr(tb) + (WRL * wave + i * RPI) * RS);
+        r.p[i] = row_ptr(at[rl]) + (((lane % LPR) ^ sw) * 16);
+      }
+    }
+    return r;
+  };
+  auto fire = [&](int b, const RowSrc& r) {
+    uint8_t* tb = tiles + (b & 3) * TB;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      if constexpr (RPI == 1) {
+        const int sw = swz_dec((WRL * wave + i) & 15);
+        dma16(r.p[i], (uint32_t)((lane ^ sw) * 16), lds_addr(tb) + (WRL * wave + i) * RS);
+      } else {
+        dma16v(r.p[i], lds_addr(tb) + (WRL * wave + i * RPI) * RS);
       }
     }
   };
-  if (nblk > 0) issue(0);
-  if (nblk > 1) issue(1);
+  if (nblk > 0) fire(0, prep(0));
+  if (nblk > 1) fire(1, prep(1));
   // top of block step i: this wave's copies of block i have landed (those of block i+1 may
   // still be in flight), then the barrier makes every wave's copies and the previous step's
-  // LDS writes visible
+  // LDS writes visible, and block i+2's copies go into the tile that block i-2 left
   auto step_sync = [&](int i) {
+    RowSrc r{};
+    if (i + 2 < nblk) r = prep(i + 2);
     if (i + 1 < nblk) HCS_WAIT_VMCNT(NLD);
     else wait_vm_zero();
     lds_barrier();
-    if (i + 2 < nblk) issue(i + 2);
+    if (i + 2 < nblk) fire(i + 2, r);
   };
 
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -964,8 +996,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
           x[mt][e] = ((valid >> row) & 1u) ? sacc[mt][e] * a.scale_log2 : kNegInf;
           tmax = fmaxf(tmax, x[mt][e]);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = max_xor16_32(tmax);
       const bool any_over = __any(tmax > m_ref + kLazyBlock);
       if (any_over) {
         // rare: new reference maxima for this wave's heads
@@ -991,8 +1022,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
         *(bf16x4*)(prow + mt * 16) = p4;
       }
     }
-    float lt = l_part + __shfl_xor(l_part, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = sum_xor16_32(l_part);
     if (g == 0) {
       hl[16 * wave + l16] = lt;
       hm[16 * wave + l16] = m_ref;
@@ -1018,15 +1048,8 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       const int b = i - 1;
       const uint8_t* T = tiles + (b & 3) * TB;
       const int pb = b & 1;
-      // rescale the heads whose reference max moved in block b
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        if (flags[pb][nt]) {
-          const float al = alpha_lds[pb][16 * nt + l16];
-#pragma unroll
-          for (int ct = 0; ct < CTO; ++ct) oacc[ct][nt] *= al;
-        }
-      }
+      // the S waves' rescale flags of block b (one read), issued with the operand reads below
+      const i32x4 fl = *reinterpret_cast<const i32x4*>(&flags[pb][0]);
       auto vload = [&](int ct) {
         const int ctg = ow * CTO + ct;
         const uint8_t* vb = T + vrow + 32 * ((ctg & 7) ^ vx) + (ctg >> 3) * 256;
@@ -1041,6 +1064,17 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       bf16x8 vf[VD];
 #pragma unroll
       for (int ct = 0; ct < VD; ++ct) vf[ct] = vload(ct);
+      // rescale the heads whose reference max moved in block b (rare)
+      if (fl.x | fl.y | fl.z | fl.w) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          if (fl[nt]) {
+            const float al = alpha_lds[pb][16 * nt + l16];
+#pragma unroll
+            for (int ct = 0; ct < CTO; ++ct) oacc[ct][nt] *= al;
+          }
+        }
+      }
 #pragma unroll
       for (int ct = 0; ct < CTO; ++ct) {
         __builtin_amdgcn_sched_barrier(0);
