@@ -832,7 +832,7 @@ constexpr int kHeadsThreads = 512;
 // s_waitcnt vmcnt(n) (gfx9 encoding, n < 16): expcnt and lgkmcnt not waited for
 #define HCS_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
-template <int D, bool SEL>
+template <int D, bool SEL, bool PAIR>
 __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a) {
   constexpr int RS = D * 2, KS = D / 32;
   constexpr int BT = 32;                          // rows per block
@@ -853,7 +853,9 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   __shared__ __attribute__((aligned(16))) __bf16 p_lds[2][64 * PR];
   __shared__ float alpha_lds[2][64];
   __shared__ __attribute__((aligned(16))) int flags[2][4];
-  __shared__ float hm[64], hl[64];
+  __shared__ float hm[64], hl[2][64];
+  __shared__ float pmax[4][32];                   // S waves' block maxima, per head pair
+  __shared__ int pseq[4];                         // S waves' step counters
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -887,6 +889,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       dma16v(src + ch * 16, lds_addr(qstage) + (8 * wave + i * QHPI) * RS);
     }
   }
+  if (tid < 4) pseq[tid] = 0;                     // ordered by the row table's barriers
   if constexpr (SEL) fill_rows_sel<kHeadsThreads>(a, t, s, q, r0, n_rows, rowtab, ptl, BT, tiles);
   else fill_rows<kHeadsThreads>(a, t, q, r0, n_rows, rowtab, ptl, BT);
   const int nblk = (n_rows + BT - 1) / BT;
@@ -949,83 +952,186 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   const bool split = a.nsplit > 1;
   if (wave < 4) {
-    // ================= S waves: heads hbase + 16 wave + l16
-    bf16x8 qreg[KS];
+    if constexpr (!PAIR) {
+      // ================= S waves: heads hbase + 16 wave + l16
+      bf16x8 qreg[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qreg[ks] = *(const bf16x8*)(qstage + (16 * wave + l16) * RS + (((4 * ks + g) ^ l16) << 4));
-    // K row 16 mt + l16, chunk (4ks + g) ^ s = 4 (ks ^ (s >> 2)) + ((g ^ s) & 3), s = swz_dec(l16)
-    const int sk = swz_dec(l16);
-    int ko4[4];
+      for (int ks = 0; ks < KS; ++ks)
+        qreg[ks] = *(const bf16x8*)(qstage + (16 * wave + l16) * RS + (((4 * ks + g) ^ l16) << 4));
+      // K row 16 mt + l16, chunk (4ks + g) ^ s = 4 (ks ^ (s >> 2)) + ((g ^ s) & 3), s = swz_dec(l16)
+      const int sk = swz_dec(l16);
+      int ko4[4];
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) ko4[k4] = l16 * RS + ((g ^ sk) & 3) * 16 + 64 * (k4 ^ (sk >> 2));
-    float m_ref = kNegInf, l_part = 0.f;
-    for (int i = 0; i <= nblk; ++i) {
-      step_sync(i);
-      if (i == nblk) break;
-      const uint8_t* T = tiles + (i & 3) * TB;
-      const int pb = i & 1;
-      const uint32_t valid = (uint32_t)__ballot(rowtab[i * BT + (lane & 31)] != kNoRow);
-      // ---- S^T[32 rows][16 heads], K fragments read PD k-steps ahead of their MFMAs
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      bf16x8 kf[PD][2];
-      auto kload = [&](int ks, bf16x8* f) {
-        const int ko = ko4[ks & 3] + (ks >> 2) * 256;
-        f[0] = *(const bf16x8*)(T + ko);
-        f[1] = *(const bf16x8*)(T + ko + 16 * RS);
-      };
+      for (int k4 = 0; k4 < 4; ++k4) ko4[k4] = l16 * RS + ((g ^ sk) & 3) * 16 + 64 * (k4 ^ (sk >> 2));
+      float m_ref = kNegInf, l_part = 0.f;
+      for (int i = 0; i <= nblk; ++i) {
+        step_sync(i);
+        if (i == nblk) break;
+        const uint8_t* T = tiles + (i & 3) * TB;
+        const int pb = i & 1;
+        const uint32_t valid = (uint32_t)__ballot(rowtab[i * BT + (lane & 31)] != kNoRow);
+        // ---- S^T[32 rows][16 heads], K fragments read PD k-steps ahead of their MFMAs
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        bf16x8 kf[PD][2];
+        auto kload = [&](int ks, bf16x8* f) {
+          const int ko = ko4[ks & 3] + (ks >> 2) * 256;
+          f[0] = *(const bf16x8*)(T + ko);
+          f[1] = *(const bf16x8*)(T + ko + 16 * RS);
+        };
 #pragma unroll
-      for (int ks = 0; ks < PD; ++ks) kload(ks, kf[ks]);
+        for (int ks = 0; ks < PD; ++ks) kload(ks, kf[ks]);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % PD][mt], qreg[ks], sacc[mt], 0, 0, 0);
+          if (ks + PD < KS) kload(ks + PD, kf[ks % PD]);
+        }
         __builtin_amdgcn_sched_barrier(0);
+        // ---- online softmax over the block's rows (this wave owns its heads' rows)
+        float x[2][4];
+        float tmax = kNegInf;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-          sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % PD][mt], qreg[ks], sacc[mt], 0, 0, 0);
-        if (ks + PD < KS) kload(ks + PD, kf[ks % PD]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- online softmax over the block's rows (this wave owns its heads' rows)
-      float x[2][4];
-      float tmax = kNegInf;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = mt * 16 + 4 * g + e;
-          x[mt][e] = ((valid >> row) & 1u) ? sacc[mt][e] * a.scale_log2 : kNegInf;
-          tmax = fmaxf(tmax, x[mt][e]);
+          for (int e = 0; e < 4; ++e) {
+            const int row = mt * 16 + 4 * g + e;
+            x[mt][e] = ((valid >> row) & 1u) ? sacc[mt][e] * a.scale_log2 : kNegInf;
+            tmax = fmaxf(tmax, x[mt][e]);
+          }
+        tmax = max_xor16_32(tmax);
+        const bool any_over = __any(tmax > m_ref + kLazyBlock);
+        if (any_over) {
+          // rare: new reference maxima for this wave's heads
+          const float mnew = tmax > m_ref + kLazy ? tmax : m_ref;
+          // 0 when m_ref = -inf; 1 for a head with no row yet (-inf - -inf would be NaN)
+          const float alpha = mnew == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_ref - mnew);
+          l_part *= alpha;
+          m_ref = mnew;
+          if (g == 0) alpha_lds[pb][16 * wave + l16] = alpha;
         }
-      tmax = max_xor16_32(tmax);
-      const bool any_over = __any(tmax > m_ref + kLazyBlock);
-      if (any_over) {
-        // rare: new reference maxima for this wave's heads
-        const float mnew = tmax > m_ref + kLazy ? tmax : m_ref;
-        // 0 when m_ref = -inf; 1 for a head with no row yet (-inf - -inf would be NaN)
-        const float alpha = mnew == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_ref - mnew);
-        l_part *= alpha;
-        m_ref = mnew;
-        if (g == 0) alpha_lds[pb][16 * wave + l16] = alpha;
-      }
-      if (lane == 0) flags[pb][wave] = any_over ? 1 : 0;
-      const float mr = m_ref == kNegInf ? 0.f : m_ref;
-      __bf16* prow = p_lds[pb] + (16 * wave + l16) * PR + 4 * g;
+        if (lane == 0) flags[pb][wave] = any_over ? 1 : 0;
+        const float mr = m_ref == kNegInf ? 0.f : m_ref;
+        __bf16* prow = p_lds[pb] + (16 * wave + l16) * PR + 4 * g;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        bf16x4 p4;
+        for (int mt = 0; mt < 2; ++mt) {
+          bf16x4 p4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(x[mt][e] - mr);
-          l_part += pv;
-          p4[e] = (__bf16)pv;
+          for (int e = 0; e < 4; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(x[mt][e] - mr);
+            l_part += pv;
+            p4[e] = (__bf16)pv;
+          }
+          *(bf16x4*)(prow + mt * 16) = p4;
         }
-        *(bf16x4*)(prow + mt * 16) = p4;
       }
-    }
-    const float lt = sum_xor16_32(l_part);
-    if (g == 0) {
-      hl[16 * wave + l16] = lt;
-      hm[16 * wave + l16] = m_ref;
+      const float lt = sum_xor16_32(l_part);
+      if (g == 0) {
+        hl[0][16 * wave + l16] = lt;
+        hl[1][16 * wave + l16] = 0.f;
+        hm[16 * wave + l16] = m_ref;
+      }
+    } else {
+      // ================= S waves: wave w takes heads hbase + 32 (w >> 1) + 16 nt + l16 (nt = 0, 1)
+      // over rows 16 (w & 1) .. +15 of each block, so each K fragment read from LDS feeds two
+      // MFMAs. The two waves of a head pair agree on each block's max per head before either
+      // writes its probabilities: each publishes its maxima and a step counter in LDS and waits
+      // for its partner's (a bounded wait; both waves are resident in this workgroup).
+      const int hp = wave >> 1, rh = wave & 1, partner = wave ^ 1;
+      bf16x8 qreg[2][KS];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qreg[nt][ks] = *(const bf16x8*)(qstage + (32 * hp + 16 * nt + l16) * RS + (((4 * ks + g) ^ l16) << 4));
+      // K row 16 rh + l16, chunk (4ks + g) ^ s = 4 (ks ^ (s >> 2)) + ((g ^ s) & 3), s = swz_dec(l16)
+      const int sk = swz_dec(l16);
+      int ko4[4];
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) ko4[k4] = (16 * rh + l16) * RS + ((g ^ sk) & 3) * 16 + 64 * (k4 ^ (sk >> 2));
+      float m_ref[2] = {kNegInf, kNegInf}, l_part[2] = {0.f, 0.f};
+      for (int i = 0; i <= nblk; ++i) {
+        step_sync(i);
+        if (i == nblk) break;
+        const uint8_t* T = tiles + (i & 3) * TB;
+        const int pb = i & 1;
+        const uint32_t valid = (uint32_t)__ballot(rowtab[i * BT + 16 * rh + (lane & 15)] != kNoRow) & 0xFFFFu;
+        // ---- S^T[16 rows][32 heads], K fragments read PD k-steps ahead of their MFMAs
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        bf16x8 kf[PD];
+        auto kload = [&](int ks) { return *(const bf16x8*)(T + ko4[ks & 3] + (ks >> 2) * 256); };
+#pragma unroll
+        for (int ks = 0; ks < PD; ++ks) kf[ks] = kload(ks);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % PD], qreg[nt][ks], sacc[nt], 0, 0, 0);
+          if (ks + PD < KS) kf[ks % PD] = kload(ks + PD);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- online softmax: lane (g, l16) holds rows 4g .. 4g+3 of this wave's 16 for head
+        // 32 hp + 16 nt + l16
+        float x[2][4], tmax[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          tmax[nt] = kNegInf;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[nt][e] = ((valid >> (4 * g + e)) & 1u) ? sacc[nt][e] * a.scale_log2 : kNegInf;
+            tmax[nt] = fmaxf(tmax[nt], x[nt][e]);
+          }
+          tmax[nt] = max_xor16_32(tmax[nt]);
+        }
+        // the partner wave's maxima of block i (LDS operations of one wave complete in order, so
+        // a partner step count of i + 1 means its maxima of block i are in place)
+        if (g == 0) {
+          pmax[wave][l16] = tmax[0];
+          pmax[wave][16 + l16] = tmax[1];
+        }
+        if (lane == 0) pseq[wave] = i + 1;
+        for (int spin = 0; spin < (1 << 16); ++spin) {
+          if (__builtin_amdgcn_readfirstlane(((volatile int*)pseq)[partner]) > i) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+        tmax[0] = fmaxf(tmax[0], ((volatile float*)pmax[partner])[l16]);
+        tmax[1] = fmaxf(tmax[1], ((volatile float*)pmax[partner])[16 + l16]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          // the same decision in both waves of the pair (same maxima, same history)
+          const bool any_over = __any(tmax[nt] > m_ref[nt] + kLazyBlock);
+          if (any_over) {
+            // rare: new reference maxima for these heads
+            const float mnew = tmax[nt] > m_ref[nt] + kLazy ? tmax[nt] : m_ref[nt];
+            // 0 when m_ref = -inf; 1 for a head with no row yet (-inf - -inf would be NaN)
+            const float alpha = mnew == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_ref[nt] - mnew);
+            l_part[nt] *= alpha;
+            m_ref[nt] = mnew;
+            if (rh == 0 && g == 0) alpha_lds[pb][32 * hp + 16 * nt + l16] = alpha;
+          }
+          if (rh == 0 && lane == 0) flags[pb][2 * hp + nt] = any_over ? 1 : 0;
+          const float mr = m_ref[nt] == kNegInf ? 0.f : m_ref[nt];
+          bf16x4 p4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(x[nt][e] - mr);
+            l_part[nt] += pv;
+            p4[e] = (__bf16)pv;
+          }
+          *(bf16x4*)(p_lds[pb] + (32 * hp + 16 * nt + l16) * PR + 16 * rh + 4 * g) = p4;
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float lt = sum_xor16_32(l_part[nt]);
+        if (g == 0) {
+          hl[rh][32 * hp + 16 * nt + l16] = lt;
+          if (rh == 0) hm[32 * hp + 16 * nt + l16] = m_ref[nt];
+        }
+      }
     }
     __syncthreads();                                // (E1) per-head (max, sum) published
     __syncthreads();                                // (E2) O waves have staged the output
@@ -1104,7 +1210,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int hh = hbase + 16 * nt + l16;
-      float M = hm[16 * nt + l16], L = hl[16 * nt + l16];
+      float M = hm[16 * nt + l16], L = hl[0][16 * nt + l16] + hl[1][16 * nt + l16];
       if (split && g == 0 && ow == 0 && hh < a.H) {
         const int64_t prow16 = ((int64_t)(t * a.n_h16 + hh / 16) * a.nsplit + s) * 16 + (hh & 15);
         a.ws_ml[prow16 * 2 + 0] = M;
@@ -1150,10 +1256,14 @@ hipError_t launch_impl(const AttnArgs& a, hipStream_t stream) {
   const int n8 = (a.N + 7) / 8;
   dim3 grid((unsigned)(n8 * 8 * a.nsplit * a.n_hg));
   if constexpr (SF == HCS_FMT_BF16) {
-    if (!a.scores) {
-      hipLaunchKernelGGL((mla_heads_kernel<D, false>), grid, dim3(kHeadsThreads), 0, stream, a);
+    if (!a.q_seq) {
+      // a prefill chunk: many row blocks per workgroup, where the S waves' head pairs (half the
+      // K reads from LDS) pay for their per-block handshake
+      hipLaunchKernelGGL((mla_heads_kernel<D, false, true>), grid, dim3(kHeadsThreads), 0, stream, a);
+    } else if (!a.scores) {
+      hipLaunchKernelGGL((mla_heads_kernel<D, false, false>), grid, dim3(kHeadsThreads), 0, stream, a);
     } else if constexpr (D == 512) {
-      hipLaunchKernelGGL((mla_heads_kernel<D, true>), grid, dim3(kHeadsThreads), 0, stream, a);
+      hipLaunchKernelGGL((mla_heads_kernel<D, true, false>), grid, dim3(kHeadsThreads), 0, stream, a);
     } else {
       return hipErrorInvalidValue;
     }
