@@ -342,10 +342,11 @@ static hcs_status prep_index(const void* q, const uint8_t* q_scale, const float*
   return HCS_OK;
 }
 
-// The selection launch after the scores (entries per scoring block: 512 MXFP4, 256 bf16).
+// The selection launch after the scores (entries per threshold block: 512 FP8; 256 bf16 and
+// MXFP4, whose scoring waves each bound their own 256 entries).
 static hcs_status run_topk(const hcs::IndexArgs& a, const hcs::TopkPlan& plan, int fmt, int topk,
                            int32_t* out_idx, float* out_score, void* ws, void* stream) {
-  const int blk_entries = fmt == HCS_FMT_MXFP4 || fmt == HCS_FMT_FP8IX ? 512 : 256;
+  const int blk_entries = fmt == HCS_FMT_FP8IX ? 512 : 256;     // MXFP4: a threshold per wave
   return hip_status(hcs::launch_topk(a, plan, topk, out_idx, out_score, static_cast<uint8_t*>(ws),
                                      blk_entries, static_cast<hipStream_t>(stream)),
                     "index_topk select");

@@ -6,7 +6,8 @@
 // more entries than k, all of them are selected ("DeepSeek V4.1 attention" API page,
 // short-context rule).
 //
-// Scores: one workgroup scores 256 (bf16) or 512 (MXFP4, FP8) consecutive entries of one query.
+// Scores: one workgroup scores 256 (bf16), 512 (FP8) or 1024 (MXFP4) consecutive entries of one
+// query.
 // The query's heads are the MFMA M dimension. bf16: a wave's 64 entries are one page of the
 // cache, copied whole into LDS with async loads (as is the query), then read in MFMA operand
 // order. MXFP4: the same, two pages per wave, and the cache's 32-value blocks are the MFMA
@@ -132,6 +133,30 @@ __device__ __forceinline__ uint32_t block_kth_key(uint32_t (&keys)[NS], int kb, 
   return *result;
 }
 
+// One wave's kb-th largest key (kb <= kMaxKb) over its lanes' keys[0..NS) (0 for none; every
+// entry held by exactly one lane), in every lane; 0 when the wave holds fewer than kb keys.
+template <int NS>
+__device__ __forceinline__ uint32_t wave_kth_key(uint32_t (&keys)[NS], int kb) {
+  const int lane = threadIdx.x & 63;
+  uint32_t wm = 0u;
+  for (int it = 0; it < kb; ++it) {
+    uint32_t lm = 0;
+    int li = -1;
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      if (keys[j] > lm) {
+        lm = keys[j];
+        li = j;
+      }
+    wm = wave_max_u32(lm);
+    const uint64_t who = __ballot(li >= 0 && lm == wm);
+    const bool mine = who != 0 && lane == (int)__builtin_ctzll(who);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) keys[j] = mine && j == li ? 0u : keys[j];
+  }
+  return wm;
+}
+
 // Scoring blocks call this after writing their scores when a.blk_thr is set: E entries per
 // block, `keys` as for block_kth_key. Writes the block's threshold when the block is full.
 template <int NS, int NW, int E>
@@ -148,6 +173,8 @@ __device__ __forceinline__ void write_block_threshold(const IndexArgs& a, int nv
 // ---------------------------------------------------------------- bf16 scores
 // A zero row for the query heads a launch pads to a multiple of 16.
 __device__ __attribute__((aligned(64))) uint8_t g_ix_zero[1024];
+// A zero page of MXFP4 keys (64 rows of 64 code bytes and 4 scale bytes) for absent pages.
+__device__ __attribute__((aligned(64))) uint8_t g_ix_zero_page[64 * 68];
 
 // Block = 256 entries of one query (4 waves x one 64-entry page each). The page of a wave's
 // entries is one contiguous region of the paged cache, so it is copied into LDS with 1 KiB
@@ -433,12 +460,15 @@ __global__ __launch_bounds__(kChunkThreads, 512 / kChunkThreads) void index_scor
 }
 
 // ---------------------------------------------------------------- MXFP4 scores (d_I = 128)
-// Block = 512 entries of one query: 4 waves x two 64-entry pages. A page (64 x 64 B codes, then
-// 64 x 4 UE8M0 bytes) is one contiguous region of the cache; it is copied into LDS with async
-// loads (the 16-byte code chunks of entry r stored at chunk ^ ((r >> 2) & 3), which makes the
-// operand reads conflict-free), as are the query's codes. Heads are the M dimension of
+// Block = 1024 entries of one query: 4 waves x four 64-entry pages. Heads are the M dimension of
 // v_mfma_scale_f32_16x16x128_f8f6f4, entries the N dimension; a lane's operand is the 16 bytes
-// (32 e2m1 values) of one 32-value block and its scale byte.
+// (32 e2m1 values) of one 32-value block and its scale byte. In the cache's layout (a page is
+// 64 x 64 B codes, then 64 x 4 UE8M0 bytes) the operand of lane (g, l16) for entry r is bytes
+// 16 g .. 16 g + 15 of row r, so the 16 rows of an MFMA are 1 KiB of consecutive bytes: keys go
+// from HBM straight into registers with coalesced loads, no LDS, and a wave has all four of
+// its pages in flight at once (the query's codes likewise, from its contiguous rows).
+constexpr int kMx4BlockEntries = 1024;
+
 template <int MT>
 __global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexArgs a) {
   constexpr int DI = 128;
@@ -446,26 +476,30 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexA
   constexpr int SB = DI / kMxBlock;                              // scale bytes per row
   constexpr int PAGE = kPageRows * (CB + SB);                    // 4352
   constexpr int SCALES = kPageRows * CB;                         // scale region offset
-  constexpr int PPW = 2;                                         // pages per wave
-  __shared__ __attribute__((aligned(16))) uint8_t qc[64 * CB];
-  __shared__ __attribute__((aligned(16))) uint8_t kb[4][PPW][PAGE];
+  constexpr int PPW = kMx4BlockEntries / 4 / kPageRows;          // pages per wave
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   if (a.cand_count && blockIdx.y == 0 && threadIdx.x == 0) a.cand_count[t] = 0u;
-  // query codes: wave w copies heads 16w .. 16w+15 (heads >= H_I read zeros)
-  {
-    const int h = 16 * wave + lane / 4, c = lane % 4;
-    const uint8_t* src = h < a.H_I ? a.q + ((int64_t)t * a.H_I + h) * CB + ((c ^ ((h >> 2) & 3)) << 4)
-                                   : g_ix_zero + lane * 16;
-    __builtin_amdgcn_global_load_lds((const void*)src,
-                                     (__attribute__((address_space(3))) void*)(qc + 16 * wave * CB), 16, 0, 0);
+  int seq, nv;
+  query_of(a, t, seq, nv);
+  const int e_base = blockIdx.y * kMx4BlockEntries + wave * (PPW * 64);   // first entry of the wave
+  // the wave's page ids: lane p < PPW reads page p's table entry
+  int my_pg = -1;
+  if (lane < PPW && e_base + 64 * lane < nv) {
+    const int pg = __ldg(a.keys.pt + (int64_t)seq * a.keys.pt_stride + (e_base >> 6) + lane);
+    my_pg = pg >= 0 && pg < a.keys.num_pages ? pg : -1;
   }
+  // query codes (head mt*16 + l16, block g) and scales, head weights
+  i32x8 qa[MT];
   int qs[MT];
   float wreg[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int h = mt * 16 + l16;
+    const i32x4 v = h < a.H_I ? *(const i32x4*)(a.q + ((int64_t)t * a.H_I + h) * CB + 16 * g)
+                              : i32x4{0, 0, 0, 0};
+    qa[mt] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
     qs[mt] = h < a.H_I ? a.q_scale[((int64_t)t * a.H_I + h) * SB + g] : 127;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -473,58 +507,33 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexA
       wreg[mt][i] = hw < a.H_I ? a.w[(int64_t)t * a.H_I + hw] : 0.f;
     }
   }
-  int seq, nv;
-  query_of(a, t, seq, nv);
-  const int e_base = blockIdx.y * (4 * PPW * 64) + wave * (PPW * 64);   // first entry of the wave
-  // the wave's page ids: lane p < PPW reads page p's table entry
-  int my_pg = -1;
-  if (lane < PPW && e_base + 64 * lane < nv) {
-    const int pg = __ldg(a.keys.pt + (int64_t)seq * a.keys.pt_stride + (e_base >> 6) + lane);
-    my_pg = pg >= 0 && pg < a.keys.num_pages ? pg : -1;
-  }
+  // every key operand of the wave's pages (a page that is not there reads the zero page)
   int pgs[PPW];
+  i32x4 kc[PPW][4];
+  int ksc[PPW][4];
 #pragma unroll
   for (int p = 0; p < PPW; ++p) {
     pgs[p] = __builtin_amdgcn_readlane(my_pg, p);
-    if (pgs[p] < 0) continue;
-    const uint8_t* page = a.keys.base + (int64_t)pgs[p] * PAGE;
-    uint8_t* dst = kb[wave][p];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {                                 // codes: 16 entries per load
-      const int r = 16 * i + lane / 4, c = lane % 4;
-      __builtin_amdgcn_global_load_lds((const void*)(page + r * CB + ((c ^ ((r >> 2) & 3)) << 4)),
-                                       (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
-    }
-    if (lane < 16)                                                // scales: 256 bytes
-      __builtin_amdgcn_global_load_lds((const void*)(page + SCALES + lane * 16),
-                                       (__attribute__((address_space(3))) void*)(dst + SCALES), 16, 0, 0);
-  }
-  __syncthreads();                                                // every copy has landed
-  uint32_t tkeys[PPW * 4];
-#pragma unroll
-  for (int j = 0; j < PPW * 4; ++j) tkeys[j] = 0u;
-  if (e_base < nv) {
-  i32x8 qa[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int h = mt * 16 + l16;
-    const i32x4 v = *(const i32x4*)(qc + h * CB + ((g ^ ((h >> 2) & 3)) << 4));
-    qa[mt] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int p = 0; p < PPW; ++p) {
-    const uint8_t* kp = kb[wave][p];
+    const uint8_t* page = pgs[p] >= 0 ? a.keys.base + (int64_t)pgs[p] * PAGE : g_ix_zero_page;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int r = nt * 16 + l16;
-      const i32x4 kc = *(const i32x4*)(kp + r * CB + ((g ^ ((r >> 2) & 3)) << 4));
-      const int ksc = kp[SCALES + r * SB + g];
-      const i32x8 kbv = {kc.x, kc.y, kc.z, kc.w, 0, 0, 0, 0};
+      kc[p][nt] = *(const i32x4*)(page + r * CB + 16 * g);
+      ksc[p][nt] = page[SCALES + r * SB + g];
+    }
+  }
+  uint32_t tkeys[PPW * 4];
+#pragma unroll
+  for (int p = 0; p < PPW; ++p) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int r = nt * 16 + l16;
+      const i32x8 kbv = {kc[p][nt].x, kc[p][nt].y, kc[p][nt].z, kc[p][nt].w, 0, 0, 0, 0};
       float part = 0.f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kbv, acc, 4, 4, 0, qs[mt], 0, ksc);
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kbv, acc, 4, 4, 0, qs[mt], 0, ksc[p][nt]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) part += wreg[mt][i] * relu(acc[i]);
       }
@@ -535,10 +544,15 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexA
       tkeys[p * 4 + nt] = g == 0 && e < nv ? f32_order_key(sv) : 0u;
     }
   }
-  }
   if (a.blk_thr) {
-    __shared__ uint32_t wbest[4 * kMaxKb + 1];
-    write_block_threshold<PPW * 4, 4, 4 * PPW * 64>(a, nv, tkeys, wbest, wbest + 4 * kMaxKb);
+    // a threshold per wave (its 256 entries are a block of the bound): the kb-th largest key of
+    // a full wave block, kb = ceil(k / full wave blocks of the query); no barrier
+    const int full = nv / (PPW * 64), wb = blockIdx.y * 4 + wave;
+    const int kb = full > 0 ? (a.topk + full - 1) / full : kMaxKb + 1;
+    if (wb < full && kb <= kMaxKb) {
+      const uint32_t kth = wave_kth_key<PPW * 4>(tkeys, kb);
+      if (lane == 0) a.blk_thr[(int64_t)t * a.thr_stride + wb] = kth;
+    }
   }
 }
 
@@ -651,6 +665,24 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_fp8_kernel(IndexArg
   }
 }
 
+// dst[i] = f(src[i]) for i < n (global to LDS), NT threads: eight loads per thread are issued
+// before their stores, at clamped indices (a conditional load would be a branch, and the
+// compiler waits for each such load alone at its merge).
+template <int NT, class T, class F>
+__device__ __forceinline__ void lds_fill(uint32_t* dst, const T* src, int n, F f) {
+  if (n <= 0) return;
+  for (int i0 = 0; i0 < n; i0 += 8 * NT) {
+    T v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[min(i0 + u * NT + (int)threadIdx.x, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * NT + (int)threadIdx.x;
+      if (i < n) dst[i] = f(v[u]);
+    }
+  }
+}
+
 // One query per workgroup: short-context fill or one-stage select over its scores.
 // NT threads, at most KL visible entries.
 template <int NT, int KL>
@@ -671,8 +703,7 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(IndexArgs a, int k, int
     }
     return;
   }
-#pragma unroll 8
-  for (int i = threadIdx.x; i < nv; i += NT) kl[i] = f32_order_key(sc[i]);
+  lds_fill<NT>(kl, sc, nv, [](float v) { return f32_order_key(v); });
   sel_reset<NT>(sh);
   __syncthreads();
   block_topk<NT>(
@@ -701,28 +732,43 @@ __global__ __launch_bounds__(kScoreThreads) void topk_filter_kernel(IndexArgs a,
   if (nv <= a.topk || lo >= nv) return;              // short context: the select fills it directly
   const int full = nv / blk_entries;
   const int kb = full > 0 ? (a.topk + full - 1) / full : kMaxKb + 1;
+  // the block's scores are requested before the threshold is reduced (independent loads)
+  const float* sc = a.scores + (int64_t)t * a.score_stride;
+  const int hi = min(nv, lo + kFilterChunk);
+  constexpr int kPer = kFilterChunk / kScoreThreads;
+  // (loads at clamped indices, results selected after: a conditional load would be a branch,
+  // and every branch merge a wait for that load alone)
+  uint32_t key[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) key[j] = __float_as_uint(sc[min(lo + j * kScoreThreads + (int)threadIdx.x, hi - 1)]);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    key[j] = lo + j * kScoreThreads + (int)threadIdx.x < hi ? f32_order_key(__uint_as_float(key[j])) : 0u;
   uint32_t T = 0u;
   if (kb <= kMaxKb) {
     uint32_t m = ~0u;
-    for (int i = threadIdx.x; i < full; i += kScoreThreads) m = min(m, a.blk_thr[(int64_t)t * a.thr_stride + i]);
+    const uint32_t* thr = a.blk_thr + (int64_t)t * a.thr_stride;
+    for (int i0 = 0; i0 < full; i0 += 8 * kScoreThreads) {
+      uint32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = thr[min(i0 + u * kScoreThreads + (int)threadIdx.x, full - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u * kScoreThreads + (int)threadIdx.x < full) m = min(m, v[u]);
+    }
     m = ~wave_max_u32(~m);
     if (lane == 0) wmin[wave] = m;
     __syncthreads();
     T = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
   }
-  const float* sc = a.scores + (int64_t)t * a.score_stride;
-  const int hi = min(nv, lo + kFilterChunk);
   // keep flags of the block's entries (entry lo + 256 j + tid for j < kPer), one counter update
   // per block: per-wave counts, block prefix in LDS, then every kept entry gets its slot
-  constexpr int kPer = kFilterChunk / kScoreThreads;
   __shared__ unsigned wcnt[kScoreThreads / 64], wbase[kScoreThreads / 64 + 1];
-  uint32_t key[kPer];
   uint64_t km[kPer];
   unsigned mine = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int i = lo + j * kScoreThreads + threadIdx.x;
-    key[j] = i < hi ? f32_order_key(sc[i]) : 0u;
     km[j] = __ballot(i < hi && key[j] >= T);
     mine += (unsigned)__popcll(km[j]);
   }
@@ -795,9 +841,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(IndexArgs a, 
       if (os) os[slot] = order_key_f32(key);
     }
   };
+  auto same = [](uint32_t v) { return v; };
+  if (n <= kSingleMax / 2) {
+    // keys and ids in LDS
+    uint32_t* kid = kl + kSingleMax / 2;
+    lds_fill<kTopkThreads>(kl, ck, n, same);
+    lds_fill<kTopkThreads>(kid, reinterpret_cast<const uint32_t*>(ci), n, same);
+    sel_reset<kTopkThreads>(sh);
+    __syncthreads();
+    block_topk<kTopkThreads>(
+        sh, n, k, [&](int i, uint32_t& key) { key = kl[i]; return true; }, [&](int i) { return (int)kid[i]; },
+        emit);
+    return;
+  }
   if (n <= kSingleMax) {
-#pragma unroll 8
-    for (int i = threadIdx.x; i < n; i += kTopkThreads) kl[i] = ck[i];
+    lds_fill<kTopkThreads>(kl, ck, n, same);
     sel_reset<kTopkThreads>(sh);
     __syncthreads();
     block_topk<kTopkThreads>(
@@ -903,7 +961,7 @@ hipError_t launch_index_scores(const IndexArgs& a, int fmt, hipStream_t stream) 
     return hipGetLastError();
   }
   if (fmt == HCS_FMT_MXFP4) {
-    const int per_wg = 512;
+    const int per_wg = kMx4BlockEntries;
     dim3 grid(a.N, (a.nv_cap + per_wg - 1) / per_wg);
     switch (MT) {
       case 1: hipLaunchKernelGGL((index_score_mxfp4_kernel<1>), grid, dim3(kScoreThreads), 0, stream, a); break;
