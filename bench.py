@@ -646,7 +646,9 @@ def main():
                      "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": ("hcs_sparse_mla_decode_select (mla_heads_kernel<512, select> + "
                                 "mla_combine_kernel<512>)") if fused else
-                               "hcs_sparse_mla_decode (mla_heads_kernel<512> + mla_combine_kernel<512>)",
+                               "hcs_sparse_mla_decode (mla_heads_kernel<512> + mla_combine_kernel<512>)"
+                               if wl.kv_fmt == "bf16" else
+                               "hcs_sparse_mla_decode (mla_fp8_kernel<QuantStage> + mla_combine_kernel<512>)",
                      "algorithmic_bytes_per_launch": dom_bytes, "us_per_launch": op_ms[dom] * 1e3},
         "ops_us": {label.get(k, k): v * 1e3 for k, v in op_ms.items()},
         "select_in_attention": fused,

@@ -33,6 +33,10 @@ namespace hcs {
 
 // A zero row: rows that take part in nothing load from here, so loads never branch.
 __device__ __attribute__((aligned(64))) uint8_t g_zero_row[1024];
+// A page of zeros in every quantised row format (the fp8_ds page is the largest): absent rows
+// are read from it, so the loads of a row never depend on whether the row exists.
+__device__ __attribute__((aligned(64))) uint8_t g_zero_page[kFp8PageBytes];
+static_assert(kFp8PageBytes >= kMx8PageBytes && kFp8PageBytes >= kNv4PageBytes, "zero page size");
 
 namespace {
 
@@ -356,14 +360,14 @@ struct RowFmt;
 template <>
 struct RowFmt<HCS_FMT_FP8DS> {
   static constexpr int PB = kFp8PageBytes;
-  __device__ static __forceinline__ void load(const uint8_t* page, int slot, int lane, i32x4& v, int& se) {
-    const int off = lane < 28 ? kFp8PageCodes + slot * kFp8Latent + lane * 16
-                              : (lane < 36 ? kFp8PageRope + slot * (kFp8Rope * 2) + (lane - 28) * 16
-                                           : kFp8PageCodes + slot * kFp8Latent);
-    const uint8_t* src = page ? page + off : g_zero_row + (lane & 31) * 16;
-    const uint8_t* ssrc = page ? page + kFp8PageScales + slot * 8 + (min(lane, 27) >> 2) : g_zero_row;
-    v = *(const i32x4*)src;
-    se = *ssrc;
+  // byte offsets in the page of the lane's 16-byte load and of its scale byte
+  __device__ static __forceinline__ int voff(int slot, int lane) {
+    const bool rope = lane >= 28 && lane < 36;
+    const int base = rope ? kFp8PageRope + (lane - 28) * 16 : kFp8PageCodes + (lane < 28 ? lane * 16 : 0);
+    return base + slot * (rope ? kFp8Rope * 2 : kFp8Latent);
+  }
+  __device__ static __forceinline__ int soff(int slot, int lane) {
+    return kFp8PageScales + slot * 8 + (min(lane, 27) >> 2);
   }
   __device__ static __forceinline__ void store(uint8_t* row, int sw, int lane, const i32x4& v, int se) {
     const float sc = __builtin_ldexpf(1.f, se - 127);
@@ -389,11 +393,9 @@ struct RowFmt<HCS_FMT_FP8DS> {
 template <>
 struct RowFmt<HCS_FMT_MXFP8> {
   static constexpr int PB = kMx8PageBytes;
-  __device__ static __forceinline__ void load(const uint8_t* page, int slot, int lane, i32x4& v, int& se) {
-    const uint8_t* src = page ? page + slot * 512 + (lane & 31) * 16 : g_zero_row + (lane & 31) * 16;
-    const uint8_t* ssrc = page ? page + kMx8Scales + slot * 16 + ((lane & 31) >> 1) : g_zero_row;
-    v = *(const i32x4*)src;
-    se = *ssrc;
+  __device__ static __forceinline__ int voff(int slot, int lane) { return slot * 512 + (lane & 31) * 16; }
+  __device__ static __forceinline__ int soff(int slot, int lane) {
+    return kMx8Scales + slot * 16 + ((lane & 31) >> 1);
   }
   __device__ static __forceinline__ void store(uint8_t* row, int sw, int lane, const i32x4& v, int se) {
     if (lane >= 32) return;
@@ -413,16 +415,14 @@ struct RowFmt<HCS_FMT_MXFP8> {
 };
 
 // NVFP4: 512 e2m1 (two per byte, element 2j low) + an e4m3 scale per 16 dims. Every lane takes
-// 8 values (4 code bytes, one 16-byte bf16 chunk) and the scale byte of its half block.
+// 8 values (4 code bytes, one 16-byte bf16 chunk) and the scale byte of its half block; the
+// 4 code bytes come in the aligned 16-byte load shared by lanes 4j .. 4j+3 (the same load
+// shape as the other formats, so a row's loads never depend on its format).
 template <>
 struct RowFmt<HCS_FMT_NVFP4> {
   static constexpr int PB = kNv4PageBytes;
-  __device__ static __forceinline__ void load(const uint8_t* page, int slot, int lane, i32x4& v, int& se) {
-    const uint8_t* src = page ? page + slot * 256 + lane * 4 : g_zero_row + lane * 4;
-    const uint8_t* ssrc = page ? page + kNv4Scales + slot * 32 + (lane >> 1) : g_zero_row;
-    v.x = *(const int*)src;
-    se = *ssrc;
-  }
+  __device__ static __forceinline__ int voff(int slot, int lane) { return slot * 256 + (lane >> 2) * 16; }
+  __device__ static __forceinline__ int soff(int slot, int lane) { return kNv4Scales + slot * 32 + (lane >> 1); }
   // byte k of the codes -> its two values (low nibble first) as bf16 by the hardware conversion
   // (unit scale), then times the e4m3 block scale; the product has at most 6 significant bits,
   // so it is exact in bf16 and the float32 result's upper half is the bf16
@@ -438,42 +438,45 @@ struct RowFmt<HCS_FMT_NVFP4> {
   __device__ static __forceinline__ void store(uint8_t* row, int sw, int lane, const i32x4& v, int se) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8(se, false);
-    const uint32_t w = (uint32_t)v.x;
+    const uint32_t w = (uint32_t)((lane & 2) ? ((lane & 1) ? v.w : v.z) : ((lane & 1) ? v.y : v.x));
     *(i32x4*)(row + (lane ^ sw) * 16) = i32x4{(int)pair<0>(w, sc.x), (int)pair<1>(w, sc.x),
                                               (int)pair<2>(w, sc.x), (int)pair<3>(w, sc.x)};
   }
 };
 
 // The rows of one attention call: window rows in format SF, compressed rows in format CF. The
-// row table entry's top bit says which cache a row comes from (wave-uniform); the source rides
-// along in bit 16 of the scale bits until the store.
+// row table entry's top bit says which cache a row comes from (wave-uniform); `load` returns it
+// for the store. Every format loads 16 bytes and a scale byte per lane, so the source only picks
+// the addresses: no branch, and no wait on one row's loads before the next row's are issued.
 template <int SF, int CF>
 struct QuantStage {
   static constexpr int D = 512, RS = D * 2;
-  __device__ static __forceinline__ void load(const uint8_t* swa_base, const uint8_t* comp_base,
+  __device__ static __forceinline__ bool load(const uint8_t* swa_base, const uint8_t* comp_base,
                                               uint32_t e, int lane, i32x4& v, int& se) {
     e = (uint32_t)__builtin_amdgcn_readfirstlane((int)e);
     const bool ok = e != kNoRow;
     const bool comp = (e >> 31) != 0;
     const uint32_t ridx = e & 0x7fffffffu;
     const int slot = (int)(ridx & 63);
-    if constexpr (SF == CF) {
-      RowFmt<SF>::load(ok ? (comp ? comp_base : swa_base) + (size_t)(ridx >> 6) * RowFmt<SF>::PB : nullptr,
-                       slot, lane, v, se);
-    } else if (comp) {
-      RowFmt<CF>::load(ok ? comp_base + (size_t)(ridx >> 6) * RowFmt<CF>::PB : nullptr, slot, lane, v, se);
-      se |= 1 << 16;
-    } else {
-      RowFmt<SF>::load(ok ? swa_base + (size_t)(ridx >> 6) * RowFmt<SF>::PB : nullptr, slot, lane, v, se);
-    }
+    const size_t pg = ridx >> 6;
+    // an absent row reads the zero page (slot 63 of it lies inside the page in every format)
+    const uint8_t* page = !ok ? g_zero_page
+                        : comp ? comp_base + pg * RowFmt<CF>::PB : swa_base + pg * RowFmt<SF>::PB;
+    const bool cf = ok && comp;
+    const int vo = cf ? RowFmt<CF>::voff(slot, lane) : RowFmt<SF>::voff(slot, lane);
+    const int so = cf ? RowFmt<CF>::soff(slot, lane) : RowFmt<SF>::soff(slot, lane);
+    v = *(const i32x4*)(page + vo);
+    se = page[so];
+    return cf;
   }
-  __device__ static __forceinline__ void store(uint8_t* tile, int r, int sw, int lane, const i32x4& v, int se) {
+  __device__ static __forceinline__ void store(uint8_t* tile, int r, int sw, int lane, const i32x4& v, int se,
+                                               bool cf) {
     uint8_t* row = tile + r * RS;
     if constexpr (SF == CF) {
       RowFmt<SF>::store(row, sw, lane, v, se);
     } else {
-      // every lane holds the same row, so its source is wave-uniform: branch on a scalar
-      if (__builtin_amdgcn_readfirstlane(se >> 16)) RowFmt<CF>::store(row, sw, lane, v, se & 0xffff);
+      // the row's source is wave-uniform (a scalar branch)
+      if (cf) RowFmt<CF>::store(row, sw, lane, v, se);
       else RowFmt<SF>::store(row, sw, lane, v, se);
     }
   }
@@ -545,6 +548,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_fp8_kernel(AttnArgs a) {
   constexpr int WR = BT / 4;                      // rows per wave
   constexpr int PR = BT + 8;                      // P row stride (elements), padded
   constexpr int NLD = WR;                         // one row per register load
+  static_assert(WR == 16, "a wave reads its rows' entries as one 16-lane LDS read");
   __shared__ __attribute__((aligned(16))) uint8_t tile0[BT * RS];
   __shared__ __attribute__((aligned(16))) uint8_t tile1[BT * RS];
   // packed (cache, page, slot) entries of the rows
@@ -586,10 +590,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_fp8_kernel(AttnArgs a) {
   // load this wave's rows of block b into registers (written to LDS at the start of block b)
   const uint8_t* swa_base = a.swa.base;
   const uint8_t* comp_base = a.comp.base;
+  // (the wave's 16 entries come in one LDS read, lane i holding entry i, and go to the scalar
+  // unit by readlane: one LDS wait per block rather than one per row)
+  uint32_t pcf = 0;                                    // bit i: row i of the wave is a CF row
   auto issue = [&](int b) __attribute__((always_inline)) {
-    const uint32_t* rt = rowtab + b * BT + wave * WR;
+    const uint32_t mine = rowtab[b * BT + wave * WR + (lane & 15)];
+    pcf = 0;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) S::load(swa_base, comp_base, rt[i], lane, pre[i], psc[i]);
+    for (int i = 0; i < NLD; ++i)
+      pcf |= (S::load(swa_base, comp_base, (uint32_t)__builtin_amdgcn_readlane((int)mine, i), lane, pre[i],
+                      psc[i]) ? 1u : 0u) << i;
   };
   if (nblk > 0) issue(0);
 
@@ -620,7 +630,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_fp8_kernel(AttnArgs a) {
   // m_ref + kLazyBlock raises a flag; only then do the waves exchange maxima and rescale.
   auto block = [&](int b, uint8_t* T, __bf16* P, int* F) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) S::store(T, wave * WR + i, swz_dec(i), lane, pre[i], psc[i]);
+    for (int i = 0; i < NLD; ++i) S::store(T, wave * WR + i, swz_dec(i), lane, pre[i], psc[i], (pcf >> i) & 1u);
     lds_barrier();                                       // block b is in LDS
     if (b + 1 < nblk) issue(b + 1);
     const bool vr = rowtab[b * BT + wave * WR + (lane & 15)] != kNoRow;
