@@ -111,6 +111,19 @@ def test_fp8_decode_small():
     _check_step(sc)
 
 
+def test_mxfp4_filter_bound_regimes():
+    """MXFP4 keys with more than 32768 visible entries (per-wave bounds, filter, select) across
+    the regimes of the filter bound: top-2048 over 40000, 33000 + 0 and 140000 entries (kb = 21,
+    24 and 6 per 256-entry wave) and top-300 over 100000 entries (more full waves than k: kb = 2).
+    A bound above the k-th score would drop selected ids and fail the top-k comparison."""
+    wl = C.CSA_DECODE_1M_FP8.with_(B=3)
+    sc = G.build(wl, seed=31, device=_dev(), ctx_per_seq=[4 * 40000, 4 * 33000 + 3, 4 * 140000 + 1])
+    _check_step(sc)
+    wl = C.CSA_DECODE_1M_FP8.with_(B=1, topk=300)
+    sc = G.build(wl, seed=32, device=_dev(), ctx_per_seq=[4 * 100000 + 2])
+    _check_step(sc)
+
+
 def test_fp8_decode_1m_sampled():
     sc = G.build(C.CSA_DECODE_1M_FP8, seed=0, device=_dev())
     _check_step(sc, queries=[0, 5])
