@@ -478,8 +478,9 @@ __global__ __launch_bounds__(kChunkThreads, 512 / kChunkThreads) void index_scor
 // its pages in flight at once (the query's codes likewise, from its contiguous rows).
 constexpr int kMx4BlockEntries = 1024;
 
+// (at least four waves per SIMD: 126 VGPRs, no spills; five would spill)
 template <int MT>
-__global__ __launch_bounds__(kScoreThreads) void index_score_mxfp4_kernel(IndexArgs a) {
+__global__ __launch_bounds__(kScoreThreads, 4) void index_score_mxfp4_kernel(IndexArgs a) {
   constexpr int DI = 128;
   constexpr int CB = DI / 2;                                     // code bytes per row
   constexpr int SB = DI / kMxBlock;                              // scale bytes per row
