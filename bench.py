@@ -8,6 +8,10 @@ already resident in HBM; the step is captured in a HIP graph over several indepe
 events on the capturing stream. One JSON line goes to stdout.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload csa_decode_bf16]
+
+The default run measures the CSA decode workload (the line's value) and, as keys of the same
+line, the HCA decode, the 1M-context CSA decode (fp8_ds rows, MXFP4 indexer) and the prefill
+chunk, each with per-step percentiles and a roofline entry for its dominant kernel.
 """
 from __future__ import annotations
 
@@ -79,12 +83,21 @@ def sources_digest(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary
-    (profiles/pmc_attention_<workload>.txt: FETCH_SIZE and WRITE_SIZE per dispatch of each
-    attention kernel, scaled by the same counters' reading for a copy of known size), or None
-    when there is no summary or the attention sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"pmc_attention_{workload}.txt")
+# sources of each op's kernels: a counter summary is used only while they are unchanged
+OP_SOURCES = {
+    "attention": ATTN_SOURCES,
+    "index_topk": ["hybrid_compressed_sparse_amd/csrc/indexer.hip", "hybrid_compressed_sparse_amd/csrc/common.h",
+                   "hybrid_compressed_sparse_amd/csrc/select.h", "hybrid_compressed_sparse_amd/csrc/kernels.h",
+                   "hybrid_compressed_sparse_amd/csrc/compress_impl.h"],
+}
+
+
+def measured_traffic(workload: str, op: str = "attention"):
+    """HBM bytes per launch of `op` from the committed rocprofv3 counter summary
+    (profiles/pmc_<op>_<workload>.txt: FETCH_SIZE and WRITE_SIZE per dispatch of each of the
+    op's kernels, scaled by the same counters' reading for a copy of known size), or None when
+    there is no summary or the op's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{op}_{workload}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -94,12 +107,24 @@ def measured_traffic(workload: str):
                 continue
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("sources_digest") != sources_digest(ATTN_SOURCES):
+    if vals.get("sources_digest") != sources_digest(OP_SOURCES[op]):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def pct_stats(samples) -> dict:
+    """p10 / p50 / p90 / mean of per-step times (ms), nearest-rank percentiles."""
+    a = sorted(samples)
+    if not a:
+        return {}
+
+    def pct(p):
+        return a[min(len(a) - 1, max(0, math.ceil(p * len(a)) - 1))]
+    return {"p10_ms": pct(0.10), "p50_ms": pct(0.50), "p90_ms": pct(0.90), "mean_ms": sum(a) / len(a),
+            "samples": len(a)}
 
 
 # ------------------------------------------------------------------ GPU step
@@ -201,6 +226,25 @@ class Bench:
                 self.run_op(op, i)
         torch.cuda.synchronize()
         return g
+
+    def distribution(self, op: str, replays: int = 10) -> dict:
+        """Percentiles of the time per step of `op` over `replays` replays of the graph of one
+        launch per input set (each sample: one replay's HIP-event time / the sets in it, on the
+        replay stream), outside the timed region of the headline value."""
+        torch = self.torch
+        g = self.graph(op)
+        g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        n = len(self.sets)
+        st = pct_stats([a.elapsed_time(b) / n for a, b in ev])
+        st["steps_per_sample"] = n
+        return st
 
     def time_graph(self, g, reps: int, warm: int) -> float:
         """Average ms per replay of g over `reps` replays (HIP events on the replay stream)."""
@@ -438,7 +482,28 @@ def bench_indexer_formats(wl, sets: int, reps: int) -> dict:
     return res
 
 
+def cpu_info() -> dict:
+    """The host's logical CPU count, the CPUs this process may run on, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    return {"nproc": os.cpu_count(), "affinity_cpus": aff, "cpu_model": model}
+
+
 def cpu_baseline(wl, seconds: float) -> dict:
+    """The oracle (float64 NumPy) timed on this host: whole steps of `wl`'s batch (the
+    compressor over every sequence's new token once, then each query's indexer + top-k and
+    attention), repeated until `seconds` are spent; queries per second."""
     from threadpoolctl import threadpool_info
 
     from oracle import pipeline as OP
@@ -447,17 +512,17 @@ def cpu_baseline(wl, seconds: float) -> dict:
     sc = G.build(wl, seed=0, device="cpu")
     OP.step(sc, queries=[0])                      # warm the caches of the decoders
     t0 = time.perf_counter()
-    done = 0
-    # cycle over the batch's queries until the time budget is spent (at least one pass)
-    while done < sc.N or time.perf_counter() - t0 < seconds:
-        OP.step(sc, queries=[done % sc.N])
-        done += 1
+    steps = 0
+    while steps == 0 or time.perf_counter() - t0 < seconds:
+        OP.step(sc)
+        steps += 1
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": done / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} query steps cycling over the {sc.N} queries of {wl.name} (per query: "
-                      f"compressor of the batch's streams, indexer + top-k, attention), float64 NumPy, "
-                      f"{dt:.1f} s"}
+    return {"value": steps * sc.N / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} whole steps of {wl.name} ({sc.N} queries each: compressor over the batch's "
+                      f"new tokens, per query indexer + top-k and attention), float64 NumPy with "
+                      f"{threads} BLAS threads, {dt:.1f} s",
+            **cpu_info()}
 
 
 # ------------------------------------------------------------------ prefill chunk
@@ -478,13 +543,13 @@ def prefill_flops(wl) -> dict:
     return {"index_topk": ix, "attention": at, "step": ix + at}
 
 
-def bench_prefill(wl, args):
+def measure_prefill(wl, args, sets: int) -> dict:
     """One prefill chunk (compressor over the chunk, indexer + top-k and attention for its Q
-    queries) per step; tokens/s and the fraction of the bf16 MFMA peak."""
-    R = max(1, min(args.sets, args.steps, 2))        # q alone is 256 MB per set
+    queries) per step: tokens/s, the fraction of the bf16 MFMA peak per op and for the step, and
+    per-step percentiles."""
+    R = max(1, min(sets, args.steps))
     log(f"[bench] {wl.name}: building {R} input sets")
-    fused = select_in_attention_ok(wl) and not args.two_call
-    bench = Bench(wl, R, seed=1000, select_in_attention=fused)
+    bench = Bench(wl, R, seed=1000)
     full, rem = divmod(args.steps, R)
 
     def timed(op):
@@ -494,22 +559,120 @@ def bench_prefill(wl, args):
         return bench.time_steps(gs, 1, 0) / args.steps
 
     ms = {op: timed(op) for op in ["step", "compress", "index_topk", "attention"]}
+    dist = bench.distribution("step")
+    del bench
+    import torch
+    torch.cuda.empty_cache()
     fl = prefill_flops(wl)
     tflops = {k: fl[k] / (ms[k] * 1e-3) / 1e12 for k in ["index_topk", "attention", "step"]}
     for k in ms:
-        log(f"[bench] {k}: {ms[k] * 1e3:.1f} us" + (f", {tflops[k]:.0f} TFLOP/s" if k in tflops else ""))
-    print(json.dumps({
+        log(f"[bench] {wl.name} {k}: {ms[k] * 1e3:.1f} us" + (f", {tflops[k]:.0f} TFLOP/s" if k in tflops else ""))
+    dom = max(["index_topk", "attention"], key=lambda k: ms[k])
+    roof = {op: {"bound": "mfma", "achieved": tflops[op], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tflops[op] / BF16_MFMA_PEAK_TFLOPS, "traffic": None, "flops_per_launch": fl[op],
+                 "us_per_launch": ms[op] * 1e3,
+                 "kernel": ("hcs_sparse_mla_prefill_chunk (mla_heads_kernel<512, head pairs>)" if op == "attention"
+                            else "hcs_index_topk_chunk (index_score_chunk_kernel + topk_single_kernel)")}
+            for op in ["index_topk", "attention"]}
+    return {
         "metric": "prefill tokens/s and % bf16 MFMA peak, CSA chunk, 1 GPU", "value": wl.Q / (ms["step"] * 1e-3),
-        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms["step"],
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "unit": "tokens/s", "ms_per_step": ms["step"], "timing": dist, "dtype": "bf16",
         "config": {"workload": wl.name, "P0": wl.P0, "Q": wl.Q, "heads": wl.H, "head_dim": wl.d,
-                   "compress_ratio": wl.m, "window": wl.window, "topk": wl.topk, "indexer": f"{wl.H_I}x{wl.d_I} bf16"},
-        "roofline": {"bound": "mfma", "achieved": tflops["step"], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops["step"] / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
-                     "flops_per_step": fl["step"]},
+                   "compress_ratio": wl.m, "window": wl.window, "topk": wl.topk,
+                   "indexer": f"{wl.H_I}x{wl.d_I} bf16", "input_sets_rotated": R},
+        "mfma_frac_step": tflops["step"] / BF16_MFMA_PEAK_TFLOPS, "flops_per_step": fl["step"],
+        "roofline": roof[dom], "rooflines": roof,
         "ops_us": {k: v * 1e3 for k, v in ms.items()},
-        "ops_tflops": tflops,
-    }))
+    }
+
+
+# ------------------------------------------------------------------ decode workloads
+
+def attention_kernel_name(wl, fused: bool) -> str:
+    if fused:
+        return "hcs_sparse_mla_decode_select (mla_heads_kernel<512, select> + mla_combine_kernel<512>)"
+    if wl.kv_fmt == "bf16":
+        return "hcs_sparse_mla_decode (mla_heads_kernel<512> + mla_combine_kernel<512>)"
+    return "hcs_sparse_mla_decode (mla_fp8_kernel<QuantStage> + mla_combine_kernel<512>)"
+
+
+def index_kernel_name(wl, fused: bool) -> str:
+    if fused:
+        return "hcs_index_scores_compress (index_score_compress_kernel)"
+    if wl.ix_fmt == "mxfp4":
+        return "hcs_index_topk (index_score_mxfp4_kernel + topk_filter_kernel + topk_select_kernel)"
+    return "hcs_index_topk (index_score_bf16_kernel + topk_single_kernel)"
+
+
+def measure_decode(wl, args, sets: int, seed: int = 1000, two_call: bool = False) -> dict:
+    """One decode workload: the step time over exactly args.steps steps (rotating `sets` input
+    sets), per-step percentiles, each op's time and, for each HBM-bound op, its roofline entry
+    (algorithmic bytes per launch / measured time per launch against the 8 TB/s peak)."""
+    import torch
+
+    n_vis = wl.ctx // wl.m
+    R = max(1, min(sets, args.steps))
+    log(f"[bench] {wl.name}: building {R} input sets")
+    fused = select_in_attention_ok(wl) and not two_call
+    bench = Bench(wl, R, seed=seed, select_in_attention=fused)
+
+    def timed(op, steps, warmup):
+        """ms per launch of `op` over exactly `steps` launches (after `warmup` untimed ones),
+        rotating the input sets: full rounds of all sets, then the remainder."""
+        full, rem = divmod(steps, R)
+        gs = ([bench.graph(op)] * full) + ([bench.graph(op, range(rem))] if rem else [])
+        wf, wr = divmod(warmup, R)
+        for _ in range(wf):
+            gs[0].replay()
+        if wr:
+            bench.graph(op, range(wr)).replay()
+        return bench.time_steps(gs, 1, 0) / steps
+
+    log(f"[bench] {wl.name}: capturing the step graph")
+    ms_step = timed("step", args.steps, args.warmup)
+    dist = bench.distribution("step")
+    ops = ["compress", "attention"] + (["index_topk"] if wl.indexer else [])
+    # with the selection inside the attention, the indexer op produces the scores only
+    label = {"index_topk": "index_scores", "attention": "attention_select"} if fused else {}
+    op_ms = {}
+    for op in ops:
+        op_ms[op] = timed(op, args.steps, args.warmup)
+        log(f"[bench] {wl.name} {label.get(op, op)}: {op_ms[op] * 1e3:.2f} us")
+    del bench
+    torch.cuda.empty_cache()
+    by = algo_bytes(wl, n_vis)
+    qps = wl.B / (ms_step * 1e-3)
+    step_gbs = by["step"] / (ms_step * 1e-3) / 1e9
+    log(f"[bench] {wl.name}: step {ms_step * 1e3:.2f} us (p50 {dist['p50_ms'] * 1e3:.2f}), {qps:,.0f} q/s, "
+        f"{step_gbs:.0f} GB/s ({100 * step_gbs / HBM_PEAK_GBS:.1f}% of HBM)")
+    op_bytes = {"attention": by["attention"], "index_topk": by["index_topk"]}
+    if fused:
+        # the attention launch reads every visible entry's score instead of the selected ids,
+        # and the indexer launch writes the scores instead of the ids
+        op_bytes["attention"] += wl.B * (n_vis * 4 - min(wl.topk, n_vis) * 4)
+        op_bytes["index_topk"] += wl.B * (n_vis * 4 - wl.topk * 8)
+    roofs = {}
+    for op in [o for o in ("attention", "index_topk") if o in op_ms]:
+        gbs = op_bytes[op] / (op_ms[op] * 1e-3) / 1e9
+        roofs[op] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name, op),
+                     "kernel": attention_kernel_name(wl, fused) if op == "attention" else index_kernel_name(wl, fused),
+                     "algorithmic_bytes_per_launch": op_bytes[op], "us_per_launch": op_ms[op] * 1e3}
+    dom = max(roofs, key=lambda o: op_ms[o])
+    return {
+        "value": qps, "unit": "queries/s", "ms_per_step": ms_step, "timing": dist,
+        "dtype": "bf16" if wl.kv_fmt == "bf16" else f"{wl.kv_fmt} KV + {wl.ix_fmt} indexer (bf16 / fp4 MFMA)",
+        "config": {"workload": wl.name, "batch": wl.B, "context": wl.ctx, "heads": wl.H,
+                   "head_dim": wl.d, "compress_ratio": wl.m, "window": wl.window,
+                   "topk": wl.topk if wl.indexer else None,
+                   "indexer": f"{wl.H_I}x{wl.d_I} {wl.ix_fmt}" if wl.indexer else None,
+                   "kv_format": wl.kv_fmt, "input_sets_rotated": R},
+        "hbm_tb_s": step_gbs / 1e3, "hbm_frac": step_gbs / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": by["step"],
+        "roofline": roofs[dom], "rooflines": roofs,
+        "ops_us": {label.get(k, k): v * 1e3 for k, v in op_ms.items()},
+        "select_in_attention": fused,
+    }
 
 
 # ------------------------------------------------------------------ main
@@ -520,10 +683,13 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="csa_decode_bf16")
-    ap.add_argument("--sets", type=int, default=8, help="independent input sets rotated per replay")
+    ap.add_argument("--sets", type=int, default=24,
+                    help="independent input sets rotated per replay (the CSA decode workload's caches: "
+                         "88 MB per set; fewer for the larger workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the HCA side measurement")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="measure only --workload (no other workloads, no side measurements)")
     ap.add_argument("--two-call", action="store_true",
                     help="CSA decode: top-k in the indexer launch (hcs_index_topk_compress + "
                          "hcs_sparse_mla_decode) instead of inside the attention")
@@ -555,10 +721,12 @@ def main():
         return
 
     wl = C.BY_NAME[args.workload]
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
     if args.side:
         if wl.kind != "decode":
             sys.exit("side measurements use a decode workload's shapes")
-        R = max(1, min(args.sets, args.steps))
+        R = max(1, min(args.sets, args.steps, 8))
         reps = max(1, args.steps // R)
         if args.side == "compress_full":
             res = bench_compress_full(wl, R, reps)
@@ -572,96 +740,51 @@ def main():
         log(f"[bench] {args.side}: {res['us_per_call']:.2f} us")
         print(json.dumps({"side": args.side, **res}))
         return
+    # input sets per workload: enough rotation that the 256 MB Infinity Cache cannot hold the
+    # step's caches between uses (CSA decode: 88 MB per set; HCA: 72 MB; 1M: 1.36 GB; prefill:
+    # 0.3 GB of q alone)
+    sets_of = {"csa_decode_bf16": args.sets, "hca_decode_bf16": min(args.sets, 16),
+               "csa_decode_1m_fp8": 2, "csa_decode_1m_v41": 2, "csa_prefill_bf16": 2}
     if wl.kind == "prefill":
-        return bench_prefill(wl, args)
+        res = measure_prefill(wl, args, sets_of.get(wl.name, 2))
+        print(json.dumps({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                          "scaling": "weak", "vs_baseline": None, "data": "synthetic", **res}))
+        return
     if wl.kind != "decode":
         sys.exit("bench workloads are the decode and prefill configurations")
-    n_vis = wl.ctx // wl.m
-    if args.steps < 1 or args.warmup < 0:
-        sys.exit("--steps must be >= 1 and --warmup >= 0")
-    R = max(1, min(args.sets, args.steps))
-    log(f"[bench] {wl.name}: building {R} input sets")
-    fused = select_in_attention_ok(wl) and not args.two_call
-    bench = Bench(wl, R, seed=1000, select_in_attention=fused)
-
-    def timed(op, steps, warmup):
-        """ms per launch of `op` over exactly `steps` launches (after `warmup` untimed ones),
-        rotating the input sets: full rounds of all sets, then the remainder."""
-        full, rem = divmod(steps, R)
-        gs = ([bench.graph(op)] * full) + ([bench.graph(op, range(rem))] if rem else [])
-        wf, wr = divmod(warmup, R)
-        for _ in range(wf):
-            gs[0].replay()
-        if wr:
-            bench.graph(op, range(wr)).replay()
-        return bench.time_steps(gs, 1, 0) / steps
 
     if args.only:
+        R = max(1, min(sets_of.get(wl.name, args.sets), args.steps))
+        fused = select_in_attention_ok(wl) and not args.two_call
+        bench = Bench(wl, R, seed=1000, select_in_attention=fused)
         if args.only != "step":
             # one round of whole steps first, so that the attention entry point reads rows
             # of a real selection (the top-k output it consumes)
             bench.graph("step").replay()
-        ms = timed(args.only, args.steps, args.warmup)
+        full, rem = divmod(args.steps, R)
+        gs = ([bench.graph(args.only)] * full) + ([bench.graph(args.only, range(rem))] if rem else [])
+        ms = bench.time_steps(gs, 1, 0) / args.steps
         log(f"[bench] {args.only}: {ms * 1e3:.2f} us per launch")
         print(json.dumps({"op": args.only, "us_per_launch": ms * 1e3, "launches": args.steps}))
         return
 
-    log("[bench] capturing the step graph")
-    ms_step = timed("step", args.steps, args.warmup)
-    ops = ["compress", "attention"] + (["index_topk"] if wl.indexer else [])
-    # with the selection inside the attention, the indexer op produces the scores only
-    label = {"index_topk": "index_scores", "attention": "attention_select"} if fused else {}
-    op_ms = {}
-    for op in ops:
-        op_ms[op] = timed(op, args.steps, args.warmup)
-        log(f"[bench] {label.get(op, op)}: {op_ms[op] * 1e3:.2f} us")
-    by = algo_bytes(wl, n_vis)
-    qps = wl.B / (ms_step * 1e-3)
-    step_gbs = by["step"] / (ms_step * 1e-3) / 1e9
-    # the roofline entry is the attention entry point (its main kernel plus, when a query's
-    # rows are split over blocks, the merge kernel): the largest share of the step
-    dom = "attention"
-    dom_bytes = by[dom]
-    if fused:
-        # the attention launch reads every visible entry's score instead of the selected ids
-        dom_bytes += wl.B * (n_vis * 4 - min(wl.topk, n_vis) * 4)
-    dom_gbs = dom_bytes / (op_ms[dom] * 1e-3) / 1e9
-    traffic = measured_traffic(wl.name)
-    log(f"[bench] step {ms_step * 1e3:.2f} us, {qps:,.0f} q/s, {step_gbs:.0f} GB/s "
-        f"({100 * step_gbs / HBM_PEAK_GBS:.1f}% of HBM)")
-
-    result = {
-        "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": wl.name, "batch": wl.B, "context": wl.ctx, "heads": wl.H,
-                   "head_dim": wl.d, "compress_ratio": wl.m, "window": wl.window,
-                   "topk": wl.topk if wl.indexer else None,
-                   "indexer": f"{wl.H_I}x{wl.d_I} {wl.ix_fmt}" if wl.indexer else None,
-                   "kv_format": wl.kv_fmt, "input_sets_rotated": R},
-        "hbm_tb_s": step_gbs / 1e3, "hbm_frac": step_gbs / HBM_PEAK_GBS,
-        "algorithmic_bytes_per_step": by["step"],
-        "roofline": {"bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": ("hcs_sparse_mla_decode_select (mla_heads_kernel<512, select> + "
-                                "mla_combine_kernel<512>)") if fused else
-                               "hcs_sparse_mla_decode (mla_heads_kernel<512> + mla_combine_kernel<512>)"
-                               if wl.kv_fmt == "bf16" else
-                               "hcs_sparse_mla_decode (mla_fp8_kernel<QuantStage> + mla_combine_kernel<512>)",
-                     "algorithmic_bytes_per_launch": dom_bytes, "us_per_launch": op_ms[dom] * 1e3},
-        "ops_us": {label.get(k, k): v * 1e3 for k, v in op_ms.items()},
-        "select_in_attention": fused,
-    }
-    del bench
-    torch.cuda.empty_cache()
+    head = measure_decode(wl, args, sets_of.get(wl.name, args.sets), two_call=args.two_call)
+    result = {"metric": METRIC, "value": head["value"], "unit": "queries/s", "n_gpus": 1,
+              "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic",
+              **{k: v for k, v in head.items() if k not in ("value", "unit", "ms_per_step")}}
 
     if not args.no_extra and wl.name == "csa_decode_bf16":
+        for other in (C.HCA_DECODE, C.CSA_DECODE_1M_FP8):
+            res = measure_decode(other, args, sets_of[other.name], seed=2000)
+            result[other.name] = res
+        result[C.CSA_PREFILL.name] = measure_prefill(C.CSA_PREFILL, args, sets_of[C.CSA_PREFILL.name])
+        R = max(1, min(args.sets, args.steps, 8))
+        reps = max(1, args.steps // R)
         log("[bench] side measurement: full compressor at this decode step")
-        result["compress_full"] = bench_compress_full(wl, R, max(1, args.steps // R))
+        result["compress_full"] = bench_compress_full(wl, R, reps)
         log(f"[bench] compress_full: {result['compress_full']['us_per_call']:.2f} us")
         log("[bench] side measurement: query preparation and SWA insert (decode step, prefill chunk)")
-        reps = max(1, args.steps // R)
         result["qnorm_rope_kv_insert"] = {"decode": bench_insert(wl, wl.B, 1, R, reps),
                                           "prefill_chunk": bench_insert(wl, 1, 4096, R, reps)}
         for k, v in result["qnorm_rope_kv_insert"].items():
@@ -674,16 +797,6 @@ def main():
             log(f"[bench] indexer {name}: " + ", ".join(
                 f"{f} {v[f]['us_per_call']:.1f} us" + (f" (recall {100 * v[f]['recall_vs_bf16']:.2f}%)" if f != "bf16" else "")
                 for f in ("bf16", "mxfp4", "fp8ix")))
-        hw = C.HCA_DECODE
-        log(f"[bench] side measurement: {hw.name}")
-        hb = Bench(hw, R, seed=2000)
-        hms = hb.time_graph(hb.graph("step"), max(1, args.steps // R), max(1, args.warmup // R)) / R
-        hby = algo_bytes(hw, hw.ctx // hw.m)
-        result["hca_decode_bf16"] = {"queries_per_s": hw.B / (hms * 1e-3), "ms_per_step": hms,
-                                     "hbm_frac": hby["step"] / (hms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                     "algorithmic_bytes_per_step": hby["step"]}
-        del hb
-        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
         L.hcs_last_error.restype = ctypes.c_char_p
         L.hcs_abi_version.restype = i32
+        L.hcs_device_errors.restype = i32
+        L.hcs_device_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
         L.hcs_compress_kv.restype = i32
         L.hcs_compress_kv.argtypes = [vp, vp, i32, i64, vp, vp, i32, i32, i32, i32, vp, vp, Paged,
                                       vp, i64, vp]
@@ -94,6 +96,18 @@ def lib() -> ctypes.CDLL:
                                           vp, vp, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
+
+
+DEVERR_PAGE_RANGE = 0x1   # a page-table entry >= num_pages was met
+DEVERR_PAIR_WAIT = 0x2    # the prefill attention's head-pair exchange timed out
+
+
+def device_errors(clear: bool = True) -> int:
+    """hcs_device_errors: waits for the current device, returns its error bits (DEVERR_*) and
+    clears them unless clear is False."""
+    v = ctypes.c_uint32(0)
+    _check(lib().hcs_device_errors(ctypes.byref(v), 1 if clear else 0), "device_errors")
+    return int(v.value)
 
 
 def _check(status: int, what: str) -> None:

@@ -56,6 +56,22 @@ extern "C" {
 const char* hcs_last_error(void) { return g_err; }
 int hcs_abi_version(void) { return HCS_ABI_VERSION; }
 
+hcs_status hcs_device_errors(uint32_t* bits, int clear) {
+  if (!bits) return fail(HCS_ERR_INVALID_ARG, "null bits");
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_status(e, "device_errors (synchronize)");
+  uint32_t v = 0;
+  hipError_t (*const readers[])(uint32_t*, bool) = {hcs::dev_errors_attention, hcs::dev_errors_compress,
+                                                    hcs::dev_errors_indexer, hcs::dev_errors_indexer_prep,
+                                                    hcs::dev_errors_insert};
+  for (auto r : readers) {
+    e = r(&v, clear != 0);
+    if (e != hipSuccess) return hip_status(e, "device_errors (read)");
+  }
+  *bits |= v;
+  return ok();
+}
+
 // ------------------------------------------------------------------------------ compressor
 // Checks of hcs_compress_kv; fills `a` (nothing is launched). B == 0 returns HCS_OK with a.B 0.
 static hcs_status prep_compress(const void* kv, const void* score, int in_dtype, int64_t row_stride,

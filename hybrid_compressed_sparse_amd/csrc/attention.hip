@@ -31,6 +31,8 @@
 
 namespace hcs {
 
+HCS_DEVICE_ERROR_WORD(attention)
+
 // A zero row: rows that take part in nothing load from here, so loads never branch.
 __device__ __attribute__((aligned(64))) uint8_t g_zero_row[1024];
 // A page of zeros in every quantised row format (the fp8_ds page is the largest): absent rows
@@ -138,7 +140,9 @@ __device__ __forceinline__ void fill_rowtab(const AttnArgs& a, int t, const Quer
     if (li < n32) {
       const bool is_swa = gr < q.n_swa;
       const int npages = is_swa ? a.swa.num_pages : a.comp.num_pages;
-      const bool ok = li < n && gr < q.R && row[i] >= 0 && pg[i] >= 0 && pg[i] < npages;
+      const bool used = li < n && gr < q.R && row[i] >= 0;
+      if (used && pg[i] >= npages) dev_error(HCS_DEVERR_PAGE_RANGE);
+      const bool ok = used && pg[i] >= 0 && pg[i] < npages;
       rowtab[li] = ok ? ((is_swa ? 0u : 0x80000000u) | (uint32_t)(pg[i] * 64 + (row[i] & 63))) : kNoRow;
     }
   }
@@ -194,7 +198,9 @@ __device__ __forceinline__ void fill_rows(const AttnArgs& a, int t, const QueryR
     int pg = spg[i];
     if (!is_swa && li < np) pg = cached ? ptl[row >> 6] : __ldg(cpt + (row >> 6));
     const int npages = is_swa ? a.swa.num_pages : a.comp.num_pages;
-    const bool ok = li < n && gr < q.R && ok_id && pg >= 0 && pg < npages;
+    const bool used = li < n && gr < q.R && ok_id;
+    if (used && pg >= npages) dev_error(HCS_DEVERR_PAGE_RANGE);
+    const bool ok = used && pg >= 0 && pg < npages;
     if (li < np) rowtab[li] = ok ? ((is_swa ? 0u : 0x80000000u) | (uint32_t)(pg * 64 + (row & 63))) : kNoRow;
   }
   wait_vm_zero();     // LDS copies the caller started before (dma16) have landed as well
@@ -267,9 +273,10 @@ __device__ __forceinline__ void fill_rows_sel(const AttnArgs& a, int t, int s, c
   sel_reset<NT>(sh);
   __syncthreads();
   if (!all)
-    block_topk<NT>(
+    block_topk<NT, false>(
         sh, nv, k, [&](int i, uint32_t& key) { key = kl[i]; return true; }, [&](int i) { return i; },
-        [&](unsigned, int id, uint32_t) { flag[id] = 1; });      // ends with a barrier
+        [&](unsigned, int id, uint32_t) { flag[id] = 1; });      // ends with a barrier (the ids are
+                                                                  // marked, so their order is free)
   // ---- position of each selected id in id order: exclusive prefix of the flag counts
   constexpr int FPT = kSelMax / NT;              // ids per thread in the scan
   static_assert(FPT % 4 == 0, "the scan reads 4 id flags per word");
@@ -318,11 +325,13 @@ __device__ __forceinline__ void fill_rows_sel(const AttnArgs& a, int t, int s, c
       if (gr < q.n_swa) {
         const int pg = spg[i];
         const int row = q.lo + gr;
+        if (pg >= a.swa.num_pages) dev_error(HCS_DEVERR_PAGE_RANGE);
         if (pg >= 0 && pg < a.swa.num_pages) e = (uint32_t)(pg * 64 + (row & 63));
       } else {
         const uint32_t id = rowtab[li];
         if (id != kNoRow) {
           const int pg = cached ? ptl[id >> 6] : __ldg(cpt + (id >> 6));
+          if (pg >= a.comp.num_pages) dev_error(HCS_DEVERR_PAGE_RANGE);
           if (pg >= 0 && pg < a.comp.num_pages) e = 0x80000000u | (uint32_t)(pg * 64 + (id & 63));
         }
       }
@@ -1102,10 +1111,13 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
           pmax[wave][16 + l16] = tmax[1];
         }
         if (lane == 0) pseq[wave] = i + 1;
-        for (int spin = 0; spin < (1 << 16); ++spin) {
-          if (__builtin_amdgcn_readfirstlane(((volatile int*)pseq)[partner]) > i) break;
-          __builtin_amdgcn_s_sleep(1);
+        bool met = false;
+        for (int spin = 0; spin < (1 << 16) && !met; ++spin) {
+          met = __builtin_amdgcn_readfirstlane(((volatile int*)pseq)[partner]) > i;
+          if (!met) __builtin_amdgcn_s_sleep(1);
         }
+        // a wait that ran out goes on with this wave's own maxima (a wrong result, reported)
+        if (!met && lane == 0) dev_error(HCS_DEVERR_PAIR_WAIT);
         asm volatile("" ::: "memory");
         tmax[0] = fmaxf(tmax[0], ((volatile float*)pmax[partner])[l16]);
         tmax[1] = fmaxf(tmax[1], ((volatile float*)pmax[partner])[16 + l16]);

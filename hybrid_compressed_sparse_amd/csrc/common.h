@@ -42,9 +42,38 @@ inline Paged to_paged(const hcs_paged& p) {
   return Paged{static_cast<const uint8_t*>(p.base), p.page_table, p.pt_stride, p.num_pages};
 }
 
-// Page id of logical row `row` of sequence `seq`, or -1 if not resident.
+// ---------------------------------------------------------------- device error word
+// Kernels OR the HCS_DEVERR_* bits of hcs.h into a word that stays set until the host reads and
+// clears it (hcs_device_errors). Each .hip file is its own device code object, so each defines
+// its own word, its dev_error() and a host reader dev_errors_<file>() with
+// HCS_DEVICE_ERROR_WORD(<file>) at namespace hcs scope.
+namespace {
+__device__ void dev_error(unsigned bits);
+}
+#define HCS_DEVICE_ERROR_WORD(NAME)                                                                   \
+  __device__ unsigned g_dev_err_##NAME;                                                               \
+  namespace {                                                                                         \
+  __device__ void dev_error(unsigned bits) { atomicOr(&g_dev_err_##NAME, bits); }                     \
+  }                                                                                                   \
+  hipError_t dev_errors_##NAME(uint32_t* bits, bool clear) {                                          \
+    uint32_t v = 0;                                                                                   \
+    hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_dev_err_##NAME), sizeof(v), 0,                \
+                                       hipMemcpyDeviceToHost);                                        \
+    if (e == hipSuccess && clear && v) {                                                              \
+      const uint32_t zero = 0;                                                                        \
+      e = hipMemcpyToSymbol(HIP_SYMBOL(g_dev_err_##NAME), &zero, sizeof(zero), 0,                     \
+                            hipMemcpyHostToDevice);                                                   \
+    }                                                                                                 \
+    *bits |= v;                                                                                       \
+    return e;                                                                                         \
+  }
+
+// Page id of logical row `row` of sequence `seq`, or -1 if not resident (a negative entry); an
+// entry past the pool (>= num_pages) is also treated as not resident and flagged in the error
+// word.
 __device__ __forceinline__ int page_of(const Paged& c, int seq, int row) {
   int pg = __ldg(c.pt + (int64_t)seq * c.pt_stride + (row >> 6));
+  if (pg >= c.num_pages) dev_error(HCS_DEVERR_PAGE_RANGE);
   return (pg >= 0 && pg < c.num_pages) ? pg : -1;
 }
 

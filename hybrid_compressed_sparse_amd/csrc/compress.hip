@@ -20,6 +20,8 @@
 
 namespace hcs {
 
+HCS_DEVICE_ERROR_WORD(compress)
+
 namespace {
 
 __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs a) {

@@ -82,6 +82,7 @@ __device__ __forceinline__ void compress_store(const CompressArgs& a, int b, int
 // Page of completed entry kb of sequence b in the compressed cache, or nullptr.
 __device__ __forceinline__ const uint8_t* compress_entry_page(const CompressArgs& a, int b, int kb) {
   const int pg = (kb >> 6) < a.comp_pt_stride ? __ldg(a.comp_pt + (int64_t)b * a.comp_pt_stride + (kb >> 6)) : -1;
+  if (pg >= a.comp_num_pages) dev_error(HCS_DEVERR_PAGE_RANGE);
   if (pg < 0 || pg >= a.comp_num_pages) return nullptr;
   const int64_t pb = a.fmt == HCS_FMT_BF16 ? (int64_t)kPageRows * a.d * 2 : kv_page_bytes(a.fmt);
   return a.comp_base + (int64_t)pg * pb;

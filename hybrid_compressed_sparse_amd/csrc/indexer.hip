@@ -34,6 +34,8 @@
 
 namespace hcs {
 
+HCS_DEVICE_ERROR_WORD(indexer)
+
 namespace {
 
 constexpr int kScoreThreads = 256;
@@ -498,6 +500,7 @@ __global__ __launch_bounds__(kScoreThreads, 4) void index_score_mxfp4_kernel(Ind
   int my_pg = -1;
   if (lane < PPW && e_base + 64 * lane < nv) {
     const int pg = __ldg(a.keys.pt + (int64_t)seq * a.keys.pt_stride + (e_base >> 6) + lane);
+    if (pg >= a.keys.num_pages) dev_error(HCS_DEVERR_PAGE_RANGE);
     my_pg = pg >= 0 && pg < a.keys.num_pages ? pg : -1;
   }
   // query codes (head mt*16 + l16, block g) and scales, head weights
@@ -612,6 +615,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_fp8_kernel(IndexArg
   int my_pg = -1;
   if (lane < PPW && e_base + 64 * lane < nv) {
     const int pg = __ldg(a.keys.pt + (int64_t)seq * a.keys.pt_stride + (e_base >> 6) + lane);
+    if (pg >= a.keys.num_pages) dev_error(HCS_DEVERR_PAGE_RANGE);
     my_pg = pg >= 0 && pg < a.keys.num_pages ? pg : -1;
   }
   int pgs[PPW];

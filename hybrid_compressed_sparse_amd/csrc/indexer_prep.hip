@@ -16,6 +16,8 @@
 
 namespace hcs {
 
+HCS_DEVICE_ERROR_WORD(indexer_prep)
+
 namespace {
 
 constexpr int kIxThreads = 256;
@@ -120,6 +122,7 @@ __global__ __launch_bounds__(kIxThreads) void indexer_k_kernel(IxKArgs a) {
   pair_angle(a.rope_cos, a.rope_sin, a.d_rope, a.rope_rows, (int)min(pos, (int64_t)INT32_MAX), lane, c, s);
   if ((ent >> 6) >= a.keys.pt_stride) return;
   const int pg = a.keys.pt[(int64_t)seq * a.keys.pt_stride + (ent >> 6)];
+  if (pg >= a.keys.num_pages) dev_error(HCS_DEVERR_PAGE_RANGE);
   if (pg < 0 || pg >= a.keys.num_pages) return;   // not resident: the write is dropped
   const float ss = warp_sum(x.u * x.u + x.v * x.v);
   const float rn = 1.f / __builtin_sqrtf(ss / (float)kIxDim + a.eps);

@@ -21,6 +21,8 @@
 
 namespace hcs {
 
+HCS_DEVICE_ERROR_WORD(insert)
+
 namespace {
 
 constexpr int kInsertThreads = 256;
@@ -135,6 +137,7 @@ __device__ __forceinline__ void insert_kv_row(const InsertArgs& a, int t, int se
   rope_row<E>(a, pos, lane, rc, rs);
   if ((pos >> 6) >= a.swa_pt_stride) return;
   const int pg = a.swa_pt[(int64_t)seq * a.swa_pt_stride + (pos >> 6)];
+  if (pg >= a.swa_num_pages) dev_error(HCS_DEVERR_PAGE_RANGE);
   if (pg < 0 || pg >= a.swa_num_pages) return;   // not resident: the write is dropped
   apply_rope<E>(a, lane, x, rc, rs);
   const int slot = pos & 63;

@@ -5,6 +5,14 @@
 
 namespace hcs {
 
+// Host readers of each source file's device error word (HCS_DEVICE_ERROR_WORD): OR the bits
+// into *bits and clear them when asked; the caller synchronises the device first.
+hipError_t dev_errors_attention(uint32_t* bits, bool clear);
+hipError_t dev_errors_compress(uint32_t* bits, bool clear);
+hipError_t dev_errors_indexer(uint32_t* bits, bool clear);
+hipError_t dev_errors_indexer_prep(uint32_t* bits, bool clear);
+hipError_t dev_errors_insert(uint32_t* bits, bool clear);
+
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
   const uint16_t* q;          // [N, H, D] bf16

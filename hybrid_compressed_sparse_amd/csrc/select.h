@@ -135,8 +135,10 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of, u
     }
     const uint64_t below = (1ull << lane) - 1;
     unsigned run = 0;
-#pragma unroll
-    for (int b = 0; b < 17; ++b) run += (unsigned)__popcll(__ballot((tot >> b) & 1u) & below) << b;
+    // every thread's total is at most `total`, so its bits above nbits are zero (a fixed bit
+    // count would truncate totals of large selections)
+    const int nbits = 32 - __builtin_clz(total | 1u);
+    for (int b = 0; b < nbits; ++b) run += (unsigned)__popcll(__ballot((tot >> b) & 1u) & below) << b;
     if (lane == 63) sh.wsum[wave] = run + tot;
     for (int j = tid; j < kBins; j += NT) sh.hist[(pass & 1) ^ 1][j] = 0;   // the next pass's
     __syncthreads();
@@ -177,15 +179,21 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of, u
 }
 
 // Select the top-k of n elements (n > k) given key_of(i, key) and id_of(i); writes k ids (and
-// scores) in arbitrary order. Ties at the k-th key go to the smaller ids.
+// scores). Ties at the k-th key go to the smaller ids.
 // The radix passes stop as soon as the bin holding the k-th key has at most kCandMax keys;
 // those candidates are gathered and ranked by one wave (larger key first, then smaller id), and
 // the r.need best are taken with every key above the bin. Only a larger bin of keys that are
 // all equal to the k-th falls back to a second select on ~id.
-template <int NT, class KeyOf, class IdOf, class Emit>
+// Slots: with ORDERED the taken elements get slots 0, 1, ... in ascending element order i and
+// the ranked candidates follow in rank order, so the output is the same on every run (each wave
+// walks a contiguous range of elements twice: once to count, once to emit); without it, slots
+// go to waves in completion order (one counter update per wave and 64 elements, no second pass),
+// for callers that only mark the selected ids.
+template <int NT, bool ORDERED = true, class KeyOf, class IdOf, class Emit>
 __device__ void block_topk(SelShared& sh, int n, int k, KeyOf key_of, IdOf id_of, Emit emit) {
   const KthResult r = radix_kth<NT>(sh, n, (unsigned)k, key_of, kCandMax);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NW = NT / 64;
   const uint64_t below = (1ull << lane) - 1;
   const bool partial = r.n_eq > r.need;            // only part of the k-th key's bin is taken
   const bool ranked = partial && r.n_eq <= (unsigned)kCandMax;
@@ -208,12 +216,11 @@ __device__ void block_topk(SelShared& sh, int n, int k, KeyOf key_of, IdOf id_of
     sh.cand_count = 0;
   }
   __syncthreads();
-  // keys above the bin (and the whole bin unless only part of it is taken); the bin's keys go
-  // to the candidate slots when they are ranked. One counter update per wave.
-  for (int i0 = threadIdx.x & ~63; i0 < n; i0 += NT) {
-    const int i = i0 + lane;
-    uint32_t key = 0;
-    bool take = false, cand = false;
+  // element i is taken when its key is above the bin (or in the bin, unless only part of it is
+  // taken); the bin's keys go to the candidate slots when they are ranked
+  auto classify = [&](int i, uint32_t& key, bool& take, bool& cand) {
+    key = 0;
+    take = cand = false;
     if (i < n && key_of(i, key)) {
       const uint32_t km = key & r.mask;
       take = km > r.prefix;
@@ -223,30 +230,70 @@ __device__ void block_topk(SelShared& sh, int n, int k, KeyOf key_of, IdOf id_of
         else take = ((~(uint32_t)id_of(i)) & r2.mask) >= r2.prefix;     // ids are distinct
       }
     }
-    const uint64_t tm = __ballot(take);
-    if (tm != 0) {
+  };
+  auto add_cand = [&](bool cand, uint32_t key, int i) {
+    const uint64_t cm = __ballot(cand);
+    if (cm != 0) {
       unsigned base = 0;
-      if (lane == __builtin_ctzll(tm)) base = atomicAdd(&sh.out_count, (unsigned)__popcll(tm));
-      base = __shfl(base, __builtin_ctzll(tm), 64);
-      if (take) emit(base + (unsigned)__popcll(tm & below), id_of(i), key);
-    }
-    if (ranked) {
-      const uint64_t cm = __ballot(cand);
-      if (cm != 0) {
-        unsigned base = 0;
-        if (lane == __builtin_ctzll(cm)) base = atomicAdd(&sh.cand_count, (unsigned)__popcll(cm));
-        base = __shfl(base, __builtin_ctzll(cm), 64);
-        if (cand) {
-          const unsigned slot = base + (unsigned)__popcll(cm & below);
-          sh.cand_key[slot] = key;
-          sh.cand_id[slot] = id_of(i);
-        }
+      if (lane == __builtin_ctzll(cm)) base = atomicAdd(&sh.cand_count, (unsigned)__popcll(cm));
+      base = __shfl(base, __builtin_ctzll(cm), 64);
+      if (cand) {
+        const unsigned slot = base + (unsigned)__popcll(cm & below);
+        sh.cand_key[slot] = key;
+        sh.cand_id[slot] = id_of(i);
       }
+    }
+  };
+  if constexpr (ORDERED) {
+    // wave w walks chunks [c0, c1) of 64 elements
+    const int nch = (n + 63) >> 6, per = (nch + NW - 1) / NW;
+    const int c0 = min(wave * per, nch), c1 = min(c0 + per, nch);
+    unsigned cnt = 0;
+    for (int c = c0; c < c1; ++c) {
+      uint32_t key;
+      bool take, cand;
+      classify(c * 64 + lane, key, take, cand);
+      cnt += (unsigned)__popcll(__ballot(take));
+      if (ranked) add_cand(cand, key, c * 64 + lane);
+    }
+    if (lane == 0) sh.wsum[wave] = cnt;
+    __syncthreads();
+    unsigned slot = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const unsigned ws = sh.wsum[w];
+      slot += w < wave ? ws : 0u;
+      total += ws;
+    }
+    for (int c = c0; c < c1; ++c) {
+      uint32_t key;
+      bool take, cand;
+      classify(c * 64 + lane, key, take, cand);
+      const uint64_t tm = __ballot(take);
+      if (take) emit(slot + (unsigned)__popcll(tm & below), id_of(c * 64 + lane), key);
+      slot += (unsigned)__popcll(tm);
+    }
+    if (lane == 0 && wave == 0) sh.out_count = total;
+  } else {
+    for (int i0 = threadIdx.x & ~63; i0 < n; i0 += NT) {
+      const int i = i0 + lane;
+      uint32_t key;
+      bool take, cand;
+      classify(i, key, take, cand);
+      const uint64_t tm = __ballot(take);
+      if (tm != 0) {
+        unsigned base = 0;
+        if (lane == __builtin_ctzll(tm)) base = atomicAdd(&sh.out_count, (unsigned)__popcll(tm));
+        base = __shfl(base, __builtin_ctzll(tm), 64);
+        if (take) emit(base + (unsigned)__popcll(tm & below), id_of(i), key);
+      }
+      if (ranked) add_cand(cand, key, i);
     }
   }
   __syncthreads();
   if (ranked && wave == 0) {
-    // rank of candidate `lane` among the n_eq (all in LDS now): larger key first, then smaller id
+    // rank of candidate `lane` among the n_eq (all in LDS now): larger key first, then smaller
+    // id; the r.need best follow every other taken key, in rank order
     const int nc = (int)r.n_eq;
     const uint32_t mk = lane < nc ? sh.cand_key[lane] : 0u;
     const int mi = lane < nc ? sh.cand_id[lane] : 0;
@@ -256,10 +303,8 @@ __device__ void block_topk(SelShared& sh, int n, int k, KeyOf key_of, IdOf id_of
       const int ij = __builtin_amdgcn_readlane(mi, j);
       rank += (kj > mk || (kj == mk && ij < mi)) ? 1u : 0u;
     }
-    const bool take = lane < nc && rank < r.need;
-    const uint64_t tm = __ballot(take);
     const unsigned base = sh.out_count;           // every other key is counted by now
-    if (take) emit(base + (unsigned)__popcll(tm & below), mi, mk);
+    if (lane < nc && rank < r.need) emit(base + rank, mi, mk);
   }
   __syncthreads();
 }

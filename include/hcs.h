@@ -35,7 +35,7 @@
  * Conventions shared by every call
  *   - Pointers are device pointers unless marked "host". The caller owns every buffer; the
  *     library allocates nothing and keeps no state between calls except the thread-local
- *     error text.
+ *     error text and the per-device error word (hcs_device_errors).
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL is the
  *     default stream). Arguments are validated on the host before any launch; a non-OK
  *     status means nothing was launched, and hcs_last_error() describes why.
@@ -49,8 +49,10 @@
  *   A cache is a pool of pages of HCS_PAGE_ROWS = 64 rows. Logical row r of sequence s lives
  *   in page page_table[s * pt_stride + r / 64] at slot r % 64. Logical rows are absolute
  *   positions for the sliding-window cache and entry indices for the compressed and indexer
- *   caches. A page id outside [0, num_pages) (e.g. -1) means "not resident": reads of such a
- *   row are skipped (the row does not take part), writes are dropped.
+ *   caches. A negative page id (e.g. -1) means "not resident": reads of such a row are skipped
+ *   (the row does not take part), writes are dropped. A page id >= num_pages is an error in
+ *   the caller's data: the row is handled as not resident and HCS_DEVERR_PAGE_RANGE is set in
+ *   the device error word (hcs_device_errors).
  *   Inside a page, each field of the 64 rows is stored contiguously (structure of arrays):
  *     HCS_FMT_BF16  dim D : [64][D] bf16                                  (2*D B per row)
  *     HCS_FMT_FP8DS dim 512: [64][448] e4m3 | [64][64] bf16 | [64][8] B    (584 B per row)
@@ -111,6 +113,21 @@ typedef struct {
 
 /* Thread-local text of the last non-OK status returned on this thread ("" if none). */
 const char* hcs_last_error(void);
+
+/* Device error word. Invalid data found on the device by a kernel (where the host cannot see
+ * it before the launch) sets bits in a per-device word that stays set until read and cleared
+ * here; the kernel goes on as stated for the case and the call's status is unaffected.
+ *   HCS_DEVERR_PAGE_RANGE  a page-table entry >= num_pages was met (a corrupt page table): the
+ *                          row is treated as not resident (reads skipped, writes dropped).
+ *   HCS_DEVERR_PAIR_WAIT   the prefill attention's two waves of a head pair did not exchange
+ *                          their block maxima within the bounded wait: some outputs of that
+ *                          call are wrong.
+ * hcs_device_errors waits for all work on the current device (hipDeviceSynchronize), ORs the
+ * device's bits into *bits (host pointer) and, if clear != 0, resets them to zero. Returns
+ * HCS_ERR_INVALID_ARG for a null bits, HCS_ERR_HIP if a HIP call fails. */
+#define HCS_DEVERR_PAGE_RANGE 0x1u
+#define HCS_DEVERR_PAIR_WAIT 0x2u
+hcs_status hcs_device_errors(uint32_t* bits, int clear);
 /* HCS_ABI_VERSION of the loaded library. */
 int hcs_abi_version(void);
 
@@ -212,11 +229,12 @@ hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w,
                           void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------ */
-/* Two-level candidate filtering ("DeepSeek V4.1 attention", `DeepseekV4Indexer`: the      */
-/* indexer of the candidate source layer also publishes its top blocks of consecutive      */
-/* compressed positions; later indexers mask their scores to those blocks before their own  */
-/* top-k). Arguments and scores as hcs_index_topk, plus cand_block (entries per block:      */
-/* block j = entries j*cand_block .. j*cand_block+cand_block-1) and n_cand. Exactly one of:  */
+/* Two-level candidate filtering ("DeepSeek V4.1 attention", `DeepseekV4Indexer`: besides  */
+/* its own top-k, the indexer of the source layer lists its best blocks of consecutive      */
+/* compressed positions, and a consumer layer restricts its top-k to entries inside the     */
+/* listed blocks). Arguments and scores as hcs_index_topk, plus cand_block (entries per     */
+/* block: block j = entries j*cand_block .. j*cand_block+cand_block-1) and n_cand. Exactly  */
+/* one of:                                                                                  */
 /*   cand_out [N, n_cand] int32 (source): after the top-k, the n_cand blocks with the       */
 /*            largest block score (the max of the block's visible entries' scores), ties to */
 /*            the smaller block id, in no particular order, -1 at the tail when the query   */

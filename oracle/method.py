@@ -26,10 +26,10 @@ Sources (DeepSeek-V4 pages):
     n_head**-0.5; `_produce_k`: k_norm (an RMSNorm) of the projected latent at
     group-boundary tokens, RoPE at the group position, quantization into the key cache;
     `_indexer_k_cache_head_dim`: 68-byte MXFP4 and 132-byte FP8 rows).
-  * candidate filtering -- same page, `DeepseekV4Indexer` docstring: the indexer of the
-    candidate source layer also publishes its top blocks of consecutive compressed
-    positions, and later indexers mask their scores to those blocks before their own
-    top-k (readings: a block's score is the max of its entries; entries outside the
+  * candidate filtering -- same page, `DeepseekV4Indexer` docstring: besides its own
+    top-k, the source layer's indexer lists its best blocks of consecutive compressed
+    positions, and a consumer layer restricts its top-k to entries inside the listed
+    blocks (readings: a block's score is the max of its entries; entries outside the
     blocks do not take part, and fewer than k taking part are all selected, -1 padded).
   * query preparation and SWA insert -- same page, "Default stream" (the fused
     q-norm / RoPE / KV insert: per-head RMSNorm of the query heads, GPT-J RoPE on

@@ -147,3 +147,9 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(hcs, "LIB_PATH", "/nonexistent/libhcs.so")
     with pytest.raises(hcs.HcsError):
         hcs.lib()
+
+
+@needs_lib
+def test_device_errors_rejects_null_before_any_hip_call():
+    L = hcs.lib()
+    assert L.hcs_device_errors(None, 1) == 1 and b"null bits" in L.hcs_last_error()

@@ -32,7 +32,9 @@ def _check_step(sc, queries=None, sink=None, split_at=None, check_entries=True):
         for b in range(len(sc.c_cu) - 1):
             U.check_entries(sc, step, dbg, ref["produced"], b)
     worst = 0.0
-    for t in qs:
+    for n_done, t in enumerate(qs):
+        if n_done and n_done % 16 == 0:
+            U.say(f"[progress] {n_done} of {len(qs)} queries compared")
         if wl.indexer:
             U.check_topk(step.idx[t].cpu().numpy(), step.score[t].cpu().numpy(), ref["topk"][t],
                          ref["scores"][t], wl.topk)
@@ -86,9 +88,9 @@ def test_hca_decode_small():
     _check_step(sc)
 
 
-def test_hca_decode_full_sampled():
+def test_hca_decode_full():
     sc = G.build(C.HCA_DECODE, seed=0, device=_dev())
-    _check_step(sc, queries=[0, 17, 63])
+    _check_step(sc)
 
 
 def test_hca_ratio_one_no_window_is_causal_attention():
@@ -124,9 +126,9 @@ def test_mxfp4_filter_bound_regimes():
     _check_step(sc)
 
 
-def test_fp8_decode_1m_sampled():
+def test_fp8_decode_1m_full():
     sc = G.build(C.CSA_DECODE_1M_FP8, seed=0, device=_dev())
-    _check_step(sc, queries=[0, 5])
+    _check_step(sc)
 
 
 def test_prefill_small():
@@ -143,8 +145,12 @@ def test_prefill_long_splits():
 
 
 def test_prefill_full_sampled():
+    """64 of the chunk's 4096 queries, spread over it with both ends: the first queries see the
+    prefix only, the last ones the chunk's own 1024 entries as well."""
     sc = G.build(C.CSA_PREFILL, seed=0, device=_dev())
-    _check_step(sc, queries=[0, 1, 2047, 4095])
+    qs = sorted(set([0, 1, 2, 3] + list(range(67, 4032, 67)) + [4092, 4093, 4094, 4095]))
+    assert len(qs) >= 64
+    _check_step(sc, queries=qs)
 
 
 def test_indexer_chunk_matches_per_query_path():
