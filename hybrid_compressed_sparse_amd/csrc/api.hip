@@ -473,8 +473,8 @@ hcs_status hcs_index_topk_compress(const void* q, const uint8_t* q_scale, const 
     return hip_status(hcs::launch_compress(c, max_new, st), "compress_kv");
   }
   hipError_t e;
-  if (keys.fmt == HCS_FMT_BF16 && !plan.large)
-    e = hcs::launch_index_scores_compress(a, c, max_new, st);
+  if ((keys.fmt == HCS_FMT_BF16 && !plan.large) || keys.fmt == HCS_FMT_MXFP4)
+    e = hcs::launch_index_scores_compress(a, c, max_new, keys.fmt, st);
   else {
     e = B > 0 ? hcs::launch_compress(c, max_new, st) : hipSuccess;
     if (e == hipSuccess) e = hcs::launch_index_scores(a, keys.fmt, st);
@@ -513,8 +513,8 @@ hcs_status hcs_index_scores_compress(const void* q, const uint8_t* q_scale, cons
   }
   if (N == 0) return B > 0 ? hip_status(hcs::launch_compress(c, max_new, st), "compress_kv") : ok();
   hipError_t e;
-  if (B > 0 && keys.fmt == HCS_FMT_BF16 && a.nv_cap <= 32768)
-    e = hcs::launch_index_scores_compress(a, c, max_new, st);
+  if (B > 0 && ((keys.fmt == HCS_FMT_BF16 && a.nv_cap <= 32768) || keys.fmt == HCS_FMT_MXFP4))
+    e = hcs::launch_index_scores_compress(a, c, max_new, keys.fmt, st);
   else {
     e = B > 0 ? hcs::launch_compress(c, max_new, st) : hipSuccess;
     if (e == hipSuccess) e = hcs::launch_index_scores(a, keys.fmt, st);

@@ -4,28 +4,23 @@
 // every query head attends over the query's sliding-window rows plus its selected (CSA) or all
 // visible (HCA) compressed entries; K and V are the same shared row.
 //
-// Building blocks shared by both kernels:
-//   * a workgroup first resolves the physical row of every logical row it will read (window
-//     position or compressed id -> page table -> page, slot) into an LDS table, with all
-//     loads issued together and no branches, so each later row load is a single independent
-//     gather; rows that do not take part read a zero row;
-//   * rows are walked in blocks through an LDS ring (64-row blocks, double-buffered, in the
-//     16-head kernel; 32-row blocks in a ring of four in the all-heads kernel), swizzled so that
-//     both readers below are free of bank conflicts;
+// Design:
+//   * a workgroup is (query, split of its rows, 64 heads), so each gathered row is read once for
+//     all heads of the query; it first resolves the physical row of every logical row it will
+//     read (window position or compressed id -> page table -> page, slot) into an LDS table,
+//     with all loads issued together and no branches, so each later row load is a single
+//     independent gather; rows that do not take part read a zero row;
+//   * rows are walked in 32-row blocks through a ring of four LDS tiles, their 16-byte chunks
+//     swizzled so that both readers below are free of bank conflicts. bf16 rows go straight
+//     from the paged cache into LDS with global_load_lds; quantized rows (fp8_ds, MXFP8, NVFP4)
+//     come through registers one block ahead and are written dequantised to bf16 (every
+//     format's values are exact in bf16);
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (rows on M, 16 heads on N, q in registers as
 //     the B operand), whose accumulator layout is the one P^T is written in, then
 //     O^T += V^T P^T with V^T read from the same LDS rows by ds_read_b64_tr_b16 (16-bit
 //     transpose across each 16-lane group); online softmax in base 2, one head per lane % 16;
 //   * a query's rows may be split over several workgroups; their partial (O, max, sum) are
 //     merged by a second kernel.
-//
-// All-heads kernel (bf16 rows): a workgroup is (query, split, 64 heads), so each gathered row is
-// read once for all heads of the query; bf16 rows go straight from the paged cache into LDS with
-// global_load_lds.
-// 16-head kernel (quantized rows: fp8_ds, MXFP8, NVFP4): a workgroup is (query, split, 16
-// heads); rows are dequantised through registers on their way into LDS (every format's values
-// are exact in bf16). The head
-// groups of a query run on one XCD, so a row fetched by one of them is an L2 hit for the others.
 #include "kernels.h"
 #include "select.h"
 
@@ -75,11 +70,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// two e4m3 values (bytes 0-1, or 2-3 with HI) times the power of two sc, as bf16 (exact: the
+// product has at most four significant bits), by one scaled hardware conversion
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, float sc) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-  return (__float_as_uint(f.x * sc) >> 16) | (__float_as_uint(f.y * sc) & 0xffff0000u);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, sc, HI);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
 }
 
 // The rows a query attends: window positions lo..lo+n_swa-1, then n_comp compressed slots.
@@ -104,50 +103,6 @@ __device__ __forceinline__ QueryRows query_rows(const AttnArgs& a, int t) {
   return q;
 }
 
-// Fill rowtab[0 .. n) with the entries of logical rows r0 .. r0+n-1 (all threads of the block),
-// and rowtab[n .. n rounded up to `pad`) with kNoRow.
-// Every thread resolves up to kRowsPerThread rows; all id loads are issued, then all page-table
-// loads, so the table costs two memory latencies whatever its length.
-constexpr int kRowsPerThread = (kMaxRowsWG + kThreads - 1) / kThreads;
-
-__device__ __forceinline__ void fill_rowtab(const AttnArgs& a, int t, const QueryRows& q, int r0,
-                                            int n, uint32_t* rowtab, int pad) {
-  int id[kRowsPerThread];
-  const int last = max(q.R - 1, 0);
-#pragma unroll
-  for (int i = 0; i < kRowsPerThread; ++i) {
-    const int gr = min(r0 + (int)threadIdx.x + i * kThreads, last);
-    const int j = min(max(gr - q.n_swa, 0), max(q.n_comp - 1, 0));
-    id[i] = a.topk_idx ? __ldg(a.topk_idx + (int64_t)t * a.topk + j) : j;
-  }
-  int pg[kRowsPerThread], row[kRowsPerThread];
-#pragma unroll
-  for (int i = 0; i < kRowsPerThread; ++i) {
-    const int gr = min(r0 + (int)threadIdx.x + i * kThreads, last);
-    const bool is_swa = gr < q.n_swa;
-    const bool ok_id = is_swa || (id[i] >= 0 && id[i] < q.nv);
-    row[i] = ok_id ? (is_swa ? q.lo + gr : id[i]) : -1;
-    const int rc = max(row[i], 0);
-    const int32_t* pt = is_swa ? a.swa.pt : a.comp.pt;
-    const int stride = is_swa ? a.swa.pt_stride : a.comp.pt_stride;
-    pg[i] = __ldg(pt + (int64_t)q.seq * stride + (rc >> 6));
-  }
-  const int n32 = min((n + pad - 1) / pad * pad, kMaxRowsWG);   // padded with kNoRow to whole tiles
-#pragma unroll
-  for (int i = 0; i < kRowsPerThread; ++i) {
-    const int li = (int)threadIdx.x + i * kThreads;
-    const int gr = r0 + li;
-    if (li < n32) {
-      const bool is_swa = gr < q.n_swa;
-      const int npages = is_swa ? a.swa.num_pages : a.comp.num_pages;
-      const bool used = li < n && gr < q.R && row[i] >= 0;
-      if (used && pg[i] >= npages) dev_error(HCS_DEVERR_PAGE_RANGE);
-      const bool ok = used && pg[i] >= 0 && pg[i] < npages;
-      rowtab[li] = ok ? ((is_swa ? 0u : 0x80000000u) | (uint32_t)(pg[i] * 64 + (row[i] & 63))) : kNoRow;
-    }
-  }
-}
-
 // Entries of a sequence's compressed page table that the all-heads kernel keeps in LDS.
 constexpr int kPtCache = 2048;
 
@@ -156,14 +111,14 @@ constexpr int kPtCache = 2048;
 // together with the selected ids and the window rows' page entries, so that a selected row's
 // page is then an LDS lookup. A sequence with more pages than that reads them from memory.
 // rowtab[0 .. n rounded up to `pad`) is written; ends with a barrier.
-template <int NT>
+template <int NT, int PTC = kPtCache>
 __device__ __forceinline__ void fill_rows(const AttnArgs& a, int t, const QueryRows& q, int r0, int n,
                                           uint32_t* rowtab, int* ptl, int pad) {
   constexpr int RPT = (kMaxRowsWG + NT - 1) / NT;
-  constexpr int PPT = kPtCache / NT;
+  constexpr int PPT = PTC / NT;
   const int tid = threadIdx.x;
   const int npg = (q.nv + 63) >> 6;
-  const bool cached = npg <= kPtCache;
+  const bool cached = npg <= PTC;
   const int32_t* cpt = a.comp.pt + (int64_t)q.seq * a.comp.pt_stride;
   const int32_t* spt = a.swa.pt + (int64_t)q.seq * a.swa.pt_stride;
   int pv[PPT];
@@ -500,19 +455,6 @@ struct QuantStage {
 constexpr float kLazy = 8.f;
 constexpr float kLazyBlock = 32.f;
 
-template <int D>
-__device__ __forceinline__ void load_q(const AttnArgs& a, int t, int head, bf16x8* qreg) {
-  constexpr int KS = D / 32;
-  const int g = (threadIdx.x & 63) >> 4;
-  const bool hv = head < a.H;
-  const uint16_t* qrow = a.q + ((int64_t)t * a.H + (hv ? head : 0)) * D;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    i32x4 v = hv ? *(const i32x4*)(qrow + 32 * ks + 8 * g) : i32x4{0, 0, 0, 0};
-    qreg[ks] = __builtin_bit_cast(bf16x8, v);
-  }
-}
-
 // Final (m, l) of one head with the optional sink; returns the factor to apply to O.
 __device__ __forceinline__ float finish_head(const AttnArgs& a, int head, float& m, float& l) {
   if (!a.sink) return 1.f;
@@ -541,268 +483,47 @@ __device__ __forceinline__ float lse_of(float m, float l) {
 
 
 
-// ================================================================ 16-head kernel (fp8_ds)
-// A block is (query, split of its rows, 16 heads); it walks its rows in 64-row blocks held in a
-// double-buffered LDS ring. Wave w loads rows 16w..16w+15 of the next block into registers
-// while the current one is processed and writes them dequantised at the start of the next.
-// Wave w computes S^T for its 16 rows, the waves agree on the block's max per head through LDS,
-// each writes its rows' probabilities (bf16) to LDS, and each accumulates O^T for its own
-// quarter of the output columns over all 64 rows: 32 accumulator registers per lane, no
-// cross-wave merge of O.
-template <class S>
-__global__ __launch_bounds__(kThreads, 1) void mla_fp8_kernel(AttnArgs a) {
-  constexpr int D = S::D, RS = S::RS, KS = D / 32;
-  constexpr int CTW = D / 16 / 4;                 // 16-column output tiles per wave
-  constexpr int BT = 64;                          // rows per block
-  constexpr int WR = BT / 4;                      // rows per wave
-  constexpr int PR = BT + 8;                      // P row stride (elements), padded
-  constexpr int NLD = WR;                         // one row per register load
-  static_assert(WR == 16, "a wave reads its rows' entries as one 16-lane LDS read");
-  __shared__ __attribute__((aligned(16))) uint8_t tile0[BT * RS];
-  __shared__ __attribute__((aligned(16))) uint8_t tile1[BT * RS];
-  // packed (cache, page, slot) entries of the rows
-  __shared__ __attribute__((aligned(16))) uint32_t rowtab[kMaxRowsWG];
-  __shared__ __attribute__((aligned(16))) __bf16 p_lds0[16 * PR];
-  __shared__ __attribute__((aligned(16))) __bf16 p_lds1[16 * PR];
-  __shared__ float mx[4][16];
-  __shared__ float lsum[4][16];
-  __shared__ int flag0[4], flag1[4];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, l16 = lane & 15;
-  // block -> (query, split, head group) with all blocks of a query on one XCD
-  const int G = a.nsplit * a.n_hg;
-  const int xcd = blockIdx.x & 7, r = blockIdx.x >> 3;
-  const int t = (r / G) * 8 + xcd;
-  if (t >= a.N) return;
-  const int j = r - (r / G) * G;
-  const int s = j / a.n_hg, hg = j - (j / a.n_hg) * a.n_hg;
-
-  const QueryRows q = query_rows(a, t);
-  const int r0 = s * a.rows_per_split;
-  const int n_rows = max(0, min(q.R, r0 + a.rows_per_split) - r0);
-  fill_rowtab(a, t, q, r0, n_rows, rowtab, BT);
-  // q of the 16 heads as the B operand (same for the 4 waves)
-  bf16x8 qreg[KS];
-  load_q<D>(a, t, hg * 16 + l16, qreg);
-
-  f32x4 oacc[CTW];
-#pragma unroll
-  for (int ct = 0; ct < CTW; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegInf, l_part = 0.f;
-  const int nblk = (n_rows + BT - 1) / BT;
-
-  i32x4 pre[NLD];
-  int psc[NLD];
-  __syncthreads();
-
-  // load this wave's rows of block b into registers (written to LDS at the start of block b)
-  const uint8_t* swa_base = a.swa.base;
-  const uint8_t* comp_base = a.comp.base;
-  // (the wave's 16 entries come in one LDS read, lane i holding entry i, and go to the scalar
-  // unit by readlane: one LDS wait per block rather than one per row)
-  uint32_t pcf = 0;                                    // bit i: row i of the wave is a CF row
-  auto issue = [&](int b) __attribute__((always_inline)) {
-    const uint32_t mine = rowtab[b * BT + wave * WR + (lane & 15)];
-    pcf = 0;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i)
-      pcf |= (S::load(swa_base, comp_base, (uint32_t)__builtin_amdgcn_readlane((int)mine, i), lane, pre[i],
-                      psc[i]) ? 1u : 0u) << i;
-  };
-  if (nblk > 0) issue(0);
-
-  // lane-constant LDS offsets
-  // K row 16w + l16, chunk (4ks + g) ^ s = 4 (ks ^ (s >> 2)) + ((g ^ s) & 3), s = swz_dec(l16)
-  const int sk = swz_dec(l16);
-  const int koff = (wave * WR + l16) * RS + ((g ^ sk) & 3) * 16;
-  int ko4[4];
-#pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4) ko4[k4] = koff + 64 * (k4 ^ (sk >> 2));
-  // V^T rows 8g + jv and 8g + 4 + jv of a 32-row step: swz_dec = 2 jv + 8 (g & 1) (+1), so
-  // chunk (2 ctg + h) lands at 2 (ctg ^ (jv + 4 (g & 1))) + (h, resp. h ^ 1)
-  const int jv = l16 >> 2, q4 = l16 & 3, h2 = q4 >> 1;
-  const int vx = jv + 4 * (g & 1);
-  const int vrow = (8 * g + jv) * RS + (q4 & 1) * 8;
-  int vo0[8], vo1[8];
-#pragma unroll
-  for (int c8 = 0; c8 < 8; ++c8) {
-    vo0[c8] = vrow + 32 * (c8 ^ vx) + 16 * h2;
-    vo1[c8] = vrow + 4 * RS + 32 * (c8 ^ vx) + 16 * (h2 ^ 1);
-  }
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-  // One block; T holds it, P/F are this block's probability buffer and flags (alternating, so
-  // a wave may write the next block's while another still reads this one's).
-  // Shared reference max: every wave uses the same m_ref for the whole block, so each can
-  // write its rows' probabilities for the column-split PV. A wave whose scores exceed
-  // m_ref + kLazyBlock raises a flag; only then do the waves exchange maxima and rescale.
-  auto block = [&](int b, uint8_t* T, __bf16* P, int* F) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) S::store(T, wave * WR + i, swz_dec(i), lane, pre[i], psc[i], (pcf >> i) & 1u);
-    lds_barrier();                                       // block b is in LDS
-    if (b + 1 < nblk) issue(b + 1);
-    const bool vr = rowtab[b * BT + wave * WR + (lane & 15)] != kNoRow;
-    const uint32_t valid = (uint32_t)__ballot(vr && lane < 16);
-    // ---- S^T for this wave's 16 rows (two accumulators halve the dependent chain)
-    f32x4 sacc2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ko = ko4[ks & 3] + (ks >> 2) * 256;
-      const bf16x8 av = *(const bf16x8*)(T + ko);
-      sacc2[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[ks], sacc2[ks & 1], 0, 0, 0);
-    }
-    const f32x4 sacc = sacc2[0] + sacc2[1];
-    float x[4];
-    float tmax = kNegInf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * g + i;
-      x[i] = ((valid >> row) & 1u) ? sacc[i] * a.scale_log2 : kNegInf;
-      tmax = fmaxf(tmax, x[i]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const bool over = tmax > m_ref + kLazyBlock;
-    const bool any_over = __any(over);
-    float mr = m_ref == kNegInf ? 0.f : m_ref;
-    bf16x4 p4;
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pv = __builtin_amdgcn_exp2f(x[i] - mr);
-      psum += pv;
-      p4[i] = (__bf16)pv;
-    }
-    if (g == 0) mx[wave][l16] = tmax;
-    if (lane == 0) F[wave] = any_over ? 1 : 0;
-    if (!any_over) *(bf16x4*)(P + l16 * PR + wave * WR + 4 * g) = p4;
-    lds_barrier();                                       // probabilities (or flags) of the block
-    if (F[0] | F[1] | F[2] | F[3]) {
-      // rare: a new reference max for the heads whose block max is above m_ref + kLazy
-      const float bmax = fmaxf(fmaxf(mx[0][l16], mx[1][l16]), fmaxf(mx[2][l16], mx[3][l16]));
-      const bool grow = bmax > m_ref + kLazy;
-      const float mnew = grow ? bmax : m_ref;
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - mnew);
-      l_part *= alpha;
-#pragma unroll
-      for (int ct = 0; ct < CTW; ++ct) oacc[ct] *= alpha;
-      m_ref = mnew;
-      mr = m_ref == kNegInf ? 0.f : m_ref;
-      psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(x[i] - mr);
-        psum += pv;
-        p4[i] = (__bf16)pv;
-      }
-      *(bf16x4*)(P + l16 * PR + wave * WR + 4 * g) = p4;
-      lds_barrier();
-    }
-    l_part += psum;
-    // ---- O^T (this wave's columns) += V^T P^T over the block's 64 rows
-#pragma unroll
-    for (int kk = 0; kk < BT / 32; ++kk) {
-      const bf16x8 pb = *(const bf16x8*)(P + l16 * PR + kk * 32 + 8 * g);
-      const uint8_t* vb = T + kk * 32 * RS;
-#pragma unroll
-      for (int ct = 0; ct < CTW; ++ct) {
-        const int ctg = wave * CTW + ct;
-        const int hi = (ctg >> 3) * 256;
-        const i16x4 v0 = lds_read_tr16(vb + vo0[ctg & 7] + hi);
-        const i16x4 v1 = lds_read_tr16(vb + vo1[ctg & 7] + hi);
-        const i16x8 v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pb, oacc[ct],
-                                                           0, 0, 0);
-      }
-    }
-  };
-  for (int b = 0; b < nblk; b += 2) {
-    block(b, tile0, p_lds0, flag0);
-    if (b + 1 < nblk) block(b + 1, tile1, p_lds1, flag1);
-  }
-
-  // ---- sums over the waves' rows (all waves share m_ref)
-  float lw = l_part + __shfl_xor(l_part, 16, 64);
-  lw += __shfl_xor(lw, 32, 64);
-  if (g == 0) lsum[wave][l16] = lw;
-  __syncthreads();
-  float L = lsum[0][l16] + lsum[1][l16] + lsum[2][l16] + lsum[3][l16];
-  float M = m_ref;
-  const int hh = hg * 16 + l16;
-  const bool hv = hh < a.H;
-  // lane holds O^T[c = 16 ctg + 4g + i][head l16] for ctg = wave * CTW + ct
-  if (a.nsplit == 1) {
-    if (!hv) return;
-    const float f = finish_head(a, hh, M, L);
-    const float inv = L > 0.f ? f / L : 0.f;
-    uint16_t* orow = a.out + ((int64_t)t * a.H + hh) * D;
-#pragma unroll
-    for (int ct = 0; ct < CTW; ++ct) {
-      const f32x4 o = oacc[ct] * inv;
-      uint2 pk;
-      pk.x = pack_bf16x2(o[0], o[1]);
-      pk.y = pack_bf16x2(o[2], o[3]);
-      *(uint2*)(orow + 16 * (wave * CTW + ct) + 4 * g) = pk;
-    }
-    if (a.lse && g == 0 && wave == 0) a.lse[(int64_t)t * a.H + hh] = lse_of(M, L);
-    return;
-  }
-
-  // ---- split: write this split's partial (unnormalised O, reference max, sum); a second
-  // kernel merges the splits (a kernel boundary orders the writes before the reads on every
-  // XCD, which in-kernel device-scope fences would do at a far higher cost)
-  const int64_t prow = ((int64_t)(t * a.n_h16 + hg) * a.nsplit + s) * 16 + l16;
-  uint16_t* po = a.ws_o + prow * D;
-  const float pinv = L > 0.f ? 1.f / L : 0.f;         // partial rows are stored normalised, bf16
-#pragma unroll
-  for (int ct = 0; ct < CTW; ++ct) {
-    const f32x4 o = oacc[ct] * pinv;
-    uint2 pk;
-    pk.x = pack_bf16x2(o[0], o[1]);
-    pk.y = pack_bf16x2(o[2], o[3]);
-    *(uint2*)(po + 16 * (wave * CTW + ct) + 4 * g) = pk;
-  }
-  if (g == 0 && wave == 0) {
-    a.ws_ml[prow * 2 + 0] = M;
-    a.ws_ml[prow * 2 + 1] = L;
-  }
-}
-
-// Merge the split partials of one query's heads: a block is (query, 4 heads), a wave one head,
-// each lane D/64 columns. A partial row holds that split's output normalised by its own sum
-// (bf16) and ws_ml its (max, sum) in log2 units; the merge weights split s by
-// sum_s * 2^(max_s - max). Splits are taken eight at a time with all their loads issued
-// together, merged online, so a query with up to eight splits costs one memory latency.
-template <int D>
+// Merge the split partials of one query head: a block is (query, head); its four waves take
+// every fourth split (wave w: splits w, w + 4, ...), each lane D/64 columns, and the waves' merged
+// parts are combined through LDS. A partial row holds that split's output normalised by its own
+// sum (bf16) and ws_ml its (max, sum) in log2 units; the merge weights split s by
+// sum_s * 2^(max_s - max). A wave takes U of its splits at a time (U >= nsplit / 4 when nsplit
+// <= 4 U), every load of a batch issued at a clamped split index before any is used (a load
+// under a condition would be a branch, and each branch a wait for that load alone), merged
+// online: one memory latency per batch.
+template <int D, int U>
 __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
   constexpr int PER = D / 64;                       // 8 (one 16-byte load) or 2 (4 bytes)
-  constexpr int U = 8;
-  const int t = blockIdx.x, h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  constexpr int NW = kThreads / 64;
+  __shared__ float wpart[NW][D];
+  __shared__ float wml[NW][2];
+  const int t = blockIdx.x, h = blockIdx.y, wave = threadIdx.x >> 6;
   const int c0 = (threadIdx.x & 63) * PER;
-  if (h >= a.H) return;
   const int64_t pbase = ((int64_t)(t * a.n_h16 + h / 16) * a.nsplit) * 16 + (h & 15);  // split 0
+  const int ns = a.nsplit, mine = (ns - wave + NW - 1) / NW;   // splits wave, wave + NW, ...
   float acc[PER];
 #pragma unroll
   for (int c = 0; c < PER; ++c) acc[c] = 0.f;
   float Ms = kNegInf, Ls = 0.f;
-  for (int s0 = 0; s0 < a.nsplit; s0 += U) {
+  for (int j0 = 0; j0 < mine; j0 += U) {
     float ms[U], ls[U];
     uint32_t v[U][PER / 2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool in = s0 + u < a.nsplit;
-      const int64_t pr = pbase + (int64_t)min(s0 + u, a.nsplit - 1) * 16;
-      ms[u] = in ? a.ws_ml[pr * 2] : kNegInf;
-      ls[u] = in ? a.ws_ml[pr * 2 + 1] : 0.f;
+      const int sp = min(wave + NW * (j0 + u), ns - 1);
+      const int64_t pr = pbase + (int64_t)sp * 16;
+      ms[u] = a.ws_ml[pr * 2];
+      ls[u] = a.ws_ml[pr * 2 + 1];
       const uint16_t* src = a.ws_o + pr * D + c0;
       if constexpr (PER == 8) {
-        const i32x4 w = in ? *(const i32x4*)src : i32x4{0, 0, 0, 0};
+        const i32x4 w = *(const i32x4*)src;
         v[u][0] = w.x; v[u][1] = w.y; v[u][2] = w.z; v[u][3] = w.w;
       } else {
-        v[u][0] = in ? *(const uint32_t*)src : 0u;
+        v[u][0] = *(const uint32_t*)src;
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) ls[u] = j0 + u < mine ? ls[u] : 0.f;   // past this wave's last split
     float mb = Ms;
 #pragma unroll
     for (int u = 0; u < U; ++u) mb = ls[u] > 0.f ? fmaxf(mb, ms[u]) : mb;
@@ -823,12 +544,34 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
       }
     }
   }
-  const float f = finish_head(a, h, Ms, Ls);
-  const float inv = Ls > 0.f ? f / Ls : 0.f;
+  // the waves' parts: (max, sum) and the unnormalised sums relative to their own max
+#pragma unroll
+  for (int c = 0; c < PER; ++c) wpart[wave][c0 + c] = acc[c];
+  if ((threadIdx.x & 63) == 0) {
+    wml[wave][0] = Ms;
+    wml[wave][1] = Ls;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = wml[w][1] > 0.f ? fmaxf(M, wml[w][0]) : M;
+  float L = 0.f, o[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) o[c] = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float f = wml[w][1] > 0.f ? __builtin_amdgcn_exp2f(wml[w][0] - M) : 0.f;
+    L += f * wml[w][1];
+#pragma unroll
+    for (int c = 0; c < PER; ++c) o[c] += f * wpart[w][c0 + c];
+  }
+  const float f = finish_head(a, h, M, L);
+  const float inv = L > 0.f ? f / L : 0.f;
   uint16_t* orow = a.out + ((int64_t)t * a.H + h) * D + c0;
 #pragma unroll
-  for (int c = 0; c < PER; c += 2) *(uint32_t*)(orow + c) = pack_bf16x2(acc[c] * inv, acc[c + 1] * inv);
-  if (a.lse && (threadIdx.x & 63) == 0) a.lse[(int64_t)t * a.H + h] = lse_of(Ms, Ls);
+  for (int c = 0; c < PER; c += 2) *(uint32_t*)(orow + c) = pack_bf16x2(o[c] * inv, o[c + 1] * inv);
+  if (a.lse && (threadIdx.x & 63) == 0) a.lse[(int64_t)t * a.H + h] = lse_of(M, L);
 }
 
 // ================================================================ all-heads kernel (bf16)
@@ -851,8 +594,10 @@ constexpr int kHeadsThreads = 512;
 // s_waitcnt vmcnt(n) (gfx9 encoding, n < 16): expcnt and lgkmcnt not waited for
 #define HCS_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
-template <int D, bool SEL, bool PAIR>
+template <int D, bool SEL, bool PAIR, int SF = HCS_FMT_BF16, int CF = HCS_FMT_BF16>
 __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a) {
+  constexpr bool QR = SF != HCS_FMT_BF16;         // quantized rows, dequantised through registers
+  static_assert(!QR || (D == 512 && !SEL), "quantized rows are 512 wide, bf16 selection only");
   constexpr int RS = D * 2, KS = D / 32;
   constexpr int BT = 32;                          // rows per block
   constexpr int TB = BT * RS;                     // bytes per tile
@@ -865,10 +610,16 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   constexpr int PD = 4;                           // K-fragment steps read ahead in S^T
   static_assert(CTO >= 1 && NLD >= 1 && NLD < 16 && KS % PD == 0, "unsupported head dim");
   static_assert(!SEL || 2 * TB >= kSelScratch, "the row selection's scratch lives in tiles 0-1");
+  // Tiles in the ring: bf16 rows are copied two blocks ahead (four tiles: S on block i, O on
+  // block i-1, copies of i+1 and i+2 in flight); quantized rows are staged one block ahead in
+  // registers and stored at the top of their step (three tiles), and the LDS this frees holds a
+  // longer page-table row (4096 pages: a 1M-token sequence's compressed cache).
+  constexpr int NTL = QR ? 3 : 4;
+  constexpr int PTC = QR ? 2 * kPtCache : kPtCache;
   // tiles 2 and 3 first hold q of the 64 heads (64 rows of RS bytes)
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[4 * TB];
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[NTL * TB];
   __shared__ __attribute__((aligned(16))) uint32_t rowtab[kMaxRowsWG];
-  __shared__ int ptl[kPtCache];
+  __shared__ int ptl[PTC];
   __shared__ __attribute__((aligned(16))) __bf16 p_lds[2][64 * PR];
   __shared__ float alpha_lds[2][64];
   __shared__ __attribute__((aligned(16))) int flags[2][4];
@@ -890,7 +641,8 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   const QueryRows q = query_rows(a, t);
   const int r0 = s * a.rows_per_split;
   const int n_rows = max(0, min(q.R, r0 + a.rows_per_split) - r0);
-  uint8_t* const qstage = tiles + 2 * TB;
+  uint8_t* const qstage = tiles + (NTL - 2) * TB;  // the last two tiles (rows reach them after the
+                                                  // S waves have read q, at the first barrier)
   // q of the block's 64 heads: one contiguous row per head, copied into tiles 2-3 by async
   // loads (wave w: heads 8w..8w+7, chunk c of head h stored at c ^ (h mod 16)); the S waves read
   // it into registers before the first barrier of the block loop, and tile 2 receives rows only
@@ -910,7 +662,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   }
   if (tid < 4) pseq[tid] = 0;                     // ordered by the row table's barriers
   if constexpr (SEL) fill_rows_sel<kHeadsThreads>(a, t, s, q, r0, n_rows, rowtab, ptl, BT, tiles);
-  else fill_rows<kHeadsThreads>(a, t, q, r0, n_rows, rowtab, ptl, BT);
+  else fill_rows<kHeadsThreads, PTC>(a, t, q, r0, n_rows, rowtab, ptl, BT);
   const int nblk = (n_rows + BT - 1) / BT;
 
   // async loads: wave w fills rows WRL w .. +WRL-1 of a block; LDS chunk slot c of row r
@@ -954,18 +706,58 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       }
     }
   };
-  if (nblk > 0) fire(0, prep(0));
-  if (nblk > 1) fire(1, prep(1));
+  // Quantized rows: wave w loads rows WRL w .. +WRL-1 of block i+1 into registers (16 bytes and a
+  // scale byte per lane, the same load shape for every format) during step i, and writes them
+  // dequantised to bf16 into the block's tile, chunk-swizzled as the copies above, at the top of
+  // step i+1; tile i mod 4 was last read by the O waves three steps before.
+  using QS = QuantStage<QR ? SF : HCS_FMT_FP8DS, QR ? CF : HCS_FMT_FP8DS>;
+  i32x4 qv[QR ? WRL : 1];
+  int qsc[QR ? WRL : 1];
+  uint32_t qcf = 0;
+  auto qload = [&](int b) {
+    if constexpr (QR) {
+      const uint32_t my = rowtab[b * BT + WRL * wave + (lane & (WRL - 1))];
+      qcf = 0;
+#pragma unroll
+      for (int i = 0; i < WRL; ++i)
+        qcf |= (QS::load(a.swa.base, a.comp.base, (uint32_t)__builtin_amdgcn_readlane((int)my, i), lane, qv[i],
+                         qsc[i]) ? 1u : 0u) << i;
+    }
+  };
+  auto qstore = [&](int b) {
+    if constexpr (QR) {
+      uint8_t* tb = tiles + (b % NTL) * TB;
+#pragma unroll
+      for (int i = 0; i < WRL; ++i) {
+        const int r = WRL * wave + i;
+        QS::store(tb, r, swz_dec(r & 15), lane, qv[i], qsc[i], (qcf >> i) & 1u);
+      }
+    }
+  };
+  if constexpr (QR) {
+    if (nblk > 0) qload(0);
+  } else {
+    if (nblk > 0) fire(0, prep(0));
+    if (nblk > 1) fire(1, prep(1));
+  }
   // top of block step i: this wave's copies of block i have landed (those of block i+1 may
   // still be in flight), then the barrier makes every wave's copies and the previous step's
   // LDS writes visible, and block i+2's copies go into the tile that block i-2 left
   auto step_sync = [&](int i) {
-    RowSrc r{};
-    if (i + 2 < nblk) r = prep(i + 2);
-    if (i + 1 < nblk) HCS_WAIT_VMCNT(NLD);
-    else wait_vm_zero();
-    lds_barrier();
-    if (i + 2 < nblk) fire(i + 2, r);
+    if constexpr (QR) {
+      if (i < nblk) {
+        qstore(i);
+        if (i + 1 < nblk) qload(i + 1);
+      }
+      lds_barrier();
+    } else {
+      RowSrc r{};
+      if (i + 2 < nblk) r = prep(i + 2);
+      if (i + 1 < nblk) HCS_WAIT_VMCNT(NLD);
+      else wait_vm_zero();
+      lds_barrier();
+      if (i + 2 < nblk) fire(i + 2, r);
+    }
   };
 
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -986,7 +778,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       for (int i = 0; i <= nblk; ++i) {
         step_sync(i);
         if (i == nblk) break;
-        const uint8_t* T = tiles + (i & 3) * TB;
+        const uint8_t* T = tiles + (i % NTL) * TB;
         const int pb = i & 1;
         const uint32_t valid = (uint32_t)__ballot(rowtab[i * BT + (lane & 31)] != kNoRow);
         // ---- S^T[32 rows][16 heads], K fragments read PD k-steps ahead of their MFMAs
@@ -1073,7 +865,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       for (int i = 0; i <= nblk; ++i) {
         step_sync(i);
         if (i == nblk) break;
-        const uint8_t* T = tiles + (i & 3) * TB;
+        const uint8_t* T = tiles + (i % NTL) * TB;
         const int pb = i & 1;
         const uint32_t valid = (uint32_t)__ballot(rowtab[i * BT + 16 * rh + (lane & 15)] != kNoRow) & 0xFFFFu;
         // ---- S^T[16 rows][32 heads], K fragments read PD k-steps ahead of their MFMAs
@@ -1174,7 +966,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       step_sync(i);
       if (i == 0) continue;
       const int b = i - 1;
-      const uint8_t* T = tiles + (b & 3) * TB;
+      const uint8_t* T = tiles + (b % NTL) * TB;
       const int pb = b & 1;
       // the S waves' rescale flags of block b (one read), issued with the operand reads below
       const i32x4 fl = *reinterpret_cast<const i32x4*>(&flags[pb][0]);
@@ -1291,10 +1083,17 @@ hipError_t launch_impl(const AttnArgs& a, hipStream_t stream) {
     }
   } else {
     static_assert(D == QuantStage<SF, CF>::D, "quantized rows are 512 wide");
-    hipLaunchKernelGGL((mla_fp8_kernel<QuantStage<SF, CF>>), grid, dim3(kThreads), 0, stream, a);
+    if (!a.q_seq)
+      hipLaunchKernelGGL((mla_heads_kernel<D, false, true, SF, CF>), grid, dim3(kHeadsThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((mla_heads_kernel<D, false, false, SF, CF>), grid, dim3(kHeadsThreads), 0, stream, a);
   }
-  if (a.nsplit > 1)
-    hipLaunchKernelGGL((mla_combine_kernel<D>), dim3(a.N, (a.H + 3) / 4), dim3(kThreads), 0, stream, a);
+  if (a.nsplit > 1) {
+    const dim3 cg(a.N, a.H);
+    if (a.nsplit <= 8) hipLaunchKernelGGL((mla_combine_kernel<D, 2>), cg, dim3(kThreads), 0, stream, a);
+    else if (a.nsplit <= 16) hipLaunchKernelGGL((mla_combine_kernel<D, 4>), cg, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((mla_combine_kernel<D, 8>), cg, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -1304,8 +1103,8 @@ AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos
   AttnPlan p{};
   const int64_t nv = (int64_t)(max_pos + 1) / m;
   const int64_t rows = (int64_t)std::min(window, max_pos + 1) + (topk > 0 ? topk : nv);
-  // bf16: 64 heads per block (all-heads kernel); fp8_ds: 16 heads per block
-  p.kind = fmt == HCS_FMT_BF16 ? 2 : 0;
+  // 64 heads per block (all-heads kernel) for every row format
+  p.kind = 2;
   const int hpb = p.kind == 2 ? 64 : 16;
   p.n_hg = (H + hpb - 1) / hpb;
   p.n_h16 = (H + 15) / 16;
@@ -1314,9 +1113,10 @@ AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos
   const int64_t blocks = std::max<int64_t>(1, (rows + kBlock - 1) / kBlock);
   const int64_t max_bps = kMaxRowsWG / kBlock;
   const int64_t per_split = (int64_t)((N + 7) / 8) * 8 * p.n_hg;
-  // enough splits to give every CU a block, but (all-heads kernel) at least four blocks each:
-  // a split adds 64 KiB of partial stores and merge reads per query
-  const int64_t min_bps = p.kind == 2 ? 4 : 1;
+  // enough splits to give every CU a block, but at least four blocks each (two for quantized
+  // rows, whose blocks cost less to fetch): a split adds 64 KiB of partial stores and merge reads
+  // per query (measured at the decode configurations: 2 .. 6 blocks per split)
+  const int64_t min_bps = fmt == HCS_FMT_BF16 ? 4 : 2;
   int64_t nsplit = std::max<int64_t>(1, (256 + per_split - 1) / per_split);
   nsplit = std::min(nsplit, std::max<int64_t>(1, blocks / min_bps));
   nsplit = std::max<int64_t>(nsplit, (blocks + max_bps - 1) / max_bps);

@@ -480,22 +480,21 @@ __global__ __launch_bounds__(kChunkThreads, 512 / kChunkThreads) void index_scor
 // its pages in flight at once (the query's codes likewise, from its contiguous rows).
 constexpr int kMx4BlockEntries = 1024;
 
-// (at least four waves per SIMD: 126 VGPRs, no spills; five would spill)
+// One scoring block of query t: entries y * kMx4BlockEntries .. + kMx4BlockEntries - 1.
 template <int MT>
-__global__ __launch_bounds__(kScoreThreads, 4) void index_score_mxfp4_kernel(IndexArgs a) {
+__device__ __forceinline__ void score_block_mxfp4(const IndexArgs& a, int t, int y) {
   constexpr int DI = 128;
   constexpr int CB = DI / 2;                                     // code bytes per row
   constexpr int SB = DI / kMxBlock;                              // scale bytes per row
   constexpr int PAGE = kPageRows * (CB + SB);                    // 4352
   constexpr int SCALES = kPageRows * CB;                         // scale region offset
   constexpr int PPW = kMx4BlockEntries / 4 / kPageRows;          // pages per wave
-  const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  if (a.cand_count && blockIdx.y == 0 && threadIdx.x == 0) a.cand_count[t] = 0u;
+  if (a.cand_count && y == 0 && threadIdx.x == 0) a.cand_count[t] = 0u;
   int seq, nv;
   query_of(a, t, seq, nv);
-  const int e_base = blockIdx.y * kMx4BlockEntries + wave * (PPW * 64);   // first entry of the wave
+  const int e_base = y * kMx4BlockEntries + wave * (PPW * 64);   // first entry of the wave
   // the wave's page ids: lane p < PPW reads page p's table entry
   int my_pg = -1;
   if (lane < PPW && e_base + 64 * lane < nv) {
@@ -560,13 +559,37 @@ __global__ __launch_bounds__(kScoreThreads, 4) void index_score_mxfp4_kernel(Ind
   if (a.blk_thr) {
     // a threshold per wave (its 256 entries are a block of the bound): the kb-th largest key of
     // a full wave block; no barrier
-    const int full = nv / (PPW * 64), wb = blockIdx.y * 4 + wave;
+    const int full = nv / (PPW * 64), wb = y * 4 + wave;
     const int kb = full > 0 ? bound_kb(a.topk, full) : kMaxKb + 1;
     if (wb < full && kb <= kMaxKb) {
       const uint32_t kth = wave_kth_key<PPW * 4>(tkeys, kb);
       if (lane == 0) a.blk_thr[(int64_t)t * a.thr_stride + wb] = kth;
     }
   }
+}
+
+// (at least four waves per SIMD: 126 VGPRs, no spills; five would spill)
+template <int MT>
+__global__ __launch_bounds__(kScoreThreads, 4) void index_score_mxfp4_kernel(IndexArgs a) {
+  score_block_mxfp4<MT>(a, blockIdx.x, blockIdx.y);
+}
+
+// The MXFP4 scoring blocks and the compressor's blocks of one decode step in one grid (as
+// index_score_compress_kernel for bf16 keys): the compressor's blocks first, then query t's
+// scoring block y at t * chunks + y.
+template <int MT>
+__global__ __launch_bounds__(kScoreThreads, 4) void index_score_mxfp4_compress_kernel(IndexArgs a, CompressArgs c,
+                                                                                   int chunks, int cy, int cz) {
+  static_assert(kScoreThreads == kCompressThreads, "one block size for both roles");
+  const int nc = c.B * cy * cz;
+  const int bid = blockIdx.x;
+  if (bid < nc) {                                   // uniform over the block
+    const int z = bid % cz, y = (bid / cz) % cy, b = bid / (cz * cy);
+    compress_block(c, b, y, z, cy);
+    return;
+  }
+  const int i = bid - nc;
+  score_block_mxfp4<MT>(a, i / chunks, i % chunks);
 }
 
 // ---------------------------------------------------------------- FP8 scores (d_I = 128)
@@ -1071,11 +1094,25 @@ hipError_t launch_index_scores(const IndexArgs& a, int fmt, hipStream_t stream) 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_index_scores_compress(const IndexArgs& a, const CompressArgs& c, int max_new,
+hipError_t launch_index_scores_compress(const IndexArgs& a, const CompressArgs& c, int max_new, int fmt,
                                         hipStream_t stream) {
   const int MT = (a.H_I + 15) / 16;
   if (a.N == 0 || a.nv_cap == 0) return launch_compress(c, max_new, stream);
-  if (c.B == 0) return launch_index_scores(a, HCS_FMT_BF16, stream);
+  if (c.B == 0) return launch_index_scores(a, fmt, stream);
+  if (fmt == HCS_FMT_MXFP4) {
+    const dim3 cg = compress_grid(c, max_new);
+    const int chunks = (a.nv_cap + kMx4BlockEntries - 1) / kMx4BlockEntries;
+    const int64_t blocks = (int64_t)cg.x * cg.y * cg.z + (int64_t)a.N * chunks;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)blocks);
+    switch (MT) {
+      case 1: hipLaunchKernelGGL((index_score_mxfp4_compress_kernel<1>), grid, dim3(kScoreThreads), 0, stream, a, c, chunks, (int)cg.y, (int)cg.z); break;
+      case 2: hipLaunchKernelGGL((index_score_mxfp4_compress_kernel<2>), grid, dim3(kScoreThreads), 0, stream, a, c, chunks, (int)cg.y, (int)cg.z); break;
+      case 3: hipLaunchKernelGGL((index_score_mxfp4_compress_kernel<3>), grid, dim3(kScoreThreads), 0, stream, a, c, chunks, (int)cg.y, (int)cg.z); break;
+      default: hipLaunchKernelGGL((index_score_mxfp4_compress_kernel<4>), grid, dim3(kScoreThreads), 0, stream, a, c, chunks, (int)cg.y, (int)cg.z); break;
+    }
+    return hipGetLastError();
+  }
   const dim3 cg = compress_grid(c, max_new);
   const int chunks = (a.nv_cap + 255) / 256;
   const int64_t blocks = (int64_t)cg.x * cg.y * cg.z + (int64_t)a.N * chunks;

@@ -160,9 +160,9 @@ struct TopkPlan {
 };
 TopkPlan topk_plan(int N, int max_pos, int m, int topk);
 hipError_t launch_index_scores(const IndexArgs& a, int fmt, hipStream_t stream);
-// the bf16 per-query scoring blocks and the compressor's blocks in one launch (neither reads
-// what the other writes)
-hipError_t launch_index_scores_compress(const IndexArgs& a, const CompressArgs& c, int max_new,
+// the per-query scoring blocks (bf16 keys with at most 32768 visible entries, or MXFP4 keys) and
+// the compressor's blocks in one launch (neither reads what the other writes)
+hipError_t launch_index_scores_compress(const IndexArgs& a, const CompressArgs& c, int max_new, int fmt,
                                         hipStream_t stream);
 hipError_t launch_topk(const IndexArgs& a, const TopkPlan& plan, int topk, int32_t* out_idx,
                        float* out_score, uint8_t* ws, int blk_entries, hipStream_t stream);

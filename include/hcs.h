@@ -276,8 +276,9 @@ hcs_status hcs_index_topk_chunk(const void* q, const uint8_t* q_scale, const flo
 /* indexer key cache, the compressor writes the KV compressed cache and its state, and    */
 /* neither reads what the other writes. This call is hcs_index_topk(q .. out_score, ws)   */
 /* followed by hcs_compress_kv(kv .. comp) with dbg = NULL, with the same arguments,      */
-/* checks and results; bf16 keys with at most 32768 visible entries score and compress in */
-/* one grid, other cases launch the two as separate kernels. m_ix is the indexer's m      */
+/* checks and results; bf16 keys with at most 32768 visible entries, and MXFP4 keys, score */
+/* and compress in one grid, other cases launch the two as separate kernels. m_ix is the  */
+/* indexer's m                                                                            */
 /* (the keys' compression ratio), m the compressor's. `comp` must not be `keys`.          */
 /* Errors: those of either call; nothing is launched if either set of arguments fails.    */
 hcs_status hcs_index_topk_compress(const void* q, const uint8_t* q_scale, const float* w,

@@ -60,9 +60,11 @@ def test_validation_errors_before_any_launch():
     # attention: workspace too small when the row list is split
     need = L.hcs_sparse_mla_workspace_size(4, 64, 512, 128, 4, 0, 2000)
     assert need > 0
+    # (the size covers the plans of every row format; a split plan of 4 queries needs far more
+    # than 4 KiB whatever the format)
     st = L.hcs_sparse_mla_decode(16, _paged(stride=32), _paged(stride=32), None, 0, 16, 16, None, 4, 64, 512,
                                  128, 4, 2000,
-                                 0.1, 16, None, 256, need - 1, None)
+                                 0.1, 16, None, 256, 4096, None)
     assert st == 3
     # indexer: top-k limits and formats
     st = L.hcs_index_topk(16, None, 16, _paged(0, 128), 16, 16, 4, 64, 128, 4, 5000, 1000, 16, None,

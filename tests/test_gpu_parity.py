@@ -137,6 +137,16 @@ def test_prefill_small():
     _check_step(sc, queries=[0, 1, 2, 3, 150, 297, 298, 299])
 
 
+@pytest.mark.parametrize("fmt", ["fp8ds", "mxfp8"])
+def test_prefill_small_quantized_rows(fmt):
+    """A prefill chunk over quantized window and compressed rows (fp8_ds, or the V4.1 MXFP8 /
+    NVFP4 pair): the head-pair attention with rows dequantised through registers."""
+    wl = C.CSA_PREFILL.with_(P0=4096 + 2, Q=300, topk=256, kv_fmt=fmt,
+                             comp_fmt="nvfp4" if fmt == "mxfp8" else "")
+    sc = G.build(wl, seed=14, device=_dev())
+    _check_step(sc, queries=[0, 1, 2, 3, 150, 297, 298, 299])
+
+
 def test_prefill_long_splits():
     """A query's 1128 rows (18 blocks, the last ragged) in one split of the attention kernel."""
     wl = C.CSA_PREFILL.with_(P0=4096 + 3, Q=256, topk=1000)
@@ -174,13 +184,20 @@ def test_indexer_chunk_matches_per_query_path():
     assert torch.equal(torch.sort(sa, dim=1).values, torch.sort(sb, dim=1).values)
 
 
-def test_index_topk_compress_matches_separate_calls():
+@pytest.mark.parametrize("keys", ["bf16", "mxfp4"])
+def test_index_topk_compress_matches_separate_calls(keys):
     """hcs_index_topk_compress (scoring and compressor blocks in one grid) leaves the same
     scores, selections, compressor state and compressed cache as hcs_compress_kv followed by
-    hcs_index_topk, bit for bit (ragged batch; some streams end a block at the step, some not)."""
+    hcs_index_topk, bit for bit (ragged batch; some streams end a block at the step, some not;
+    MXFP4 keys with fp8_ds rows, one query above 32768 visible entries)."""
     dev = _dev()
-    wl = C.CSA_DECODE.with_(B=5, topk=96)
-    sc = G.build(wl, seed=13, device=dev, ctx_per_seq=[1000, 2049, 4096, 3, 777])
+    if keys == "bf16":
+        wl = C.CSA_DECODE.with_(B=5, topk=96)
+        ctx = [1000, 2049, 4096, 3, 777]
+    else:
+        wl = C.CSA_DECODE_1M_FP8.with_(B=5, topk=300)
+        ctx = [1000, 2049, 4 * 40000 + 3, 3, 777]
+    sc = G.build(wl, seed=13, device=dev, ctx_per_seq=ctx)
     B, d, m = wl.B, wl.d, wl.m
     lens = [sc.c_cu[b + 1] - sc.c_cu[b] for b in range(B)]
     pre = torch.cat([torch.arange(sc.c_cu[b], sc.c_cu[b + 1] - 1, device=dev) for b in range(B)])
