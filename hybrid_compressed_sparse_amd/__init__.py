@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.hcs_sparse_mla_decode.restype = i32
         L.hcs_sparse_mla_decode.argtypes = [vp, Paged, Paged, vp, i32, vp, vp, vp, i32, i32, i32, i32,
                                             i32, i32, f32, vp, vp, vp, sz, vp]
+        L.hcs_sparse_mla_decode_noalloc.restype = i32
+        L.hcs_sparse_mla_decode_noalloc.argtypes = [vp, Paged, Paged, vp, i32, vp, vp, vp, i32, i32, i32, i32,
+                                                    i32, i32, f32, vp, vp, vp]
         L.hcs_sparse_mla_prefill_workspace_size.restype = sz
         L.hcs_sparse_mla_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.hcs_sparse_mla_prefill_chunk.restype = i32
@@ -403,6 +406,21 @@ def sparse_mla_decode(q: torch.Tensor, swa, comp, topk_idx: Optional[torch.Tenso
         _ptr(sink, torch.float32, "sink"), N, H, d, window, m, max_pos, scale,
         _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _ptr(ws, name="ws"),
         0 if ws is None else ws.numel() * ws.element_size(), _stream()), "sparse_mla_decode")
+
+
+def sparse_mla_decode_noalloc(q: torch.Tensor, swa, comp, topk_idx: Optional[torch.Tensor], q_seq: torch.Tensor,
+                              q_pos: torch.Tensor, window: int, m: int, max_pos: int, scale: float,
+                              out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                              sink: Optional[torch.Tensor] = None) -> None:
+    """hcs_sparse_mla_decode_noalloc: hcs_sparse_mla_decode with the library's static scratch
+    instead of a workspace (nothing is allocated)."""
+    N, H, d = q.shape
+    topk = 0 if topk_idx is None else topk_idx.shape[1]
+    _check(lib().hcs_sparse_mla_decode_noalloc(
+        _ptr(q, torch.bfloat16, "q"), _as_paged(swa), _as_paged(comp), _ptr(topk_idx, torch.int32, "topk_idx"),
+        topk, _ptr(q_seq, torch.int32, "q_seq"), _ptr(q_pos, torch.int32, "q_pos"),
+        _ptr(sink, torch.float32, "sink"), N, H, d, window, m, max_pos, scale,
+        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _stream()), "sparse_mla_decode_noalloc")
 
 
 def sparse_mla_decode_select(q: torch.Tensor, swa, comp, scores: torch.Tensor, topk: int,

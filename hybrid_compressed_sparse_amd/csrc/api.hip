@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -651,6 +652,59 @@ hcs_status hcs_sparse_mla_decode_select(const void* q, hcs_paged swa, hcs_paged 
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   return run_attn(a, d, swa.fmt, comp.fmt, window, m, topk, max_pos, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------------------ decode without allocation
+// The split partials of hcs_sparse_mla_decode_noalloc live in this file-scope device array (each
+// device the library runs on holds its own copy until the process ends). Host code never uses
+// the array's name as an address: the address is taken once per device with
+// hipGetSymbolAddress and kept in g_scratch_dev.
+static __device__ __align__(256) uint8_t scratch[HCS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+hcs_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "sparse_mla_decode_noalloc (hipGetDevice)");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HCS_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                 "sparse_mla_decode_noalloc (hipGetSymbolAddress)");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return HCS_OK;
+}
+}  // namespace
+
+hcs_status hcs_sparse_mla_decode_noalloc(const void* q, hcs_paged swa, hcs_paged comp,
+                                         const int32_t* topk_idx, int topk, const int32_t* q_seq,
+                                         const int32_t* q_pos, const float* sink, int N, int H, int d,
+                                         int window, int m, int max_pos, float scale, void* out,
+                                         float* lse, void* stream) {
+  hcs_status s = check_attn(q, swa, comp, topk_idx, topk, N, H, d, window, m, out);
+  if (s != HCS_OK) return s;
+  if (max_pos < 0) return fail(HCS_ERR_INVALID_ARG, "max_pos must be >= 0");
+  if (N == 0) return ok();
+  const size_t need = hcs::attn_plan(N, H, d, window, m, topk_idx ? topk : 0, max_pos, swa.fmt).ws_bytes;
+  if (need > (size_t)HCS_NOALLOC_SCRATCH_BYTES)
+    return fail(HCS_ERR_WORKSPACE_TOO_SMALL, "sparse_mla_decode_noalloc: the call needs %zu bytes of scratch, "
+                "the library's static scratch holds %zu (use hcs_sparse_mla_decode with a workspace)",
+                need, (size_t)HCS_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need) {
+    s = scratch_of_current_device(&ws);
+    if (s != HCS_OK) return s;
+  }
+  return hcs_sparse_mla_decode(q, swa, comp, topk_idx, topk, q_seq, q_pos, sink, N, H, d, window, m, max_pos,
+                               scale, out, lse, ws, need ? (size_t)HCS_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 size_t hcs_sparse_mla_prefill_workspace_size(int Q, int H, int d, int window, int m, int topk, int P0) {

@@ -340,6 +340,23 @@ hcs_status hcs_sparse_mla_decode(const void* q, hcs_paged swa, hcs_paged comp,
                                  float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------ */
+/* hcs_sparse_mla_decode for callers that cannot allocate device memory (code under HIP    */
+/* graph capture, serving loops, harnesses that forbid allocation): the same computation,  */
+/* arguments and results as hcs_sparse_mla_decode, with no workspace argument. The split   */
+/* partials go to a static device array of HCS_NOALLOC_SCRATCH_BYTES inside the library  */
+/* (one per device it runs on, held until the process ends); the call allocates nothing   */
+/* and calls no allocating routine. A call whose split plan needs more scratch than that   */
+/* (hcs_sparse_mla_workspace_size) returns HCS_ERR_WORKSPACE_TOO_SMALL before any launch. */
+/* All calls on one device share its scratch: calls that overlap in time on one device    */
+/* (several streams) race and give wrong results; calls in order on one stream are safe.  */
+#define HCS_NOALLOC_SCRATCH_BYTES (32u << 20)
+hcs_status hcs_sparse_mla_decode_noalloc(const void* q, hcs_paged swa, hcs_paged comp,
+                                         const int32_t* topk_idx, int topk, const int32_t* q_seq,
+                                         const int32_t* q_pos, const float* sink, int N, int H, int d,
+                                         int window, int m, int max_pos, float scale, void* out,
+                                         float* lse, void* stream);
+
+/* ------------------------------------------------------------------------------------ */
 /* hcs_sparse_mla_decode for CSA with the selection inside the attention launch: query    */
 /* t's compressed rows are the top-k of its indexer scores scores[t, i], i < n_visible,   */
 /* chosen exactly as hcs_index_topk chooses them ("Code Reading Map", "Aux stream 0": the */

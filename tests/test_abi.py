@@ -155,3 +155,14 @@ def test_binding_fails_loudly_without_library(monkeypatch):
 def test_device_errors_rejects_null_before_any_hip_call():
     L = hcs.lib()
     assert L.hcs_device_errors(None, 1) == 1 and b"null bits" in L.hcs_last_error()
+
+
+@needs_lib
+def test_noalloc_rejects_plans_beyond_its_scratch_before_any_launch():
+    L = hcs.lib()
+    # 64 queries over 18528 rows each split nine ways: ~38 MB of partials, above the 32 MiB scratch
+    need = L.hcs_sparse_mla_workspace_size(64, 64, 512, 128, 4, 0, 4 * 18400)
+    assert need > (32 << 20)
+    st = L.hcs_sparse_mla_decode_noalloc(16, _paged(stride=400), _paged(stride=400), None, 0, 16, 16, None, 64,
+                                         64, 512, 128, 4, 4 * 18400, 0.1, 16, None, None)
+    assert st == 3 and b"static scratch" in L.hcs_last_error()
