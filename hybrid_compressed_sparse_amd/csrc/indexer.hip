@@ -534,12 +534,14 @@ __device__ __forceinline__ void score_block_mxfp4(const IndexArgs& a, int t, int
       ksc[p][nt] = page[SCALES + r * SB + g];
     }
   }
-  uint32_t tkeys[PPW * 4];
+  // after the sum over heads every lane of a 16-lane group holds the score of entry row r = 16 nt
+  // + l16; lane (g, l16) keeps group nt == g's, so the 64 lanes hold the 64 entries of each page
+  // once (entry e_base + 64 p + lane)
+  float sc[PPW];
 #pragma unroll
   for (int p = 0; p < PPW; ++p) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const int r = nt * 16 + l16;
       const i32x8 kbv = {kc[p][nt].x, kc[p][nt].y, kc[p][nt].z, kc[p][nt].w, 0, 0, 0, 0};
       float part = 0.f;
 #pragma unroll
@@ -550,19 +552,32 @@ __device__ __forceinline__ void score_block_mxfp4(const IndexArgs& a, int t, int
         for (int i = 0; i < 4; ++i) part += wreg[mt][i] * relu(acc[i]);
       }
       part = sum_xor16_32(part);
-      const int e = e_base + 64 * p + r;
-      const float sv = pgs[p] >= 0 ? part : kNegInf;
-      if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = sv;
-      tkeys[p * 4 + nt] = g == 0 && e < nv ? f32_order_key(sv) : 0u;
+      if (nt == 0 || g == nt) sc[p] = part;
+    }
+  }
+  uint32_t lmax = 0u;                                 // this lane's largest key (0: none)
+#pragma unroll
+  for (int p = 0; p < PPW; ++p) {
+    const int e = e_base + 64 * p + lane;
+    const float sv = pgs[p] >= 0 ? sc[p] : kNegInf;
+    if (e < nv) {
+      a.scores[(int64_t)t * a.score_stride + e] = sv;
+      lmax = max(lmax, f32_order_key(sv));
     }
   }
   if (a.blk_thr) {
-    // a threshold per wave (its 256 entries are a block of the bound): the kb-th largest key of
-    // a full wave block; no barrier
+    // a threshold per wave (its 256 entries are a block of the bound): the kb-th largest of the
+    // 64 lanes' largest keys. At least kb lanes, so at least kb distinct entries, have a key at
+    // or above it, which is all the bound needs; no barrier
     const int full = nv / (PPW * 64), wb = y * 4 + wave;
     const int kb = full > 0 ? bound_kb(a.topk, full) : kMaxKb + 1;
     if (wb < full && kb <= kMaxKb) {
-      const uint32_t kth = wave_kth_key<PPW * 4>(tkeys, kb);
+      uint32_t kth = 0u, v = lmax;
+      for (int it = 0; it < kb; ++it) {
+        kth = wave_max_u32(v);
+        const uint64_t who = __ballot(v == kth);
+        if (lane == (int)__builtin_ctzll(who)) v = 0u;   // who != 0: the maximum is some lane's
+      }
       if (lane == 0) a.blk_thr[(int64_t)t * a.thr_stride + wb] = kth;
     }
   }
@@ -933,6 +948,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(IndexArgs a, 
   }
   const uint32_t* ck = ckey + (int64_t)t * cstride;
   const int32_t* ci = cid + (int64_t)t * cstride;
+  // the first kSpec candidates are loaded together with their count, so that a query with no
+  // more (the usual case) costs one memory latency here instead of two
+  constexpr int kSpecPT = 8, kSpec = kSpecPT * kTopkThreads;
+  uint32_t sk[kSpecPT];
+  uint32_t sid[kSpecPT];
+  if (!cand_mode) {
+#pragma unroll
+    for (int u = 0; u < kSpecPT; ++u) {
+      const int64_t i = min((int64_t)(u * kTopkThreads + (int)threadIdx.x), cstride - 1);
+      sk[u] = ck[i];
+      sid[u] = (uint32_t)ci[i];
+    }
+  }
   const int n = (int)ccount[t];                      // > k: every key >= the k-th is a candidate
   auto emit = [&](unsigned slot, int id, uint32_t key) {
     if (slot < (unsigned)k) {
@@ -941,6 +969,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(IndexArgs a, 
     }
   };
   auto same = [](uint32_t v) { return v; };
+  static_assert(kSpec <= kSingleMax / 2, "the loaded candidates fit the LDS key and id halves");
+  if (!cand_mode && n <= kSpec) {
+    uint32_t* kid = kl + kSingleMax / 2;
+#pragma unroll
+    for (int u = 0; u < kSpecPT; ++u) {
+      const int i = u * kTopkThreads + (int)threadIdx.x;
+      if (i < n) {
+        kl[i] = sk[u];
+        kid[i] = sid[u];
+      }
+    }
+    sel_reset<kTopkThreads>(sh);
+    __syncthreads();
+    block_topk<kTopkThreads>(
+        sh, n, k, [&](int i, uint32_t& key) { key = kl[i]; return true; }, [&](int i) { return (int)kid[i]; },
+        emit);
+    return;
+  }
   if (n <= kSingleMax / 2) {
     // keys and ids in LDS
     uint32_t* kid = kl + kSingleMax / 2;
