@@ -569,7 +569,8 @@ def measure_prefill(wl, args, sets: int) -> dict:
         log(f"[bench] {wl.name} {k}: {ms[k] * 1e3:.1f} us" + (f", {tflops[k]:.0f} TFLOP/s" if k in tflops else ""))
     dom = max(["index_topk", "attention"], key=lambda k: ms[k])
     roof = {op: {"bound": "mfma", "achieved": tflops[op], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": tflops[op] / BF16_MFMA_PEAK_TFLOPS, "traffic": None, "flops_per_launch": fl[op],
+                 "frac": tflops[op] / BF16_MFMA_PEAK_TFLOPS, "traffic": measured_traffic(wl.name, op),
+                 "flops_per_launch": fl[op],
                  "us_per_launch": ms[op] * 1e3,
                  "kernel": ("hcs_sparse_mla_prefill_chunk (mla_heads_kernel<512, head pairs>)" if op == "attention"
                             else "hcs_index_topk_chunk (index_score_chunk_kernel + topk_single_kernel)")}
