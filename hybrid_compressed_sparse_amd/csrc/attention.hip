@@ -66,8 +66,11 @@ __device__ __forceinline__ float sum_xor16_32(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// two floats -> packed bf16 (round to nearest even), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // two e4m3 values (bytes 0-1, or 2-3 with HI) times the power of two sc, as bf16 (exact: the
@@ -751,12 +754,19 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       }
       lds_barrier();
     } else {
-      RowSrc r{};
+      // step 0 also issues block 3: the S waves have read q out of tiles 2-3 before its barrier
+      RowSrc r{}, r3{};
       if (i + 2 < nblk) r = prep(i + 2);
-      if (i + 1 < nblk) HCS_WAIT_VMCNT(NLD);
-      else wait_vm_zero();
+      if (i == 0 && nblk > 3) r3 = prep(3);
+      if (i + 1 < nblk) {
+        if (i == 1 && nblk > 3) HCS_WAIT_VMCNT(2 * NLD);   // blocks 2 and 3 may be in flight
+        else HCS_WAIT_VMCNT(NLD);
+      } else {
+        wait_vm_zero();
+      }
       lds_barrier();
-      if (i + 2 < nblk) fire(i + 2, r);
+      if (i + 2 < nblk && i != 1) fire(i + 2, r);
+      if (i == 0 && nblk > 3) fire(3, r3);
     }
   };
 
@@ -947,8 +957,8 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
         }
       }
     }
-    __syncthreads();                                // (E1) per-head (max, sum) published
-    __syncthreads();                                // (E2) O waves have staged the output
+    lds_barrier();                                  // (E1) per-head (max, sum) published
+    lds_barrier();                                  // (E2) O waves have staged the output
   } else {
     // ================= O waves: output columns D/4 * ow .. +D/4 of all 64 heads
     const int ow = wave - 4;
@@ -1014,7 +1024,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       const int hh = hbase + 16 * nt + l16;
       sink2[nt] = a.sink && hh < a.H && !split ? a.sink[hh] * kLog2e : kNegInf;
     }
-    __syncthreads();                                // (E1)
+    lds_barrier();                                  // (E1)
     // The result goes through LDS so that each global store writes whole rows: lane holds
     // O^T[c = 16 (ow * CTO + ct) + 4g + e][head 16 nt + l16]; in LDS (tiles 0-1, free now), row h
     // holds head h with its 16-byte chunks XOR-swizzled by h mod 16 (conflict-free for both the
@@ -1044,7 +1054,8 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
         *(uint2*)(hrow + ((((cb >> 4) ^ l16) << 4) | (cb & 15))) = pk;
       }
     }
-    __syncthreads();                                // (E2)
+    lds_barrier();                                  // (E2): LDS only, the partials' (max, sum)
+                                                    // stores need no wait inside this kernel
   }
   constexpr int LPH = RS / 16;                       // lanes per head row
   constexpr int HPI = 64 / LPH;                      // heads per wave instruction
