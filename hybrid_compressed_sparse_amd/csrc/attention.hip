@@ -166,24 +166,25 @@ __device__ __forceinline__ void fill_rows(const AttnArgs& a, int t, const QueryR
 }
 
 // fill_rows for a block that selects its query's compressed rows itself from the indexer scores
-// (a.scores): the top-k of the visible entries' scores, by the same exact radix select as the
-// indexer's selection kernels (ties at the k-th score go to the smaller ids), or every visible
-// entry when there are at most k. The selected ids are ordered by id, so that every split of the
-// query computes the same row order and takes its own range of it. `scratch` is LDS of
-// kSelScratch bytes that nothing else uses until the caller's next barrier; rowtab[0 .. n
-// rounded up to `pad`) is written; ends with a barrier. Split 0 writes the ids to a.sel_out.
-constexpr int kSelScratch = 4 * kSelMax + 17 * 1024 + kSelMax;   // keys, SelShared, id flags
-static_assert(sizeof(SelShared) <= 17 * 1024, "selection scratch layout");
+// (a.scores): the top-k of the visible entries' scores, exact, ties at the k-th score going to the
+// smaller ids (the rule of the indexer's selection kernels), or every visible entry when there
+// are at most k. Each thread holds the keys of a contiguous run of ids in registers; the k-th key
+// comes from reg_kth, then one block-wide prefix sum of each thread's counts of keys above it and
+// equal to it places the selected ids in id order, so that every split of the query computes the
+// same row order and takes its own range of it. `scratch` is LDS of kSelScratch bytes that
+// nothing else uses until the caller's next barrier; rowtab[0 .. n rounded up to `pad`) is
+// written; ends with a barrier. Split 0 writes the ids to a.sel_out.
+constexpr int kSelScratch = (int)sizeof(SelShared);
 
-template <int NT>
+// IPT: the scores a thread holds (ids tid * IPT ..), the least of 4, 8, 16 with NT * IPT >= nv
+template <int NT, int IPT>
 __device__ __forceinline__ void fill_rows_sel(const AttnArgs& a, int t, int s, const QueryRows& q, int r0,
                                               int n, uint32_t* rowtab, int* ptl, int pad, uint8_t* scratch) {
+  static_assert(NT * 16 >= kSelMax && IPT <= 16, "selection size");
   constexpr int RPT = (kMaxRowsWG + NT - 1) / NT;
   constexpr int PPT = kPtCache / NT;
-  constexpr int IPT = kSelMax / NT;              // scores per thread in the loads
-  uint32_t* kl = reinterpret_cast<uint32_t*>(scratch);
-  SelShared& sh = *reinterpret_cast<SelShared*>(scratch + 4 * kSelMax);
-  uint8_t* flag = scratch + 4 * kSelMax + 17 * 1024;
+  constexpr int NW = NT / 64;
+  SelShared& sh = *reinterpret_cast<SelShared*>(scratch);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nv = q.nv, k = a.topk;
   const int npg = (nv + 63) >> 6;
@@ -191,7 +192,8 @@ __device__ __forceinline__ void fill_rows_sel(const AttnArgs& a, int t, int s, c
   const int32_t* cpt = a.comp.pt + (int64_t)q.seq * a.comp.pt_stride;
   const int32_t* spt = a.swa.pt + (int64_t)q.seq * a.swa.pt_stride;
   const float* sc = a.scores + (int64_t)t * a.score_stride;
-  // ---- every load at once: compressed page table, window rows' pages, the scores
+  // ---- every load at once: compressed page table, window rows' pages, the scores of this
+  // thread's ids i0 .. i0 + c - 1
   int pv[PPT];
 #pragma unroll
   for (int j = 0; j < PPT; ++j) {
@@ -204,23 +206,20 @@ __device__ __forceinline__ void fill_rows_sel(const AttnArgs& a, int t, int s, c
     const int gr = r0 + tid + i * NT;
     spg[i] = gr < q.n_swa ? __ldg(spt + ((q.lo + gr) >> 6)) : 0;
   }
+  const int i0 = tid * IPT;
   float sv[IPT];
 #pragma unroll
-  for (int j = 0; j < IPT; ++j) {
-    const int i = tid + j * NT;
-    sv[j] = i < nv ? __ldg(sc + i) : 0.f;
-  }
+  for (int j = 0; j < IPT; ++j) sv[j] = i0 + j < nv ? __ldg(sc + i0 + j) : 0.f;
 #pragma unroll
   for (int j = 0; j < PPT; ++j) {
     const int idx = tid + j * NT;
     if (idx < npg && cached) ptl[idx] = pv[j];
   }
-  const bool all = nv <= k;
+  uint32_t key[IPT], vmask = 0u;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
-    const int i = tid + j * NT;
-    kl[i] = f32_order_key(sv[j]);
-    flag[i] = all && i < nv ? 1 : 0;
+    key[j] = f32_order_key(sv[j]);
+    vmask |= (i0 + j < nv ? 1u : 0u) << j;
   }
   const int np = min((n + pad - 1) / pad * pad, kMaxRowsWG);
 #pragma unroll
@@ -230,47 +229,56 @@ __device__ __forceinline__ void fill_rows_sel(const AttnArgs& a, int t, int s, c
   }
   sel_reset<NT>(sh);
   __syncthreads();
-  if (!all)
-    block_topk<NT, false>(
-        sh, nv, k, [&](int i, uint32_t& key) { key = kl[i]; return true; }, [&](int i) { return i; },
-        [&](unsigned, int id, uint32_t) { flag[id] = 1; });      // ends with a barrier (the ids are
-                                                                  // marked, so their order is free)
-  // ---- position of each selected id in id order: exclusive prefix of the flag counts
-  constexpr int FPT = kSelMax / NT;              // ids per thread in the scan
-  static_assert(FPT % 4 == 0, "the scan reads 4 id flags per word");
-  const int i0 = tid * FPT;
-  uint32_t fw[FPT / 4];
-  unsigned cnt = 0;
-#pragma unroll
-  for (int j = 0; j < FPT / 4; ++j) {
-    fw[j] = *reinterpret_cast<const uint32_t*>(flag + i0 + 4 * j);
-    cnt += (unsigned)__popc(fw[j]);                 // flags are 0 / 1 bytes
+  KthResult r;
+  if (nv > k) {
+    r = reg_kth<NT, IPT>(sh, key, vmask, (unsigned)k);
+  } else {
+    r.prefix = 0u;                                // every visible entry
+    r.mask = 0u;
+    r.need = r.n_eq = (unsigned)nv;
   }
-  const uint64_t below = (1ull << lane) - 1;
-  unsigned run = 0;
+  // ---- selected ids in id order: a key above the k-th bin is taken, one in it is taken while
+  // fewer than r.need such keys come before it (all of them unless the bin holds equal keys)
+  unsigned na = 0, ne = 0;
 #pragma unroll
-  for (int b = 0; b < 6; ++b) run += (unsigned)__popcll(__ballot((cnt >> b) & 1u) & below) << b;
-  if (lane == 63) sh.wsum[wave] = run + cnt;
-  __syncthreads();
-  unsigned total = 0;
+  for (int j = 0; j < IPT; ++j) {
+    if ((vmask >> j) & 1u) {
+      const uint32_t km = key[j] & r.mask;
+      na += km > r.prefix ? 1u : 0u;
+      ne += km == r.prefix ? 1u : 0u;
+    }
+  }
+  const unsigned packed = (na << 16) | ne;        // both sums stay below 2^16 (nv <= kSelMax)
+  const unsigned incl = wave_incl_scan_u32(packed);
+  if (lane == 63) sh.wsum[wave] = incl;
+  lds_barrier();
+  unsigned before = incl - packed, all = 0;
 #pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const unsigned ws = sh.wsum[w];
-    run += w < wave ? ws : 0u;
-    total += ws;
+    before += w < wave ? ws : 0u;
+    all += ws;
   }
+  unsigned eq_seen = before & 0xFFFFu;
+  unsigned pos = (before >> 16) + min(eq_seen, r.need);
+  const unsigned n_sel = (all >> 16) + min(all & 0xFFFFu, r.need);
   int32_t* out = a.sel_out && s == 0 ? a.sel_out + (int64_t)t * k : nullptr;
 #pragma unroll
-  for (int j = 0; j < FPT; ++j) {
-    if ((fw[j >> 2] >> (8 * (j & 3))) & 1u) {
-      const int li = q.n_swa + (int)run - r0;
-      if (li >= 0 && li < n) rowtab[li] = (uint32_t)(i0 + j);
-      if (out) out[run] = i0 + j;
-      ++run;
+  for (int j = 0; j < IPT; ++j) {
+    if ((vmask >> j) & 1u) {
+      const uint32_t km = key[j] & r.mask;
+      bool take = km > r.prefix;
+      if (km == r.prefix) take = eq_seen++ < r.need;
+      if (take) {
+        const int li = q.n_swa + (int)pos - r0;
+        if (li >= 0 && li < n) rowtab[li] = (uint32_t)(i0 + j);
+        if (out && pos < (unsigned)k) out[pos] = i0 + j;
+        ++pos;
+      }
     }
   }
   if (out)
-    for (int j = (int)total + tid; j < k; j += NT) out[j] = -1;
+    for (int j = (int)n_sel + tid; j < k; j += NT) out[j] = -1;
   __syncthreads();
   // ---- ids -> row entries (each thread converts the entries it owns)
 #pragma unroll
@@ -664,7 +672,11 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
     }
   }
   if (tid < 4) pseq[tid] = 0;                     // ordered by the row table's barriers
-  if constexpr (SEL) fill_rows_sel<kHeadsThreads>(a, t, s, q, r0, n_rows, rowtab, ptl, BT, tiles);
+  if constexpr (SEL) {
+    if (q.nv <= 4 * kHeadsThreads) fill_rows_sel<kHeadsThreads, 4>(a, t, s, q, r0, n_rows, rowtab, ptl, BT, tiles);
+    else if (q.nv <= 8 * kHeadsThreads) fill_rows_sel<kHeadsThreads, 8>(a, t, s, q, r0, n_rows, rowtab, ptl, BT, tiles);
+    else fill_rows_sel<kHeadsThreads, 16>(a, t, s, q, r0, n_rows, rowtab, ptl, BT, tiles);
+  }
   else fill_rows<kHeadsThreads, PTC>(a, t, q, r0, n_rows, rowtab, ptl, BT);
   const int nblk = (n_rows + BT - 1) / BT;
 

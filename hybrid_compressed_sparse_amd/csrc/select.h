@@ -17,6 +17,7 @@ constexpr int kCandMax = 64;            // a k-th key bin this small is resolved
 struct SelShared {
   unsigned hist[2][kBins];               // pass p counts into hist[p & 1]; the other is cleared
   unsigned wsum[16];                     // per-wave bin totals of a pass
+  unsigned wmax[16], wmin[16], wcnt[16]; // per-wave key range and count (register-key select)
   unsigned bin, above, cnt_bin;
   unsigned kmax, kmin, count;            // range and number of the participating keys
   unsigned out_count;
@@ -46,6 +47,22 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, by DPP: within each row of 16 lanes the sums
+// of the 1, 2, 3 lanes before (row_shr), then of 4 and 8 lanes before (on the banks those reach),
+// then the last lane of row 0 into row 1 and of row 2 into row 3 (row_bcast:15), then the last
+// lane of row 1 into rows 2-3 (row_bcast:31). Disabled and out-of-row lanes contribute 0.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  uint32_t x = v;
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x113, 0xF, 0xF, true);   // row_shr:3
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xE, false);  // row_shr:4, lanes 4-15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xC, false);  // row_shr:8, lanes 8-15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1, 3
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2, 3
+  return x;
 }
 
 // Clears what radix_kth expects cleared; the caller puts a barrier between this and the call.
@@ -170,6 +187,110 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of, u
     sh.kmax = 0u;
     sh.kmin = ~0u;
     sh.count = 0u;
+  }
+  r.prefix = prefix;
+  r.mask = mask;
+  r.need = remaining;
+  r.n_eq = cnt_bin;
+  return r;
+}
+
+// Radix select of the k-th largest key when every thread holds its keys in registers (up to IPT,
+// slot j present when bit j of vmask is set) in a block of exactly 512 threads: the key range and
+// count come from wave reductions, then 11-bit digits below the keys' common leading part, each
+// pass one histogram (LDS atomics issued back to back), a wave prefix sum over 4 bins per thread
+// and the bin search, with three LDS-only barriers. The passes stop once the bin of the k-th key
+// holds exactly the keys still needed, or every bit is resolved (then that bin holds equal keys).
+// All present keys are taken when there are at most k of them (mask 0: every key is in the
+// "bin"). Expects hist[0] cleared and a barrier after; leaves both histograms cleared (ordered
+// by the caller's next barrier).
+template <int NT, int IPT>
+__device__ KthResult reg_kth(SelShared& sh, const uint32_t (&key)[IPT], uint32_t vmask, unsigned k) {
+  static_assert(NT == 512 && kBins == 4 * NT, "four bins per thread");
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t lmax = 0u, lmin = ~0u;
+  unsigned lcnt = 0;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    if ((vmask >> j) & 1u) {
+      lmax = max(lmax, key[j]);
+      lmin = min(lmin, key[j]);
+      ++lcnt;
+    }
+  }
+  lmax = wave_max_u32(lmax);
+  lmin = wave_min_u32(lmin);
+  lcnt = wave_sum_u32(lcnt);
+  if (lane == 0) {
+    sh.wmax[wave] = lmax;
+    sh.wmin[wave] = lmin;
+    sh.wcnt[wave] = lcnt;
+  }
+  lds_barrier();
+  uint32_t kmax = 0u, kmin = ~0u;
+  unsigned total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    kmax = max(kmax, sh.wmax[w]);
+    kmin = min(kmin, sh.wmin[w]);
+    total += sh.wcnt[w];
+  }
+  KthResult r;
+  if (total <= k) {
+    r.prefix = 0u;
+    r.mask = 0u;
+    r.need = r.n_eq = total;
+    return r;
+  }
+  const uint32_t diff = kmax ^ kmin;
+  if (diff == 0u) {                      // all present keys are equal
+    r.prefix = kmax;
+    r.mask = ~0u;
+    r.need = k;
+    r.n_eq = total;
+    return r;
+  }
+  int top = 31 - __builtin_clz(diff);
+  uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
+  uint32_t prefix = kmax & mask;
+  unsigned remaining = k, cnt_bin = total;
+  for (int pass = 0; top >= 0; ++pass) {
+    const int width = min(kDigitBits, top + 1);
+    const int shift = top - width + 1;
+    unsigned* hist = sh.hist[pass & 1];
+#pragma unroll
+    for (int j = 0; j < IPT; ++j)
+      if (((vmask >> j) & 1u) && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & (kBins - 1)], 1u);
+    lds_barrier();
+    // thread t owns bins kBins-1-4t down to kBins-4-4t, one 16-byte read
+    const uint4 c4 = *reinterpret_cast<const uint4*>(hist + kBins - 4 - 4 * tid);
+    const unsigned cc[4] = {c4.w, c4.z, c4.y, c4.x};
+    const unsigned tot = cc[0] + cc[1] + cc[2] + cc[3];
+    const unsigned incl = wave_incl_scan_u32(tot);
+    if (lane == 63) sh.wsum[wave] = incl;
+    for (int j = tid; j < kBins; j += NT) sh.hist[(pass & 1) ^ 1][j] = 0;   // the next pass's
+    lds_barrier();
+    unsigned run = incl - tot;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) run += w < wave ? sh.wsum[w] : 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (run < remaining && run + cc[j] >= remaining) {
+        sh.bin = kBins - 1 - 4 * tid - j;
+        sh.above = run;
+        sh.cnt_bin = cc[j];
+      }
+      run += cc[j];
+    }
+    lds_barrier();
+    prefix |= sh.bin << shift;
+    mask |= ((1u << width) - 1u) << shift;
+    remaining -= sh.above;
+    cnt_bin = sh.cnt_bin;
+    top = shift - 1;
+    for (int j = tid; j < kBins; j += NT) hist[j] = 0;
+    if (cnt_bin == remaining) break;
   }
   r.prefix = prefix;
   r.mask = mask;
