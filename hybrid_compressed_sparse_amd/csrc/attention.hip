@@ -168,10 +168,9 @@ __device__ __forceinline__ void fill_rows(const AttnArgs& a, int t, const QueryR
 // fill_rows for a block that selects its query's compressed rows itself from the indexer scores
 // (a.scores): the top-k of the visible entries' scores, exact, ties at the k-th score going to the
 // smaller ids (the rule of the indexer's selection kernels), or every visible entry when there
-// are at most k. Each thread holds the keys of a contiguous run of ids in registers; the k-th key
-// comes from reg_kth, then one block-wide prefix sum of each thread's counts of keys above it and
-// equal to it places the selected ids in id order, so that every split of the query computes the
-// same row order and takes its own range of it. `scratch` is LDS of kSelScratch bytes that
+// are at most k. Each thread holds the keys of a contiguous run of ids in registers, and reg_topk
+// places the selected ids in id order, so that every split of the query computes the same row
+// order and takes its own range of it. `scratch` is LDS of kSelScratch bytes that
 // nothing else uses until the caller's next barrier; rowtab[0 .. n rounded up to `pad`) is
 // written; ends with a barrier. Split 0 writes the ids to a.sel_out.
 constexpr int kSelScratch = (int)sizeof(SelShared);
@@ -183,9 +182,8 @@ __device__ __forceinline__ void fill_rows_sel(const AttnArgs& a, int t, int s, c
   static_assert(NT * 16 >= kSelMax && IPT <= 16, "selection size");
   constexpr int RPT = (kMaxRowsWG + NT - 1) / NT;
   constexpr int PPT = kPtCache / NT;
-  constexpr int NW = NT / 64;
   SelShared& sh = *reinterpret_cast<SelShared*>(scratch);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int nv = q.nv, k = a.topk;
   const int npg = (nv + 63) >> 6;
   const bool cached = npg <= kPtCache;
@@ -229,57 +227,18 @@ __device__ __forceinline__ void fill_rows_sel(const AttnArgs& a, int t, int s, c
   }
   sel_reset<NT>(sh);
   __syncthreads();
-  KthResult r;
-  if (nv > k) {
-    r = reg_kth<NT, IPT>(sh, key, vmask, (unsigned)k);
-  } else {
-    r.prefix = 0u;                                // every visible entry
-    r.mask = 0u;
-    r.need = r.n_eq = (unsigned)nv;
-  }
-  // ---- selected ids in id order: a key above the k-th bin is taken, one in it is taken while
-  // fewer than r.need such keys come before it (all of them unless the bin holds equal keys)
-  unsigned na = 0, ne = 0;
-#pragma unroll
-  for (int j = 0; j < IPT; ++j) {
-    if ((vmask >> j) & 1u) {
-      const uint32_t km = key[j] & r.mask;
-      na += km > r.prefix ? 1u : 0u;
-      ne += km == r.prefix ? 1u : 0u;
-    }
-  }
-  const unsigned packed = (na << 16) | ne;        // both sums stay below 2^16 (nv <= kSelMax)
-  const unsigned incl = wave_incl_scan_u32(packed);
-  if (lane == 63) sh.wsum[wave] = incl;
-  lds_barrier();
-  unsigned before = incl - packed, all = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const unsigned ws = sh.wsum[w];
-    before += w < wave ? ws : 0u;
-    all += ws;
-  }
-  unsigned eq_seen = before & 0xFFFFu;
-  unsigned pos = (before >> 16) + min(eq_seen, r.need);
-  const unsigned n_sel = (all >> 16) + min(all & 0xFFFFu, r.need);
+  // ---- the top-k (every visible entry when nv <= k), in id order: rowtab entries of this
+  // split's range, and split 0 writes the ids to a.sel_out
   int32_t* out = a.sel_out && s == 0 ? a.sel_out + (int64_t)t * k : nullptr;
-#pragma unroll
-  for (int j = 0; j < IPT; ++j) {
-    if ((vmask >> j) & 1u) {
-      const uint32_t km = key[j] & r.mask;
-      bool take = km > r.prefix;
-      if (km == r.prefix) take = eq_seen++ < r.need;
-      if (take) {
+  const unsigned n_sel = reg_topk<NT, IPT>(
+      sh, key, vmask, (unsigned)k, true, [&](int j) { return i0 + j; },
+      [&](unsigned pos, int j, uint32_t) {
         const int li = q.n_swa + (int)pos - r0;
         if (li >= 0 && li < n) rowtab[li] = (uint32_t)(i0 + j);
         if (out && pos < (unsigned)k) out[pos] = i0 + j;
-        ++pos;
-      }
-    }
-  }
+      });
   if (out)
     for (int j = (int)n_sel + tid; j < k; j += NT) out[j] = -1;
-  __syncthreads();
   // ---- ids -> row entries (each thread converts the entries it owns)
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {

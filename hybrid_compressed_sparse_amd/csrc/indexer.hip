@@ -735,13 +735,41 @@ __device__ __forceinline__ void lds_fill(uint32_t* dst, const T* src, int n, F f
   }
 }
 
-// One query per workgroup: short-context fill or one-stage select over its scores.
+// One query's select over its scores with IPT keys per thread (ids tid * IPT ..), in registers.
+template <int NT, int IPT>
+__device__ __forceinline__ void topk_single_regs(SelShared& sh, const float* sc, int nv, int k, int32_t* oi,
+                                                 float* os) {
+  const int i0 = threadIdx.x * IPT;
+  float v[IPT];
+  // loads at clamped indices (a conditional load would be a branch and a wait of its own)
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) v[j] = sc[min(i0 + j, nv - 1)];
+  uint32_t key[IPT], vmask = 0u;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    key[j] = f32_order_key(v[j]);
+    vmask |= (i0 + j < nv ? 1u : 0u) << j;
+  }
+  sel_reset<NT>(sh);
+  __syncthreads();
+  reg_topk<NT, IPT>(sh, key, vmask, (unsigned)k, true, [&](int j) { return i0 + j; },
+                    [&](unsigned pos, int j, uint32_t kk) {
+                      if (pos < (unsigned)k) {
+                        oi[pos] = i0 + j;
+                        if (os) os[pos] = order_key_f32(kk);
+                      }
+                    });
+}
+
+// One query per workgroup: short-context fill or one-stage select over its scores. Up to 8 NT
+// visible entries: keys in registers, ids in ascending order; more (prefill chunks): keys in LDS,
+// the ids above the k-th key in ascending order, then those equal to it by rank.
 // NT threads, at most KL visible entries.
 template <int NT, int KL>
 __global__ __launch_bounds__(NT) void topk_single_kernel(IndexArgs a, int k, int32_t* out_idx,
                                                          float* out_score) {
   __shared__ SelShared sh;
-  __shared__ uint32_t kl[KL];            // the query's order keys, read once from memory
+  __shared__ uint32_t kl[KL];            // the query's order keys, read once from memory (> 8 NT)
   const int t = blockIdx.x;
   int seq, nv;
   query_of(a, t, seq, nv);
@@ -753,6 +781,14 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(IndexArgs a, int k, int
       oi[j] = j < nv ? j : -1;
       if (os) os[j] = j < nv ? sc[j] : 0.f;
     }
+    return;
+  }
+  if (nv <= 4 * NT) {
+    topk_single_regs<NT, 4>(sh, sc, nv, k, oi, os);
+    return;
+  }
+  if (nv <= 8 * NT) {
+    topk_single_regs<NT, 8>(sh, sc, nv, k, oi, os);
     return;
   }
   lds_fill<NT>(kl, sc, nv, [](float v) { return f32_order_key(v); });
@@ -969,24 +1005,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(IndexArgs a, 
     }
   };
   auto same = [](uint32_t v) { return v; };
-  static_assert(kSpec <= kSingleMax / 2, "the loaded candidates fit the LDS key and id halves");
   if (!cand_mode && n <= kSpec) {
-    uint32_t* kid = kl + kSingleMax / 2;
+    // the loaded candidates are the keys (slot u of a thread: candidate u * kTopkThreads + tid)
+    uint32_t vmask = 0u;
 #pragma unroll
-    for (int u = 0; u < kSpecPT; ++u) {
-      const int i = u * kTopkThreads + (int)threadIdx.x;
-      if (i < n) {
-        kl[i] = sk[u];
-        kid[i] = sid[u];
-      }
-    }
+    for (int u = 0; u < kSpecPT; ++u) vmask |= (u * kTopkThreads + (int)threadIdx.x < n ? 1u : 0u) << u;
     sel_reset<kTopkThreads>(sh);
     __syncthreads();
-    block_topk<kTopkThreads>(
-        sh, n, k, [&](int i, uint32_t& key) { key = kl[i]; return true; }, [&](int i) { return (int)kid[i]; },
-        emit);
+    reg_topk<kTopkThreads, kSpecPT>(sh, sk, vmask, (unsigned)k, false, [&](int u) { return (int)sid[u]; },
+                                    [&](unsigned pos, int u, uint32_t key) { emit(pos, (int)sid[u], key); });
     return;
   }
+  static_assert(kSpec <= kSingleMax / 2, "the loaded candidates fit the LDS key and id halves");
   if (n <= kSingleMax / 2) {
     // keys and ids in LDS
     uint32_t* kid = kl + kSingleMax / 2;

@@ -196,18 +196,18 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of, u
 }
 
 // Radix select of the k-th largest key when every thread holds its keys in registers (up to IPT,
-// slot j present when bit j of vmask is set) in a block of exactly 512 threads: the key range and
+// slot j present when bit j of vmask is set) in a block of 512 or 1024 threads: the key range and
 // count come from wave reductions, then 11-bit digits below the keys' common leading part, each
-// pass one histogram (LDS atomics issued back to back), a wave prefix sum over 4 bins per thread
-// and the bin search, with three LDS-only barriers. The passes stop once the bin of the k-th key
+// pass one histogram (LDS atomics issued back to back), a wave prefix sum over the 4 or 2 bins of
+// each thread and the bin search, with three LDS-only barriers. The passes stop once the bin of the k-th key
 // holds exactly the keys still needed, or every bit is resolved (then that bin holds equal keys).
 // All present keys are taken when there are at most k of them (mask 0: every key is in the
 // "bin"). Expects hist[0] cleared and a barrier after; leaves both histograms cleared (ordered
 // by the caller's next barrier).
 template <int NT, int IPT>
 __device__ KthResult reg_kth(SelShared& sh, const uint32_t (&key)[IPT], uint32_t vmask, unsigned k) {
-  static_assert(NT == 512 && kBins == 4 * NT, "four bins per thread");
-  constexpr int NW = NT / 64;
+  static_assert((NT == 512 || NT == 1024) && IPT <= 32, "512 or 1024 threads");
+  constexpr int NW = NT / 64, BPT = kBins / NT;   // bins per thread in the scan: 4 or 2
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t lmax = 0u, lmin = ~0u;
   unsigned lcnt = 0;
@@ -263,10 +263,21 @@ __device__ KthResult reg_kth(SelShared& sh, const uint32_t (&key)[IPT], uint32_t
     for (int j = 0; j < IPT; ++j)
       if (((vmask >> j) & 1u) && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & (kBins - 1)], 1u);
     lds_barrier();
-    // thread t owns bins kBins-1-4t down to kBins-4-4t, one 16-byte read
-    const uint4 c4 = *reinterpret_cast<const uint4*>(hist + kBins - 4 - 4 * tid);
-    const unsigned cc[4] = {c4.w, c4.z, c4.y, c4.x};
-    const unsigned tot = cc[0] + cc[1] + cc[2] + cc[3];
+    // thread t owns bins kBins-1-BPT t down to kBins-BPT-BPT t, one 16- or 8-byte read
+    unsigned cc[BPT], tot = 0;
+    if constexpr (BPT == 4) {
+      const uint4 c4 = *reinterpret_cast<const uint4*>(hist + kBins - 4 - 4 * tid);
+      cc[0] = c4.w;
+      cc[1] = c4.z;
+      cc[2] = c4.y;
+      cc[3] = c4.x;
+    } else {
+      const uint2 c2 = *reinterpret_cast<const uint2*>(hist + kBins - 2 - 2 * tid);
+      cc[0] = c2.y;
+      cc[1] = c2.x;
+    }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) tot += cc[j];
     const unsigned incl = wave_incl_scan_u32(tot);
     if (lane == 63) sh.wsum[wave] = incl;
     for (int j = tid; j < kBins; j += NT) sh.hist[(pass & 1) ^ 1][j] = 0;   // the next pass's
@@ -275,9 +286,9 @@ __device__ KthResult reg_kth(SelShared& sh, const uint32_t (&key)[IPT], uint32_t
 #pragma unroll
     for (int w = 0; w < NW; ++w) run += w < wave ? sh.wsum[w] : 0u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < BPT; ++j) {
       if (run < remaining && run + cc[j] >= remaining) {
-        sh.bin = kBins - 1 - 4 * tid - j;
+        sh.bin = kBins - 1 - BPT * tid - j;
         sh.above = run;
         sh.cnt_bin = cc[j];
       }
@@ -297,6 +308,73 @@ __device__ KthResult reg_kth(SelShared& sh, const uint32_t (&key)[IPT], uint32_t
   r.need = remaining;
   r.n_eq = cnt_bin;
   return r;
+}
+
+// Top-k over keys held in registers (as reg_kth; element order is thread, then slot), ties at the
+// k-th key going to the smaller ids: with ids_ascending (ids rise with element order) the first
+// ones in element order, otherwise a second select on ~id among the keys equal to the k-th.
+// emit(pos, slot, key) for every selected element, pos = 0, 1, ... in element order; returns
+// their number (min(k, present keys)). Expects hist[0] cleared (sel_reset) and a barrier after;
+// leaves both histograms cleared. Ends with an LDS-only barrier after the emits.
+template <int NT, int IPT, class IdOf, class Emit>
+__device__ unsigned reg_topk(SelShared& sh, const uint32_t (&key)[IPT], uint32_t vmask, unsigned k,
+                             bool ids_ascending, IdOf id_of, Emit emit) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const KthResult r = reg_kth<NT, IPT>(sh, key, vmask, k);
+  // the keys equal to the k-th that are taken: all of them unless r.need < r.n_eq
+  uint32_t tmask = 0u;                              // slots of keys in the k-th key's bin
+#pragma unroll
+  for (int j = 0; j < IPT; ++j)
+    tmask |= (((vmask >> j) & 1u) && (key[j] & r.mask) == r.prefix ? 1u : 0u) << j;
+  const bool by_id = r.need < r.n_eq && !ids_ascending;
+  uint32_t take_tie = tmask;                        // by_id: those of the r.need smallest ids
+  if (by_id) {
+    uint32_t nid[IPT];
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) nid[j] = ~(uint32_t)id_of(j);
+    lds_barrier();                                  // the histograms' clears are done
+    const KthResult r2 = reg_kth<NT, IPT>(sh, nid, tmask, r.need);
+    take_tie = 0u;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j)
+      take_tie |= (((tmask >> j) & 1u) && (nid[j] & r2.mask) >= r2.prefix ? 1u : 0u) << j;
+  }
+  // counts of this thread: keys above the bin, keys in it (ties)
+  unsigned na = 0, ne = 0;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    if ((vmask >> j) & 1u) {
+      na += (key[j] & r.mask) > r.prefix ? 1u : 0u;
+      ne += (take_tie >> j) & 1u;
+    }
+  }
+  const unsigned packed = (na << 16) | ne;          // both sums stay below 2^16 (<= 32768 keys)
+  const unsigned incl = wave_incl_scan_u32(packed);
+  if (lane == 63) sh.wsum[wave] = incl;
+  lds_barrier();
+  unsigned before = incl - packed, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const unsigned ws = sh.wsum[w];
+    before += w < wave ? ws : 0u;
+    all += ws;
+  }
+  // in element order the ties taken are the first r.need of the bin (ids_ascending) or the
+  // marked ones (by id); both counts below are exact for this thread's position
+  unsigned eq_seen = before & 0xFFFFu;
+  const unsigned need = by_id ? ~0u : r.need;
+  unsigned pos = (before >> 16) + min(eq_seen, need);
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    if ((vmask >> j) & 1u) {
+      bool take = (key[j] & r.mask) > r.prefix;
+      if ((take_tie >> j) & 1u) take = eq_seen++ < need;
+      if (take) emit(pos++, j, key[j]);
+    }
+  }
+  lds_barrier();
+  return (all >> 16) + min(all & 0xFFFFu, need);
 }
 
 // Select the top-k of n elements (n > k) given key_of(i, key) and id_of(i); writes k ids (and
