@@ -724,8 +724,17 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
         if (i + 1 < nblk) qload(i + 1);
       }
       lds_barrier();
+    } else if constexpr (PAIR) {
+      RowSrc r{};
+      if (i + 2 < nblk) r = prep(i + 2);
+      if (i + 1 < nblk) HCS_WAIT_VMCNT(NLD);
+      else wait_vm_zero();
+      lds_barrier();
+      if (i + 2 < nblk) fire(i + 2, r);
     } else {
-      // step 0 also issues block 3: the S waves have read q out of tiles 2-3 before its barrier
+      // decode (a few blocks per workgroup): step 0 also issues block 3, the S waves having read
+      // q out of tiles 2-3 before its barrier (in the long prefill loop these branches cost more
+      // than the earlier copy gains)
       RowSrc r{}, r3{};
       if (i + 2 < nblk) r = prep(i + 2);
       if (i == 0 && nblk > 3) r3 = prep(3);

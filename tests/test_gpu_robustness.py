@@ -67,8 +67,8 @@ def test_repeat_runs_bitwise_prefill_chunk():
 
 
 def test_repeat_runs_two_call_ids_in_ascending_order():
-    """The one-stage select writes the ids above the k-th key in ascending order, then the
-    k-th key's bin by rank: the same order on every run."""
+    """The decode select (at most 8192 visible entries, keys in registers) writes the selected
+    ids in ascending order, padded with -1: the same order on every run."""
     wl = C.CSA_DECODE.with_(B=4, topk=200)
     sc = G.build(wl, seed=23, device=_dev(), ctx_per_seq=[8192, 6000, 3001, 999])
     U.say(f"[case] ordered ids {wl.name} seed=23")
@@ -77,6 +77,10 @@ def test_repeat_runs_two_call_ids_in_ascending_order():
         step, _ = U.run_step(sc)
         runs.append(step.idx.clone())
     assert torch.equal(runs[0], runs[1])
+    for t in range(4):
+        ids = runs[0][t].cpu().numpy()
+        v = ids[ids >= 0]
+        assert np.all(ids[v.size:] == -1) and np.all(np.diff(v) > 0), t
 
 
 def test_page_range_error_word():
