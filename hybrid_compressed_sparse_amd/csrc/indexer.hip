@@ -761,15 +761,41 @@ __device__ __forceinline__ void topk_single_regs(SelShared& sh, const float* sc,
                     });
 }
 
-// One query per workgroup: short-context fill or one-stage select over its scores. Up to 8 NT
-// visible entries: keys in registers, ids in ascending order; more (prefill chunks): keys in LDS,
-// the ids above the k-th key in ascending order, then those equal to it by rank.
-// NT threads, at most KL visible entries.
+// The same with the ids strided over the threads (slot j of thread tid: id j NT + tid), so that
+// every load instruction reads consecutive scores and every thread holds keys; the output order
+// is thread, then slot (fixed, not ascending), ties to the smaller ids by a second select.
+template <int NT, int IPT>
+__device__ __forceinline__ void topk_single_strided(SelShared& sh, const float* sc, int nv, int k, int32_t* oi,
+                                                    float* os) {
+  const int tid = threadIdx.x;
+  float v[IPT];
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) v[j] = sc[min(j * NT + tid, nv - 1)];
+  uint32_t key[IPT], vmask = 0u;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    key[j] = f32_order_key(v[j]);
+    vmask |= (j * NT + tid < nv ? 1u : 0u) << j;
+  }
+  sel_reset<NT>(sh);
+  __syncthreads();
+  reg_topk<NT, IPT>(sh, key, vmask, (unsigned)k, false, [&](int j) { return j * NT + tid; },
+                    [&](unsigned pos, int j, uint32_t kk) {
+                      if (pos < (unsigned)k) {
+                        oi[pos] = j * NT + tid;
+                        if (os) os[pos] = order_key_f32(kk);
+                      }
+                    });
+}
+
+// One query per workgroup: short-context fill or one-stage select over its scores, the keys in
+// registers. Up to 8 NT visible entries (decode) the ids come out in ascending order; more
+// (prefill chunks) in a fixed order of their own. NT threads, at most KL visible entries.
 template <int NT, int KL>
 __global__ __launch_bounds__(NT) void topk_single_kernel(IndexArgs a, int k, int32_t* out_idx,
                                                          float* out_score) {
+  static_assert(KL <= 32 * NT, "at most 32 keys per thread");
   __shared__ SelShared sh;
-  __shared__ uint32_t kl[KL];            // the query's order keys, read once from memory (> 8 NT)
   const int t = blockIdx.x;
   int seq, nv;
   query_of(a, t, seq, nv);
@@ -791,18 +817,29 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(IndexArgs a, int k, int
     topk_single_regs<NT, 8>(sh, sc, nv, k, oi, os);
     return;
   }
-  lds_fill<NT>(kl, sc, nv, [](float v) { return f32_order_key(v); });
-  sel_reset<NT>(sh);
-  __syncthreads();
-  block_topk<NT>(
-      sh, nv, k, [&](int i, uint32_t& key) { key = kl[i]; return true; },
-      [&](int i) { return i; },
-      [&](unsigned slot, int id, uint32_t key) {
-        if (slot < (unsigned)k) {
-          oi[slot] = id;
-          if (os) os[slot] = order_key_f32(key);
-        }
-      });
+  if (nv <= 16 * NT) {
+    topk_single_strided<NT, 16>(sh, sc, nv, k, oi, os);
+    return;
+  }
+  // 32 keys per thread spill registers: instantiated only where KL needs it
+  if constexpr (KL <= 24 * NT) {
+    topk_single_strided<NT, 24>(sh, sc, nv, k, oi, os);
+  } else {
+    if (nv <= 24 * NT) topk_single_strided<NT, 24>(sh, sc, nv, k, oi, os);
+    else topk_single_strided<NT, 32>(sh, sc, nv, k, oi, os);
+  }
+}
+
+// The one-stage select launch for at most nv_cap visible entries per query.
+hipError_t launch_topk_single(const IndexArgs& a, int nv_cap, int k, int32_t* out_idx, float* out_score,
+                              hipStream_t stream) {
+  if (nv_cap <= 24 * kTopkThreads)
+    hipLaunchKernelGGL((topk_single_kernel<kTopkThreads, 24 * kTopkThreads>), dim3(a.N), dim3(kTopkThreads), 0,
+                       stream, a, k, out_idx, out_score);
+  else
+    hipLaunchKernelGGL((topk_single_kernel<kTopkThreads, kSingleMax>), dim3(a.N), dim3(kTopkThreads), 0, stream,
+                       a, k, out_idx, out_score);
+  return hipGetLastError();
 }
 
 // Large selections, step 2: keep every key >= the query's threshold T (the minimum of its full
@@ -1211,9 +1248,7 @@ hipError_t launch_topk(const IndexArgs& a, const TopkPlan& plan, int topk, int32
                        float* out_score, uint8_t* ws, int blk_entries, hipStream_t stream) {
   if (a.N == 0) return hipSuccess;
   if (!plan.large) {
-    hipLaunchKernelGGL((topk_single_kernel<kTopkThreads, kSingleMax>), dim3(a.N), dim3(kTopkThreads),
-                       0, stream, a, topk, out_idx, out_score);
-    return hipGetLastError();
+    return launch_topk_single(a, a.nv_cap, topk, out_idx, out_score, stream);
   }
   const int64_t cstride = a.score_stride;
   uint32_t* ckey = reinterpret_cast<uint32_t*>(ws + plan.cand_off);
@@ -1271,9 +1306,7 @@ hipError_t launch_candidate_blocks(const IndexArgs& a, const CandPlan& cp, uint8
   b.nv_div = cand_block;
   b.blk_thr = nullptr;
   b.cand_count = nullptr;
-  hipLaunchKernelGGL((topk_single_kernel<kTopkThreads, kSingleMax>), dim3(a.N), dim3(kTopkThreads), 0, stream, b,
-                     n_cand, cand_out, static_cast<float*>(nullptr));
-  return hipGetLastError();
+  return launch_topk_single(b, nb_cap, n_cand, cand_out, static_cast<float*>(nullptr), stream);
 }
 
 }  // namespace hcs

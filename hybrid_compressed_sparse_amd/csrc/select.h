@@ -196,7 +196,7 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of, u
 }
 
 // Radix select of the k-th largest key when every thread holds its keys in registers (up to IPT,
-// slot j present when bit j of vmask is set) in a block of 512 or 1024 threads: the key range and
+// key_at(j) the key of slot j, present when bit j of vmask is set) in a block of 512 or 1024 threads: the key range and
 // count come from wave reductions, then 11-bit digits below the keys' common leading part, each
 // pass one histogram (LDS atomics issued back to back), a wave prefix sum over the 4 or 2 bins of
 // each thread and the bin search, with three LDS-only barriers. The passes stop once the bin of the k-th key
@@ -204,8 +204,8 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of, u
 // All present keys are taken when there are at most k of them (mask 0: every key is in the
 // "bin"). Expects hist[0] cleared and a barrier after; leaves both histograms cleared (ordered
 // by the caller's next barrier).
-template <int NT, int IPT>
-__device__ KthResult reg_kth(SelShared& sh, const uint32_t (&key)[IPT], uint32_t vmask, unsigned k) {
+template <int NT, int IPT, class KeyAt>
+__device__ KthResult reg_kth(SelShared& sh, KeyAt key_at, uint32_t vmask, unsigned k) {
   static_assert((NT == 512 || NT == 1024) && IPT <= 32, "512 or 1024 threads");
   constexpr int NW = NT / 64, BPT = kBins / NT;   // bins per thread in the scan: 4 or 2
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -214,8 +214,8 @@ __device__ KthResult reg_kth(SelShared& sh, const uint32_t (&key)[IPT], uint32_t
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
     if ((vmask >> j) & 1u) {
-      lmax = max(lmax, key[j]);
-      lmin = min(lmin, key[j]);
+      lmax = max(lmax, key_at(j));
+      lmin = min(lmin, key_at(j));
       ++lcnt;
     }
   }
@@ -261,7 +261,7 @@ __device__ KthResult reg_kth(SelShared& sh, const uint32_t (&key)[IPT], uint32_t
     unsigned* hist = sh.hist[pass & 1];
 #pragma unroll
     for (int j = 0; j < IPT; ++j)
-      if (((vmask >> j) & 1u) && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & (kBins - 1)], 1u);
+      if (((vmask >> j) & 1u) && (key_at(j) & mask) == prefix) atomicAdd(&hist[(key_at(j) >> shift) & (kBins - 1)], 1u);
     lds_barrier();
     // thread t owns bins kBins-1-BPT t down to kBins-BPT-BPT t, one 16- or 8-byte read
     unsigned cc[BPT], tot = 0;
@@ -321,7 +321,7 @@ __device__ unsigned reg_topk(SelShared& sh, const uint32_t (&key)[IPT], uint32_t
                              bool ids_ascending, IdOf id_of, Emit emit) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const KthResult r = reg_kth<NT, IPT>(sh, key, vmask, k);
+  const KthResult r = reg_kth<NT, IPT>(sh, [&](int j) { return key[j]; }, vmask, k);
   // the keys equal to the k-th that are taken: all of them unless r.need < r.n_eq
   uint32_t tmask = 0u;                              // slots of keys in the k-th key's bin
 #pragma unroll
@@ -330,15 +330,14 @@ __device__ unsigned reg_topk(SelShared& sh, const uint32_t (&key)[IPT], uint32_t
   const bool by_id = r.need < r.n_eq && !ids_ascending;
   uint32_t take_tie = tmask;                        // by_id: those of the r.need smallest ids
   if (by_id) {
-    uint32_t nid[IPT];
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) nid[j] = ~(uint32_t)id_of(j);
+    // keys ~id, recomputed where used rather than held in registers
+    const auto nid = [&](int j) { return ~(uint32_t)id_of(j); };
     lds_barrier();                                  // the histograms' clears are done
     const KthResult r2 = reg_kth<NT, IPT>(sh, nid, tmask, r.need);
     take_tie = 0u;
 #pragma unroll
     for (int j = 0; j < IPT; ++j)
-      take_tie |= (((tmask >> j) & 1u) && (nid[j] & r2.mask) >= r2.prefix ? 1u : 0u) << j;
+      take_tie |= (((tmask >> j) & 1u) && (nid(j) & r2.mask) >= r2.prefix ? 1u : 0u) << j;
   }
   // counts of this thread: keys above the bin, keys in it (ties)
   unsigned na = 0, ne = 0;
