@@ -195,17 +195,29 @@ __device__ KthResult radix_kth(SelShared& sh, int n, unsigned k, KeyOf key_of, u
   return r;
 }
 
+// The bin of the k-th largest key as a key range: keys k with k - lo <= span (k >= lo) are in
+// it, keys above lo + span are above the k-th; `need` of its n_eq keys belong to the top k.
+struct KthRange {
+  uint32_t lo, span;
+  unsigned need, n_eq;
+  __device__ bool in_bin(uint32_t key) const { return key >= lo && key - lo <= span; }
+  __device__ bool above(uint32_t key) const { return key >= lo && key - lo > span; }
+};
+
 // Radix select of the k-th largest key when every thread holds its keys in registers (up to IPT,
-// key_at(j) the key of slot j, present when bit j of vmask is set) in a block of 512 or 1024 threads: the key range and
-// count come from wave reductions, then 11-bit digits below the keys' common leading part, each
-// pass one histogram (LDS atomics issued back to back), a wave prefix sum over the 4 or 2 bins of
-// each thread and the bin search, with three LDS-only barriers. The passes stop once the bin of the k-th key
-// holds exactly the keys still needed, or every bit is resolved (then that bin holds equal keys).
-// All present keys are taken when there are at most k of them (mask 0: every key is in the
-// "bin"). Expects hist[0] cleared and a barrier after; leaves both histograms cleared (ordered
-// by the caller's next barrier).
+// key_at(j) the key of slot j, present when bit j of vmask is set) in a block of 512 or 1024
+// threads: the key range and count come from wave reductions; the digits are taken from the
+// offset key - min (so that the first pass spreads the keys over its 2048 bins by value even
+// when they straddle a power of two, where a digit below the common leading bits would put
+// nearly all of them in a few bins and serialise the histogram's atomics), 11 bits per pass.
+// Each pass is one histogram (LDS atomics issued back to back), a wave prefix sum over the 4
+// or 2 bins of each thread and the bin search, with three LDS-only barriers. The passes stop
+// once the bin of the k-th key holds exactly the keys still needed, or every bit is resolved
+// (then that bin holds equal keys). All present keys are taken when there are at most k of
+// them (the "bin" is every key). Expects hist[0] cleared and a barrier after; leaves both
+// histograms cleared (ordered by the caller's next barrier).
 template <int NT, int IPT, class KeyAt>
-__device__ KthResult reg_kth(SelShared& sh, KeyAt key_at, uint32_t vmask, unsigned k) {
+__device__ KthRange reg_kth(SelShared& sh, KeyAt key_at, uint32_t vmask, unsigned k) {
   static_assert((NT == 512 || NT == 1024) && IPT <= 32, "512 or 1024 threads");
   constexpr int NW = NT / 64, BPT = kBins / NT;   // bins per thread in the scan: 4 or 2
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -231,37 +243,39 @@ __device__ KthResult reg_kth(SelShared& sh, KeyAt key_at, uint32_t vmask, unsign
   uint32_t kmax = 0u, kmin = ~0u;
   unsigned total = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    kmax = max(kmax, sh.wmax[w]);
-    kmin = min(kmin, sh.wmin[w]);
-    total += sh.wcnt[w];
+  for (int v = 0; v < NW; ++v) {
+    kmax = max(kmax, sh.wmax[v]);
+    kmin = min(kmin, sh.wmin[v]);
+    total += sh.wcnt[v];
   }
-  KthResult r;
+  KthRange r;
   if (total <= k) {
-    r.prefix = 0u;
-    r.mask = 0u;
+    r.lo = 0u;
+    r.span = ~0u;
     r.need = r.n_eq = total;
     return r;
   }
-  const uint32_t diff = kmax ^ kmin;
-  if (diff == 0u) {                      // all present keys are equal
-    r.prefix = kmax;
-    r.mask = ~0u;
+  if (kmax == kmin) {                    // all present keys are equal
+    r.lo = kmax;
+    r.span = 0u;
     r.need = k;
     r.n_eq = total;
     return r;
   }
-  int top = 31 - __builtin_clz(diff);
-  uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
-  uint32_t prefix = kmax & mask;
+  // the bin so far: keys lo .. lo + 2^w - 1 (w <= 32: kmax - kmin < 2^w)
+  uint32_t lo = kmin;
+  int w = 32 - __builtin_clz(kmax - kmin);
   unsigned remaining = k, cnt_bin = total;
-  for (int pass = 0; top >= 0; ++pass) {
-    const int width = min(kDigitBits, top + 1);
-    const int shift = top - width + 1;
+  for (int pass = 0; w > 0; ++pass) {
+    const int width = min(kDigitBits, w);
+    const int shift = w - width;
+    const uint32_t wspan = w >= 32 ? ~0u : (1u << w) - 1u;
     unsigned* hist = sh.hist[pass & 1];
 #pragma unroll
-    for (int j = 0; j < IPT; ++j)
-      if (((vmask >> j) & 1u) && (key_at(j) & mask) == prefix) atomicAdd(&hist[(key_at(j) >> shift) & (kBins - 1)], 1u);
+    for (int j = 0; j < IPT; ++j) {
+      const uint32_t off = key_at(j) - lo;
+      if (((vmask >> j) & 1u) && key_at(j) >= lo && off <= wspan) atomicAdd(&hist[off >> shift], 1u);
+    }
     lds_barrier();
     // thread t owns bins kBins-1-BPT t down to kBins-BPT-BPT t, one 16- or 8-byte read
     unsigned cc[BPT], tot = 0;
@@ -284,7 +298,7 @@ __device__ KthResult reg_kth(SelShared& sh, KeyAt key_at, uint32_t vmask, unsign
     lds_barrier();
     unsigned run = incl - tot;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) run += w < wave ? sh.wsum[w] : 0u;
+    for (int v = 0; v < NW; ++v) run += v < wave ? sh.wsum[v] : 0u;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
       if (run < remaining && run + cc[j] >= remaining) {
@@ -295,16 +309,15 @@ __device__ KthResult reg_kth(SelShared& sh, KeyAt key_at, uint32_t vmask, unsign
       run += cc[j];
     }
     lds_barrier();
-    prefix |= sh.bin << shift;
-    mask |= ((1u << width) - 1u) << shift;
+    lo += sh.bin << shift;
     remaining -= sh.above;
     cnt_bin = sh.cnt_bin;
-    top = shift - 1;
+    w = shift;
     for (int j = tid; j < kBins; j += NT) hist[j] = 0;
     if (cnt_bin == remaining) break;
   }
-  r.prefix = prefix;
-  r.mask = mask;
+  r.lo = lo;
+  r.span = w >= 32 ? ~0u : (1u << w) - 1u;
   r.need = remaining;
   r.n_eq = cnt_bin;
   return r;
@@ -321,30 +334,30 @@ __device__ unsigned reg_topk(SelShared& sh, const uint32_t (&key)[IPT], uint32_t
                              bool ids_ascending, IdOf id_of, Emit emit) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const KthResult r = reg_kth<NT, IPT>(sh, [&](int j) { return key[j]; }, vmask, k);
+  const KthRange r = reg_kth<NT, IPT>(sh, [&](int j) { return key[j]; }, vmask, k);
   // the keys equal to the k-th that are taken: all of them unless r.need < r.n_eq
   uint32_t tmask = 0u;                              // slots of keys in the k-th key's bin
 #pragma unroll
   for (int j = 0; j < IPT; ++j)
-    tmask |= (((vmask >> j) & 1u) && (key[j] & r.mask) == r.prefix ? 1u : 0u) << j;
+    tmask |= (((vmask >> j) & 1u) && r.in_bin(key[j]) ? 1u : 0u) << j;
   const bool by_id = r.need < r.n_eq && !ids_ascending;
   uint32_t take_tie = tmask;                        // by_id: those of the r.need smallest ids
   if (by_id) {
     // keys ~id, recomputed where used rather than held in registers
     const auto nid = [&](int j) { return ~(uint32_t)id_of(j); };
     lds_barrier();                                  // the histograms' clears are done
-    const KthResult r2 = reg_kth<NT, IPT>(sh, nid, tmask, r.need);
+    const KthRange r2 = reg_kth<NT, IPT>(sh, nid, tmask, r.need);
     take_tie = 0u;
 #pragma unroll
     for (int j = 0; j < IPT; ++j)
-      take_tie |= (((tmask >> j) & 1u) && (nid(j) & r2.mask) >= r2.prefix ? 1u : 0u) << j;
+      take_tie |= (((tmask >> j) & 1u) && nid(j) >= r2.lo ? 1u : 0u) << j;
   }
   // counts of this thread: keys above the bin, keys in it (ties)
   unsigned na = 0, ne = 0;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
     if ((vmask >> j) & 1u) {
-      na += (key[j] & r.mask) > r.prefix ? 1u : 0u;
+      na += r.above(key[j]) ? 1u : 0u;
       ne += (take_tie >> j) & 1u;
     }
   }
@@ -367,7 +380,7 @@ __device__ unsigned reg_topk(SelShared& sh, const uint32_t (&key)[IPT], uint32_t
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
     if ((vmask >> j) & 1u) {
-      bool take = (key[j] & r.mask) > r.prefix;
+      bool take = r.above(key[j]);
       if ((take_tie >> j) & 1u) take = eq_seen++ < need;
       if (take) emit(pos++, j, key[j]);
     }
