@@ -343,6 +343,9 @@ static hcs_status prep_index(const void* q, const uint8_t* q_scale, const float*
   hcs_status s = prep_index_args(q, q_scale, w, keys, q_seq, q_pos, seq, P0, N, H_I, d_I, m, max_pos, a);
   if (s != HCS_OK || N == 0) return s;
   if (!out_idx) return fail(HCS_ERR_INVALID_ARG, "null out_idx");
+  if ((int64_t)(max_pos + 1) / m > hcs::kMaxTopkVisible)
+    return fail(HCS_ERR_UNSUPPORTED, "(max_pos + 1) / m = %lld visible entries exceed %lld",
+                (long long)((int64_t)(max_pos + 1) / m), (long long)hcs::kMaxTopkVisible);
   plan = hcs::topk_plan(N, max_pos, m, topk);
   if (!ws || ws_bytes < plan.ws_bytes)
     return fail(HCS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.ws_bytes, ws_bytes);
@@ -353,7 +356,6 @@ static hcs_status prep_index(const void* q, const uint8_t* q_scale, const float*
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   if (plan.large) {
     a.blk_thr = reinterpret_cast<uint32_t*>(w8 + plan.thr_off);
-    a.cand_count = reinterpret_cast<unsigned*>(w8 + plan.cnt_off);
     a.thr_stride = plan.thr_stride;
   }
   return HCS_OK;

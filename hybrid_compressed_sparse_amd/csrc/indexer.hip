@@ -843,12 +843,15 @@ hipError_t launch_topk_single(const IndexArgs& a, int nv_cap, int k, int32_t* ou
 }
 
 // Large selections, step 2: keep every key >= the query's threshold T (the minimum of its full
-// scoring blocks' thresholds, or 0 when there is no bound) as a candidate (key, id), appended
-// through a per-query counter that the scoring launch zeroed. Block = (query, 8192 entries).
+// scoring blocks' thresholds, or 0 when there is no bound) as a candidate (key, id). Block =
+// (query, chunk of 8192 entries); the chunk's candidates go to the start of its own 8192 slots
+// and their number to its count (plain stores: no counter shared between blocks).
 constexpr int kFilterChunk = 8192;
+constexpr int kMaxFilterChunks = (int)(kMaxTopkVisible / kFilterChunk);
 __global__ __launch_bounds__(kScoreThreads) void topk_filter_kernel(IndexArgs a, int blk_entries,
                                                                     uint32_t* ckey, int32_t* cid,
-                                                                    unsigned* ccount, int64_t cstride) {
+                                                                    unsigned* ccount, int ccs,
+                                                                    int64_t cstride) {
   __shared__ uint32_t wmin[kScoreThreads / 64];
   const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int seq, nv;
@@ -857,7 +860,16 @@ __global__ __launch_bounds__(kScoreThreads) void topk_filter_kernel(IndexArgs a,
   if (nv <= a.topk || lo >= nv) return;              // short context: the select fills it directly
   const int full = nv / blk_entries;
   const int kb = full > 0 ? bound_kb(a.topk, full) : kMaxKb + 1;
-  // the block's scores are requested before the threshold is reduced (independent loads)
+  constexpr int kThrRegs = 8;                        // block bounds held per thread
+  const uint32_t* thr = a.blk_thr + (int64_t)t * a.thr_stride;
+  const bool few_bounds = kb <= kMaxKb && full <= kThrRegs * kScoreThreads;
+  // the bounds are requested first (the threshold needs them), then the block's scores, which
+  // stay in flight while the threshold is reduced
+  uint32_t v[kThrRegs];
+  if (few_bounds) {
+#pragma unroll
+    for (int u = 0; u < kThrRegs; ++u) v[u] = thr[min(u * kScoreThreads + (int)threadIdx.x, full - 1)];
+  }
   const float* sc = a.scores + (int64_t)t * a.score_stride;
   const int hi = min(nv, lo + kFilterChunk);
   constexpr int kPer = kFilterChunk / kScoreThreads;
@@ -866,21 +878,13 @@ __global__ __launch_bounds__(kScoreThreads) void topk_filter_kernel(IndexArgs a,
   uint32_t key[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) key[j] = __float_as_uint(sc[min(lo + j * kScoreThreads + (int)threadIdx.x, hi - 1)]);
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    key[j] = lo + j * kScoreThreads + (int)threadIdx.x < hi ? f32_order_key(__uint_as_float(key[j])) : 0u;
   uint32_t T = 0u;
-  constexpr int kThrRegs = 8;                        // block bounds held per thread
-  const uint32_t* thr = a.blk_thr + (int64_t)t * a.thr_stride;
-  if (kb <= kMaxKb && full <= kThrRegs * kScoreThreads) {
+  if (few_bounds) {
     // T = the lower edge of the highest of 256 equal bins over [min b, max b] whose suffix
     // holds at least J = ceil(k / kb) bounds: at least J bounds are >= T (valid), and T is
     // within one bin of the J-th largest bound
     __shared__ uint32_t wmax[kScoreThreads / 64], hist[256], tsel;
     const uint32_t J = (uint32_t)((a.topk + kb - 1) / kb);
-    uint32_t v[kThrRegs];
-#pragma unroll
-    for (int u = 0; u < kThrRegs; ++u) v[u] = thr[min(u * kScoreThreads + (int)threadIdx.x, full - 1)];
     uint32_t blo = ~0u, bhi = 0u;
 #pragma unroll
     for (int u = 0; u < kThrRegs; ++u)
@@ -948,9 +952,11 @@ __global__ __launch_bounds__(kScoreThreads) void topk_filter_kernel(IndexArgs a,
     __syncthreads();
     T = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
   }
-  // keep flags of the block's entries (entry lo + 256 j + tid for j < kPer), one counter update
-  // per block: per-wave counts, block prefix in LDS, then every kept entry gets its slot
-  __shared__ unsigned wcnt[kScoreThreads / 64], wbase[kScoreThreads / 64 + 1];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) key[j] = f32_order_key(__uint_as_float(key[j]));
+  // keep flags of the block's entries (entry lo + 256 j + tid for j < kPer): per-wave counts,
+  // the block's prefix from LDS, then every kept entry gets its slot in the chunk's range
+  __shared__ unsigned wcnt[kScoreThreads / 64];
   uint64_t km[kPer];
   unsigned mine = 0;
 #pragma unroll
@@ -961,104 +967,164 @@ __global__ __launch_bounds__(kScoreThreads) void topk_filter_kernel(IndexArgs a,
   }
   if (lane == 0) wcnt[wave] = mine;                  // the wave's kept entries
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned tot = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-    const unsigned base = tot ? atomicAdd(ccount + t, tot) : 0u;
-    unsigned run = base;
-    for (int w = 0; w < kScoreThreads / 64; ++w) {
-      wbase[w] = run;
-      run += wcnt[w];
-    }
-  }
-  __syncthreads();
-  unsigned slot = wbase[wave];
+  unsigned slot = 0;
+#pragma unroll
+  for (int w = 0; w < kScoreThreads / 64; ++w) slot += w < wave ? wcnt[w] : 0u;
+  if (threadIdx.x == 0) ccount[(int64_t)t * ccs + blockIdx.y] = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+  uint32_t* ck = ckey + (int64_t)t * cstride + lo;   // slots < hi - lo: inside the query's range
+  int32_t* ci = cid + (int64_t)t * cstride + lo;
   const uint64_t below = (1ull << lane) - 1;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     if ((km[j] >> lane) & 1ull) {
       const unsigned sl = slot + (unsigned)__popcll(km[j] & below);
-      ckey[(int64_t)t * cstride + sl] = key[j];
-      cid[(int64_t)t * cstride + sl] = lo + j * kScoreThreads + threadIdx.x;
+      ck[sl] = key[j];
+      ci[sl] = lo + j * kScoreThreads + threadIdx.x;
     }
     slot += (unsigned)__popcll(km[j]);
   }
 }
 
-// Large selections, step 3: the top-k of a query's candidates (keys in LDS when they fit).
+// Large selections, step 3: the top-k of a query's candidates, in one of two layouts:
+//  * filter (cand_mode 0): chunk c of the query's 8192-entry chunks has ccount[t * ccs + c]
+//    candidates at slots c * 8192 + 0, 1, ...; at most 32 chunks of at most 256 candidates each
+//    (the usual case) are loaded with their counts in one go, slot u of a thread holding slot
+//    (u % 4) * 64 + lane of chunk 2 wave + u / 4, and selected in registers; otherwise the
+//    chunks' offsets are summed in LDS and candidate i is found by a search over them;
+//  * listed blocks (cand_mode 1): ccount[t] candidates at slots 0, 1, ... .
+// With more candidates than fit the register or LDS selections, keys (and ids) are read from
+// memory where each pass needs them.
 __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(IndexArgs a, int k,
                                                                    const uint32_t* ckey,
                                                                    const int32_t* cid,
-                                                                   const unsigned* ccount,
+                                                                   const unsigned* ccount, int ccs,
                                                                    int64_t cstride,
                                                                    int32_t* out_idx,
                                                                    float* out_score,
                                                                    int cand_mode) {
   __shared__ SelShared sh;
   __shared__ uint32_t kl[kSingleMax];
-  const int t = blockIdx.x;
+  __shared__ unsigned coff[kMaxFilterChunks + 1];
+  __shared__ unsigned wfit[kTopkThreads / 64];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int seq, nv;
   query_of(a, t, seq, nv);
   int32_t* oi = out_idx + (int64_t)t * k;
   float* os = out_score ? out_score + (int64_t)t * k : nullptr;
-  if (cand_mode) {                                   // the listed blocks' entries are the candidates
-    const int n = (int)ccount[t];
-    if (n <= k) {
-      const uint32_t* ck = ckey + (int64_t)t * cstride;
-      const int32_t* ci = cid + (int64_t)t * cstride;
-      for (int j = threadIdx.x; j < k; j += kTopkThreads) {
-        oi[j] = j < n ? ci[j] : -1;
-        if (os) os[j] = j < n ? order_key_f32(ck[j]) : 0.f;
-      }
-      return;
-    }
-  } else if (nv <= k) {
-    const float* sc = a.scores + (int64_t)t * a.score_stride;
-    for (int j = threadIdx.x; j < k; j += kTopkThreads) {
-      oi[j] = j < nv ? j : -1;
-      if (os) os[j] = j < nv ? sc[j] : 0.f;
-    }
-    return;
-  }
   const uint32_t* ck = ckey + (int64_t)t * cstride;
   const int32_t* ci = cid + (int64_t)t * cstride;
-  // the first kSpec candidates are loaded together with their count, so that a query with no
-  // more (the usual case) costs one memory latency here instead of two
-  constexpr int kSpecPT = 8, kSpec = kSpecPT * kTopkThreads;
-  uint32_t sk[kSpecPT];
-  uint32_t sid[kSpecPT];
-  if (!cand_mode) {
-#pragma unroll
-    for (int u = 0; u < kSpecPT; ++u) {
-      const int64_t i = min((int64_t)(u * kTopkThreads + (int)threadIdx.x), cstride - 1);
-      sk[u] = ck[i];
-      sid[u] = (uint32_t)ci[i];
-    }
-  }
-  const int n = (int)ccount[t];                      // > k: every key >= the k-th is a candidate
   auto emit = [&](unsigned slot, int id, uint32_t key) {
     if (slot < (unsigned)k) {
       oi[slot] = id;
       if (os) os[slot] = order_key_f32(key);
     }
   };
-  auto same = [](uint32_t v) { return v; };
-  if (!cand_mode && n <= kSpec) {
-    // the loaded candidates are the keys (slot u of a thread: candidate u * kTopkThreads + tid)
-    uint32_t vmask = 0u;
+  int n;                                             // candidates
+  int nch = 0;                                       // filter: chunks (offsets in coff)
+  if (cand_mode) {                                   // the listed blocks' entries are the candidates
+    n = (int)ccount[t];
+    if (n <= k) {
+      for (int j = tid; j < k; j += kTopkThreads) {
+        oi[j] = j < n ? ci[j] : -1;
+        if (os) os[j] = j < n ? order_key_f32(ck[j]) : 0.f;
+      }
+      return;
+    }
+  } else {
+    if (nv <= k) {
+      const float* sc = a.scores + (int64_t)t * a.score_stride;
+      for (int j = tid; j < k; j += kTopkThreads) {
+        oi[j] = j < nv ? j : -1;
+        if (os) os[j] = j < nv ? sc[j] : 0.f;
+      }
+      return;
+    }
+    nch = (nv + kFilterChunk - 1) / kFilterChunk;
+    const unsigned* cc = ccount + (int64_t)t * ccs;
+    // the first 256 slots of chunks 2 wave and 2 wave + 1, loaded with the two counts
+    constexpr int kSpecPT = 8, kSpecChunk = 256;
+    static_assert(kSpecPT * kTopkThreads == 32 * kSpecChunk, "two chunks per wave");
+    uint32_t sk[kSpecPT], sid[kSpecPT];
 #pragma unroll
-    for (int u = 0; u < kSpecPT; ++u) vmask |= (u * kTopkThreads + (int)threadIdx.x < n ? 1u : 0u) << u;
+    for (int u = 0; u < kSpecPT; ++u) {
+      const int64_t i = min((int64_t)(2 * wave + u / 4) * kFilterChunk + (u % 4) * 64 + lane, cstride - 1);
+      sk[u] = ck[i];
+      sid[u] = (uint32_t)ci[i];
+    }
+    const unsigned n0 = 2 * wave < nch ? cc[min(2 * wave, nch - 1)] : 0u;
+    const unsigned n1 = 2 * wave + 1 < nch ? cc[min(2 * wave + 1, nch - 1)] : 0u;
+    if (lane == 0) wfit[wave] = n0 <= kSpecChunk && n1 <= kSpecChunk ? 1u : 0u;
     sel_reset<kTopkThreads>(sh);
     __syncthreads();
-    reg_topk<kTopkThreads, kSpecPT>(sh, sk, vmask, (unsigned)k, false, [&](int u) { return (int)sid[u]; },
-                                    [&](unsigned pos, int u, uint32_t key) { emit(pos, (int)sid[u], key); });
-    return;
+    bool fits = nch <= 32;
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / 64; ++w) fits = fits && wfit[w] != 0u;
+    if (fits) {
+      uint32_t vmask = 0u;
+#pragma unroll
+      for (int u = 0; u < kSpecPT; ++u) vmask |= ((u % 4) * 64 + lane < (int)(u < 4 ? n0 : n1) ? 1u : 0u) << u;
+      const unsigned n_sel = reg_topk<kTopkThreads, kSpecPT>(
+          sh, sk, vmask, (unsigned)k, false, [&](int u) { return (int)sid[u]; },
+          [&](unsigned pos, int u, uint32_t key) { emit(pos, (int)sid[u], key); });
+      for (int j = (int)n_sel + tid; j < k; j += kTopkThreads) oi[j] = -1;   // (fewer than k: not expected)
+      return;
+    }
+    // chunk offsets: exclusive prefix sum of the counts (nch <= kMaxFilterChunks <= threads)
+    static_assert(kMaxFilterChunks <= kTopkThreads, "one chunk count per thread");
+    const unsigned c = tid < nch ? cc[tid] : 0u;
+    const unsigned incl = wave_incl_scan_u32(c);
+    if (lane == 63) sh.wsum[wave] = incl;
+    __syncthreads();
+    unsigned before = incl - c, all = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / 64; ++w) {
+      before += w < wave ? sh.wsum[w] : 0u;
+      all += sh.wsum[w];
+    }
+    if (tid < nch) coff[tid] = before;
+    if (tid == 0) coff[nch] = all;
+    n = (int)all;
+    __syncthreads();
+    if (n <= k) {                                    // (not expected: T is at most the k-th key)
+      for (int j = tid; j < k; j += kTopkThreads) {
+        int id = -1;
+        uint32_t key = 0u;
+        if (j < n) {
+          int lo = 0, hi = nch;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (coff[mid] <= (unsigned)j) lo = mid;
+            else hi = mid;
+          }
+          const int64_t sl = (int64_t)lo * kFilterChunk + (j - (int)coff[lo]);
+          id = ci[sl];
+          key = ck[sl];
+        }
+        oi[j] = id;
+        if (os) os[j] = j < n ? order_key_f32(key) : 0.f;
+      }
+      return;
+    }
   }
-  static_assert(kSpec <= kSingleMax / 2, "the loaded candidates fit the LDS key and id halves");
+  // slot of candidate i: i itself (listed blocks) or its place in its chunk (filter)
+  auto slot_of = [&](int i) -> int64_t {
+    if (cand_mode) return i;
+    int lo = 0, hi = nch;                            // coff[lo] <= i < coff[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (coff[mid] <= (unsigned)i) lo = mid;
+      else hi = mid;
+    }
+    return (int64_t)lo * kFilterChunk + (i - (int)coff[lo]);
+  };
   if (n <= kSingleMax / 2) {
     // keys and ids in LDS
     uint32_t* kid = kl + kSingleMax / 2;
-    lds_fill<kTopkThreads>(kl, ck, n, same);
-    lds_fill<kTopkThreads>(kid, reinterpret_cast<const uint32_t*>(ci), n, same);
+    for (int i = tid; i < n; i += kTopkThreads) {
+      const int64_t sl = slot_of(i);
+      kl[i] = ck[sl];
+      kid[i] = (uint32_t)ci[sl];
+    }
     sel_reset<kTopkThreads>(sh);
     __syncthreads();
     block_topk<kTopkThreads>(
@@ -1067,19 +1133,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(IndexArgs a, 
     return;
   }
   if (n <= kSingleMax) {
-    lds_fill<kTopkThreads>(kl, ck, n, same);
+    for (int i = tid; i < n; i += kTopkThreads) kl[i] = ck[slot_of(i)];
     sel_reset<kTopkThreads>(sh);
     __syncthreads();
     block_topk<kTopkThreads>(
-        sh, n, k, [&](int i, uint32_t& key) { key = kl[i]; return true; }, [&](int i) { return ci[i]; },
+        sh, n, k, [&](int i, uint32_t& key) { key = kl[i]; return true; }, [&](int i) { return ci[slot_of(i)]; },
         emit);
     return;
   }
   sel_reset<kTopkThreads>(sh);
   __syncthreads();
   block_topk<kTopkThreads>(
-      sh, n, k, [&](int i, uint32_t& key) { key = ck[i]; return true; }, [&](int i) { return ci[i]; },
-      emit);
+      sh, n, k, [&](int i, uint32_t& key) { key = ck[slot_of(i)]; return true; },
+      [&](int i) { return ci[slot_of(i)]; }, emit);
 }
 
 // ---------------------------------------------------------------- two-level candidate filtering
@@ -1152,8 +1218,9 @@ TopkPlan topk_plan(int N, int max_pos, int m, int topk) {
     off += up((size_t)N * p.thr_stride * sizeof(uint32_t));
     p.cand_off = off;                                // keys [N, stride] then ids [N, stride]
     off += up((size_t)N * stride * sizeof(uint32_t)) + up((size_t)N * stride * sizeof(int32_t));
+    p.cnt_stride = (int)((nv + kFilterChunk - 1) / kFilterChunk);   // per-chunk candidate counts
     p.cnt_off = off;
-    off += up((size_t)N * sizeof(unsigned));
+    off += up((size_t)N * p.cnt_stride * sizeof(unsigned));
   }
   p.ws_bytes = off;
   return p;
@@ -1253,11 +1320,12 @@ hipError_t launch_topk(const IndexArgs& a, const TopkPlan& plan, int topk, int32
   const int64_t cstride = a.score_stride;
   uint32_t* ckey = reinterpret_cast<uint32_t*>(ws + plan.cand_off);
   int32_t* cid = reinterpret_cast<int32_t*>(ws + plan.cand_off + ((size_t)a.N * cstride * 4 + 255) / 256 * 256);
-  unsigned* cnt = a.cand_count;
+  unsigned* cnt = reinterpret_cast<unsigned*>(ws + plan.cnt_off);
+  if (plan.cnt_stride > kMaxFilterChunks) return hipErrorInvalidValue;
   hipLaunchKernelGGL(topk_filter_kernel, dim3(a.N, (a.nv_cap + kFilterChunk - 1) / kFilterChunk),
-                     dim3(kScoreThreads), 0, stream, a, blk_entries, ckey, cid, cnt, cstride);
+                     dim3(kScoreThreads), 0, stream, a, blk_entries, ckey, cid, cnt, plan.cnt_stride, cstride);
   hipLaunchKernelGGL(topk_select_kernel, dim3(a.N), dim3(kTopkThreads), 0, stream, a, topk, ckey, cid,
-                     cnt, cstride, out_idx, out_score, 0);
+                     cnt, plan.cnt_stride, cstride, out_idx, out_score, 0);
   return hipGetLastError();
 }
 
@@ -1288,7 +1356,7 @@ hipError_t launch_topk_in_blocks(const IndexArgs& a, const CandPlan& cp, uint8_t
   unsigned* cnt = reinterpret_cast<unsigned*>(ws + cp.cnt_off);
   hipLaunchKernelGGL(cand_gather_kernel, dim3(a.N, n_cand), dim3(kScoreThreads), 0, stream, a, cand_in, n_cand,
                      cand_block, ckey, cid, cnt, cp.cstride);
-  hipLaunchKernelGGL(topk_select_kernel, dim3(a.N), dim3(kTopkThreads), 0, stream, a, topk, ckey, cid, cnt,
+  hipLaunchKernelGGL(topk_select_kernel, dim3(a.N), dim3(kTopkThreads), 0, stream, a, topk, ckey, cid, cnt, 1,
                      cp.cstride, out_idx, out_score, 1);
   return hipGetLastError();
 }

@@ -144,7 +144,8 @@ struct IndexArgs {
   // large selections: per scoring block, the kb-th largest score key of a full block
   // (kb = ceil(topk / full blocks of the query)); nullptr when not needed
   uint32_t* blk_thr;          // [N, thr_stride]
-  unsigned* cand_count;       // [N] candidate counters of the filter, zeroed by the scoring launch
+  unsigned* cand_count;       // [N] candidate counters of the listed-block gather, zeroed by the
+                              // scoring launch (nullptr: none)
   int thr_stride, topk;
   // a chunk of consecutive queries of one sequence (q_seq == nullptr): query t is at position
   // p0 + t of sequence seq_const
@@ -153,9 +154,12 @@ struct IndexArgs {
   int nv_div;
 };
 
+// the most visible entries per query of an indexer selection (the filter's 512 chunks of 8192)
+constexpr int64_t kMaxTopkVisible = 4194304;
 struct TopkPlan {
   int large;                  // n_visible may exceed kSingleMax: threshold + filter + select
   int thr_stride;             // block thresholds per query (scoring blocks of >= 256 entries)
+  int cnt_stride;             // filter chunks (of 8192 entries) per query: candidate counts
   size_t score_bytes, thr_off, cand_off, cnt_off, ws_bytes;
 };
 TopkPlan topk_plan(int N, int max_pos, int m, int topk);

@@ -221,7 +221,7 @@ hcs_status hcs_compress_kv_full(const void* kv, const void* score, int in_dtype,
 /*          256-byte aligned (score scratch; no initial contents needed). Calls that overlap */
 /*          in time must not share it.                                                     */
 /* Constraints: H_I in 1..64, d_I in {32, 64, 128} (bf16) or d_I == 128 (mxfp4, fp8ix),   */
-/* 1 <= topk <= 4096.                                                                     */
+/* 1 <= topk <= 4096, (max_pos + 1) / m <= 4194304 visible entries (HCS_ERR_UNSUPPORTED). */
 size_t hcs_index_topk_workspace_size(int N, int max_pos, int m, int topk);
 hcs_status hcs_index_topk(const void* q, const uint8_t* q_scale, const float* w, hcs_paged keys,
                           const int32_t* q_seq, const int32_t* q_pos, int N, int H_I, int d_I,

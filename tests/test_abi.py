@@ -76,6 +76,13 @@ def test_validation_errors_before_any_launch():
     st = L.hcs_index_topk(16, None, 16, _paged(0, 128), 16, 16, 4, 64, 128, 4, 64, 1000, 16, None,
                           None, 0, None)
     assert st == 3
+    # at most 4194304 visible entries per query (m = 1: max_pos + 1 entries)
+    st = L.hcs_index_topk(16, None, 16, _paged(0, 128, stride=70000), 16, 16, 4, 64, 128, 1, 64, 4194304, 16,
+                          None, None, 0, None)
+    assert st == 2 and b"visible entries" in L.hcs_last_error()
+    st = L.hcs_index_topk(16, None, 16, _paged(0, 128, stride=70000), 16, 16, 4, 64, 128, 1, 64, 4194303, 16,
+                          None, None, 0, None)
+    assert st == 3
     # compressor: bad dtype, coarse m, wrong cache dim
     assert L.hcs_compress_kv(16, 16, 7, 512, 16, 16, 2, 4, 512, 4, None, 16, _paged(), None, 0, None) == 1
     assert L.hcs_compress_kv(16, 16, 1, 512, 16, 16, 2, 4, 512, 2000, None, 16, _paged(), None, 0, None) == 2

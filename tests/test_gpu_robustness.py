@@ -118,6 +118,58 @@ def test_page_range_error_word():
     pt.copy_(saved)
 
 
+def _select_with_keys(wl, ctx, seed, mutate):
+    """The CSA decode select of one query over keys changed by mutate(keys) (the generated logical
+    copy, which the oracle reads, and the pool get the same rows); returns (gpu ids, gpu scores,
+    oracle ids, oracle scores)."""
+    from synth import layout as SL
+    sc = G.build(wl, seed=seed, device=_dev(), ctx_per_seq=[ctx])
+    keys = sc.ix.rows[0]
+    assert sc.ix.lo[0] == 0
+    mutate(keys, sc)
+    ids_all = torch.arange(keys.shape[0], device=_dev())
+    SL.scatter_rows(sc.ix.pool, sc.ix.fmt, sc.ix.dim, sc.ix.page_table[0], ids_all, keys)
+    step = PathStep(U.shape_of(sc), device=_dev())
+    q, qs = U._ix_q_args(sc)
+    step.select(q, qs, sc.ix_w.contiguous(), sc.ix, sc.q_seq, sc.q_pos)
+    torch.cuda.synchronize()
+    ids, s = OP.query_topk(sc, 0)
+    return step.idx[0].cpu().numpy(), step.score[0].cpu().numpy(), ids, s
+
+
+def test_select_candidates_clustered_in_one_chunk():
+    """The top-2048 of 40000 entries concentrated in one 8192-entry chunk of the filter (3000 keys
+    there scaled by 4): that chunk keeps more candidates than the register select loads per
+    chunk, so the select finds candidates through the chunks' offsets (keys and ids in LDS)."""
+    nv, k = 40000, 2048
+    wl = C.CSA_DECODE.with_(B=1, topk=k)
+    U.say(f"[case] clustered candidates {wl.name} nv={nv} k={k} seed=26")
+
+    def mutate(keys, sc):
+        keys[2 * 8192: 2 * 8192 + 3000] *= 4
+    gi, gs, ids, s = _select_with_keys(wl, 4 * nv + 1, 26, mutate)
+    in_chunk = ((ids[:k] >= 2 * 8192) & (ids[:k] < 3 * 8192)).sum()
+    assert in_chunk > 256, in_chunk                   # that chunk alone holds more than 256 candidates
+    U.check_topk(gi, gs, ids, s, k)
+
+
+def test_select_between_16384_and_32768_candidates():
+    """20000 equal keys above every other score among 60000 entries (the best-scoring row doubled,
+    exact in bf16): more candidates than the LDS holds with their ids (keys in LDS, ids read
+    through the chunk offsets), and the top-300 is the 300 smallest ids of the tie."""
+    nv, k = 60000, 300
+    wl = C.CSA_DECODE.with_(B=1, topk=k)
+    U.say(f"[case] 16384..32768 candidates {wl.name} nv={nv} k={k} seed=27")
+
+    def mutate(keys, sc):
+        best = int(OP.query_topk(sc, 0)[0][0])
+        keys[:20000] = (keys[best:best + 1] * 2).expand(20000, -1)
+    gi, gs, ids, s = _select_with_keys(wl, 4 * nv + 1, 27, mutate)
+    assert np.all(s[:20000] == s[0]) and s[0] > s[20000:].max()
+    assert np.array_equal(np.sort(gi), np.arange(k))
+    U.check_topk(gi, gs, ids, s, k)
+
+
 def test_select_bin_larger_than_131072():
     """More than 131072 candidates share the k-th key's radix bin (almost every key equal, a few
     slightly larger and smaller): the exact top-k is the larger ones plus the smallest ids of
