@@ -854,30 +854,36 @@ __global__ __launch_bounds__(kScoreThreads) void topk_filter_kernel(IndexArgs a,
                                                                     int64_t cstride) {
   __shared__ uint32_t wmin[kScoreThreads / 64];
   const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int seq, nv;
-  query_of(a, t, seq, nv);
-  const int lo = blockIdx.y * kFilterChunk;
-  if (nv <= a.topk || lo >= nv) return;              // short context: the select fills it directly
-  const int full = nv / blk_entries;
-  const int kb = full > 0 ? bound_kb(a.topk, full) : kMaxKb + 1;
+  const int lo = blockIdx.y * kFilterChunk;          // < nv_cap: the grid covers nv_cap
+  // The block bounds and the chunk's scores are requested before the query's position is known
+  // (indices clamped to the plan's capacity, entries past the query's visible ones masked
+  // later), so that the position's load and theirs overlap. The output pointers are formed here
+  // too, so that their kernel arguments are read at the start, not after the barriers where
+  // they are first used (a scalar load there would cost a memory latency of its own).
   constexpr int kThrRegs = 8;                        // block bounds held per thread
-  const uint32_t* thr = a.blk_thr + (int64_t)t * a.thr_stride;
-  const bool few_bounds = kb <= kMaxKb && full <= kThrRegs * kScoreThreads;
-  // the bounds are requested first (the threshold needs them), then the block's scores, which
-  // stay in flight while the threshold is reduced
-  uint32_t v[kThrRegs];
-  if (few_bounds) {
-#pragma unroll
-    for (int u = 0; u < kThrRegs; ++u) v[u] = thr[min(u * kScoreThreads + (int)threadIdx.x, full - 1)];
-  }
-  const float* sc = a.scores + (int64_t)t * a.score_stride;
-  const int hi = min(nv, lo + kFilterChunk);
   constexpr int kPer = kFilterChunk / kScoreThreads;
+  const uint32_t* thr = a.blk_thr + (int64_t)t * a.thr_stride;
+  uint32_t v[kThrRegs];
+#pragma unroll
+  for (int u = 0; u < kThrRegs; ++u) v[u] = thr[min(u * kScoreThreads + (int)threadIdx.x, a.thr_stride - 1)];
+  const float* sc = a.scores + (int64_t)t * a.score_stride;
+  const int cap = min(lo + kFilterChunk, a.nv_cap) - 1;
   // (loads at clamped indices, results selected after: a conditional load would be a branch,
   // and every branch merge a wait for that load alone)
   uint32_t key[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) key[j] = __float_as_uint(sc[min(lo + j * kScoreThreads + (int)threadIdx.x, hi - 1)]);
+  for (int j = 0; j < kPer; ++j) key[j] = __float_as_uint(sc[min(lo + j * kScoreThreads + (int)threadIdx.x, cap)]);
+  uint32_t* ck = ckey + (int64_t)t * cstride + lo;   // slots < hi - lo: inside the query's range
+  int32_t* ci = cid + (int64_t)t * cstride + lo;
+  unsigned* cnt_out = ccount + (int64_t)t * ccs + blockIdx.y;
+  asm volatile("" : "+s"(ck), "+s"(ci), "+s"(cnt_out));
+  int seq, nv;
+  query_of(a, t, seq, nv);
+  if (nv <= a.topk || lo >= nv) return;              // short context: the select fills it directly
+  const int full = nv / blk_entries;
+  const int kb = full > 0 ? bound_kb(a.topk, full) : kMaxKb + 1;
+  const bool few_bounds = kb <= kMaxKb && full <= kThrRegs * kScoreThreads;
+  const int hi = min(nv, lo + kFilterChunk);
   uint32_t T = 0u;
   if (few_bounds) {
     // T = the lower edge of the highest of 256 equal bins over [min b, max b] whose suffix
@@ -954,34 +960,29 @@ __global__ __launch_bounds__(kScoreThreads) void topk_filter_kernel(IndexArgs a,
   }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) key[j] = f32_order_key(__uint_as_float(key[j]));
-  // keep flags of the block's entries (entry lo + 256 j + tid for j < kPer): per-wave counts,
-  // the block's prefix from LDS, then every kept entry gets its slot in the chunk's range
+  // keep flags of the block's entries (entry lo + 256 j + tid for j < kPer) as one bit mask per
+  // thread; slots in thread order, then j: the thread's prefix within its wave (DPP scan) plus
+  // the earlier waves' counts from LDS
   __shared__ unsigned wcnt[kScoreThreads / 64];
-  uint64_t km[kPer];
-  unsigned mine = 0;
+  uint32_t keep = 0u;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = lo + j * kScoreThreads + threadIdx.x;
-    km[j] = __ballot(i < hi && key[j] >= T);
-    mine += (unsigned)__popcll(km[j]);
-  }
-  if (lane == 0) wcnt[wave] = mine;                  // the wave's kept entries
+  for (int j = 0; j < kPer; ++j)
+    keep |= (lo + j * kScoreThreads + (int)threadIdx.x < hi && key[j] >= T ? 1u : 0u) << j;
+  const unsigned mine = (unsigned)__popc(keep);
+  const unsigned incl = wave_incl_scan_u32(mine);
+  if (lane == 63) wcnt[wave] = incl;                 // the wave's kept entries
   __syncthreads();
-  unsigned slot = 0;
+  unsigned slot = incl - mine;
 #pragma unroll
   for (int w = 0; w < kScoreThreads / 64; ++w) slot += w < wave ? wcnt[w] : 0u;
-  if (threadIdx.x == 0) ccount[(int64_t)t * ccs + blockIdx.y] = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-  uint32_t* ck = ckey + (int64_t)t * cstride + lo;   // slots < hi - lo: inside the query's range
-  int32_t* ci = cid + (int64_t)t * cstride + lo;
-  const uint64_t below = (1ull << lane) - 1;
+  if (threadIdx.x == 0) *cnt_out = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    if ((km[j] >> lane) & 1ull) {
-      const unsigned sl = slot + (unsigned)__popcll(km[j] & below);
-      ck[sl] = key[j];
-      ci[sl] = lo + j * kScoreThreads + threadIdx.x;
+    if ((keep >> j) & 1u) {
+      ck[slot] = key[j];
+      ci[slot] = lo + j * kScoreThreads + threadIdx.x;
+      ++slot;
     }
-    slot += (unsigned)__popcll(km[j]);
   }
 }
 
@@ -1007,12 +1008,30 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(IndexArgs a, 
   __shared__ unsigned coff[kMaxFilterChunks + 1];
   __shared__ unsigned wfit[kTopkThreads / 64];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t* ck = ckey + (int64_t)t * cstride;
+  const int32_t* ci = cid + (int64_t)t * cstride;
+  // filter layout: the first 256 slots of chunks 2 wave and 2 wave + 1 and the two counts are
+  // requested before the query's position is known (indices clamped to the plan's capacity;
+  // chunks past the query's are dropped once it is)
+  constexpr int kSpecPT = 8, kSpecChunk = 256;
+  static_assert(kSpecPT * kTopkThreads == 32 * kSpecChunk, "two chunks per wave");
+  uint32_t sk[kSpecPT], sid[kSpecPT];
+  unsigned n0 = 0u, n1 = 0u;
+  const unsigned* cc = ccount + (int64_t)t * ccs;
+  if (!cand_mode) {
+#pragma unroll
+    for (int u = 0; u < kSpecPT; ++u) {
+      const int64_t i = min((int64_t)(2 * wave + u / 4) * kFilterChunk + (u % 4) * 64 + lane, cstride - 1);
+      sk[u] = ck[i];
+      sid[u] = (uint32_t)ci[i];
+    }
+    n0 = cc[min(2 * wave, ccs - 1)];
+    n1 = cc[min(2 * wave + 1, ccs - 1)];
+  }
   int seq, nv;
   query_of(a, t, seq, nv);
   int32_t* oi = out_idx + (int64_t)t * k;
   float* os = out_score ? out_score + (int64_t)t * k : nullptr;
-  const uint32_t* ck = ckey + (int64_t)t * cstride;
-  const int32_t* ci = cid + (int64_t)t * cstride;
   auto emit = [&](unsigned slot, int id, uint32_t key) {
     if (slot < (unsigned)k) {
       oi[slot] = id;
@@ -1040,19 +1059,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(IndexArgs a, 
       return;
     }
     nch = (nv + kFilterChunk - 1) / kFilterChunk;
-    const unsigned* cc = ccount + (int64_t)t * ccs;
-    // the first 256 slots of chunks 2 wave and 2 wave + 1, loaded with the two counts
-    constexpr int kSpecPT = 8, kSpecChunk = 256;
-    static_assert(kSpecPT * kTopkThreads == 32 * kSpecChunk, "two chunks per wave");
-    uint32_t sk[kSpecPT], sid[kSpecPT];
-#pragma unroll
-    for (int u = 0; u < kSpecPT; ++u) {
-      const int64_t i = min((int64_t)(2 * wave + u / 4) * kFilterChunk + (u % 4) * 64 + lane, cstride - 1);
-      sk[u] = ck[i];
-      sid[u] = (uint32_t)ci[i];
-    }
-    const unsigned n0 = 2 * wave < nch ? cc[min(2 * wave, nch - 1)] : 0u;
-    const unsigned n1 = 2 * wave + 1 < nch ? cc[min(2 * wave + 1, nch - 1)] : 0u;
+    n0 = 2 * wave < nch ? n0 : 0u;
+    n1 = 2 * wave + 1 < nch ? n1 : 0u;
     if (lane == 0) wfit[wave] = n0 <= kSpecChunk && n1 <= kSpecChunk ? 1u : 0u;
     sel_reset<kTopkThreads>(sh);
     __syncthreads();
