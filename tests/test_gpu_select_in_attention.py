@@ -20,11 +20,13 @@ def _dev():
     return torch.device("cuda:0")
 
 
-def _scores(sc):
-    """Indexer scores of every query over its visible entries (no top-k)."""
+def _scores(sc, aligned=False):
+    """Indexer scores of every query over its visible entries (no top-k); rows of nv_cap + 5
+    floats, or of a multiple of 64 floats (16-byte aligned rows) when `aligned`."""
     wl = sc.wl
     nv_cap = (sc.max_pos() + 1) // wl.m
-    scores = torch.full((sc.N, nv_cap + 5), float("nan"), dtype=torch.float32, device=_dev())
+    stride = (nv_cap + 63) // 64 * 64 if aligned else nv_cap + 5
+    scores = torch.full((sc.N, stride), float("nan"), dtype=torch.float32, device=_dev())
     q, qs = U._ix_q_args(sc)
     hcs.index_scores_compress(q, qs, sc.ix_w.contiguous(), sc.ix, sc.q_seq, sc.q_pos, wl.m, sc.max_pos(),
                               scores)
@@ -41,12 +43,12 @@ def _select_attend(sc, scores, sink=None):
     return out, lse, sel
 
 
-def _check(sc, sink=None):
+def _check(sc, sink=None, aligned=False):
     wl = sc.wl
     U.say(f"[case] select-in-attention {wl.name} N={sc.N} topk={wl.topk} seed={sc.seed}")
     state = torch.zeros((len(sc.c_cu) - 1, 3 * wl.d), dtype=torch.float32, device=_dev())
     U.compress_calls(sc, state)
-    scores = _scores(sc)
+    scores = _scores(sc, aligned)
     out, lse, sel = _select_attend(sc, scores, sink=sink)
     # the two-call path on the same caches
     idx = torch.empty((sc.N, wl.topk), dtype=torch.int32, device=_dev())
@@ -85,13 +87,16 @@ def test_select_in_attention_ragged():
     wl = C.CSA_DECODE.with_(B=6, topk=100)
     ctx = [8192, 7001, 4000, 402, 130, 64 * 7 + 3]
     _check(G.build(wl, seed=21, device=_dev(), ctx_per_seq=ctx))
+    _check(G.build(wl, seed=27, device=_dev(), ctx_per_seq=ctx), aligned=True)
 
 
 def test_select_in_attention_csa_decode_full_with_sink():
-    """The CSA decode configuration (32 queries, 2048 visible entries, top-512, five splits)."""
+    """The CSA decode configuration (32 queries, 2048 visible entries, top-512, five splits), with
+    score rows of nv_cap + 5 floats and of a multiple of 64 floats."""
     sc = G.build(C.CSA_DECODE, seed=22, device=_dev())
     sink = torch.linspace(-2.0, 3.0, C.CSA_DECODE.H, device=_dev())
     _check(sc, sink=sink)
+    _check(sc, sink=sink, aligned=True)
 
 
 def test_select_in_attention_largest_visible_count():
@@ -114,6 +119,31 @@ def test_select_in_attention_ties_go_to_smaller_ids():
     torch.cuda.synchronize()
     for t in range(2):
         assert np.array_equal(sel[t].cpu().numpy(), np.arange(k))
+
+
+@pytest.mark.parametrize("nv,k", [(2048, 512), (1000, 100)])
+def test_select_in_attention_partial_tie_takes_smaller_ids(nv, k):
+    """Scores given directly: 100 entries at 2, 300 at 0.5 and the rest tied at 1. The top-k is
+    the 100 larger entries and the k - 100 smallest ids of the tie, whose group straddles the
+    k-th key."""
+    wl = C.CSA_DECODE.with_(B=2, topk=k)
+    sc = G.build(wl, seed=26, device=_dev(), ctx_per_seq=[4 * nv, 4 * nv + 3])
+    U.say(f"[case] select-in-attention partial tie nv={nv} k={k}")
+    nv_cap = (sc.max_pos() + 1) // wl.m
+    rng = np.random.default_rng(26)
+    s = np.ones((2, nv_cap + 5), dtype=np.float32)
+    expect = []
+    for t in range(2):
+        up = rng.choice(nv, 100, replace=False)
+        down = rng.choice(np.setdiff1d(np.arange(nv), up), 300, replace=False)
+        s[t, up] = 2.0
+        s[t, down] = 0.5
+        tie = np.setdiff1d(np.arange(nv), np.concatenate([up, down]))
+        expect.append(np.sort(np.concatenate([up, tie[: k - 100]])))
+    _, _, sel = _select_attend(sc, torch.from_numpy(s).to(_dev()))
+    torch.cuda.synchronize()
+    for t in range(2):
+        assert np.array_equal(sel[t].cpu().numpy(), expect[t]), t
 
 
 def test_index_scores_compress_matches_separate_calls():
