@@ -544,6 +544,70 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
   if (a.lse && (threadIdx.x & 63) == 0) a.lse[(int64_t)t * a.H + h] = lse_of(M, L);
 }
 
+// The split merge with one wave per (query, head), for at most four splits: the wave loads every
+// split of its head at once (all loads issued before any is used), merges them and writes the
+// head's output; four heads per workgroup, no LDS and no barrier. (Measured at HCA decode, four
+// splits: merge 0.6 us faster than mla_combine_kernel; at five splits and more the four-wave
+// merge is faster.)
+template <int D, int U>
+__global__ __launch_bounds__(256) void mla_combine_wave_kernel(AttnArgs a) {
+  constexpr int PER = D / 64;
+  const int t = blockIdx.x, h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (h >= a.H) return;
+  const int c0 = (threadIdx.x & 63) * PER;
+  const int64_t pbase = ((int64_t)(t * a.n_h16 + h / 16) * a.nsplit) * 16 + (h & 15);  // split 0
+  const int ns = a.nsplit;
+  float acc[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) acc[c] = 0.f;
+  float Ms = kNegInf, Ls = 0.f;
+  for (int j0 = 0; j0 < ns; j0 += U) {
+    float ms[U], ls[U];
+    uint32_t v[U][PER / 2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sp = min(j0 + u, ns - 1);
+      const int64_t pr = pbase + (int64_t)sp * 16;
+      ms[u] = a.ws_ml[pr * 2];
+      ls[u] = a.ws_ml[pr * 2 + 1];
+      const uint16_t* src = a.ws_o + pr * D + c0;
+      if constexpr (PER == 8) {
+        const i32x4 w = *(const i32x4*)src;
+        v[u][0] = w.x; v[u][1] = w.y; v[u][2] = w.z; v[u][3] = w.w;
+      } else {
+        v[u][0] = *(const uint32_t*)src;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) ls[u] = j0 + u < ns ? ls[u] : 0.f;
+    float mb = Ms;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mb = ls[u] > 0.f ? fmaxf(mb, ms[u]) : mb;
+    if (mb == kNegInf) continue;
+    const float r = Ms == kNegInf ? 0.f : __builtin_amdgcn_exp2f(Ms - mb);
+    Ls *= r;
+#pragma unroll
+    for (int c = 0; c < PER; ++c) acc[c] *= r;
+    Ms = mb;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = ls[u] > 0.f ? ls[u] * __builtin_amdgcn_exp2f(ms[u] - Ms) : 0.f;
+      Ls += f;
+#pragma unroll
+      for (int c = 0; c < PER / 2; ++c) {
+        acc[2 * c] += f * __uint_as_float(v[u][c] << 16);
+        acc[2 * c + 1] += f * __uint_as_float(v[u][c] & 0xffff0000u);
+      }
+    }
+  }
+  const float f = finish_head(a, h, Ms, Ls);
+  const float inv = Ls > 0.f ? f / Ls : 0.f;
+  uint16_t* orow = a.out + ((int64_t)t * a.H + h) * D + c0;
+#pragma unroll
+  for (int c = 0; c < PER; c += 2) *(uint32_t*)(orow + c) = pack_bf16x2(acc[c] * inv, acc[c + 1] * inv);
+  if (a.lse && (threadIdx.x & 63) == 0) a.lse[(int64_t)t * a.H + h] = lse_of(Ms, Ls);
+}
+
 // ================================================================ all-heads kernel (bf16)
 // A block is (query, split of its rows, 64 heads), so every gathered row is read once for all
 // heads of the query. Rows go from the paged cache straight into a ring of four 32-row LDS
@@ -1081,7 +1145,9 @@ hipError_t launch_impl(const AttnArgs& a, hipStream_t stream) {
   }
   if (a.nsplit > 1) {
     const dim3 cg(a.N, a.H);
-    if (a.nsplit <= 8) hipLaunchKernelGGL((mla_combine_kernel<D, 2>), cg, dim3(kThreads), 0, stream, a);
+    if (a.nsplit <= 4)
+      hipLaunchKernelGGL((mla_combine_wave_kernel<D, 4>), dim3(a.N, (a.H + 3) / 4), dim3(256), 0, stream, a);
+    else if (a.nsplit <= 8) hipLaunchKernelGGL((mla_combine_kernel<D, 2>), cg, dim3(kThreads), 0, stream, a);
     else if (a.nsplit <= 16) hipLaunchKernelGGL((mla_combine_kernel<D, 4>), cg, dim3(kThreads), 0, stream, a);
     else hipLaunchKernelGGL((mla_combine_kernel<D, 8>), cg, dim3(kThreads), 0, stream, a);
   }

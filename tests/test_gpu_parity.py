@@ -93,6 +93,22 @@ def test_hca_decode_full():
     _check_step(sc)
 
 
+def test_hca_three_splits_36_heads_with_sink():
+    """96 queries give three splits per query, merged by one wave per head (four heads per
+    workgroup, 36 heads: the last workgroup half empty), with a sink; a ragged batch in which some
+    queries have no rows in the later splits."""
+    wl = C.HCA_DECODE.with_(B=96, H=36)
+    rng = np.random.default_rng(34)
+    ctx = [131072] + [int(x) for x in rng.integers(1, 131072, size=95)]
+    ctx[1:6] = [1, 127, 128, 129, 4096]
+    sc = G.build(wl, seed=34, device=_dev(), ctx_per_seq=ctx)
+    # three splits: the partials' workspace is N x ceil(H/16) x nsplit x 16 rows of d bf16 + 2 floats
+    ws = hcs.sparse_mla_workspace_size(sc.N, wl.H, wl.d, wl.window, wl.m, 0, sc.max_pos())
+    assert ws == sc.N * ((wl.H + 15) // 16) * 3 * 16 * (2 * wl.d + 8), ws
+    sink = torch.linspace(-1.0, 2.0, wl.H, device=_dev())
+    _check_step(sc, sink=sink)
+
+
 def test_hca_ratio_one_no_window_is_causal_attention():
     """HCA with m=1, window 0 and no top-k is full causal attention (spec invariant)."""
     wl = C.Workload(name="hca_m1", kind="tiny", B=1, ctx=300, H=64, d=512, d_rope=64, m=1, window=0,
