@@ -259,6 +259,16 @@ def test_csa_decode_large_selection_ragged():
     _check_step(sc)
 
 
+def test_csa_decode_one_stage_select_up_to_32768():
+    """bf16 keys with at most 32768 visible entries take the one-stage select (no filter): keys in
+    registers strided over 1024 threads, 16, 24 or 32 per thread (30000, 20000 and 9000 visible
+    entries) and contiguous for up to 8192 (5000), top-2048."""
+    wl = C.CSA_DECODE.with_(B=4, topk=2048)
+    ctx = [4 * 30000, 4 * 20000 + 1, 4 * 9000 + 2, 4 * 5000 + 3]
+    sc = G.build(wl, seed=35, device=_dev(), ctx_per_seq=ctx)
+    _check_step(sc)
+
+
 def _tie_case(nv: int, k: int, seed: int):
     """Every indexer key equal, so every score ties: the selection must be the k smallest ids."""
     wl = C.CSA_DECODE.with_(B=2, topk=k)
