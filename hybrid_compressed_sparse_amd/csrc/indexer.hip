@@ -449,21 +449,42 @@ __global__ __launch_bounds__(kChunkThreads, 512 / kChunkThreads) void index_scor
 #pragma unroll
         for (int i = 0; i < 4; ++i) wreg[mt][i] = w4[i];
       }
+      // Software-pipelined over the wave's four entry tiles: tile nt's 16 MFMAs are issued among
+      // tile nt-1's ReLU, weight and cross-lane reduction (scheduling groups of one MFMA and two
+      // VALU instructions), so the VALU work runs in the MFMAs' shadow instead of after them.
+      // Each accumulator still sums its k-steps in order: the same bits as before.
+      f32x4 acc[2][MT];
+      auto mfma_tile = [&](int nt, f32x4 (&ac)[MT]) {
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
+        for (int mt = 0; mt < MT; ++mt) ac[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            ac[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kreg[nt][ks], ac[mt], 0, 0, 0);
+      };
+      auto reduce_tile = [&](const f32x4 (&ac)[MT]) {
         float part = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kreg[nt][ks], acc, 0, 0, 0);
+          for (int i = 0; i < 4; ++i) part += wreg[mt][i] * relu(ac[mt][i]);
+        return sum_xor16_32(part);
+      };
+      mfma_tile(0, acc[0]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) part += wreg[mt][i] * relu(acc[i]);
+      for (int nt = 1; nt < NTW; ++nt) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_tile(nt, acc[nt & 1]);
+        sc[u][nt - 1] = reduce_tile(acc[(nt - 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < MT * KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
-        part = sum_xor16_32(part);
-        sc[u][nt] = part;
+        __builtin_amdgcn_sched_barrier(0);
       }
+      sc[u][NTW - 1] = reduce_tile(acc[(NTW - 1) & 1]);
     }
     t_prev = t;
   }
