@@ -259,28 +259,53 @@ __device__ __forceinline__ void score_block_bf16(const IndexArgs& a, uint8_t* sm
     for (int kk = 0; kk < KS; ++kk)
       qreg[mt][kk] = *(const bf16x8*)(qs + h * RB + (((4 * kk + g) ^ (h & (CPR - 1))) << 4));
   }
+  bf16x8 kreg[NT][KS];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = nt * 16 + l16;
-    bf16x8 kreg[KS];
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) kreg[kk] = *(const bf16x8*)(kl + r * RB + (((4 * kk + g) ^ (r & (CPR - 1))) << 4));
+    for (int kk = 0; kk < KS; ++kk) {
+      const int r = nt * 16 + l16;
+      kreg[nt][kk] = *(const bf16x8*)(kl + r * RB + (((4 * kk + g) ^ (r & (CPR - 1))) << 4));
+    }
+  // Software-pipelined over the wave's entry tiles: tile nt's MFMAs are issued among tile nt-1's
+  // ReLU, weighting and cross-lane sum (groups of one MFMA and two VALU instructions). Every
+  // accumulator and partial sum keeps its order, so the bits do not depend on the interleave.
+  f32x4 acc[2][MT];
+  auto mfma_tile = [&](int nt, f32x4 (&ac)[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) ac[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        ac[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qreg[mt][kk], kreg[nt][kk], ac[mt], 0, 0, 0);
+  };
+  auto finish_tile = [&](int nt, const f32x4 (&ac)[MT]) {
     float part = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qreg[mt][kk], kreg[kk], acc, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part += wreg[mt][i] * relu(acc[i]);
-    }
+      for (int i = 0; i < 4; ++i) part += wreg[mt][i] * relu(ac[mt][i]);
     part = sum_xor16_32(part);
-    const int e = e_base + r;
+    const int e = e_base + nt * 16 + l16;
     const float sv = pg >= 0 ? part : kNegInf;
     if (g == 0 && e < nv) a.scores[(int64_t)t * a.score_stride + e] = sv;
     tkeys[nt] = g == 0 && e < nv ? f32_order_key(sv) : 0u;
+  };
+  mfma_tile(0, acc[0]);
+#pragma unroll
+  for (int nt = 1; nt < NT; ++nt) {
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_tile(nt, acc[nt & 1]);
+    finish_tile(nt - 1, acc[(nt - 1) & 1]);
+#pragma unroll
+    for (int i = 0; i < MT * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
+  finish_tile(NT - 1, acc[(NT - 1) & 1]);
 }
 
 template <int DI, int MT>
