@@ -957,11 +957,11 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
           pmax[wave][16 + l16] = tmax[1];
         }
         if (lane == 0) pseq[wave] = i + 1;
+        // (a tight spin: an s_sleep between the reads made the wake-up later by up to its 64
+        // clocks, 3% of a prefill chunk's attention; the partner is a block phase away at most)
         bool met = false;
-        for (int spin = 0; spin < (1 << 16) && !met; ++spin) {
+        for (int spin = 0; spin < (1 << 16) && !met; ++spin)
           met = __builtin_amdgcn_readfirstlane(((volatile int*)pseq)[partner]) > i;
-          if (!met) __builtin_amdgcn_s_sleep(1);
-        }
         // a wait that ran out goes on with this wave's own maxima (a wrong result, reported)
         if (!met && lane == 0) dev_error(HCS_DEVERR_PAIR_WAIT);
         asm volatile("" ::: "memory");
