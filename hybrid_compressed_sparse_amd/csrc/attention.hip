@@ -627,6 +627,8 @@ constexpr int kHeadsThreads = 512;
 
 // s_waitcnt vmcnt(n) (gfx9 encoding, n < 16): expcnt and lgkmcnt not waited for
 #define HCS_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+// the same for n < 64 (vmcnt bits 5:4 sit at bits 15:14 of the immediate)
+#define HCS_WAIT_VMCNT_WIDE(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
 template <int D, bool SEL, bool PAIR, int SF = HCS_FMT_BF16, int CF = HCS_FMT_BF16>
 __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a) {
@@ -744,6 +746,45 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       }
     }
   };
+  // With head pairs (prefill) and with the selection inside the kernel, the O waves issue all of
+  // a block's copies (rows 8 (w - 4) .. +7 each), so the S waves' critical path has no copies,
+  // table reads or waits for them (the O waves wait at each step's end for the S waves anyway):
+  // prefill attention 1336 -> 1295 us, CSA decode with the selection 0.3 us faster. Plain decode
+  // (HCA, two-call CSA) keeps copies on all eight waves, where this measured slower.
+  constexpr bool OCOPY = PAIR || SEL;
+  constexpr int WRO = BT / 4, NLO = WRO / RPI;
+  struct RowSrcO { const uint8_t* p[NLO]; };
+  auto prep_o = [&](int b) {
+    RowSrcO r;
+    const int ow = wave - 4;
+    const uint32_t* at = rowtab + b * BT + WRO * ow;
+    if constexpr (RPI == 1) {
+      const uint32_t my = at[lane & (WRO - 1)];
+#pragma unroll
+      for (int i = 0; i < NLO; ++i) r.p[i] = row_ptr((uint32_t)__builtin_amdgcn_readlane((int)my, i));
+    } else {
+#pragma unroll
+      for (int i = 0; i < NLO; ++i) {
+        const int rl = i * RPI + lane / LPR;
+        const int sw = swz_dec((WRO * ow + rl) & 15);
+        r.p[i] = row_ptr(at[rl]) + (((lane % LPR) ^ sw) * 16);
+      }
+    }
+    return r;
+  };
+  auto fire_o = [&](int b, const RowSrcO& r) {
+    const int ow = wave - 4;
+    uint8_t* tb = tiles + (b & 3) * TB;
+#pragma unroll
+    for (int i = 0; i < NLO; ++i) {
+      if constexpr (RPI == 1) {
+        const int sw = swz_dec((WRO * ow + i) & 15);
+        dma16(r.p[i], (uint32_t)((lane ^ sw) * 16), lds_addr(tb) + (WRO * ow + i) * RS);
+      } else {
+        dma16v(r.p[i], lds_addr(tb) + (WRO * ow + i * RPI) * RS);
+      }
+    }
+  };
   // Quantized rows: wave w loads rows WRL w .. +WRL-1 of block i+1 into registers (16 bytes and a
   // scale byte per lane, the same load shape for every format) during step i, and writes them
   // dequantised to bf16 into the block's tile, chunk-swizzled as the copies above, at the top of
@@ -775,8 +816,15 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   if constexpr (QR) {
     if (nblk > 0) qload(0);
   } else {
-    if (nblk > 0) fire(0, prep(0));
-    if (nblk > 1) fire(1, prep(1));
+    if constexpr (OCOPY) {
+      if (wave >= 4) {
+        if (nblk > 0) fire_o(0, prep_o(0));
+        if (nblk > 1) fire_o(1, prep_o(1));
+      }
+    } else {
+      if (nblk > 0) fire(0, prep(0));
+      if (nblk > 1) fire(1, prep(1));
+    }
   }
   // top of block step i: this wave's copies of block i have landed (those of block i+1 may
   // still be in flight), then the barrier makes every wave's copies and the previous step's
@@ -789,28 +837,51 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       }
       lds_barrier();
     } else if constexpr (PAIR) {
-      RowSrc r{};
-      if (i + 2 < nblk) r = prep(i + 2);
-      if (i + 1 < nblk) HCS_WAIT_VMCNT(NLD);
-      else wait_vm_zero();
-      lds_barrier();
-      if (i + 2 < nblk) fire(i + 2, r);
+      if (wave >= 4) {
+        RowSrcO r{};
+        if (i + 2 < nblk) r = prep_o(i + 2);
+        if (i + 1 < nblk) HCS_WAIT_VMCNT(NLO);
+        else wait_vm_zero();
+        lds_barrier();
+        if (i + 2 < nblk) fire_o(i + 2, r);
+      } else {
+        lds_barrier();
+      }
     } else {
       // decode (a few blocks per workgroup): step 0 also issues block 3, the S waves having read
       // q out of tiles 2-3 before its barrier (in the long prefill loop these branches cost more
       // than the earlier copy gains)
-      RowSrc r{}, r3{};
-      if (i + 2 < nblk) r = prep(i + 2);
-      if (i == 0 && nblk > 3) r3 = prep(3);
-      if (i + 1 < nblk) {
-        if (i == 1 && nblk > 3) HCS_WAIT_VMCNT(2 * NLD);   // blocks 2 and 3 may be in flight
-        else HCS_WAIT_VMCNT(NLD);
+      if constexpr (OCOPY) {
+        if (wave >= 4) {
+          RowSrcO r{}, r3{};
+          if (i + 2 < nblk) r = prep_o(i + 2);
+          if (i == 0 && nblk > 3) r3 = prep_o(3);
+          if (i + 1 < nblk) {
+            if (i == 1 && nblk > 3) HCS_WAIT_VMCNT_WIDE(2 * NLO);   // blocks 2 and 3 may be in flight
+            else HCS_WAIT_VMCNT(NLO);
+          } else {
+            wait_vm_zero();
+          }
+          lds_barrier();
+          if (i + 2 < nblk && i != 1) fire_o(i + 2, r);
+          if (i == 0 && nblk > 3) fire_o(3, r3);
+        } else {
+          lds_barrier();
+        }
       } else {
-        wait_vm_zero();
+        RowSrc r{}, r3{};
+        if (i + 2 < nblk) r = prep(i + 2);
+        if (i == 0 && nblk > 3) r3 = prep(3);
+        if (i + 1 < nblk) {
+          if (i == 1 && nblk > 3) HCS_WAIT_VMCNT(2 * NLD);   // blocks 2 and 3 may be in flight
+          else HCS_WAIT_VMCNT(NLD);
+        } else {
+          wait_vm_zero();
+        }
+        lds_barrier();
+        if (i + 2 < nblk && i != 1) fire(i + 2, r);
+        if (i == 0 && nblk > 3) fire(3, r3);
       }
-      lds_barrier();
-      if (i + 2 < nblk && i != 1) fire(i + 2, r);
-      if (i == 0 && nblk > 3) fire(3, r3);
     }
   };
 
