@@ -567,7 +567,6 @@ static hcs_status run_attn(hcs::AttnArgs& a, int d, int fmt, int comp_fmt, int w
   if (plan.ws_bytes && (!ws || ws_bytes < plan.ws_bytes))
     return fail(HCS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.ws_bytes, ws_bytes);
   if (plan.ws_bytes && !aligned(ws, 256)) return fail(HCS_ERR_INVALID_ARG, "ws must be 256-byte aligned");
-  a.kind = plan.kind;
   a.nsplit = plan.nsplit;
   a.n_hg = plan.n_hg;
   a.n_h16 = plan.n_h16;

@@ -1231,13 +1231,11 @@ AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos
   AttnPlan p{};
   const int64_t nv = (int64_t)(max_pos + 1) / m;
   const int64_t rows = (int64_t)std::min(window, max_pos + 1) + (topk > 0 ? topk : nv);
-  // 64 heads per block (all-heads kernel) for every row format
-  p.kind = 2;
-  const int hpb = p.kind == 2 ? 64 : 16;
-  p.n_hg = (H + hpb - 1) / hpb;
+  // 64 heads per kernel block (the all-heads kernel, every row format), 32 rows per row block;
+  // splits are whole row blocks
+  p.n_hg = (H + 63) / 64;
   p.n_h16 = (H + 15) / 16;
-  // rows per block: 64 in the 16-head kernel, 32 in the all-heads kernel; splits are whole blocks
-  const int64_t kBlock = p.kind == 2 ? 32 : 64;
+  const int64_t kBlock = 32;
   const int64_t blocks = std::max<int64_t>(1, (rows + kBlock - 1) / kBlock);
   const int64_t max_bps = kMaxRowsWG / kBlock;
   const int64_t per_split = (int64_t)((N + 7) / 8) * 8 * p.n_hg;

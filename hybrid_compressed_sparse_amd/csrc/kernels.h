@@ -24,7 +24,6 @@ struct AttnArgs {
   int seq_const, p0;
   const float* sink;          // [H] or nullptr
   int N, H, window, m, nv_cap, pos_cap;
-  int kind;                   // 0: 16-head decode kernel (fp8_ds rows), 2: all-heads kernel (bf16)
   int nsplit, n_hg, n_h16, rows_per_split;   // n_hg: head groups of a kernel block
   float scale_log2;           // softmax scale * log2(e)
   uint16_t* out;              // [N, H, D] bf16
@@ -44,7 +43,7 @@ struct AttnArgs {
 constexpr int kSelMax = 8192;
 
 struct AttnPlan {
-  int kind, nsplit, n_hg, n_h16, rows_per_split;
+  int nsplit, n_hg, n_h16, rows_per_split;
   size_t ws_o_bytes, ws_ml_bytes, ws_bytes;
 };
 AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos, int fmt);
