@@ -451,13 +451,11 @@ __device__ __forceinline__ float lse_of(float m, float l) {
   return l > 0.f ? (m + __builtin_log2f(l)) * 0.6931471805599453f : kNegInf;
 }
 
-
-
 // Merge the split partials of one query head: a block is (query, head); its four waves take
 // every fourth split (wave w: splits w, w + 4, ...), each lane D/64 columns, and the waves' merged
-// parts are combined through LDS. A partial row holds that split's output normalised by its own
-// sum (bf16) and ws_ml its (max, sum) in log2 units; the merge weights split s by
-// sum_s * 2^(max_s - max). A wave takes U of its splits at a time (U >= nsplit / 4 when nsplit
+// parts are combined through LDS. A partial row holds that split's sums of p * v with p relative
+// to its own reference max, unnormalised (bf16), and ws_ml its (max, sum of p) in log2 units; the
+// merge weights split s by 2^(max_s - max) and its sum likewise. A wave takes U of its splits at a time (U >= nsplit / 4 when nsplit
 // <= 4 U), every load of a batch issued at a clamped split index before any is used (a load
 // under a condition would be a branch, and each branch a wait for that load alone), merged
 // online: one memory latency per batch.
@@ -505,8 +503,9 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
     Ms = mb;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float f = ls[u] > 0.f ? ls[u] * __builtin_amdgcn_exp2f(ms[u] - Ms) : 0.f;
-      Ls += f;
+      // a split's partial rows are its sums relative to its own max (unnormalised)
+      const float f = ls[u] > 0.f ? __builtin_amdgcn_exp2f(ms[u] - Ms) : 0.f;
+      Ls += f * ls[u];
 #pragma unroll
       for (int c = 0; c < PER / 2; ++c) {
         acc[2 * c] += f * __uint_as_float(v[u][c] << 16);
@@ -591,8 +590,9 @@ __global__ __launch_bounds__(256) void mla_combine_wave_kernel(AttnArgs a) {
     Ms = mb;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float f = ls[u] > 0.f ? ls[u] * __builtin_amdgcn_exp2f(ms[u] - Ms) : 0.f;
-      Ls += f;
+      // a split's partial rows are its sums relative to its own max (unnormalised)
+      const float f = ls[u] > 0.f ? __builtin_amdgcn_exp2f(ms[u] - Ms) : 0.f;
+      Ls += f * ls[u];
 #pragma unroll
       for (int c = 0; c < PER / 2; ++c) {
         acc[2 * c] += f * __uint_as_float(v[u][c] << 16);
@@ -1144,29 +1144,44 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
     // O^T[c = 16 (ow * CTO + ct) + 4g + e][head 16 nt + l16]; in LDS (tiles 0-1, free now), row h
     // holds head h with its 16-byte chunks XOR-swizzled by h mod 16 (conflict-free for both the
     // scattered writes here and the row reads below). Whole rows then go to `out` (normalised,
-    // with the sink) or, when the rows are split, to this split's partial rows (normalised by
-    // this split's own sum; its (max, sum) go to ws_ml for the merge).
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int hh = hbase + 16 * nt + l16;
-      float M = hm[16 * nt + l16], L = hl[0][16 * nt + l16] + hl[1][16 * nt + l16];
-      if (split && g == 0 && ow == 0 && hh < a.H) {
-        const int64_t prow16 = ((int64_t)(t * a.n_h16 + hh / 16) * a.nsplit + s) * 16 + (hh & 15);
-        a.ws_ml[prow16 * 2 + 0] = M;
-        a.ws_ml[prow16 * 2 + 1] = L;
-      }
-      const float f = split ? 1.f : finish_head_s2(sink2[nt], M, L);
-      const float inv = L > 0.f ? f / L : 0.f;
-      if (!split && a.lse && g == 0 && ow == 0 && hh < a.H) a.lse[(int64_t)t * a.H + hh] = lse_of(M, L);
+    // with the sink) or, when the rows are split, to this split's partial rows: its unnormalised
+    // sums relative to its reference max, with that (max, sum) in ws_ml for the merge, so the
+    // staging of a split's rows waits for neither the per-head sums nor a division.
+    auto stage = [&](int nt, float inv, bool scale) {
       uint8_t* hrow = tiles + (16 * nt + l16) * RS;
 #pragma unroll
       for (int ct = 0; ct < CTO; ++ct) {
-        const f32x4 o = oacc[ct][nt] * inv;
+        const f32x4 o = scale ? oacc[ct][nt] * inv : oacc[ct][nt];
         uint2 pk;
         pk.x = pack_bf16x2(o[0], o[1]);
         pk.y = pack_bf16x2(o[2], o[3]);
         const int cb = (16 * (ow * CTO + ct) + 4 * g) * 2;           // byte in the row
         *(uint2*)(hrow + ((((cb >> 4) ^ l16) << 4) | (cb & 15))) = pk;
+      }
+    };
+    if (split) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) stage(nt, 1.f, false);
+      if (ow == 0 && g == 0) {                      // lanes 0-15 of the first O wave
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int hh = hbase + 16 * nt + l16;
+          if (hh < a.H) {
+            const int64_t prow16 = ((int64_t)(t * a.n_h16 + hh / 16) * a.nsplit + s) * 16 + (hh & 15);
+            a.ws_ml[prow16 * 2 + 0] = hm[16 * nt + l16];
+            a.ws_ml[prow16 * 2 + 1] = hl[0][16 * nt + l16] + hl[1][16 * nt + l16];
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int hh = hbase + 16 * nt + l16;
+        float M = hm[16 * nt + l16], L = hl[0][16 * nt + l16] + hl[1][16 * nt + l16];
+        const float f = finish_head_s2(sink2[nt], M, L);
+        const float inv = L > 0.f ? f / L : 0.f;
+        if (a.lse && g == 0 && ow == 0 && hh < a.H) a.lse[(int64_t)t * a.H + hh] = lse_of(M, L);
+        stage(nt, inv, true);
       }
     }
     lds_barrier();                                  // (E2): LDS only, the partials' (max, sum)

@@ -28,8 +28,8 @@ struct AttnArgs {
   float scale_log2;           // softmax scale * log2(e)
   uint16_t* out;              // [N, H, D] bf16
   float* lse;                 // [N, H] or nullptr
-  uint16_t* ws_o;             // [N, n_h16, nsplit, 16, D] bf16 partial outputs, each
-                              // normalised by its split's sum (nsplit > 1)
+  uint16_t* ws_o;             // [N, n_h16, nsplit, 16, D] bf16 partial outputs: each split's
+                              // unnormalised sums relative to its max (nsplit > 1)
   float* ws_ml;               // [N, n_h16, nsplit, 16, 2] partial (max, sum), log2 units
   // rows selected by the kernel itself (topk_idx == nullptr): the top-k of each query's indexer
   // scores [N, score_stride] over its visible entries; the selected ids in ascending order go
