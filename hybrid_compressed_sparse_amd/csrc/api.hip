@@ -550,9 +550,8 @@ static hcs_status check_attn(const void* q, const hcs_paged& swa, const hcs_page
 
 size_t hcs_sparse_mla_workspace_size(int N, int H, int d, int window, int m, int topk, int max_pos) {
   if (N <= 0 || H <= 0 || m < 1 || max_pos < 0 || window < 0) return 0;
-  // the plan depends on the cache format, which is not an argument here: cover both
-  return std::max(hcs::attn_plan(N, H, d, window, m, topk, max_pos, HCS_FMT_BF16).ws_bytes,
-                  hcs::attn_plan(N, H, d, window, m, topk, max_pos, HCS_FMT_FP8DS).ws_bytes);
+  // (the same plan for every cache format)
+  return hcs::attn_plan(N, H, d, window, m, topk, max_pos).ws_bytes;
 }
 
 static hcs_status run_attn(hcs::AttnArgs& a, int d, int fmt, int comp_fmt, int window, int m, int topk,
@@ -563,7 +562,7 @@ static hcs_status run_attn(hcs::AttnArgs& a, int d, int fmt, int comp_fmt, int w
   if ((int64_t)a.comp.pt_stride * HCS_PAGE_ROWS < (int64_t)(max_pos + 1) / m)
     return fail(HCS_ERR_INVALID_ARG, "comp: pt_stride %d does not cover %d entries", a.comp.pt_stride,
                 (max_pos + 1) / m);
-  const hcs::AttnPlan plan = hcs::attn_plan(a.N, a.H, d, window, m, topk, max_pos, fmt);
+  const hcs::AttnPlan plan = hcs::attn_plan(a.N, a.H, d, window, m, topk, max_pos);
   if (plan.ws_bytes && (!ws || ws_bytes < plan.ws_bytes))
     return fail(HCS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.ws_bytes, ws_bytes);
   if (plan.ws_bytes && !aligned(ws, 256)) return fail(HCS_ERR_INVALID_ARG, "ws must be 256-byte aligned");
@@ -694,7 +693,7 @@ hcs_status hcs_sparse_mla_decode_noalloc(const void* q, hcs_paged swa, hcs_paged
   if (s != HCS_OK) return s;
   if (max_pos < 0) return fail(HCS_ERR_INVALID_ARG, "max_pos must be >= 0");
   if (N == 0) return ok();
-  const size_t need = hcs::attn_plan(N, H, d, window, m, topk_idx ? topk : 0, max_pos, swa.fmt).ws_bytes;
+  const size_t need = hcs::attn_plan(N, H, d, window, m, topk_idx ? topk : 0, max_pos).ws_bytes;
   if (need > (size_t)HCS_NOALLOC_SCRATCH_BYTES)
     return fail(HCS_ERR_WORKSPACE_TOO_SMALL, "sparse_mla_decode_noalloc: the call needs %zu bytes of scratch, "
                 "the library's static scratch holds %zu (use hcs_sparse_mla_decode with a workspace)",

@@ -1244,7 +1244,7 @@ hipError_t launch_impl(const AttnArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos, int fmt) {
+AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos) {
   AttnPlan p{};
   const int64_t nv = (int64_t)(max_pos + 1) / m;
   const int64_t rows = (int64_t)std::min(window, max_pos + 1) + (topk > 0 ? topk : nv);
@@ -1256,10 +1256,11 @@ AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos
   const int64_t blocks = std::max<int64_t>(1, (rows + kBlock - 1) / kBlock);
   const int64_t max_bps = kMaxRowsWG / kBlock;
   const int64_t per_split = (int64_t)((N + 7) / 8) * 8 * p.n_hg;
-  // enough splits to give every CU a block, but at least four blocks each (two for quantized
-  // rows, whose blocks cost less to fetch): a split adds 64 KiB of partial stores and merge reads
-  // per query (measured at the decode configurations: 2 .. 6 blocks per split)
-  const int64_t min_bps = fmt == HCS_FMT_BF16 ? 4 : 2;
+  // enough splits to give every CU a block, but at least two blocks each: a split adds 64 KiB of
+  // partial stores and merge reads per query (measured at the decode configurations: CSA seven
+  // splits of three blocks against five of four, 0.4 us faster; at 1M 23 splits of three against
+  // 17 of four, 1.4 us faster)
+  const int64_t min_bps = 2;
   int64_t nsplit = std::max<int64_t>(1, (256 + per_split - 1) / per_split);
   nsplit = std::min(nsplit, std::max<int64_t>(1, blocks / min_bps));
   nsplit = std::max<int64_t>(nsplit, (blocks + max_bps - 1) / max_bps);

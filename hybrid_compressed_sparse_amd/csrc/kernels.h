@@ -46,7 +46,7 @@ struct AttnPlan {
   int nsplit, n_hg, n_h16, rows_per_split;
   size_t ws_o_bytes, ws_ml_bytes, ws_bytes;
 };
-AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos, int fmt);
+AttnPlan attn_plan(int N, int H, int d, int window, int m, int topk, int max_pos);
 bool attn_formats_supported(int d, int swa_fmt, int comp_fmt);
 hipError_t launch_sparse_mla(const AttnArgs& a, int d, int swa_fmt, int comp_fmt, hipStream_t stream);
 
