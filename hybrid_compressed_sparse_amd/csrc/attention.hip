@@ -255,7 +255,9 @@ __device__ __forceinline__ void fill_rows_sel(const AttnArgs& a, int t, int s, c
       } else {
         const uint32_t id = rowtab[li];
         if (id != kNoRow) {
-          const int pg = cached ? ptl[id >> 6] : __ldg(cpt + (id >> 6));
+          // (nv <= kSelMax: the page-table row is always in LDS; no flat load)
+          static_assert(kSelMax / 64 <= kPtCache, "the selection's page-table row fits in LDS");
+          const int pg = ptl[id >> 6];
           if (pg >= a.comp.num_pages) dev_error(HCS_DEVERR_PAGE_RANGE);
           if (pg >= 0 && pg < a.comp.num_pages) e = 0x80000000u | (uint32_t)(pg * 64 + (id & 63));
         }
@@ -1030,14 +1032,17 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
         if (lane == 0) pseq[wave] = i + 1;
         // (a tight spin: an s_sleep between the reads made the wake-up later by up to its 64
         // clocks, 3% of a prefill chunk's attention; the partner is a block phase away at most)
+        // (LDS atomic loads: a volatile access through a generic pointer would be a flat load,
+        // whose wait also covers every copy in flight)
         bool met = false;
         for (int spin = 0; spin < (1 << 16) && !met; ++spin)
-          met = __builtin_amdgcn_readfirstlane(((volatile int*)pseq)[partner]) > i;
+          met = __builtin_amdgcn_readfirstlane(
+                    __hip_atomic_load(&pseq[partner], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) > i;
         // a wait that ran out goes on with this wave's own maxima (a wrong result, reported)
         if (!met && lane == 0) dev_error(HCS_DEVERR_PAIR_WAIT);
-        asm volatile("" ::: "memory");
-        tmax[0] = fmaxf(tmax[0], ((volatile float*)pmax[partner])[l16]);
-        tmax[1] = fmaxf(tmax[1], ((volatile float*)pmax[partner])[16 + l16]);
+        tmax[0] = fmaxf(tmax[0], __hip_atomic_load(&pmax[partner][l16], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        tmax[1] = fmaxf(tmax[1], __hip_atomic_load(&pmax[partner][16 + l16], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           // the same decision in both waves of the pair (same maxima, same history)

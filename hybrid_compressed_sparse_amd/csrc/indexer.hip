@@ -919,10 +919,15 @@ __global__ __launch_bounds__(kScoreThreads) void topk_filter_kernel(IndexArgs a,
   uint32_t key[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) key[j] = __float_as_uint(sc[min(lo + j * kScoreThreads + (int)threadIdx.x, cap)]);
-  uint32_t* ck = ckey + (int64_t)t * cstride + lo;   // slots < hi - lo: inside the query's range
-  int32_t* ci = cid + (int64_t)t * cstride + lo;
-  unsigned* cnt_out = ccount + (int64_t)t * ccs + blockIdx.y;
-  asm volatile("" : "+s"(ck), "+s"(ci), "+s"(cnt_out));
+  uint32_t* ck0 = ckey + (int64_t)t * cstride + lo;   // slots < hi - lo: inside the query's range
+  int32_t* ci0 = cid + (int64_t)t * cstride + lo;
+  unsigned* cnt0 = ccount + (int64_t)t * ccs + blockIdx.y;
+  asm volatile("" : "+s"(ck0), "+s"(ci0), "+s"(cnt0));
+  // global pointers again (through the asm the compiler no longer knows the address space, and
+  // a generic store is a flat store, whose waits also cover LDS operations)
+  auto* ck = (__attribute__((address_space(1))) uint32_t*)ck0;
+  auto* ci = (__attribute__((address_space(1))) int32_t*)ci0;
+  auto* cnt_out = (__attribute__((address_space(1))) unsigned*)cnt0;
   int seq, nv;
   query_of(a, t, seq, nv);
   if (nv <= a.topk || lo >= nv) return;              // short context: the select fills it directly
