@@ -1217,24 +1217,20 @@ template <int D, int SF, int CF>
 hipError_t launch_impl(const AttnArgs& a, hipStream_t stream) {
   const int n8 = (a.N + 7) / 8;
   dim3 grid((unsigned)(n8 * 8 * a.nsplit * a.n_hg));
+  // The S waves work in head pairs everywhere (half the K reads from LDS for a per-block exchange
+  // of maxima; at decode, once the S waves issued no row copies and the wait became a plain LDS
+  // read, it paid there too: HCA step 34.8 -> 33.5 us).
   if constexpr (SF == HCS_FMT_BF16) {
-    if (!a.q_seq) {
-      // a prefill chunk: many row blocks per workgroup, where the S waves' head pairs (half the
-      // K reads from LDS) pay for their per-block handshake
+    if (!a.scores) {
       hipLaunchKernelGGL((mla_heads_kernel<D, false, true>), grid, dim3(kHeadsThreads), 0, stream, a);
-    } else if (!a.scores) {
-      hipLaunchKernelGGL((mla_heads_kernel<D, false, false>), grid, dim3(kHeadsThreads), 0, stream, a);
     } else if constexpr (D == 512) {
-      hipLaunchKernelGGL((mla_heads_kernel<D, true, false>), grid, dim3(kHeadsThreads), 0, stream, a);
+      hipLaunchKernelGGL((mla_heads_kernel<D, true, true>), grid, dim3(kHeadsThreads), 0, stream, a);
     } else {
       return hipErrorInvalidValue;
     }
   } else {
     static_assert(D == QuantStage<SF, CF>::D, "quantized rows are 512 wide");
-    if (!a.q_seq)
-      hipLaunchKernelGGL((mla_heads_kernel<D, false, true, SF, CF>), grid, dim3(kHeadsThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((mla_heads_kernel<D, false, false, SF, CF>), grid, dim3(kHeadsThreads), 0, stream, a);
+    hipLaunchKernelGGL((mla_heads_kernel<D, false, true, SF, CF>), grid, dim3(kHeadsThreads), 0, stream, a);
   }
   if (a.nsplit > 1) {
     const dim3 cg(a.N, a.H);
