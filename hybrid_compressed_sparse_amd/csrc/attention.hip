@@ -617,11 +617,12 @@ __global__ __launch_bounds__(256) void mla_combine_wave_kernel(AttnArgs a) {
 // addresses), from a table of row byte addresses built once per block.
 // The eight waves have two roles, one of each per SIMD, and work on consecutive row blocks at
 // the same time, so that one role's MFMAs cover the other's LDS waits:
-//   S waves (0..3): wave w holds q of heads 16w .. 16w+15 in registers and computes S^T for all
-//     32 rows of block i, its online softmax (each wave owns whole heads, so no cross-wave
-//     max), and writes P^T (bf16) and any rescale factors to LDS;
+//   S waves (0..3), in head pairs: wave w holds q of heads 32 (w >> 1) .. +31 in registers and
+//     computes S^T for rows 16 (w & 1) .. +15 of block i (each K fragment read from LDS feeds two
+//     MFMAs), agrees on the block's per-head maxima with its partner, runs the online softmax
+//     and writes P^T (bf16) and any rescale factors to LDS;
 //   O waves (4..7): wave 4+c accumulates O^T for output columns D/4 * c .. +D/4 of all 64
-//     heads over block i-1, from that block's tile and P^T.
+//     heads over block i-1, from that block's tile and P^T, and issues the row copies.
 // While block i is scored and block i-1 accumulated, the rows of blocks i+1 and i+2 are in
 // flight into the other two tiles. Each role runs its own loop (so q and the O accumulators are
 // never live in the same wave) and both pass one barrier per block.
@@ -629,10 +630,8 @@ constexpr int kHeadsThreads = 512;
 
 // s_waitcnt vmcnt(n) (gfx9 encoding, n < 16): expcnt and lgkmcnt not waited for
 #define HCS_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
-// the same for n < 64 (vmcnt bits 5:4 sit at bits 15:14 of the immediate)
-#define HCS_WAIT_VMCNT_WIDE(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
-template <int D, bool SEL, bool PAIR, int SF = HCS_FMT_BF16, int CF = HCS_FMT_BF16>
+template <int D, bool SEL, int SF = HCS_FMT_BF16, int CF = HCS_FMT_BF16>
 __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a) {
   constexpr bool QR = SF != HCS_FMT_BF16;         // quantized rows, dequantised through registers
   static_assert(!QR || (D == 512 && !SEL), "quantized rows are 512 wide, bf16 selection only");
@@ -643,10 +642,11 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   constexpr int PR = BT + 8;                      // P row stride (elements), padded
   constexpr int RPI = 1024 / RS;                  // rows per 1 KiB async load
   constexpr int LPR = 64 / RPI;                   // lanes per row in an async load
-  constexpr int WRL = BT / 8;                     // rows each wave loads per block
-  constexpr int NLD = WRL / RPI;                  // async loads per wave per block
+  constexpr int WRL = BT / 8;                     // quantized rows each wave stages per block
+  constexpr int WRO = BT / 4;                     // rows each O wave copies per block
+  constexpr int NLO = WRO / RPI;                  // async loads per O wave per block
   constexpr int PD = 4;                           // K-fragment steps read ahead in S^T
-  static_assert(CTO >= 1 && NLD >= 1 && NLD < 16 && KS % PD == 0, "unsupported head dim");
+  static_assert(CTO >= 1 && NLO >= 1 && NLO < 16 && KS % PD == 0, "unsupported head dim");
   static_assert(!SEL || 2 * TB >= kSelScratch, "the row selection's scratch lives in tiles 0-1");
   // Tiles in the ring: bf16 rows are copied two blocks ahead (four tiles: S on block i, O on
   // block i-1, copies of i+1 and i+2 in flight); quantized rows are staged one block ahead in
@@ -707,7 +707,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   else fill_rows<kHeadsThreads, PTC>(a, t, q, r0, n_rows, rowtab, ptl, BT);
   const int nblk = (n_rows + BT - 1) / BT;
 
-  // async loads: wave w fills rows WRL w .. +WRL-1 of a block; LDS chunk slot c of row r
+  // async loads: O wave 4 + ow fills rows WRO ow .. +WRO-1 of a block; LDS chunk slot c of row r
   // receives source chunk c ^ swz_dec(r mod 16)
   auto row_ptr = [&](uint32_t e) {
     return e != kNoRow ? ((e >> 31) ? a.comp.base : a.swa.base) + (size_t)(e & 0x7fffffffu) * RS
@@ -716,45 +716,10 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   // A block's copies in two halves: the source addresses come from the row table (fixed after
   // the prologue), so they are read before a step's waits; the copies themselves are issued
   // after its barrier, once their tile is free. RPI == 1: one row per copy, the address
-  // wave-uniform; otherwise each lane has its own row's address.
-  struct RowSrc { const uint8_t* p[NLD]; };
-  auto prep = [&](int b) {
-    RowSrc r;
-    const uint32_t* at = rowtab + b * BT + WRL * wave;
-    if constexpr (RPI == 1) {
-      // lane j < WRL reads the entry of row j; each copy takes it from that lane
-      const uint32_t my = at[lane & (WRL - 1)];
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) r.p[i] = row_ptr((uint32_t)__builtin_amdgcn_readlane((int)my, i));
-    } else {
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int rl = i * RPI + lane / LPR;
-        const int sw = swz_dec((WRL * wave + rl) & 15);
-        r.p[i] = row_ptr(at[rl]) + (((lane % LPR) ^ sw) * 16);
-      }
-    }
-    return r;
-  };
-  auto fire = [&](int b, const RowSrc& r) {
-    uint8_t* tb = tiles + (b & 3) * TB;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      if constexpr (RPI == 1) {
-        const int sw = swz_dec((WRL * wave + i) & 15);
-        dma16(r.p[i], (uint32_t)((lane ^ sw) * 16), lds_addr(tb) + (WRL * wave + i) * RS);
-      } else {
-        dma16v(r.p[i], lds_addr(tb) + (WRL * wave + i * RPI) * RS);
-      }
-    }
-  };
-  // With head pairs (prefill) and with the selection inside the kernel, the O waves issue all of
-  // a block's copies (rows 8 (w - 4) .. +7 each), so the S waves' critical path has no copies,
-  // table reads or waits for them (the O waves wait at each step's end for the S waves anyway):
-  // prefill attention 1336 -> 1295 us, CSA decode with the selection 0.3 us faster. Plain decode
-  // (HCA, two-call CSA) keeps copies on all eight waves, where this measured slower.
-  constexpr bool OCOPY = PAIR || SEL;
-  constexpr int WRO = BT / 4, NLO = WRO / RPI;
+  // wave-uniform; otherwise each lane has its own row's address. The O waves issue them all: they
+  // finish each step early and wait at its barrier, while the S waves' chain (S^T, maxima, pair
+  // wait, probabilities) sets the step time (prefill attention 1336 -> 1295 us against copies on
+  // all eight waves).
   struct RowSrcO { const uint8_t* p[NLO]; };
   auto prep_o = [&](int b) {
     RowSrcO r;
@@ -818,19 +783,14 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
   if constexpr (QR) {
     if (nblk > 0) qload(0);
   } else {
-    if constexpr (OCOPY) {
-      if (wave >= 4) {
-        if (nblk > 0) fire_o(0, prep_o(0));
-        if (nblk > 1) fire_o(1, prep_o(1));
-      }
-    } else {
-      if (nblk > 0) fire(0, prep(0));
-      if (nblk > 1) fire(1, prep(1));
+    if (wave >= 4) {
+      if (nblk > 0) fire_o(0, prep_o(0));
+      if (nblk > 1) fire_o(1, prep_o(1));
     }
   }
-  // top of block step i: this wave's copies of block i have landed (those of block i+1 may
-  // still be in flight), then the barrier makes every wave's copies and the previous step's
-  // LDS writes visible, and block i+2's copies go into the tile that block i-2 left
+  // top of block step i: the O waves' copies of block i have landed (those of block i+1 may
+  // still be in flight), then the barrier makes them and the previous step's LDS writes
+  // visible, and block i+2's copies go into the tile that block i-2 left
   auto step_sync = [&](int i) {
     if constexpr (QR) {
       if (i < nblk) {
@@ -838,7 +798,7 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
         if (i + 1 < nblk) qload(i + 1);
       }
       lds_barrier();
-    } else if constexpr (PAIR) {
+    } else {
       if (wave >= 4) {
         RowSrcO r{};
         if (i + 2 < nblk) r = prep_o(i + 2);
@@ -849,128 +809,13 @@ __global__ __launch_bounds__(kHeadsThreads, 1) void mla_heads_kernel(AttnArgs a)
       } else {
         lds_barrier();
       }
-    } else {
-      // decode (a few blocks per workgroup): step 0 also issues block 3, the S waves having read
-      // q out of tiles 2-3 before its barrier (in the long prefill loop these branches cost more
-      // than the earlier copy gains)
-      if constexpr (OCOPY) {
-        if (wave >= 4) {
-          RowSrcO r{}, r3{};
-          if (i + 2 < nblk) r = prep_o(i + 2);
-          if (i == 0 && nblk > 3) r3 = prep_o(3);
-          if (i + 1 < nblk) {
-            if (i == 1 && nblk > 3) HCS_WAIT_VMCNT_WIDE(2 * NLO);   // blocks 2 and 3 may be in flight
-            else HCS_WAIT_VMCNT(NLO);
-          } else {
-            wait_vm_zero();
-          }
-          lds_barrier();
-          if (i + 2 < nblk && i != 1) fire_o(i + 2, r);
-          if (i == 0 && nblk > 3) fire_o(3, r3);
-        } else {
-          lds_barrier();
-        }
-      } else {
-        RowSrc r{}, r3{};
-        if (i + 2 < nblk) r = prep(i + 2);
-        if (i == 0 && nblk > 3) r3 = prep(3);
-        if (i + 1 < nblk) {
-          if (i == 1 && nblk > 3) HCS_WAIT_VMCNT(2 * NLD);   // blocks 2 and 3 may be in flight
-          else HCS_WAIT_VMCNT(NLD);
-        } else {
-          wait_vm_zero();
-        }
-        lds_barrier();
-        if (i + 2 < nblk && i != 1) fire(i + 2, r);
-        if (i == 0 && nblk > 3) fire(3, r3);
-      }
     }
   };
 
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   const bool split = a.nsplit > 1;
   if (wave < 4) {
-    if constexpr (!PAIR) {
-      // ================= S waves: heads hbase + 16 wave + l16
-      bf16x8 qreg[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qreg[ks] = *(const bf16x8*)(qstage + (16 * wave + l16) * RS + (((4 * ks + g) ^ l16) << 4));
-      // K row 16 mt + l16, chunk (4ks + g) ^ s = 4 (ks ^ (s >> 2)) + ((g ^ s) & 3), s = swz_dec(l16)
-      const int sk = swz_dec(l16);
-      int ko4[4];
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) ko4[k4] = l16 * RS + ((g ^ sk) & 3) * 16 + 64 * (k4 ^ (sk >> 2));
-      float m_ref = kNegInf, l_part = 0.f;
-      for (int i = 0; i <= nblk; ++i) {
-        step_sync(i);
-        if (i == nblk) break;
-        const uint8_t* T = tiles + (i % NTL) * TB;
-        const int pb = i & 1;
-        const uint32_t valid = (uint32_t)__ballot(rowtab[i * BT + (lane & 31)] != kNoRow);
-        // ---- S^T[32 rows][16 heads], K fragments read PD k-steps ahead of their MFMAs
-        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        bf16x8 kf[PD][2];
-        auto kload = [&](int ks, bf16x8* f) {
-          const int ko = ko4[ks & 3] + (ks >> 2) * 256;
-          f[0] = *(const bf16x8*)(T + ko);
-          f[1] = *(const bf16x8*)(T + ko + 16 * RS);
-        };
-#pragma unroll
-        for (int ks = 0; ks < PD; ++ks) kload(ks, kf[ks]);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % PD][mt], qreg[ks], sacc[mt], 0, 0, 0);
-          if (ks + PD < KS) kload(ks + PD, kf[ks % PD]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // ---- online softmax over the block's rows (this wave owns its heads' rows)
-        float x[2][4];
-        float tmax = kNegInf;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = mt * 16 + 4 * g + e;
-            x[mt][e] = ((valid >> row) & 1u) ? sacc[mt][e] * a.scale_log2 : kNegInf;
-            tmax = fmaxf(tmax, x[mt][e]);
-          }
-        tmax = max_xor16_32(tmax);
-        const bool any_over = __any(tmax > m_ref + kLazyBlock);
-        if (any_over) {
-          // rare: new reference maxima for this wave's heads
-          const float mnew = tmax > m_ref + kLazy ? tmax : m_ref;
-          // 0 when m_ref = -inf; 1 for a head with no row yet (-inf - -inf would be NaN)
-          const float alpha = mnew == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_ref - mnew);
-          l_part *= alpha;
-          m_ref = mnew;
-          if (g == 0) alpha_lds[pb][16 * wave + l16] = alpha;
-        }
-        if (lane == 0) flags[pb][wave] = any_over ? 1 : 0;
-        const float mr = m_ref == kNegInf ? 0.f : m_ref;
-        __bf16* prow = p_lds[pb] + (16 * wave + l16) * PR + 4 * g;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          bf16x4 p4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float pv = __builtin_amdgcn_exp2f(x[mt][e] - mr);
-            l_part += pv;
-            p4[e] = (__bf16)pv;
-          }
-          *(bf16x4*)(prow + mt * 16) = p4;
-        }
-      }
-      const float lt = sum_xor16_32(l_part);
-      if (g == 0) {
-        hl[0][16 * wave + l16] = lt;
-        hl[1][16 * wave + l16] = 0.f;
-        hm[16 * wave + l16] = m_ref;
-      }
-    } else {
+    {
       // ================= S waves: wave w takes heads hbase + 32 (w >> 1) + 16 nt + l16 (nt = 0, 1)
       // over rows 16 (w & 1) .. +15 of each block, so each K fragment read from LDS feeds two
       // MFMAs. The two waves of a head pair agree on each block's max per head before either
@@ -1217,20 +1062,20 @@ template <int D, int SF, int CF>
 hipError_t launch_impl(const AttnArgs& a, hipStream_t stream) {
   const int n8 = (a.N + 7) / 8;
   dim3 grid((unsigned)(n8 * 8 * a.nsplit * a.n_hg));
-  // The S waves work in head pairs everywhere (half the K reads from LDS for a per-block exchange
-  // of maxima; at decode, once the S waves issued no row copies and the wait became a plain LDS
-  // read, it paid there too: HCA step 34.8 -> 33.5 us).
+  // (The S waves work in head pairs at decode too: once they issued no row copies and their wait
+  // became a plain LDS read, half the K reads from LDS paid for the per-block exchange of
+  // maxima there as well: HCA step 34.8 -> 33.5 us.)
   if constexpr (SF == HCS_FMT_BF16) {
     if (!a.scores) {
-      hipLaunchKernelGGL((mla_heads_kernel<D, false, true>), grid, dim3(kHeadsThreads), 0, stream, a);
+      hipLaunchKernelGGL((mla_heads_kernel<D, false>), grid, dim3(kHeadsThreads), 0, stream, a);
     } else if constexpr (D == 512) {
-      hipLaunchKernelGGL((mla_heads_kernel<D, true, true>), grid, dim3(kHeadsThreads), 0, stream, a);
+      hipLaunchKernelGGL((mla_heads_kernel<D, true>), grid, dim3(kHeadsThreads), 0, stream, a);
     } else {
       return hipErrorInvalidValue;
     }
   } else {
     static_assert(D == QuantStage<SF, CF>::D, "quantized rows are 512 wide");
-    hipLaunchKernelGGL((mla_heads_kernel<D, false, true, SF, CF>), grid, dim3(kHeadsThreads), 0, stream, a);
+    hipLaunchKernelGGL((mla_heads_kernel<D, false, SF, CF>), grid, dim3(kHeadsThreads), 0, stream, a);
   }
   if (a.nsplit > 1) {
     const dim3 cg(a.N, a.H);
