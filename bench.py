@@ -590,11 +590,14 @@ def measure_prefill(wl, args, sets: int) -> dict:
 # ------------------------------------------------------------------ decode workloads
 
 def attention_kernel_name(wl, fused: bool) -> str:
+    # the split merge is mla_combine_wave_kernel<512, 4> for at most four splits per query,
+    # mla_combine_kernel<512> above that
+    merge = "split merge"
     if fused:
-        return "hcs_sparse_mla_decode_select (mla_heads_kernel<512, select> + mla_combine_kernel<512>)"
+        return f"hcs_sparse_mla_decode_select (mla_heads_kernel<512, select> + {merge})"
     if wl.kv_fmt == "bf16":
-        return "hcs_sparse_mla_decode (mla_heads_kernel<512> + mla_combine_kernel<512>)"
-    return "hcs_sparse_mla_decode (mla_fp8_kernel<QuantStage> + mla_combine_kernel<512>)"
+        return f"hcs_sparse_mla_decode (mla_heads_kernel<512> + {merge})"
+    return f"hcs_sparse_mla_decode (mla_heads_kernel<512, quantized rows> + {merge})"
 
 
 def index_kernel_name(wl, fused: bool) -> str:
