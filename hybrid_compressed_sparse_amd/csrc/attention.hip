@@ -427,19 +427,16 @@ struct QuantStage {
 constexpr float kLazy = 8.f;
 constexpr float kLazyBlock = 32.f;
 
-// Final (m, l) of one head with the optional sink; returns the factor to apply to O.
-__device__ __forceinline__ float finish_head(const AttnArgs& a, int head, float& m, float& l) {
-  if (!a.sink) return 1.f;
-  const float s2 = a.sink[head] * kLog2e;
-  const float mm = fmaxf(m, s2);
-  if (mm == kNegInf) return 1.f;
-  const float f = __builtin_amdgcn_exp2f(m - mm);
-  l = l * f + __builtin_amdgcn_exp2f(s2 - mm);
-  m = mm;
-  return f;
+// A merge's sink logit of head h in log2 units (-inf without sinks), from a load issued
+// whether or not there are sinks (a zero word without), so that it goes out with the partials'
+// loads instead of behind a branch and a wait of its own.
+__device__ __forceinline__ float merge_sink2(const AttnArgs& a, int h) {
+  const float v = *(a.sink ? a.sink + h : reinterpret_cast<const float*>(g_zero_row));
+  return a.sink ? v * kLog2e : kNegInf;
 }
 
-// The same with the sink logit already loaded (in log2 units; -inf when there is none).
+// Final (m, l) of one head with the optional sink, its logit s2 already loaded (in log2 units;
+// -inf when there is none); returns the factor to apply to O.
 __device__ __forceinline__ float finish_head_s2(float s2, float& m, float& l) {
   const float mm = fmaxf(m, s2);
   if (mm == kNegInf || s2 == kNegInf) return 1.f;
@@ -468,6 +465,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
   __shared__ float wpart[NW][D];
   __shared__ float wml[NW][2];
   const int t = blockIdx.x, h = blockIdx.y, wave = threadIdx.x >> 6;
+  const float sink2 = merge_sink2(a, h);
   const int c0 = (threadIdx.x & 63) * PER;
   const int64_t pbase = ((int64_t)(t * a.n_h16 + h / 16) * a.nsplit) * 16 + (h & 15);  // split 0
   const int ns = a.nsplit, mine = (ns - wave + NW - 1) / NW;   // splits wave, wave + NW, ...
@@ -497,8 +495,9 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
     float mb = Ms;
 #pragma unroll
     for (int u = 0; u < U; ++u) mb = ls[u] > 0.f ? fmaxf(mb, ms[u]) : mb;
-    if (mb == kNegInf) continue;                    // nothing in these splits (nor before)
-    const float r = Ms == kNegInf ? 0.f : __builtin_amdgcn_exp2f(Ms - mb);
+    // (no early exit when mb = -inf: everything below then multiplies by 0, and a branch here let
+    // the compiler move the row loads behind the wait for the (max, sum) loads)
+    const float r = Ms == kNegInf || mb == kNegInf ? 0.f : __builtin_amdgcn_exp2f(Ms - mb);
     Ls *= r;
 #pragma unroll
     for (int c = 0; c < PER; ++c) acc[c] *= r;
@@ -537,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < PER; ++c) o[c] += f * wpart[w][c0 + c];
   }
-  const float f = finish_head(a, h, M, L);
+  const float f = finish_head_s2(sink2, M, L);
   const float inv = L > 0.f ? f / L : 0.f;
   uint16_t* orow = a.out + ((int64_t)t * a.H + h) * D + c0;
 #pragma unroll
@@ -555,6 +554,7 @@ __global__ __launch_bounds__(256) void mla_combine_wave_kernel(AttnArgs a) {
   constexpr int PER = D / 64;
   const int t = blockIdx.x, h = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (h >= a.H) return;
+  const float sink2 = merge_sink2(a, h);
   const int c0 = (threadIdx.x & 63) * PER;
   const int64_t pbase = ((int64_t)(t * a.n_h16 + h / 16) * a.nsplit) * 16 + (h & 15);  // split 0
   const int ns = a.nsplit;
@@ -584,8 +584,8 @@ __global__ __launch_bounds__(256) void mla_combine_wave_kernel(AttnArgs a) {
     float mb = Ms;
 #pragma unroll
     for (int u = 0; u < U; ++u) mb = ls[u] > 0.f ? fmaxf(mb, ms[u]) : mb;
-    if (mb == kNegInf) continue;
-    const float r = Ms == kNegInf ? 0.f : __builtin_amdgcn_exp2f(Ms - mb);
+    // (no early exit when mb = -inf, as in mla_combine_kernel)
+    const float r = Ms == kNegInf || mb == kNegInf ? 0.f : __builtin_amdgcn_exp2f(Ms - mb);
     Ls *= r;
 #pragma unroll
     for (int c = 0; c < PER; ++c) acc[c] *= r;
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(256) void mla_combine_wave_kernel(AttnArgs a) {
       }
     }
   }
-  const float f = finish_head(a, h, Ms, Ls);
+  const float f = finish_head_s2(sink2, Ms, Ls);
   const float inv = Ls > 0.f ? f / Ls : 0.f;
   uint16_t* orow = a.out + ((int64_t)t * a.H + h) * D + c0;
 #pragma unroll
